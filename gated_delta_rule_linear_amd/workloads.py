@@ -1,0 +1,304 @@
+"""Seeded synthetic inputs for the linear-attention recurrence.
+
+This module holds input generation only: random draws, the gate
+parameterisations that define the input distributions, per-token L2
+normalisation of q and k where a workload asks for it, and rounding to the
+storage dtype. It contains none of the recurrence's arithmetic, so both the
+GPU path's tests and the oracle can take their inputs from here.
+
+Recipe (every workload):
+  * numpy ``default_rng(seed)`` (PCG64); arrays are drawn in C order, in the
+    order q, k, v, then the gate pre-activations (u, then w for GDN), in fp64;
+  * gate transforms and normalisation are done in fp64;
+  * values are rounded fp64 -> fp32 (round to nearest even), then, for bf16
+    storage, fp32 -> bf16 (round to nearest even on the fp32 bit pattern);
+  * the fp64 copies handed to the oracle are the rounded values, exactly.
+
+Gate parameterisations (input distributions, per workload):
+  * GLA: g = exp(logsigmoid(u) / 16), u ~ N(0, 1) per (token, key dim)
+    (forget gate per key dimension, "Linear / RNN 路线" section 2.2);
+  * GDN: alpha = exp(-softplus(u)) = sigmoid(-u), beta = sigmoid(w), u, w ~
+    N(0, 1) per (token, head) (scalar gates in (0, 1), "线性注意力与 SSM"
+    section GDN);
+  * extra gate kinds for carry-sensitive tests: "slow" (alpha or g =
+    exp(logsigmoid(u) / 16), about 0.95), "ones" (g = 1 or alpha = 1),
+    "beta0" (beta = 0), "beta1" (beta = 1).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# bf16 helpers (storage format: uint16 bit patterns)
+# ---------------------------------------------------------------------------
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even) and return uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def round_to(x64: np.ndarray, dtype: str):
+    """Round fp64 values to the storage dtype.
+
+    Returns (stored, exact): ``stored`` is float32 or uint16 bf16 bits,
+    ``exact`` the float64 value of what is stored.
+    """
+    f32 = np.asarray(x64, dtype=np.float64).astype(np.float32)
+    if dtype == "f32":
+        return f32, f32.astype(np.float64)
+    if dtype == "bf16":
+        bits = f32_to_bf16_bits(f32)
+        return bits, bf16_bits_to_f32(bits).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def _logsigmoid(u):
+    # stable: log(sigmoid(u)) = -log1p(exp(-u)) for u >= 0, u - log1p(exp(u)) for u < 0
+    return np.where(u >= 0, -np.log1p(np.exp(-np.abs(u))), u - np.log1p(np.exp(-np.abs(u))))
+
+
+def _sigmoid(u):
+    return np.exp(_logsigmoid(u))
+
+
+# ---------------------------------------------------------------------------
+# Workload registry
+# ---------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    variant: str            # "kath" | "gla" | "gdn"
+    B: int
+    H: int
+    N: int
+    dk: int
+    dv: int
+    io: str                 # storage dtype of q, k, v, o: "f32" | "bf16"
+    gate_io: str            # storage dtype of gates: "f32" | "bf16"
+    seed: int
+    eps: float = 1e-6
+    qk_scale: float = 1.0   # q, k ~ N(0, qk_scale^2)
+    v_scale: float = 1.0
+    l2norm_qk: bool = False
+    gate_kind: str = "default"
+    decode: bool = False
+    description: str = field(default="", compare=False)
+
+    @property
+    def token_heads(self) -> int:
+        return self.B * self.H * self.N
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    "kath_f32_n256_d16": Workload(
+        "kath_f32_n256_d16", "kath", 1, 1, 256, 16, 16, "f32", "f32", seed=1,
+        description="normalized ELU+1 linear attention, 1 head, N=256, d=16, fp32"),
+    "gla_bf16_b2h8_n2048_d128": Workload(
+        "gla_bf16_b2h8_n2048_d128", "gla", 2, 8, 2048, 128, 128, "bf16", "bf16", seed=2,
+        qk_scale=1.0 / np.sqrt(128.0), v_scale=1.0 / np.sqrt(128.0),
+        description="GLA per-key-dim gate forward, B=2 H=8 N=2048 d=128, bf16"),
+    "kath_bf16_b1h16_n32768_dk128_dv64": Workload(
+        "kath_bf16_b1h16_n32768_dk128_dv64", "kath", 1, 16, 32768, 128, 64, "bf16", "bf16",
+        seed=3, description="normalized ELU+1 linear attention, B=1 H=16 N=32768 "
+                            "dphi=128 dv=64, bf16"),
+    "gdn_bf16_b4h16_n8192_d128": Workload(
+        "gdn_bf16_b4h16_n8192_d128", "gdn", 4, 16, 8192, 128, 128, "bf16", "bf16", seed=4,
+        l2norm_qk=True, description="Gated DeltaNet forward, B=4 H=16 N=8192 d=128, bf16, "
+                                    "q/k L2-normalized"),
+    "decode_gdn_256x32_d128": Workload(
+        "decode_gdn_256x32_d128", "gdn", 256, 32, 1, 128, 128, "bf16", "bf16", seed=5,
+        l2norm_qk=True, decode=True,
+        description="GDN decode step, 256 sequences x 32 heads, d=128, fp32 state"),
+    "decode_gla_256x32_d128": Workload(
+        "decode_gla_256x32_d128", "gla", 256, 32, 1, 128, 128, "bf16", "bf16", seed=5,
+        qk_scale=1.0 / np.sqrt(128.0), v_scale=1.0 / np.sqrt(128.0), decode=True,
+        description="GLA decode step, 256 sequences x 32 heads, d=128, fp32 state"),
+}
+
+DECODE_STATE_STD = 0.02   # decode state S ~ N(0, 0.02^2): std 0.02 (torch normal(mean, std))
+DECODE_POOL = 8           # distinct token sets cycled through by repeated decode steps
+
+
+@dataclass
+class Inputs:
+    """Device-format arrays plus their exact fp64 values.
+
+    ``dev`` maps name -> float32 array or uint16 bf16 bits; ``exact`` maps name
+    -> float64 copy of the same values. Names: q, k, v, and g (GLA gate or GDN
+    alpha) and beta (GDN), S0 / z0 when present.
+    """
+    wl: Workload
+    dev: dict
+    exact: dict
+
+
+def _draw_gates(rng, wl: Workload, shape_tok):
+    """Draw gate pre-activations and transform them (fp64). Returns dict."""
+    B, H, N = shape_tok
+    out = {}
+    kind = wl.gate_kind
+    if wl.variant == "gla":
+        u = rng.standard_normal((B, H, N, wl.dk))
+        if kind in ("default", "slow"):
+            g = np.exp(_logsigmoid(u) / 16.0)
+        elif kind == "ones":
+            g = np.ones_like(u)
+        elif kind == "fast":
+            g = _sigmoid(u + 1.0)          # strong forgetting, about 0.7 on average
+        else:
+            raise ValueError(kind)
+        out["g"] = g
+    elif wl.variant == "gdn":
+        u = rng.standard_normal((B, H, N))
+        w = rng.standard_normal((B, H, N))
+        if kind == "default":
+            alpha = _sigmoid(-u)                 # exp(-softplus(u))
+            beta = _sigmoid(w)
+        elif kind == "slow":
+            alpha = np.exp(_logsigmoid(u) / 16.0)
+            beta = _sigmoid(w)
+        elif kind == "ones":                      # DeltaNet: no decay
+            alpha = np.ones_like(u)
+            beta = _sigmoid(w)
+        elif kind == "beta0":                     # pure decay, no write
+            alpha = np.exp(_logsigmoid(u) / 16.0)
+            beta = np.zeros_like(w)
+        elif kind == "beta1":
+            alpha = _sigmoid(-u)
+            beta = np.ones_like(w)
+        else:
+            raise ValueError(kind)
+        out["g"] = alpha
+        out["beta"] = beta
+    return out
+
+
+def make_inputs(wl: Workload | str, *, with_state: bool = False, state_std: float = 0.5,
+                seed: int | None = None, N: int | None = None) -> Inputs:
+    """Generate one batch of seeded inputs for a prefill workload.
+
+    ``with_state`` adds a nonzero initial state S0 (and z0 for KATH, drawn
+    positive since z accumulates phi(k) > 0). ``seed`` / ``N`` override the
+    workload's values.
+    """
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    if N is not None:
+        wl = wl.with_(N=N)
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    B, H, N, dk, dv = wl.B, wl.H, wl.N, wl.dk, wl.dv
+    q = rng.standard_normal((B, H, N, dk)) * wl.qk_scale
+    k = rng.standard_normal((B, H, N, dk)) * wl.qk_scale
+    v = rng.standard_normal((B, H, N, dv)) * wl.v_scale
+    if wl.l2norm_qk:
+        q = q / np.linalg.norm(q, axis=-1, keepdims=True)
+        k = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    raw = {"q": q, "k": k, "v": v}
+    gates = _draw_gates(rng, wl, (B, H, N))
+    dev, exact = {}, {}
+    for name, arr in raw.items():
+        dev[name], exact[name] = round_to(arr, wl.io)
+    for name, arr in gates.items():
+        dev[name], exact[name] = round_to(arr, wl.gate_io)
+    if with_state:
+        S0 = rng.standard_normal((B, H, dk, dv)) * state_std
+        dev["S0"], exact["S0"] = round_to(S0, "f32")
+        if wl.variant == "kath":
+            z0 = np.abs(rng.standard_normal((B, H, dk))) * state_std * 4 + 0.5
+            dev["z0"], exact["z0"] = round_to(z0, "f32")
+    return Inputs(wl, dev, exact)
+
+
+def make_decode_pool(wl: Workload | str, *, pool: int = DECODE_POOL, seed: int | None = None,
+                     B: int | None = None, with_exact: bool = True):
+    """Decode workload: initial state S ~ N(0, 0.02^2) fp32 and a pool of token sets.
+
+    Token set j (q, k, v and gates, each [B, H, d] or [B, H]) is drawn like the
+    matching prefill workload with N = 1. Step s of a repeated decode run uses
+    token set s mod pool. Returns (S0_f32, S0_exact_or_None, [Inputs] * pool).
+    """
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    if B is not None:
+        wl = wl.with_(B=B)
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    S = rng.standard_normal((wl.B, wl.H, wl.dk, wl.dv), dtype=np.float64) * DECODE_STATE_STD
+    S32 = S.astype(np.float32)
+    del S
+    sets = []
+    for j in range(pool):
+        sub = make_inputs(wl.with_(N=1), seed=(wl.seed if seed is None else seed) * 1000 + 1 + j)
+        dev = {k: (a.reshape(a.shape[:2] + a.shape[3:]) if a.ndim >= 3 else a)
+               for k, a in sub.dev.items()}
+        ex = {k: (a.reshape(a.shape[:2] + a.shape[3:]) if a.ndim >= 3 else a)
+              for k, a in sub.exact.items()} if with_exact else {}
+        sets.append(Inputs(wl, dev, ex))
+    return S32, (S32.astype(np.float64) if with_exact else None), sets
+
+
+def algorithmic_bytes_per_token_head(wl: Workload) -> int:
+    """Bytes one pass must move at minimum: every input read once, every output written once.
+
+    Prefill: q, k, v (+ gates) read, o written, in their storage dtypes.
+    S_final (and z_final) are counted separately per sequence (see
+    ``algorithmic_bytes``). Decode: the fp32 state read and written once per
+    head plus the token's q, k, v, gates and o.
+    """
+    isz = 4 if wl.io == "f32" else 2
+    gsz = 4 if wl.gate_io == "f32" else 2
+    b = (2 * wl.dk + wl.dv) * isz + wl.dv * isz
+    if wl.variant == "gla":
+        b += wl.dk * gsz
+    elif wl.variant == "gdn":
+        b += 2 * gsz
+    return b
+
+
+def algorithmic_bytes(wl: Workload) -> int:
+    per = algorithmic_bytes_per_token_head(wl)
+    seqs = wl.B * wl.H
+    if wl.decode:
+        state = wl.dk * wl.dv * 4 * 2 + (wl.dk * 4 * 2 if wl.variant == "kath" else 0)
+        return seqs * (per + state)
+    state_out = wl.dk * wl.dv * 4 + (wl.dk * 4 if wl.variant == "kath" else 0)
+    return wl.token_heads * per + seqs * state_out
+
+
+def algorithmic_flops(wl: Workload, chunk: int = 64) -> int:
+    """Flops of the chunked method with full C x C tiles (C = chunk), per pass.
+
+    Per token-head: 2*C*d per C x C contraction and 2*dk*dv per state
+    contraction. KATH/GLA: Q K^T (2*C*dk), P V (2*C*dv), Q S and K^T V
+    (2 x 2*dk*dv); KATH adds the normaliser column (2*C + 2*dk for P 1, phi(q) z,
+    and dk for z += phi(k)). GDN: K K^T, Q K^T (2 x 2*C*dk), T (beta gamma K)
+    (2*C*dk), T (beta V) and P U (2 x 2*C*dv), Q S, W S and K^T U
+    (3 x 2*dk*dv) and the triangular inverse (C^2/3 per token).
+    Decode: 2*dk*dv per state read or write product (GLA 5, GDN 7, KATH 4 dk*dv).
+    """
+    dk, dv, C = wl.dk, wl.dv, chunk
+    if wl.decode:
+        per = {"gla": 5, "gdn": 7, "kath": 4}[wl.variant] * dk * dv
+        return wl.B * wl.H * per
+    if wl.variant == "gla":
+        per = 2 * C * dk + 2 * C * dv + 4 * dk * dv
+    elif wl.variant == "kath":
+        per = 2 * C * dk + 2 * C * (dv + 1) + 4 * dk * dv + 3 * dk
+    else:
+        per = 6 * C * dk + 4 * C * dv + 6 * dk * dv + (C * C) // 3
+    return wl.token_heads * per

@@ -1,0 +1,249 @@
+/*
+ * Oracle for the causal linear-attention state recurrence: plain, slow, fp64,
+ * token by token, on the host.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library. The GPU library never
+ * links, calls or includes anything from here, and nothing here comes from
+ * the GPU library: the two share no code, tables or constants.
+ *
+ * What it computes, for every (b, h) sequence independently and t = 1..N,
+ * with S_0 = S0 (or zeros) and z_0 = z0 (or zeros). The state is key-major,
+ * S in R^{d_k x d_v}:
+ *
+ *  KATH  "Linear / RNN 路线" (walkerchi.com playbook), section 2.1, the
+ *        recurrence and the step function; "线性注意力与 SSM" (ailearn), section
+ *        02; "状态空间与线性注意力" (wineandchord), section 线性注意力, normalized
+ *        output with epsilon:
+ *          phi(x) = x + 1 (x > 0), exp(x) (x <= 0)      [ELU with alpha 1, plus 1]
+ *          S_t = S_{t-1} + phi(k_t) v_t^T,  z_t = z_{t-1} + phi(k_t)
+ *          o_t = phi(q_t)^T S_t / (phi(q_t)^T z_t + eps)
+ *  GLA   "Linear / RNN 路线", section 2.2, boxed equation:
+ *          S_t = diag(g_t) S_{t-1} + k_t v_t^T,  o_t = S_t^T q_t
+ *  GDN   "线性注意力与 SSM", section GDN (gated delta rule), which writes the
+ *        state value-major as S_t = a_t S_{t-1}(I - b_t k_t k_t^T) + b_t v_t k_t^T
+ *        and notes that the write equals a correction by v_t - a_t S_{t-1} k_t.
+ *        Key-major this is S_t = a_t S_{t-1} + k_t u_t^T with
+ *          u_t = b_t (v_t - a_t S_{t-1}^T k_t),   o_t = S_t^T q_t.
+ *
+ * Every variant reads the state after the token's update (the post-update
+ * read of all three pages' output equations).
+ *
+ * Decode is the same per-token body applied once, in place.
+ *
+ * Counters (work accounting, "线性注意力与 SSM" section 02 hand count): each
+ * state-update multiply-add and each state-read multiply-add is counted as it
+ * is executed.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_KATH = 0, OR_GLA = 1, OR_GDN = 2 };
+
+typedef struct {
+    uint64_t state_update_macs; /* multiply-adds that write S */
+    uint64_t state_read_macs;   /* multiply-adds that read S into an output */
+    uint64_t norm_update_adds;  /* additions into z (KATH) */
+    uint64_t norm_read_macs;    /* multiply-adds of phi(q)^T z (KATH) */
+    uint64_t tokens;            /* token-heads processed */
+} oracle_counts;
+
+static double elu_plus_one(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
+
+/* One token of one head. S: dk x dv (row i = key dim i), z: dk (KATH only).
+ * work: scratch of at least 2*dk + dv doubles. */
+static void token_step(int variant, int dk, int dv, const double *q, const double *k,
+                       const double *v, const double *g, double beta, double eps,
+                       double *S, double *z, double *o, double *work, oracle_counts *c)
+{
+    int i, j;
+    if (variant == OR_KATH) {
+        double *fq = work, *fk = work + dk;
+        double den = 0.0;
+        for (i = 0; i < dk; ++i) {
+            fq[i] = elu_plus_one(q[i]);
+            fk[i] = elu_plus_one(k[i]);
+        }
+        for (i = 0; i < dk; ++i) {
+            for (j = 0; j < dv; ++j) S[(size_t)i * dv + j] += fk[i] * v[j];
+            c->state_update_macs += (uint64_t)dv;
+            z[i] += fk[i];
+        }
+        c->norm_update_adds += (uint64_t)dk;
+        for (i = 0; i < dk; ++i) den += fq[i] * z[i];
+        c->norm_read_macs += (uint64_t)dk;
+        den += eps;
+        for (j = 0; j < dv; ++j) {
+            double num = 0.0;
+            for (i = 0; i < dk; ++i) num += fq[i] * S[(size_t)i * dv + j];
+            o[j] = num / den;
+        }
+        c->state_read_macs += (uint64_t)dk * (uint64_t)dv;
+    } else if (variant == OR_GLA) {
+        /* row i of S is scaled by the gate of key dim i, then the outer product is added */
+        for (i = 0; i < dk; ++i) {
+            for (j = 0; j < dv; ++j)
+                S[(size_t)i * dv + j] = g[i] * S[(size_t)i * dv + j] + k[i] * v[j];
+            c->state_update_macs += (uint64_t)dv;
+        }
+        for (j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (i = 0; i < dk; ++i) acc += q[i] * S[(size_t)i * dv + j];
+            o[j] = acc;
+        }
+        c->state_read_macs += (uint64_t)dk * (uint64_t)dv;
+    } else { /* OR_GDN: alpha is g[0] */
+        double alpha = g[0];
+        double *u = work; /* dv */
+        for (j = 0; j < dv; ++j) {
+            double pred = 0.0; /* (S_{t-1}^T k_t)_j: what the old state recalls for k_t */
+            for (i = 0; i < dk; ++i) pred += S[(size_t)i * dv + j] * k[i];
+            u[j] = beta * (v[j] - alpha * pred);
+        }
+        for (i = 0; i < dk; ++i) {
+            for (j = 0; j < dv; ++j)
+                S[(size_t)i * dv + j] = alpha * S[(size_t)i * dv + j] + k[i] * u[j];
+            c->state_update_macs += (uint64_t)dv;
+        }
+        for (j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (i = 0; i < dk; ++i) acc += q[i] * S[(size_t)i * dv + j];
+            o[j] = acc;
+        }
+        c->state_read_macs += (uint64_t)dk * (uint64_t)dv;
+    }
+    c->tokens += 1;
+}
+
+static int check_args(int variant, int B, int H, int N, int dk, int dv)
+{
+    if (variant < OR_KATH || variant > OR_GDN) return 1;
+    if (B < 0 || H < 0 || N < 0 || dk < 1 || dv < 1) return 1;
+    return 0;
+}
+
+/*
+ * Whole-sequence forward.
+ *   q, k: [B,H,N,dk]   v: [B,H,N,dv]
+ *   g:    GLA [B,H,N,dk]; GDN alpha [B,H,N]; KATH unused (may be NULL)
+ *   beta: GDN [B,H,N]; otherwise unused
+ *   S0:   [B,H,dk,dv] or NULL (zeros);   z0: [B,H,dk] or NULL (zeros), KATH only
+ *   o:    [B,H,N,dv] out;  S: [B,H,dk,dv] out (final state);  z: [B,H,dk] out (KATH, may be NULL otherwise)
+ *   counts: optional, summed over all sequences.
+ *   threads: OpenMP threads over the B*H sequences (<= 0: runtime default).
+ * Returns 0, or 1 on a bad argument.
+ */
+int oracle_prefill(int variant, int B, int H, int N, int dk, int dv,
+                   const double *q, const double *k, const double *v,
+                   const double *g, const double *beta,
+                   const double *S0, const double *z0, double eps,
+                   double *o, double *S, double *z, int threads, oracle_counts *counts)
+{
+    long long seq, nseq;
+    oracle_counts total;
+    if (check_args(variant, B, H, N, dk, dv)) return 1;
+    if (variant == OR_KATH && z == NULL) return 1;
+    if (variant != OR_KATH && g == NULL) return 1;
+    if (variant == OR_GDN && beta == NULL) return 1;
+    memset(&total, 0, sizeof(total));
+    nseq = (long long)B * H;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel
+    {
+        oracle_counts c;
+        double *work = (double *)malloc(sizeof(double) * (size_t)(2 * dk + dv));
+        memset(&c, 0, sizeof(c));
+#pragma omp for schedule(dynamic, 1)
+        for (seq = 0; seq < nseq; ++seq) {
+            double *Sh = S + (size_t)seq * dk * dv;
+            double *zh = (variant == OR_KATH) ? z + (size_t)seq * dk : NULL;
+            int t;
+            if (S0) memcpy(Sh, S0 + (size_t)seq * dk * dv, sizeof(double) * (size_t)dk * dv);
+            else memset(Sh, 0, sizeof(double) * (size_t)dk * dv);
+            if (zh) {
+                if (z0) memcpy(zh, z0 + (size_t)seq * dk, sizeof(double) * (size_t)dk);
+                else memset(zh, 0, sizeof(double) * (size_t)dk);
+            }
+            for (t = 0; t < N; ++t) {
+                size_t tok = (size_t)seq * N + t;
+                const double *gt = NULL;
+                double bt = 0.0;
+                if (variant == OR_GLA) gt = g + tok * dk;
+                if (variant == OR_GDN) { gt = g + tok; bt = beta[tok]; }
+                token_step(variant, dk, dv, q + tok * dk, k + tok * dk, v + tok * dv, gt, bt,
+                           eps, Sh, zh, o + tok * dv, work, &c);
+            }
+        }
+#pragma omp critical
+        {
+            total.state_update_macs += c.state_update_macs;
+            total.state_read_macs += c.state_read_macs;
+            total.norm_update_adds += c.norm_update_adds;
+            total.norm_read_macs += c.norm_read_macs;
+            total.tokens += c.tokens;
+        }
+        free(work);
+    }
+    if (counts) *counts = total;
+    return 0;
+}
+
+/*
+ * One decode step for B*H independent states, in place.
+ *   q, k: [B,H,dk]  v: [B,H,dv]  g: GLA [B,H,dk] / GDN alpha [B,H]  beta: GDN [B,H]
+ *   S: [B,H,dk,dv] in/out;  z: [B,H,dk] in/out (KATH);  o: [B,H,dv] out.
+ */
+int oracle_decode_step(int variant, int B, int H, int dk, int dv,
+                       const double *q, const double *k, const double *v,
+                       const double *g, const double *beta, double eps,
+                       double *S, double *z, double *o, int threads)
+{
+    long long seq, nseq;
+    if (check_args(variant, B, H, 1, dk, dv)) return 1;
+    if (variant == OR_KATH && z == NULL) return 1;
+    if (variant != OR_KATH && g == NULL) return 1;
+    if (variant == OR_GDN && beta == NULL) return 1;
+    nseq = (long long)B * H;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel
+    {
+        oracle_counts c;
+        double *work = (double *)malloc(sizeof(double) * (size_t)(2 * dk + dv));
+        memset(&c, 0, sizeof(c));
+#pragma omp for schedule(static)
+        for (seq = 0; seq < nseq; ++seq) {
+            const double *gt = NULL;
+            double bt = 0.0;
+            if (variant == OR_GLA) gt = g + (size_t)seq * dk;
+            if (variant == OR_GDN) { gt = g + seq; bt = beta[seq]; }
+            token_step(variant, dk, dv, q + (size_t)seq * dk, k + (size_t)seq * dk,
+                       v + (size_t)seq * dv, gt, bt, eps, S + (size_t)seq * dk * dv,
+                       variant == OR_KATH ? z + (size_t)seq * dk : NULL,
+                       o + (size_t)seq * dv, work, &c);
+        }
+        free(work);
+    }
+    return 0;
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,370 @@
+"""Pins for the fp64 oracle: facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` function raises AssertionError when the oracle library at
+``lib`` (a path, or None for the built one) disagrees with a fact that does
+not come from the oracle itself:
+
+  * explicit masked quadratic (semiseparable) forms built without any
+    recurrence ("状态空间与线性注意力", section State Space Duality, the
+    matrix M_{j,i} = C_j^T A_j ... A_{i+1} B_i; and the validation matrix's
+    "explicit lower-triangular matrix" row);
+  * split / carry invariance ("状态空间与线性注意力", minimal semantic
+    implementation: split anywhere, carry the state, equal the whole scan);
+  * the gated delta rule written in its value-major matrix form
+    ("线性注意力与 SSM", section GDN) and the KDA recurrence with a broadcast
+    gate ("状态空间与线性注意力", section KDA);
+  * the worked delta-rule example (golden fixture);
+  * the single-head hand count (golden fixture);
+  * closed forms for constant inputs; special cases that reduce to known
+    forms (plain causal linear attention, RetNet's decayed parallel form,
+    DeltaNet, pure decay); causality; linearity in V.
+
+The functions are shared by ``test_oracle_pins.py`` (against the built
+oracle) and the mutation tests (against deliberately broken copies of the
+oracle source, which must fail at least one pin).
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+def phi_lib(x: np.ndarray) -> np.ndarray:
+    """ELU (alpha = 1) plus one, from torch's ELU in float64."""
+    return (torch.nn.functional.elu(torch.from_numpy(np.asarray(x, np.float64))) + 1.0).numpy()
+
+
+def rand_case(variant, B=1, H=2, N=12, dk=5, dv=4, seed=0, with_state=True, unit_keys=False):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, N, dk))
+    k = rng.standard_normal((B, H, N, dk))
+    v = rng.standard_normal((B, H, N, dv))
+    g = beta = None
+    if unit_keys:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    if variant == "gla":
+        g = rng.uniform(0.5, 1.0, (B, H, N, dk))
+    elif variant == "gdn":
+        g = rng.uniform(0.5, 1.0, (B, H, N))
+        beta = rng.uniform(0.05, 0.95, (B, H, N))
+    S0 = rng.standard_normal((B, H, dk, dv)) * 0.7 if with_state else None
+    z0 = (rng.uniform(0.5, 2.0, (B, H, dk)) if (with_state and variant == "kath") else None)
+    return dict(q=q, k=k, v=v, g=g, beta=beta, S0=S0, z0=z0)
+
+
+def run(variant, case, lib=None, eps=1e-6, **kw):
+    return oracle.prefill(variant, case["q"], case["k"], case["v"], case["g"], case["beta"],
+                          case["S0"], case["z0"], eps=eps, lib_path=lib, **kw)
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ---------------------------------------------------------------------------
+# explicit quadratic forms (no recurrence), one head at a time
+# ---------------------------------------------------------------------------
+
+def quad_kath(q, k, v, S0, z0, eps):
+    T = q.shape[0]
+    fq, fk = phi_lib(q), phi_lib(k)
+    A = np.tril(fq @ fk.T)
+    num = A @ v + fq @ S0
+    den = A @ np.ones(T) + fq @ z0 + eps
+    O = num / den[:, None]
+    return O, S0 + fk.T @ v, z0 + fk.sum(axis=0)
+
+
+def quad_gla(q, k, v, g, S0):
+    T, dk = q.shape
+    M = np.zeros((T, T))
+    for t in range(T):
+        for s in range(t + 1):
+            w = np.prod(g[s + 1:t + 1], axis=0) if t > s else np.ones(dk)
+            M[t, s] = np.sum(q[t] * k[s] * w)
+    pref = np.array([np.prod(g[:t + 1], axis=0) for t in range(T)])  # prod_{r<=t} g_r
+    O = M @ v + (q * pref) @ S0
+    S = pref[-1][:, None] * S0
+    for s in range(T):
+        w = np.prod(g[s + 1:], axis=0) if s < T - 1 else np.ones(dk)
+        S = S + np.outer(w * k[s], v[s])
+    return O, S
+
+
+def quad_gdn(q, k, v, alpha, beta, S0):
+    """Key-major state; F_t = alpha_t (I - beta_t k_t k_t^T), later factors on the left."""
+    T, dk = q.shape
+    I = np.eye(dk)
+    F = [alpha[t] * (I - beta[t] * np.outer(k[t], k[t])) for t in range(T)]
+
+    def chain(t, s):  # F_t F_{t-1} ... F_{s+1}   (identity when t == s)
+        P = I.copy()
+        for r in range(s + 1, t + 1):
+            P = F[r] @ P
+        return P
+
+    M = np.zeros((T, T))
+    for t in range(T):
+        for s in range(t + 1):
+            M[t, s] = beta[s] * q[t] @ chain(t, s) @ k[s]
+    O = M @ v + np.array([q[t] @ (chain(t, -1) @ S0) for t in range(T)])
+    S = chain(T - 1, -1) @ S0
+    for s in range(T):
+        S = S + chain(T - 1, s) @ np.outer(beta[s] * k[s], v[s])
+    return O, S
+
+
+# ---------------------------------------------------------------------------
+# pins
+# ---------------------------------------------------------------------------
+
+def pin_quadratic_form(lib=None):
+    for variant, dk, dv in (("kath", 5, 3), ("gla", 5, 3), ("gdn", 4, 6), ("gdn", 6, 4)):
+        case = rand_case(variant, B=2, H=1, N=11, dk=dk, dv=dv, seed=7, with_state=True)
+        eps = 0.3 if variant == "kath" else 1e-6
+        o, S, z = run(variant, case, lib, eps=eps)
+        for b in range(2):
+            sl = (b, 0)
+            if variant == "kath":
+                O_ref, S_ref, z_ref = quad_kath(case["q"][sl], case["k"][sl], case["v"][sl],
+                                                case["S0"][sl], case["z0"][sl], eps)
+                assert rel(z[sl], z_ref) < 1e-12, "KATH z vs quadratic form"
+            elif variant == "gla":
+                O_ref, S_ref = quad_gla(case["q"][sl], case["k"][sl], case["v"][sl],
+                                        case["g"][sl], case["S0"][sl])
+            else:
+                O_ref, S_ref = quad_gdn(case["q"][sl], case["k"][sl], case["v"][sl],
+                                        case["g"][sl], case["beta"][sl], case["S0"][sl])
+            assert rel(o[sl], O_ref) < 1e-12, f"{variant} o vs quadratic form: {rel(o[sl], O_ref)}"
+            assert rel(S[sl], S_ref) < 1e-12, f"{variant} S vs quadratic form"
+
+
+def pin_split_invariance(lib=None):
+    for variant in ("kath", "gla", "gdn"):
+        case = rand_case(variant, B=1, H=3, N=23, dk=6, dv=5, seed=11, with_state=True)
+        o, S, z = run(variant, case, lib)
+        for m in (1, 7, 16, 22):
+            left = {kk: (vv[:, :, :m] if (vv is not None and kk in ("q", "k", "v", "g", "beta"))
+                         else vv) for kk, vv in case.items()}
+            oL, SL, zL = run(variant, left, lib)
+            right = {kk: (vv[:, :, m:] if (vv is not None and kk in ("q", "k", "v", "g", "beta"))
+                          else vv) for kk, vv in case.items()}
+            right["S0"], right["z0"] = SL, zL
+            oR, SR, zR = run(variant, right, lib)
+            assert np.array_equal(np.concatenate([oL, oR], axis=2), o), f"{variant} split o m={m}"
+            assert np.array_equal(SR, S), f"{variant} split S m={m}"
+            if variant == "kath":
+                assert np.array_equal(zR, z), f"{variant} split z m={m}"
+
+
+def pin_gdn_page_forms(lib=None):
+    """Value-major matrix form and the KDA recurrence with alpha broadcast, step by step."""
+    case = rand_case("gdn", B=1, H=1, N=9, dk=5, dv=3, seed=5, with_state=True, unit_keys=True)
+    q, k, v = case["q"][0, 0], case["k"][0, 0], case["v"][0, 0]
+    a, b = case["g"][0, 0], case["beta"][0, 0]
+    o, S, _ = run("gdn", case, lib)
+    Sv = case["S0"][0, 0].T.copy()          # value-major d_v x d_k
+    Sk = case["S0"][0, 0].copy()            # key-major for the KDA form
+    I = np.eye(5)
+    for t in range(9):
+        Sv = a[t] * Sv @ (I - b[t] * np.outer(k[t], k[t])) + b[t] * np.outer(v[t], k[t])
+        Sbar = (a[t] * np.ones(5))[:, None] * Sk
+        Sk = Sbar + b[t] * np.outer(k[t], v[t] - k[t] @ Sbar)
+        assert rel(o[0, 0, t], Sv @ q[t]) < 1e-12, "GDN o vs value-major form"
+        assert rel(o[0, 0, t], Sk.T @ q[t]) < 1e-12, "GDN o vs KDA form"
+    assert rel(S[0, 0], Sv.T) < 1e-12 and rel(S[0, 0], Sk) < 1e-12
+
+
+def pin_delta_identity(lib=None):
+    """S_t - a_t S_{t-1} = b_t k_t (v_t - a_t S_{t-1}^T k_t)^T at every step (decode steps)."""
+    case = rand_case("gdn", B=1, H=2, N=8, dk=4, dv=3, seed=9, with_state=True)
+    S = case["S0"].copy()
+    for t in range(8):
+        prev = S.copy()
+        oracle.decode_step("gdn", case["q"][:, :, t], case["k"][:, :, t], case["v"][:, :, t], S,
+                           g=case["g"][:, :, t], beta=case["beta"][:, :, t], lib_path=lib)
+        for h in range(2):
+            kk, vv = case["k"][0, h, t], case["v"][0, h, t]
+            a, b = case["g"][0, h, t], case["beta"][0, h, t]
+            lhs = S[0, h] - a * prev[0, h]
+            rhs = b * np.outer(kk, vv - a * prev[0, h].T @ kk)
+            assert rel(lhs, rhs) < 1e-12, "delta-rule identity"
+
+
+def pin_worked_example(lib=None):
+    with open(os.path.join(GOLDEN, "delta_rule_worked_example.json")) as f:
+        ex = json.load(f)
+    keys = np.array(ex["keys"])
+    values = np.array(ex["values"])
+    beta = np.array(ex["beta"])
+    T, dk = keys.shape
+    dv = values.shape[1]
+    sh = lambda a: a.reshape((1, 1) + a.shape)
+    # GDN with alpha = 1 and beta = 1; queries = keys so the post-write read recalls the value
+    o, S, _ = oracle.prefill("gdn", sh(keys), sh(keys), sh(values), sh(np.ones(T)), sh(beta),
+                             lib_path=lib)
+    assert np.array_equal(keys @ S[0, 0], np.array(ex["final_state_times_keys"])), "keys @ S"
+    assert np.array_equal(o[0, 0], values), "post-write recall"
+    # reads before each write: S_{t-1}^T k_t from the state after the prefix
+    state = np.zeros((1, 1, dk, dv))
+    reads = []
+    for t in range(T):
+        reads.append(state[0, 0].T @ keys[t])
+        oracle.decode_step("gdn", sh(keys[t]), sh(keys[t]), sh(values[t]), state,
+                           g=np.ones((1, 1)), beta=np.full((1, 1), beta[t]), lib_path=lib)
+    assert np.array_equal(np.array(reads), np.array(ex["reads_before_write"]))
+
+
+def pin_hand_count(lib=None):
+    with open(os.path.join(GOLDEN, "hand_count_single_head.json")) as f:
+        hc = json.load(f)
+    N, dk, dv = hc["N"], hc["d_phi"], hc["d_v"]
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((1, 1, N, dk)).astype(np.float32).astype(np.float64)
+    k = rng.standard_normal((1, 1, N, dk)).astype(np.float32).astype(np.float64)
+    v = rng.standard_normal((1, 1, N, dv)).astype(np.float32).astype(np.float64)
+    o, S, z, c = oracle.prefill("kath", q, k, v, with_counts=True, lib_path=lib)
+    assert S[0, 0].size == hc["state_elements"] and z[0, 0].size == hc["z_elements"]
+    assert c.state_update_macs == hc["main_term_macs"], c
+    assert c.state_read_macs == hc["main_term_macs"], c
+    assert abs(c.state_update_macs - hc["main_term_macs_rounded"]) / hc["main_term_macs_rounded"] < 5e-4
+    assert c.tokens == N and c.norm_update_adds == N * dk and c.norm_read_macs == N * dk
+    assert N * N == hc["full_attention_scores"]
+
+
+def pin_closed_forms(lib=None):
+    T, eps = 40, 0.25
+    # KATH, constant tokens: S_t = t phi(k) v^T, z_t = t phi(k), o_t = v * t a / (t a + eps)
+    qv = np.array([-1.0, 0.0, 0.5, 2.0, -0.3])
+    kv = np.array([0.7, -2.0, 0.0, 1.5, -0.1])
+    vv = np.array([1.0, -2.0, 0.5])
+    fq = np.array([np.exp(-1.0), 1.0, 1.5, 3.0, np.exp(-0.3)])      # ELU(x)+1 by its definition
+    fk = np.array([1.7, np.exp(-2.0), 1.0, 2.5, np.exp(-0.1)])
+    assert rel(phi_lib(qv), fq) < 1e-15 and rel(phi_lib(kv), fk) < 1e-15
+    tile = lambda x: np.broadcast_to(x, (1, 1, T, x.size)).copy()
+    o, S, z = oracle.prefill("kath", tile(qv), tile(kv), tile(vv), eps=eps, lib_path=lib)
+    a = fq @ fk
+    t = np.arange(1, T + 1)[:, None]
+    assert rel(o[0, 0], vv[None, :] * (t * a) / (t * a + eps)) < 1e-13, "KATH closed form"
+    assert rel(S[0, 0], T * np.outer(fk, vv)) < 1e-13 and rel(z[0, 0], T * fk) < 1e-13
+    # GLA, constant tokens and gate: S_t = diag((1 - g^t) / (1 - g)) k v^T
+    gv = np.array([0.9, 0.5, 0.99, 0.7, 0.3])
+    o, S, _ = oracle.prefill("gla", tile(qv), tile(kv), tile(vv), g=tile(gv), lib_path=lib)
+    for tt in (1, 2, 17, T):
+        St = np.outer((1 - gv ** tt) / (1 - gv) * kv, vv)
+        assert rel(o[0, 0, tt - 1], St.T @ qv) < 1e-13, "GLA closed form o"
+    assert rel(S[0, 0], np.outer((1 - gv ** T) / (1 - gv) * kv, vv)) < 1e-13
+    # GDN, constant tokens with |k| = 1: S_t = k p_t^T, p_t = beta v (1 - rho^t) / (1 - rho)
+    ku = kv / np.linalg.norm(kv)
+    al, be = 0.8, 0.6
+    rho = al * (1 - be)
+    o, S, _ = oracle.prefill("gdn", tile(qv), tile(ku), tile(vv), g=np.full((1, 1, T), al),
+                             beta=np.full((1, 1, T), be), lib_path=lib)
+    for tt in (1, 2, 9, T):
+        p = be * vv * (1 - rho ** tt) / (1 - rho)
+        assert rel(o[0, 0, tt - 1], (ku @ qv) * p) < 1e-13, "GDN closed form o"
+    assert rel(S[0, 0], np.outer(ku, be * vv * (1 - rho ** T) / (1 - rho))) < 1e-13
+
+
+def pin_special_cases(lib=None):
+    # GDN beta = 0: pure decay of S0
+    case = rand_case("gdn", B=1, H=2, N=10, dk=4, dv=3, seed=3, with_state=True)
+    case["beta"] = np.zeros_like(case["beta"])
+    o, S, _ = run("gdn", case, lib)
+    pref = np.cumprod(case["g"], axis=2)
+    for h in range(2):
+        for t in range(10):
+            ref = pref[0, h, t] * case["S0"][0, h].T @ case["q"][0, h, t]
+            assert rel(o[0, h, t], ref) < 1e-13, "GDN beta=0"
+        assert rel(S[0, h], pref[0, h, -1] * case["S0"][0, h]) < 1e-13
+    # GDN alpha = 1: DeltaNet, S_t = S_{t-1} + beta k (v - S_{t-1}^T k)^T
+    case = rand_case("gdn", B=1, H=1, N=10, dk=4, dv=3, seed=4, with_state=True)
+    case["g"] = np.ones_like(case["g"])
+    o, S, _ = run("gdn", case, lib)
+    St = case["S0"][0, 0].copy()
+    for t in range(10):
+        kk = case["k"][0, 0, t]
+        St = St + case["beta"][0, 0, t] * np.outer(kk, case["v"][0, 0, t] - St.T @ kk)
+        assert rel(o[0, 0, t], St.T @ case["q"][0, 0, t]) < 1e-12, "DeltaNet"
+    # GLA g = 1: plain causal linear attention, O = tril(Q K^T) V + Q S0
+    case = rand_case("gla", B=1, H=1, N=13, dk=5, dv=4, seed=5, with_state=True)
+    case["g"] = np.ones_like(case["g"])
+    o, S, _ = run("gla", case, lib)
+    Q, K, V = case["q"][0, 0], case["k"][0, 0], case["v"][0, 0]
+    assert rel(o[0, 0], np.tril(Q @ K.T) @ V + Q @ case["S0"][0, 0]) < 1e-12, "GLA g=1"
+    assert rel(S[0, 0], case["S0"][0, 0] + K.T @ V) < 1e-12
+    # GLA with one scalar gate for all key dims: RetNet parallel form with D_ts = gamma^(t-s)
+    case = rand_case("gla", B=1, H=1, N=13, dk=5, dv=4, seed=6, with_state=False)
+    gam = 0.83
+    case["g"] = np.full_like(case["g"], gam)
+    o, S, _ = run("gla", case, lib)
+    Q, K, V = case["q"][0, 0], case["k"][0, 0], case["v"][0, 0]
+    tt = np.arange(13)
+    D = np.where(tt[:, None] >= tt[None, :], gam ** (tt[:, None] - tt[None, :]).clip(0), 0.0)
+    assert rel(o[0, 0], ((Q @ K.T) * D) @ V) < 1e-12, "RetNet form"
+
+
+def pin_causality(lib=None):
+    for variant in ("kath", "gla", "gdn"):
+        case = rand_case(variant, B=1, H=2, N=16, dk=4, dv=3, seed=13, with_state=True)
+        o, _, _ = run(variant, case, lib)
+        for tp in (0, 5, 15):
+            c2 = {kk: (None if vv is None else vv.copy()) for kk, vv in case.items()}
+            c2["q"][:, :, tp] += 1.5
+            c2["k"][:, :, tp] -= 0.75
+            c2["v"][:, :, tp] *= -3.0
+            if c2["g"] is not None:
+                c2["g"][:, :, tp] *= 0.5
+            o2, _, _ = run(variant, c2, lib)
+            assert np.array_equal(o2[:, :, :tp], o[:, :, :tp]), f"{variant} causality t'={tp}"
+            assert not np.array_equal(o2[:, :, tp], o[:, :, tp])
+
+
+def pin_linearity(lib=None):
+    for variant in ("gla", "gdn"):
+        case = rand_case(variant, B=1, H=2, N=14, dk=5, dv=4, seed=17, with_state=False)
+        rng = np.random.default_rng(1)
+        v1, v2 = rng.standard_normal(case["v"].shape), rng.standard_normal(case["v"].shape)
+        a, b = 1.7, -0.4
+        outs = []
+        for vv in (v1, v2, a * v1 + b * v2):
+            c2 = dict(case)
+            c2["v"] = vv
+            outs.append(run(variant, c2, lib))
+        assert rel(outs[2][0], a * outs[0][0] + b * outs[1][0]) < 1e-12, f"{variant} linear in V"
+        assert rel(outs[2][1], a * outs[0][1] + b * outs[1][1]) < 1e-12
+
+
+def pin_decode_matches_prefill(lib=None):
+    for variant in ("kath", "gla", "gdn"):
+        case = rand_case(variant, B=2, H=2, N=6, dk=4, dv=3, seed=21, with_state=True)
+        o, S, z = run(variant, case, lib)
+        St = case["S0"].copy()
+        zt = case["z0"].copy() if variant == "kath" else None
+        for t in range(6):
+            ot = oracle.decode_step(
+                variant, case["q"][:, :, t], case["k"][:, :, t], case["v"][:, :, t], St,
+                g=None if case["g"] is None else case["g"][:, :, t],
+                beta=None if case["beta"] is None else case["beta"][:, :, t], z=zt, lib_path=lib)
+            assert np.array_equal(ot, o[:, :, t]), f"{variant} decode step {t}"
+        assert np.array_equal(St, S)
+        if variant == "kath":
+            assert np.array_equal(zt, z)
+
+
+ALL_PINS = [pin_quadratic_form, pin_split_invariance, pin_gdn_page_forms, pin_delta_identity,
+            pin_worked_example, pin_closed_forms, pin_special_cases, pin_causality,
+            pin_linearity, pin_decode_matches_prefill]

@@ -1,0 +1,51 @@
+"""Plant plausible mistakes in copies of the oracle source and check that the pins catch each.
+
+Each mutation is a textual edit of ``oracle/oracle.c`` compiled into a
+temporary library (CPU only). A mutation that no pin detects would mean a
+part of the oracle is not pinned.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins as P
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTATIONS = {
+    "kath_no_eps": ("den += eps;", "den += 0.0;"),
+    "kath_elu_without_plus_one": ("x + 1.0 : exp(x)", "x + 1.0 : exp(x) - 1.0"),
+    "kath_z_not_updated": ("z[i] += fk[i];", "z[i] += 0.0;"),
+    "kath_phi_on_v_side": ("S[(size_t)i * dv + j] += fk[i] * v[j];",
+                           "S[(size_t)i * dv + j] += k[i] * v[j];"),
+    "gla_gate_after_write": ("g[i] * S[(size_t)i * dv + j] + k[i] * v[j]",
+                             "g[i] * (S[(size_t)i * dv + j] + k[i] * v[j])"),
+    "gla_gate_previous_token": ("gt = g + tok * dk;", "gt = g + (t > 0 ? tok - 1 : tok) * dk;"),
+    "gdn_sign": ("u[j] = beta * (v[j] - alpha * pred);", "u[j] = beta * (v[j] + alpha * pred);"),
+    "gdn_prediction_not_decayed": ("u[j] = beta * (v[j] - alpha * pred);",
+                                   "u[j] = beta * (v[j] - pred);"),
+    "gdn_no_beta": ("u[j] = beta * (v[j] - alpha * pred);", "u[j] = (v[j] - alpha * pred);"),
+    "gdn_transposed_read": ("pred += S[(size_t)i * dv + j] * k[i];",
+                            "pred += S[(size_t)j * dv + i] * k[i];"),
+    "initial_state_ignored": ("if (S0) memcpy", "if (0) memcpy"),
+    "read_uses_key": ("for (i = 0; i < dk; ++i) acc += q[i] * S[(size_t)i * dv + j];\n            o[j] = acc;\n        }\n        c->state_read_macs += (uint64_t)dk * (uint64_t)dv;\n    } else {",
+                      "for (i = 0; i < dk; ++i) acc += k[i] * S[(size_t)i * dv + j];\n            o[j] = acc;\n        }\n        c->state_read_macs += (uint64_t)dk * (uint64_t)dv;\n    } else {"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {name}"
+    mutated = tmp_path / "oracle_mut.c"
+    mutated.write_text(src.replace(old, new, 1))
+    lib = oracle.compile_library(str(mutated), str(tmp_path / f"liboracle_{name}.so"))
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin detects the planted mistake {name}"
