@@ -1,0 +1,180 @@
+"""ctypes binding of ``liblinattn.so`` (declared in ``include/linattn.h``).
+
+Argument marshalling only: torch supplies device memory and the stream, every
+step of the computation runs in the library's HIP kernels. If the library is
+missing the first call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblinattn.so")
+
+LA_OK, LA_ERR_INVALID, LA_ERR_UNSUPPORTED, LA_ERR_HIP, LA_ERR_WORKSPACE = 0, 1, 2, 3, 4
+LA_KATH, LA_GLA, LA_GDN = 0, 1, 2
+LA_F32, LA_BF16 = 0, 1
+LA_PATH_AUTO, LA_PATH_VALU, LA_PATH_MFMA = 0, 1, 2
+
+VARIANTS = {"kath": LA_KATH, "gla": LA_GLA, "gdn": LA_GDN}
+PATHS = {"auto": LA_PATH_AUTO, "valu": LA_PATH_VALU, "mfma": LA_PATH_MFMA}
+EXPORTS = ("la_prefill", "la_prefill_workspace_size", "la_decode_step", "la_status_str",
+           "la_abi_version")
+
+
+class LinAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+        ("variant", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+        ("gate_dtype", ctypes.c_int32), ("eps", ctypes.c_float),
+        ("path", ctypes.c_int32), ("chunk", ctypes.c_int32), ("segments", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library (once). Raises FileNotFoundError when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path} is missing: build it with "
+                                f"`python -m gated_delta_rule_linear_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    dp = ctypes.POINTER(Desc)
+    lib.la_prefill.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.la_prefill.restype = ctypes.c_int
+    lib.la_prefill_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
+    lib.la_prefill_workspace_size.restype = ctypes.c_int
+    lib.la_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.la_decode_step.restype = ctypes.c_int
+    lib.la_status_str.argtypes = [ctypes.c_int]
+    lib.la_status_str.restype = ctypes.c_char_p
+    lib.la_abi_version.argtypes = []
+    lib.la_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().la_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != LA_OK:
+        raise LinAttnError(status, where)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return LA_F32
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream, device):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_desc(variant, B, H, N, dk, dv, io_dtype, gate_dtype=LA_F32, eps=1e-6, path="auto",
+              chunk=0, segments=0) -> Desc:
+    return Desc(B, H, N, dk, dv, VARIANTS[variant] if isinstance(variant, str) else int(variant),
+                io_dtype, gate_dtype, float(eps), PATHS[path] if isinstance(path, str) else path,
+                chunk, segments)
+
+
+def _require_contig(name, t):
+    if t is not None and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def prefill_workspace_bytes(desc: Desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().la_prefill_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
+           "la_prefill_workspace_size")
+    return int(n.value)
+
+
+def prefill(q, k, v, g=None, beta=None, *, variant: str, S0=None, z0=None, eps: float = 1e-6,
+            path: str = "auto", chunk: int = 0, segments: int = 0, o=None, S_final=None,
+            z_final=None, workspace=None, stream=None):
+    """Chunked prefill through ``la_prefill``.
+
+    q, k [B,H,N,dk], v [B,H,N,dv] (float32 or bfloat16, one dtype); g (GLA
+    [B,H,N,dk] / GDN alpha [B,H,N]) and beta (GDN [B,H,N]) float32 or bfloat16;
+    S0 [B,H,dk,dv] and z0 [B,H,dk] float32 or None. Outputs are allocated with
+    torch unless given. Returns (o, S_final, z_final or None).
+    """
+    import torch
+    lib = load()
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("S0", S0),
+                    ("z0", z0), ("o", o), ("S_final", S_final), ("z_final", z_final)):
+        _require_contig(name, t)
+    io = _dtype_code(q)
+    gate_t = g if g is not None else beta
+    gd = _dtype_code(gate_t) if gate_t is not None else LA_F32
+    desc = make_desc(variant, B, H, N, dk, dv, io, gd, eps, path, chunk, segments)
+    dev = q.device
+    if o is None:
+        o = torch.empty((B, H, N, dv), dtype=q.dtype, device=dev)
+    if S_final is None:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if z_final is None and desc.variant == LA_KATH:
+        z_final = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+    ws_bytes = prefill_workspace_bytes(desc)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.la_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                        _ptr(S0), _ptr(z0), _ptr(o), _ptr(S_final), _ptr(z_final),
+                        _ptr(workspace if ws_bytes else None), wsz, _stream_handle(stream, dev))
+    _check(rc, "la_prefill")
+    return o, S_final, z_final
+
+
+def decode_step(q, k, v, S, g=None, beta=None, *, variant: str, z=None, eps: float = 1e-6,
+                o=None, stream=None):
+    """One in-place decode step through ``la_decode_step``.
+
+    q, k [B,H,dk]; v [B,H,dv]; S [B,H,dk,dv] float32 (updated in place);
+    g (GLA [B,H,dk] / GDN alpha [B,H]); beta (GDN [B,H]); z [B,H,dk] (KATH,
+    updated in place). Returns o [B,H,dv].
+    """
+    import torch
+    lib = load()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("S", S),
+                    ("z", z), ("o", o)):
+        _require_contig(name, t)
+    io = _dtype_code(q)
+    gate_t = g if g is not None else beta
+    gd = _dtype_code(gate_t) if gate_t is not None else LA_F32
+    desc = make_desc(variant, B, H, 1, dk, dv, io, gd, eps)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    rc = lib.la_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                            _ptr(S), _ptr(z), _ptr(o), _stream_handle(stream, q.device))
+    _check(rc, "la_decode_step")
+    return o

@@ -1,0 +1,82 @@
+// Device helpers shared by the kernel translation units: storage-dtype loads and
+// stores, and small wavefront utilities. gfx950 only (64-wide wavefronts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace la {
+
+constexpr int kWave = 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming accesses that bypass cache retention (state read-modify-write)
+__device__ __forceinline__ float4 load_nt4(const float* p) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_nt4(float* p, float4 x) {
+    f32x4 v = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+
+// bf16 bit pattern -> fp32 (exact)
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(uint32_t(b) << 16);
+}
+
+// fp32 -> bf16 bit pattern, round to nearest, ties to even; NaN stays a quiet NaN
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+
+// Element i of an array stored as fp32 (bf16 == false) or bf16 bits.
+__device__ __forceinline__ float load_elem(const void* p, size_t i, bool bf16) {
+    return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i])
+                : static_cast<const float*>(p)[i];
+}
+
+__device__ __forceinline__ void store_elem(void* p, size_t i, float x, bool bf16) {
+    if (bf16)
+        static_cast<uint16_t*>(p)[i] = f32_to_bf16(x);
+    else
+        static_cast<float*>(p)[i] = x;
+}
+
+// Four consecutive elements starting at i (i a multiple of 4; 8- or 16-byte access).
+__device__ __forceinline__ float4 load4(const void* p, size_t i, bool bf16) {
+    if (bf16) {
+        const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+        return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                           __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+    }
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+}
+
+__device__ __forceinline__ void store4(void* p, size_t i, float4 x, bool bf16) {
+    if (bf16) {
+        uint2 w;
+        w.x = uint32_t(f32_to_bf16(x.x)) | (uint32_t(f32_to_bf16(x.y)) << 16);
+        w.y = uint32_t(f32_to_bf16(x.z)) | (uint32_t(f32_to_bf16(x.w)) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = w;
+    } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = x;
+    }
+}
+
+// ELU(x) + 1 (alpha = 1): x + 1 for x > 0, exp(x) otherwise. The feature map of
+// normalized linear attention; it keeps features positive.
+__device__ __forceinline__ float elu_plus_one(float x) { return x > 0.f ? x + 1.f : expf(x); }
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
+}  // namespace la

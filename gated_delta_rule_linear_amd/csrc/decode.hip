@@ -1,0 +1,215 @@
+// Decode: one token per (b, h) sequence, state updated in place.
+//
+// The step is pure state read-modify-write: the fp32 state (d_k x d_v, 64 KiB at
+// 128 x 128) is read once and written once, everything else is a few hundred
+// bytes. So the kernel is laid out for HBM streaming: one workgroup per state,
+// each thread owns RPT rows x 4 consecutive columns (16-byte accesses; a wave
+// covers whole contiguous rows), keeps them in registers across the reductions,
+// and writes them back once.
+//
+// Each variant needs a single reduction over the key dim of the OLD state,
+// because the post-update read can be expanded (columns of S never mix):
+//   GDN  p = S^T k, r = S^T q;  u = beta (v - alpha p);  S <- alpha S + k u^T;
+//        o = S_new^T q = alpha r + (k . q) u
+//   GLA  r = S^T (q * g);  S <- diag(g) S + k v^T;  o = r + (q . k) v
+//   KATH r = S^T phi(q);  S <- S + phi(k) v^T;  z <- z + phi(k);
+//        o = (r + (phi(q) . phi(k)) v) / (phi(q) . z_new + eps)
+// ("Linear / RNN 路线", sections 2.1 and 2.2; "线性注意力与 SSM", section GDN.)
+#include "common.hpp"
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+struct DecodeArgs {
+    const void *q, *k, *v, *g, *beta;
+    float *S, *z;
+    void* o;
+    float eps;
+    int io_bf16, gate_bf16;
+};
+
+template <int DK, int DV>
+struct DecodeShape {
+    static constexpr int NCG = DV / 4;                         // 4-column groups
+    static constexpr int RG_ALL = 256 / NCG;
+    static constexpr int RG = RG_ALL < DK ? RG_ALL : DK;       // row groups
+    static constexpr int RPT = DK / RG;                        // rows per thread
+    static constexpr int NT = NCG * RG;                        // threads per workgroup
+    static_assert(NT > 0 && NT <= 256 && RPT * RG == DK, "decode tiling");
+};
+
+constexpr int decode_threads(int dk, int dv) {
+    return (dv / 4) * ((256 / (dv / 4)) < dk ? (256 / (dv / 4)) : dk);
+}
+
+template <int VAR, int DK, int DV>
+__global__ __launch_bounds__(decode_threads(DK, DV)) void decode_kernel(DecodeArgs a) {
+    using Sh = DecodeShape<DK, DV>;
+    constexpr int NCG = Sh::NCG, RG = Sh::RG, RPT = Sh::RPT, NT = Sh::NT;
+    const int tid = threadIdx.x;
+    const int cg = tid % NCG, rg = tid / NCG;
+    const size_t seq = blockIdx.x;
+    float* S = a.S + seq * (size_t(DK) * DV);
+
+    __shared__ float sq[DK], sk[DK], sw[DK];  // sw: q*g (GLA)
+    __shared__ float sv[DV];
+    __shared__ float4 red[2][RG][NCG];
+    __shared__ float scal[4];
+
+    // Issue the state loads first: they are the whole cost of the step.
+    float4 s[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int i = rg + RG * r;
+        s[r] = load_nt4(S + size_t(i) * DV + cg * 4);
+    }
+
+    const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
+    for (int i = tid; i < DK; i += NT) {
+        float qi = load_elem(a.q, seq * DK + i, iob);
+        float ki = load_elem(a.k, seq * DK + i, iob);
+        if (VAR == LA_KATH) {
+            qi = elu_plus_one(qi);
+            ki = elu_plus_one(ki);
+        }
+        sq[i] = qi;
+        sk[i] = ki;
+        if (VAR == LA_GLA) sw[i] = load_elem(a.g, seq * DK + i, gb);
+    }
+    for (int j = tid; j < DV; j += NT) sv[j] = load_elem(a.v, seq * DV + j, iob);
+    __syncthreads();
+
+    // wave 0: the scalar dot products
+    if (tid < kWave) {
+        float qk = 0.f, qz = 0.f;
+        for (int i = tid; i < DK; i += kWave) {
+            qk += sq[i] * sk[i];
+            if (VAR == LA_KATH) qz += sq[i] * (a.z[seq * DK + i] + sk[i]);
+        }
+        qk = wave_sum(qk);
+        if (VAR == LA_KATH) qz = wave_sum(qz);
+        if (tid == 0) {
+            scal[0] = qk;
+            scal[1] = qz + a.eps;
+            if (VAR == LA_GDN) {
+                scal[2] = load_elem(a.g, seq, gb);
+                scal[3] = load_elem(a.beta, seq, gb);
+            }
+        }
+    }
+
+    // partial reductions of the old state over this thread's rows
+    float4 pr = make_float4(0.f, 0.f, 0.f, 0.f), rr = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int i = rg + RG * r;
+        float wq = sq[i];
+        if (VAR == LA_GLA) wq *= sw[i];
+        rr.x += s[r].x * wq; rr.y += s[r].y * wq; rr.z += s[r].z * wq; rr.w += s[r].w * wq;
+        if (VAR == LA_GDN) {
+            const float ki = sk[i];
+            pr.x += s[r].x * ki; pr.y += s[r].y * ki; pr.z += s[r].z * ki; pr.w += s[r].w * ki;
+        }
+    }
+    red[0][rg][cg] = rr;
+    if (VAR == LA_GDN) red[1][rg][cg] = pr;
+    __syncthreads();
+    float4 R = make_float4(0.f, 0.f, 0.f, 0.f), P = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+    for (int x = 0; x < RG; ++x) {
+        const float4 t = red[0][x][cg];
+        R.x += t.x; R.y += t.y; R.z += t.z; R.w += t.w;
+        if (VAR == LA_GDN) {
+            const float4 t2 = red[1][x][cg];
+            P.x += t2.x; P.y += t2.y; P.z += t2.z; P.w += t2.w;
+        }
+    }
+    const float qk = scal[0];
+    const float4 v4 = make_float4(sv[cg * 4], sv[cg * 4 + 1], sv[cg * 4 + 2], sv[cg * 4 + 3]);
+    float4 o4;
+    if (VAR == LA_GDN) {
+        const float al = scal[2], be = scal[3];
+        float4 u;
+        u.x = be * (v4.x - al * P.x); u.y = be * (v4.y - al * P.y);
+        u.z = be * (v4.z - al * P.z); u.w = be * (v4.w - al * P.w);
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int i = rg + RG * r;
+            const float ki = sk[i];
+            float4 n;
+            n.x = al * s[r].x + ki * u.x; n.y = al * s[r].y + ki * u.y;
+            n.z = al * s[r].z + ki * u.z; n.w = al * s[r].w + ki * u.w;
+            store_nt4(S + size_t(i) * DV + cg * 4, n);
+        }
+        o4.x = al * R.x + qk * u.x; o4.y = al * R.y + qk * u.y;
+        o4.z = al * R.z + qk * u.z; o4.w = al * R.w + qk * u.w;
+    } else {
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int i = rg + RG * r;
+            const float ki = sk[i];
+            const float gi = VAR == LA_GLA ? sw[i] : 1.f;
+            float4 n;
+            n.x = gi * s[r].x + ki * v4.x; n.y = gi * s[r].y + ki * v4.y;
+            n.z = gi * s[r].z + ki * v4.z; n.w = gi * s[r].w + ki * v4.w;
+            store_nt4(S + size_t(i) * DV + cg * 4, n);
+        }
+        o4.x = R.x + qk * v4.x; o4.y = R.y + qk * v4.y;
+        o4.z = R.z + qk * v4.z; o4.w = R.w + qk * v4.w;
+        if (VAR == LA_KATH) {
+            const float inv = 1.f / scal[1];
+            o4.x *= inv; o4.y *= inv; o4.z *= inv; o4.w *= inv;
+        }
+    }
+    if (VAR == LA_KATH) {
+        // z is read by wave 0 above; every thread is past the reduction barrier,
+        // so the old values have been consumed before any write below.
+        for (int i = tid; i < DK; i += NT) a.z[seq * DK + i] += sk[i];
+    }
+    if (rg == 0) store4(a.o, seq * DV + size_t(cg) * 4, o4, iob);
+}
+
+template <int VAR, int DK, int DV>
+hipError_t launch_one(const Problem& p, const DecodeArgs& a) {
+    const unsigned nseq = unsigned(size_t(p.B) * size_t(p.H));
+    decode_kernel<VAR, DK, DV><<<dim3(nseq), dim3(DecodeShape<DK, DV>::NT), 0, p.stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int VAR, int DK>
+hipError_t dispatch_dv(const Problem& p, const DecodeArgs& a) {
+    switch (p.dv) {
+        case 16: return launch_one<VAR, DK, 16>(p, a);
+        case 32: return launch_one<VAR, DK, 32>(p, a);
+        case 64: return launch_one<VAR, DK, 64>(p, a);
+        case 128: return launch_one<VAR, DK, 128>(p, a);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int VAR>
+hipError_t dispatch_dk(const Problem& p, const DecodeArgs& a) {
+    switch (p.dk) {
+        case 16: return dispatch_dv<VAR, 16>(p, a);
+        case 32: return dispatch_dv<VAR, 32>(p, a);
+        case 64: return dispatch_dv<VAR, 64>(p, a);
+        case 128: return dispatch_dv<VAR, 128>(p, a);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const Problem& p) {
+    if (size_t(p.B) * size_t(p.H) > 0x7fffffffull) return hipErrorInvalidValue;
+    DecodeArgs a{p.q, p.k, p.v, p.g, p.beta, p.S, p.z, p.o, p.eps, p.io_bf16, p.gate_bf16};
+    switch (p.variant) {
+        case LA_KATH: return dispatch_dk<LA_KATH>(p, a);
+        case LA_GLA: return dispatch_dk<LA_GLA>(p, a);
+        case LA_GDN: return dispatch_dk<LA_GDN>(p, a);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace la

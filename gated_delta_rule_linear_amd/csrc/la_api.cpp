@@ -1,0 +1,268 @@
+// C-ABI entry points: argument validation, planning (path, chunk, segments,
+// workspace) and dispatch to the kernel launchers. All validation happens
+// before the first HIP call, so an invalid call enqueues nothing and touches
+// no output.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "la_internal.h"
+
+namespace {
+
+using la::Problem;
+
+constexpr uint64_t kMaxElems = uint64_t(1) << 46;  // per buffer; keeps every size in 64 bits
+
+bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// a * b, or 0 on overflow past kMaxElems
+uint64_t mul(uint64_t a, uint64_t b) {
+    if (a == 0 || b == 0) return 0;
+    if (a > kMaxElems / b) return UINT64_MAX;
+    return a * b;
+}
+
+struct Range {
+    uintptr_t lo = 0, hi = 0;  // [lo, hi)
+    bool empty() const { return hi <= lo; }
+};
+
+Range range(const void* p, uint64_t bytes) {
+    Range r;
+    if (p && bytes && bytes != UINT64_MAX) {
+        r.lo = reinterpret_cast<uintptr_t>(p);
+        r.hi = r.lo + bytes;
+    }
+    return r;
+}
+
+bool overlap(Range a, Range b) { return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Sizes {
+    uint64_t q, k, v, o, g, beta, S, z;
+};
+
+// Byte sizes of every buffer for this descriptor (decode: N = 1).
+Sizes sizes_of(const la_desc& d) {
+    Sizes s{};
+    const uint64_t isz = d.io_dtype == LA_BF16 ? 2 : 4, gsz = d.gate_dtype == LA_BF16 ? 2 : 4;
+    const uint64_t tok = mul(mul(uint64_t(d.B), uint64_t(d.H)), uint64_t(d.N));
+    const uint64_t seq = mul(uint64_t(d.B), uint64_t(d.H));
+    s.q = s.k = mul(mul(tok, d.dk), isz);
+    s.v = s.o = mul(mul(tok, d.dv), isz);
+    s.g = d.variant == LA_GLA ? mul(mul(tok, d.dk), gsz) : d.variant == LA_GDN ? mul(tok, gsz) : 0;
+    s.beta = d.variant == LA_GDN ? mul(tok, gsz) : 0;
+    s.S = mul(mul(mul(seq, d.dk), d.dv), 4);
+    s.z = d.variant == LA_KATH ? mul(mul(seq, d.dk), 4) : 0;
+    return s;
+}
+
+// Descriptor checks shared by prefill, decode and the workspace query.
+int check_desc(const la_desc* d, bool decode) {
+    if (!d) return LA_ERR_INVALID;
+    if (d->variant < LA_KATH || d->variant > LA_GDN) return LA_ERR_INVALID;
+    if (d->io_dtype != LA_F32 && d->io_dtype != LA_BF16) return LA_ERR_INVALID;
+    if (d->variant != LA_KATH && d->gate_dtype != LA_F32 && d->gate_dtype != LA_BF16)
+        return LA_ERR_INVALID;
+    if (d->B < 0 || d->H < 0 || d->N < 0) return LA_ERR_INVALID;
+    if (decode && d->N != 1) return LA_ERR_INVALID;
+    if (d->variant == LA_KATH && !(std::isfinite(d->eps) && d->eps >= 0.f)) return LA_ERR_INVALID;
+    if (d->path < LA_PATH_AUTO || d->path > LA_PATH_MFMA) return LA_ERR_INVALID;
+    if (d->chunk < 0 || d->segments < 0) return LA_ERR_INVALID;
+    if (!supported_dim(d->dk) || !supported_dim(d->dv)) return LA_ERR_UNSUPPORTED;
+    const Sizes s = sizes_of(*d);
+    if (s.q == UINT64_MAX || s.v == UINT64_MAX || s.g == UINT64_MAX || s.S == UINT64_MAX ||
+        s.z == UINT64_MAX)
+        return LA_ERR_INVALID;
+    return LA_OK;
+}
+
+// Resolve path, chunk and segments for a prefill descriptor.
+int plan_prefill(const la_desc& d, Problem& p) {
+    p.B = d.B; p.H = d.H; p.N = d.N; p.dk = d.dk; p.dv = d.dv;
+    p.variant = d.variant;
+    p.io_bf16 = d.io_dtype == LA_BF16;
+    p.gate_bf16 = d.gate_dtype == LA_BF16;
+    p.eps = d.eps;
+    const bool mfma_ok = d.variant == LA_GDN
+                             ? la::gdn_mfma_supported(d.dk, d.dv, p.io_bf16)
+                             : la::diag_mfma_supported(d.variant, d.dk, d.dv, p.io_bf16);
+    int path = d.path;
+    if (path == LA_PATH_AUTO) path = mfma_ok ? LA_PATH_MFMA : LA_PATH_VALU;
+    if (path == LA_PATH_MFMA && !mfma_ok) return LA_ERR_UNSUPPORTED;
+    p.path = path;
+    p.chunk = path == LA_PATH_MFMA ? la::kMfmaChunk : la::kValuChunk;
+    if (d.chunk != 0 && d.chunk != p.chunk) return LA_ERR_UNSUPPORTED;
+    p.segments = 1;
+    if (path == LA_PATH_MFMA && d.variant != LA_GDN && d.N > 0) {
+        const int nchunks = (d.N + p.chunk - 1) / p.chunk;
+        int segs = d.segments > 0 ? d.segments : la::diag_mfma_auto_segments(p);
+        if (segs > nchunks) segs = nchunks;
+        if (segs < 1) segs = 1;
+        p.segments = segs;
+    }
+    return LA_OK;
+}
+
+size_t workspace_for(const Problem& p) {
+    if (p.N == 0 || p.B == 0 || p.H == 0) return 0;
+    if (p.path == LA_PATH_MFMA && p.variant != LA_GDN) return la::diag_mfma_workspace_bytes(p);
+    return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int la_abi_version(void) { return LA_ABI_VERSION; }
+
+const char* la_status_str(int status) {
+    switch (status) {
+        case LA_OK: return "ok";
+        case LA_ERR_INVALID: return "invalid argument";
+        case LA_ERR_UNSUPPORTED: return "unsupported shape, dtype, path or chunk size";
+        case LA_ERR_HIP: return "HIP kernel launch failed";
+        case LA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        default: return "unknown status";
+    }
+}
+
+int la_prefill_workspace_size(const la_desc* d, size_t* bytes) {
+    int rc = check_desc(d, false);
+    if (rc != LA_OK) return rc;
+    if (!bytes) return LA_ERR_INVALID;
+    Problem p;
+    rc = plan_prefill(*d, p);
+    if (rc != LA_OK) return rc;
+    *bytes = workspace_for(p);
+    return LA_OK;
+}
+
+int la_prefill(const la_desc* d, const void* q, const void* k, const void* v, const void* g,
+               const void* beta, const float* S0, const float* z0, void* o, float* S_final,
+               float* z_final, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_desc(d, false);
+    if (rc != LA_OK) return rc;
+    Problem p;
+    rc = plan_prefill(*d, p);
+    if (rc != LA_OK) return rc;
+    const bool kath = d->variant == LA_KATH, gla = d->variant == LA_GLA,
+               gdn = d->variant == LA_GDN;
+    const bool empty_seq = (uint64_t(d->B) * uint64_t(d->H)) == 0;
+    const bool tokens = !empty_seq && d->N > 0;
+    // presence rules
+    if (kath && (g || beta)) return LA_ERR_INVALID;
+    if (gla && beta) return LA_ERR_INVALID;
+    if (!kath && (z0 || z_final)) return LA_ERR_INVALID;
+    if (!empty_seq) {
+        if (!S_final) return LA_ERR_INVALID;
+        if (kath && !z_final) return LA_ERR_INVALID;
+    }
+    if (tokens) {
+        if (!q || !k || !v || !o) return LA_ERR_INVALID;
+        if ((gla || gdn) && !g) return LA_ERR_INVALID;
+        if (gdn && !beta) return LA_ERR_INVALID;
+    }
+    // alignment (16 bytes for every array: kernels use 128-bit accesses)
+    const void* all[] = {q, k, v, g, beta, S0, z0, o, S_final, z_final};
+    for (const void* ptr : all)
+        if (ptr && !aligned(ptr, 16)) return LA_ERR_INVALID;
+    // aliasing: outputs overlap nothing, except S_final == S0 and z_final == z0 exactly
+    const Sizes s = sizes_of(*d);
+    const Range rq = range(q, tokens ? s.q : 0), rk = range(k, tokens ? s.k : 0),
+                rv = range(v, tokens ? s.v : 0), rg = range(g, tokens ? s.g : 0),
+                rb = range(beta, tokens ? s.beta : 0), rS0 = range(S0, s.S), rz0 = range(z0, s.z),
+                ro = range(o, tokens ? s.o : 0), rS = range(S_final, s.S),
+                rz = range(z_final, s.z);
+    const Range inputs[] = {rq, rk, rv, rg, rb, rS0, rz0};
+    for (const Range& in : inputs) {
+        if (overlap(ro, in)) return LA_ERR_INVALID;
+    }
+    if (overlap(ro, rS) || overlap(ro, rz) || overlap(rS, rz)) return LA_ERR_INVALID;
+    const Range nonstate_inputs[] = {rq, rk, rv, rg, rb};
+    for (const Range& in : nonstate_inputs) {
+        if (overlap(rS, in) || overlap(rz, in)) return LA_ERR_INVALID;
+    }
+    if (overlap(rS, rS0) && S_final != S0) return LA_ERR_INVALID;
+    if (overlap(rS, rz0) || overlap(rz, rS0)) return LA_ERR_INVALID;
+    if (overlap(rz, rz0) && z_final != z0) return LA_ERR_INVALID;
+    // workspace
+    const size_t need = workspace_for(p);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+            return LA_ERR_WORKSPACE;
+        const Range rw = range(workspace, need);
+        const Range every[] = {rq, rk, rv, rg, rb, rS0, rz0, ro, rS, rz};
+        for (const Range& x : every)
+            if (overlap(rw, x)) return LA_ERR_INVALID;
+    }
+    if (empty_seq) return LA_OK;
+
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.S0 = S0; p.z0 = z0; p.o = o; p.S = S_final; p.z = z_final;
+    p.ws = workspace; p.ws_bytes = workspace_bytes;
+    p.stream = static_cast<hipStream_t>(stream);
+
+    (void)hipGetLastError();  // clear a stale error so the check below sees this call's
+    hipError_t err;
+    if (p.N == 0)
+        err = la::launch_state_init(p);
+    else if (p.path == LA_PATH_MFMA)
+        err = gdn ? la::launch_prefill_gdn_mfma(p) : la::launch_prefill_diag_mfma(p);
+    else
+        err = la::launch_prefill_valu(p);
+    if (err == hipSuccess) err = hipGetLastError();
+    return err == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+int la_decode_step(const la_desc* d, const void* q, const void* k, const void* v, const void* g,
+                   const void* beta, float* S, float* z, void* o, void* stream) {
+    int rc = check_desc(d, true);
+    if (rc != LA_OK) return rc;
+    const bool kath = d->variant == LA_KATH, gla = d->variant == LA_GLA,
+               gdn = d->variant == LA_GDN;
+    if (kath && (g || beta)) return LA_ERR_INVALID;
+    if (gla && beta) return LA_ERR_INVALID;
+    if (!kath && z) return LA_ERR_INVALID;
+    const bool empty_seq = (uint64_t(d->B) * uint64_t(d->H)) == 0;
+    if (!empty_seq) {
+        if (!q || !k || !v || !o || !S) return LA_ERR_INVALID;
+        if ((gla || gdn) && !g) return LA_ERR_INVALID;
+        if (gdn && !beta) return LA_ERR_INVALID;
+        if (kath && !z) return LA_ERR_INVALID;
+    }
+    const void* all[] = {q, k, v, g, beta, S, z, o};
+    for (const void* ptr : all)
+        if (ptr && !aligned(ptr, 16)) return LA_ERR_INVALID;
+    const Sizes s = sizes_of(*d);
+    const Range rq = range(q, s.q), rk = range(k, s.k), rv = range(v, s.v), rg = range(g, s.g),
+                rb = range(beta, s.beta), rS = range(S, s.S), rz = range(z, s.z),
+                ro = range(o, s.o);
+    const Range others[] = {rq, rk, rv, rg, rb, rS, rz};
+    for (const Range& x : others)
+        if (overlap(ro, x)) return LA_ERR_INVALID;
+    const Range tok_inputs[] = {rq, rk, rv, rg, rb};
+    for (const Range& x : tok_inputs)
+        if (overlap(rS, x) || overlap(rz, x)) return LA_ERR_INVALID;
+    if (overlap(rS, rz)) return LA_ERR_INVALID;
+    if (empty_seq) return LA_OK;
+
+    Problem p;
+    p.B = d->B; p.H = d->H; p.N = 1; p.dk = d->dk; p.dv = d->dv;
+    p.variant = d->variant;
+    p.io_bf16 = d->io_dtype == LA_BF16;
+    p.gate_bf16 = d->gate_dtype == LA_BF16;
+    p.eps = d->eps;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.S = S; p.z = z; p.o = o;
+    p.stream = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    hipError_t err = la::launch_decode(p);
+    if (err == hipSuccess) err = hipGetLastError();
+    return err == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Internal interface between the C-ABI layer (la_api.cpp) and the kernel
+// translation units. Nothing here is exported from the shared library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "linattn.h"
+
+namespace la {
+
+// A validated, planned call. Pointers are device pointers.
+struct Problem {
+    int B = 0, H = 0, N = 0, dk = 0, dv = 0;
+    int variant = 0;
+    bool io_bf16 = false, gate_bf16 = false;
+    float eps = 0.f;
+    int path = LA_PATH_VALU;  // resolved: VALU or MFMA
+    int chunk = 16;           // resolved chunk size
+    int segments = 1;         // resolved segment count (KATH / GLA MFMA path)
+    const void *q = nullptr, *k = nullptr, *v = nullptr, *g = nullptr, *beta = nullptr;
+    const float *S0 = nullptr, *z0 = nullptr;
+    void* o = nullptr;
+    float *S = nullptr, *z = nullptr;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    hipStream_t stream = nullptr;
+};
+
+constexpr int kValuChunk = 16;
+constexpr int kMfmaChunk = 64;
+
+// decode.hip
+hipError_t launch_decode(const Problem& p);
+// prefill_valu.hip
+hipError_t launch_prefill_valu(const Problem& p);
+// state_init.hip: S_final <- S0 (or 0), z_final <- z0 (or 0), for N = 0
+hipError_t launch_state_init(const Problem& p);
+// prefill_diag_mfma.hip (KATH, GLA)
+bool diag_mfma_supported(int variant, int dk, int dv, bool io_bf16);
+size_t diag_mfma_workspace_bytes(const Problem& p);
+int diag_mfma_auto_segments(const Problem& p);
+hipError_t launch_prefill_diag_mfma(const Problem& p);
+// prefill_gdn_mfma.hip (GDN)
+bool gdn_mfma_supported(int dk, int dv, bool io_bf16);
+hipError_t launch_prefill_gdn_mfma(const Problem& p);
+
+}  // namespace la

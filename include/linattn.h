@@ -1,0 +1,146 @@
+/*
+ * linattn.h -- C ABI of the causal linear-attention state recurrence on MI355X (gfx950).
+ *
+ * The library computes, for every (b, h) sequence independently, the recurrence
+ * over a key-major matrix state S in R^{d_k x d_v} (row i belongs to key dim i):
+ *
+ *   LA_KATH  normalized Katharopoulos linear attention ("Linear / RNN 路线",
+ *            section 2.1; "线性注意力与 SSM", section 02; "状态空间与线性注意力",
+ *            section 线性注意力):
+ *              phi(x) = ELU(x) + 1 = x + 1 (x > 0), exp(x) (x <= 0), on q and k only
+ *              S_t = S_{t-1} + phi(k_t) v_t^T,   z_t = z_{t-1} + phi(k_t)
+ *              o_t = phi(q_t)^T S_t / (phi(q_t)^T z_t + eps)
+ *   LA_GLA   gated linear attention with a per-key-dim forget gate ("Linear / RNN 路线",
+ *            section 2.2): S_t = diag(g_t) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t
+ *   LA_GDN   gated delta rule ("线性注意力与 SSM", section GDN), stored key-major (the
+ *            transpose of the page's value-major form, identical since I - b k k^T is
+ *            symmetric): S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T, that is
+ *              u_t = b_t (v_t - a_t S_{t-1}^T k_t),  S_t = a_t S_{t-1} + k_t u_t^T,
+ *              o_t = S_t^T q_t
+ *
+ * Every variant reads the state after the token's update. Prefill runs the
+ * recurrence over N tokens with the chunkwise-parallel method (quadratic, causally
+ * masked work inside a chunk, the state carried between chunks); decode applies one
+ * token in place. Chunk size and tiling are internal and do not change the result
+ * beyond rounding.
+ *
+ * Layouts (all dense, row-major, no strides; "io" = io_dtype, "gate" = gate_dtype):
+ *   q, k     [B, H, N, d_k]  io        v, o  [B, H, N, d_v]  io
+ *   g        LA_GLA: [B, H, N, d_k] gate, values in (0, 1]
+ *            LA_GDN: alpha [B, H, N] gate, values in (0, 1]
+ *   beta     LA_GDN: [B, H, N] gate, values in [0, 1]
+ *   S0, S    [B, H, d_k, d_v] fp32 (key-major)
+ *   z0, z    [B, H, d_k] fp32 (LA_KATH only)
+ * For decode N = 1 and the token arrays are [B, H, d] (respectively [B, H]).
+ * The output o is rounded to nearest even from fp32 when io is bf16.
+ *
+ * Ownership and threading: the caller allocates every buffer in device memory and
+ * passes plain device pointers and a hipStream_t (NULL = the default stream). The
+ * library never allocates, frees or synchronizes; calls only enqueue work on the
+ * given stream and return. It keeps no mutable global state and is re-entrant.
+ *
+ * Errors: every entry point validates all arguments first. On any error it returns
+ * a nonzero status, enqueues nothing and touches no output. No exception crosses
+ * the ABI. LA_ERR_HIP means a kernel launch failed (hipGetLastError); work enqueued
+ * before the failing launch of the same call may have run.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_ABI_VERSION 1
+
+/* status codes */
+enum {
+    LA_OK = 0,
+    LA_ERR_INVALID = 1,      /* null required pointer, bad enum, negative size, misaligned
+                                pointer (16 bytes; 256 for the workspace), overlap of an
+                                output with any other buffer, gate passed / missing for
+                                the variant, N != 1 for decode */
+    LA_ERR_UNSUPPORTED = 2,  /* d_k or d_v not in {16, 32, 64, 128}, or a requested path /
+                                chunk size that this shape or dtype does not support */
+    LA_ERR_HIP = 3,          /* a kernel launch failed */
+    LA_ERR_WORKSPACE = 4     /* workspace missing or smaller than la_prefill_workspace_size */
+};
+
+/* variants */
+enum { LA_KATH = 0, LA_GLA = 1, LA_GDN = 2 };
+
+/* storage dtypes */
+enum { LA_F32 = 0, LA_BF16 = 1 };
+
+/* kernel path selection (semantics never depend on it) */
+enum {
+    LA_PATH_AUTO = 0, /* bf16 MFMA kernels where the shape allows, else the fp32 VALU kernels */
+    LA_PATH_VALU = 1, /* fp32 arithmetic on the vector ALUs (chunk 16) */
+    LA_PATH_MFMA = 2  /* bf16 matrix cores with fp32 accumulation and fp32 state (chunk 64);
+                         needs d_k = 128 and d_v in {64, 128} */
+};
+
+typedef struct la_desc {
+    int32_t B, H, N;      /* batch, heads, tokens per sequence (N = 1 for decode) */
+    int32_t dk, dv;       /* key and value dims, each in {16, 32, 64, 128} */
+    int32_t variant;      /* LA_KATH | LA_GLA | LA_GDN */
+    int32_t io_dtype;     /* LA_F32 | LA_BF16: q, k, v, o */
+    int32_t gate_dtype;   /* LA_F32 | LA_BF16: g / alpha, beta (ignored for LA_KATH) */
+    float eps;            /* LA_KATH denominator epsilon, finite and >= 0 */
+    int32_t path;         /* LA_PATH_* */
+    int32_t chunk;        /* 0 = the path's chunk size; otherwise it must equal it */
+    int32_t segments;     /* 0 = automatic. LA_KATH / LA_GLA on the MFMA path split each
+                             sequence into this many segments that run in parallel and
+                             are joined by a scan of their state summaries */
+} la_desc;
+
+/* Bytes of device workspace la_prefill needs for this descriptor (0 if none).
+ * Returns LA_OK and writes *bytes, or an error status for an invalid descriptor. */
+int la_prefill_workspace_size(const la_desc* d, size_t* bytes);
+
+/* Whole-sequence forward.
+ *   q, k, v, g, beta   inputs as laid out above; g and beta must be NULL when the
+ *                      variant does not take them.
+ *   S0, z0             initial state, or NULL for zeros; z0 must be NULL unless LA_KATH.
+ *   o                  output [B, H, N, d_v] io; must not overlap any other buffer.
+ *   S_final            final state [B, H, d_k, d_v] fp32, required. It may be the same
+ *                      pointer as S0 (in-place carry) but must not otherwise overlap.
+ *   z_final            final normalizer [B, H, d_k] fp32: required for LA_KATH (may equal
+ *                      z0), NULL otherwise.
+ *   workspace          device scratch of at least la_prefill_workspace_size bytes,
+ *                      256-byte aligned, owned by the caller, not read as input; NULL
+ *                      when the size is 0. Contents on return are unspecified.
+ *   stream             hipStream_t.
+ * N = 0 is accepted: o is untouched and S_final / z_final receive S0 / z0 (or zeros).
+ * B * H = 0 is accepted and does nothing. */
+int la_prefill(const la_desc* d, const void* q, const void* k, const void* v,
+               const void* g, const void* beta, const float* S0, const float* z0,
+               void* o, float* S_final, float* z_final,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* One decode step, in place: the per-token step of "Linear / RNN 路线", section 2.1,
+ * applied to the carried state; the decode carry of "线性注意力与 SSM", section 01, is
+ * the final recurrent state only, so the cost of a step does not depend on how many
+ * tokens came before.
+ *   d->N must be 1. q, k [B, H, d_k]; v [B, H, d_v]; g (GLA [B, H, d_k], GDN alpha
+ *   [B, H]); beta (GDN [B, H]); S [B, H, d_k, d_v] fp32 read and overwritten;
+ *   z [B, H, d_k] fp32 read and overwritten (LA_KATH, NULL otherwise);
+ *   o [B, H, d_v] io written. o must not overlap S, z or any input. */
+int la_decode_step(const la_desc* d, const void* q, const void* k, const void* v,
+                   const void* g, const void* beta, float* S, float* z, void* o,
+                   void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* la_status_str(int status);
+
+/* LA_ABI_VERSION of the built library. */
+int la_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

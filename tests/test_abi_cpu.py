@@ -1,0 +1,221 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and rejects
+invalid calls before touching any buffer (no GPU needed: validation precedes all HIP calls)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from gated_delta_rule_linear_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        from gated_delta_rule_linear_amd import build
+        build.build()
+    return bd.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(bd.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = os.popen(f"nm -D --defined-only {bd.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), f"{n} not exported"
+
+
+def test_version_and_status(lib):
+    hdr = open(HEADER).read()
+    ver = int(re.search(r"#define LA_ABI_VERSION (\d+)", hdr).group(1))
+    assert lib.la_abi_version() == ver
+    for code in range(5):
+        assert bd.status_str(code)
+    assert bd.status_str(99) == "unknown status"
+
+
+# fake, suitably aligned, non-overlapping "device" addresses: validation never dereferences
+BASE = 1 << 40
+GAP = 1 << 34
+
+
+def addr(i, off=0):
+    return ctypes.c_void_p(BASE + i * GAP + off)
+
+
+def call_prefill(lib, desc, q=None, k=None, v=None, g=None, beta=None, S0=None, z0=None,
+                 o=None, S=None, z=None, ws=None, ws_bytes=0):
+    return lib.la_prefill(ctypes.byref(desc) if desc is not None else None, q, k, v, g, beta,
+                          S0, z0, o, S, z, ws, ws_bytes, None)
+
+
+def good(variant="gla", **kw):
+    base = dict(variant=variant, B=2, H=3, N=40, dk=64, dv=32, io_dtype=bd.LA_BF16,
+                gate_dtype=bd.LA_BF16, eps=1e-6, path="valu")
+    base.update(kw)
+    return bd.make_desc(base.pop("variant"), base.pop("B"), base.pop("H"), base.pop("N"),
+                        base.pop("dk"), base.pop("dv"), base.pop("io_dtype"),
+                        base.pop("gate_dtype"), base.pop("eps"), base.pop("path"),
+                        base.pop("chunk", 0), base.pop("segments", 0))
+
+
+def ptrs(variant):
+    p = dict(q=addr(0), k=addr(1), v=addr(2), o=addr(7), S=addr(8))
+    if variant in ("gla", "gdn"):
+        p["g"] = addr(3)
+    if variant == "gdn":
+        p["beta"] = addr(4)
+    if variant == "kath":
+        p["z"] = addr(9)
+    return p
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_desc", bd.LA_ERR_INVALID),
+    ("bad_variant", bd.LA_ERR_INVALID),
+    ("bad_io_dtype", bd.LA_ERR_INVALID),
+    ("negative_N", bd.LA_ERR_INVALID),
+    ("nan_eps", bd.LA_ERR_INVALID),
+    ("bad_path", bd.LA_ERR_INVALID),
+    ("dk_48", bd.LA_ERR_UNSUPPORTED),
+    ("dv_256", bd.LA_ERR_UNSUPPORTED),
+    ("mfma_f32", bd.LA_ERR_UNSUPPORTED),
+    ("chunk_mismatch", bd.LA_ERR_UNSUPPORTED),
+    ("null_q", bd.LA_ERR_INVALID),
+    ("null_S_final", bd.LA_ERR_INVALID),
+    ("misaligned_v", bd.LA_ERR_INVALID),
+    ("o_overlaps_q", bd.LA_ERR_INVALID),
+    ("S_partial_overlap_S0", bd.LA_ERR_INVALID),
+    ("S_overlaps_k", bd.LA_ERR_INVALID),
+    ("gla_missing_gate", bd.LA_ERR_INVALID),
+    ("gla_with_beta", bd.LA_ERR_INVALID),
+    ("gdn_missing_beta", bd.LA_ERR_INVALID),
+    ("kath_with_gate", bd.LA_ERR_INVALID),
+    ("kath_missing_z", bd.LA_ERR_INVALID),
+    ("gla_with_z", bd.LA_ERR_INVALID),
+])
+def test_prefill_rejects(lib, case, expect):
+    variant = {"gdn_missing_beta": "gdn", "kath_with_gate": "kath", "kath_missing_z": "kath"}.get(
+        case, "gla")
+    d = good(variant)
+    p = ptrs(variant)
+    if case == "null_desc":
+        d = None
+    elif case == "bad_variant":
+        d.variant = 7
+    elif case == "bad_io_dtype":
+        d.io_dtype = 3
+    elif case == "negative_N":
+        d.N = -1
+    elif case == "nan_eps":
+        d = good("kath", eps=float("nan"))
+        p = ptrs("kath")
+    elif case == "bad_path":
+        d.path = 9
+    elif case == "dk_48":
+        d.dk = 48
+    elif case == "dv_256":
+        d.dv = 256
+    elif case == "mfma_f32":
+        d = good("gdn", io_dtype=bd.LA_F32, path="mfma")
+        p = ptrs("gdn")
+    elif case == "chunk_mismatch":
+        d.chunk = 48
+    elif case == "null_q":
+        p["q"] = None
+    elif case == "null_S_final":
+        p["S"] = None
+    elif case == "misaligned_v":
+        p["v"] = addr(2, 8)
+    elif case == "o_overlaps_q":
+        p["o"] = addr(0, 256)
+    elif case == "S_partial_overlap_S0":
+        p["S0"] = addr(8, 64)
+    elif case == "S_overlaps_k":
+        p["S"] = addr(1, 1024)
+    elif case == "gla_missing_gate":
+        p.pop("g")
+    elif case == "gla_with_beta":
+        p["beta"] = addr(4)
+    elif case == "gdn_missing_beta":
+        p.pop("beta")
+    elif case == "kath_with_gate":
+        p["g"] = addr(3)
+    elif case == "kath_missing_z":
+        p.pop("z")
+    elif case == "gla_with_z":
+        p["z"] = addr(9)
+    assert call_prefill(lib, d, **p) == expect
+
+
+def test_invalid_call_touches_nothing(lib):
+    """A rejected call must leave every output byte as it was (host buffers stand in)."""
+    d = good("gdn", B=1, H=1, N=8, dk=16, dv=16)
+    bufs = {n: np.full(4096, 7, np.uint8) for n in ("q", "k", "v", "g", "o", "S")}
+    p = {n: ctypes.c_void_p(b.ctypes.data) for n, b in bufs.items()}
+    # beta missing -> invalid before any access
+    assert call_prefill(lib, d, **p) == bd.LA_ERR_INVALID
+    for b in bufs.values():
+        assert np.all(b == 7)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("N_not_1", bd.LA_ERR_INVALID),
+    ("null_S", bd.LA_ERR_INVALID),
+    ("o_overlaps_S", bd.LA_ERR_INVALID),
+    ("kath_missing_z", bd.LA_ERR_INVALID),
+    ("gdn_missing_alpha", bd.LA_ERR_INVALID),
+    ("dk_24", bd.LA_ERR_UNSUPPORTED),
+])
+def test_decode_rejects(lib, case, expect):
+    variant = {"kath_missing_z": "kath"}.get(case, "gdn")
+    d = good(variant, N=1)
+    p = dict(q=addr(0), k=addr(1), v=addr(2), g=addr(3), beta=addr(4), S=addr(8), z=None,
+             o=addr(7))
+    if variant == "kath":
+        p["g"] = p["beta"] = None
+        p["z"] = addr(9)
+    if case == "N_not_1":
+        d.N = 2
+    elif case == "null_S":
+        p["S"] = None
+    elif case == "o_overlaps_S":
+        p["o"] = addr(8, 512)
+    elif case == "kath_missing_z":
+        p["z"] = None
+    elif case == "gdn_missing_alpha":
+        p["g"] = None
+    elif case == "dk_24":
+        d.dk = 24
+    rc = lib.la_decode_step(ctypes.byref(d), p["q"], p["k"], p["v"], p["g"], p["beta"], p["S"],
+                            p["z"], p["o"], None)
+    assert rc == expect
+
+
+def test_workspace_query(lib):
+    assert bd.prefill_workspace_bytes(good("gla")) == 0      # VALU path needs none
+    n = ctypes.c_size_t(123)
+    assert lib.la_prefill_workspace_size(None, ctypes.byref(n)) == bd.LA_ERR_INVALID
+    d = good("gla", dk=48)
+    assert lib.la_prefill_workspace_size(ctypes.byref(d), ctypes.byref(n)) == \
+        bd.LA_ERR_UNSUPPORTED
+
+
+def test_empty_batch_is_noop(lib):
+    d = good("gla", B=0)
+    assert call_prefill(lib, d) == bd.LA_OK
+    d = good("gdn", B=2, H=0, N=1)
+    assert lib.la_decode_step(ctypes.byref(d), None, None, None, None, None, None, None, None,
+                              None) == bd.LA_OK
