@@ -41,6 +41,19 @@ bool overlap(Range a, Range b) { return !a.empty() && !b.empty() && a.lo < b.hi 
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+bool check_alignment(const la_desc& d, const void* q, const void* k, const void* v,
+                     const void* g, const void* beta, const void* S0, const void* z0,
+                     const void* o, const void* S, const void* z) {
+    const void* vec[] = {q, k, v, S0, z0, o, S, z};
+    for (const void* ptr : vec)
+        if (ptr && !aligned(ptr, 16)) return false;
+    const uintptr_t gsz = d.gate_dtype == LA_BF16 ? 2 : 4;
+    if (d.variant == LA_GLA && g && !aligned(g, 16)) return false;
+    if (d.variant == LA_GDN && ((g && !aligned(g, gsz)) || (beta && !aligned(beta, gsz))))
+        return false;
+    return true;
+}
+
 struct Sizes {
     uint64_t q, k, v, o, g, beta, S, z;
 };
@@ -102,7 +115,9 @@ int plan_prefill(const la_desc& d, Problem& p) {
         int segs = d.segments > 0 ? d.segments : la::diag_mfma_auto_segments(p);
         if (segs > nchunks) segs = nchunks;
         if (segs < 1) segs = 1;
-        p.segments = segs;
+        // equal segments of cps chunks; drop segments that would be empty
+        const int cps = (nchunks + segs - 1) / segs;
+        p.segments = (nchunks + cps - 1) / cps;
     }
     return LA_OK;
 }
@@ -166,10 +181,10 @@ int la_prefill(const la_desc* d, const void* q, const void* k, const void* v, co
         if ((gla || gdn) && !g) return LA_ERR_INVALID;
         if (gdn && !beta) return LA_ERR_INVALID;
     }
-    // alignment (16 bytes for every array: kernels use 128-bit accesses)
-    const void* all[] = {q, k, v, g, beta, S0, z0, o, S_final, z_final};
-    for (const void* ptr : all)
-        if (ptr && !aligned(ptr, 16)) return LA_ERR_INVALID;
+    // alignment: 16 bytes for the arrays read or written with 128-bit accesses; the
+    // per-token scalar gates of GDN (alpha, beta) only need element alignment
+    if (!check_alignment(*d, q, k, v, g, beta, S0, z0, o, S_final, z_final))
+        return LA_ERR_INVALID;
     // aliasing: outputs overlap nothing, except S_final == S0 and z_final == z0 exactly
     const Sizes s = sizes_of(*d);
     const Range rq = range(q, tokens ? s.q : 0), rk = range(k, tokens ? s.k : 0),
@@ -234,9 +249,7 @@ int la_decode_step(const la_desc* d, const void* q, const void* k, const void* v
         if (gdn && !beta) return LA_ERR_INVALID;
         if (kath && !z) return LA_ERR_INVALID;
     }
-    const void* all[] = {q, k, v, g, beta, S, z, o};
-    for (const void* ptr : all)
-        if (ptr && !aligned(ptr, 16)) return LA_ERR_INVALID;
+    if (!check_alignment(*d, q, k, v, g, beta, nullptr, nullptr, o, S, z)) return LA_ERR_INVALID;
     const Sizes s = sizes_of(*d);
     const Range rq = range(q, s.q), rk = range(k, s.k), rv = range(v, s.v), rg = range(g, s.g),
                 rb = range(beta, s.beta), rS = range(S, s.S), rz = range(z, s.z),

@@ -1,0 +1,105 @@
+// Matrix-core helpers for gfx950: v_mfma_f32_16x16x32_bf16 fragments read from LDS.
+//
+// Lane layout of the 16x16x32 bf16 MFMA (64 lanes, g = lane / 16, j = lane % 16):
+//   A (16 x 32): lane holds row j, k = 8g .. 8g+7
+//   B (32 x 16): lane holds col j, k = 8g .. 8g+7
+//   D (16 x 16): lane holds col j, rows 4g .. 4g+3 (f32x4)
+// A fragment whose K index runs along the rows of a row-major LDS tile (for example
+// the token index of a [token][feature] tile) is fetched with the LDS transpose read
+// ds_read_b64_tr_b16: within each 16-lane group, lane L addresses row L/4, columns
+// 4*(L%4) .. +3 of a 4-row block, and lane j receives column j of those 4 rows.
+#pragma once
+
+#include "common.hpp"
+
+namespace la {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+// Fragment from a row-major bf16 tile whose rows are the M (or N) index and whose
+// columns are K: rows r0 .. r0+15, K = k0 .. k0+31. Needs pitch % 8 == 0.
+__device__ __forceinline__ bf16x8_t frag_kc(const uint16_t* t, int pitch, int r0, int k0,
+                                            int lane) {
+    return *reinterpret_cast<const bf16x8_t*>(t + (r0 + (lane & 15)) * pitch + k0 +
+                                              (lane >> 4) * 8);
+}
+
+// Fragment from a row-major bf16 tile whose rows are K and whose columns are the M (or
+// N) index (transpose read): M/N = n0 .. n0+15, K = k0 .. k0+31. Needs pitch % 4 == 0.
+__device__ __forceinline__ bf16x8_t frag_kr(const uint16_t* t, int pitch, int k0, int n0,
+                                            int lane) {
+    const int g = lane >> 4, L = lane & 15;
+    const uint16_t* p = t + (k0 + g * 8 + (L >> 2)) * pitch + n0 + (L & 3) * 4;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 4 * pitch));
+    const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
+}
+
+// Store a D tile (rows m0.., cols n0..) transposed into a bf16 tile t[col][row]
+// (8-byte write per lane: t[n0 + j][m0 + 4g .. +3]). Needs pitch % 4 == 0.
+__device__ __forceinline__ void store_dT(uint16_t* t, int pitch, int m0, int n0, f32x4_t d,
+                                         int lane) {
+    uint2 w;
+    w.x = pack_bf16x2(d[0], d[1]);
+    w.y = pack_bf16x2(d[2], d[3]);
+    *reinterpret_cast<uint2*>(t + (n0 + (lane & 15)) * pitch + m0 + (lane >> 4) * 4) = w;
+}
+
+// Load 8 consecutive bf16 (16 bytes) from global memory as raw bits.
+__device__ __forceinline__ uint4 ld_g16(const uint16_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ void unpack8(uint4 w, float (&f)[8]) {
+    f[0] = __uint_as_float(w.x << 16); f[1] = __uint_as_float(w.x & 0xffff0000u);
+    f[2] = __uint_as_float(w.y << 16); f[3] = __uint_as_float(w.y & 0xffff0000u);
+    f[4] = __uint_as_float(w.z << 16); f[5] = __uint_as_float(w.z & 0xffff0000u);
+    f[6] = __uint_as_float(w.w << 16); f[7] = __uint_as_float(w.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+    uint4 w;
+    w.x = pack_bf16x2(f[0], f[1]);
+    w.y = pack_bf16x2(f[2], f[3]);
+    w.z = pack_bf16x2(f[4], f[5]);
+    w.w = pack_bf16x2(f[6], f[7]);
+    return w;
+}
+
+// Workgroup id -> (sequence, tile) with the tiles of one sequence on one XCD.
+// Workgroups are dispatched round-robin over the 8 XCDs (id % 8), each with its own
+// L2, so tiles that re-read the same q/k rows are placed at ids = xcd + 8 * slot.
+struct XcdMap {
+    int seq, tile;
+    bool valid;
+};
+__device__ __forceinline__ XcdMap xcd_map(int bid, int ntiles, int nseq) {
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int tile = slot % ntiles, group = slot / ntiles;
+    XcdMap m;
+    m.seq = group * 8 + xcd;
+    m.tile = tile;
+    m.valid = m.seq < nseq;
+    return m;
+}
+__host__ __device__ constexpr int xcd_grid(int ntiles, int nseq) {
+    return ((nseq + 7) / 8) * 8 * ntiles;
+}
+
+}  // namespace la

@@ -1,12 +1,718 @@
-// Chunked prefill for the diagonal-transition variants (KATH, GLA) on bf16 MFMA.
-#include "common.hpp"
+// Chunked prefill for the diagonal-transition variants on bf16 MFMA (d_k = 128,
+// chunk C = 64): normalized Katharopoulos attention (KATH, "Linear / RNN 路线" section
+// 2.1) and gated linear attention with a per-key-dim gate (GLA, section 2.2).
+//
+// A diagonal transition lets a sequence be cut into segments that run in parallel:
+// the state entering segment j is an associative scan of per-segment summaries,
+//   S_in[j+1] = diag(A_j) S_in[j] + dS_j,   A_j = prod of the gates over segment j,
+//   dS_j = sum_{s in seg j} diag(prod_{s < r <= end of seg} g_r) k_s v_s^T
+// (KATH: A_j = 1, keys phi(k), and z carried the same way). Three kernels:
+//   summary  (seq, segment < P-1, value tile): dS_j, log A_j (and dz_j), walking the
+//            segment backwards so that every key is scaled by its suffix decay <= 1
+//   scan     (seq, state element): S_in[j] for j = 1 .. P-1
+//   forward  (seq, segment, value tile): the chunked forward from S_in[j]; the last
+//            segment writes S_final (and z_final)
+// Per chunk of the forward pass, with B_r = sum_{s<=r} log g_s (chunk-local, per key dim):
+//   P_rs = sum_i q_ri k_si exp(B_ri - B_si)  (s <= r)       [KATH: phi(q_r).phi(k_s)]
+//   o_r  = (q_r * exp(B_r))^T S + sum_s P_rs v_s             [KATH: / (phi(q_r).z + sum_s P_rs + eps)]
+//   S    = diag(exp(B_last)) S + sum_s diag(exp(B_last - B_s)) k_s v_s^T
+// P is formed on the matrix cores from scaled copies of q and k. To keep every scale
+// factor bounded the chunk is cut into four 16-row blocks; row block b uses the
+// reference rho_b = B at its middle row:
+//   q~_r = q_r exp(B_r - rho_b),  k~(b)_s = k_s exp(rho_b - B_s)  (s < 16(b+1))
+// so no factor exceeds exp(8 * max |log g|). The matrix-core path clamps log g at
+// -10 (g >= 4.5e-5; a gate below that keeps less than 4.5e-5 of the state, so the
+// clamp changes no result beyond bf16 rounding) which bounds every factor by e^80.
 #include "la_internal.h"
+#include "mfma.hpp"
 
 namespace la {
+namespace {
 
-bool diag_mfma_supported(int, int, int, bool) { return false; }
-size_t diag_mfma_workspace_bytes(const Problem&) { return 0; }
-int diag_mfma_auto_segments(const Problem&) { return 1; }
-hipError_t launch_prefill_diag_mfma(const Problem&) { return hipErrorInvalidValue; }
+constexpr int DK = 128;
+constexpr int C = kMfmaChunk;  // 64
+constexpr int NT = 256;
+constexpr int PQ = DK + 8;
+constexpr int PC = C + 8;
+constexpr int PB = DK + 4;     // pitch of the fp32 [64][128] gate tile
+constexpr float kLogGateMin = -10.f;
+
+// row offset of the k~(b) copy inside the stacked key tile (GLA): 16 + 32 + 48 + 64 rows
+__host__ __device__ constexpr int koff(int b) { return 8 * b * (b + 1); }
+
+template <int VAR, int VT>
+struct __align__(16) FwdSmem {
+    static constexpr int PV = VT + 8;
+    static constexpr int KROWS = VAR == LA_GLA ? 160 : 64;
+    __align__(16) uint16_t qt[C * PQ];       // q~ (KATH: phi(q))
+    __align__(16) uint16_t qh[VAR == LA_GLA ? C * PQ : 8];  // q^ = q exp(B) (GLA)
+    __align__(16) uint16_t kt[KROWS * PQ];   // k~ copies (KATH: phi(k))
+    __align__(16) uint16_t kh[VAR == LA_GLA ? C * PQ : 8];  // k^ = k exp(B_last - B) (GLA)
+    __align__(16) uint16_t st[VT * PQ];      // S^T [c][i], bf16
+    __align__(16) uint16_t v[C * PV];        // V [s][c]
+    __align__(16) uint16_t p[C * PC];        // P [r][s]
+    __align__(16) float bg[VAR == LA_GLA ? C * PB : 4];     // gate scan (GLA)
+    float rho[4][DK];                        // GLA references; KATH: unused
+    float fac[4][DK];                        // GLA: exp(rho_b); KATH: unused
+    float dec[DK];                           // GLA: exp(B_last); KATH: z
+    float psum[10][16];                      // KATH: partial row sums of P per tile
+    float qz[C];                             // KATH: phi(q_r).z
+};
+
+struct DiagArgs {
+    const uint16_t *q, *k, *v;
+    const void* g;
+    const float *S0, *z0;
+    uint16_t* o;
+    float *S, *z;
+    float *dS, *lgA, *dz, *Sin, *zin;  // workspace
+    int N, nseq, ntiles, nseg, cps, gate_bf16;
+    float eps;
+};
+
+// ---------------------------------------------------------------------------
+// staging helpers
+// ---------------------------------------------------------------------------
+
+// Thread -> (row, 8-column group) for a [64][128] tile, x4 = 0..3.
+__device__ __forceinline__ void tile_rc(int tid, int x4, int& r, int& col) {
+    const int x = tid + NT * x4;
+    r = x >> 4;
+    col = (x & 15) * 8;
+}
+
+__device__ __forceinline__ void load8_gate(const void* g, size_t e, bool gb, float (&f)[8]) {
+    if (gb) {
+        unpack8(ld_g16(static_cast<const uint16_t*>(g) + e), f);
+    } else {
+        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(g) + e);
+        const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(g) + e + 4);
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    }
+}
+
+// In-place inclusive (reverse = false) or exclusive-suffix (reverse = true) scan down
+// the 64 rows of each column of a fp32 [64][PB] LDS tile; returns via the tile. Two
+// threads per column, 32 rows each. Ends with a barrier.
+template <bool REVERSE>
+__device__ void column_scan(float* bg, int tid) {
+    const int col = tid & 127, half = tid >> 7;
+    float x[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) x[r] = bg[(half * 32 + r) * PB + col];
+    __syncthreads();
+    float tot = 0.f;
+    if (!REVERSE) {
+#pragma unroll
+        for (int r = 0; r < 32; ++r) { tot += x[r]; x[r] = tot; }
+    } else {
+        // exclusive suffix: x[r] <- sum_{r' > r} x[r'] (within this half)
+#pragma unroll
+        for (int r = 31; r >= 0; --r) { const float t = x[r]; x[r] = tot; tot += t; }
+    }
+    __shared__ float part[128];
+    if (REVERSE ? half == 1 : half == 0) part[col] = tot;
+    __syncthreads();
+    const float add = (REVERSE ? half == 0 : half == 1) ? part[col] : 0.f;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) bg[(half * 32 + r) * PB + col] = x[r] + add;
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// summary kernel: dS_j = sum over segment of (k_s * suffix decay)^T v_s
+// ---------------------------------------------------------------------------
+
+template <int VAR, int VT>
+struct __align__(16) SumSmem {
+    static constexpr int PV = VT + 8;
+    __align__(16) uint16_t kh[C * PQ];
+    __align__(16) uint16_t v[C * PV];
+    __align__(16) float bg[VAR == LA_GLA ? C * PB : 4];
+};
+
+template <int VAR, int VT>
+__global__ __launch_bounds__(NT) void diag_summary_kernel(DiagArgs a) {
+    constexpr int NVT = VT / 16;
+    constexpr int PV = SumSmem<VAR, VT>::PV;
+    constexpr int VV = VT / 8;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    SumSmem<VAR, VT>& sm = *reinterpret_cast<SumSmem<VAR, VT>*>(smem_raw);
+    const int nsum = a.nseg - 1;
+    const XcdMap mp = xcd_map(blockIdx.x, a.ntiles * nsum, a.nseq);
+    if (!mp.valid) return;
+    const int seg = mp.tile / a.ntiles, vtile = mp.tile % a.ntiles;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, jl = lane & 15;
+    const int DV = a.ntiles * VT, c0 = vtile * VT;
+    const size_t seq = size_t(mp.seq), tok0 = seq * size_t(a.N);
+    const bool gb = a.gate_bf16 != 0;
+    const int nchunks = (a.N + C - 1) / C;
+    const int ch_lo = seg * a.cps, ch_hi = min(nchunks, ch_lo + a.cps);
+
+    f32x4_t acc[2][NVT];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int ct = 0; ct < NVT; ++ct) acc[ib][ct] = zero4();
+    float zacc[8 * 4];   // KATH: column partial sums of phi(k) (x4, column)
+#pragma unroll
+    for (int e = 0; e < 32; ++e) zacc[e] = 0.f;
+    // GLA: running sum of log g over the chunks already processed (the later ones)
+    __shared__ float runcol[DK];
+    if (tid < DK) runcol[tid] = 0.f;
+    __syncthreads();
+
+    for (int ch = ch_hi - 1; ch >= ch_lo; --ch) {
+        const int t0 = ch * C, n = min(C, a.N - t0);
+        uint4 kraw[4];
+        float lg[4][8];
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4) {
+            int r, col;
+            tile_rc(tid, x4, r, col);
+            const size_t e = (tok0 + t0 + r) * DK + col;
+            kraw[x4] = r < n ? ld_g16(a.k + e) : make_uint4(0, 0, 0, 0);
+            if (VAR == LA_GLA) {
+                if (r < n) {
+                    float f[8];
+                    load8_gate(a.g, e, gb, f);
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) lg[x4][q] = fmaxf(logf(f[q]), kLogGateMin);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) lg[x4][q] = 0.f;
+                }
+            }
+        }
+        for (int x = tid; x < C * VV; x += NT) {
+            const int r = x / VV, col = (x % VV) * 8;
+            const uint4 vv = r < n ? ld_g16(a.v + (tok0 + t0 + r) * DV + c0 + col) : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(sm.v + r * PV + col) = vv;
+        }
+        if (VAR == LA_GLA) {
+#pragma unroll
+            for (int x4 = 0; x4 < 4; ++x4) {
+                int r, col;
+                tile_rc(tid, x4, r, col);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) sm.bg[r * PB + col + q] = lg[x4][q];
+            }
+            __syncthreads();
+            column_scan<true>(sm.bg, tid);   // bg[r][i] = sum_{r' > r in chunk} log g
+        }
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4) {
+            int r, col;
+            tile_rc(tid, x4, r, col);
+            float f[8];
+            unpack8(kraw[x4], f);
+            if (VAR == LA_KATH) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) f[q] = r < n ? elu_plus_one(f[q]) : 0.f;
+                // z uses the same bf16-rounded features as the matrix cores
+                const uint4 pk = pack8(f);
+                float fr[8];
+                unpack8(pk, fr);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) zacc[x4 * 8 + q] += fr[q];
+                *reinterpret_cast<uint4*>(sm.kh + r * PQ + col) = pk;
+            } else {
+                // suffix decay of key s to the end of the segment, exponent <= 0
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    f[q] *= __expf(sm.bg[r * PB + col + q] + runcol[col + q]);
+                *reinterpret_cast<uint4*>(sm.kh + r * PQ + col) = pack8(f);
+            }
+        }
+        __syncthreads();
+        // dS += kh^T V  (wave w: key blocks 2w, 2w+1)
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct) {
+                f32x4_t s_ = acc[ib][ct];
+#pragma unroll
+                for (int kk = 0; kk < C / 32; ++kk)
+                    s_ = mfma16(frag_kr(sm.kh, PQ, 32 * kk, 16 * (2 * w + ib), lane),
+                                frag_kr(sm.v, PV, 32 * kk, 16 * ct, lane), s_);
+                acc[ib][ct] = s_;
+            }
+        if (VAR == LA_GLA) {
+            // chunk total of log g = exclusive suffix at row 0 + row 0's own log gate;
+            // the 16 threads that hold row 0 (x4 = 0) fold it into the running sum
+            if (tid < 16) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int col = tid * 8 + q;
+                    runcol[col] += sm.bg[col] + lg[0][q];
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // write dS_j tile
+    float* dS = a.dS + ((seq * nsum + seg) * DK) * DV;
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int ct = 0; ct < NVT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = 16 * (2 * w + ib) + 4 * g + j, c = 16 * ct + jl;
+                dS[size_t(i) * DV + c0 + c] = acc[ib][ct][j];
+            }
+    if (vtile == 0) {
+        if (VAR == LA_GLA) {
+            if (tid < DK) a.lgA[(seq * nsum + seg) * DK + tid] = runcol[tid];
+        } else {
+            // reduce the per-thread column partial sums of phi(k): thread covers columns
+            // (tid & 15) * 8 .. +7 for rows (tid >> 4) + 16 * x4
+#pragma unroll
+            for (int x4 = 1; x4 < 4; ++x4)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) zacc[q] += zacc[x4 * 8 + q];
+            // 16 threads share each column group: reduce over tid >> 4 through LDS
+            __shared__ float zred[16][DK];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) zred[tid >> 4][(tid & 15) * 8 + q] = zacc[q];
+            __syncthreads();
+            if (tid < DK) {
+                float s = 0.f;
+#pragma unroll
+                for (int x = 0; x < 16; ++x) s += zred[x][tid];
+                a.dz[(seq * nsum + seg) * DK + tid] = s;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// scan kernel: S_in[j] = diag(A_{j-1}) S_in[j-1] + dS_{j-1}, j = 1 .. P-1
+// ---------------------------------------------------------------------------
+
+template <int VAR>
+__global__ void diag_scan_kernel(DiagArgs a, int dv) {
+    const size_t per = size_t(DK) * dv;
+    const size_t idx = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const size_t seq = blockIdx.y;
+    const int nsum = a.nseg - 1;
+    if (idx < per) {
+        const int i = int(idx / dv);
+        float s = a.S0 ? a.S0[seq * per + idx] : 0.f;
+        for (int j = 0; j < nsum; ++j) {
+            const size_t sj = seq * nsum + j;
+            const float dec = VAR == LA_GLA ? __expf(a.lgA[sj * DK + i]) : 1.f;
+            s = dec * s + a.dS[sj * per + idx];
+            a.Sin[sj * per + idx] = s;   // entering state of segment j + 1
+        }
+    }
+    if (VAR == LA_KATH && idx < DK) {
+        float zz = a.z0 ? a.z0[seq * DK + idx] : 0.f;
+        for (int j = 0; j < nsum; ++j) {
+            const size_t sj = seq * nsum + j;
+            zz += a.dz[sj * DK + idx];
+            a.zin[sj * DK + idx] = zz;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// forward kernel
+// ---------------------------------------------------------------------------
+
+template <int VAR, int VT>
+__global__ __launch_bounds__(NT) void diag_fwd_kernel(DiagArgs a) {
+    constexpr int NVT = VT / 16;
+    using Sm = FwdSmem<VAR, VT>;
+    constexpr int PV = Sm::PV;
+    constexpr int VV = VT / 8;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
+    const XcdMap mp = xcd_map(blockIdx.x, a.ntiles * a.nseg, a.nseq);
+    if (!mp.valid) return;
+    const int seg = mp.tile / a.ntiles, vtile = mp.tile % a.ntiles;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, jl = lane & 15;
+    const int DV = a.ntiles * VT, c0 = vtile * VT;
+    const size_t seq = size_t(mp.seq), tok0 = seq * size_t(a.N);
+    const bool gb = a.gate_bf16 != 0;
+    const int nchunks = (a.N + C - 1) / C;
+    const int ch_lo = seg * a.cps, ch_hi = min(nchunks, ch_lo + a.cps);
+    const int nsum = a.nseg - 1;
+
+    // entering state of this segment
+    const float* Sin = seg == 0 ? a.S0 : a.Sin + ((seq * nsum + seg - 1) * DK) * DV;
+    const size_t sin_off = seg == 0 ? seq * DK * DV : 0;
+    f32x4_t S[2][NVT];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int ct = 0; ct < NVT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = 16 * (2 * w + ib) + 4 * g + j, c = 16 * ct + jl;
+                S[ib][ct][j] = Sin ? Sin[sin_off + size_t(i) * DV + c0 + c] : 0.f;
+            }
+    if (VAR == LA_KATH && tid < DK) {
+        const float* zin = seg == 0 ? a.z0 : a.zin + (seq * nsum + seg - 1) * DK;
+        const size_t zoff = seg == 0 ? seq * DK : 0;
+        sm.dec[tid] = zin ? zin[zoff + tid] : 0.f;
+    }
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int ct = 0; ct < NVT; ++ct) store_dT(sm.st, PQ, 16 * (2 * w + ib), 16 * ct, S[ib][ct], lane);
+
+    uint4 pq[4], pk[4], pv[2];
+    float lgr[4][8];
+    auto load_chunk = [&](int ch) {
+        const int t0 = ch * C, n = min(C, a.N - t0);
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4) {
+            int r, col;
+            tile_rc(tid, x4, r, col);
+            const size_t e = (tok0 + t0 + r) * DK + col;
+            if (r < n) {
+                pq[x4] = ld_g16(a.q + e);
+                pk[x4] = ld_g16(a.k + e);
+            } else {
+                pq[x4] = pk[x4] = make_uint4(0, 0, 0, 0);
+            }
+            if (VAR == LA_GLA) {
+                if (r < n) {
+                    load8_gate(a.g, e, gb, lgr[x4]);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) lgr[x4][q] = 1.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int x2 = 0; x2 < 2; ++x2) {
+            const int x = tid + NT * x2, r = x / VV, col = (x % VV) * 8;
+            pv[x2] = make_uint4(0, 0, 0, 0);
+            if (x < C * VV && r < n) pv[x2] = ld_g16(a.v + (tok0 + t0 + r) * DV + c0 + col);
+        }
+    };
+    if (ch_lo < ch_hi) load_chunk(ch_lo);
+    __syncthreads();
+
+    for (int ch = ch_lo; ch < ch_hi; ++ch) {
+        const int t0 = ch * C, n = min(C, a.N - t0);
+        // ---- phase 0: stage operands
+        if (VAR == LA_GLA) {
+#pragma unroll
+            for (int x4 = 0; x4 < 4; ++x4) {
+                int r, col;
+                tile_rc(tid, x4, r, col);
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    sm.bg[r * PB + col + q] = fmaxf(logf(lgr[x4][q]), kLogGateMin);
+            }
+            __syncthreads();
+            column_scan<false>(sm.bg, tid);   // bg[r][i] = B_r (inclusive)
+            if (tid < DK) {
+                const float bl = sm.bg[(C - 1) * PB + tid];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const float rb = sm.bg[(16 * b + 7) * PB + tid];
+                    sm.rho[b][tid] = rb;
+                    sm.fac[b][tid] = __expf(rb);
+                }
+                sm.dec[tid] = __expf(bl);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int x4 = 0; x4 < 4; ++x4) {
+                int r, col;
+                tile_rc(tid, x4, r, col);
+                const int b = r >> 4;
+                float fq[8], fk[8], qt[8], qh[8], kh[8];
+                unpack8(pq[x4], fq);
+                unpack8(pk[x4], fk);
+                float inv[8];
+                const float bl_base = 0.f;
+                (void)bl_base;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const float br = sm.bg[r * PB + col + q];
+                    const float x = __expf(br - sm.rho[b][col + q]);   // exp(B_r - rho_b)
+                    inv[q] = 1.f / x;                                   // exp(rho_b - B_r)
+                    qt[q] = fq[q] * x;
+                    qh[q] = fq[q] * x * sm.fac[b][col + q];
+                    kh[q] = fk[q] * __expf(sm.bg[(C - 1) * PB + col + q] - br);
+                }
+                *reinterpret_cast<uint4*>(sm.qt + r * PQ + col) = pack8(qt);
+                *reinterpret_cast<uint4*>(sm.qh + r * PQ + col) = pack8(qh);
+                *reinterpret_cast<uint4*>(sm.kh + r * PQ + col) = pack8(kh);
+                // k~(bb) for every row block bb >= b
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    if (bb < b) continue;
+                    float kt[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const float scale = bb == b ? inv[q]
+                                                    : inv[q] * __expf(sm.rho[bb][col + q] - sm.rho[b][col + q]);
+                        kt[q] = fk[q] * scale;
+                    }
+                    *reinterpret_cast<uint4*>(sm.kt + (koff(bb) + r) * PQ + col) = pack8(kt);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int x4 = 0; x4 < 4; ++x4) {
+                int r, col;
+                tile_rc(tid, x4, r, col);
+                float f[8];
+                unpack8(pq[x4], f);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) f[q] = r < n ? elu_plus_one(f[q]) : 0.f;
+                *reinterpret_cast<uint4*>(sm.qt + r * PQ + col) = pack8(f);
+                unpack8(pk[x4], f);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) f[q] = r < n ? elu_plus_one(f[q]) : 0.f;
+                *reinterpret_cast<uint4*>(sm.kt + r * PQ + col) = pack8(f);
+            }
+        }
+#pragma unroll
+        for (int x2 = 0; x2 < 2; ++x2) {
+            const int x = tid + NT * x2, r = x / VV, col = (x % VV) * 8;
+            if (x < C * VV) *reinterpret_cast<uint4*>(sm.v + r * PV + col) = pv[x2];
+        }
+        __syncthreads();
+        if (ch + 1 < ch_hi) load_chunk(ch + 1);
+
+        const uint16_t* QH = VAR == LA_GLA ? sm.qh : sm.qt;
+        const uint16_t* KH = VAR == LA_GLA ? sm.kh : sm.kt;
+
+        // ---- phase 1: P (10 lower tiles) and, for KATH, phi(q).z
+        for (int ti = w; ti < 10; ti += 4) {
+            const int rb = ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3;
+            const int sb = ti - (rb * (rb + 1)) / 2;
+            const int kbase = VAR == LA_GLA ? koff(rb) : 0;
+            f32x4_t acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk)
+                acc = mfma16(frag_kc(sm.kt, PQ, kbase + 16 * sb, 32 * kk, lane),
+                             frag_kc(sm.qt, PQ, 16 * rb, 32 * kk, lane), acc);   // D[s][r]
+            const int r = 16 * rb + jl;
+            f32x4_t pv4;
+            float rs = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int s = 16 * sb + 4 * g + j;
+                pv4[j] = s <= r ? acc[j] : 0.f;
+                rs += pv4[j];
+            }
+            store_dT(sm.p, PC, 16 * sb, 16 * rb, pv4, lane);
+            if (VAR == LA_KATH) {
+                rs += __shfl_xor(rs, 16, 64);
+                rs += __shfl_xor(rs, 32, 64);
+                if (g == 0) sm.psum[ti][jl] = rs;
+            }
+        }
+        if (w < 2) {   // zero the upper tiles (0,1) and (2,3) read by the P V products
+            const int rb = w == 0 ? 0 : 2, sb = rb + 1;
+            const int r = 16 * rb + (lane >> 2), s = 16 * sb + (lane & 3) * 4;
+            *reinterpret_cast<uint2*>(sm.p + r * PC + s) = make_uint2(0, 0);
+        }
+        if (VAR == LA_KATH) {
+            // phi(q_r) . z with the bf16 features: 4 threads per row
+            const int r = tid >> 2, part = tid & 3;
+            float acc = 0.f;
+#pragma unroll
+            for (int q8 = 0; q8 < 4; ++q8) {
+                const int col = part * 32 + q8 * 8;
+                float f[8];
+                unpack8(*reinterpret_cast<const uint4*>(sm.qt + r * PQ + col), f);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc += f[q] * sm.dec[col + q];
+            }
+            acc += __shfl_xor(acc, 1, 64);
+            acc += __shfl_xor(acc, 2, 64);
+            if (part == 0) sm.qz[r] = acc;
+        }
+        __syncthreads();
+
+        // ---- phase 2: O^T = S^T Q^T + V^T P^T  (row block w), then o
+        {
+            const int r = 16 * w + jl;
+            float inv_den = 1.f;
+            if (VAR == LA_KATH) {
+                float den = sm.qz[r] + a.eps;
+                const int tb = (w * (w + 1)) / 2;
+                for (int sb = 0; sb <= w; ++sb) den += sm.psum[tb + sb][jl];
+                inv_den = 1.f / den;
+            }
+            const int nk = w < 2 ? 1 : 2;
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct) {
+                f32x4_t o_ = zero4();
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk)
+                    o_ = mfma16(frag_kc(sm.st, PQ, 16 * ct, 32 * kk, lane),
+                                frag_kc(QH, PQ, 16 * w, 32 * kk, lane), o_);
+                for (int kk = 0; kk < nk; ++kk)
+                    o_ = mfma16(frag_kr(sm.v, PV, 32 * kk, 16 * ct, lane),
+                                frag_kc(sm.p, PC, 16 * w, 32 * kk, lane), o_);
+                if (r < n) {
+                    o_ = o_ * inv_den;
+                    uint2 wv;
+                    wv.x = pack_bf16x2(o_[0], o_[1]);
+                    wv.y = pack_bf16x2(o_[2], o_[3]);
+                    *reinterpret_cast<uint2*>(a.o + (tok0 + t0 + r) * DV + c0 + 16 * ct + 4 * g) = wv;
+                }
+            }
+        }
+        __syncthreads();   // all reads of S^T and z done
+
+        // ---- phase 3: S = diag(dec) S + K^^T V; KATH: z += sum phi(k)
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+            const int i0 = 16 * (2 * w + ib);
+            f32x4_t dec4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dec4[j] = VAR == LA_GLA ? sm.dec[i0 + 4 * g + j] : 1.f;
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct) {
+                f32x4_t s_ = S[ib][ct] * dec4;
+#pragma unroll
+                for (int kk = 0; kk < C / 32; ++kk)
+                    s_ = mfma16(frag_kr(KH, PQ, 32 * kk, i0, lane),
+                                frag_kr(sm.v, PV, 32 * kk, 16 * ct, lane), s_);
+                S[ib][ct] = s_;
+                store_dT(sm.st, PQ, i0, 16 * ct, s_, lane);
+            }
+        }
+        if (VAR == LA_KATH && tid < DK) {
+            float s = 0.f;
+            for (int r = 0; r < C; ++r) s += bf16_to_f32(sm.kt[r * PQ + tid]);
+            sm.dec[tid] += s;
+        }
+        __syncthreads();
+    }
+
+    if (seg == a.nseg - 1) {
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = 16 * (2 * w + ib) + 4 * g + j, c = 16 * ct + jl;
+                    a.S[seq * DK * DV + size_t(i) * DV + c0 + c] = S[ib][ct][j];
+                }
+        if (VAR == LA_KATH && vtile == 0 && tid < DK) a.z[seq * DK + tid] = sm.dec[tid];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+int pick_vt(const Problem& p) {
+    const size_t nseq = size_t(p.B) * size_t(p.H);
+    if (p.dv >= 32 && nseq * size_t(p.dv / 32) >= 64) return 32;
+    return 16;
+}
+
+struct WsLayout {
+    size_t dS, lgA, dz, Sin, zin, total;
+};
+
+WsLayout ws_layout(const Problem& p) {
+    const size_t nseq = size_t(p.B) * size_t(p.H);
+    const size_t nsum = size_t(p.segments > 1 ? p.segments - 1 : 0);
+    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+    WsLayout L{};
+    size_t off = 0;
+    L.dS = off;  off += al(nseq * nsum * DK * p.dv * 4);
+    L.Sin = off; off += al(nseq * nsum * DK * p.dv * 4);
+    L.lgA = off; off += al(p.variant == LA_GLA ? nseq * nsum * DK * 4 : 0);
+    L.dz = off;  off += al(p.variant == LA_KATH ? nseq * nsum * DK * 4 : 0);
+    L.zin = off; off += al(p.variant == LA_KATH ? nseq * nsum * DK * 4 : 0);
+    L.total = nsum ? off : 0;
+    return L;
+}
+
+template <int VAR, int VT>
+hipError_t launch_var_vt(const Problem& p) {
+    DiagArgs a{};
+    a.q = static_cast<const uint16_t*>(p.q);
+    a.k = static_cast<const uint16_t*>(p.k);
+    a.v = static_cast<const uint16_t*>(p.v);
+    a.g = p.g;
+    a.S0 = p.S0;
+    a.z0 = p.z0;
+    a.o = static_cast<uint16_t*>(p.o);
+    a.S = p.S;
+    a.z = p.z;
+    a.N = p.N;
+    const size_t nseq = size_t(p.B) * size_t(p.H);
+    if (nseq > (1u << 24)) return hipErrorInvalidValue;
+    a.nseq = int(nseq);
+    a.ntiles = p.dv / VT;
+    const int nchunks = (p.N + C - 1) / C;
+    a.cps = (nchunks + p.segments - 1) / p.segments;
+    a.nseg = p.segments;   // exact: every segment holds at least one chunk
+    if ((a.nseg - 1) * a.cps >= nchunks) return hipErrorInvalidValue;
+    a.gate_bf16 = p.gate_bf16;
+    a.eps = p.eps;
+    const WsLayout L = ws_layout(p);
+    char* ws = static_cast<char*>(p.ws);
+    a.dS = reinterpret_cast<float*>(ws + L.dS);
+    a.Sin = reinterpret_cast<float*>(ws + L.Sin);
+    a.lgA = reinterpret_cast<float*>(ws + L.lgA);
+    a.dz = reinterpret_cast<float*>(ws + L.dz);
+    a.zin = reinterpret_cast<float*>(ws + L.zin);
+    if (a.nseg > 1) {
+        if (!ws) return hipErrorInvalidValue;
+        const size_t smem = sizeof(SumSmem<VAR, VT>);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&diag_summary_kernel<VAR, VT>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+        if (e != hipSuccess) return e;
+        diag_summary_kernel<VAR, VT><<<dim3(xcd_grid(a.ntiles * (a.nseg - 1), a.nseq)), dim3(NT), smem,
+                                       p.stream>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int per = DK * p.dv;
+        diag_scan_kernel<VAR><<<dim3((per + 255) / 256, unsigned(nseq)), dim3(256), 0, p.stream>>>(a, p.dv);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const size_t smem = sizeof(FwdSmem<VAR, VT>);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&diag_fwd_kernel<VAR, VT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+    if (e != hipSuccess) return e;
+    diag_fwd_kernel<VAR, VT><<<dim3(xcd_grid(a.ntiles * a.nseg, a.nseq)), dim3(NT), smem, p.stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int VAR>
+hipError_t launch_var(const Problem& p) {
+    return pick_vt(p) == 32 ? launch_var_vt<VAR, 32>(p) : launch_var_vt<VAR, 16>(p);
+}
+
+}  // namespace
+
+bool diag_mfma_supported(int variant, int dk, int dv, bool io_bf16) {
+    return io_bf16 && (variant == LA_KATH || variant == LA_GLA) && dk == DK &&
+           (dv == 16 || dv == 32 || dv == 64 || dv == 128);
+}
+
+int diag_mfma_auto_segments(const Problem& p) {
+    const size_t nseq = size_t(p.B) * size_t(p.H);
+    const size_t tiles = nseq * size_t(p.dv / pick_vt(p));
+    const int nchunks = (p.N + C - 1) / C;
+    // enough chains for one workgroup per CU, but keep at least 4 chunks per segment
+    size_t want = (256 + tiles - 1) / tiles;
+    const size_t cap = size_t((nchunks + 3) / 4);
+    if (want > cap) want = cap;
+    return want < 1 ? 1 : int(want);
+}
+
+size_t diag_mfma_workspace_bytes(const Problem& p) { return ws_layout(p).total; }
+
+hipError_t launch_prefill_diag_mfma(const Problem& p) {
+    return p.variant == LA_GLA ? launch_var<LA_GLA>(p) : launch_var<LA_KATH>(p);
+}
 
 }  // namespace la

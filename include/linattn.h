@@ -60,9 +60,10 @@ extern "C" {
 enum {
     LA_OK = 0,
     LA_ERR_INVALID = 1,      /* null required pointer, bad enum, negative size, misaligned
-                                pointer (16 bytes; 256 for the workspace), overlap of an
-                                output with any other buffer, gate passed / missing for
-                                the variant, N != 1 for decode */
+                                pointer (16 bytes for q, k, v, o, GLA g, S and z; element
+                                alignment for GDN alpha and beta; 256 bytes for the
+                                workspace), overlap of an output with any other buffer,
+                                gate passed / missing for the variant, N != 1 for decode */
     LA_ERR_UNSUPPORTED = 2,  /* d_k or d_v not in {16, 32, 64, 128}, or a requested path /
                                 chunk size that this shape or dtype does not support */
     LA_ERR_HIP = 3,          /* a kernel launch failed */

@@ -96,6 +96,7 @@ def ptrs(variant):
     ("null_q", bd.LA_ERR_INVALID),
     ("null_S_final", bd.LA_ERR_INVALID),
     ("misaligned_v", bd.LA_ERR_INVALID),
+    ("misaligned_gla_gate", bd.LA_ERR_INVALID),
     ("o_overlaps_q", bd.LA_ERR_INVALID),
     ("S_partial_overlap_S0", bd.LA_ERR_INVALID),
     ("S_overlaps_k", bd.LA_ERR_INVALID),
@@ -139,6 +140,8 @@ def test_prefill_rejects(lib, case, expect):
         p["S"] = None
     elif case == "misaligned_v":
         p["v"] = addr(2, 8)
+    elif case == "misaligned_gla_gate":
+        p["g"] = addr(3, 2)
     elif case == "o_overlaps_q":
         p["o"] = addr(0, 256)
     elif case == "S_partial_overlap_S0":
@@ -202,6 +205,17 @@ def test_decode_rejects(lib, case, expect):
     rc = lib.la_decode_step(ctypes.byref(d), p["q"], p["k"], p["v"], p["g"], p["beta"], p["S"],
                             p["z"], p["o"], None)
     assert rc == expect
+
+
+def test_gdn_scalar_gates_need_element_alignment_only(lib):
+    """GDN alpha/beta are per-token scalars: a 2-byte offset (bf16) is accepted by the
+    validation (the call then fails later only because no GPU / fake pointers)."""
+    d = good("gdn", B=0)          # empty batch: validated fully, then a no-op
+    p = ptrs("gdn")
+    p["g"], p["beta"] = addr(3, 2), addr(4, 6)
+    assert call_prefill(lib, d, **p) == bd.LA_OK
+    p["g"] = addr(3, 1)           # not even element aligned
+    assert call_prefill(lib, d, **p) == bd.LA_ERR_INVALID
 
 
 def test_workspace_query(lib):
