@@ -1,0 +1,370 @@
+#!/usr/bin/env python3
+"""Benchmark of the linear-attention hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--only WORKLOAD] [--no-cpu] [--no-extras]
+
+A step is one chunked prefill of the headline workload (GLA, B=2 H=8 N=2048
+d_k=d_v=128, bf16 inputs, fp32 state, chunk 64) over one batch of seeded
+synthetic inputs already resident in HBM. Eight distinct input sets rotate so
+that the 43 MB working set does not sit in the 256 MB last-level cache. The
+timed loop replays a HIP graph of those launches (same kernels and work as an
+eager call, without host launch gaps); the graph's output is checked bit for bit
+against an eager call first, and the eager time is reported beside it.
+
+The other workloads (Gated DeltaNet prefill, long normalized-attention prefill,
+decode steps for GDN and GLA, the small fp32 case) are timed the same way and
+reported under "workloads", each with its roofline. One JSON line is printed.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill Mtok/s & MFMA util (GLA/GDN chunked); decode state-update HBM GB/s"
+MAIN = "gla_bf16_b2h8_n2048_d128"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2516.6    # dense bf16 MFMA, 256 CU x 4096 flop/clk x 2.4 GHz
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_linear_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if taken on this kernel source."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    w = t.get("workloads", {}).get(name)
+    return None if w is None else w.get("hbm_bytes_per_step")
+
+
+# ---------------------------------------------------------------------------
+
+
+def to_dev(a, torch, device):
+    import numpy as np
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class PrefillCase:
+    """Preallocated buffers and a lean ctypes call for repeated prefills."""
+
+    def __init__(self, wl, rotate, torch, bd, W, device):
+        import ctypes
+        self.wl, self.torch, self.bd = wl, torch, bd
+        inp = W.make_inputs(wl)
+        self.exact = inp.exact
+        base = {k: to_dev(v, torch, device) for k, v in inp.dev.items()}
+        self.sets = [base]
+        for r in range(1, rotate):   # distinct memory, same value distribution
+            self.sets.append({k: torch.roll(v, shifts=97 * r, dims=2).contiguous()
+                              for k, v in base.items()})
+        io = bd.LA_BF16 if wl.io == "bf16" else bd.LA_F32
+        gd = bd.LA_BF16 if wl.gate_io == "bf16" else bd.LA_F32
+        self.desc = bd.make_desc(wl.variant, wl.B, wl.H, wl.N, wl.dk, wl.dv, io, gd, wl.eps)
+        self.ws_bytes = bd.prefill_workspace_bytes(self.desc)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+        dt = torch.bfloat16 if wl.io == "bf16" else torch.float32
+        self.outs = []
+        for _ in self.sets:
+            o = torch.empty((wl.B, wl.H, wl.N, wl.dv), dtype=dt, device=device)
+            S = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=device)
+            z = (torch.empty((wl.B, wl.H, wl.dk), dtype=torch.float32, device=device)
+                 if wl.variant == "kath" else None)
+            self.outs.append((o, S, z))
+        P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+        self.args = []
+        for s, (o, S, z) in zip(self.sets, self.outs):
+            self.args.append((P(s["q"]), P(s["k"]), P(s["v"]), P(s.get("g")), P(s.get("beta")),
+                              None, None, P(o), P(S), P(z),
+                              P(self.ws) if self.ws_bytes else None, self.ws_bytes))
+        self.lib = bd.load()
+        self.pdesc = ctypes.byref(self.desc)
+        self.ctypes = ctypes
+
+    def call(self, i, stream):
+        a = self.args[i % len(self.args)]
+        rc = self.lib.la_prefill(self.pdesc, *a, self.ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise self.bd.LinAttnError(rc, "la_prefill")
+
+
+def time_eager(fn, n, warmup, torch, stream):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def time_graph(case, per_graph, replays, warmup, torch, stream):
+    """Capture per_graph consecutive calls (rotating sets) and replay; ms per call."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(per_graph):
+            case.call(i, stream)
+    for _ in range(max(1, warmup)):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (replays * per_graph), g
+
+
+def prefill_record(name, ms, wl, W, chunk=64):
+    byts = W.algorithmic_bytes(wl)
+    flops = W.algorithmic_flops(wl, chunk=chunk)
+    s = ms / 1e3
+    gbs = byts / s / 1e9
+    tfl = flops / s / 1e12
+    return {
+        "ms": ms,
+        "Mtok_per_s": wl.B * wl.N / s / 1e6,
+        "token_heads_per_s": wl.token_heads / s,
+        "GB_per_s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+        "TFLOP_per_s": tfl, "mfma_frac": tfl / PEAK_BF16_TFLOPS,
+        "algorithmic_bytes": byts, "algorithmic_flops": flops,
+        "binding_frac": max(byts / (PEAK_HBM_GBS * 1e9), flops / (PEAK_BF16_TFLOPS * 1e12)) / s,
+    }
+
+
+def bench_prefill(name, steps, warmup, rotate, torch, bd, W, device, stream, graph=True):
+    wl = W.WORKLOADS[name]
+    log(f"prefill {name}: generating inputs")
+    case = PrefillCase(wl, rotate, torch, bd, W, device)
+    fn = lambda i: case.call(i, stream)
+    ms_eager = time_eager(fn, steps, warmup, torch, stream)
+    rec = {"workload": name, "eager_ms": ms_eager}
+    ms = ms_eager
+    if graph:
+        # eager reference outputs of set 0, then graph replay must reproduce them exactly
+        case.call(0, stream)
+        torch.cuda.synchronize()
+        ref = [t.clone() if t is not None else None for t in case.outs[0]]
+        per_graph = max(1, min(len(case.sets), steps))
+        replays = max(1, steps // per_graph)
+        ms, g = time_graph(case, per_graph, replays, warmup, torch, stream)
+        torch.cuda.synchronize()
+        same = all(torch.equal(a, b) for a, b in zip(case.outs[0], ref) if a is not None)
+        rec["graph_replay_matches_eager"] = bool(same)
+        if not same:
+            log(f"{name}: graph replay differs from eager; reporting eager timing")
+            ms = ms_eager
+        else:
+            rec["graph_ms"] = ms
+        del g
+    rec.update(prefill_record(name, ms, wl, W))
+    o = case.outs[0][0]
+    rec["finite"] = bool(torch.isfinite(o.float()).all().item())
+    rec["segments"] = None
+    return rec, case
+
+
+def bench_decode(name, steps, warmup, torch, bd, W, device, stream):
+    import ctypes
+    wl = W.WORKLOADS[name]
+    log(f"decode {name}: generating state and token pool")
+    S32, _, sets = W.make_decode_pool(wl, with_exact=False)
+    S = torch.from_numpy(S32).to(device)
+    del S32
+    dsets = [{k: to_dev(v, torch, device) for k, v in s.dev.items()} for s in sets]
+    o = torch.empty((wl.B, wl.H, wl.dv), dtype=torch.bfloat16, device=device)
+    desc = bd.make_desc(wl.variant, wl.B, wl.H, 1, wl.dk, wl.dv, bd.LA_BF16, bd.LA_BF16, wl.eps)
+    lib = bd.load()
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    args = [(P(d["q"]), P(d["k"]), P(d["v"]), P(d.get("g")), P(d.get("beta")), P(S), None, P(o))
+            for d in dsets]
+    pd = ctypes.byref(desc)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def fn(i):
+        rc = lib.la_decode_step(pd, *args[i % len(args)], sh)
+        if rc != 0:
+            raise bd.LinAttnError(rc, "la_decode_step")
+
+    ms = time_eager(fn, steps, warmup, torch, stream)
+    byts = W.algorithmic_bytes(wl)
+    flops = W.algorithmic_flops(wl)
+    s = ms / 1e3
+    gbs = byts / s / 1e9
+    return {"workload": name, "ms": ms, "us_per_step": ms * 1e3, "GB_per_s": gbs,
+            "hbm_frac": gbs / PEAK_HBM_GBS, "TFLOP_per_s": flops / s / 1e12,
+            "algorithmic_bytes": byts, "steps": steps,
+            "finite": bool(torch.isfinite(S).all().item())}
+
+
+def cpu_baseline(case, wl, budget_s=8.0):
+    """Time the fp64 oracle on a bounded sample of the workload's sequences."""
+    import numpy as np
+
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    nseq = wl.B * wl.H
+    e = case.exact
+    flat = lambda a: None if a is None else a.reshape((-1,) + a.shape[2:])
+    fe = {k: flat(v) for k, v in e.items()}
+    # one sequence first, single-threaded (a per-core rate), then a batch across cores
+    t0 = time.perf_counter()
+    sel = lambda a, idx: None if a is None else a[idx][None]
+    oracle.prefill(wl.variant, sel(fe["q"], [0]), sel(fe["k"], [0]), sel(fe["v"], [0]),
+                   sel(fe.get("g"), [0]), sel(fe.get("beta"), [0]), eps=wl.eps, threads=1)
+    t1 = time.perf_counter() - t0
+    per_seq = max(t1, 1e-6)
+    k = int(min(nseq, max(1, cores * max(1, int(budget_s / per_seq)))))
+    k = min(k, nseq)
+    idx = list(range(k))
+    threads = min(cores, k)
+    t0 = time.perf_counter()
+    oracle.prefill(wl.variant, sel(fe["q"], idx), sel(fe["k"], idx), sel(fe["v"], idx),
+                   sel(fe.get("g"), idx), sel(fe.get("beta"), idx), eps=wl.eps, threads=threads)
+    tk = time.perf_counter() - t0
+    tokens = k / wl.H * wl.N   # B*N tokens = sequences / H * N
+    return {"value": tokens / tk / 1e6, "unit": "Mtok/s", "cores": threads, "kind": "oracle",
+            "sample": f"{k} of {nseq} (b,h) sequences x N={wl.N} of {wl.name}, fp64 token "
+                      f"recurrence, {threads} OpenMP threads, {tk:.2f} s wall; single-thread "
+                      f"one sequence {t1:.3f} s",
+            "seconds": tk}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only", default=None, help="time only this workload")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 512 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every (b, h) sequence is independent; see the sharding notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_delta_rule_linear_amd import binding as bd
+    from gated_delta_rule_linear_amd import workloads as W
+
+    if not os.path.exists(bd.LIB_PATH):
+        raise SystemExit(f"{bd.LIB_PATH} missing: run `python -m gated_delta_rule_linear_amd.build`")
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    # all timed work runs on one side stream (default priority); graph capture needs a
+    # non-default stream
+    stream = torch.cuda.Stream(device)
+    torch.cuda.set_stream(stream)
+    use_graph = not args.no_graph
+
+    if args.copy_calib:
+        n = 512 << 20
+        a = torch.empty(n, dtype=torch.uint8, device=device)
+        b = torch.empty(n, dtype=torch.uint8, device=device)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 512 MiB device copies")
+
+    results = {}
+    main_name = args.only or MAIN
+    if main_name.startswith("decode"):
+        rec = bench_decode(main_name, args.steps, args.warmup, torch, bd, W, device, stream)
+        main_case = None
+    else:
+        rotate = 8 if main_name == MAIN else 2
+        rec, main_case = bench_prefill(main_name, args.steps, args.warmup, rotate, torch, bd, W,
+                                       device, stream, graph=use_graph)
+    results[main_name] = rec
+
+    if not args.no_extras and not args.only:
+        for name in ("gdn_bf16_b4h16_n8192_d128", "kath_bf16_b1h16_n32768_dk128_dv64",
+                     "kath_f32_n256_d16"):
+            r, c = bench_prefill(name, max(20, args.steps // 8), 5, 2, torch, bd, W, device,
+                                 stream, graph=use_graph)
+            results[name] = r
+            del c
+            torch.cuda.empty_cache()
+        for name in ("decode_gdn_256x32_d128", "decode_gla_256x32_d128"):
+            results[name] = bench_decode(name, 1000, 10, torch, bd, W, device, stream)
+            torch.cuda.empty_cache()
+
+    wl = W.WORKLOADS[main_name]
+    m = results[main_name]
+    if main_name.startswith("decode"):
+        value, unit = m["GB_per_s"], "GB/s"
+        roof = {"bound": "hbm", "achieved": m["GB_per_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": m["hbm_frac"], "traffic": load_traffic(main_name),
+                "kernel": "decode_kernel", "duration_us": m["us_per_step"]}
+    else:
+        value, unit = m["Mtok_per_s"], "Mtok/s"
+        roof = {"bound": "hbm", "achieved": m["GB_per_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": m["hbm_frac"], "traffic": load_traffic(main_name),
+                "kernel": ("diag_summary_kernel + diag_scan_kernel + diag_fwd_kernel"
+                           if wl.variant != "gdn" else "gdn_fwd_kernel"),
+                "duration_us": m["ms"] * 1e3,
+                "mfma": {"achieved": m["TFLOP_per_s"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": m["mfma_frac"]}}
+    cpu = None
+    if not args.no_cpu and main_case is not None:
+        log("cpu baseline: timing the oracle")
+        cpu = cpu_baseline(main_case, wl)
+    line = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": m["ms"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.io == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": main_name, "variant": wl.variant, "B": wl.B, "H": wl.H, "N": wl.N,
+                   "dk": wl.dk, "dv": wl.dv, "chunk": 64, "state": "fp32",
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "workloads": results,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -27,13 +27,32 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(uint32_t(b) << 16);
 }
 
-// fp32 -> bf16 bit pattern, round to nearest, ties to even; NaN stays a quiet NaN
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return uint16_t(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (low half = a), round to nearest even, in one
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const f32x2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
+
+// fp32 -> bf16 bit pattern, round to nearest even
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return uint16_t(pack_bf16x2(f, 0.f) & 0xffffu);
+}
+
+// Workgroup barrier that orders LDS traffic only: waits for this wave's LDS
+// operations, not for its outstanding global loads, so loads issued ahead for
+// the next chunk stay in flight across it. The memory clobber keeps the compiler
+// from moving shared-memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Within one wave: make this wave's LDS writes visible to its own later LDS reads
+// (a wave's LDS operations execute in order once issued).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Element i of an array stored as fp32 (bf16 == false) or bf16 bits.
 __device__ __forceinline__ float load_elem(const void* p, size_t i, bool bf16) {
@@ -61,8 +80,8 @@ __device__ __forceinline__ float4 load4(const void* p, size_t i, bool bf16) {
 __device__ __forceinline__ void store4(void* p, size_t i, float4 x, bool bf16) {
     if (bf16) {
         uint2 w;
-        w.x = uint32_t(f32_to_bf16(x.x)) | (uint32_t(f32_to_bf16(x.y)) << 16);
-        w.y = uint32_t(f32_to_bf16(x.z)) | (uint32_t(f32_to_bf16(x.w)) << 16);
+        w.x = pack_bf16x2(x.x, x.y);
+        w.y = pack_bf16x2(x.z, x.w);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = w;
     } else {
         *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = x;
@@ -72,6 +91,8 @@ __device__ __forceinline__ void store4(void* p, size_t i, float4 x, bool bf16) {
 // ELU(x) + 1 (alpha = 1): x + 1 for x > 0, exp(x) otherwise. The feature map of
 // normalized linear attention; it keeps features positive.
 __device__ __forceinline__ float elu_plus_one(float x) { return x > 0.f ? x + 1.f : expf(x); }
+// Same with the hardware exp (a few ulp; used where operands are rounded to bf16).
+__device__ __forceinline__ float elu_plus_one_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -124,7 +124,8 @@ int plan_prefill(const la_desc& d, Problem& p) {
 
 size_t workspace_for(const Problem& p) {
     if (p.N == 0 || p.B == 0 || p.H == 0) return 0;
-    if (p.path == LA_PATH_MFMA && p.variant != LA_GDN) return la::diag_mfma_workspace_bytes(p);
+    if (p.path == LA_PATH_MFMA)
+        return p.variant == LA_GDN ? la::gdn_mfma_workspace_bytes(p) : la::diag_mfma_workspace_bytes(p);
     return 0;
 }
 

@@ -45,6 +45,7 @@ int diag_mfma_auto_segments(const Problem& p);
 hipError_t launch_prefill_diag_mfma(const Problem& p);
 // prefill_gdn_mfma.hip (GDN)
 bool gdn_mfma_supported(int dk, int dv, bool io_bf16);
+size_t gdn_mfma_workspace_bytes(const Problem& p);
 hipError_t launch_prefill_gdn_mfma(const Problem& p);
 
 }  // namespace la

@@ -47,9 +47,6 @@ __device__ __forceinline__ bf16x8_t frag_kr(const uint16_t* t, int pitch, int k0
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
-}
 
 // Store a D tile (rows m0.., cols n0..) transposed into a bf16 tile t[col][row]
 // (8-byte write per lane: t[n0 + j][m0 + 4g .. +3]). Needs pitch % 4 == 0.
@@ -81,6 +78,42 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
     w.w = pack_bf16x2(f[6], f[7]);
     return w;
 }
+
+// Raw bits of one gate element (bf16 or fp32 storage), converted later so that a
+// prefetch load is not consumed right after it is issued.
+template <bool GB>
+__device__ __forceinline__ uint32_t ld_gate_raw(const void* p, size_t i) {
+    if constexpr (GB) return static_cast<const uint16_t*>(p)[i];
+    else return static_cast<const uint32_t*>(p)[i];
+}
+template <bool GB>
+__device__ __forceinline__ float gate_val(uint32_t raw) {
+    return GB ? __uint_as_float(raw << 16) : __uint_as_float(raw);
+}
+// Eight consecutive gate elements, raw: GB -> w[0] holds 8 bf16; fp32 -> w[0], w[1].
+template <bool GB>
+__device__ __forceinline__ void ld_gate8_raw(const void* p, size_t i, uint4 (&w)[2]) {
+    if constexpr (GB) {
+        w[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+        w[1] = make_uint4(0, 0, 0, 0);
+    } else {
+        w[0] = *reinterpret_cast<const uint4*>(static_cast<const float*>(p) + i);
+        w[1] = *reinterpret_cast<const uint4*>(static_cast<const float*>(p) + i + 4);
+    }
+}
+template <bool GB>
+__device__ __forceinline__ void gate8_val(const uint4 (&w)[2], float (&f)[8]) {
+    if constexpr (GB) {
+        unpack8(w[0], f);
+    } else {
+        f[0] = __uint_as_float(w[0].x); f[1] = __uint_as_float(w[0].y);
+        f[2] = __uint_as_float(w[0].z); f[3] = __uint_as_float(w[0].w);
+        f[4] = __uint_as_float(w[1].x); f[5] = __uint_as_float(w[1].y);
+        f[6] = __uint_as_float(w[1].z); f[7] = __uint_as_float(w[1].w);
+    }
+}
+
+__device__ __forceinline__ uint4 zero_u4() { return make_uint4(0, 0, 0, 0); }
 
 // Workgroup id -> (sequence, tile) with the tiles of one sequence on one XCD.
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8), each with its own

@@ -6,12 +6,12 @@
 // the state entering segment j is an associative scan of per-segment summaries,
 //   S_in[j+1] = diag(A_j) S_in[j] + dS_j,   A_j = prod of the gates over segment j,
 //   dS_j = sum_{s in seg j} diag(prod_{s < r <= end of seg} g_r) k_s v_s^T
-// (KATH: A_j = 1, keys phi(k), and z carried the same way). Three kernels:
+// (KATH: A_j = 1, keys phi(k), and z carried the same way). Two kernels:
 //   summary  (seq, segment < P-1, value tile): dS_j, log A_j (and dz_j), walking the
 //            segment backwards so that every key is scaled by its suffix decay <= 1
-//   scan     (seq, state element): S_in[j] for j = 1 .. P-1
-//   forward  (seq, segment, value tile): the chunked forward from S_in[j]; the last
-//            segment writes S_final (and z_final)
+//   forward  (seq, segment, value tile): folds S0 and the earlier summaries into
+//            S_in[j] (the scan), then runs the chunked forward; the last segment
+//            writes S_final (and z_final)
 // Per chunk of the forward pass, with B_r = sum_{s<=r} log g_s (chunk-local, per key dim):
 //   P_rs = sum_i q_ri k_si exp(B_ri - B_si)  (s <= r)       [KATH: phi(q_r).phi(k_s)]
 //   o_r  = (q_r * exp(B_r))^T S + sum_s P_rs v_s             [KATH: / (phi(q_r).z + sum_s P_rs + eps)]
@@ -43,21 +43,32 @@ __host__ __device__ constexpr int koff(int b) { return 8 * b * (b + 1); }
 template <int VAR, int VT>
 struct __align__(16) FwdSmem {
     static constexpr int PV = VT + 8;
-    static constexpr int KROWS = VAR == LA_GLA ? 160 : 64;
-    __align__(16) uint16_t qt[C * PQ];       // q~ (KATH: phi(q))
-    __align__(16) uint16_t qh[VAR == LA_GLA ? C * PQ : 8];  // q^ = q exp(B) (GLA)
-    __align__(16) uint16_t kt[KROWS * PQ];   // k~ copies (KATH: phi(k))
-    __align__(16) uint16_t kh[VAR == LA_GLA ? C * PQ : 8];  // k^ = k exp(B_last - B) (GLA)
-    __align__(16) uint16_t st[VT * PQ];      // S^T [c][i], bf16
-    __align__(16) uint16_t v[C * PV];        // V [s][c]
-    __align__(16) uint16_t p[C * PC];        // P [r][s]
-    __align__(16) float bg[VAR == LA_GLA ? C * PB : 4];     // gate scan (GLA)
-    float rho[4][DK];                        // GLA references; KATH: unused
-    float fac[4][DK];                        // GLA: exp(rho_b); KATH: unused
-    float dec[DK];                           // GLA: exp(B_last); KATH: z
-    float psum[10][16];                      // KATH: partial row sums of P per tile
-    float qz[C];                             // KATH: phi(q_r).z
+    static constexpr bool G = VAR == LA_GLA;
+    static constexpr int KROWS = G ? 160 : 64;
+    __align__(16) uint16_t qt[C * PQ];            // q~ (KATH: phi(q))
+    __align__(16) uint16_t qh[G ? C * PQ : 8];    // q^ = q exp(B) (GLA)
+    __align__(16) uint16_t kt[KROWS * PQ];        // k~ copies (KATH: phi(k))
+    __align__(16) uint16_t kh[G ? C * PQ : 8];    // k^ = k exp(B_last - B) (GLA)
+    __align__(16) uint16_t st[VT * PQ];           // S^T [c][i], bf16
+    __align__(16) uint16_t v[C * PV];             // V [s][c]
+    __align__(16) uint16_t p[C * PC];             // P [r][s]
+    // GLA: gate scan; KATH: per-thread column partial sums of phi(k) for z
+    __align__(16) float bg[G ? C * PB : 16 * DK];
+    // GLA per-column factor tables (chunk-local): rho_b, exp(rho_b), exp(B_last - rho_b),
+    // exp(rho_bb - rho_b) for the six pairs b < bb
+    __align__(16) float rho[G ? 4 : 1][DK];
+    __align__(16) float fq[G ? 4 : 1][DK];
+    __align__(16) float fk[G ? 4 : 1][DK];
+    __align__(16) float fe[G ? 6 : 1][DK];
+    __align__(16) float dec[DK];                  // GLA: exp(B_last); KATH: z
+    float psum[G ? 1 : 10][16];                   // KATH: partial row sums of P per tile
+    float qz[G ? 1 : C];                          // KATH: phi(q_r).z
 };
+
+// index of the pair (b, bb), b < bb, in the exp(rho_bb - rho_b) table
+__host__ __device__ constexpr int pair_index(int b, int bb) {
+    return b == 0 ? bb - 1 : b == 1 ? bb + 1 : 5;
+}
 
 struct DiagArgs {
     const uint16_t *q, *k, *v;
@@ -65,7 +76,7 @@ struct DiagArgs {
     const float *S0, *z0;
     uint16_t* o;
     float *S, *z;
-    float *dS, *lgA, *dz, *Sin, *zin;  // workspace
+    float *dS, *lgA, *dz;  // workspace: segment summaries
     int N, nseq, ntiles, nseg, cps, gate_bf16;
     float eps;
 };
@@ -81,16 +92,6 @@ __device__ __forceinline__ void tile_rc(int tid, int x4, int& r, int& col) {
     col = (x & 15) * 8;
 }
 
-__device__ __forceinline__ void load8_gate(const void* g, size_t e, bool gb, float (&f)[8]) {
-    if (gb) {
-        unpack8(ld_g16(static_cast<const uint16_t*>(g) + e), f);
-    } else {
-        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(g) + e);
-        const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(g) + e + 4);
-        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-    }
-}
-
 // In-place inclusive (reverse = false) or exclusive-suffix (reverse = true) scan down
 // the 64 rows of each column of a fp32 [64][PB] LDS tile; returns via the tile. Two
 // threads per column, 32 rows each. Ends with a barrier.
@@ -100,7 +101,7 @@ __device__ void column_scan(float* bg, int tid) {
     float x[32];
 #pragma unroll
     for (int r = 0; r < 32; ++r) x[r] = bg[(half * 32 + r) * PB + col];
-    __syncthreads();
+    lds_barrier();
     float tot = 0.f;
     if (!REVERSE) {
 #pragma unroll
@@ -112,11 +113,11 @@ __device__ void column_scan(float* bg, int tid) {
     }
     __shared__ float part[128];
     if (REVERSE ? half == 1 : half == 0) part[col] = tot;
-    __syncthreads();
+    lds_barrier();
     const float add = (REVERSE ? half == 0 : half == 1) ? part[col] : 0.f;
 #pragma unroll
     for (int r = 0; r < 32; ++r) bg[(half * 32 + r) * PB + col] = x[r] + add;
-    __syncthreads();
+    lds_barrier();
 }
 
 // ---------------------------------------------------------------------------
@@ -128,10 +129,11 @@ struct __align__(16) SumSmem {
     static constexpr int PV = VT + 8;
     __align__(16) uint16_t kh[C * PQ];
     __align__(16) uint16_t v[C * PV];
-    __align__(16) float bg[VAR == LA_GLA ? C * PB : 4];
+    __align__(16) float bg[VAR == LA_GLA ? C * PB : 16 * DK];   // GLA scan / KATH z partials
+    float runcol[DK];
 };
 
-template <int VAR, int VT>
+template <int VAR, int VT, bool GB>
 __global__ __launch_bounds__(NT) void diag_summary_kernel(DiagArgs a) {
     constexpr int NVT = VT / 16;
     constexpr int PV = SumSmem<VAR, VT>::PV;
@@ -154,50 +156,55 @@ __global__ __launch_bounds__(NT) void diag_summary_kernel(DiagArgs a) {
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
         for (int ct = 0; ct < NVT; ++ct) acc[ib][ct] = zero4();
-    float zacc[8 * 4];   // KATH: column partial sums of phi(k) (x4, column)
+    float zacc[8];   // KATH: this thread's column partial sums of phi(k)
 #pragma unroll
-    for (int e = 0; e < 32; ++e) zacc[e] = 0.f;
-    // GLA: running sum of log g over the chunks already processed (the later ones)
-    __shared__ float runcol[DK];
-    if (tid < DK) runcol[tid] = 0.f;
-    __syncthreads();
+    for (int e = 0; e < 8; ++e) zacc[e] = 0.f;
+    if (tid < DK) sm.runcol[tid] = 0.f;   // GLA: sum of log g over the later chunks
+    lds_barrier();
 
     for (int ch = ch_hi - 1; ch >= ch_lo; --ch) {
         const int t0 = ch * C, n = min(C, a.N - t0);
-        uint4 kraw[4];
-        float lg[4][8];
+        uint4 kraw[4], graw[4][2];
+        float lg0[8];
+        // loads from clamped rows (always valid, no control flow), padding applied below
 #pragma unroll
         for (int x4 = 0; x4 < 4; ++x4) {
             int r, col;
             tile_rc(tid, x4, r, col);
-            const size_t e = (tok0 + t0 + r) * DK + col;
-            kraw[x4] = r < n ? ld_g16(a.k + e) : make_uint4(0, 0, 0, 0);
-            if (VAR == LA_GLA) {
-                if (r < n) {
-                    float f[8];
-                    load8_gate(a.g, e, gb, f);
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) lg[x4][q] = fmaxf(logf(f[q]), kLogGateMin);
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) lg[x4][q] = 0.f;
-                }
-            }
+            const size_t e = (tok0 + t0 + min(r, n - 1)) * DK + col;
+            kraw[x4] = ld_g16(a.k + e);
+            if (VAR == LA_GLA) ld_gate8_raw<GB>(a.g, e, graw[x4]);
         }
-        for (int x = tid; x < C * VV; x += NT) {
-            const int r = x / VV, col = (x % VV) * 8;
-            const uint4 vv = r < n ? ld_g16(a.v + (tok0 + t0 + r) * DV + c0 + col) : make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4*>(sm.v + r * PV + col) = vv;
+        uint4 vraw[2];
+#pragma unroll
+        for (int x2 = 0; x2 < 2; ++x2) {
+            const int x = tid + NT * x2, r = x / VV, col = (x % VV) * 8;
+            if (x < C * VV) vraw[x2] = ld_g16(a.v + (tok0 + t0 + min(r, n - 1)) * DV + c0 + col);
+        }
+#pragma unroll
+        for (int x2 = 0; x2 < 2; ++x2) {
+            const int x = tid + NT * x2, r = x / VV, col = (x % VV) * 8;
+            if (x < C * VV) *reinterpret_cast<uint4*>(sm.v + r * PV + col) = r < n ? vraw[x2] : zero_u4();
         }
         if (VAR == LA_GLA) {
 #pragma unroll
             for (int x4 = 0; x4 < 4; ++x4) {
                 int r, col;
                 tile_rc(tid, x4, r, col);
+                float f[8];
+                gate8_val<GB>(graw[x4], f);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) sm.bg[r * PB + col + q] = lg[x4][q];
+                for (int q = 0; q < 8; ++q) f[q] = r < n ? fmaxf(__logf(f[q]), kLogGateMin) : 0.f;
+                if (x4 == 0) {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) lg0[q] = f[q];
+                }
+                *reinterpret_cast<float4*>(sm.bg + r * PB + col) = make_float4(f[0], f[1], f[2], f[3]);
+                *reinterpret_cast<float4*>(sm.bg + r * PB + col + 4) = make_float4(f[4], f[5], f[6], f[7]);
             }
-            __syncthreads();
+        }
+        if (VAR == LA_GLA) {
+            lds_barrier();
             column_scan<true>(sm.bg, tid);   // bg[r][i] = sum_{r' > r in chunk} log g
         }
 #pragma unroll
@@ -205,26 +212,31 @@ __global__ __launch_bounds__(NT) void diag_summary_kernel(DiagArgs a) {
             int r, col;
             tile_rc(tid, x4, r, col);
             float f[8];
-            unpack8(kraw[x4], f);
+            unpack8(r < n ? kraw[x4] : zero_u4(), f);
             if (VAR == LA_KATH) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) f[q] = r < n ? elu_plus_one(f[q]) : 0.f;
+                for (int q = 0; q < 8; ++q) f[q] = r < n ? elu_plus_one_fast(f[q]) : 0.f;
                 // z uses the same bf16-rounded features as the matrix cores
                 const uint4 pk = pack8(f);
                 float fr[8];
                 unpack8(pk, fr);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) zacc[x4 * 8 + q] += fr[q];
+                for (int q = 0; q < 8; ++q) zacc[q] += fr[q];
                 *reinterpret_cast<uint4*>(sm.kh + r * PQ + col) = pk;
             } else {
                 // suffix decay of key s to the end of the segment, exponent <= 0
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    f[q] *= __expf(sm.bg[r * PB + col + q] + runcol[col + q]);
+                const float4 b0 = *reinterpret_cast<const float4*>(sm.bg + r * PB + col);
+                const float4 b1 = *reinterpret_cast<const float4*>(sm.bg + r * PB + col + 4);
+                const float4 r0 = *reinterpret_cast<const float4*>(sm.runcol + col);
+                const float4 r1 = *reinterpret_cast<const float4*>(sm.runcol + col + 4);
+                f[0] *= __expf(b0.x + r0.x); f[1] *= __expf(b0.y + r0.y);
+                f[2] *= __expf(b0.z + r0.z); f[3] *= __expf(b0.w + r0.w);
+                f[4] *= __expf(b1.x + r1.x); f[5] *= __expf(b1.y + r1.y);
+                f[6] *= __expf(b1.z + r1.z); f[7] *= __expf(b1.w + r1.w);
                 *reinterpret_cast<uint4*>(sm.kh + r * PQ + col) = pack8(f);
             }
         }
-        __syncthreads();
+        lds_barrier();
         // dS += kh^T V  (wave w: key blocks 2w, 2w+1)
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
@@ -237,18 +249,12 @@ __global__ __launch_bounds__(NT) void diag_summary_kernel(DiagArgs a) {
                                 frag_kr(sm.v, PV, 32 * kk, 16 * ct, lane), s_);
                 acc[ib][ct] = s_;
             }
-        if (VAR == LA_GLA) {
-            // chunk total of log g = exclusive suffix at row 0 + row 0's own log gate;
-            // the 16 threads that hold row 0 (x4 = 0) fold it into the running sum
-            if (tid < 16) {
+        if (VAR == LA_GLA && tid < 16) {
+            // chunk total of log g = exclusive suffix at row 0 + row 0's own log gate
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int col = tid * 8 + q;
-                    runcol[col] += sm.bg[col] + lg[0][q];
-                }
-            }
+            for (int q = 0; q < 8; ++q) sm.runcol[tid * 8 + q] += sm.bg[tid * 8 + q] + lg0[q];
         }
-        __syncthreads();
+        lds_barrier();
     }
     // write dS_j tile
     float* dS = a.dS + ((seq * nsum + seg) * DK) * DV;
@@ -263,55 +269,18 @@ __global__ __launch_bounds__(NT) void diag_summary_kernel(DiagArgs a) {
             }
     if (vtile == 0) {
         if (VAR == LA_GLA) {
-            if (tid < DK) a.lgA[(seq * nsum + seg) * DK + tid] = runcol[tid];
+            if (tid < DK) a.lgA[(seq * nsum + seg) * DK + tid] = sm.runcol[tid];
         } else {
-            // reduce the per-thread column partial sums of phi(k): thread covers columns
-            // (tid & 15) * 8 .. +7 for rows (tid >> 4) + 16 * x4
+            // 16 threads share each 8-column group: reduce over tid >> 4 through LDS
 #pragma unroll
-            for (int x4 = 1; x4 < 4; ++x4)
-#pragma unroll
-                for (int q = 0; q < 8; ++q) zacc[q] += zacc[x4 * 8 + q];
-            // 16 threads share each column group: reduce over tid >> 4 through LDS
-            __shared__ float zred[16][DK];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) zred[tid >> 4][(tid & 15) * 8 + q] = zacc[q];
-            __syncthreads();
+            for (int q = 0; q < 8; ++q) sm.bg[(tid >> 4) * DK + (tid & 15) * 8 + q] = zacc[q];
+            lds_barrier();
             if (tid < DK) {
-                float s = 0.f;
+                float s_ = 0.f;
 #pragma unroll
-                for (int x = 0; x < 16; ++x) s += zred[x][tid];
-                a.dz[(seq * nsum + seg) * DK + tid] = s;
+                for (int x = 0; x < 16; ++x) s_ += sm.bg[x * DK + tid];
+                a.dz[(seq * nsum + seg) * DK + tid] = s_;
             }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// scan kernel: S_in[j] = diag(A_{j-1}) S_in[j-1] + dS_{j-1}, j = 1 .. P-1
-// ---------------------------------------------------------------------------
-
-template <int VAR>
-__global__ void diag_scan_kernel(DiagArgs a, int dv) {
-    const size_t per = size_t(DK) * dv;
-    const size_t idx = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    const size_t seq = blockIdx.y;
-    const int nsum = a.nseg - 1;
-    if (idx < per) {
-        const int i = int(idx / dv);
-        float s = a.S0 ? a.S0[seq * per + idx] : 0.f;
-        for (int j = 0; j < nsum; ++j) {
-            const size_t sj = seq * nsum + j;
-            const float dec = VAR == LA_GLA ? __expf(a.lgA[sj * DK + i]) : 1.f;
-            s = dec * s + a.dS[sj * per + idx];
-            a.Sin[sj * per + idx] = s;   // entering state of segment j + 1
-        }
-    }
-    if (VAR == LA_KATH && idx < DK) {
-        float zz = a.z0 ? a.z0[seq * DK + idx] : 0.f;
-        for (int j = 0; j < nsum; ++j) {
-            const size_t sj = seq * nsum + j;
-            zz += a.dz[sj * DK + idx];
-            a.zin[sj * DK + idx] = zz;
         }
     }
 }
@@ -320,7 +289,7 @@ __global__ void diag_scan_kernel(DiagArgs a, int dv) {
 // forward kernel
 // ---------------------------------------------------------------------------
 
-template <int VAR, int VT>
+template <int VAR, int VT, bool GB>
 __global__ __launch_bounds__(NT) void diag_fwd_kernel(DiagArgs a) {
     constexpr int NVT = VT / 16;
     using Sm = FwdSmem<VAR, VT>;
@@ -339,9 +308,8 @@ __global__ __launch_bounds__(NT) void diag_fwd_kernel(DiagArgs a) {
     const int ch_lo = seg * a.cps, ch_hi = min(nchunks, ch_lo + a.cps);
     const int nsum = a.nseg - 1;
 
-    // entering state of this segment
-    const float* Sin = seg == 0 ? a.S0 : a.Sin + ((seq * nsum + seg - 1) * DK) * DV;
-    const size_t sin_off = seg == 0 ? seq * DK * DV : 0;
+    // entering state: S0, then the summaries of the earlier segments folded in order
+    // (S <- diag(A_j) S + dS_j; the scan of the segment-level recurrence)
     f32x4_t S[2][NVT];
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
@@ -350,115 +318,141 @@ __global__ __launch_bounds__(NT) void diag_fwd_kernel(DiagArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int i = 16 * (2 * w + ib) + 4 * g + j, c = 16 * ct + jl;
-                S[ib][ct][j] = Sin ? Sin[sin_off + size_t(i) * DV + c0 + c] : 0.f;
+                S[ib][ct][j] = a.S0 ? a.S0[seq * DK * DV + size_t(i) * DV + c0 + c] : 0.f;
             }
+    for (int j = 0; j < seg; ++j) {
+        const float* dS = a.dS + ((seq * nsum + j) * DK) * DV;
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int i = 16 * (2 * w + ib) + 4 * g + jj;
+                const float dec = VAR == LA_GLA ? __expf(a.lgA[(seq * nsum + j) * DK + i]) : 1.f;
+#pragma unroll
+                for (int ct = 0; ct < NVT; ++ct)
+                    S[ib][ct][jj] = dec * S[ib][ct][jj] + dS[size_t(i) * DV + c0 + 16 * ct + jl];
+            }
+    }
     if (VAR == LA_KATH && tid < DK) {
-        const float* zin = seg == 0 ? a.z0 : a.zin + (seq * nsum + seg - 1) * DK;
-        const size_t zoff = seg == 0 ? seq * DK : 0;
-        sm.dec[tid] = zin ? zin[zoff + tid] : 0.f;
+        float z = a.z0 ? a.z0[seq * DK + tid] : 0.f;
+        for (int j = 0; j < seg; ++j) z += a.dz[(seq * nsum + j) * DK + tid];
+        sm.dec[tid] = z;
     }
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
         for (int ct = 0; ct < NVT; ++ct) store_dT(sm.st, PQ, 16 * (2 * w + ib), 16 * ct, S[ib][ct], lane);
+    // zero, once, the P tiles above the diagonal that the row-block products read
+    if (w < 2) {
+        const int rb = w == 0 ? 0 : 2, sb = rb + 1;
+        const int r = 16 * rb + (lane >> 2), s = 16 * sb + (lane & 3) * 4;
+        *reinterpret_cast<uint2*>(sm.p + r * PC + s) = make_uint2(0, 0);
+    }
 
-    uint4 pq[4], pk[4], pv[2];
-    float lgr[4][8];
+    // register prefetch of one chunk: loads from clamped rows (always valid) without
+    // control flow, so nothing waits on them until the next chunk is staged
+    uint4 pq[4], pk[4], pv[2], pg[4][2];
     auto load_chunk = [&](int ch) {
         const int t0 = ch * C, n = min(C, a.N - t0);
 #pragma unroll
         for (int x4 = 0; x4 < 4; ++x4) {
             int r, col;
             tile_rc(tid, x4, r, col);
-            const size_t e = (tok0 + t0 + r) * DK + col;
-            if (r < n) {
-                pq[x4] = ld_g16(a.q + e);
-                pk[x4] = ld_g16(a.k + e);
-            } else {
-                pq[x4] = pk[x4] = make_uint4(0, 0, 0, 0);
-            }
-            if (VAR == LA_GLA) {
-                if (r < n) {
-                    load8_gate(a.g, e, gb, lgr[x4]);
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) lgr[x4][q] = 1.f;
-                }
-            }
+            const size_t e = (tok0 + t0 + min(r, n - 1)) * DK + col;
+            pq[x4] = ld_g16(a.q + e);
+            pk[x4] = ld_g16(a.k + e);
+            if (VAR == LA_GLA) ld_gate8_raw<GB>(a.g, e, pg[x4]);
         }
 #pragma unroll
         for (int x2 = 0; x2 < 2; ++x2) {
             const int x = tid + NT * x2, r = x / VV, col = (x % VV) * 8;
-            pv[x2] = make_uint4(0, 0, 0, 0);
-            if (x < C * VV && r < n) pv[x2] = ld_g16(a.v + (tok0 + t0 + r) * DV + c0 + col);
+            if (x < C * VV) pv[x2] = ld_g16(a.v + (tok0 + t0 + min(r, n - 1)) * DV + c0 + col);
         }
     };
     if (ch_lo < ch_hi) load_chunk(ch_lo);
-    __syncthreads();
+    lds_barrier();
 
     for (int ch = ch_lo; ch < ch_hi; ++ch) {
         const int t0 = ch * C, n = min(C, a.N - t0);
-        // ---- phase 0: stage operands
+        // ---- stage operands
         if (VAR == LA_GLA) {
 #pragma unroll
             for (int x4 = 0; x4 < 4; ++x4) {
                 int r, col;
                 tile_rc(tid, x4, r, col);
+                float f[8];
+                gate8_val<GB>(pg[x4], f);
 #pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    sm.bg[r * PB + col + q] = fmaxf(logf(lgr[x4][q]), kLogGateMin);
+                for (int q = 0; q < 8; ++q) f[q] = r < n ? fmaxf(__logf(f[q]), kLogGateMin) : 0.f;
+                *reinterpret_cast<float4*>(sm.bg + r * PB + col) = make_float4(f[0], f[1], f[2], f[3]);
+                *reinterpret_cast<float4*>(sm.bg + r * PB + col + 4) = make_float4(f[4], f[5], f[6], f[7]);
             }
-            __syncthreads();
+            lds_barrier();
             column_scan<false>(sm.bg, tid);   // bg[r][i] = B_r (inclusive)
             if (tid < DK) {
                 const float bl = sm.bg[(C - 1) * PB + tid];
+                float rb[4];
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    const float rb = sm.bg[(16 * b + 7) * PB + tid];
-                    sm.rho[b][tid] = rb;
-                    sm.fac[b][tid] = __expf(rb);
+                    rb[b] = sm.bg[(16 * b + 7) * PB + tid];
+                    sm.rho[b][tid] = rb[b];
+                    sm.fq[b][tid] = __expf(rb[b]);
+                    sm.fk[b][tid] = __expf(bl - rb[b]);
                 }
+#pragma unroll
+                for (int b = 0; b < 3; ++b)
+#pragma unroll
+                    for (int bb = b + 1; bb < 4; ++bb) sm.fe[pair_index(b, bb)][tid] = __expf(rb[bb] - rb[b]);
                 sm.dec[tid] = __expf(bl);
             }
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
             for (int x4 = 0; x4 < 4; ++x4) {
                 int r, col;
                 tile_rc(tid, x4, r, col);
-                const int b = r >> 4;
-                float fq[8], fk[8], qt[8], qh[8], kh[8];
-                unpack8(pq[x4], fq);
-                unpack8(pk[x4], fk);
-                float inv[8];
-                const float bl_base = 0.f;
-                (void)bl_base;
+                const int b = x4;   // rows (tid >> 4) + 16 x4 lie in row block x4
+                float q8[8], k8[8], br[8], rho[8], fq[8], fk[8];
+                unpack8(r < n ? pq[x4] : zero_u4(), q8);
+                unpack8(r < n ? pk[x4] : zero_u4(), k8);
+                auto ld8 = [&](const float* src, float (&dst)[8]) {
+                    const float4 u0 = *reinterpret_cast<const float4*>(src);
+                    const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
+                    dst[0] = u0.x; dst[1] = u0.y; dst[2] = u0.z; dst[3] = u0.w;
+                    dst[4] = u1.x; dst[5] = u1.y; dst[6] = u1.z; dst[7] = u1.w;
+                };
+                ld8(sm.bg + r * PB + col, br);
+                ld8(sm.rho[b] + col, rho);
+                ld8(sm.fq[b] + col, fq);
+                ld8(sm.fk[b] + col, fk);
+                float qt[8], qh[8], kt[8], kh[8];
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    const float br = sm.bg[r * PB + col + q];
-                    const float x = __expf(br - sm.rho[b][col + q]);   // exp(B_r - rho_b)
-                    inv[q] = 1.f / x;                                   // exp(rho_b - B_r)
-                    qt[q] = fq[q] * x;
-                    qh[q] = fq[q] * x * sm.fac[b][col + q];
-                    kh[q] = fk[q] * __expf(sm.bg[(C - 1) * PB + col + q] - br);
+                    const float x = __expf(br[q] - rho[q]);   // exp(B_r - rho_b)
+                    const float inv = __builtin_amdgcn_rcpf(x);  // exp(rho_b - B_r)
+                    qt[q] = q8[q] * x;
+                    qh[q] = qt[q] * fq[q];                     // q exp(B_r)
+                    kt[q] = k8[q] * inv;                       // k exp(rho_b - B_r)
+                    kh[q] = kt[q] * fk[q];                     // k exp(B_last - B_r)
                 }
                 *reinterpret_cast<uint4*>(sm.qt + r * PQ + col) = pack8(qt);
                 *reinterpret_cast<uint4*>(sm.qh + r * PQ + col) = pack8(qh);
                 *reinterpret_cast<uint4*>(sm.kh + r * PQ + col) = pack8(kh);
-                // k~(bb) for every row block bb >= b
+                *reinterpret_cast<uint4*>(sm.kt + (koff(b) + r) * PQ + col) = pack8(kt);
+                // k~(bb) = k exp(rho_bb - B_r) for the later row blocks bb
 #pragma unroll
                 for (int bb = 0; bb < 4; ++bb) {
-                    if (bb < b) continue;
-                    float kt[8];
+                    if (bb <= b) continue;
+                    float fe[8], kb[8];
+                    ld8(sm.fe[pair_index(b, bb)] + col, fe);
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const float scale = bb == b ? inv[q]
-                                                    : inv[q] * __expf(sm.rho[bb][col + q] - sm.rho[b][col + q]);
-                        kt[q] = fk[q] * scale;
-                    }
-                    *reinterpret_cast<uint4*>(sm.kt + (koff(bb) + r) * PQ + col) = pack8(kt);
+                    for (int q = 0; q < 8; ++q) kb[q] = kt[q] * fe[q];
+                    *reinterpret_cast<uint4*>(sm.kt + (koff(bb) + r) * PQ + col) = pack8(kb);
                 }
             }
         } else {
+            float zp[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) zp[q] = 0.f;
 #pragma unroll
             for (int x4 = 0; x4 < 4; ++x4) {
                 int r, col;
@@ -466,26 +460,34 @@ __global__ __launch_bounds__(NT) void diag_fwd_kernel(DiagArgs a) {
                 float f[8];
                 unpack8(pq[x4], f);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) f[q] = r < n ? elu_plus_one(f[q]) : 0.f;
+                for (int q = 0; q < 8; ++q) f[q] = r < n ? elu_plus_one_fast(f[q]) : 0.f;
                 *reinterpret_cast<uint4*>(sm.qt + r * PQ + col) = pack8(f);
                 unpack8(pk[x4], f);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) f[q] = r < n ? elu_plus_one(f[q]) : 0.f;
-                *reinterpret_cast<uint4*>(sm.kt + r * PQ + col) = pack8(f);
+                for (int q = 0; q < 8; ++q) f[q] = r < n ? elu_plus_one_fast(f[q]) : 0.f;
+                const uint4 pk8 = pack8(f);
+                *reinterpret_cast<uint4*>(sm.kt + r * PQ + col) = pk8;
+                float fr[8];
+                unpack8(pk8, fr);   // z uses the bf16 features the matrix cores see
+#pragma unroll
+                for (int q = 0; q < 8; ++q) zp[q] += fr[q];
             }
+            const int col = (tid & 15) * 8;
+            *reinterpret_cast<float4*>(sm.bg + (tid >> 4) * DK + col) = make_float4(zp[0], zp[1], zp[2], zp[3]);
+            *reinterpret_cast<float4*>(sm.bg + (tid >> 4) * DK + col + 4) = make_float4(zp[4], zp[5], zp[6], zp[7]);
         }
 #pragma unroll
         for (int x2 = 0; x2 < 2; ++x2) {
             const int x = tid + NT * x2, r = x / VV, col = (x % VV) * 8;
-            if (x < C * VV) *reinterpret_cast<uint4*>(sm.v + r * PV + col) = pv[x2];
+            if (x < C * VV) *reinterpret_cast<uint4*>(sm.v + r * PV + col) = r < n ? pv[x2] : zero_u4();
         }
-        __syncthreads();
+        lds_barrier();
         if (ch + 1 < ch_hi) load_chunk(ch + 1);
 
         const uint16_t* QH = VAR == LA_GLA ? sm.qh : sm.qt;
         const uint16_t* KH = VAR == LA_GLA ? sm.kh : sm.kt;
 
-        // ---- phase 1: P (10 lower tiles) and, for KATH, phi(q).z
+        // ---- P (10 lower tiles) and, for KATH, phi(q).z
         for (int ti = w; ti < 10; ti += 4) {
             const int rb = ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3;
             const int sb = ti - (rb * (rb + 1)) / 2;
@@ -496,25 +498,19 @@ __global__ __launch_bounds__(NT) void diag_fwd_kernel(DiagArgs a) {
                 acc = mfma16(frag_kc(sm.kt, PQ, kbase + 16 * sb, 32 * kk, lane),
                              frag_kc(sm.qt, PQ, 16 * rb, 32 * kk, lane), acc);   // D[s][r]
             const int r = 16 * rb + jl;
-            f32x4_t pv4;
             float rs = 0.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int s = 16 * sb + 4 * g + j;
-                pv4[j] = s <= r ? acc[j] : 0.f;
-                rs += pv4[j];
+                acc[j] = s <= r ? acc[j] : 0.f;
+                rs += acc[j];
             }
-            store_dT(sm.p, PC, 16 * sb, 16 * rb, pv4, lane);
+            store_dT(sm.p, PC, 16 * sb, 16 * rb, acc, lane);
             if (VAR == LA_KATH) {
                 rs += __shfl_xor(rs, 16, 64);
                 rs += __shfl_xor(rs, 32, 64);
                 if (g == 0) sm.psum[ti][jl] = rs;
             }
-        }
-        if (w < 2) {   // zero the upper tiles (0,1) and (2,3) read by the P V products
-            const int rb = w == 0 ? 0 : 2, sb = rb + 1;
-            const int r = 16 * rb + (lane >> 2), s = 16 * sb + (lane & 3) * 4;
-            *reinterpret_cast<uint2*>(sm.p + r * PC + s) = make_uint2(0, 0);
         }
         if (VAR == LA_KATH) {
             // phi(q_r) . z with the bf16 features: 4 threads per row
@@ -525,16 +521,18 @@ __global__ __launch_bounds__(NT) void diag_fwd_kernel(DiagArgs a) {
                 const int col = part * 32 + q8 * 8;
                 float f[8];
                 unpack8(*reinterpret_cast<const uint4*>(sm.qt + r * PQ + col), f);
-#pragma unroll
-                for (int q = 0; q < 8; ++q) acc += f[q] * sm.dec[col + q];
+                const float4 z0 = *reinterpret_cast<const float4*>(sm.dec + col);
+                const float4 z1 = *reinterpret_cast<const float4*>(sm.dec + col + 4);
+                acc += f[0] * z0.x + f[1] * z0.y + f[2] * z0.z + f[3] * z0.w;
+                acc += f[4] * z1.x + f[5] * z1.y + f[6] * z1.z + f[7] * z1.w;
             }
             acc += __shfl_xor(acc, 1, 64);
             acc += __shfl_xor(acc, 2, 64);
             if (part == 0) sm.qz[r] = acc;
         }
-        __syncthreads();
+        lds_barrier();
 
-        // ---- phase 2: O^T = S^T Q^T + V^T P^T  (row block w), then o
+        // ---- O^T = S^T Q^^T + V^T P^T  (row block w), then o
         {
             const int r = 16 * w + jl;
             float inv_den = 1.f;
@@ -564,9 +562,9 @@ __global__ __launch_bounds__(NT) void diag_fwd_kernel(DiagArgs a) {
                 }
             }
         }
-        __syncthreads();   // all reads of S^T and z done
+        lds_barrier();   // all reads of S^T and z are done
 
-        // ---- phase 3: S = diag(dec) S + K^^T V; KATH: z += sum phi(k)
+        // ---- S = diag(dec) S + K^^T V; KATH: z += sum of phi(k)
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
             const int i0 = 16 * (2 * w + ib);
@@ -585,11 +583,12 @@ __global__ __launch_bounds__(NT) void diag_fwd_kernel(DiagArgs a) {
             }
         }
         if (VAR == LA_KATH && tid < DK) {
-            float s = 0.f;
-            for (int r = 0; r < C; ++r) s += bf16_to_f32(sm.kt[r * PQ + tid]);
-            sm.dec[tid] += s;
+            float s_ = 0.f;
+#pragma unroll
+            for (int x = 0; x < 16; ++x) s_ += sm.bg[x * DK + tid];
+            sm.dec[tid] += s_;
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     if (seg == a.nseg - 1) {
@@ -610,14 +609,14 @@ __global__ __launch_bounds__(NT) void diag_fwd_kernel(DiagArgs a) {
 // host side
 // ---------------------------------------------------------------------------
 
-int pick_vt(const Problem& p) {
-    const size_t nseq = size_t(p.B) * size_t(p.H);
-    if (p.dv >= 32 && nseq * size_t(p.dv / 32) >= 64) return 32;
-    return 16;
+// value-tile width: 32 columns (KATH then fits two workgroups per CU in LDS)
+int pick_vt(int variant, int dv) {
+    (void)variant;
+    return dv >= 32 ? 32 : 16;
 }
 
 struct WsLayout {
-    size_t dS, lgA, dz, Sin, zin, total;
+    size_t dS, lgA, dz, total;
 };
 
 WsLayout ws_layout(const Problem& p) {
@@ -627,15 +626,13 @@ WsLayout ws_layout(const Problem& p) {
     WsLayout L{};
     size_t off = 0;
     L.dS = off;  off += al(nseq * nsum * DK * p.dv * 4);
-    L.Sin = off; off += al(nseq * nsum * DK * p.dv * 4);
     L.lgA = off; off += al(p.variant == LA_GLA ? nseq * nsum * DK * 4 : 0);
     L.dz = off;  off += al(p.variant == LA_KATH ? nseq * nsum * DK * 4 : 0);
-    L.zin = off; off += al(p.variant == LA_KATH ? nseq * nsum * DK * 4 : 0);
     L.total = nsum ? off : 0;
     return L;
 }
 
-template <int VAR, int VT>
+template <int VAR, int VT, bool GB>
 hipError_t launch_var_vt(const Problem& p) {
     DiagArgs a{};
     a.q = static_cast<const uint16_t*>(p.q);
@@ -661,34 +658,40 @@ hipError_t launch_var_vt(const Problem& p) {
     const WsLayout L = ws_layout(p);
     char* ws = static_cast<char*>(p.ws);
     a.dS = reinterpret_cast<float*>(ws + L.dS);
-    a.Sin = reinterpret_cast<float*>(ws + L.Sin);
     a.lgA = reinterpret_cast<float*>(ws + L.lgA);
     a.dz = reinterpret_cast<float*>(ws + L.dz);
-    a.zin = reinterpret_cast<float*>(ws + L.zin);
+    hipError_t e;
     if (a.nseg > 1) {
         if (!ws) return hipErrorInvalidValue;
         const size_t smem = sizeof(SumSmem<VAR, VT>);
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&diag_summary_kernel<VAR, VT>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&diag_summary_kernel<VAR, VT, GB>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
         if (e != hipSuccess) return e;
-        diag_summary_kernel<VAR, VT><<<dim3(xcd_grid(a.ntiles * (a.nseg - 1), a.nseq)), dim3(NT), smem,
+        diag_summary_kernel<VAR, VT, GB><<<dim3(xcd_grid(a.ntiles * (a.nseg - 1), a.nseq)), dim3(NT), smem,
                                        p.stream>>>(a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        const int per = DK * p.dv;
-        diag_scan_kernel<VAR><<<dim3((per + 255) / 256, unsigned(nseq)), dim3(256), 0, p.stream>>>(a, p.dv);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const size_t smem = sizeof(FwdSmem<VAR, VT>);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&diag_fwd_kernel<VAR, VT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&diag_fwd_kernel<VAR, VT, GB>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
     if (e != hipSuccess) return e;
-    diag_fwd_kernel<VAR, VT><<<dim3(xcd_grid(a.ntiles * a.nseg, a.nseq)), dim3(NT), smem, p.stream>>>(a);
+    diag_fwd_kernel<VAR, VT, GB><<<dim3(xcd_grid(a.ntiles * a.nseg, a.nseq)), dim3(NT), smem, p.stream>>>(a);
     return hipGetLastError();
 }
 
-template <int VAR>
-hipError_t launch_var(const Problem& p) {
-    return pick_vt(p) == 32 ? launch_var_vt<VAR, 32>(p) : launch_var_vt<VAR, 16>(p);
+hipError_t launch_gla(const Problem& p) {
+    const bool w32 = pick_vt(LA_GLA, p.dv) == 32;
+    if (p.gate_bf16) return w32 ? launch_var_vt<LA_GLA, 32, true>(p) : launch_var_vt<LA_GLA, 16, true>(p);
+    return w32 ? launch_var_vt<LA_GLA, 32, false>(p) : launch_var_vt<LA_GLA, 16, false>(p);
+}
+
+hipError_t launch_kath(const Problem& p) {
+    // KATH has no gates: the gate-dtype parameter is unused
+    switch (pick_vt(LA_KATH, p.dv)) {
+        case 64: return launch_var_vt<LA_KATH, 64, true>(p);
+        case 32: return launch_var_vt<LA_KATH, 32, true>(p);
+        default: return launch_var_vt<LA_KATH, 16, true>(p);
+    }
 }
 
 }  // namespace
@@ -700,10 +703,12 @@ bool diag_mfma_supported(int variant, int dk, int dv, bool io_bf16) {
 
 int diag_mfma_auto_segments(const Problem& p) {
     const size_t nseq = size_t(p.B) * size_t(p.H);
-    const size_t tiles = nseq * size_t(p.dv / pick_vt(p));
+    const size_t tiles = nseq * size_t(p.dv / pick_vt(p.variant, p.dv));
     const int nchunks = (p.N + C - 1) / C;
-    // enough chains for one workgroup per CU, but keep at least 4 chunks per segment
-    size_t want = (256 + tiles - 1) / tiles;
+    // enough chains for two workgroups per CU (KATH) or one (GLA, LDS-bound), but keep
+    // at least 4 chunks per segment
+    const size_t target = p.variant == LA_KATH ? 512 : 256;
+    size_t want = (target + tiles - 1) / tiles;
     const size_t cap = size_t((nchunks + 3) / 4);
     if (want > cap) want = cap;
     return want < 1 ? 1 : int(want);
@@ -712,7 +717,7 @@ int diag_mfma_auto_segments(const Problem& p) {
 size_t diag_mfma_workspace_bytes(const Problem& p) { return ws_layout(p).total; }
 
 hipError_t launch_prefill_diag_mfma(const Problem& p) {
-    return p.variant == LA_GLA ? launch_var<LA_GLA>(p) : launch_var<LA_KATH>(p);
+    return p.variant == LA_GLA ? launch_gla(p) : launch_kath(p);
 }
 
 }  // namespace la
