@@ -91,8 +91,41 @@ __device__ __forceinline__ void store4(void* p, size_t i, float4 x, bool bf16) {
 // ELU(x) + 1 (alpha = 1): x + 1 for x > 0, exp(x) otherwise. The feature map of
 // normalized linear attention; it keeps features positive.
 __device__ __forceinline__ float elu_plus_one(float x) { return x > 0.f ? x + 1.f : expf(x); }
-// Same with the hardware exp (a few ulp; used where operands are rounded to bf16).
-__device__ __forceinline__ float elu_plus_one_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+// Index of this thread's wave in the workgroup, as a wave-uniform (scalar) value so
+// that control flow depending on it compiles to scalar branches.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Natural log and exp on the hardware transcendental units (log2 / exp2), a few ulp.
+__device__ __forceinline__ float fast_log(float x) { return __builtin_amdgcn_logf(x) * 0.69314718f; }
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504f); }
+
+// ELU(x) + 1 with the hardware exponential (a few ulp; used where operands are rounded
+// to bf16), branch-free.
+__device__ __forceinline__ float elu_plus_one_fast(float x) {
+    const float e = fast_exp(fminf(x, 0.f));
+    return x > 0.f ? x + 1.f : e;
+}
+
+// DPP lane permutation of a float: lanes outside the enabled rows/banks (or with no
+// source lane) receive 0.
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, BANK_MASK, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane shifts: shifts of
+// 1, 2, 4, 8 within each row of 16 lanes, then row 15 / lane 31 broadcasts across rows.
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+    x += dpp_f<0x111, 0xf, 0xf>(x);  // row_shr:1
+    x += dpp_f<0x112, 0xf, 0xf>(x);  // row_shr:2
+    x += dpp_f<0x114, 0xf, 0xf>(x);  // row_shr:4
+    x += dpp_f<0x118, 0xf, 0xf>(x);  // row_shr:8
+    x += dpp_f<0x142, 0xa, 0xf>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_f<0x143, 0xc, 0xf>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

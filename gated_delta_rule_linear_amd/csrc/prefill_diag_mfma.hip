@@ -144,7 +144,7 @@ __global__ __launch_bounds__(NT) void diag_summary_kernel(DiagArgs a) {
     const XcdMap mp = xcd_map(blockIdx.x, a.ntiles * nsum, a.nseq);
     if (!mp.valid) return;
     const int seg = mp.tile / a.ntiles, vtile = mp.tile % a.ntiles;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, jl = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4, jl = lane & 15;
     const int DV = a.ntiles * VT, c0 = vtile * VT;
     const size_t seq = size_t(mp.seq), tok0 = seq * size_t(a.N);
     const bool gb = a.gate_bf16 != 0;
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(NT) void diag_summary_kernel(DiagArgs a) {
                 float f[8];
                 gate8_val<GB>(graw[x4], f);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) f[q] = r < n ? fmaxf(__logf(f[q]), kLogGateMin) : 0.f;
+                for (int q = 0; q < 8; ++q) { const float lg = fmaxf(fast_log(f[q]), kLogGateMin); f[q] = r < n ? lg : 0.f; }
                 if (x4 == 0) {
 #pragma unroll
                     for (int q = 0; q < 8; ++q) lg0[q] = f[q];
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(NT) void diag_summary_kernel(DiagArgs a) {
             unpack8(r < n ? kraw[x4] : zero_u4(), f);
             if (VAR == LA_KATH) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) f[q] = r < n ? elu_plus_one_fast(f[q]) : 0.f;
+                for (int q = 0; q < 8; ++q) { const float e = elu_plus_one_fast(f[q]); f[q] = r < n ? e : 0.f; }
                 // z uses the same bf16-rounded features as the matrix cores
                 const uint4 pk = pack8(f);
                 float fr[8];
@@ -229,10 +229,10 @@ __global__ __launch_bounds__(NT) void diag_summary_kernel(DiagArgs a) {
                 const float4 b1 = *reinterpret_cast<const float4*>(sm.bg + r * PB + col + 4);
                 const float4 r0 = *reinterpret_cast<const float4*>(sm.runcol + col);
                 const float4 r1 = *reinterpret_cast<const float4*>(sm.runcol + col + 4);
-                f[0] *= __expf(b0.x + r0.x); f[1] *= __expf(b0.y + r0.y);
-                f[2] *= __expf(b0.z + r0.z); f[3] *= __expf(b0.w + r0.w);
-                f[4] *= __expf(b1.x + r1.x); f[5] *= __expf(b1.y + r1.y);
-                f[6] *= __expf(b1.z + r1.z); f[7] *= __expf(b1.w + r1.w);
+                f[0] *= fast_exp(b0.x + r0.x); f[1] *= fast_exp(b0.y + r0.y);
+                f[2] *= fast_exp(b0.z + r0.z); f[3] *= fast_exp(b0.w + r0.w);
+                f[4] *= fast_exp(b1.x + r1.x); f[5] *= fast_exp(b1.y + r1.y);
+                f[6] *= fast_exp(b1.z + r1.z); f[7] *= fast_exp(b1.w + r1.w);
                 *reinterpret_cast<uint4*>(sm.kh + r * PQ + col) = pack8(f);
             }
         }
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(NT) void diag_fwd_kernel(DiagArgs a) {
     const XcdMap mp = xcd_map(blockIdx.x, a.ntiles * a.nseg, a.nseq);
     if (!mp.valid) return;
     const int seg = mp.tile / a.ntiles, vtile = mp.tile % a.ntiles;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, jl = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4, jl = lane & 15;
     const int DV = a.ntiles * VT, c0 = vtile * VT;
     const size_t seq = size_t(mp.seq), tok0 = seq * size_t(a.N);
     const bool gb = a.gate_bf16 != 0;
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(NT) void diag_fwd_kernel(DiagArgs a) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int i = 16 * (2 * w + ib) + 4 * g + jj;
-                const float dec = VAR == LA_GLA ? __expf(a.lgA[(seq * nsum + j) * DK + i]) : 1.f;
+                const float dec = VAR == LA_GLA ? fast_exp(a.lgA[(seq * nsum + j) * DK + i]) : 1.f;
 #pragma unroll
                 for (int ct = 0; ct < NVT; ++ct)
                     S[ib][ct][jj] = dec * S[ib][ct][jj] + dS[size_t(i) * DV + c0 + 16 * ct + jl];
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(NT) void diag_fwd_kernel(DiagArgs a) {
                 float f[8];
                 gate8_val<GB>(pg[x4], f);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) f[q] = r < n ? fmaxf(__logf(f[q]), kLogGateMin) : 0.f;
+                for (int q = 0; q < 8; ++q) { const float lg = fmaxf(fast_log(f[q]), kLogGateMin); f[q] = r < n ? lg : 0.f; }
                 *reinterpret_cast<float4*>(sm.bg + r * PB + col) = make_float4(f[0], f[1], f[2], f[3]);
                 *reinterpret_cast<float4*>(sm.bg + r * PB + col + 4) = make_float4(f[4], f[5], f[6], f[7]);
             }
@@ -396,14 +396,14 @@ __global__ __launch_bounds__(NT) void diag_fwd_kernel(DiagArgs a) {
                 for (int b = 0; b < 4; ++b) {
                     rb[b] = sm.bg[(16 * b + 7) * PB + tid];
                     sm.rho[b][tid] = rb[b];
-                    sm.fq[b][tid] = __expf(rb[b]);
-                    sm.fk[b][tid] = __expf(bl - rb[b]);
+                    sm.fq[b][tid] = fast_exp(rb[b]);
+                    sm.fk[b][tid] = fast_exp(bl - rb[b]);
                 }
 #pragma unroll
                 for (int b = 0; b < 3; ++b)
 #pragma unroll
-                    for (int bb = b + 1; bb < 4; ++bb) sm.fe[pair_index(b, bb)][tid] = __expf(rb[bb] - rb[b]);
-                sm.dec[tid] = __expf(bl);
+                    for (int bb = b + 1; bb < 4; ++bb) sm.fe[pair_index(b, bb)][tid] = fast_exp(rb[bb] - rb[b]);
+                sm.dec[tid] = fast_exp(bl);
             }
             lds_barrier();
 #pragma unroll
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(NT) void diag_fwd_kernel(DiagArgs a) {
                 float qt[8], qh[8], kt[8], kh[8];
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    const float x = __expf(br[q] - rho[q]);   // exp(B_r - rho_b)
+                    const float x = fast_exp(br[q] - rho[q]);   // exp(B_r - rho_b)
                     const float inv = __builtin_amdgcn_rcpf(x);  // exp(rho_b - B_r)
                     qt[q] = q8[q] * x;
                     qh[q] = qt[q] * fq[q];                     // q exp(B_r)
@@ -460,11 +460,11 @@ __global__ __launch_bounds__(NT) void diag_fwd_kernel(DiagArgs a) {
                 float f[8];
                 unpack8(pq[x4], f);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) f[q] = r < n ? elu_plus_one_fast(f[q]) : 0.f;
+                for (int q = 0; q < 8; ++q) { const float e = elu_plus_one_fast(f[q]); f[q] = r < n ? e : 0.f; }
                 *reinterpret_cast<uint4*>(sm.qt + r * PQ + col) = pack8(f);
                 unpack8(pk[x4], f);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) f[q] = r < n ? elu_plus_one_fast(f[q]) : 0.f;
+                for (int q = 0; q < 8; ++q) { const float e = elu_plus_one_fast(f[q]); f[q] = r < n ? e : 0.f; }
                 const uint4 pk8 = pack8(f);
                 *reinterpret_cast<uint4*>(sm.kt + r * PQ + col) = pk8;
                 float fr[8];

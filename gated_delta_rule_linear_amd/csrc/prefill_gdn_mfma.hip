@@ -95,15 +95,8 @@ __device__ __forceinline__ bf16x8_t k16(bf16x8_t f, int lane) {
 }
 
 // Inclusive scan of log alpha over the chunk by wave 0 (lane = row); padding rows
-// carry log alpha = 0. Writes cum (and gam, dec when given).
-__device__ __forceinline__ float scan64(float x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    return x;
-}
+// carry log alpha = 0.
+__device__ __forceinline__ float scan64(float x, int) { return wave_inclusive_scan(x); }
 
 // ---------------------------------------------------------------------------
 // prep kernel: T = (I + L)^{-1} per chunk
@@ -112,7 +105,7 @@ template <bool GB>
 __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int g = lane >> 4, jl = lane & 15;
     const size_t seq = blockIdx.x / a.nchunks;
     const int ch = blockIdx.x % a.nchunks;
@@ -134,7 +127,8 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
         *reinterpret_cast<uint4*>(sm.k + r * PQ + col) = r < n ? kv[x4] : zero_u4();
     }
     if (w == 0) {
-        const float x = lane < n ? __logf(gate_val<GB>(graw)) : 0.f;
+        const float lg = fast_log(gate_val<GB>(graw));
+        const float x = lane < n ? lg : 0.f;
         sm.cum[lane] = scan64(x, lane);
     } else if (w == 1) {
         sm.beta[lane] = lane < n ? gate_val<GB>(graw) : 0.f;
@@ -167,7 +161,8 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int s = 16 * b + 4 * g + j;
-                vv[j] = s < r ? br * __expf(cr - sm.cum[s]) * d[j] : 0.f;
+                const float e = br * fast_exp(cr - sm.cum[s]) * d[j];
+                vv[j] = s < r ? e : 0.f;
             }
             *reinterpret_cast<float4*>(sm.ld[b] + jl * PD + 4 * g) = val;
         }
@@ -206,7 +201,7 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
             const int r = 16 * rb + jl;
             const float br = sm.beta[r], cr = sm.cum[r];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) d[j] *= br * __expf(cr - sm.cum[16 * sb + 4 * g + j]);
+            for (int j = 0; j < 4; ++j) d[j] *= br * fast_exp(cr - sm.cum[16 * sb + 4 * g + j]);
             store_dT(sm.lo, PC, 16 * sb, 16 * rb, d, lane);
         }
     }
@@ -263,7 +258,7 @@ __global__ __launch_bounds__(NT) void gdn_fwd_kernel(GdnArgs a) {
 
     const XcdMap mp = xcd_map(blockIdx.x, a.ntiles, a.nseq);
     if (!mp.valid) return;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int g = lane >> 4, jl = lane & 15;
     const int DV = a.ntiles * VT;
     const int c0 = mp.tile * VT;
@@ -324,24 +319,35 @@ __global__ __launch_bounds__(NT) void gdn_fwd_kernel(GdnArgs a) {
         const int t0 = ch * C, n = min(C, a.N - t0);
         // ---- stage: gates (wave 0 scans log alpha, wave 1 holds beta), q, k, v, T
         if (w == 0) {
-            const float x = scan64(lane < n ? __logf(gate_val<GB>(pg)) : 0.f, lane);
+            const float lg = fast_log(gate_val<GB>(pg));
+            const float x = scan64(lane < n ? lg : 0.f, lane);
             const float clast = __shfl(x, 63, 64);
             sm.cum[lane] = x;
-            sm.gam[lane] = __expf(x);
-            sm.dec[lane] = __expf(clast - x);
+            sm.gam[lane] = fast_exp(x);
+            sm.dec[lane] = fast_exp(clast - x);
         } else if (w == 1) {
             sm.beta[lane] = lane < n ? gate_val<GB>(pg) : 0.f;
+        }
+        if (n < C) {   // tail chunk: padding rows are zero
+#pragma unroll
+            for (int x4 = 0; x4 < 4; ++x4) {
+                const int r = (tid + NT * x4) >> 4;
+                if (r >= n) pq[x4] = pk[x4] = zero_u4();
+            }
+#pragma unroll
+            for (int x2 = 0; x2 < 2; ++x2)
+                if ((tid + NT * x2) / VV >= n) pv[x2] = zero_u4();
         }
 #pragma unroll
         for (int x4 = 0; x4 < 4; ++x4) {
             const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
-            *reinterpret_cast<uint4*>(sm.q + r * PQ + col) = r < n ? pq[x4] : zero_u4();
-            *reinterpret_cast<uint4*>(sm.k + r * PQ + col) = r < n ? pk[x4] : zero_u4();
+            *reinterpret_cast<uint4*>(sm.q + r * PQ + col) = pq[x4];
+            *reinterpret_cast<uint4*>(sm.k + r * PQ + col) = pk[x4];
         }
 #pragma unroll
         for (int x2 = 0; x2 < 2; ++x2) {
             const int x = tid + NT * x2, r = x / VV, col = (x % VV) * 8;
-            if (x < C * VV) *reinterpret_cast<uint4*>(sm.v + r * PV + col) = r < n ? pv[x2] : zero_u4();
+            if (x < C * VV) *reinterpret_cast<uint4*>(sm.v + r * PV + col) = pv[x2];
             const int rt = x >> 3, ctl = (x & 7) * 8;
             *reinterpret_cast<uint4*>(sm.t + rt * PC + ctl) = pt[x2];
         }
@@ -372,10 +378,13 @@ __global__ __launch_bounds__(NT) void gdn_fwd_kernel(GdnArgs a) {
                                frag_kc(sm.q, PQ, 16 * rb, 32 * kk, lane), d);
                 const int r = 16 * rb + jl;
                 const float cr = sm.cum[r];
+                const float4 cs = *reinterpret_cast<const float4*>(sm.cum + 16 * sb + 4 * g);
+                const float csv[4] = {cs.x, cs.y, cs.z, cs.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int s = 16 * sb + 4 * g + j;
-                    d[j] = s <= r ? __expf(cr - sm.cum[s]) * d[j] : 0.f;
+                    const float e = fast_exp(cr - csv[j]) * d[j];
+                    d[j] = s <= r ? e : 0.f;
                 }
                 store_dT(sm.p, PC, 16 * sb, 16 * rb, d, lane);
             } else {
