@@ -115,6 +115,42 @@ __device__ __forceinline__ void gate8_val(const uint4 (&w)[2], float (&f)[8]) {
 
 __device__ __forceinline__ uint4 zero_u4() { return make_uint4(0, 0, 0, 0); }
 
+// Raw buffer access (stride 0) through a resource over [base, base + bytes): the
+// memory unit returns zero for loads at offsets >= bytes and drops such stores, so
+// ragged tails need no branches and every load and store is issued unconditionally
+// (which keeps the compiler's memory-counter waits exact across the chunk loop).
+// Offsets are byte offsets below 2^31.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld16(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint2 buf_ld8(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_ld4(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_ld2(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_st8(rsrc_t r, uint32_t off, uint2 v) {
+    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_st16(rsrc_t r, uint32_t off, uint4 v) {
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, 0);
+}
+// One gate element (bf16 or fp32 storage) as raw bits, converted with gate_val.
+template <bool GB>
+__device__ __forceinline__ uint32_t buf_ld_gate(rsrc_t r, uint32_t index) {
+    if constexpr (GB) return buf_ld2(r, index * 2u);
+    else return buf_ld4(r, index * 4u);
+}
+
 // Workgroup id -> (sequence, tile) with the tiles of one sequence on one XCD.
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8), each with its own
 // L2, so tiles that re-read the same q/k rows are placed at ids = xcd + 8 * slot.

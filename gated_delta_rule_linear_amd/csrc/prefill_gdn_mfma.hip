@@ -51,7 +51,9 @@ constexpr int PY = 32 + 8;     // pitch of the bf16 32-row scratch tiles
 
 struct __align__(16) PrepSmem {
     __align__(16) uint16_t k[C * PQ];
+    __align__(16) uint16_t q[C * PQ];
     __align__(16) uint16_t t[C * PC];      // T [r][s]
+    __align__(16) uint16_t p[C * PC];      // P [r][s] = exp(c_r - c_s) q_r.k_s, s <= r
     __align__(16) uint16_t lo[C * PC];     // off-diagonal blocks of L [r][s]
     __align__(16) uint16_t ya[2][32 * PY];  // level-a scratch: Y = L_ij T_jj (16 rows used)
     __align__(16) uint16_t yb[32 * PY];    // level-b scratch: Y = L[32:64, 0:32] A^{-1}
@@ -62,16 +64,11 @@ struct __align__(16) PrepSmem {
 template <int VT>
 struct __align__(16) FwdSmem {
     static constexpr int PV = VT + 8;
-    __align__(16) uint16_t q[C * PQ];
-    __align__(16) uint16_t k[C * PQ];
-    __align__(16) uint16_t st[VT * PQ];    // S^T [c][i], bf16
-    __align__(16) uint16_t v[C * PV];      // V [s][c]
+    __align__(16) uint16_t k[2][C * PQ];   // K [s][i] of the current and the next chunk
+    __align__(16) uint16_t st[VT * PQ];    // S^T [c][i], bf16 copy of the state tile
+    __align__(16) uint16_t x[C * PV];      // X [s][c]
     __align__(16) uint16_t u[C * PV];      // U [s][c]
     __align__(16) uint16_t uh[C * PV];     // U scaled by exp(c_last - c_s)
-    __align__(16) uint16_t p[C * PC];      // P [r][s]
-    __align__(16) uint16_t t[C * PC];      // T [r][s]
-    __align__(16) uint16_t xt[VT * PC];    // X^T [c][s]
-    float cum[C], gam[C], beta[C], dec[C];
 };
 
 struct GdnArgs {
@@ -80,7 +77,7 @@ struct GdnArgs {
     const float* S0;
     uint16_t* o;
     float* S;
-    uint16_t* T;   // workspace: [nseq][nchunks][64][64] bf16
+    uint16_t* T;   // workspace: [nseq][nchunks][2][64][64] bf16, T then P per chunk
     int N, nseq, ntiles, nchunks, gate_bf16;
 };
 
@@ -113,11 +110,12 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
     const size_t tok0 = seq * size_t(a.N);
 
     // loads from clamped rows (always valid), padding applied when staging
-    uint4 kv[4];
+    uint4 kv[4], qv[4];
 #pragma unroll
     for (int x4 = 0; x4 < 4; ++x4) {
         const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
         kv[x4] = ld_g16(a.k + (tok0 + t0 + min(r, n - 1)) * DK + col);
+        qv[x4] = ld_g16(a.q + (tok0 + t0 + min(r, n - 1)) * DK + col);
     }
     uint32_t graw = 0;
     if (w < 2) graw = ld_gate_raw<GB>(w == 0 ? a.alpha : a.beta, tok0 + t0 + min(lane, n - 1));
@@ -125,6 +123,7 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
     for (int x4 = 0; x4 < 4; ++x4) {
         const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
         *reinterpret_cast<uint4*>(sm.k + r * PQ + col) = r < n ? kv[x4] : zero_u4();
+        *reinterpret_cast<uint4*>(sm.q + r * PQ + col) = r < n ? qv[x4] : zero_u4();
     }
     if (w == 0) {
         const float lg = fast_log(gate_val<GB>(graw));
@@ -133,12 +132,14 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
     } else if (w == 1) {
         sm.beta[lane] = lane < n ? gate_val<GB>(graw) : 0.f;
     } else {
-        // zero the six upper blocks of T and the unused rows of the level-a scratch
+        // zero the six upper blocks of T and P and the unused rows of the level-a scratch
         const int r = lane >> 2, cc = (lane & 3) * 4;
         const int ub[6][2] = {{0, 1}, {0, 2}, {0, 3}, {1, 2}, {1, 3}, {2, 3}};
-        for (int x = w - 2; x < 6; x += 2)
-            *reinterpret_cast<uint2*>(sm.t + (16 * ub[x][0] + r) * PC + 16 * ub[x][1] + cc) =
-                make_uint2(0, 0);
+        for (int x = w - 2; x < 6; x += 2) {
+            const int off = (16 * ub[x][0] + r) * PC + 16 * ub[x][1] + cc;
+            *reinterpret_cast<uint2*>(sm.t + off) = make_uint2(0, 0);
+            *reinterpret_cast<uint2*>(sm.p + off) = make_uint2(0, 0);
+        }
         uint16_t* y = sm.ya[w - 2];
         for (int x = lane; x < 32 * PY / 4; x += 64) *reinterpret_cast<uint2*>(y + 4 * x) = make_uint2(0, 0);
     }
@@ -190,19 +191,36 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
         for (int r = 0; r < 16; ++r) sm.t[(16 * b + r) * PC + 16 * b + jc] = f32_to_bf16(tc[r]);
     } else {
         // waves 1..3: the six off-diagonal L blocks (bf16): D'[s][r] = k_s . k_r -> lo[r][s..]
-        for (int task = w - 1; task < 6; task += 3) {
-            const int rb = task < 1 ? 1 : task < 3 ? 2 : 3;
-            const int sb = task - (rb * (rb - 1)) / 2;
+        // and the ten lower blocks of P: D'[s][r] = k_s . q_r -> p[r][s..]
+        for (int task = w - 1; task < 16; task += 3) {
+            const bool is_p = task >= 6;
+            const int pt = is_p ? task - 6 : task;
+            int rb, sb;
+            if (is_p) {
+                rb = pt < 1 ? 0 : pt < 3 ? 1 : pt < 6 ? 2 : 3;
+                sb = pt - (rb * (rb + 1)) / 2;
+            } else {
+                rb = pt < 1 ? 1 : pt < 3 ? 2 : 3;
+                sb = pt - (rb * (rb - 1)) / 2;
+            }
+            const uint16_t* rsrc = is_p ? sm.q : sm.k;
             f32x4_t d = zero4();
 #pragma unroll
             for (int kk = 0; kk < DK / 32; ++kk)
                 d = mfma16(frag_kc(sm.k, PQ, 16 * sb, 32 * kk, lane),
-                           frag_kc(sm.k, PQ, 16 * rb, 32 * kk, lane), d);
+                           frag_kc(rsrc, PQ, 16 * rb, 32 * kk, lane), d);
             const int r = 16 * rb + jl;
-            const float br = sm.beta[r], cr = sm.cum[r];
+            const float cr = sm.cum[r];
+            const float br = is_p ? 1.f : sm.beta[r];
+            const float4 cs = *reinterpret_cast<const float4*>(sm.cum + 16 * sb + 4 * g);
+            const float csv[4] = {cs.x, cs.y, cs.z, cs.w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) d[j] *= br * fast_exp(cr - sm.cum[16 * sb + 4 * g + j]);
-            store_dT(sm.lo, PC, 16 * sb, 16 * rb, d, lane);
+            for (int j = 0; j < 4; ++j) {
+                const int s = 16 * sb + 4 * g + j;
+                const float e = br * fast_exp(cr - csv[j]) * d[j];
+                d[j] = s <= r ? e : 0.f;   // L blocks are strictly below the diagonal
+            }
+            store_dT(is_p ? sm.p : sm.lo, PC, 16 * sb, 16 * rb, d, lane);
         }
     }
     lds_barrier();
@@ -237,35 +255,111 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
         store_dT(sm.t, PC, 16 * jb, 32 + 16 * rb, -d, lane);
     }
     lds_barrier();
-    uint16_t* Tg = a.T + (seq * a.nchunks + ch) * size_t(C * C);
+    // T then P, each in fragment order: 16-byte piece (rb, kk, lane = 16 g + j) holds
+    // row 16 rb + j, columns 32 kk + 8 g .. + 7, so that a wave of the forward kernel
+    // reads its B fragment as one contiguous kilobyte
+    uint16_t* Tg = a.T + (seq * a.nchunks + ch) * size_t(2 * C * C);
 #pragma unroll
     for (int x2 = 0; x2 < 2; ++x2) {
-        const int x = tid + NT * x2, r = x >> 3, col = (x & 7) * 8;
-        *reinterpret_cast<uint4*>(Tg + r * C + col) = *reinterpret_cast<const uint4*>(sm.t + r * PC + col);
+        const int x = tid + NT * x2, rb = x >> 7, kk = (x >> 6) & 1, l = x & 63;
+        const int off = (16 * rb + (l & 15)) * PC + 32 * kk + 8 * (l >> 4);
+        *reinterpret_cast<uint4*>(Tg + 8 * x) = *reinterpret_cast<const uint4*>(sm.t + off);
+        *reinterpret_cast<uint4*>(Tg + C * C + 8 * x) = *reinterpret_cast<const uint4*>(sm.p + off);
     }
 }
 
 // ---------------------------------------------------------------------------
 // forward kernel
 // ---------------------------------------------------------------------------
-template <int VT, bool GB>
-__global__ __launch_bounds__(NT) void gdn_fwd_kernel(GdnArgs a) {
-    constexpr int NVT = VT / 16;
+// Value columns of a wave's 16 NVT-column slice as seen by its column tiles: tile ct,
+// tile-local index j (0..15) -> column. With NVT = 2 the lane group g of a D tile (rows
+// 4 g .. 4 g + 3) owns the 8 contiguous columns 8 g .. 8 g + 7 across both tiles, so V
+// is loaded and O stored with 16-byte accesses. colmap(ct, 4 q + e) = colmap(ct, 4 q) + e.
+template <int NVT>
+__device__ __forceinline__ int colmap(int ct, int j) {
+    if constexpr (NVT == 2) return 8 * (j >> 2) + 4 * ct + (j & 3);
+    else return 16 * ct + j;
+}
+// Fragment from a row-major [K rows][columns] tile whose M/N index is tile ct's columns
+// (LDS transpose read; each lane quad addresses 4 consecutive columns).
+template <int NVT>
+__device__ __forceinline__ bf16x8_t frag_kr_cols(const uint16_t* t, int pitch, int k0, int cb,
+                                                 int ct, int lane) {
+    const int g = lane >> 4, L = lane & 15;
+    const uint16_t* p = t + (k0 + g * 8 + (L >> 2)) * pitch + cb + colmap<NVT>(ct, 4 * (L & 3));
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 4 * pitch));
+    const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+// Fragment from a row-major [columns][K] tile (S^T) whose M index is tile ct's columns.
+template <int NVT>
+__device__ __forceinline__ bf16x8_t frag_st(const uint16_t* t, int pitch, int cb, int ct, int k0,
+                                            int lane) {
+    return *reinterpret_cast<const bf16x8_t*>(t + (cb + colmap<NVT>(ct, lane & 15)) * pitch + k0 +
+                                              (lane >> 4) * 8);
+}
+// D tile [M = tile ct's columns][N = rows n0 ..] to a row-major [rows][columns] tile.
+template <int NVT>
+__device__ __forceinline__ void store_rows(uint16_t* t, int pitch, int cb, int ct, int n0,
+                                           f32x4_t d, int lane) {
+    uint2 w;
+    w.x = pack_bf16x2(d[0], d[1]);
+    w.y = pack_bf16x2(d[2], d[3]);
+    *reinterpret_cast<uint2*>(t + (n0 + (lane & 15)) * pitch + cb +
+                              colmap<NVT>(ct, 4 * (lane >> 4))) = w;
+}
+// D tile [M = key rows i0 ..][N = tile ct's columns] to the [columns][keys] tile S^T.
+template <int NVT>
+__device__ __forceinline__ void store_st(uint16_t* t, int pitch, int i0, int cb, int ct,
+                                         f32x4_t d, int lane) {
+    uint2 w;
+    w.x = pack_bf16x2(d[0], d[1]);
+    w.y = pack_bf16x2(d[2], d[3]);
+    *reinterpret_cast<uint2*>(t + (cb + colmap<NVT>(ct, lane & 15)) * pitch + i0 +
+                              4 * (lane >> 4)) = w;
+}
+
+// Per-chunk operands a wave reads straight from global memory in MFMA fragment layout
+// (lane = 16 g + j): rows 16 rb + j of q, T and P, K halves 8 g .. 8 g + 7 of each
+// 32-wide slice; V at the X tile's D layout; the chunk's alpha / beta at lane = token;
+// and this thread's share of the chunk's K rows for the LDS copy.
+template <int NVT, int KST>
+struct ChunkRegs {
+    uint4 q[4], t[2], p[2], kst[KST];
+    uint2 v[NVT];
+    uint32_t ga, gb;
+};
+
+// Forward kernel. A workgroup owns VT = 16 NVT CG value columns of one sequence and
+// runs 4 CG waves: wave w works on row block rb = w % 4 of every chunk (rows of q, T, P,
+// key rows 32 rb .. of S) for column group cg = w / 4 (16 NVT columns). The CG column
+// groups share the LDS copy of K and load the same q / T / P lines, so a wider group
+// cuts the vector-memory traffic per column.
+template <int NVT, int CG, bool GB>
+__global__ __launch_bounds__(NT * CG) void gdn_fwd_kernel(GdnArgs a) {
+    constexpr int VT = 16 * NVT * CG;
+    constexpr int NTW = NT * CG;          // threads per workgroup
+    constexpr int KST = (C * DK / 8) / NTW;   // 16-byte K pieces per thread
     constexpr int PV = FwdSmem<VT>::PV;
-    constexpr int VV = VT / 8;  // 16-byte vectors per V row
     extern __shared__ __align__(16) unsigned char smem_raw[];
     FwdSmem<VT>& sm = *reinterpret_cast<FwdSmem<VT>*>(smem_raw);
 
     const XcdMap mp = xcd_map(blockIdx.x, a.ntiles, a.nseq);
     if (!mp.valid) return;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int rb = w & 3, cg = w >> 2;
     const int g = lane >> 4, jl = lane & 15;
     const int DV = a.ntiles * VT;
-    const int c0 = mp.tile * VT;
+    const int cw = 16 * NVT * cg;      // first column of this wave, within the tile
+    const int c0 = mp.tile * VT + cw;  // ... and within the row
     const size_t seq = size_t(mp.seq);
     const size_t tok0 = seq * size_t(a.N);
+    const int nchunks = a.nchunks;
+    const int rw = 16 * rb + jl;       // this lane's row of the wave's 16-row block
+    const int nk = rb < 2 ? 1 : 2;     // T and P vanish for s >= 16 (rb + 1)
 
-    // state tiles held by this wave: key blocks 2w + ib, column tiles ct
+    // state tiles held by this wave: key blocks 2 rb + ib, column tiles ct (D layout)
     f32x4_t S[2][NVT];
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
@@ -273,192 +367,186 @@ __global__ __launch_bounds__(NT) void gdn_fwd_kernel(GdnArgs a) {
         for (int ct = 0; ct < NVT; ++ct)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int i = 16 * (2 * w + ib) + 4 * g + j, c = 16 * ct + jl;
+                const int i = 16 * (2 * rb + ib) + 4 * g + j, c = colmap<NVT>(ct, jl);
                 S[ib][ct][j] = a.S0 ? a.S0[seq * DK * DV + size_t(i) * DV + c0 + c] : 0.f;
             }
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-        for (int ct = 0; ct < NVT; ++ct) store_dT(sm.st, PQ, 16 * (2 * w + ib), 16 * ct, S[ib][ct], lane);
-    // zero, once, the P tiles above the diagonal that the row-block products read
-    if (w < 2) {
-        const int rb = w == 0 ? 0 : 2, sb = rb + 1;
-        const int r = 16 * rb + (lane >> 2), s = 16 * sb + (lane & 3) * 4;
-        *reinterpret_cast<uint2*>(sm.p + r * PC + s) = make_uint2(0, 0);
-    }
+        for (int ct = 0; ct < NVT; ++ct)
+            store_st<NVT>(sm.st, PQ, 16 * (2 * rb + ib), cw, ct, S[ib][ct], lane);
 
-    // register prefetch of one chunk: loads from clamped rows (always valid) without
-    // control flow, so nothing waits on them until the next chunk is staged
-    uint4 pq[4], pk[4], pv[2], pt[2];
-    uint32_t pg = 0;
-    auto load_chunk = [&](int ch) {
-        const int t0 = ch * C, n = min(C, a.N - t0);
+    // Per-sequence buffer resources: rows past the end of the sequence read as zero
+    // (the ragged last chunk's padding) and o rows past it are dropped on store.
+    const rsrc_t rq = make_rsrc(a.q + tok0 * DK, uint32_t(a.N) * DK * 2u);
+    const rsrc_t rk = make_rsrc(a.k + tok0 * DK, uint32_t(a.N) * DK * 2u);
+    const rsrc_t rv = make_rsrc(a.v + tok0 * DV, uint32_t(a.N) * uint32_t(DV) * 2u);
+    const rsrc_t ro = make_rsrc(a.o + tok0 * DV, uint32_t(a.N) * uint32_t(DV) * 2u);
+    const rsrc_t rt = make_rsrc(a.T + seq * nchunks * size_t(2 * C * C),
+                                uint32_t(nchunks) * (2u * C * C * 2u));
+    constexpr uint32_t GS = GB ? 2u : 4u;
+    const rsrc_t ra = make_rsrc(static_cast<const char*>(a.alpha) + tok0 * GS, uint32_t(a.N) * GS);
+    const rsrc_t rb_ = make_rsrc(static_cast<const char*>(a.beta) + tok0 * GS, uint32_t(a.N) * GS);
+
+    // loads of one chunk, all unconditional (a chunk index past the end reads zeros);
+    // K first, since its LDS copy is written before the other operands are needed
+    auto load_chunk = [&](ChunkRegs<NVT, KST>& R, int ch) {
+        const uint32_t t0 = uint32_t(ch) * C;
 #pragma unroll
-        for (int x4 = 0; x4 < 4; ++x4) {
-            const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
-            const size_t e = (tok0 + t0 + min(r, n - 1)) * DK + col;
-            pq[x4] = ld_g16(a.q + e);
-            pk[x4] = ld_g16(a.k + e);
+        for (int x4 = 0; x4 < KST; ++x4) {
+            const int x = tid + NTW * x4, r = x >> 4, col = (x & 15) * 8;
+            R.kst[x4] = buf_ld16(rk, ((t0 + r) * DK + col) * 2u);
         }
+        const uint32_t oq = ((t0 + rw) * DK + 8 * g) * 2u;
 #pragma unroll
-        for (int x2 = 0; x2 < 2; ++x2) {
-            const int x = tid + NT * x2, r = x / VV, col = (x % VV) * 8;
-            if (x < C * VV) pv[x2] = ld_g16(a.v + (tok0 + t0 + min(r, n - 1)) * DV + c0 + col);
-            const int rt = x >> 3, ctl = (x & 7) * 8;
-            pt[x2] = ld_g16(a.T + (seq * a.nchunks + ch) * size_t(C * C) + rt * C + ctl);
+        for (int kk = 0; kk < 4; ++kk) R.q[kk] = buf_ld16(rq, oq + 64u * kk);
+        const uint32_t ot = (uint32_t(ch) * (2 * C * C) + (2 * rb * 64 + lane) * 8) * 2u;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            R.t[kk] = buf_ld16(rt, ot + 1024u * kk);
+            R.p[kk] = buf_ld16(rt, ot + (C * C) * 2u + 1024u * kk);
         }
-        if (tid < 2 * C)
-            pg = ld_gate_raw<GB>(tid < C ? a.alpha : a.beta, tok0 + t0 + min(tid & (C - 1), n - 1));
+        const uint32_t ov = ((t0 + rw) * uint32_t(DV) + c0 + colmap<NVT>(0, 4 * g)) * 2u;
+        if constexpr (NVT == 2) {
+            const uint4 v4 = buf_ld16(rv, ov);
+            R.v[0] = make_uint2(v4.x, v4.y);
+            R.v[1] = make_uint2(v4.z, v4.w);
+        } else {
+            R.v[0] = buf_ld8(rv, ov);
+        }
+        R.ga = buf_ld_gate<GB>(ra, t0 + lane);
+        R.gb = buf_ld_gate<GB>(rb_, t0 + lane);
+        // keep each chunk's loads together and in program order: the memory-counter
+        // waits before a chunk is used count the loads issued after it
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto stage_k = [&](const ChunkRegs<NVT, KST>& R, uint16_t* kb) {
+#pragma unroll
+        for (int x4 = 0; x4 < KST; ++x4) {
+            const int x = tid + NTW * x4, r = x >> 4, col = (x & 15) * 8;
+            *reinterpret_cast<uint4*>(kb + r * PQ + col) = R.kst[x4];
+        }
     };
 
-    const int nchunks = a.nchunks;
-    if (nchunks > 0) load_chunk(0);
-    lds_barrier();
-
-    for (int ch = 0; ch < nchunks; ++ch) {
+    auto process = [&](const ChunkRegs<NVT, KST>& R, const ChunkRegs<NVT, KST>& Rn, int ch,
+                       int cur) {
         const int t0 = ch * C, n = min(C, a.N - t0);
-        // ---- stage: gates (wave 0 scans log alpha, wave 1 holds beta), q, k, v, T
-        if (w == 0) {
-            const float lg = fast_log(gate_val<GB>(pg));
-            const float x = scan64(lane < n ? lg : 0.f, lane);
-            const float clast = __shfl(x, 63, 64);
-            sm.cum[lane] = x;
-            sm.gam[lane] = fast_exp(x);
-            sm.dec[lane] = fast_exp(clast - x);
-        } else if (w == 1) {
-            sm.beta[lane] = lane < n ? gate_val<GB>(pg) : 0.f;
-        }
-        if (n < C) {   // tail chunk: padding rows are zero
-#pragma unroll
-            for (int x4 = 0; x4 < 4; ++x4) {
-                const int r = (tid + NT * x4) >> 4;
-                if (r >= n) pq[x4] = pk[x4] = zero_u4();
-            }
-#pragma unroll
-            for (int x2 = 0; x2 < 2; ++x2)
-                if ((tid + NT * x2) / VV >= n) pv[x2] = zero_u4();
-        }
-#pragma unroll
-        for (int x4 = 0; x4 < 4; ++x4) {
-            const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
-            *reinterpret_cast<uint4*>(sm.q + r * PQ + col) = pq[x4];
-            *reinterpret_cast<uint4*>(sm.k + r * PQ + col) = pk[x4];
-        }
-#pragma unroll
-        for (int x2 = 0; x2 < 2; ++x2) {
-            const int x = tid + NT * x2, r = x / VV, col = (x % VV) * 8;
-            if (x < C * VV) *reinterpret_cast<uint4*>(sm.v + r * PV + col) = pv[x2];
-            const int rt = x >> 3, ctl = (x & 7) * 8;
-            *reinterpret_cast<uint4*>(sm.t + rt * PC + ctl) = pt[x2];
-        }
-        lds_barrier();
-        if (ch + 1 < nchunks) load_chunk(ch + 1);
+        const uint16_t* kc = sm.k[cur];
+        // gates: every wave scans log alpha itself (lane = token); lane (g, j) then
+        // takes the values of token 16 rb + j
+        const float lg = fast_log(gate_val<GB>(R.ga));
+        const float cum = wave_inclusive_scan(lane < n ? lg : 0.f);
+        const float clast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), 63));
+        const float braw = gate_val<GB>(R.gb);
+        const float cr = __shfl(cum, rw, 64);
+        const float br = rw < n ? __shfl(braw, rw, 64) : 0.f;
+        const float gr = fast_exp(cr);
+        const float dr = fast_exp(clast - cr);
+        const float glast = fast_exp(clast);
 
-        // ---- O^T = S^T Q^T for row block w (scaled by gamma later); P and X tiles
-        f32x4_t oacc[NVT];
+        // ---- (S^T Q^T) and (S^T K^T) for rows 16 rb .. : D[c][r]; the S^T fragment
+        // is shared by both products
+        f32x4_t oq[NVT], ks[NVT];
+#pragma unroll
+        for (int ct = 0; ct < NVT; ++ct) { oq[ct] = zero4(); ks[ct] = zero4(); }
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+            const bf16x8_t kf = frag_kc(kc, PQ, 16 * rb, 32 * kk, lane);
+            const bf16x8_t qf = __builtin_bit_cast(bf16x8_t, R.q[kk]);   // rows >= n unused
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct) {
+                const bf16x8_t sf = frag_st<NVT>(sm.st, PQ, cw, ct, 32 * kk, lane);
+                oq[ct] = mfma16(sf, qf, oq[ct]);
+                ks[ct] = mfma16(sf, kf, ks[ct]);
+            }
+        }
+        // ---- X[s][c] = beta_s (v_s,c - gamma_s (S^T k_s)_c), s = 16 rb + j
 #pragma unroll
         for (int ct = 0; ct < NVT; ++ct) {
-            f32x4_t o_ = zero4();
+            const uint2 vv = R.v[ct];
+            const float vf[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
+                                 __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
+            f32x4_t x_;
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk)
-                o_ = mfma16(frag_kc(sm.st, PQ, 16 * ct, 32 * kk, lane),
-                            frag_kc(sm.q, PQ, 16 * w, 32 * kk, lane), o_);   // D[c][r]
-            oacc[ct] = o_;
-        }
-        constexpr int NTASK = 10 + 4 * NVT;
-        for (int task = w; task < NTASK; task += 4) {
-            if (task < 10) {
-                // P tile (rb, sb), sb <= rb: D'[s][r] = k_s . q_r -> p[r][s..]
-                const int rb = task < 1 ? 0 : task < 3 ? 1 : task < 6 ? 2 : 3;
-                const int sb = task - (rb * (rb + 1)) / 2;
-                f32x4_t d = zero4();
-#pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk)
-                    d = mfma16(frag_kc(sm.k, PQ, 16 * sb, 32 * kk, lane),
-                               frag_kc(sm.q, PQ, 16 * rb, 32 * kk, lane), d);
-                const int r = 16 * rb + jl;
-                const float cr = sm.cum[r];
-                const float4 cs = *reinterpret_cast<const float4*>(sm.cum + 16 * sb + 4 * g);
-                const float csv[4] = {cs.x, cs.y, cs.z, cs.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int s = 16 * sb + 4 * g + j;
-                    const float e = fast_exp(cr - csv[j]) * d[j];
-                    d[j] = s <= r ? e : 0.f;
-                }
-                store_dT(sm.p, PC, 16 * sb, 16 * rb, d, lane);
-            } else {
-                // X tile (s block sb, column tile ct): X = beta (V - gamma K S)
-                const int xi = task - 10, sb = xi / NVT, ct = xi % NVT;
-                f32x4_t d = zero4();
-#pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk)
-                    d = mfma16(frag_kc(sm.k, PQ, 16 * sb, 32 * kk, lane),
-                               frag_kc(sm.st, PQ, 16 * ct, 32 * kk, lane), d);   // D[s][c]
-                const int c = 16 * ct + jl;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int s = 16 * sb + 4 * g + j;
-                    d[j] = sm.beta[s] * (bf16_to_f32(sm.v[s * PV + c]) - sm.gam[s] * d[j]);
-                }
-                store_dT(sm.xt, PC, 16 * sb, 16 * ct, d, lane);   // X^T[c][s]
-            }
+            for (int j = 0; j < 4; ++j) x_[j] = br * (vf[j] - gr * ks[ct][j]);
+            store_rows<NVT>(sm.x, PV, cw, ct, 16 * rb, x_, lane);   // X[s][c]
         }
         lds_barrier();
 
-        // ---- U^T = X^T T^T (row block w): U and U scaled by exp(c_last - c_r)
-        const int nk = w < 2 ? 1 : 2;   // T and P vanish for s >= 16 (w + 1)
-        {
-            const int r = 16 * w + jl;
-            const float dr = sm.dec[r];
+        // ---- U^T = X^T T^T for rows 16 rb .. : D[c][r] -> U[r][c], U^[r][c]
 #pragma unroll
-            for (int ct = 0; ct < NVT; ++ct) {
-                f32x4_t u_ = zero4();
-                for (int kk = 0; kk < nk; ++kk)
-                    u_ = mfma16(frag_kc(sm.xt, PC, 16 * ct, 32 * kk, lane),
-                                frag_kc(sm.t, PC, 16 * w, 32 * kk, lane), u_);   // D[c][r]
-                store_dT(sm.u, PV, 16 * ct, 16 * w, u_, lane);                       // U[r][c]
-                store_dT(sm.uh, PV, 16 * ct, 16 * w, u_ * dr, lane);
-            }
+        for (int ct = 0; ct < NVT; ++ct) {
+            f32x4_t u_ = mfma16(frag_kr_cols<NVT>(sm.x, PV, 0, cw, ct, lane),
+                                __builtin_bit_cast(bf16x8_t, R.t[0]), zero4());
+            if (nk > 1)
+                u_ = mfma16(frag_kr_cols<NVT>(sm.x, PV, 32, cw, ct, lane),
+                            __builtin_bit_cast(bf16x8_t, R.t[1]), u_);
+            store_rows<NVT>(sm.u, PV, cw, ct, 16 * rb, u_, lane);
+            store_rows<NVT>(sm.uh, PV, cw, ct, 16 * rb, u_ * dr, lane);
         }
         lds_barrier();
 
-        // ---- O^T = gamma O^T + U^T P^T -> o;  S = gamma_last S + K^T U^
+        // ---- O^T = gamma_r (S^T Q^T) + U^T P^T -> o rows 16 rb ..
+        uint2 ow[NVT];
+#pragma unroll
+        for (int ct = 0; ct < NVT; ++ct) {
+            f32x4_t o_ = mfma16(frag_kr_cols<NVT>(sm.u, PV, 0, cw, ct, lane),
+                                __builtin_bit_cast(bf16x8_t, R.p[0]), oq[ct] * gr);
+            if (nk > 1)
+                o_ = mfma16(frag_kr_cols<NVT>(sm.u, PV, 32, cw, ct, lane),
+                            __builtin_bit_cast(bf16x8_t, R.p[1]), o_);
+            ow[ct].x = pack_bf16x2(o_[0], o_[1]);
+            ow[ct].y = pack_bf16x2(o_[2], o_[3]);
+        }
         {
-            const int r = 16 * w + jl;
-            const float gr = sm.gam[r];
+            const uint32_t oo = ((uint32_t(t0) + rw) * uint32_t(DV) + c0 + colmap<NVT>(0, 4 * g)) * 2u;
+            if constexpr (NVT == 2) buf_st16(ro, oo, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
+            else buf_st8(ro, oo, ow[0]);
+        }
+        // ---- S = gamma_last S + K^T U^ (key rows 32 rb ..), bf16 copy to st
+        bf16x8_t uf[2][NVT];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct)
+                uf[kk][ct] = frag_kr_cols<NVT>(sm.uh, PV, 32 * kk, cw, ct, lane);
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+            const int i0 = 16 * (2 * rb + ib);
+            const bf16x8_t kt0 = frag_kr(kc, PQ, 0, i0, lane);
+            const bf16x8_t kt1 = frag_kr(kc, PQ, 32, i0, lane);
 #pragma unroll
             for (int ct = 0; ct < NVT; ++ct) {
-                f32x4_t o_ = oacc[ct] * gr;
-                for (int kk = 0; kk < nk; ++kk)
-                    o_ = mfma16(frag_kr(sm.u, PV, 32 * kk, 16 * ct, lane),
-                                frag_kc(sm.p, PC, 16 * w, 32 * kk, lane), o_);
-                if (r < n) {
-                    uint2 wv;
-                    wv.x = pack_bf16x2(o_[0], o_[1]);
-                    wv.y = pack_bf16x2(o_[2], o_[3]);
-                    *reinterpret_cast<uint2*>(a.o + (tok0 + t0 + r) * DV + c0 + 16 * ct + 4 * g) = wv;
-                }
+                f32x4_t s_ = S[ib][ct] * glast;
+                s_ = mfma16(kt0, uf[0][ct], s_);
+                s_ = mfma16(kt1, uf[1][ct], s_);
+                S[ib][ct] = s_;
+                store_st<NVT>(sm.st, PQ, i0, cw, ct, s_, lane);
             }
         }
-        {
-            const float gl = sm.gam[C - 1];
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const int i0 = 16 * (2 * w + ib);
-#pragma unroll
-                for (int ct = 0; ct < NVT; ++ct) {
-                    f32x4_t s_ = S[ib][ct] * gl;
-#pragma unroll
-                    for (int kk = 0; kk < C / 32; ++kk)
-                        s_ = mfma16(frag_kr(sm.k, PQ, 32 * kk, i0, lane),
-                                    frag_kr(sm.uh, PV, 32 * kk, 16 * ct, lane), s_);
-                    S[ib][ct] = s_;
-                    store_dT(sm.st, PQ, i0, 16 * ct, s_, lane);
-                }
-            }
-        }
+        // next chunk's K into the other buffer (its readers finished before the
+        // previous barrier)
+        stage_k(Rn, sm.k[cur ^ 1]);
         lds_barrier();
+    };
+
+    // three register sets rotate so that each chunk's loads are issued two chunks
+    // before it is processed (one chunk of compute is shorter than the memory latency)
+    ChunkRegs<NVT, KST> RA, RB, RC;
+    load_chunk(RA, 0);
+    load_chunk(RB, 1);
+    stage_k(RA, sm.k[0]);
+    lds_barrier();
+    // whole triples only: a chunk past the end reads zeros (alpha = beta = 0 masked to
+    // the identity step, T = 0), leaves the state unchanged and stores nothing, so no
+    // exit sits between the triple's memory operations
+    for (int ch = 0; ch < nchunks; ch += 3) {
+        load_chunk(RC, ch + 2);
+        process(RA, RB, ch, ch & 1);
+        load_chunk(RA, ch + 3);
+        process(RB, RC, ch + 1, (ch + 1) & 1);
+        load_chunk(RB, ch + 4);
+        process(RC, RA, ch + 2, ch & 1);
     }
 
 #pragma unroll
@@ -467,7 +555,7 @@ __global__ __launch_bounds__(NT) void gdn_fwd_kernel(GdnArgs a) {
         for (int ct = 0; ct < NVT; ++ct)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int i = 16 * (2 * w + ib) + 4 * g + j, c = 16 * ct + jl;
+                const int i = 16 * (2 * rb + ib) + 4 * g + j, c = colmap<NVT>(ct, jl);
                 a.S[seq * DK * DV + size_t(i) * DV + c0 + c] = S[ib][ct][j];
             }
 }
@@ -490,8 +578,9 @@ GdnArgs make_args(const Problem& p) {
     return a;
 }
 
-template <int VT, bool GB>
-hipError_t launch_vt(const Problem& p) {
+template <int NVT, int CG, bool GB>
+hipError_t launch_cfg(const Problem& p) {
+    constexpr int VT = 16 * NVT * CG;
     GdnArgs a = make_args(p);
     a.ntiles = p.dv / VT;
     hipError_t e;
@@ -506,11 +595,17 @@ hipError_t launch_vt(const Problem& p) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const size_t smem = sizeof(FwdSmem<VT>);
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gdn_fwd_kernel<VT, GB>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gdn_fwd_kernel<NVT, CG, GB>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
     if (e != hipSuccess) return e;
-    gdn_fwd_kernel<VT, GB><<<dim3(xcd_grid(a.ntiles, a.nseq)), dim3(NT), smem, p.stream>>>(a);
+    gdn_fwd_kernel<NVT, CG, GB>
+        <<<dim3(xcd_grid(a.ntiles, a.nseq)), dim3(NT * CG), smem, p.stream>>>(a);
     return hipGetLastError();
+}
+
+template <bool GB>
+hipError_t launch_gb(const Problem& p, bool wide) {
+    return wide ? launch_cfg<2, 1, GB>(p) : launch_cfg<1, 1, GB>(p);
 }
 
 }  // namespace
@@ -521,18 +616,21 @@ bool gdn_mfma_supported(int dk, int dv, bool io_bf16) {
 
 size_t gdn_mfma_workspace_bytes(const Problem& p) {
     const size_t nchunks = size_t((p.N + C - 1) / C);
-    return size_t(p.B) * size_t(p.H) * nchunks * C * C * sizeof(uint16_t);
+    return size_t(p.B) * size_t(p.H) * nchunks * 2 * C * C * sizeof(uint16_t);
 }
 
 hipError_t launch_prefill_gdn_mfma(const Problem& p) {
     const size_t nseq = size_t(p.B) * size_t(p.H);
     if (nseq > (1u << 26) || !p.ws) return hipErrorInvalidValue;
-    // value tile: 16 columns keeps the forward kernel's LDS under half a CU, so two
-    // workgroups share each CU and hide each other's barrier and LDS latency; 32
-    // columns only when 16 would leave more than two waves of workgroups per CU
-    const bool wide = p.dv >= 32 && nseq * size_t(p.dv / 16) > 2048;
-    if (p.gate_bf16) return wide ? launch_vt<32, true>(p) : launch_vt<16, true>(p);
-    return wide ? launch_vt<32, false>(p) : launch_vt<16, false>(p);
+    // Forward shape: each value tile is an independent chain of chunks, so the tile
+    // count sets the parallelism, while every tile re-reads the chunk's q, K, T and P
+    // through the vector memory path, whose request rate bounds the loop. 32-column
+    // tiles on 4 waves (one workgroup per CU at 64 sequences x 128 columns) halve that
+    // traffic per column and measure faster than 16-column tiles at two per CU, or
+    // 32-column tiles on 8 waves.
+    const bool wide = p.dv >= 32;
+    if (p.gate_bf16) return launch_gb<true>(p, wide);
+    return launch_gb<false>(p, wide);
 }
 
 }  // namespace la
