@@ -21,20 +21,24 @@
 // the off-diagonal products run on the matrix cores in bf16 with fp32 accumulation.
 //
 // Two kernels:
-//   prep     one workgroup per (sequence, chunk), fully parallel: L and T = (I + L)^{-1}
-//            for every chunk, written to the workspace in bf16 (T depends only on the
-//            chunk's k, alpha, beta, never on the state);
-//   forward  one workgroup per (sequence, value tile of VT columns): walks the chunks
-//            in order with its fp32 state tile in registers (MFMA accumulators).
-//            Columns of S never mix, so value tiles are independent chains; the tiles
-//            of one sequence share an XCD so their q/k/T reads hit the same L2.
-// Taking the triangular inverse out of the sequential loop leaves that loop four
-// barriers per chunk of pure matrix-core work; the cost is one extra pass over k
-// and a 64 x 64 bf16 T per chunk in HBM.
+//   prep     one workgroup per (sequence, chunk), fully parallel: T = (I + L)^{-1} and
+//            the decayed, causally masked score tile P_rs = exp(c_r - c_s) q_r.k_s
+//            (s <= r) of every chunk, written to the workspace in bf16 and in MFMA
+//            fragment order (neither depends on the state);
+//   forward  one workgroup per (sequence, value tile): walks the chunks in order with
+//            its fp32 state tile in MFMA accumulators. Columns of S never mix, so value
+//            tiles are independent chains; the tiles of one sequence share an XCD so
+//            their q/k/T/P reads hit the same L2.
+// Per chunk the forward kernel has three barriers: (S^T q, S^T k) -> X | U = T X |
+// O = gamma (S^T q) + P U and S = gamma_last S + K^T U^. Each wave loads the
+// operands that only it uses (rows of T, P, V; its own alpha/beta) straight into
+// registers in fragment layout through per-sequence buffer resources, two chunks
+// ahead; K and the bf16 copy of S^T are shared through LDS. Ragged tails need no
+// branches: buffer loads past the sequence read zeros and stores past it are
+// dropped.
 //
-// MFMA products are arranged so that result tiles are written to LDS transposed
-// (8-byte writes) and read back as contiguous 16-byte fragments; fragments whose K
-// index runs along tile rows use the LDS transpose read.
+// Fragments whose K index runs along tile rows use the LDS transpose read; result
+// tiles are written to LDS with 8-byte stores.
 #include "la_internal.h"
 #include "mfma.hpp"
 
