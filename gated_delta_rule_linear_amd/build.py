@@ -29,7 +29,7 @@ COMMON = [
 ]
 
 SOURCES = ["la_api.cpp", "decode.hip", "prefill_valu.hip", "prefill_diag_mfma.hip",
-           "prefill_gdn_mfma.hip"]
+           "prefill_gla_mfma.hip", "prefill_gdn_mfma.hip"]
 
 
 def _compile(src: str) -> str:

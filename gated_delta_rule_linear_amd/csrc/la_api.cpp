@@ -100,9 +100,9 @@ int plan_prefill(const la_desc& d, Problem& p) {
     p.io_bf16 = d.io_dtype == LA_BF16;
     p.gate_bf16 = d.gate_dtype == LA_BF16;
     p.eps = d.eps;
-    const bool mfma_ok = d.variant == LA_GDN
-                             ? la::gdn_mfma_supported(d.dk, d.dv, p.io_bf16)
-                             : la::diag_mfma_supported(d.variant, d.dk, d.dv, p.io_bf16);
+    const bool mfma_ok = d.variant == LA_GDN   ? la::gdn_mfma_supported(d.dk, d.dv, p.io_bf16)
+                         : d.variant == LA_GLA ? la::gla_mfma_supported(d.dk, d.dv, p.io_bf16)
+                                               : la::diag_mfma_supported(d.variant, d.dk, d.dv, p.io_bf16);
     int path = d.path;
     if (path == LA_PATH_AUTO) path = mfma_ok ? LA_PATH_MFMA : LA_PATH_VALU;
     if (path == LA_PATH_MFMA && !mfma_ok) return LA_ERR_UNSUPPORTED;
@@ -112,7 +112,9 @@ int plan_prefill(const la_desc& d, Problem& p) {
     p.segments = 1;
     if (path == LA_PATH_MFMA && d.variant != LA_GDN && d.N > 0) {
         const int nchunks = (d.N + p.chunk - 1) / p.chunk;
-        int segs = d.segments > 0 ? d.segments : la::diag_mfma_auto_segments(p);
+        int segs = d.segments > 0                 ? d.segments
+                   : d.variant == LA_GLA ? la::gla_mfma_auto_segments(p)
+                                         : la::diag_mfma_auto_segments(p);
         if (segs > nchunks) segs = nchunks;
         if (segs < 1) segs = 1;
         // equal segments of cps chunks; drop segments that would be empty
@@ -125,7 +127,9 @@ int plan_prefill(const la_desc& d, Problem& p) {
 size_t workspace_for(const Problem& p) {
     if (p.N == 0 || p.B == 0 || p.H == 0) return 0;
     if (p.path == LA_PATH_MFMA)
-        return p.variant == LA_GDN ? la::gdn_mfma_workspace_bytes(p) : la::diag_mfma_workspace_bytes(p);
+        return p.variant == LA_GDN   ? la::gdn_mfma_workspace_bytes(p)
+               : p.variant == LA_GLA ? la::gla_mfma_workspace_bytes(p)
+                                     : la::diag_mfma_workspace_bytes(p);
     return 0;
 }
 
@@ -227,7 +231,9 @@ int la_prefill(const la_desc* d, const void* q, const void* k, const void* v, co
     if (p.N == 0)
         err = la::launch_state_init(p);
     else if (p.path == LA_PATH_MFMA)
-        err = gdn ? la::launch_prefill_gdn_mfma(p) : la::launch_prefill_diag_mfma(p);
+        err = gdn                     ? la::launch_prefill_gdn_mfma(p)
+              : p.variant == LA_GLA ? la::launch_prefill_gla_mfma(p)
+                                    : la::launch_prefill_diag_mfma(p);
     else
         err = la::launch_prefill_valu(p);
     if (err == hipSuccess) err = hipGetLastError();

@@ -43,6 +43,11 @@ bool diag_mfma_supported(int variant, int dk, int dv, bool io_bf16);
 size_t diag_mfma_workspace_bytes(const Problem& p);
 int diag_mfma_auto_segments(const Problem& p);
 hipError_t launch_prefill_diag_mfma(const Problem& p);
+// prefill_gla_mfma.hip (GLA)
+bool gla_mfma_supported(int dk, int dv, bool io_bf16);
+size_t gla_mfma_workspace_bytes(const Problem& p);
+int gla_mfma_auto_segments(const Problem& p);
+hipError_t launch_prefill_gla_mfma(const Problem& p);
 // prefill_gdn_mfma.hip (GDN)
 bool gdn_mfma_supported(int dk, int dv, bool io_bf16);
 size_t gdn_mfma_workspace_bytes(const Problem& p);

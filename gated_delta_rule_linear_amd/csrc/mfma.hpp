@@ -79,6 +79,56 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
     return w;
 }
 
+// Value columns of a 16 NVT-column slice as seen by its NVT column tiles: tile ct,
+// tile-local index j (0..15) -> column 4 NVT (j / 4) + 4 ct + j % 4. The lane group g
+// of a D tile (rows 4 g .. 4 g + 3) then owns the 4 NVT contiguous columns 4 NVT g ..
+// across all tiles, so value loads and output stores are 8 NVT-byte accesses. Also
+// colmap(ct, 4 q + e) = colmap(ct, 4 q) + e. NVT = 1 is the identity.
+template <int NVT>
+__device__ __forceinline__ int colmap(int ct, int j) {
+    return 4 * NVT * (j >> 2) + 4 * ct + (j & 3);
+}
+// Fragment from a row-major [K rows][columns] bf16 tile whose M/N index is tile ct's
+// columns (LDS transpose read; each lane quad addresses 4 consecutive columns).
+template <int NVT>
+__device__ __forceinline__ bf16x8_t frag_kr_cols(const uint16_t* t, int pitch, int k0, int cb,
+                                                 int ct, int lane) {
+    const int g = lane >> 4, L = lane & 15;
+    const uint16_t* p = t + (k0 + g * 8 + (L >> 2)) * pitch + cb + colmap<NVT>(ct, 4 * (L & 3));
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 4 * pitch));
+    const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+// Fragment from a row-major [columns][K] bf16 tile (S^T) whose M index is tile ct's
+// columns.
+template <int NVT>
+__device__ __forceinline__ bf16x8_t frag_st(const uint16_t* t, int pitch, int cb, int ct, int k0,
+                                            int lane) {
+    return *reinterpret_cast<const bf16x8_t*>(t + (cb + colmap<NVT>(ct, lane & 15)) * pitch + k0 +
+                                              (lane >> 4) * 8);
+}
+// D tile [M = tile ct's columns][N = rows n0 ..] to a row-major [rows][columns] tile.
+template <int NVT>
+__device__ __forceinline__ void store_rows(uint16_t* t, int pitch, int cb, int ct, int n0,
+                                           f32x4_t d, int lane) {
+    uint2 w;
+    w.x = pack_bf16x2(d[0], d[1]);
+    w.y = pack_bf16x2(d[2], d[3]);
+    *reinterpret_cast<uint2*>(t + (n0 + (lane & 15)) * pitch + cb +
+                              colmap<NVT>(ct, 4 * (lane >> 4))) = w;
+}
+// D tile [M = key rows i0 ..][N = tile ct's columns] to the [columns][keys] tile S^T.
+template <int NVT>
+__device__ __forceinline__ void store_st(uint16_t* t, int pitch, int i0, int cb, int ct,
+                                         f32x4_t d, int lane) {
+    uint2 w;
+    w.x = pack_bf16x2(d[0], d[1]);
+    w.y = pack_bf16x2(d[2], d[3]);
+    *reinterpret_cast<uint2*>(t + (cb + colmap<NVT>(ct, lane & 15)) * pitch + i0 +
+                              4 * (lane >> 4)) = w;
+}
+
 // Raw bits of one gate element (bf16 or fp32 storage), converted later so that a
 // prefetch load is not consumed right after it is issued.
 template <bool GB>

@@ -1,0 +1,627 @@
+// Chunked prefill for gated linear attention with a per-key-dim gate (GLA, "Linear /
+// RNN 路线" section 2.2: S_t = diag(g_t) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t) on bf16
+// MFMA, d_k = 128, chunk C = 64.
+//
+// Per chunk, with B_r = sum_{s<=r} log g_s (chunk-local, per key dim i) and the state S
+// entering the chunk:
+//   o_r = (q_r * exp(B_r))^T S + sum_{s<=r} P_rs v_s,  P_rs = sum_i q_ri k_si exp(B_ri - B_si)
+//   S  <- diag(a) S + sum_s (k_s * exp(B_last - B_s)) v_s^T,  a = exp(B_last)
+// an exact rewrite of the token recurrence. Everything that involves the gates depends
+// on one chunk's q, k, g only, never on the state, so it is done once per chunk in a
+// fully parallel prep kernel; what remains per chunk on the sequential path is three
+// dense products on the matrix cores. A diagonal transition also lets the sequence be
+// cut into segments that run in parallel: the state entering segment j is a scan of
+// per-segment summaries, S_in[j+1] = diag(A_j) S_in[j] + dS_j (the parallel-scan idea
+// the same page applies to linear recurrences). Four kernels:
+//   prep     (sequence, chunk): B by a column scan, then q^ = q exp(B), k^ = k exp(B_last
+//            - B), a = exp(B_last) and the masked score tile P, all to the workspace;
+//   summary  (sequence, segment < last, value tile): dS_j and A_j = prod of a over the
+//            segment, by the state update alone from a zero state;
+//   scan     (sequence, state element): S_in[j] for every segment, in place over dS;
+//   forward  (sequence, segment, value tile): from S_in[j], per chunk o = q^ S + P V and
+//            the state update; the last segment writes S_final.
+// P is formed from scaled copies of q and k. To keep every factor bounded the chunk is
+// cut into four 16-row blocks; row block b uses the reference rho_b = B at its middle
+// row: q~_r = q_r exp(B_r - rho_b), k~(b)_s = k_s exp(rho_b - B_s) for s < 16 (b + 1), so
+// no factor exceeds exp(8 max |log g|). log g is clamped at -10 (g >= 4.5e-5: a gate
+// below that keeps less than 4.5e-5 of the state, so the clamp changes no result
+// beyond bf16 rounding), which bounds every factor by e^80 in fp32.
+#include "la_internal.h"
+#include "mfma.hpp"
+
+namespace la {
+namespace {
+
+constexpr int DK = 128;
+constexpr int C = kMfmaChunk;  // 64
+constexpr int NT = 256;
+constexpr int PQ = DK + 8;     // pitch of [*][128] bf16 tiles
+constexpr int PC = C + 8;      // pitch of [*][64] bf16 tiles
+constexpr int PB = DK + 4;     // pitch of the fp32 [64][128] gate tile
+constexpr float kLogGateMin = -10.f;
+
+// Workspace of one chunk, written by prep (bytes): q^ in fragment order (piece (rb, kk,
+// lane = 16 g + j) = row 16 rb + j, columns 32 kk + 8 g .. + 7), k^ row-major, P in
+// fragment order (as q^, two K halves), a (fp32).
+constexpr uint32_t kWsQ = 0, kWsK = 16384, kWsP = 32768, kWsA = 40960, kWsChunk = 41472;
+
+// row offset of the k~(b) copy inside the stacked key tile: 0, 16, 48, 96 (16, 32, 48, 64 rows)
+__host__ __device__ constexpr int koff(int b) { return 8 * b * (b + 1); }
+__host__ __device__ constexpr int pair_index(int b, int bb) {   // (0,1)..(2,3) -> 0..5
+    return b == 0 ? bb - 1 : b == 1 ? bb + 1 : 5;
+}
+
+struct GlaArgs {
+    const uint16_t *q, *k, *v;
+    const void* g;
+    const float* S0;
+    uint16_t* o;
+    float* S;
+    unsigned char* ws;   // per-chunk prep output
+    float* dS;           // [nseq][nseg - 1][DK][DV]: summaries, then S_in[1 ..]
+    float* A;            // [nseq][nseg - 1][DK]
+    int N, nseq, nchunks, nseg, cps, ntiles, DV;
+};
+
+// ---------------------------------------------------------------------------
+// prep
+// ---------------------------------------------------------------------------
+struct __align__(16) PrepSmem {
+    // the fp32 gate tile is dead once every thread holds its B values, so the scaled
+    // q / k copies reuse its storage
+    union {
+        __align__(16) float bg[C * PB];
+        struct {
+            __align__(16) uint16_t qt[C * PQ];
+            __align__(16) uint16_t kt[160 * PQ];   // k~(b), b = 0..3, stacked (koff)
+        } s;
+    } u;
+    __align__(16) uint16_t p[C * PC];
+    __align__(16) float rho[4][DK];
+    __align__(16) float fq[4][DK];    // exp(rho_b)
+    __align__(16) float fk[4][DK];    // exp(B_last - rho_b)
+    __align__(16) float fe[6][DK];    // exp(rho_bb - rho_b), b < bb
+    __align__(16) float dec[DK];      // exp(B_last)
+};
+
+template <bool GB>
+__global__ __launch_bounds__(NT) void gla_prep_kernel(GlaArgs a) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int g = lane >> 4, jl = lane & 15;
+    const size_t seq = blockIdx.x / a.nchunks;
+    const int ch = blockIdx.x % a.nchunks;
+    const int t0 = ch * C, n = min(C, a.N - t0);
+    const size_t tok0 = seq * size_t(a.N);
+
+    // rows past the end of the sequence read as zero
+    const uint32_t rows_left = uint32_t(a.N - t0);
+    const rsrc_t rq = make_rsrc(a.q + (tok0 + t0) * DK, rows_left * DK * 2u);
+    const rsrc_t rk = make_rsrc(a.k + (tok0 + t0) * DK, rows_left * DK * 2u);
+    constexpr uint32_t GS = GB ? 2u : 4u;
+    const rsrc_t rg = make_rsrc(static_cast<const char*>(a.g) + (tok0 + t0) * DK * GS,
+                                rows_left * DK * GS);
+    uint4 qv[4], kv[4], gv[4][2];
+#pragma unroll
+    for (int x4 = 0; x4 < 4; ++x4) {
+        const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
+        const uint32_t e = uint32_t(r * DK + col);
+        qv[x4] = buf_ld16(rq, e * 2u);
+        kv[x4] = buf_ld16(rk, e * 2u);
+        if constexpr (GB) {
+            gv[x4][0] = buf_ld16(rg, e * 2u);
+        } else {
+            gv[x4][0] = buf_ld16(rg, e * 4u);
+            gv[x4][1] = buf_ld16(rg, e * 4u + 16u);
+        }
+    }
+    // log g, clamped, zero on padding rows
+#pragma unroll
+    for (int x4 = 0; x4 < 4; ++x4) {
+        const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
+        float f[8];
+        gate8_val<GB>(gv[x4], f);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float lg = fmaxf(fast_log(f[q]), kLogGateMin);
+            f[q] = r < n ? lg : 0.f;
+        }
+        *reinterpret_cast<float4*>(sm.u.bg + r * PB + col) = make_float4(f[0], f[1], f[2], f[3]);
+        *reinterpret_cast<float4*>(sm.u.bg + r * PB + col + 4) = make_float4(f[4], f[5], f[6], f[7]);
+    }
+    lds_barrier();
+    // inclusive scan down each column: two threads per column, 32 rows each
+    {
+        const int col = tid & 127, half = tid >> 7;
+        float x[32];
+#pragma unroll
+        for (int r = 0; r < 32; ++r) x[r] = sm.u.bg[(half * 32 + r) * PB + col];
+        float tot = 0.f;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) { tot += x[r]; x[r] = tot; }
+        // the lower half adds the upper half's column total
+        __shared__ float part[DK];
+        if (half == 0) part[col] = tot;
+        lds_barrier();
+        const float add = half == 1 ? part[col] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) sm.u.bg[(half * 32 + r) * PB + col] = x[r] + add;
+    }
+    lds_barrier();
+    if (tid < DK) {
+        const float bl = sm.u.bg[(C - 1) * PB + tid];
+        float rb[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            rb[b] = sm.u.bg[(16 * b + 7) * PB + tid];
+            sm.rho[b][tid] = rb[b];
+            sm.fq[b][tid] = fast_exp(rb[b]);
+            sm.fk[b][tid] = fast_exp(bl - rb[b]);
+        }
+#pragma unroll
+        for (int b = 0; b < 3; ++b)
+#pragma unroll
+            for (int bb = b + 1; bb < 4; ++bb) sm.fe[pair_index(b, bb)][tid] = fast_exp(rb[bb] - rb[b]);
+        sm.dec[tid] = fast_exp(bl);
+    }
+    // every thread takes its B values before the gate tile is overwritten
+    float br[4][8];
+#pragma unroll
+    for (int x4 = 0; x4 < 4; ++x4) {
+        const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
+        const float4 u0 = *reinterpret_cast<const float4*>(sm.u.bg + r * PB + col);
+        const float4 u1 = *reinterpret_cast<const float4*>(sm.u.bg + r * PB + col + 4);
+        br[x4][0] = u0.x; br[x4][1] = u0.y; br[x4][2] = u0.z; br[x4][3] = u0.w;
+        br[x4][4] = u1.x; br[x4][5] = u1.y; br[x4][6] = u1.z; br[x4][7] = u1.w;
+    }
+    lds_barrier();
+
+    unsigned char* wsc = a.ws + (seq * a.nchunks + ch) * size_t(kWsChunk);
+    auto ld8 = [&](const float* src, float (&dst)[8]) {
+        const float4 u0 = *reinterpret_cast<const float4*>(src);
+        const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
+        dst[0] = u0.x; dst[1] = u0.y; dst[2] = u0.z; dst[3] = u0.w;
+        dst[4] = u1.x; dst[5] = u1.y; dst[6] = u1.z; dst[7] = u1.w;
+    };
+#pragma unroll
+    for (int x4 = 0; x4 < 4; ++x4) {
+        const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
+        const int b = x4;   // rows (tid >> 4) + 16 x4 lie in row block x4
+        float q8[8], k8[8], rho[8], fq[8], fk[8];
+        unpack8(qv[x4], q8);   // padding rows read as zero
+        unpack8(kv[x4], k8);
+        ld8(sm.rho[b] + col, rho);
+        ld8(sm.fq[b] + col, fq);
+        ld8(sm.fk[b] + col, fk);
+        float qt[8], qh[8], kt[8], kh[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float e = fast_exp(br[x4][q] - rho[q]);   // exp(B_r - rho_b)
+            const float inv = __builtin_amdgcn_rcpf(e);      // exp(rho_b - B_r)
+            qt[q] = q8[q] * e;
+            qh[q] = qt[q] * fq[q];                          // q exp(B_r)
+            kt[q] = k8[q] * inv;                            // k exp(rho_b - B_r)
+            kh[q] = kt[q] * fk[q];                          // k exp(B_last - B_r)
+        }
+        *reinterpret_cast<uint4*>(sm.u.s.qt + r * PQ + col) = pack8(qt);
+        *reinterpret_cast<uint4*>(sm.u.s.kt + (koff(b) + r) * PQ + col) = pack8(kt);
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            if (bb <= b) continue;
+            float fe[8], kb[8];
+            ld8(sm.fe[pair_index(b, bb)] + col, fe);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) kb[q] = kt[q] * fe[q];
+            *reinterpret_cast<uint4*>(sm.u.s.kt + (koff(bb) + r) * PQ + col) = pack8(kb);
+        }
+        // q^ in fragment order, k^ row-major
+        const int jr = r & 15, kk = col >> 5, gg = (col & 31) >> 3;
+        *reinterpret_cast<uint4*>(wsc + kWsQ + (((r >> 4) * 4 + kk) * 64 + 16 * gg + jr) * 16) = pack8(qh);
+        *reinterpret_cast<uint4*>(wsc + kWsK + (r * DK + col) * 2) = pack8(kh);
+    }
+    if (tid < DK / 4)
+        *reinterpret_cast<float4*>(wsc + kWsA + tid * 16) = *reinterpret_cast<const float4*>(sm.dec + 4 * tid);
+    // zero the six upper blocks of P
+    if (w >= 2) {
+        const int r = lane >> 2, cc = (lane & 3) * 4;
+        const int ub[6][2] = {{0, 1}, {0, 2}, {0, 3}, {1, 2}, {1, 3}, {2, 3}};
+        for (int x = w - 2; x < 6; x += 2)
+            *reinterpret_cast<uint2*>(sm.p + (16 * ub[x][0] + r) * PC + 16 * ub[x][1] + cc) = make_uint2(0, 0);
+    }
+    lds_barrier();
+    // P: ten lower tiles, D'[s][r] = k~(rb)_s . q~_r -> p[r][s..]
+    for (int ti = w; ti < 10; ti += 4) {
+        const int rb = ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3;
+        const int sb = ti - (rb * (rb + 1)) / 2;
+        f32x4_t acc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk)
+            acc = mfma16(frag_kc(sm.u.s.kt, PQ, koff(rb) + 16 * sb, 32 * kk, lane),
+                         frag_kc(sm.u.s.qt, PQ, 16 * rb, 32 * kk, lane), acc);
+        const int r = 16 * rb + jl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int s = 16 * sb + 4 * g + j;
+            acc[j] = s <= r ? acc[j] : 0.f;
+        }
+        store_dT(sm.p, PC, 16 * sb, 16 * rb, acc, lane);
+    }
+    lds_barrier();
+    // P in fragment order
+#pragma unroll
+    for (int x2 = 0; x2 < 2; ++x2) {
+        const int x = tid + NT * x2, rb = x >> 7, kk = (x >> 6) & 1, l = x & 63;
+        const int off = (16 * rb + (l & 15)) * PC + 32 * kk + 8 * (l >> 4);
+        *reinterpret_cast<uint4*>(wsc + kWsP + x * 16) = *reinterpret_cast<const uint4*>(sm.p + off);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// summary (OUT = false) and forward (OUT = true): the chunk walk of one segment
+// ---------------------------------------------------------------------------
+template <int VT>
+struct __align__(16) ChainSmem {
+    static constexpr int PV = VT + 8;
+    __align__(16) uint16_t kh[2][C * PQ];   // k^ [s][i]
+    __align__(16) uint16_t v[2][C * PV];    // V [s][c]
+    __align__(16) uint16_t st[2][VT * PQ];  // S^T [c][i], bf16 (forward only)
+};
+
+// One chunk's operands in registers: the k^ / V pieces this thread copies to LDS, and
+// (forward) the wave's q^ and P fragments; a for the wave's state rows.
+template <int KV>
+struct ChainRegs {
+    uint4 kst[4], vst[KV], qf[4], pf[2], af[2];
+};
+
+template <bool OUT, int NVT>
+__global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
+    constexpr int VT = 16 * NVT;
+    constexpr int PV = ChainSmem<VT>::PV;
+    constexpr int KV = VT >= 32 ? VT / 32 : 1;   // 16-byte V pieces per thread
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    ChainSmem<VT>& sm = *reinterpret_cast<ChainSmem<VT>*>(smem_raw);
+
+    const int nrun = OUT ? a.nseg : a.nseg - 1;   // segments this kernel walks
+    const XcdMap mp = xcd_map(blockIdx.x, a.ntiles, a.nseq * nrun);
+    if (!mp.valid) return;
+    const int seq = mp.seq / nrun, seg = mp.seq % nrun;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int g = lane >> 4, jl = lane & 15;
+    const int DV = a.DV;
+    const int c0 = mp.tile * VT;
+    const size_t tok0 = size_t(seq) * size_t(a.N);
+    const int ch0 = seg * a.cps, ch1 = min(a.nchunks, ch0 + a.cps);
+    const int nk = w < 2 ? 1 : 2;   // P rows 16 w .. vanish for s >= 16 (w + 1)
+    const int rw = 16 * w + jl;
+
+    // state tile: key rows 16 (2 w + ib) + 4 g + j, columns c0 + colmap(ct, jl)
+    f32x4_t S[2][NVT];
+    const float* Sinit = nullptr;
+    if (OUT) Sinit = seg == 0 ? (a.S0 ? a.S0 + size_t(seq) * DK * DV : nullptr)
+                              : a.dS + (size_t(seq) * (a.nseg - 1) + seg - 1) * DK * DV;
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int ct = 0; ct < NVT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = 16 * (2 * w + ib) + 4 * g + j, c = c0 + colmap<NVT>(ct, jl);
+                S[ib][ct][j] = Sinit ? Sinit[size_t(i) * DV + c] : 0.f;
+            }
+    if (OUT) {
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct)
+                store_st<NVT>(sm.st[0], PQ, 16 * (2 * w + ib), 0, ct, S[ib][ct], lane);
+    }
+    float aprod[2][4];   // running product of the chunk decays (summary)
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) aprod[ib][j] = 1.f;
+
+    // every load is unconditional: chunk indices past the segment read zeros (the
+    // workspace resource covers this sequence's chunks [ch0, ch1) only) and past-the-end
+    // output rows are dropped
+    const rsrc_t rw_ = make_rsrc(a.ws + (size_t(seq) * a.nchunks + ch0) * kWsChunk,
+                                 uint32_t(ch1 - ch0) * kWsChunk);
+    const rsrc_t rv = make_rsrc(a.v + tok0 * DV, uint32_t(a.N) * uint32_t(DV) * 2u);
+    const rsrc_t ro = make_rsrc(a.o + tok0 * DV, uint32_t(a.N) * uint32_t(DV) * 2u);
+
+    auto load_chunk = [&](ChainRegs<KV>& R, int lc) {   // lc: chunk index within the segment
+        const uint32_t cb = uint32_t(lc) * kWsChunk;
+        const uint32_t t0 = uint32_t(ch0 + lc) * C;
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4) {
+            const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
+            R.kst[x4] = buf_ld16(rw_, cb + kWsK + uint32_t(r * DK + col) * 2u);
+        }
+#pragma unroll
+        for (int x = 0; x < KV; ++x) {
+            // V pieces: 64 rows x VT columns in 16-byte pieces, VT / 8 per row; with
+            // VT = 16 the upper half of the threads reads past the range (zeros, unused)
+            const int id = tid + NT * x, r = id / (VT / 8), col = (id % (VT / 8)) * 8;
+            const uint32_t off = VT >= 32 || id < C * VT / 8
+                                     ? ((t0 + r) * uint32_t(DV) + c0 + col) * 2u
+                                     : uint32_t(a.N) * uint32_t(DV) * 2u;
+            R.vst[x] = buf_ld16(rv, off);
+        }
+        if (OUT) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                R.qf[kk] = buf_ld16(rw_, cb + kWsQ + uint32_t((w * 4 + kk) * 64 + lane) * 16u);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                R.pf[kk] = buf_ld16(rw_, cb + kWsP + uint32_t((w * 2 + kk) * 64 + lane) * 16u);
+        }
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+            R.af[ib] = buf_ld16(rw_, cb + kWsA + uint32_t(16 * (2 * w + ib) + 4 * g) * 4u);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto stage = [&](const ChainRegs<KV>& R, int buf) {
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4) {
+            const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
+            *reinterpret_cast<uint4*>(sm.kh[buf] + r * PQ + col) = R.kst[x4];
+        }
+#pragma unroll
+        for (int x = 0; x < KV; ++x) {
+            const int id = tid + NT * x, r = id / (VT / 8), col = (id % (VT / 8)) * 8;
+            if (VT >= 32 || id < C * VT / 8)
+                *reinterpret_cast<uint4*>(sm.v[buf] + r * PV + col) = R.vst[x];
+        }
+    };
+
+    auto process = [&](const ChainRegs<KV>& R, const ChainRegs<KV>& Rn, int lc, int cur) {
+        const uint16_t* kh = sm.kh[cur];
+        const uint16_t* vv = sm.v[cur];
+        if (OUT) {
+            // O^T = S^T q^^T + V^T P^T for rows 16 w ..; 4 NVT contiguous columns per lane
+            uint2 ow[NVT];
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct) {
+                f32x4_t o_ = zero4();
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk)
+                    o_ = mfma16(frag_st<NVT>(sm.st[cur], PQ, 0, ct, 32 * kk, lane),
+                                __builtin_bit_cast(bf16x8_t, R.qf[kk]), o_);
+                o_ = mfma16(frag_kr_cols<NVT>(vv, PV, 0, 0, ct, lane),
+                            __builtin_bit_cast(bf16x8_t, R.pf[0]), o_);
+                if (nk > 1)
+                    o_ = mfma16(frag_kr_cols<NVT>(vv, PV, 32, 0, ct, lane),
+                                __builtin_bit_cast(bf16x8_t, R.pf[1]), o_);
+                ow[ct].x = pack_bf16x2(o_[0], o_[1]);
+                ow[ct].y = pack_bf16x2(o_[2], o_[3]);
+            }
+            const uint32_t orow = (uint32_t(ch0 + lc) * C + rw) * uint32_t(DV) + c0 + 4 * NVT * g;
+            if constexpr (NVT == 4) {
+                buf_st16(ro, orow * 2u, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
+                buf_st16(ro, orow * 2u + 16u, make_uint4(ow[2].x, ow[2].y, ow[3].x, ow[3].y));
+            } else if constexpr (NVT == 2) {
+                buf_st16(ro, orow * 2u, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
+            } else {
+                buf_st8(ro, orow * 2u, ow[0]);
+            }
+        }
+        // S = diag(a) S + K^^T V (key rows 32 w ..)
+        bf16x8_t vf[2][NVT];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct) vf[kk][ct] = frag_kr_cols<NVT>(vv, PV, 32 * kk, 0, ct, lane);
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+            const int i0 = 16 * (2 * w + ib);
+            const float4 a4 = __builtin_bit_cast(float4, R.af[ib]);
+            const f32x4_t av = {a4.x, a4.y, a4.z, a4.w};
+            if (!OUT) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) aprod[ib][j] *= av[j];
+            }
+            const bf16x8_t k0f = frag_kr(kh, PQ, 0, i0, lane);
+            const bf16x8_t k1f = frag_kr(kh, PQ, 32, i0, lane);
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct) {
+                f32x4_t s_ = S[ib][ct] * av;
+                s_ = mfma16(k0f, vf[0][ct], s_);
+                s_ = mfma16(k1f, vf[1][ct], s_);
+                S[ib][ct] = s_;
+                if (OUT) store_st<NVT>(sm.st[cur ^ 1], PQ, i0, 0, ct, s_, lane);
+            }
+        }
+        stage(Rn, cur ^ 1);
+        lds_barrier();
+    };
+
+    const int nloc = ch1 - ch0;
+    ChainRegs<KV> RA, RB;
+    load_chunk(RA, 0);
+    stage(RA, 0);
+    lds_barrier();
+    // whole pairs: a chunk past the segment reads zeros (a = 0 would clear the state, so
+    // its update is skipped by the loop bound below, never by a branch between loads)
+    for (int lc = 0; lc < nloc; lc += 2) {
+        load_chunk(RB, lc + 1);
+        process(RA, RB, lc, 0);
+        if (lc + 1 >= nloc) break;
+        load_chunk(RA, lc + 2);
+        process(RB, RA, lc + 1, 1);
+    }
+
+    if (OUT) {
+        if (seg == a.nseg - 1) {
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int ct = 0; ct < NVT; ++ct)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int i = 16 * (2 * w + ib) + 4 * g + j, c = c0 + colmap<NVT>(ct, jl);
+                        a.S[size_t(seq) * DK * DV + size_t(i) * DV + c] = S[ib][ct][j];
+                    }
+        }
+    } else {
+        float* dS = a.dS + (size_t(seq) * (a.nseg - 1) + seg) * DK * DV;
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = 16 * (2 * w + ib) + 4 * g + j, c = c0 + colmap<NVT>(ct, jl);
+                    dS[size_t(i) * DV + c] = S[ib][ct][j];
+                }
+        if (mp.tile == 0 && jl == 0) {
+            float* A = a.A + (size_t(seq) * (a.nseg - 1) + seg) * DK;
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) A[16 * (2 * w + ib) + 4 * g + j] = aprod[ib][j];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// scan over segments: S_in[j + 1] = diag(A_j) S_in[j] + dS_j, in place over dS_j
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gla_scan_kernel(GlaArgs a) {
+    const int per_seq = DK * (a.DV / 4);
+    const size_t idx = size_t(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= size_t(a.nseq) * per_seq) return;
+    const size_t seq = idx / per_seq;
+    const int e = int(idx % per_seq), i = e / (a.DV / 4), c = (e % (a.DV / 4)) * 4;
+    const size_t so = size_t(i) * a.DV + c;
+    float4 s = a.S0 ? *reinterpret_cast<const float4*>(a.S0 + seq * DK * a.DV + so)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int nsum = a.nseg - 1;
+    for (int j = 0; j < nsum; ++j) {
+        float4* d = reinterpret_cast<float4*>(a.dS + (seq * nsum + j) * DK * a.DV + so);
+        const float aj = a.A[(seq * nsum + j) * DK + i];
+        const float4 ds = *d;
+        s.x = aj * s.x + ds.x;
+        s.y = aj * s.y + ds.y;
+        s.z = aj * s.z + ds.z;
+        s.w = aj * s.w + ds.w;
+        *d = s;
+    }
+}
+
+struct WsLayout {
+    size_t chunks, dS, A, total;
+};
+WsLayout ws_layout(const Problem& p) {
+    const size_t nseq = size_t(p.B) * size_t(p.H);
+    const size_t nchunks = size_t((p.N + C - 1) / C);
+    const size_t nsum = size_t(p.segments > 1 ? p.segments - 1 : 0);
+    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    WsLayout L{};
+    L.chunks = 0;
+    size_t off = al(nseq * nchunks * kWsChunk);
+    L.dS = off;
+    off += al(nseq * nsum * DK * size_t(p.dv) * 4);
+    L.A = off;
+    off += al(nseq * nsum * DK * 4);
+    L.total = off;
+    return L;
+}
+
+int pick_nvt(int dv) { return dv >= 64 ? 4 : dv / 16; }
+
+template <bool GB, int NVT>
+hipError_t launch_nvt(const Problem& p) {
+    constexpr int VT = 16 * NVT;
+    const WsLayout L = ws_layout(p);
+    GlaArgs a{};
+    a.q = static_cast<const uint16_t*>(p.q);
+    a.k = static_cast<const uint16_t*>(p.k);
+    a.v = static_cast<const uint16_t*>(p.v);
+    a.g = p.g;
+    a.S0 = p.S0;
+    a.o = static_cast<uint16_t*>(p.o);
+    a.S = p.S;
+    unsigned char* ws = static_cast<unsigned char*>(p.ws);
+    a.ws = ws + L.chunks;
+    a.dS = reinterpret_cast<float*>(ws + L.dS);
+    a.A = reinterpret_cast<float*>(ws + L.A);
+    a.N = p.N;
+    a.nseq = int(size_t(p.B) * size_t(p.H));
+    a.nchunks = (p.N + C - 1) / C;
+    a.nseg = p.segments;
+    a.cps = (a.nchunks + a.nseg - 1) / a.nseg;
+    a.DV = p.dv;
+    a.ntiles = p.dv / VT;
+    hipError_t e;
+    {
+        const size_t smem = sizeof(PrepSmem);
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_prep_kernel<GB>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+        if (e != hipSuccess) return e;
+        const size_t blocks = size_t(a.nseq) * size_t(a.nchunks);
+        if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
+        gla_prep_kernel<GB><<<dim3(unsigned(blocks)), dim3(NT), smem, p.stream>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const size_t smem = sizeof(ChainSmem<VT>);
+    if (a.nseg > 1) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_chain_kernel<false, NVT>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+        if (e != hipSuccess) return e;
+        gla_chain_kernel<false, NVT><<<dim3(xcd_grid(a.ntiles, a.nseq * (a.nseg - 1))), dim3(NT),
+                                       smem, p.stream>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const size_t n = size_t(a.nseq) * DK * (p.dv / 4);
+        gla_scan_kernel<<<dim3(unsigned((n + 255) / 256)), dim3(256), 0, p.stream>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_chain_kernel<true, NVT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+    if (e != hipSuccess) return e;
+    gla_chain_kernel<true, NVT><<<dim3(xcd_grid(a.ntiles, a.nseq * a.nseg)), dim3(NT), smem,
+                                  p.stream>>>(a);
+    return hipGetLastError();
+}
+
+template <bool GB>
+hipError_t launch_gb(const Problem& p) {
+    switch (pick_nvt(p.dv)) {
+        case 1: return launch_nvt<GB, 1>(p);
+        case 2: return launch_nvt<GB, 2>(p);
+        default: return launch_nvt<GB, 4>(p);
+    }
+}
+
+}  // namespace
+
+bool gla_mfma_supported(int dk, int dv, bool io_bf16) {
+    return io_bf16 && dk == DK && (dv == 16 || dv == 32 || dv == 64 || dv == 128);
+}
+
+size_t gla_mfma_workspace_bytes(const Problem& p) { return ws_layout(p).total; }
+
+int gla_mfma_auto_segments(const Problem& p) {
+    // enough (sequence, segment, value tile) units for one workgroup per CU, with at
+    // least two chunks per segment
+    const size_t nseq = size_t(p.B) * size_t(p.H);
+    const size_t ntiles = size_t(p.dv / (16 * pick_nvt(p.dv)));
+    const size_t nchunks = size_t((p.N + C - 1) / C);
+    const size_t units = nseq * ntiles;
+    size_t want = (256 + units - 1) / units;
+    const size_t cap = nchunks / 2;
+    if (want > cap) want = cap;
+    return want < 1 ? 1 : int(want);
+}
+
+hipError_t launch_prefill_gla_mfma(const Problem& p) {
+    const size_t nseq = size_t(p.B) * size_t(p.H);
+    if (nseq > (1u << 24) || !p.ws) return hipErrorInvalidValue;
+    // buffer offsets are 32-bit: one sequence's v / o rows and its chunk workspace
+    if (size_t(p.N) * size_t(p.dv) * 2 >= (size_t(1) << 31)) return hipErrorInvalidValue;
+    if (size_t((p.N + C - 1) / C) * kWsChunk >= (size_t(1) << 31)) return hipErrorInvalidValue;
+    return p.gate_bf16 ? launch_gb<true>(p) : launch_gb<false>(p);
+}
+
+}  // namespace la
