@@ -36,17 +36,18 @@ constexpr int DK = 128;
 constexpr int C = kMfmaChunk;  // 64
 constexpr int NT = 256;
 constexpr int PQ = DK + 8;     // pitch of [*][128] bf16 tiles
-constexpr int PC = C + 8;      // pitch of [*][64] bf16 tiles
-constexpr int PB = DK + 4;     // pitch of the fp32 [64][128] gate tile
+constexpr int PB = DK;         // pitch of the fp32 [64][128] gate tile
 constexpr float kLogGateMin = -10.f;
 
-// Workspace of one chunk, written by prep (bytes): q^ in fragment order (piece (rb, kk,
-// lane = 16 g + j) = row 16 rb + j, columns 32 kk + 8 g .. + 7), k^ row-major, P in
-// fragment order (as q^, two K halves), a (fp32).
+// Workspace of one chunk, written by prep (bytes), each matrix in MFMA fragment order
+// so that a wave reads its fragment as one contiguous kilobyte: q^ (piece (rb, kk, lane =
+// 16 g + j) = row 16 rb + j, columns 32 kk + 8 g .. + 7), k^ transposed (piece (ib, kk,
+// lane) = key dim 16 ib + j, tokens 32 kk + 8 g .. + 7), P (piece (rb, kk, lane) = row
+// 16 rb + j, tokens 32 kk + 4 g .. + 3 then 32 kk + 16 + 4 g .. + 3: the order in which
+// the matrix cores return the tile, matched by the forward kernel's V fragment), then
+// a (fp32).
 constexpr uint32_t kWsQ = 0, kWsK = 16384, kWsP = 32768, kWsA = 40960, kWsChunk = 41472;
 
-// row offset of the k~(b) copy inside the stacked key tile: 0, 16, 48, 96 (16, 32, 48, 64 rows)
-__host__ __device__ constexpr int koff(int b) { return 8 * b * (b + 1); }
 __host__ __device__ constexpr int pair_index(int b, int bb) {   // (0,1)..(2,3) -> 0..5
     return b == 0 ? bb - 1 : b == 1 ? bb + 1 : 5;
 }
@@ -68,15 +69,14 @@ struct GlaArgs {
 // ---------------------------------------------------------------------------
 struct __align__(16) PrepSmem {
     // the fp32 gate tile is dead once every thread holds its B values, so the scaled
-    // q / k copies reuse its storage
+    // q / k copies reuse its storage (and k^ reuses q~ once P is done)
     union {
         __align__(16) float bg[C * PB];
         struct {
-            __align__(16) uint16_t qt[C * PQ];
-            __align__(16) uint16_t kt[160 * PQ];   // k~(b), b = 0..3, stacked (koff)
+            __align__(16) uint16_t qt[C * PQ];   // q~ (row block's own reference)
+            __align__(16) uint16_t kt[C * PQ];   // k~ (row block's own reference)
         } s;
     } u;
-    __align__(16) uint16_t p[C * PC];
     __align__(16) float rho[4][DK];
     __align__(16) float fq[4][DK];    // exp(rho_b)
     __align__(16) float fk[4][DK];    // exp(B_last - rho_b)
@@ -90,8 +90,11 @@ __global__ __launch_bounds__(NT) void gla_prep_kernel(GlaArgs a) {
     PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int g = lane >> 4, jl = lane & 15;
-    const size_t seq = blockIdx.x / a.nchunks;
-    const int ch = blockIdx.x % a.nchunks;
+    // all chunks of a sequence on one XCD, where its later kernels run too
+    const XcdMap mp = xcd_map(blockIdx.x, a.nchunks, a.nseq);
+    if (!mp.valid) return;
+    const size_t seq = size_t(mp.seq);
+    const int ch = mp.tile;
     const int t0 = ch * C, n = min(C, a.N - t0);
     const size_t tok0 = seq * size_t(a.N);
 
@@ -167,6 +170,7 @@ __global__ __launch_bounds__(NT) void gla_prep_kernel(GlaArgs a) {
     }
     // every thread takes its B values before the gate tile is overwritten
     float br[4][8];
+    uint4 khp[4];
 #pragma unroll
     for (int x4 = 0; x4 < 4; ++x4) {
         const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(NT) void gla_prep_kernel(GlaArgs a) {
         ld8(sm.rho[b] + col, rho);
         ld8(sm.fq[b] + col, fq);
         ld8(sm.fk[b] + col, fk);
-        float qt[8], qh[8], kt[8], kh[8];
+        float qt[8], qh[8], kt[8], kh[8];   // k^ stays in registers until after P
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const float e = fast_exp(br[x4][q] - rho[q]);   // exp(B_r - rho_b)
@@ -205,56 +209,66 @@ __global__ __launch_bounds__(NT) void gla_prep_kernel(GlaArgs a) {
             kh[q] = kt[q] * fk[q];                          // k exp(B_last - B_r)
         }
         *reinterpret_cast<uint4*>(sm.u.s.qt + r * PQ + col) = pack8(qt);
-        *reinterpret_cast<uint4*>(sm.u.s.kt + (koff(b) + r) * PQ + col) = pack8(kt);
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            if (bb <= b) continue;
-            float fe[8], kb[8];
-            ld8(sm.fe[pair_index(b, bb)] + col, fe);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) kb[q] = kt[q] * fe[q];
-            *reinterpret_cast<uint4*>(sm.u.s.kt + (koff(bb) + r) * PQ + col) = pack8(kb);
-        }
+        *reinterpret_cast<uint4*>(sm.u.s.kt + r * PQ + col) = pack8(kt);
         // q^ in fragment order, k^ row-major
         const int jr = r & 15, kk = col >> 5, gg = (col & 31) >> 3;
         *reinterpret_cast<uint4*>(wsc + kWsQ + (((r >> 4) * 4 + kk) * 64 + 16 * gg + jr) * 16) = pack8(qh);
-        *reinterpret_cast<uint4*>(wsc + kWsK + (r * DK + col) * 2) = pack8(kh);
+        khp[x4] = pack8(kh);
     }
     if (tid < DK / 4)
         *reinterpret_cast<float4*>(wsc + kWsA + tid * 16) = *reinterpret_cast<const float4*>(sm.dec + 4 * tid);
-    // zero the six upper blocks of P
-    if (w >= 2) {
-        const int r = lane >> 2, cc = (lane & 3) * 4;
-        const int ub[6][2] = {{0, 1}, {0, 2}, {0, 3}, {1, 2}, {1, 3}, {2, 3}};
-        for (int x = w - 2; x < 6; x += 2)
-            *reinterpret_cast<uint2*>(sm.p + (16 * ub[x][0] + r) * PC + 16 * ub[x][1] + cc) = make_uint2(0, 0);
-    }
     lds_barrier();
-    // P: ten lower tiles, D'[s][r] = k~(rb)_s . q~_r -> p[r][s..]
+    // P: ten lower tiles, D'[s][r] = k~_s . q~_r exp(rho_rb - rho_sb) for key block sb <
+    // row block rb (the q~ fragment rescaled on the fly, a factor <= 1), stored straight
+    // from the accumulators as half pieces; the two upper half pieces the forward
+    // kernel reads, (0, 1) and (2, 3), are written as zeros
     for (int ti = w; ti < 10; ti += 4) {
         const int rb = ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3;
         const int sb = ti - (rb * (rb + 1)) / 2;
         f32x4_t acc = zero4();
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk)
-            acc = mfma16(frag_kc(sm.u.s.kt, PQ, koff(rb) + 16 * sb, 32 * kk, lane),
-                         frag_kc(sm.u.s.qt, PQ, 16 * rb, 32 * kk, lane), acc);
+        for (int kk = 0; kk < DK / 32; ++kk) {
+            bf16x8_t qb = frag_kc(sm.u.s.qt, PQ, 16 * rb, 32 * kk, lane);
+            if (sb < rb) {
+                float f[8], fe[8];
+                unpack8(__builtin_bit_cast(uint4, qb), f);
+                ld8(sm.fe[pair_index(sb, rb)] + 32 * kk + 8 * g, fe);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) f[q] *= fe[q];
+                qb = __builtin_bit_cast(bf16x8_t, pack8(f));
+            }
+            acc = mfma16(frag_kc(sm.u.s.kt, PQ, 16 * sb, 32 * kk, lane), qb, acc);
+        }
         const int r = 16 * rb + jl;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int s = 16 * sb + 4 * g + j;
             acc[j] = s <= r ? acc[j] : 0.f;
         }
-        store_dT(sm.p, PC, 16 * sb, 16 * rb, acc, lane);
+        unsigned char* piece = wsc + kWsP + ((rb * 2 + (sb >> 1)) * 64 + lane) * 16;
+        *reinterpret_cast<uint2*>(piece + (sb & 1) * 8) =
+            make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+        if (sb == rb && (rb & 1) == 0) *reinterpret_cast<uint2*>(piece + 8) = make_uint2(0, 0);
     }
     lds_barrier();
-    // P in fragment order
+    // k^ row-major into the (now dead) q~ storage, then transposed out
+    uint16_t* kht = sm.u.s.qt;
 #pragma unroll
-    for (int x2 = 0; x2 < 2; ++x2) {
-        const int x = tid + NT * x2, rb = x >> 7, kk = (x >> 6) & 1, l = x & 63;
-        const int off = (16 * rb + (l & 15)) * PC + 32 * kk + 8 * (l >> 4);
-        *reinterpret_cast<uint4*>(wsc + kWsP + x * 16) = *reinterpret_cast<const uint4*>(sm.p + off);
+    for (int x4 = 0; x4 < 4; ++x4) {
+        const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
+        *reinterpret_cast<uint4*>(kht + r * PQ + col) = khp[x4];
     }
+    lds_barrier();
+    // k^ transposed, in fragment order: wave w writes key blocks 2 w, 2 w + 1
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int blk = 2 * w + ib;
+            const bf16x8_t f = frag_kr(kht, PQ, 32 * kk, 16 * blk, lane);
+            *reinterpret_cast<uint4*>(wsc + kWsK + ((blk * 2 + kk) * 64 + lane) * 16) =
+                __builtin_bit_cast(uint4, f);
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -263,16 +277,30 @@ __global__ __launch_bounds__(NT) void gla_prep_kernel(GlaArgs a) {
 template <int VT>
 struct __align__(16) ChainSmem {
     static constexpr int PV = VT + 8;
-    __align__(16) uint16_t kh[2][C * PQ];   // k^ [s][i]
     __align__(16) uint16_t v[2][C * PV];    // V [s][c]
     __align__(16) uint16_t st[2][VT * PQ];  // S^T [c][i], bf16 (forward only)
+    __align__(16) float a[2][DK];           // chunk decay exp(B_last)
 };
 
-// One chunk's operands in registers: the k^ / V pieces this thread copies to LDS, and
-// (forward) the wave's q^ and P fragments; a for the wave's state rows.
+// A fragment of V^T (rows = tile ct's value columns) whose K order matches the P
+// pieces: slots 0..3 are tokens 32 kk + 4 g + 0..3, slots 4..7 tokens 32 kk + 16 + 4 g + 0..3.
+template <int NVT>
+__device__ __forceinline__ bf16x8_t frag_v_pk(const uint16_t* t, int pitch, int kk, int ct,
+                                              int lane) {
+    const int g = lane >> 4, L = lane & 15;
+    const uint16_t* p = t + (32 * kk + 4 * g + (L >> 2)) * pitch + colmap<NVT>(ct, 4 * (L & 3));
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 16 * pitch));
+    const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// One chunk's operands in registers: the wave's k^T fragments (state update, key rows
+// 32 w ..), q^ and P fragments (forward), this thread's V pieces and decay piece for the
+// LDS copies.
 template <int KV>
 struct ChainRegs {
-    uint4 kst[4], vst[KV], qf[4], pf[2], af[2];
+    uint4 kt[4], qf[4], pf[2], vst[KV], ast;
 };
 
 template <bool OUT, int NVT>
@@ -284,15 +312,17 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
     ChainSmem<VT>& sm = *reinterpret_cast<ChainSmem<VT>*>(smem_raw);
 
     const int nrun = OUT ? a.nseg : a.nseg - 1;   // segments this kernel walks
-    const XcdMap mp = xcd_map(blockIdx.x, a.ntiles, a.nseq * nrun);
+    // all (segment, tile) units of a sequence on the XCD that prepared its chunks
+    const XcdMap mp = xcd_map(blockIdx.x, a.ntiles * nrun, a.nseq);
     if (!mp.valid) return;
-    const int seq = mp.seq / nrun, seg = mp.seq % nrun;
+    const int seq = mp.seq, seg = mp.tile / a.ntiles, tile = mp.tile % a.ntiles;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int g = lane >> 4, jl = lane & 15;
     const int DV = a.DV;
-    const int c0 = mp.tile * VT;
+    const int c0 = tile * VT;
     const size_t tok0 = size_t(seq) * size_t(a.N);
     const int ch0 = seg * a.cps, ch1 = min(a.nchunks, ch0 + a.cps);
+    const int nloc = ch1 - ch0;
     const int nk = w < 2 ? 1 : 2;   // P rows 16 w .. vanish for s >= 16 (w + 1)
     const int rw = 16 * w + jl;
 
@@ -323,32 +353,34 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) aprod[ib][j] = 1.f;
 
-    // every load is unconditional: chunk indices past the segment read zeros (the
-    // workspace resource covers this sequence's chunks [ch0, ch1) only) and past-the-end
-    // output rows are dropped
+    // Every load is unconditional: the workspace resource covers this segment's chunks
+    // only, so a prefetch past the segment reads zeros.
     const rsrc_t rw_ = make_rsrc(a.ws + (size_t(seq) * a.nchunks + ch0) * kWsChunk,
-                                 uint32_t(ch1 - ch0) * kWsChunk);
+                                 uint32_t(nloc) * kWsChunk);
     const rsrc_t rv = make_rsrc(a.v + tok0 * DV, uint32_t(a.N) * uint32_t(DV) * 2u);
-    const rsrc_t ro = make_rsrc(a.o + tok0 * DV, uint32_t(a.N) * uint32_t(DV) * 2u);
+    const uint32_t obytes = uint32_t(a.N) * uint32_t(DV) * 2u;
+    const rsrc_t ro = make_rsrc(a.o + tok0 * DV, obytes);
 
     auto load_chunk = [&](ChainRegs<KV>& R, int lc) {   // lc: chunk index within the segment
         const uint32_t cb = uint32_t(lc) * kWsChunk;
         const uint32_t t0 = uint32_t(ch0 + lc) * C;
 #pragma unroll
-        for (int x4 = 0; x4 < 4; ++x4) {
-            const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
-            R.kst[x4] = buf_ld16(rw_, cb + kWsK + uint32_t(r * DK + col) * 2u);
-        }
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                R.kt[2 * ib + kk] =
+                    buf_ld16(rw_, cb + kWsK + uint32_t(((2 * w + ib) * 2 + kk) * 64 + lane) * 16u);
 #pragma unroll
         for (int x = 0; x < KV; ++x) {
             // V pieces: 64 rows x VT columns in 16-byte pieces, VT / 8 per row; with
             // VT = 16 the upper half of the threads reads past the range (zeros, unused)
             const int id = tid + NT * x, r = id / (VT / 8), col = (id % (VT / 8)) * 8;
             const uint32_t off = VT >= 32 || id < C * VT / 8
-                                     ? ((t0 + r) * uint32_t(DV) + c0 + col) * 2u
-                                     : uint32_t(a.N) * uint32_t(DV) * 2u;
+                                     ? ((t0 + r) * uint32_t(DV) + c0 + col) * 2u : obytes;
             R.vst[x] = buf_ld16(rv, off);
         }
+        R.ast = buf_ld16(rw_, tid < DK / 4 ? cb + kWsA + uint32_t(tid) * 16u
+                                           : uint32_t(nloc) * kWsChunk);
         if (OUT) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
@@ -357,27 +389,19 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
             for (int kk = 0; kk < 2; ++kk)
                 R.pf[kk] = buf_ld16(rw_, cb + kWsP + uint32_t((w * 2 + kk) * 64 + lane) * 16u);
         }
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-            R.af[ib] = buf_ld16(rw_, cb + kWsA + uint32_t(16 * (2 * w + ib) + 4 * g) * 4u);
         __builtin_amdgcn_sched_barrier(0);
     };
     auto stage = [&](const ChainRegs<KV>& R, int buf) {
-#pragma unroll
-        for (int x4 = 0; x4 < 4; ++x4) {
-            const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
-            *reinterpret_cast<uint4*>(sm.kh[buf] + r * PQ + col) = R.kst[x4];
-        }
 #pragma unroll
         for (int x = 0; x < KV; ++x) {
             const int id = tid + NT * x, r = id / (VT / 8), col = (id % (VT / 8)) * 8;
             if (VT >= 32 || id < C * VT / 8)
                 *reinterpret_cast<uint4*>(sm.v[buf] + r * PV + col) = R.vst[x];
         }
+        if (tid < DK / 4) *reinterpret_cast<uint4*>(sm.a[buf] + 4 * tid) = R.ast;
     };
 
     auto process = [&](const ChainRegs<KV>& R, const ChainRegs<KV>& Rn, int lc, int cur) {
-        const uint16_t* kh = sm.kh[cur];
         const uint16_t* vv = sm.v[cur];
         if (OUT) {
             // O^T = S^T q^^T + V^T P^T for rows 16 w ..; 4 NVT contiguous columns per lane
@@ -389,22 +413,22 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
                 for (int kk = 0; kk < DK / 32; ++kk)
                     o_ = mfma16(frag_st<NVT>(sm.st[cur], PQ, 0, ct, 32 * kk, lane),
                                 __builtin_bit_cast(bf16x8_t, R.qf[kk]), o_);
-                o_ = mfma16(frag_kr_cols<NVT>(vv, PV, 0, 0, ct, lane),
+                o_ = mfma16(frag_v_pk<NVT>(vv, PV, 0, ct, lane),
                             __builtin_bit_cast(bf16x8_t, R.pf[0]), o_);
                 if (nk > 1)
-                    o_ = mfma16(frag_kr_cols<NVT>(vv, PV, 32, 0, ct, lane),
+                    o_ = mfma16(frag_v_pk<NVT>(vv, PV, 1, ct, lane),
                                 __builtin_bit_cast(bf16x8_t, R.pf[1]), o_);
                 ow[ct].x = pack_bf16x2(o_[0], o_[1]);
                 ow[ct].y = pack_bf16x2(o_[2], o_[3]);
             }
-            const uint32_t orow = (uint32_t(ch0 + lc) * C + rw) * uint32_t(DV) + c0 + 4 * NVT * g;
+            const uint32_t orow = ((uint32_t(ch0 + lc) * C + rw) * uint32_t(DV) + c0 + 4 * NVT * g) * 2u;
             if constexpr (NVT == 4) {
-                buf_st16(ro, orow * 2u, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
-                buf_st16(ro, orow * 2u + 16u, make_uint4(ow[2].x, ow[2].y, ow[3].x, ow[3].y));
+                buf_st16(ro, orow, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
+                buf_st16(ro, orow + 16u, make_uint4(ow[2].x, ow[2].y, ow[3].x, ow[3].y));
             } else if constexpr (NVT == 2) {
-                buf_st16(ro, orow * 2u, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
+                buf_st16(ro, orow, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
             } else {
-                buf_st8(ro, orow * 2u, ow[0]);
+                buf_st8(ro, orow, ow[0]);
             }
         }
         // S = diag(a) S + K^^T V (key rows 32 w ..)
@@ -416,19 +440,17 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
             const int i0 = 16 * (2 * w + ib);
-            const float4 a4 = __builtin_bit_cast(float4, R.af[ib]);
+            const float4 a4 = *reinterpret_cast<const float4*>(sm.a[cur] + i0 + 4 * g);
             const f32x4_t av = {a4.x, a4.y, a4.z, a4.w};
             if (!OUT) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) aprod[ib][j] *= av[j];
             }
-            const bf16x8_t k0f = frag_kr(kh, PQ, 0, i0, lane);
-            const bf16x8_t k1f = frag_kr(kh, PQ, 32, i0, lane);
 #pragma unroll
             for (int ct = 0; ct < NVT; ++ct) {
                 f32x4_t s_ = S[ib][ct] * av;
-                s_ = mfma16(k0f, vf[0][ct], s_);
-                s_ = mfma16(k1f, vf[1][ct], s_);
+                s_ = mfma16(__builtin_bit_cast(bf16x8_t, R.kt[2 * ib]), vf[0][ct], s_);
+                s_ = mfma16(__builtin_bit_cast(bf16x8_t, R.kt[2 * ib + 1]), vf[1][ct], s_);
                 S[ib][ct] = s_;
                 if (OUT) store_st<NVT>(sm.st[cur ^ 1], PQ, i0, 0, ct, s_, lane);
             }
@@ -437,19 +459,22 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
         lds_barrier();
     };
 
-    const int nloc = ch1 - ch0;
-    ChainRegs<KV> RA, RB;
+    // three register sets rotate: each chunk's loads go out two chunks before it is
+    // processed (a prefetch past the segment reads zeros and is never processed)
+    ChainRegs<KV> RA, RB, RC;
     load_chunk(RA, 0);
+    load_chunk(RB, 1);
     stage(RA, 0);
     lds_barrier();
-    // whole pairs: a chunk past the segment reads zeros (a = 0 would clear the state, so
-    // its update is skipped by the loop bound below, never by a branch between loads)
-    for (int lc = 0; lc < nloc; lc += 2) {
-        load_chunk(RB, lc + 1);
-        process(RA, RB, lc, 0);
+    for (int lc = 0; lc < nloc; lc += 3) {
+        load_chunk(RC, lc + 2);
+        process(RA, RB, lc, lc & 1);
         if (lc + 1 >= nloc) break;
-        load_chunk(RA, lc + 2);
-        process(RB, RA, lc + 1, 1);
+        load_chunk(RA, lc + 3);
+        process(RB, RC, lc + 1, (lc + 1) & 1);
+        if (lc + 2 >= nloc) break;
+        load_chunk(RB, lc + 4);
+        process(RC, RA, lc + 2, lc & 1);
     }
 
     if (OUT) {
@@ -475,7 +500,7 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
                     const int i = 16 * (2 * w + ib) + 4 * g + j, c = c0 + colmap<NVT>(ct, jl);
                     dS[size_t(i) * DV + c] = S[ib][ct][j];
                 }
-        if (mp.tile == 0 && jl == 0) {
+        if (tile == 0 && jl == 0) {
             float* A = a.A + (size_t(seq) * (a.nseg - 1) + seg) * DK;
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib)
@@ -488,25 +513,38 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
 // ---------------------------------------------------------------------------
 // scan over segments: S_in[j + 1] = diag(A_j) S_in[j] + dS_j, in place over dS_j
 // ---------------------------------------------------------------------------
+// One thread per 4 consecutive state elements; a sequence's blocks run on its XCD.
 __global__ __launch_bounds__(256) void gla_scan_kernel(GlaArgs a) {
     const int per_seq = DK * (a.DV / 4);
-    const size_t idx = size_t(blockIdx.x) * 256 + threadIdx.x;
-    if (idx >= size_t(a.nseq) * per_seq) return;
-    const size_t seq = idx / per_seq;
-    const int e = int(idx % per_seq), i = e / (a.DV / 4), c = (e % (a.DV / 4)) * 4;
+    const XcdMap mp = xcd_map(blockIdx.x, per_seq / 256, a.nseq);
+    if (!mp.valid) return;
+    const size_t seq = size_t(mp.seq);
+    const int e = mp.tile * 256 + int(threadIdx.x), i = e / (a.DV / 4), c = (e % (a.DV / 4)) * 4;
     const size_t so = size_t(i) * a.DV + c;
     float4 s = a.S0 ? *reinterpret_cast<const float4*>(a.S0 + seq * DK * a.DV + so)
                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    // all summaries are loaded before the dependent chain; up to kScanBatch at a time
     const int nsum = a.nseg - 1;
-    for (int j = 0; j < nsum; ++j) {
-        float4* d = reinterpret_cast<float4*>(a.dS + (seq * nsum + j) * DK * a.DV + so);
-        const float aj = a.A[(seq * nsum + j) * DK + i];
-        const float4 ds = *d;
-        s.x = aj * s.x + ds.x;
-        s.y = aj * s.y + ds.y;
-        s.z = aj * s.z + ds.z;
-        s.w = aj * s.w + ds.w;
-        *d = s;
+    constexpr int kScanBatch = 16;
+    for (int j0 = 0; j0 < nsum; j0 += kScanBatch) {
+        float4 ds[kScanBatch];
+        float aj[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) {
+            const int j = min(j0 + u, nsum - 1);
+            ds[u] = *reinterpret_cast<const float4*>(a.dS + (seq * nsum + j) * DK * a.DV + so);
+            aj[u] = a.A[(seq * nsum + j) * DK + i];
+        }
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) {
+            if (j0 + u < nsum) {
+                s.x = aj[u] * s.x + ds[u].x;
+                s.y = aj[u] * s.y + ds[u].y;
+                s.z = aj[u] * s.z + ds[u].z;
+                s.w = aj[u] * s.w + ds[u].w;
+                *reinterpret_cast<float4*>(a.dS + (seq * nsum + j0 + u) * DK * a.DV + so) = s;
+            }
+        }
     }
 }
 
@@ -560,8 +598,8 @@ hipError_t launch_nvt(const Problem& p) {
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_prep_kernel<GB>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
         if (e != hipSuccess) return e;
-        const size_t blocks = size_t(a.nseq) * size_t(a.nchunks);
-        if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
+        const size_t blocks = size_t(xcd_grid(a.nchunks, (a.nseq + 7) & ~7));
+        if (size_t(a.nseq + 7) * size_t(a.nchunks) > 0x7fffffffull) return hipErrorInvalidValue;
         gla_prep_kernel<GB><<<dim3(unsigned(blocks)), dim3(NT), smem, p.stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -570,17 +608,16 @@ hipError_t launch_nvt(const Problem& p) {
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_chain_kernel<false, NVT>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
         if (e != hipSuccess) return e;
-        gla_chain_kernel<false, NVT><<<dim3(xcd_grid(a.ntiles, a.nseq * (a.nseg - 1))), dim3(NT),
+        gla_chain_kernel<false, NVT><<<dim3(xcd_grid(a.ntiles * (a.nseg - 1), a.nseq)), dim3(NT),
                                        smem, p.stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        const size_t n = size_t(a.nseq) * DK * (p.dv / 4);
-        gla_scan_kernel<<<dim3(unsigned((n + 255) / 256)), dim3(256), 0, p.stream>>>(a);
+        gla_scan_kernel<<<dim3(xcd_grid(DK * (p.dv / 4) / 256, a.nseq)), dim3(256), 0, p.stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_chain_kernel<true, NVT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
     if (e != hipSuccess) return e;
-    gla_chain_kernel<true, NVT><<<dim3(xcd_grid(a.ntiles, a.nseq * a.nseg)), dim3(NT), smem,
+    gla_chain_kernel<true, NVT><<<dim3(xcd_grid(a.ntiles * a.nseg, a.nseq)), dim3(NT), smem,
                                   p.stream>>>(a);
     return hipGetLastError();
 }
