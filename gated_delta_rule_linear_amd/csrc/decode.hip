@@ -29,18 +29,23 @@ struct DecodeArgs {
     int io_bf16, gate_bf16;
 };
 
+// Threads per workgroup: a 64 KiB state tile streamed by 512 threads with nontemporal
+// 16-byte accesses measured 6.2 TB/s for an in-place read-modify-write on MI355X, against
+// 5.8 TB/s with 256 threads.
+constexpr int kDecodeThreads = 512;
+
 template <int DK, int DV>
 struct DecodeShape {
     static constexpr int NCG = DV / 4;                         // 4-column groups
-    static constexpr int RG_ALL = 256 / NCG;
+    static constexpr int RG_ALL = kDecodeThreads / NCG;
     static constexpr int RG = RG_ALL < DK ? RG_ALL : DK;       // row groups
     static constexpr int RPT = DK / RG;                        // rows per thread
     static constexpr int NT = NCG * RG;                        // threads per workgroup
-    static_assert(NT > 0 && NT <= 256 && RPT * RG == DK, "decode tiling");
+    static_assert(NT > 0 && NT <= kDecodeThreads && RPT * RG == DK, "decode tiling");
 };
 
 constexpr int decode_threads(int dk, int dv) {
-    return (dv / 4) * ((256 / (dv / 4)) < dk ? (256 / (dv / 4)) : dk);
+    return (dv / 4) * ((kDecodeThreads / (dv / 4)) < dk ? (kDecodeThreads / (dv / 4)) : dk);
 }
 
 template <int VAR, int DK, int DV>
