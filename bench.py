@@ -33,6 +33,12 @@ MAIN = "gla_bf16_b2h8_n2048_d128"
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2516.6    # dense bf16 MFMA, 256 CU x 4096 flop/clk x 2.4 GHz
 PROFILES = os.path.join(ROOT, "profiles")
+# the kernels one prefill step launches, per variant (the roofline covers the whole step)
+STEP_KERNELS = {
+    "gla": "gla_prep_kernel + gla_chain_kernel (summary) + gla_scan_kernel + gla_chain_kernel",
+    "kath": "kath_chain_kernel (summary) + kath_scan_kernel + kath_chain_kernel",
+    "gdn": "gdn_prep_kernel + gdn_fwd_kernel",
+}
 
 
 def log(msg):
@@ -341,8 +347,7 @@ def main():
         value, unit = m["Mtok_per_s"], "Mtok/s"
         roof = {"bound": "hbm", "achieved": m["GB_per_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": m["hbm_frac"], "traffic": load_traffic(main_name),
-                "kernel": ("diag_summary_kernel + diag_scan_kernel + diag_fwd_kernel"
-                           if wl.variant != "gdn" else "gdn_fwd_kernel"),
+                "kernel": STEP_KERNELS[wl.variant],
                 "duration_us": m["ms"] * 1e3,
                 "mfma": {"achieved": m["TFLOP_per_s"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": m["mfma_frac"]}}

@@ -102,7 +102,7 @@ int plan_prefill(const la_desc& d, Problem& p) {
     p.eps = d.eps;
     const bool mfma_ok = d.variant == LA_GDN   ? la::gdn_mfma_supported(d.dk, d.dv, p.io_bf16)
                          : d.variant == LA_GLA ? la::gla_mfma_supported(d.dk, d.dv, p.io_bf16)
-                                               : la::diag_mfma_supported(d.variant, d.dk, d.dv, p.io_bf16);
+                                               : la::kath_mfma_supported(d.dk, d.dv, p.io_bf16);
     int path = d.path;
     if (path == LA_PATH_AUTO) path = mfma_ok ? LA_PATH_MFMA : LA_PATH_VALU;
     if (path == LA_PATH_MFMA && !mfma_ok) return LA_ERR_UNSUPPORTED;
@@ -114,7 +114,7 @@ int plan_prefill(const la_desc& d, Problem& p) {
         const int nchunks = (d.N + p.chunk - 1) / p.chunk;
         int segs = d.segments > 0                 ? d.segments
                    : d.variant == LA_GLA ? la::gla_mfma_auto_segments(p)
-                                         : la::diag_mfma_auto_segments(p);
+                                         : la::kath_mfma_auto_segments(p);
         if (segs > nchunks) segs = nchunks;
         if (segs < 1) segs = 1;
         // equal segments of cps chunks; drop segments that would be empty
@@ -129,7 +129,7 @@ size_t workspace_for(const Problem& p) {
     if (p.path == LA_PATH_MFMA)
         return p.variant == LA_GDN   ? la::gdn_mfma_workspace_bytes(p)
                : p.variant == LA_GLA ? la::gla_mfma_workspace_bytes(p)
-                                     : la::diag_mfma_workspace_bytes(p);
+                                     : la::kath_mfma_workspace_bytes(p);
     return 0;
 }
 
@@ -233,7 +233,7 @@ int la_prefill(const la_desc* d, const void* q, const void* k, const void* v, co
     else if (p.path == LA_PATH_MFMA)
         err = gdn                     ? la::launch_prefill_gdn_mfma(p)
               : p.variant == LA_GLA ? la::launch_prefill_gla_mfma(p)
-                                    : la::launch_prefill_diag_mfma(p);
+                                    : la::launch_prefill_kath_mfma(p);
     else
         err = la::launch_prefill_valu(p);
     if (err == hipSuccess) err = hipGetLastError();

@@ -19,7 +19,7 @@ struct Problem {
     float eps = 0.f;
     int path = LA_PATH_VALU;  // resolved: VALU or MFMA
     int chunk = 16;           // resolved chunk size
-    int segments = 1;         // resolved segment count (KATH / GLA MFMA path)
+    int segments = 1;         // resolved segment count (KATH / GLA matrix-core path)
     const void *q = nullptr, *k = nullptr, *v = nullptr, *g = nullptr, *beta = nullptr;
     const float *S0 = nullptr, *z0 = nullptr;
     void* o = nullptr;
@@ -38,11 +38,11 @@ hipError_t launch_decode(const Problem& p);
 hipError_t launch_prefill_valu(const Problem& p);
 // state_init.hip: S_final <- S0 (or 0), z_final <- z0 (or 0), for N = 0
 hipError_t launch_state_init(const Problem& p);
-// prefill_diag_mfma.hip (KATH, GLA)
-bool diag_mfma_supported(int variant, int dk, int dv, bool io_bf16);
-size_t diag_mfma_workspace_bytes(const Problem& p);
-int diag_mfma_auto_segments(const Problem& p);
-hipError_t launch_prefill_diag_mfma(const Problem& p);
+// prefill_kath_mfma.hip (KATH)
+bool kath_mfma_supported(int dk, int dv, bool io_bf16);
+size_t kath_mfma_workspace_bytes(const Problem& p);
+int kath_mfma_auto_segments(const Problem& p);
+hipError_t launch_prefill_kath_mfma(const Problem& p);
 // prefill_gla_mfma.hip (GLA)
 bool gla_mfma_supported(int dk, int dv, bool io_bf16);
 size_t gla_mfma_workspace_bytes(const Problem& p);

@@ -1,0 +1,474 @@
+// Chunked prefill for normalized Katharopoulos linear attention (KATH: phi = ELU + 1,
+// "Linear / RNN 路线" section 2.1; "线性注意力与 SSM" section 02 for the normalized form
+// with epsilon) on bf16 MFMA, d_k = 128, chunk C = 64.
+//
+// Per chunk, with phi applied to q and k (padding rows are identity steps: phi rows 0)
+// and the state (S, z) entering the chunk:
+//   P_rs = phi(q_r) . phi(k_s)  (s <= r)
+//   o_r  = (phi(q_r)^T S + sum_s P_rs v_s) / (phi(q_r) . z + sum_s P_rs + eps)
+//   S   += sum_s phi(k_s) v_s^T,   z += sum_s phi(k_s)
+// an exact rewrite of the token recurrence with the post-update read. The transition is
+// the identity, so a sequence cuts into segments that run in parallel: the state
+// entering segment j is the sum of S0 and the earlier segments' summaries. Three
+// kernels, all placing one sequence's work on one XCD:
+//   summary  (sequence, segment < last, value tile): dS_j = sum phi(k)^T V over the
+//            segment and dz_j = sum phi(k);
+//   scan     (sequence, state element): S_in[j] and z_in[j] for every segment, in place
+//            over the summaries;
+//   forward  (sequence, segment, value tile): from (S_in[j], z_in[j]), per chunk the
+//            output and the state update; the last segment writes S_final and z_final.
+// phi is computed where the chunk is staged, in both chain kernels: it is one exponential
+// per element, cheaper than a pass that would write phi(q), phi(k) to memory.
+#include <cstddef>
+
+#include "la_internal.h"
+#include "mfma.hpp"
+
+namespace la {
+namespace {
+
+constexpr int DK = 128;
+constexpr int C = kMfmaChunk;  // 64
+constexpr int NT = 256;
+constexpr int PQ = DK + 8;     // pitch of [*][128] bf16 tiles
+constexpr int PC = C + 8;      // pitch of [*][64] bf16 tiles
+
+struct KathArgs {
+    const uint16_t *q, *k, *v;
+    const float *S0, *z0;
+    uint16_t* o;
+    float *S, *z;
+    float* dS;   // [nseq][nseg - 1][DK][DV]: summaries, then S_in[1 ..]
+    float* dz;   // [nseq][nseg - 1][DK]: likewise for z
+    float eps;
+    int N, nseq, nchunks, nseg, cps, ntiles, DV;
+};
+
+// The summary kernel uses only the fields up to `qt`, and is launched with that much
+// LDS.
+template <int VT>
+struct __align__(16) ChainSmem {
+    static constexpr int PV = VT + 8;
+    __align__(16) uint16_t kt[2][C * PQ];   // phi(k) [s][i]
+    __align__(16) uint16_t v[2][C * PV];    // V [s][c]
+    __align__(16) float zp[2][16][DK];      // per-thread-row-group column sums of phi(k)
+    __align__(16) float z[DK];              // z entering the chunk
+    __align__(16) uint16_t qt[2][C * PQ];   // phi(q) [r][i] (forward)
+    __align__(16) uint16_t st[2][VT * PQ];  // S^T [c][i], bf16 (forward)
+    __align__(16) uint16_t p[C * PC];       // P [r][s] (forward)
+    float psum[10][16];                     // row sums of the P tiles
+    float qz[C];                            // phi(q_r) . z
+};
+
+template <int KV>
+struct ChainRegs {
+    uint4 kst[4], qst[4], vst[KV];
+};
+
+template <bool OUT, int NVT>
+__global__ __launch_bounds__(NT) void kath_chain_kernel(KathArgs a) {
+    constexpr int VT = 16 * NVT;
+    constexpr int PV = ChainSmem<VT>::PV;
+    constexpr int KV = VT >= 32 ? VT / 32 : 1;   // 16-byte V pieces per thread
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    ChainSmem<VT>& sm = *reinterpret_cast<ChainSmem<VT>*>(smem_raw);
+
+    const int nrun = OUT ? a.nseg : a.nseg - 1;
+    const XcdMap mp = xcd_map(blockIdx.x, a.ntiles * nrun, a.nseq);
+    if (!mp.valid) return;
+    const int seq = mp.seq, seg = mp.tile / a.ntiles, tile = mp.tile % a.ntiles;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int g = lane >> 4, jl = lane & 15;
+    const int DV = a.DV;
+    const int c0 = tile * VT;
+    const size_t tok0 = size_t(seq) * size_t(a.N);
+    const int ch0 = seg * a.cps, ch1 = min(a.nchunks, ch0 + a.cps);
+    const int nloc = ch1 - ch0;
+    const int nsum = a.nseg - 1;
+    const int rw = 16 * w + jl;
+
+    // entering state
+    f32x4_t S[2][NVT];
+    const float* Sinit = nullptr;
+    const float* zinit = nullptr;
+    if (OUT) {
+        Sinit = seg == 0 ? (a.S0 ? a.S0 + size_t(seq) * DK * DV : nullptr)
+                         : a.dS + (size_t(seq) * nsum + seg - 1) * DK * DV;
+        zinit = seg == 0 ? (a.z0 ? a.z0 + size_t(seq) * DK : nullptr)
+                         : a.dz + (size_t(seq) * nsum + seg - 1) * DK;
+    }
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int ct = 0; ct < NVT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = 16 * (2 * w + ib) + 4 * g + j, c = c0 + colmap<NVT>(ct, jl);
+                S[ib][ct][j] = Sinit ? Sinit[size_t(i) * DV + c] : 0.f;
+            }
+    if (tid < DK) sm.z[tid] = zinit ? zinit[tid] : 0.f;
+    if (OUT) {
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct)
+                store_st<NVT>(sm.st[0], PQ, 16 * (2 * w + ib), 0, ct, S[ib][ct], lane);
+        // the P blocks above the diagonal that the row-block products read stay zero
+        if (w < 2) {
+            const int rb = w == 0 ? 0 : 2, sb = rb + 1;
+            const int r = 16 * rb + (lane >> 2), s = 16 * sb + (lane & 3) * 4;
+            *reinterpret_cast<uint2*>(sm.p + r * PC + s) = make_uint2(0, 0);
+        }
+    }
+
+    // Per-sequence resources: rows past the end of the sequence read as zero and
+    // output rows past it are dropped. Every load is unconditional.
+    const uint32_t obytes = uint32_t(a.N) * uint32_t(DV) * 2u;
+    const rsrc_t rq = make_rsrc(a.q + tok0 * DK, uint32_t(a.N) * DK * 2u);
+    const rsrc_t rk = make_rsrc(a.k + tok0 * DK, uint32_t(a.N) * DK * 2u);
+    const rsrc_t rv = make_rsrc(a.v + tok0 * DV, obytes);
+    const rsrc_t ro = make_rsrc(a.o + tok0 * DV, obytes);
+
+    auto load_chunk = [&](ChainRegs<KV>& R, int lc) {
+        const uint32_t t0 = uint32_t(ch0 + lc) * C;
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4) {
+            const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
+            R.kst[x4] = buf_ld16(rk, ((t0 + r) * DK + col) * 2u);
+            if (OUT) R.qst[x4] = buf_ld16(rq, ((t0 + r) * DK + col) * 2u);
+        }
+#pragma unroll
+        for (int x = 0; x < KV; ++x) {
+            const int id = tid + NT * x, r = id / (VT / 8), col = (id % (VT / 8)) * 8;
+            const uint32_t off = VT >= 32 || id < C * VT / 8
+                                     ? ((t0 + r) * uint32_t(DV) + c0 + col) * 2u : obytes;
+            R.vst[x] = buf_ld16(rv, off);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // phi of one chunk's q and k (zero on padding rows), V, and the column sums of phi(k)
+    auto stage = [&](const ChainRegs<KV>& R, int buf, int lc) {
+        const int n = min(C, a.N - (ch0 + lc) * C);
+        float zpart[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) zpart[q] = 0.f;
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4) {
+            const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
+            float f[8];
+            unpack8(R.kst[x4], f);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) { const float e = elu_plus_one_fast(f[q]); f[q] = r < n ? e : 0.f; }
+            const uint4 pk = pack8(f);
+            *reinterpret_cast<uint4*>(sm.kt[buf] + r * PQ + col) = pk;
+            unpack8(pk, f);   // z sums the bf16 features the matrix cores see
+#pragma unroll
+            for (int q = 0; q < 8; ++q) zpart[q] += f[q];
+            if (OUT) {
+                unpack8(R.qst[x4], f);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) { const float e = elu_plus_one_fast(f[q]); f[q] = r < n ? e : 0.f; }
+                *reinterpret_cast<uint4*>(sm.qt[buf] + r * PQ + col) = pack8(f);
+            }
+        }
+        const int col = (tid & 15) * 8;
+        *reinterpret_cast<float4*>(&sm.zp[buf][tid >> 4][col]) = make_float4(zpart[0], zpart[1], zpart[2], zpart[3]);
+        *reinterpret_cast<float4*>(&sm.zp[buf][tid >> 4][col + 4]) = make_float4(zpart[4], zpart[5], zpart[6], zpart[7]);
+#pragma unroll
+        for (int x = 0; x < KV; ++x) {
+            const int id = tid + NT * x, r = id / (VT / 8), vc = (id % (VT / 8)) * 8;
+            if (VT >= 32 || id < C * VT / 8)
+                *reinterpret_cast<uint4*>(sm.v[buf] + r * PV + vc) = R.vst[x];
+        }
+    };
+
+    auto process = [&](const ChainRegs<KV>& Rn, int lc, int cur) {
+        const uint16_t* kt = sm.kt[cur];
+        const uint16_t* vv = sm.v[cur];
+        if (OUT) {
+            const uint16_t* qt = sm.qt[cur];
+            // ---- P (10 lower tiles, row sums) and phi(q_r) . z
+            for (int ti = w; ti < 10; ti += 4) {
+                const int rb = ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3;
+                const int sb = ti - (rb * (rb + 1)) / 2;
+                f32x4_t acc = zero4();
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk)
+                    acc = mfma16(frag_kc(kt, PQ, 16 * sb, 32 * kk, lane),
+                                 frag_kc(qt, PQ, 16 * rb, 32 * kk, lane), acc);   // D[s][r]
+                const int r = 16 * rb + jl;
+                float rs = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int s = 16 * sb + 4 * g + j;
+                    acc[j] = s <= r ? acc[j] : 0.f;
+                    rs += acc[j];
+                }
+                store_dT(sm.p, PC, 16 * sb, 16 * rb, acc, lane);
+                rs += __shfl_xor(rs, 16, 64);
+                rs += __shfl_xor(rs, 32, 64);
+                if (g == 0) sm.psum[ti][jl] = rs;
+            }
+            {
+                // four threads per row, with the bf16 features
+                const int r = tid >> 2, part = tid & 3;
+                float acc = 0.f;
+#pragma unroll
+                for (int q8 = 0; q8 < 4; ++q8) {
+                    const int col = part * 32 + q8 * 8;
+                    float f[8];
+                    unpack8(*reinterpret_cast<const uint4*>(qt + r * PQ + col), f);
+                    const float4 z0 = *reinterpret_cast<const float4*>(sm.z + col);
+                    const float4 z1 = *reinterpret_cast<const float4*>(sm.z + col + 4);
+                    acc += f[0] * z0.x + f[1] * z0.y + f[2] * z0.z + f[3] * z0.w;
+                    acc += f[4] * z1.x + f[5] * z1.y + f[6] * z1.z + f[7] * z1.w;
+                }
+                acc += __shfl_xor(acc, 1, 64);
+                acc += __shfl_xor(acc, 2, 64);
+                if (part == 0) sm.qz[r] = acc;
+            }
+            lds_barrier();
+            // ---- O^T = S^T phi(Q)^T + V^T P^T, divided by the row's denominator
+            float den = sm.qz[rw] + a.eps;
+            const int tb = (w * (w + 1)) / 2;
+            for (int sb = 0; sb <= w; ++sb) den += sm.psum[tb + sb][jl];
+            const float inv = 1.f / den;
+            const int nk = w < 2 ? 1 : 2;
+            uint2 ow[NVT];
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct) {
+                f32x4_t o_ = zero4();
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk)
+                    o_ = mfma16(frag_st<NVT>(sm.st[cur], PQ, 0, ct, 32 * kk, lane),
+                                frag_kc(qt, PQ, 16 * w, 32 * kk, lane), o_);
+                for (int kk = 0; kk < nk; ++kk)
+                    o_ = mfma16(frag_kr_cols<NVT>(vv, PV, 32 * kk, 0, ct, lane),
+                                frag_kc(sm.p, PC, 16 * w, 32 * kk, lane), o_);
+                o_ = o_ * inv;
+                ow[ct].x = pack_bf16x2(o_[0], o_[1]);
+                ow[ct].y = pack_bf16x2(o_[2], o_[3]);
+            }
+            const uint32_t orow = ((uint32_t(ch0 + lc) * C + rw) * uint32_t(DV) + c0 + 4 * NVT * g) * 2u;
+            if constexpr (NVT == 4) {
+                buf_st16(ro, orow, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
+                buf_st16(ro, orow + 16u, make_uint4(ow[2].x, ow[2].y, ow[3].x, ow[3].y));
+            } else if constexpr (NVT == 2) {
+                buf_st16(ro, orow, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
+            } else {
+                buf_st8(ro, orow, ow[0]);
+            }
+        }
+        // ---- S += phi(K)^T V (key rows 32 w ..); z += column sums of phi(k)
+        bf16x8_t vf[2][NVT];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct) vf[kk][ct] = frag_kr_cols<NVT>(vv, PV, 32 * kk, 0, ct, lane);
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+            const int i0 = 16 * (2 * w + ib);
+            const bf16x8_t k0f = frag_kr(kt, PQ, 0, i0, lane);
+            const bf16x8_t k1f = frag_kr(kt, PQ, 32, i0, lane);
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct) {
+                f32x4_t s_ = mfma16(k0f, vf[0][ct], S[ib][ct]);
+                s_ = mfma16(k1f, vf[1][ct], s_);
+                S[ib][ct] = s_;
+                if (OUT) store_st<NVT>(sm.st[cur ^ 1], PQ, i0, 0, ct, s_, lane);
+            }
+        }
+        if (tid < DK) {
+            float zs = sm.z[tid];
+#pragma unroll
+            for (int rgp = 0; rgp < 16; ++rgp) zs += sm.zp[cur][rgp][tid];
+            sm.z[tid] = zs;
+        }
+        stage(Rn, cur ^ 1, lc + 1);
+        lds_barrier();
+    };
+
+    ChainRegs<KV> RA, RB, RC;
+    load_chunk(RA, 0);
+    load_chunk(RB, 1);
+    stage(RA, 0, 0);
+    lds_barrier();
+    for (int lc = 0; lc < nloc; lc += 3) {
+        load_chunk(RC, lc + 2);
+        process(RB, lc, lc & 1);
+        if (lc + 1 >= nloc) break;
+        load_chunk(RA, lc + 3);
+        process(RC, lc + 1, (lc + 1) & 1);
+        if (lc + 2 >= nloc) break;
+        load_chunk(RB, lc + 4);
+        process(RA, lc + 2, lc & 1);
+    }
+
+    if (OUT) {
+        if (seg == a.nseg - 1) {
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int ct = 0; ct < NVT; ++ct)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int i = 16 * (2 * w + ib) + 4 * g + j, c = c0 + colmap<NVT>(ct, jl);
+                        a.S[size_t(seq) * DK * DV + size_t(i) * DV + c] = S[ib][ct][j];
+                    }
+            if (tile == 0 && tid < DK) a.z[size_t(seq) * DK + tid] = sm.z[tid];
+        }
+    } else {
+        float* dS = a.dS + (size_t(seq) * nsum + seg) * DK * DV;
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = 16 * (2 * w + ib) + 4 * g + j, c = c0 + colmap<NVT>(ct, jl);
+                    dS[size_t(i) * DV + c] = S[ib][ct][j];
+                }
+        if (tile == 0 && tid < DK) a.dz[(size_t(seq) * nsum + seg) * DK + tid] = sm.z[tid];
+    }
+}
+
+// S_in[j + 1] = S_in[j] + dS_j and z_in[j + 1] = z_in[j] + dz_j, in place over the
+// summaries; one thread per 4 consecutive elements of S (the z row rides along with
+// the threads of column group 0).
+__global__ __launch_bounds__(256) void kath_scan_kernel(KathArgs a) {
+    const int per_seq = DK * (a.DV / 4);
+    const XcdMap mp = xcd_map(blockIdx.x, (per_seq + 255) / 256, a.nseq);
+    if (!mp.valid) return;
+    const int e = mp.tile * 256 + int(threadIdx.x);
+    if (e >= per_seq) return;
+    const size_t seq = size_t(mp.seq);
+    const int i = e / (a.DV / 4), c = (e % (a.DV / 4)) * 4;
+    const size_t so = size_t(i) * a.DV + c;
+    const int nsum = a.nseg - 1;
+    float4 s = a.S0 ? *reinterpret_cast<const float4*>(a.S0 + seq * DK * a.DV + so)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    const bool zrow = c == 0;
+    float z = zrow && a.z0 ? a.z0[seq * DK + i] : 0.f;
+    constexpr int kBatch = 16;
+    for (int j0 = 0; j0 < nsum; j0 += kBatch) {
+        float4 ds[kBatch];
+        float dz[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int j = min(j0 + u, nsum - 1);
+            ds[u] = *reinterpret_cast<const float4*>(a.dS + (seq * nsum + j) * DK * a.DV + so);
+            dz[u] = zrow ? a.dz[(seq * nsum + j) * DK + i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (j0 + u < nsum) {
+                s.x += ds[u].x; s.y += ds[u].y; s.z += ds[u].z; s.w += ds[u].w;
+                *reinterpret_cast<float4*>(a.dS + (seq * nsum + j0 + u) * DK * a.DV + so) = s;
+                if (zrow) {
+                    z += dz[u];
+                    a.dz[(seq * nsum + j0 + u) * DK + i] = z;
+                }
+            }
+        }
+    }
+}
+
+struct WsLayout {
+    size_t dS, dz, total;
+};
+WsLayout ws_layout(const Problem& p) {
+    const size_t nseq = size_t(p.B) * size_t(p.H);
+    const size_t nsum = size_t(p.segments > 1 ? p.segments - 1 : 0);
+    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    WsLayout L{};
+    L.dS = 0;
+    size_t off = al(nseq * nsum * DK * size_t(p.dv) * 4);
+    L.dz = off;
+    off += al(nseq * nsum * DK * 4);
+    L.total = nsum ? off : 0;
+    return L;
+}
+
+int pick_nvt(int dv) { return dv >= 64 ? 4 : dv / 16; }
+
+template <int NVT>
+hipError_t launch_nvt(const Problem& p) {
+    constexpr int VT = 16 * NVT;
+    const WsLayout L = ws_layout(p);
+    KathArgs a{};
+    a.q = static_cast<const uint16_t*>(p.q);
+    a.k = static_cast<const uint16_t*>(p.k);
+    a.v = static_cast<const uint16_t*>(p.v);
+    a.S0 = p.S0;
+    a.z0 = p.z0;
+    a.o = static_cast<uint16_t*>(p.o);
+    a.S = p.S;
+    a.z = p.z;
+    unsigned char* ws = static_cast<unsigned char*>(p.ws);
+    a.dS = ws ? reinterpret_cast<float*>(ws + L.dS) : nullptr;
+    a.dz = ws ? reinterpret_cast<float*>(ws + L.dz) : nullptr;
+    a.eps = p.eps;
+    a.N = p.N;
+    a.nseq = int(size_t(p.B) * size_t(p.H));
+    a.nchunks = (p.N + C - 1) / C;
+    a.nseg = p.segments;
+    a.cps = (a.nchunks + a.nseg - 1) / a.nseg;
+    a.DV = p.dv;
+    a.ntiles = p.dv / VT;
+    const size_t smem = sizeof(ChainSmem<VT>);
+    const size_t smem_sum = offsetof(ChainSmem<VT>, qt);
+    hipError_t e;
+    if (a.nseg > 1) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kath_chain_kernel<false, NVT>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(smem_sum));
+        if (e != hipSuccess) return e;
+        kath_chain_kernel<false, NVT><<<dim3(xcd_grid(a.ntiles * (a.nseg - 1), a.nseq)), dim3(NT),
+                                        smem_sum, p.stream>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int blocks = (DK * (p.dv / 4) + 255) / 256;
+        kath_scan_kernel<<<dim3(xcd_grid(blocks, a.nseq)), dim3(256), 0, p.stream>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kath_chain_kernel<true, NVT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+    if (e != hipSuccess) return e;
+    kath_chain_kernel<true, NVT><<<dim3(xcd_grid(a.ntiles * a.nseg, a.nseq)), dim3(NT), smem,
+                                   p.stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool kath_mfma_supported(int dk, int dv, bool io_bf16) {
+    return io_bf16 && dk == DK && (dv == 16 || dv == 32 || dv == 64 || dv == 128);
+}
+
+size_t kath_mfma_workspace_bytes(const Problem& p) { return ws_layout(p).total; }
+
+int kath_mfma_auto_segments(const Problem& p) {
+    // one forward workgroup per CU (its LDS takes most of a CU) over (sequence, segment,
+    // value tile), at least four chunks per segment
+    const size_t nseq = size_t(p.B) * size_t(p.H);
+    const size_t ntiles = size_t(p.dv / (16 * pick_nvt(p.dv)));
+    const size_t nchunks = size_t((p.N + C - 1) / C);
+    const size_t units = nseq * ntiles;
+    size_t want = (256 + units - 1) / units;
+    const size_t cap = nchunks / 4;
+    if (want > cap) want = cap;
+    return want < 1 ? 1 : int(want);
+}
+
+hipError_t launch_prefill_kath_mfma(const Problem& p) {
+    const size_t nseq = size_t(p.B) * size_t(p.H);
+    if (nseq > (1u << 24)) return hipErrorInvalidValue;
+    if (p.segments > 1 && !p.ws) return hipErrorInvalidValue;
+    // buffer offsets are 32-bit: one sequence's q / k / v / o rows
+    if (size_t(p.N) * DK * 2 >= (size_t(1) << 31)) return hipErrorInvalidValue;
+    switch (pick_nvt(p.dv)) {
+        case 1: return launch_nvt<1>(p);
+        case 2: return launch_nvt<2>(p);
+        default: return launch_nvt<4>(p);
+    }
+}
+
+}  // namespace la
