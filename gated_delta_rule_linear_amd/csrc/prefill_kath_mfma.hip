@@ -45,13 +45,13 @@ struct KathArgs {
 };
 
 // The summary kernel uses only the fields up to `qt`, and is launched with that much
-// LDS.
-template <int VT>
+// LDS. NW = waves per workgroup.
+template <int VT, int NW>
 struct __align__(16) ChainSmem {
     static constexpr int PV = VT + 8;
     __align__(16) uint16_t kt[2][C * PQ];   // phi(k) [s][i]
     __align__(16) uint16_t v[2][C * PV];    // V [s][c]
-    __align__(16) float zp[2][16][DK];      // per-thread-row-group column sums of phi(k)
+    __align__(16) float zp[2][NW][DK];      // per-wave column sums of phi(k)
     __align__(16) float z[DK];              // z entering the chunk
     __align__(16) uint16_t qt[2][C * PQ];   // phi(q) [r][i] (forward)
     __align__(16) uint16_t st[2][VT * PQ];  // S^T [c][i], bf16 (forward)
@@ -60,34 +60,43 @@ struct __align__(16) ChainSmem {
     float qz[C];                            // phi(q_r) . z
 };
 
-template <int KV>
+template <int KST, int KV>
 struct ChainRegs {
-    uint4 kst[4], qst[4], vst[KV];
+    uint4 kst[KST], qst[KST], vst[KV];
 };
 
-template <bool OUT, int NVT>
-__global__ __launch_bounds__(NT) void kath_chain_kernel(KathArgs a) {
-    constexpr int VT = 16 * NVT;
-    constexpr int PV = ChainSmem<VT>::PV;
-    constexpr int KV = VT >= 32 ? VT / 32 : 1;   // 16-byte V pieces per thread
+// A workgroup owns VT = 16 NVT CG value columns of one (sequence, segment) and runs
+// 4 CG waves: wave w takes row block rb = w % 4 (output rows 16 rb .., state key rows
+// 32 rb ..) of column group cg = w / 4 (16 NVT columns). The column groups share the
+// staged phi(q), phi(k), V and P.
+template <bool OUT, int NVT, int CG>
+__global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
+    constexpr int VT = 16 * NVT * CG;
+    constexpr int NW = 4 * CG, NTW = NT * CG;
+    constexpr int PV = ChainSmem<VT, NW>::PV;
+    constexpr int KST = 4 / CG;                      // 16-byte q / k pieces per thread
+    constexpr int VP = C * VT / 8;                   // 16-byte V pieces per chunk
+    constexpr int KV = VP >= NTW ? VP / NTW : 1;     // ... per thread
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    ChainSmem<VT>& sm = *reinterpret_cast<ChainSmem<VT>*>(smem_raw);
+    ChainSmem<VT, NW>& sm = *reinterpret_cast<ChainSmem<VT, NW>*>(smem_raw);
 
     const int nrun = OUT ? a.nseg : a.nseg - 1;
     const XcdMap mp = xcd_map(blockIdx.x, a.ntiles * nrun, a.nseq);
     if (!mp.valid) return;
     const int seq = mp.seq, seg = mp.tile / a.ntiles, tile = mp.tile % a.ntiles;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int rb = w & 3, cg = w >> 2;
     const int g = lane >> 4, jl = lane & 15;
     const int DV = a.DV;
+    const int cw = 16 * NVT * cg;              // the wave's first column in the tile
     const int c0 = tile * VT;
     const size_t tok0 = size_t(seq) * size_t(a.N);
     const int ch0 = seg * a.cps, ch1 = min(a.nchunks, ch0 + a.cps);
     const int nloc = ch1 - ch0;
     const int nsum = a.nseg - 1;
-    const int rw = 16 * w + jl;
+    const int rw = 16 * rb + jl;
 
-    // entering state
+    // entering state: key rows 16 (2 rb + ib) + 4 g + j, columns c0 + cw + colmap(ct, jl)
     f32x4_t S[2][NVT];
     const float* Sinit = nullptr;
     const float* zinit = nullptr;
@@ -103,7 +112,7 @@ __global__ __launch_bounds__(NT) void kath_chain_kernel(KathArgs a) {
         for (int ct = 0; ct < NVT; ++ct)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int i = 16 * (2 * w + ib) + 4 * g + j, c = c0 + colmap<NVT>(ct, jl);
+                const int i = 16 * (2 * rb + ib) + 4 * g + j, c = c0 + cw + colmap<NVT>(ct, jl);
                 S[ib][ct][j] = Sinit ? Sinit[size_t(i) * DV + c] : 0.f;
             }
     if (tid < DK) sm.z[tid] = zinit ? zinit[tid] : 0.f;
@@ -112,11 +121,11 @@ __global__ __launch_bounds__(NT) void kath_chain_kernel(KathArgs a) {
         for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
             for (int ct = 0; ct < NVT; ++ct)
-                store_st<NVT>(sm.st[0], PQ, 16 * (2 * w + ib), 0, ct, S[ib][ct], lane);
+                store_st<NVT>(sm.st[0], PQ, 16 * (2 * rb + ib), cw, ct, S[ib][ct], lane);
         // the P blocks above the diagonal that the row-block products read stay zero
         if (w < 2) {
-            const int rb = w == 0 ? 0 : 2, sb = rb + 1;
-            const int r = 16 * rb + (lane >> 2), s = 16 * sb + (lane & 3) * 4;
+            const int zb = w == 0 ? 0 : 2, sb = zb + 1;
+            const int r = 16 * zb + (lane >> 2), s = 16 * sb + (lane & 3) * 4;
             *reinterpret_cast<uint2*>(sm.p + r * PC + s) = make_uint2(0, 0);
         }
     }
@@ -129,32 +138,33 @@ __global__ __launch_bounds__(NT) void kath_chain_kernel(KathArgs a) {
     const rsrc_t rv = make_rsrc(a.v + tok0 * DV, obytes);
     const rsrc_t ro = make_rsrc(a.o + tok0 * DV, obytes);
 
-    auto load_chunk = [&](ChainRegs<KV>& R, int lc) {
+    auto load_chunk = [&](ChainRegs<KST, KV>& R, int lc) {
         const uint32_t t0 = uint32_t(ch0 + lc) * C;
 #pragma unroll
-        for (int x4 = 0; x4 < 4; ++x4) {
-            const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
+        for (int x4 = 0; x4 < KST; ++x4) {
+            const int x = tid + NTW * x4, r = x >> 4, col = (x & 15) * 8;
             R.kst[x4] = buf_ld16(rk, ((t0 + r) * DK + col) * 2u);
             if (OUT) R.qst[x4] = buf_ld16(rq, ((t0 + r) * DK + col) * 2u);
         }
 #pragma unroll
         for (int x = 0; x < KV; ++x) {
-            const int id = tid + NT * x, r = id / (VT / 8), col = (id % (VT / 8)) * 8;
-            const uint32_t off = VT >= 32 || id < C * VT / 8
-                                     ? ((t0 + r) * uint32_t(DV) + c0 + col) * 2u : obytes;
+            // V pieces, VT / 8 per row; threads past the pieces read past the range
+            const int id = tid + NTW * x, r = id / (VT / 8), col = (id % (VT / 8)) * 8;
+            const uint32_t off = id < VP ? ((t0 + r) * uint32_t(DV) + c0 + col) * 2u : obytes;
             R.vst[x] = buf_ld16(rv, off);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    // phi of one chunk's q and k (zero on padding rows), V, and the column sums of phi(k)
-    auto stage = [&](const ChainRegs<KV>& R, int buf, int lc) {
+    // phi of one chunk's q and k (zero on padding rows), V, and per-wave column sums
+    // of phi(k)
+    auto stage = [&](const ChainRegs<KST, KV>& R, int buf, int lc) {
         const int n = min(C, a.N - (ch0 + lc) * C);
         float zpart[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) zpart[q] = 0.f;
 #pragma unroll
-        for (int x4 = 0; x4 < 4; ++x4) {
-            const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
+        for (int x4 = 0; x4 < KST; ++x4) {
+            const int x = tid + NTW * x4, r = x >> 4, col = (x & 15) * 8;
             float f[8];
             unpack8(R.kst[x4], f);
 #pragma unroll
@@ -171,32 +181,39 @@ __global__ __launch_bounds__(NT) void kath_chain_kernel(KathArgs a) {
                 *reinterpret_cast<uint4*>(sm.qt[buf] + r * PQ + col) = pack8(f);
             }
         }
-        const int col = (tid & 15) * 8;
-        *reinterpret_cast<float4*>(&sm.zp[buf][tid >> 4][col]) = make_float4(zpart[0], zpart[1], zpart[2], zpart[3]);
-        *reinterpret_cast<float4*>(&sm.zp[buf][tid >> 4][col + 4]) = make_float4(zpart[4], zpart[5], zpart[6], zpart[7]);
+        // the four 16-lane groups of a wave hold the same columns: fold them first
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            zpart[q] += __shfl_xor(zpart[q], 16, 64);
+            zpart[q] += __shfl_xor(zpart[q], 32, 64);
+        }
+        if (g == 0) {
+            const int col = jl * 8;
+            *reinterpret_cast<float4*>(&sm.zp[buf][w][col]) = make_float4(zpart[0], zpart[1], zpart[2], zpart[3]);
+            *reinterpret_cast<float4*>(&sm.zp[buf][w][col + 4]) = make_float4(zpart[4], zpart[5], zpart[6], zpart[7]);
+        }
 #pragma unroll
         for (int x = 0; x < KV; ++x) {
-            const int id = tid + NT * x, r = id / (VT / 8), vc = (id % (VT / 8)) * 8;
-            if (VT >= 32 || id < C * VT / 8)
-                *reinterpret_cast<uint4*>(sm.v[buf] + r * PV + vc) = R.vst[x];
+            const int id = tid + NTW * x, r = id / (VT / 8), vc = (id % (VT / 8)) * 8;
+            if (id < VP) *reinterpret_cast<uint4*>(sm.v[buf] + r * PV + vc) = R.vst[x];
         }
     };
 
-    auto process = [&](const ChainRegs<KV>& Rn, int lc, int cur) {
+    auto process = [&](const ChainRegs<KST, KV>& Rn, int lc, int cur) {
         const uint16_t* kt = sm.kt[cur];
         const uint16_t* vv = sm.v[cur];
         if (OUT) {
             const uint16_t* qt = sm.qt[cur];
             // ---- P (10 lower tiles, row sums) and phi(q_r) . z
-            for (int ti = w; ti < 10; ti += 4) {
-                const int rb = ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3;
-                const int sb = ti - (rb * (rb + 1)) / 2;
+            for (int ti = w; ti < 10; ti += NW) {
+                const int pr = ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3;
+                const int sb = ti - (pr * (pr + 1)) / 2;
                 f32x4_t acc = zero4();
 #pragma unroll
                 for (int kk = 0; kk < DK / 32; ++kk)
                     acc = mfma16(frag_kc(kt, PQ, 16 * sb, 32 * kk, lane),
-                                 frag_kc(qt, PQ, 16 * rb, 32 * kk, lane), acc);   // D[s][r]
-                const int r = 16 * rb + jl;
+                                 frag_kc(qt, PQ, 16 * pr, 32 * kk, lane), acc);   // D[s][r]
+                const int r = 16 * pr + jl;
                 float rs = 0.f;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -204,18 +221,19 @@ __global__ __launch_bounds__(NT) void kath_chain_kernel(KathArgs a) {
                     acc[j] = s <= r ? acc[j] : 0.f;
                     rs += acc[j];
                 }
-                store_dT(sm.p, PC, 16 * sb, 16 * rb, acc, lane);
+                store_dT(sm.p, PC, 16 * sb, 16 * pr, acc, lane);
                 rs += __shfl_xor(rs, 16, 64);
                 rs += __shfl_xor(rs, 32, 64);
                 if (g == 0) sm.psum[ti][jl] = rs;
             }
             {
-                // four threads per row, with the bf16 features
-                const int r = tid >> 2, part = tid & 3;
+                // NTW / 64 threads per row, with the bf16 features
+                constexpr int TPR = NTW / C, CPT = DK / TPR;
+                const int r = tid / TPR, part = tid % TPR;
                 float acc = 0.f;
 #pragma unroll
-                for (int q8 = 0; q8 < 4; ++q8) {
-                    const int col = part * 32 + q8 * 8;
+                for (int q8 = 0; q8 < CPT / 8; ++q8) {
+                    const int col = part * CPT + q8 * 8;
                     float f[8];
                     unpack8(*reinterpret_cast<const uint4*>(qt + r * PQ + col), f);
                     const float4 z0 = *reinterpret_cast<const float4*>(sm.z + col);
@@ -223,33 +241,34 @@ __global__ __launch_bounds__(NT) void kath_chain_kernel(KathArgs a) {
                     acc += f[0] * z0.x + f[1] * z0.y + f[2] * z0.z + f[3] * z0.w;
                     acc += f[4] * z1.x + f[5] * z1.y + f[6] * z1.z + f[7] * z1.w;
                 }
-                acc += __shfl_xor(acc, 1, 64);
-                acc += __shfl_xor(acc, 2, 64);
+#pragma unroll
+                for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
                 if (part == 0) sm.qz[r] = acc;
             }
             lds_barrier();
             // ---- O^T = S^T phi(Q)^T + V^T P^T, divided by the row's denominator
             float den = sm.qz[rw] + a.eps;
-            const int tb = (w * (w + 1)) / 2;
-            for (int sb = 0; sb <= w; ++sb) den += sm.psum[tb + sb][jl];
+            const int tb = (rb * (rb + 1)) / 2;
+            for (int sb = 0; sb <= rb; ++sb) den += sm.psum[tb + sb][jl];
             const float inv = 1.f / den;
-            const int nk = w < 2 ? 1 : 2;
+            const int nk = rb < 2 ? 1 : 2;
             uint2 ow[NVT];
 #pragma unroll
             for (int ct = 0; ct < NVT; ++ct) {
                 f32x4_t o_ = zero4();
 #pragma unroll
                 for (int kk = 0; kk < DK / 32; ++kk)
-                    o_ = mfma16(frag_st<NVT>(sm.st[cur], PQ, 0, ct, 32 * kk, lane),
-                                frag_kc(qt, PQ, 16 * w, 32 * kk, lane), o_);
+                    o_ = mfma16(frag_st<NVT>(sm.st[cur], PQ, cw, ct, 32 * kk, lane),
+                                frag_kc(qt, PQ, 16 * rb, 32 * kk, lane), o_);
                 for (int kk = 0; kk < nk; ++kk)
-                    o_ = mfma16(frag_kr_cols<NVT>(vv, PV, 32 * kk, 0, ct, lane),
-                                frag_kc(sm.p, PC, 16 * w, 32 * kk, lane), o_);
+                    o_ = mfma16(frag_kr_cols<NVT>(vv, PV, 32 * kk, cw, ct, lane),
+                                frag_kc(sm.p, PC, 16 * rb, 32 * kk, lane), o_);
                 o_ = o_ * inv;
                 ow[ct].x = pack_bf16x2(o_[0], o_[1]);
                 ow[ct].y = pack_bf16x2(o_[2], o_[3]);
             }
-            const uint32_t orow = ((uint32_t(ch0 + lc) * C + rw) * uint32_t(DV) + c0 + 4 * NVT * g) * 2u;
+            const uint32_t orow =
+                ((uint32_t(ch0 + lc) * C + rw) * uint32_t(DV) + c0 + cw + 4 * NVT * g) * 2u;
             if constexpr (NVT == 4) {
                 buf_st16(ro, orow, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
                 buf_st16(ro, orow + 16u, make_uint4(ow[2].x, ow[2].y, ow[3].x, ow[3].y));
@@ -259,15 +278,15 @@ __global__ __launch_bounds__(NT) void kath_chain_kernel(KathArgs a) {
                 buf_st8(ro, orow, ow[0]);
             }
         }
-        // ---- S += phi(K)^T V (key rows 32 w ..); z += column sums of phi(k)
+        // ---- S += phi(K)^T V (key rows 32 rb ..); z += column sums of phi(k)
         bf16x8_t vf[2][NVT];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int ct = 0; ct < NVT; ++ct) vf[kk][ct] = frag_kr_cols<NVT>(vv, PV, 32 * kk, 0, ct, lane);
+            for (int ct = 0; ct < NVT; ++ct) vf[kk][ct] = frag_kr_cols<NVT>(vv, PV, 32 * kk, cw, ct, lane);
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
-            const int i0 = 16 * (2 * w + ib);
+            const int i0 = 16 * (2 * rb + ib);
             const bf16x8_t k0f = frag_kr(kt, PQ, 0, i0, lane);
             const bf16x8_t k1f = frag_kr(kt, PQ, 32, i0, lane);
 #pragma unroll
@@ -275,20 +294,20 @@ __global__ __launch_bounds__(NT) void kath_chain_kernel(KathArgs a) {
                 f32x4_t s_ = mfma16(k0f, vf[0][ct], S[ib][ct]);
                 s_ = mfma16(k1f, vf[1][ct], s_);
                 S[ib][ct] = s_;
-                if (OUT) store_st<NVT>(sm.st[cur ^ 1], PQ, i0, 0, ct, s_, lane);
+                if (OUT) store_st<NVT>(sm.st[cur ^ 1], PQ, i0, cw, ct, s_, lane);
             }
         }
         if (tid < DK) {
             float zs = sm.z[tid];
 #pragma unroll
-            for (int rgp = 0; rgp < 16; ++rgp) zs += sm.zp[cur][rgp][tid];
+            for (int ww = 0; ww < NW; ++ww) zs += sm.zp[cur][ww][tid];
             sm.z[tid] = zs;
         }
         stage(Rn, cur ^ 1, lc + 1);
         lds_barrier();
     };
 
-    ChainRegs<KV> RA, RB, RC;
+    ChainRegs<KST, KV> RA, RB, RC;
     load_chunk(RA, 0);
     load_chunk(RB, 1);
     stage(RA, 0, 0);
@@ -312,7 +331,8 @@ __global__ __launch_bounds__(NT) void kath_chain_kernel(KathArgs a) {
                 for (int ct = 0; ct < NVT; ++ct)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const int i = 16 * (2 * w + ib) + 4 * g + j, c = c0 + colmap<NVT>(ct, jl);
+                        const int i = 16 * (2 * rb + ib) + 4 * g + j;
+                        const int c = c0 + cw + colmap<NVT>(ct, jl);
                         a.S[size_t(seq) * DK * DV + size_t(i) * DV + c] = S[ib][ct][j];
                     }
             if (tile == 0 && tid < DK) a.z[size_t(seq) * DK + tid] = sm.z[tid];
@@ -325,7 +345,8 @@ __global__ __launch_bounds__(NT) void kath_chain_kernel(KathArgs a) {
             for (int ct = 0; ct < NVT; ++ct)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int i = 16 * (2 * w + ib) + 4 * g + j, c = c0 + colmap<NVT>(ct, jl);
+                    const int i = 16 * (2 * rb + ib) + 4 * g + j;
+                    const int c = c0 + cw + colmap<NVT>(ct, jl);
                     dS[size_t(i) * DV + c] = S[ib][ct][j];
                 }
         if (tile == 0 && tid < DK) a.dz[(size_t(seq) * nsum + seg) * DK + tid] = sm.z[tid];
@@ -389,11 +410,20 @@ WsLayout ws_layout(const Problem& p) {
     return L;
 }
 
-int pick_nvt(int dv) { return dv >= 64 ? 4 : dv / 16; }
+// Value tile: NVT 16-column tiles per wave times CG column groups. dv >= 64 takes
+// 64-column tiles on 8 waves (two column groups of 32): twice the waves of a 4-wave
+// tile for the same staged phi(q), phi(k), V and P.
+struct TileCfg {
+    int nvt, cg;
+};
+TileCfg pick_tile(int dv) {
+    if (dv >= 64) return {2, 2};
+    return {dv / 16, 1};
+}
 
-template <int NVT>
-hipError_t launch_nvt(const Problem& p) {
-    constexpr int VT = 16 * NVT;
+template <int NVT, int CG>
+hipError_t launch_cfg(const Problem& p) {
+    constexpr int VT = 16 * NVT * CG;
     const WsLayout L = ws_layout(p);
     KathArgs a{};
     a.q = static_cast<const uint16_t*>(p.q);
@@ -415,25 +445,26 @@ hipError_t launch_nvt(const Problem& p) {
     a.cps = (a.nchunks + a.nseg - 1) / a.nseg;
     a.DV = p.dv;
     a.ntiles = p.dv / VT;
-    const size_t smem = sizeof(ChainSmem<VT>);
-    const size_t smem_sum = offsetof(ChainSmem<VT>, qt);
+    using Sm = ChainSmem<VT, 4 * CG>;
+    const size_t smem = sizeof(Sm);
+    const size_t smem_sum = offsetof(Sm, qt);
     hipError_t e;
     if (a.nseg > 1) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kath_chain_kernel<false, NVT>),
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kath_chain_kernel<false, NVT, CG>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(smem_sum));
         if (e != hipSuccess) return e;
-        kath_chain_kernel<false, NVT><<<dim3(xcd_grid(a.ntiles * (a.nseg - 1), a.nseq)), dim3(NT),
-                                        smem_sum, p.stream>>>(a);
+        kath_chain_kernel<false, NVT, CG><<<dim3(xcd_grid(a.ntiles * (a.nseg - 1), a.nseq)),
+                                            dim3(NT * CG), smem_sum, p.stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int blocks = (DK * (p.dv / 4) + 255) / 256;
         kath_scan_kernel<<<dim3(xcd_grid(blocks, a.nseq)), dim3(256), 0, p.stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kath_chain_kernel<true, NVT>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kath_chain_kernel<true, NVT, CG>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
     if (e != hipSuccess) return e;
-    kath_chain_kernel<true, NVT><<<dim3(xcd_grid(a.ntiles * a.nseg, a.nseq)), dim3(NT), smem,
-                                   p.stream>>>(a);
+    kath_chain_kernel<true, NVT, CG><<<dim3(xcd_grid(a.ntiles * a.nseg, a.nseq)), dim3(NT * CG),
+                                       smem, p.stream>>>(a);
     return hipGetLastError();
 }
 
@@ -449,7 +480,8 @@ int kath_mfma_auto_segments(const Problem& p) {
     // one forward workgroup per CU (its LDS takes most of a CU) over (sequence, segment,
     // value tile), at least four chunks per segment
     const size_t nseq = size_t(p.B) * size_t(p.H);
-    const size_t ntiles = size_t(p.dv / (16 * pick_nvt(p.dv)));
+    const TileCfg t = pick_tile(p.dv);
+    const size_t ntiles = size_t(p.dv / (16 * t.nvt * t.cg));
     const size_t nchunks = size_t((p.N + C - 1) / C);
     const size_t units = nseq * ntiles;
     size_t want = (256 + units - 1) / units;
@@ -464,11 +496,9 @@ hipError_t launch_prefill_kath_mfma(const Problem& p) {
     if (p.segments > 1 && !p.ws) return hipErrorInvalidValue;
     // buffer offsets are 32-bit: one sequence's q / k / v / o rows
     if (size_t(p.N) * DK * 2 >= (size_t(1) << 31)) return hipErrorInvalidValue;
-    switch (pick_nvt(p.dv)) {
-        case 1: return launch_nvt<1>(p);
-        case 2: return launch_nvt<2>(p);
-        default: return launch_nvt<4>(p);
-    }
+    const TileCfg t = pick_tile(p.dv);
+    if (t.cg == 2) return launch_cfg<2, 2>(p);
+    return t.nvt == 1 ? launch_cfg<1, 1>(p) : launch_cfg<2, 1>(p);
 }
 
 }  // namespace la
