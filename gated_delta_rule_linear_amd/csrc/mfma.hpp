@@ -100,6 +100,29 @@ __device__ __forceinline__ bf16x8_t frag_kr_cols(const uint16_t* t, int pitch, i
     const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8_t, v);
 }
+// As frag_kr_cols for K = 32 kk .. 32 kk + 31, with the K slots in the order in which
+// the matrix cores return a pair of 16 x 16 tiles of a 32-wide K range: slots 0..3 are
+// K = 32 kk + 4 g + 0..3, slots 4..7 are K = 32 kk + 16 + 4 g + 0..3. Paired with a
+// fragment packed straight from two D tiles (D rows = that K range), no transpose of
+// the tiles is needed.
+template <int NVT>
+__device__ __forceinline__ bf16x8_t frag_kr_cols_pk(const uint16_t* t, int pitch, int kk, int cb,
+                                                    int ct, int lane) {
+    const int g = lane >> 4, L = lane & 15;
+    const uint16_t* p = t + (32 * kk + 4 * g + (L >> 2)) * pitch + cb + colmap<NVT>(ct, 4 * (L & 3));
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 16 * pitch));
+    const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+// B fragment packed from two D tiles d0 (K = 32 kk + 4 g ..) and d1 (K = 32 kk + 16 + 4 g ..)
+// in the slot order of frag_kr_cols_pk.
+__device__ __forceinline__ bf16x8_t pack_pk(f32x4_t d0, f32x4_t d1) {
+    const uint4 w = make_uint4(pack_bf16x2(d0[0], d0[1]), pack_bf16x2(d0[2], d0[3]),
+                               pack_bf16x2(d1[0], d1[1]), pack_bf16x2(d1[2], d1[3]));
+    return __builtin_bit_cast(bf16x8_t, w);
+}
+
 // Fragment from a row-major [columns][K] bf16 tile (S^T) whose M index is tile ct's
 // columns.
 template <int NVT>

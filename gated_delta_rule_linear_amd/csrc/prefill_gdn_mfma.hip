@@ -21,21 +21,21 @@
 // the off-diagonal products run on the matrix cores in bf16 with fp32 accumulation.
 //
 // Two kernels:
-//   prep     one workgroup per (sequence, chunk), fully parallel: T = (I + L)^{-1} and
-//            the decayed, causally masked score tile P_rs = exp(c_r - c_s) q_r.k_s
-//            (s <= r) of every chunk, written to the workspace in bf16 and in MFMA
-//            fragment order (neither depends on the state);
+//   prep     one workgroup per (sequence, chunk), fully parallel: T = (I + L)^{-1} of
+//            every chunk, written to the workspace in bf16 and in MFMA fragment order
+//            (T depends only on the chunk's k, alpha, beta, never on the state);
 //   forward  one workgroup per (sequence, value tile): walks the chunks in order with
 //            its fp32 state tile in MFMA accumulators. Columns of S never mix, so value
 //            tiles are independent chains; the tiles of one sequence share an XCD so
 //            their q/k/T/P reads hit the same L2.
-// Per chunk the forward kernel has three barriers: (S^T q, S^T k) -> X | U = T X |
-// O = gamma (S^T q) + P U and S = gamma_last S + K^T U^. Each wave loads the
-// operands that only it uses (rows of T, P, V; its own alpha/beta) straight into
-// registers in fragment layout through per-sequence buffer resources, two chunks
-// ahead; K and the bf16 copy of S^T are shared through LDS. Ragged tails need no
-// branches: buffer loads past the sequence read zeros and stores past it are
-// dropped.
+// Per chunk the forward kernel has three barriers: (S^T q, S^T k) -> X | U = T X and
+// the causal score tile P_rs = exp(c_r - c_s) q_r.k_s (s <= r) of the wave's rows |
+// O = gamma (S^T q) + P U and S = gamma_last S + K^T U^. Each wave loads the operands
+// that only it uses (rows of q, T, V; its own alpha/beta) straight into registers in
+// fragment layout through per-sequence buffer resources, two chunks ahead; K and the
+// bf16 copy of S^T are shared through LDS. P stays in registers in the order the
+// matrix cores return it. Ragged tails need no branches: buffer loads past the
+// sequence read zeros and stores past it are dropped.
 //
 // Fragments whose K index runs along tile rows use the LDS transpose read; result
 // tiles are written to LDS with 8-byte stores.
@@ -55,9 +55,7 @@ constexpr int PY = 32 + 8;     // pitch of the bf16 32-row scratch tiles
 
 struct __align__(16) PrepSmem {
     __align__(16) uint16_t k[C * PQ];
-    __align__(16) uint16_t q[C * PQ];
     __align__(16) uint16_t t[C * PC];      // T [r][s]
-    __align__(16) uint16_t p[C * PC];      // P [r][s] = exp(c_r - c_s) q_r.k_s, s <= r
     __align__(16) uint16_t lo[C * PC];     // off-diagonal blocks of L [r][s]
     __align__(16) uint16_t ya[2][32 * PY];  // level-a scratch: Y = L_ij T_jj (16 rows used)
     __align__(16) uint16_t yb[32 * PY];    // level-b scratch: Y = L[32:64, 0:32] A^{-1}
@@ -73,6 +71,7 @@ struct __align__(16) FwdSmem {
     __align__(16) uint16_t x[C * PV];      // X [s][c]
     __align__(16) uint16_t u[C * PV];      // U [s][c]
     __align__(16) uint16_t uh[C * PV];     // U scaled by exp(c_last - c_s)
+    __align__(16) float cum[8][C];         // each wave's prefix sums of log alpha
 };
 
 struct GdnArgs {
@@ -81,7 +80,7 @@ struct GdnArgs {
     const float* S0;
     uint16_t* o;
     float* S;
-    uint16_t* T;   // workspace: [nseq][nchunks][2][64][64] bf16, T then P per chunk
+    uint16_t* T;   // workspace: [nseq][nchunks][64][64] bf16, T per chunk
     int N, nseq, ntiles, nchunks, gate_bf16;
 };
 
@@ -114,12 +113,11 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
     const size_t tok0 = seq * size_t(a.N);
 
     // loads from clamped rows (always valid), padding applied when staging
-    uint4 kv[4], qv[4];
+    uint4 kv[4];
 #pragma unroll
     for (int x4 = 0; x4 < 4; ++x4) {
         const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
         kv[x4] = ld_g16(a.k + (tok0 + t0 + min(r, n - 1)) * DK + col);
-        qv[x4] = ld_g16(a.q + (tok0 + t0 + min(r, n - 1)) * DK + col);
     }
     uint32_t graw = 0;
     if (w < 2) graw = ld_gate_raw<GB>(w == 0 ? a.alpha : a.beta, tok0 + t0 + min(lane, n - 1));
@@ -127,7 +125,6 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
     for (int x4 = 0; x4 < 4; ++x4) {
         const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
         *reinterpret_cast<uint4*>(sm.k + r * PQ + col) = r < n ? kv[x4] : zero_u4();
-        *reinterpret_cast<uint4*>(sm.q + r * PQ + col) = r < n ? qv[x4] : zero_u4();
     }
     if (w == 0) {
         const float lg = fast_log(gate_val<GB>(graw));
@@ -136,14 +133,12 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
     } else if (w == 1) {
         sm.beta[lane] = lane < n ? gate_val<GB>(graw) : 0.f;
     } else {
-        // zero the six upper blocks of T and P and the unused rows of the level-a scratch
+        // zero the six upper blocks of T and the unused rows of the level-a scratch
         const int r = lane >> 2, cc = (lane & 3) * 4;
         const int ub[6][2] = {{0, 1}, {0, 2}, {0, 3}, {1, 2}, {1, 3}, {2, 3}};
-        for (int x = w - 2; x < 6; x += 2) {
-            const int off = (16 * ub[x][0] + r) * PC + 16 * ub[x][1] + cc;
-            *reinterpret_cast<uint2*>(sm.t + off) = make_uint2(0, 0);
-            *reinterpret_cast<uint2*>(sm.p + off) = make_uint2(0, 0);
-        }
+        for (int x = w - 2; x < 6; x += 2)
+            *reinterpret_cast<uint2*>(sm.t + (16 * ub[x][0] + r) * PC + 16 * ub[x][1] + cc) =
+                make_uint2(0, 0);
         uint16_t* y = sm.ya[w - 2];
         for (int x = lane; x < 32 * PY / 4; x += 64) *reinterpret_cast<uint2*>(y + 4 * x) = make_uint2(0, 0);
     }
@@ -195,36 +190,21 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
         for (int r = 0; r < 16; ++r) sm.t[(16 * b + r) * PC + 16 * b + jc] = f32_to_bf16(tc[r]);
     } else {
         // waves 1..3: the six off-diagonal L blocks (bf16): D'[s][r] = k_s . k_r -> lo[r][s..]
-        // and the ten lower blocks of P: D'[s][r] = k_s . q_r -> p[r][s..]
-        for (int task = w - 1; task < 16; task += 3) {
-            const bool is_p = task >= 6;
-            const int pt = is_p ? task - 6 : task;
-            int rb, sb;
-            if (is_p) {
-                rb = pt < 1 ? 0 : pt < 3 ? 1 : pt < 6 ? 2 : 3;
-                sb = pt - (rb * (rb + 1)) / 2;
-            } else {
-                rb = pt < 1 ? 1 : pt < 3 ? 2 : 3;
-                sb = pt - (rb * (rb - 1)) / 2;
-            }
-            const uint16_t* rsrc = is_p ? sm.q : sm.k;
+        for (int task = w - 1; task < 6; task += 3) {
+            const int rb = task < 1 ? 1 : task < 3 ? 2 : 3;
+            const int sb = task - (rb * (rb - 1)) / 2;
             f32x4_t d = zero4();
 #pragma unroll
             for (int kk = 0; kk < DK / 32; ++kk)
                 d = mfma16(frag_kc(sm.k, PQ, 16 * sb, 32 * kk, lane),
-                           frag_kc(rsrc, PQ, 16 * rb, 32 * kk, lane), d);
+                           frag_kc(sm.k, PQ, 16 * rb, 32 * kk, lane), d);
             const int r = 16 * rb + jl;
-            const float cr = sm.cum[r];
-            const float br = is_p ? 1.f : sm.beta[r];
+            const float cr = sm.cum[r], br = sm.beta[r];
             const float4 cs = *reinterpret_cast<const float4*>(sm.cum + 16 * sb + 4 * g);
             const float csv[4] = {cs.x, cs.y, cs.z, cs.w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int s = 16 * sb + 4 * g + j;
-                const float e = br * fast_exp(cr - csv[j]) * d[j];
-                d[j] = s <= r ? e : 0.f;   // L blocks are strictly below the diagonal
-            }
-            store_dT(is_p ? sm.p : sm.lo, PC, 16 * sb, 16 * rb, d, lane);
+            for (int j = 0; j < 4; ++j) d[j] *= br * fast_exp(cr - csv[j]);
+            store_dT(sm.lo, PC, 16 * sb, 16 * rb, d, lane);
         }
     }
     lds_barrier();
@@ -259,16 +239,15 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
         store_dT(sm.t, PC, 16 * jb, 32 + 16 * rb, -d, lane);
     }
     lds_barrier();
-    // T then P, each in fragment order: 16-byte piece (rb, kk, lane = 16 g + j) holds
-    // row 16 rb + j, columns 32 kk + 8 g .. + 7, so that a wave of the forward kernel
-    // reads its B fragment as one contiguous kilobyte
-    uint16_t* Tg = a.T + (seq * a.nchunks + ch) * size_t(2 * C * C);
+    // T in fragment order: 16-byte piece (rb, kk, lane = 16 g + j) holds row 16 rb + j,
+    // columns 32 kk + 8 g .. + 7, so that a wave of the forward kernel reads its B
+    // fragment as one contiguous kilobyte
+    uint16_t* Tg = a.T + (seq * a.nchunks + ch) * size_t(C * C);
 #pragma unroll
     for (int x2 = 0; x2 < 2; ++x2) {
         const int x = tid + NT * x2, rb = x >> 7, kk = (x >> 6) & 1, l = x & 63;
         const int off = (16 * rb + (l & 15)) * PC + 32 * kk + 8 * (l >> 4);
         *reinterpret_cast<uint4*>(Tg + 8 * x) = *reinterpret_cast<const uint4*>(sm.t + off);
-        *reinterpret_cast<uint4*>(Tg + C * C + 8 * x) = *reinterpret_cast<const uint4*>(sm.p + off);
     }
 }
 
@@ -276,12 +255,12 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
 // forward kernel
 // ---------------------------------------------------------------------------
 // Per-chunk operands a wave reads straight from global memory in MFMA fragment layout
-// (lane = 16 g + j): rows 16 rb + j of q, T and P, K halves 8 g .. 8 g + 7 of each
-// 32-wide slice; V at the X tile's D layout; the chunk's alpha / beta at lane = token;
-// and this thread's share of the chunk's K rows for the LDS copy.
+// (lane = 16 g + j): rows 16 rb + j of q and T, K halves 8 g .. 8 g + 7 of each 32-wide
+// slice; V at the X tile's D layout; the chunk's alpha / beta at lane = token; and this
+// thread's share of the chunk's K rows for the LDS copy.
 template <int NVT, int KST>
 struct ChunkRegs {
-    uint4 q[4], t[2], p[2], kst[KST];
+    uint4 q[4], t[2], kst[KST];
     uint2 v[NVT];
     uint32_t ga, gb;
 };
@@ -289,8 +268,8 @@ struct ChunkRegs {
 // Forward kernel. A workgroup owns VT = 16 NVT CG value columns of one sequence and
 // runs 4 CG waves: wave w works on row block rb = w % 4 of every chunk (rows of q, T, P,
 // key rows 32 rb .. of S) for column group cg = w / 4 (16 NVT columns). The CG column
-// groups share the LDS copy of K and load the same q / T / P lines, so a wider group
-// cuts the vector-memory traffic per column.
+// groups share the LDS copy of K and load the same q / T lines, so a wider group cuts
+// the vector-memory traffic per column.
 template <int NVT, int CG, bool GB>
 __global__ __launch_bounds__(NT * CG) void gdn_fwd_kernel(GdnArgs a) {
     constexpr int VT = 16 * NVT * CG;
@@ -337,8 +316,8 @@ __global__ __launch_bounds__(NT * CG) void gdn_fwd_kernel(GdnArgs a) {
     const rsrc_t rk = make_rsrc(a.k + tok0 * DK, uint32_t(a.N) * DK * 2u);
     const rsrc_t rv = make_rsrc(a.v + tok0 * DV, uint32_t(a.N) * uint32_t(DV) * 2u);
     const rsrc_t ro = make_rsrc(a.o + tok0 * DV, uint32_t(a.N) * uint32_t(DV) * 2u);
-    const rsrc_t rt = make_rsrc(a.T + seq * nchunks * size_t(2 * C * C),
-                                uint32_t(nchunks) * (2u * C * C * 2u));
+    const rsrc_t rt = make_rsrc(a.T + seq * nchunks * size_t(C * C),
+                                uint32_t(nchunks) * (C * C * 2u));
     constexpr uint32_t GS = GB ? 2u : 4u;
     const rsrc_t ra = make_rsrc(static_cast<const char*>(a.alpha) + tok0 * GS, uint32_t(a.N) * GS);
     const rsrc_t rb_ = make_rsrc(static_cast<const char*>(a.beta) + tok0 * GS, uint32_t(a.N) * GS);
@@ -355,12 +334,9 @@ __global__ __launch_bounds__(NT * CG) void gdn_fwd_kernel(GdnArgs a) {
         const uint32_t oq = ((t0 + rw) * DK + 8 * g) * 2u;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) R.q[kk] = buf_ld16(rq, oq + 64u * kk);
-        const uint32_t ot = (uint32_t(ch) * (2 * C * C) + (2 * rb * 64 + lane) * 8) * 2u;
+        const uint32_t ot = (uint32_t(ch) * (C * C) + (2 * rb * 64 + lane) * 8) * 2u;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            R.t[kk] = buf_ld16(rt, ot + 1024u * kk);
-            R.p[kk] = buf_ld16(rt, ot + (C * C) * 2u + 1024u * kk);
-        }
+        for (int kk = 0; kk < 2; ++kk) R.t[kk] = buf_ld16(rt, ot + 1024u * kk);
         const uint32_t ov = ((t0 + rw) * uint32_t(DV) + c0 + colmap<NVT>(0, 4 * g)) * 2u;
         if constexpr (NVT == 2) {
             const uint4 v4 = buf_ld16(rv, ov);
@@ -398,6 +374,7 @@ __global__ __launch_bounds__(NT * CG) void gdn_fwd_kernel(GdnArgs a) {
         const float gr = fast_exp(cr);
         const float dr = fast_exp(clast - cr);
         const float glast = fast_exp(clast);
+        sm.cum[w][lane] = cum;   // read back by this wave only (for the P tiles)
 
         // ---- (S^T Q^T) and (S^T K^T) for rows 16 rb .. : D[c][r]; the S^T fragment
         // is shared by both products
@@ -439,17 +416,36 @@ __global__ __launch_bounds__(NT * CG) void gdn_fwd_kernel(GdnArgs a) {
             store_rows<NVT>(sm.u, PV, cw, ct, 16 * rb, u_, lane);
             store_rows<NVT>(sm.uh, PV, cw, ct, 16 * rb, u_ * dr, lane);
         }
+        // ---- P^T tiles of rows 16 rb ..: D[s][r] = exp(c_r - c_s) k_s . q_r (s <= r),
+        // kept as B fragments in the order the matrix cores return them
+        f32x4_t pt[4];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+            pt[sb] = zero4();
+            if (sb <= rb) {
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk)
+                    pt[sb] = mfma16(frag_kc(kc, PQ, 16 * sb, 32 * kk, lane),
+                                    __builtin_bit_cast(bf16x8_t, R.q[kk]), pt[sb]);
+                const float4 cs = *reinterpret_cast<const float4*>(sm.cum[w] + 16 * sb + 4 * g);
+                const float csv[4] = {cs.x, cs.y, cs.z, cs.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int s = 16 * sb + 4 * g + j;
+                    const float e = fast_exp(cr - csv[j]) * pt[sb][j];
+                    pt[sb][j] = s <= rw ? e : 0.f;
+                }
+            }
+        }
+        const bf16x8_t pf0 = pack_pk(pt[0], pt[1]), pf1 = pack_pk(pt[2], pt[3]);
         lds_barrier();
 
         // ---- O^T = gamma_r (S^T Q^T) + U^T P^T -> o rows 16 rb ..
         uint2 ow[NVT];
 #pragma unroll
         for (int ct = 0; ct < NVT; ++ct) {
-            f32x4_t o_ = mfma16(frag_kr_cols<NVT>(sm.u, PV, 0, cw, ct, lane),
-                                __builtin_bit_cast(bf16x8_t, R.p[0]), oq[ct] * gr);
-            if (nk > 1)
-                o_ = mfma16(frag_kr_cols<NVT>(sm.u, PV, 32, cw, ct, lane),
-                            __builtin_bit_cast(bf16x8_t, R.p[1]), o_);
+            f32x4_t o_ = mfma16(frag_kr_cols_pk<NVT>(sm.u, PV, 0, cw, ct, lane), pf0, oq[ct] * gr);
+            if (nk > 1) o_ = mfma16(frag_kr_cols_pk<NVT>(sm.u, PV, 1, cw, ct, lane), pf1, o_);
             ow[ct].x = pack_bf16x2(o_[0], o_[1]);
             ow[ct].y = pack_bf16x2(o_[2], o_[3]);
         }
@@ -571,7 +567,7 @@ bool gdn_mfma_supported(int dk, int dv, bool io_bf16) {
 
 size_t gdn_mfma_workspace_bytes(const Problem& p) {
     const size_t nchunks = size_t((p.N + C - 1) / C);
-    return size_t(p.B) * size_t(p.H) * nchunks * 2 * C * C * sizeof(uint16_t);
+    return size_t(p.B) * size_t(p.H) * nchunks * C * C * sizeof(uint16_t);
 }
 
 hipError_t launch_prefill_gdn_mfma(const Problem& p) {

@@ -282,19 +282,6 @@ struct __align__(16) ChainSmem {
     __align__(16) float a[2][DK];           // chunk decay exp(B_last)
 };
 
-// A fragment of V^T (rows = tile ct's value columns) whose K order matches the P
-// pieces: slots 0..3 are tokens 32 kk + 4 g + 0..3, slots 4..7 tokens 32 kk + 16 + 4 g + 0..3.
-template <int NVT>
-__device__ __forceinline__ bf16x8_t frag_v_pk(const uint16_t* t, int pitch, int kk, int ct,
-                                              int lane) {
-    const int g = lane >> 4, L = lane & 15;
-    const uint16_t* p = t + (32 * kk + 4 * g + (L >> 2)) * pitch + colmap<NVT>(ct, 4 * (L & 3));
-    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
-    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 16 * pitch));
-    const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8_t, v);
-}
-
 // One chunk's operands in registers: the wave's k^T fragments (state update, key rows
 // 32 w ..), q^ and P fragments (forward), this thread's V pieces and decay piece for the
 // LDS copies.
@@ -413,10 +400,10 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
                 for (int kk = 0; kk < DK / 32; ++kk)
                     o_ = mfma16(frag_st<NVT>(sm.st[cur], PQ, 0, ct, 32 * kk, lane),
                                 __builtin_bit_cast(bf16x8_t, R.qf[kk]), o_);
-                o_ = mfma16(frag_v_pk<NVT>(vv, PV, 0, ct, lane),
+                o_ = mfma16(frag_kr_cols_pk<NVT>(vv, PV, 0, 0, ct, lane),
                             __builtin_bit_cast(bf16x8_t, R.pf[0]), o_);
                 if (nk > 1)
-                    o_ = mfma16(frag_v_pk<NVT>(vv, PV, 1, ct, lane),
+                    o_ = mfma16(frag_kr_cols_pk<NVT>(vv, PV, 1, 0, ct, lane),
                                 __builtin_bit_cast(bf16x8_t, R.pf[1]), o_);
                 ow[ct].x = pack_bf16x2(o_[0], o_[1]);
                 ow[ct].y = pack_bf16x2(o_[2], o_[3]);
