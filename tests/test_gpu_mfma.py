@@ -89,6 +89,28 @@ def test_mfma_gate_kinds(variant, kind):
     check(inp, run_gpu(inp), run_oracle(inp))
 
 
+@pytest.mark.parametrize("variant", ["gla", "gdn"])
+@pytest.mark.parametrize("N", [70, 449])
+def test_mfma_fp32_gates(variant, N):
+    """bf16 q, k, v with fp32 gates (the other gate storage the ABI accepts)."""
+    wl = wl_for(variant, 1, 2, N, 64, seed=N + 1).with_(gate_io="f32")
+    inp = W.make_inputs(wl, with_state=True)
+    assert inp.dev["g"].dtype == np.float32
+    banner(f"mfma {variant} fp32 gates N={N}")
+    check(inp, run_gpu(inp), run_oracle(inp))
+
+
+@pytest.mark.parametrize("variant", ["kath", "gla", "gdn"])
+@pytest.mark.parametrize("segments", [3, 7])
+def test_mfma_wide_tiles_segments(variant, segments):
+    """d_v = 128 (the widest value tiles) with an explicit segment count and a ragged
+    last chunk; GDN ignores the segment count."""
+    inp = W.make_inputs(wl_for(variant, 1, 3, 64 * 13 + 9, 128, seed=40 + segments),
+                        with_state=True)
+    banner(f"mfma {variant} dv=128 segments={segments}")
+    check(inp, run_gpu(inp, segments=segments), run_oracle(inp))
+
+
 def test_gla_tiny_gates_clamped():
     """Gates far below exp(-10) (the matrix-core clamp) still match the oracle."""
     wl = wl_for("gla", 1, 2, 200, 32, seed=3)
