@@ -31,26 +31,29 @@ struct DecodeArgs {
 
 // Threads per workgroup: a 64 KiB state tile streamed by 512 threads with nontemporal
 // 16-byte accesses measured 6.2 TB/s for an in-place read-modify-write on MI355X, against
-// 5.8 TB/s with 256 threads.
-constexpr int kDecodeThreads = 512;
+// 5.8 TB/s with 256 threads. GLA (the lighter kernel) measured faster still with 1024
+// threads; GDN, with twice the registers per thread, slower.
+template <int VAR>
+constexpr int decode_nthreads() { return VAR == LA_GLA ? 1024 : 512; }
 
-template <int DK, int DV>
+template <int DK, int DV, int NTH>
 struct DecodeShape {
     static constexpr int NCG = DV / 4;                         // 4-column groups
-    static constexpr int RG_ALL = kDecodeThreads / NCG;
+    static constexpr int RG_ALL = NTH / NCG;
     static constexpr int RG = RG_ALL < DK ? RG_ALL : DK;       // row groups
     static constexpr int RPT = DK / RG;                        // rows per thread
     static constexpr int NT = NCG * RG;                        // threads per workgroup
-    static_assert(NT > 0 && NT <= kDecodeThreads && RPT * RG == DK, "decode tiling");
+    static_assert(NT > 0 && NT <= NTH && RPT * RG == DK, "decode tiling");
 };
 
-constexpr int decode_threads(int dk, int dv) {
-    return (dv / 4) * ((kDecodeThreads / (dv / 4)) < dk ? (kDecodeThreads / (dv / 4)) : dk);
+constexpr int decode_threads(int dk, int dv, int nth) {
+    return (dv / 4) * ((nth / (dv / 4)) < dk ? (nth / (dv / 4)) : dk);
 }
 
 template <int VAR, int DK, int DV>
-__global__ __launch_bounds__(decode_threads(DK, DV)) void decode_kernel(DecodeArgs a) {
-    using Sh = DecodeShape<DK, DV>;
+__global__ __launch_bounds__(decode_threads(DK, DV, decode_nthreads<VAR>())) void decode_kernel(
+    DecodeArgs a) {
+    using Sh = DecodeShape<DK, DV, decode_nthreads<VAR>()>;
     constexpr int NCG = Sh::NCG, RG = Sh::RG, RPT = Sh::RPT, NT = Sh::NT;
     const int tid = threadIdx.x;
     const int cg = tid % NCG, rg = tid / NCG;
@@ -178,7 +181,8 @@ __global__ __launch_bounds__(decode_threads(DK, DV)) void decode_kernel(DecodeAr
 template <int VAR, int DK, int DV>
 hipError_t launch_one(const Problem& p, const DecodeArgs& a) {
     const unsigned nseq = unsigned(size_t(p.B) * size_t(p.H));
-    decode_kernel<VAR, DK, DV><<<dim3(nseq), dim3(DecodeShape<DK, DV>::NT), 0, p.stream>>>(a);
+    decode_kernel<VAR, DK, DV>
+        <<<dim3(nseq), dim3(DecodeShape<DK, DV, decode_nthreads<VAR>()>::NT), 0, p.stream>>>(a);
     return hipGetLastError();
 }
 
