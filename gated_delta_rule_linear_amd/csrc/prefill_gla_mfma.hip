@@ -134,22 +134,30 @@ __global__ __launch_bounds__(NT) void gla_prep_kernel(GlaArgs a) {
         *reinterpret_cast<float4*>(sm.u.bg + r * PB + col + 4) = make_float4(f[4], f[5], f[6], f[7]);
     }
     lds_barrier();
-    // inclusive scan down each column: two threads per column, 32 rows each
+    // inclusive scan down each column: a thread takes 4 columns x 8 rows (16-byte LDS
+    // accesses), scans them, then adds the totals of the row groups above it
     {
-        const int col = tid & 127, half = tid >> 7;
-        float x[32];
+        const int c4 = (tid & 31) * 4, rg = tid >> 5;
+        float4 x[8];
 #pragma unroll
-        for (int r = 0; r < 32; ++r) x[r] = sm.u.bg[(half * 32 + r) * PB + col];
-        float tot = 0.f;
+        for (int r = 0; r < 8; ++r) x[r] = *reinterpret_cast<const float4*>(sm.u.bg + (8 * rg + r) * PB + c4);
 #pragma unroll
-        for (int r = 0; r < 32; ++r) { tot += x[r]; x[r] = tot; }
-        // the lower half adds the upper half's column total
-        __shared__ float part[DK];
-        if (half == 0) part[col] = tot;
+        for (int r = 1; r < 8; ++r) {
+            x[r].x += x[r - 1].x; x[r].y += x[r - 1].y; x[r].z += x[r - 1].z; x[r].w += x[r - 1].w;
+        }
+        __shared__ float4 part[8][DK / 4];
+        part[rg][tid & 31] = x[7];
         lds_barrier();
-        const float add = half == 1 ? part[col] : 0.f;
+        float4 add = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int q = 0; q < rg; ++q) {
+            const float4 t = part[q][tid & 31];
+            add.x += t.x; add.y += t.y; add.z += t.z; add.w += t.w;
+        }
 #pragma unroll
-        for (int r = 0; r < 32; ++r) sm.u.bg[(half * 32 + r) * PB + col] = x[r] + add;
+        for (int r = 0; r < 8; ++r) {
+            x[r].x += add.x; x[r].y += add.y; x[r].z += add.z; x[r].w += add.w;
+            *reinterpret_cast<float4*>(sm.u.bg + (8 * rg + r) * PB + c4) = x[r];
+        }
     }
     lds_barrier();
     if (tid < DK) {
@@ -222,7 +230,11 @@ __global__ __launch_bounds__(NT) void gla_prep_kernel(GlaArgs a) {
     // row block rb (the q~ fragment rescaled on the fly, a factor <= 1), stored straight
     // from the accumulators as half pieces; the two upper half pieces the forward
     // kernel reads, (0, 1) and (2, 3), are written as zeros
-    for (int ti = w; ti < 10; ti += 4) {
+    // (unrolled over a wave's up to three tiles so that their MFMA chains interleave)
+#pragma unroll
+    for (int tt = 0; tt < 3; ++tt) {
+        const int ti = w + 4 * tt;
+        if (ti >= 10) continue;
         const int rb = ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3;
         const int sb = ti - (rb * (rb + 1)) / 2;
         f32x4_t acc = zero4();
