@@ -10,16 +10,19 @@
 // on one chunk's q, k, g only, never on the state, so it is done once per chunk in a
 // fully parallel prep kernel; what remains per chunk on the sequential path is three
 // dense products on the matrix cores. A diagonal transition also lets the sequence be
-// cut into segments that run in parallel: the state entering segment j is a scan of
-// per-segment summaries, S_in[j+1] = diag(A_j) S_in[j] + dS_j (the parallel-scan idea
-// the same page applies to linear recurrences). Four kernels:
+// cut into segments that run in parallel: the state entering segment j is
+// S_in[j] = sum_{m < j} (prod_{m < l < j} A_l) dS_m + (prod_{l < j} A_l) S0, a sum over
+// per-segment summaries (the parallel-scan idea the same page applies to linear
+// recurrences). Three kernels:
 //   prep     (sequence, chunk): B by a column scan, then q^ = q exp(B), k^ = k exp(B_last
 //            - B), a = exp(B_last) and the masked score tile P, all to the workspace;
 //   summary  (sequence, segment < last, value tile): dS_j and A_j = prod of a over the
-//            segment, by the state update alone from a zero state;
-//   scan     (sequence, state element): S_in[j] for every segment, in place over dS;
-//   forward  (sequence, segment, value tile): from S_in[j], per chunk o = q^ S + P V and
-//            the state update; the last segment writes S_final.
+//            segment, by the state update alone from a zero state (segment 0 also
+//            copies its tile of S0 to the workspace);
+//   forward  (sequence, segment, value tile): S_in[j] from the summaries before it, then
+//            per chunk o = q^ S + P V and the state update; the last segment writes
+//            S_final. No workgroup that reads S0 runs beside one that writes S_final,
+//            so the two may be one buffer.
 // P is formed from scaled copies of q and k. To keep every factor bounded the chunk is
 // cut into four 16-row blocks; row block b uses the reference rho_b = B at its middle
 // row: q~_r = q_r exp(B_r - rho_b), k~(b)_s = k_s exp(rho_b - B_s) for s < 16 (b + 1), so
@@ -59,7 +62,7 @@ struct GlaArgs {
     uint16_t* o;
     float* S;
     unsigned char* ws;   // per-chunk prep output
-    float* dS;           // [nseq][nseg - 1][DK][DV]: summaries, then S_in[1 ..]
+    float* dS;           // [nseq][nseg][tile][DK x VT]: S0, then the segment summaries
     float* A;            // [nseq][nseg - 1][DK]
     int N, nseq, nchunks, nseg, cps, ntiles, DV;
 };
@@ -327,25 +330,19 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
 
     // state tile: key rows 16 (2 w + ib) + 4 g + j, columns c0 + colmap(ct, jl)
     f32x4_t S[2][NVT];
-    const float* Sinit = nullptr;
-    if (OUT) Sinit = seg == 0 ? (a.S0 ? a.S0 + size_t(seq) * DK * DV : nullptr)
-                              : a.dS + (size_t(seq) * (a.nseg - 1) + seg - 1) * DK * DV;
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-        for (int ct = 0; ct < NVT; ++ct)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int i = 16 * (2 * w + ib) + 4 * g + j, c = c0 + colmap<NVT>(ct, jl);
-                S[ib][ct][j] = Sinit ? Sinit[size_t(i) * DV + c] : 0.f;
-            }
-    if (OUT) {
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-            for (int ct = 0; ct < NVT; ++ct)
-                store_st<NVT>(sm.st[0], PQ, 16 * (2 * w + ib), 0, ct, S[ib][ct], lane);
-    }
+        for (int ct = 0; ct < NVT; ++ct) S[ib][ct] = zero4();
+    // Segment state slots, in this kernel's register order (slot m, tile: the float4
+    // (ib NVT + ct) NT + tid): slot 0 holds S0's tile, slot m + 1 the summary dS_m.
+    float4* const slots = reinterpret_cast<float4*>(a.dS) +
+                          (size_t(seq) * a.nseg * a.ntiles + tile) * (DK * VT / 4);
+    const size_t slot_stride = size_t(a.ntiles) * (DK * VT / 4);
+    auto S0_elem = [&](int ib, int ct, int j) {
+        const int i = 16 * (2 * w + ib) + 4 * g + j, c = c0 + colmap<NVT>(ct, jl);
+        return a.S0[size_t(seq) * DK * DV + size_t(i) * DV + c];
+    };
     float aprod[2][4];   // running product of the chunk decays (summary)
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
@@ -359,6 +356,15 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
     const rsrc_t rv = make_rsrc(a.v + tok0 * DV, uint32_t(a.N) * uint32_t(DV) * 2u);
     const uint32_t obytes = uint32_t(a.N) * uint32_t(DV) * 2u;
     const rsrc_t ro = make_rsrc(a.o + tok0 * DV, obytes);
+    if (!OUT && seg == 0 && a.S0) {
+        // the forward reads S0 from slot 0, so S_final may alias S0
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct)
+                slots[(ib * NVT + ct) * NT + tid] = make_float4(S0_elem(ib, ct, 0), S0_elem(ib, ct, 1),
+                                                                S0_elem(ib, ct, 2), S0_elem(ib, ct, 3));
+    }
 
     auto load_chunk = [&](ChainRegs<KV>& R, int lc) {   // lc: chunk index within the segment
         const uint32_t cb = uint32_t(lc) * kWsChunk;
@@ -463,6 +469,75 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
     ChainRegs<KV> RA, RB, RC;
     load_chunk(RA, 0);
     load_chunk(RB, 1);
+    if (OUT) {
+        if (a.nseg == 1) {
+            if (a.S0) {
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                    for (int ct = 0; ct < NVT; ++ct)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) S[ib][ct][j] = S0_elem(ib, ct, j);
+            }
+        } else {
+            // state entering segment seg, from the summaries of the segments before it:
+            // S_in = sum_m (prod_{l > m} A_l) dS_m + (prod_l A_l) S0, newest first, two
+            // summaries per batch of loads
+            float dcur[2][4];
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dcur[ib][j] = 1.f;
+            const float* Abase = a.A + size_t(seq) * (a.nseg - 1) * DK + 16 * (2 * w) + 4 * g;
+            for (int m = seg - 1; m >= 0; m -= 2) {
+                float4 ds[2][2][NVT], am[2][2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int mm = max(m - u, 0);
+#pragma unroll
+                    for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+                        for (int ct = 0; ct < NVT; ++ct)
+                            ds[u][ib][ct] = slots[(mm + 1) * slot_stride + (ib * NVT + ct) * NT + tid];
+                        am[u][ib] = *reinterpret_cast<const float4*>(Abase + size_t(mm) * DK + 16 * ib);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    if (m - u < 0) break;
+#pragma unroll
+                    for (int ib = 0; ib < 2; ++ib) {
+                        const float av[4] = {am[u][ib].x, am[u][ib].y, am[u][ib].z, am[u][ib].w};
+#pragma unroll
+                        for (int ct = 0; ct < NVT; ++ct) {
+                            const float dv4[4] = {ds[u][ib][ct].x, ds[u][ib][ct].y, ds[u][ib][ct].z,
+                                                  ds[u][ib][ct].w};
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) S[ib][ct][j] += dcur[ib][j] * dv4[j];
+                        }
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) dcur[ib][j] *= av[j];
+                    }
+                }
+            }
+            if (a.S0) {
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                    for (int ct = 0; ct < NVT; ++ct) {
+                        const float4 x = slots[(ib * NVT + ct) * NT + tid];
+                        const float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) S[ib][ct][j] += dcur[ib][j] * xv[j];
+                    }
+            }
+        }
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct)
+                store_st<NVT>(sm.st[0], PQ, 16 * (2 * w + ib), 0, ct, S[ib][ct], lane);
+    }
     stage(RA, 0);
     lds_barrier();
     for (int lc = 0; lc < nloc; lc += 3) {
@@ -489,60 +564,18 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
                     }
         }
     } else {
-        float* dS = a.dS + (size_t(seq) * (a.nseg - 1) + seg) * DK * DV;
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
             for (int ct = 0; ct < NVT; ++ct)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int i = 16 * (2 * w + ib) + 4 * g + j, c = c0 + colmap<NVT>(ct, jl);
-                    dS[size_t(i) * DV + c] = S[ib][ct][j];
-                }
+                slots[(seg + 1) * slot_stride + (ib * NVT + ct) * NT + tid] =
+                    make_float4(S[ib][ct][0], S[ib][ct][1], S[ib][ct][2], S[ib][ct][3]);
         if (tile == 0 && jl == 0) {
             float* A = a.A + (size_t(seq) * (a.nseg - 1) + seg) * DK;
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) A[16 * (2 * w + ib) + 4 * g + j] = aprod[ib][j];
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// scan over segments: S_in[j + 1] = diag(A_j) S_in[j] + dS_j, in place over dS_j
-// ---------------------------------------------------------------------------
-// One thread per 4 consecutive state elements; a sequence's blocks run on its XCD.
-__global__ __launch_bounds__(256) void gla_scan_kernel(GlaArgs a) {
-    const int per_seq = DK * (a.DV / 4);
-    const XcdMap mp = xcd_map(blockIdx.x, per_seq / 256, a.nseq);
-    if (!mp.valid) return;
-    const size_t seq = size_t(mp.seq);
-    const int e = mp.tile * 256 + int(threadIdx.x), i = e / (a.DV / 4), c = (e % (a.DV / 4)) * 4;
-    const size_t so = size_t(i) * a.DV + c;
-    float4 s = a.S0 ? *reinterpret_cast<const float4*>(a.S0 + seq * DK * a.DV + so)
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
-    // all summaries are loaded before the dependent chain; up to kScanBatch at a time
-    const int nsum = a.nseg - 1;
-    constexpr int kScanBatch = 16;
-    for (int j0 = 0; j0 < nsum; j0 += kScanBatch) {
-        float4 ds[kScanBatch];
-        float aj[kScanBatch];
-#pragma unroll
-        for (int u = 0; u < kScanBatch; ++u) {
-            const int j = min(j0 + u, nsum - 1);
-            ds[u] = *reinterpret_cast<const float4*>(a.dS + (seq * nsum + j) * DK * a.DV + so);
-            aj[u] = a.A[(seq * nsum + j) * DK + i];
-        }
-#pragma unroll
-        for (int u = 0; u < kScanBatch; ++u) {
-            if (j0 + u < nsum) {
-                s.x = aj[u] * s.x + ds[u].x;
-                s.y = aj[u] * s.y + ds[u].y;
-                s.z = aj[u] * s.z + ds[u].z;
-                s.w = aj[u] * s.w + ds[u].w;
-                *reinterpret_cast<float4*>(a.dS + (seq * nsum + j0 + u) * DK * a.DV + so) = s;
-            }
         }
     }
 }
@@ -554,12 +587,13 @@ WsLayout ws_layout(const Problem& p) {
     const size_t nseq = size_t(p.B) * size_t(p.H);
     const size_t nchunks = size_t((p.N + C - 1) / C);
     const size_t nsum = size_t(p.segments > 1 ? p.segments - 1 : 0);
+    const size_t nslot = p.segments > 1 ? size_t(p.segments) : 0;
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
     WsLayout L{};
     L.chunks = 0;
     size_t off = al(nseq * nchunks * kWsChunk);
     L.dS = off;
-    off += al(nseq * nsum * DK * size_t(p.dv) * 4);
+    off += al(nseq * nslot * DK * size_t(p.dv) * 4);
     L.A = off;
     off += al(nseq * nsum * DK * 4);
     L.total = off;
@@ -609,8 +643,6 @@ hipError_t launch_nvt(const Problem& p) {
         if (e != hipSuccess) return e;
         gla_chain_kernel<false, NVT><<<dim3(xcd_grid(a.ntiles * (a.nseg - 1), a.nseq)), dim3(NT),
                                        smem, p.stream>>>(a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        gla_scan_kernel<<<dim3(xcd_grid(DK * (p.dv / 4) / 256, a.nseq)), dim3(256), 0, p.stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_chain_kernel<true, NVT>),
