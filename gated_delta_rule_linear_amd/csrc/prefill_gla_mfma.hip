@@ -24,11 +24,12 @@
 //            S_final. No workgroup that reads S0 runs beside one that writes S_final,
 //            so the two may be one buffer.
 // P is formed from scaled copies of q and k. To keep every factor bounded the chunk is
-// cut into four 16-row blocks; row block b uses the reference rho_b = B at its middle
-// row: q~_r = q_r exp(B_r - rho_b), k~(b)_s = k_s exp(rho_b - B_s) for s < 16 (b + 1), so
-// no factor exceeds exp(8 max |log g|). log g is clamped at -10 (g >= 4.5e-5: a gate
-// below that keeps less than 4.5e-5 of the state, so the clamp changes no result
-// beyond bf16 rounding), which bounds every factor by e^80 in fp32.
+// cut into four 16-row blocks; row block b uses the reference rho_b = B at its row 7:
+// q~_r = q_r exp(B_r - rho_b), k~_s = k_s exp(rho_b - B_s) within the block, and an
+// off-diagonal block pair takes the bounded factor exp(rho_rb - rho_sb) <= 1 on one
+// side. Gates are clamped at g >= exp(-10) (a gate below that keeps less than 4.5e-5
+// of the state, so the clamp changes no result beyond bf16 rounding), which keeps
+// every factor within [exp(-80), exp(80)], inside fp32's normal range.
 #include "la_internal.h"
 #include "mfma.hpp"
 
@@ -39,8 +40,6 @@ constexpr int DK = 128;
 constexpr int C = kMfmaChunk;  // 64
 constexpr int NT = 256;
 constexpr int PQ = DK + 8;     // pitch of [*][128] bf16 tiles
-constexpr int PB = DK;         // pitch of the fp32 [64][128] gate tile
-constexpr float kLogGateMin = -10.f;
 
 // Workspace of one chunk, written by prep (bytes), each matrix in MFMA fragment order
 // so that a wave reads its fragment as one contiguous kilobyte: q^ (piece (rb, kk, lane =
@@ -70,25 +69,34 @@ struct GlaArgs {
 // ---------------------------------------------------------------------------
 // prep
 // ---------------------------------------------------------------------------
+// One workgroup of 8 waves per chunk. Wave w owns the 8-row group rows 8 w .. 8 w + 7
+// (row block b = w / 2, its lower half for even w) and lane l the key columns 2 l,
+// 2 l + 1. Every gate factor is a product of clamped gates (g >= exp(-10), the clamp
+// above): the wave's own running products down its 8 rows (inclusive prefix pp,
+// exclusive suffix ss) and the eight group totals T_h, shared through LDS. Row block
+// b's reference rho_b = B at its row 7 is the last row of its lower group, so
+//   lower group: exp(rho_b - B_r) = ss_r,  upper group: exp(B_r - rho_b) = pp_r,
+// each in [exp(-80), 1], the other of the pair one reciprocal; q^ = q Pre pp and
+// k^ = k ss Suf with Pre / Suf the products of the groups before / after (these two
+// may underflow to zero, exactly where the true factor leaves fp32's range). An
+// off-diagonal score block (rb, sb < rb) needs one of its operands rescaled by
+// exp(rho_rb - rho_sb) <= 1, the product of groups 2 sb + 1 .. 2 rb: the rescaled
+// copy of block sb's k~ for the pairs (0,1) (0,2) (1,2) (2,3), and of block rb's q~
+// for (0,3) (1,3), so no wave writes more than two copies.
+constexpr int NTP = 512;
+constexpr float kGateMin = 4.539993e-05f;   // exp(-10)
+
+__host__ __device__ constexpr bool pair_on_q(int sb, int rb) { return rb == 3 && sb <= 1; }
+
 struct __align__(16) PrepSmem {
-    // the fp32 gate tile is dead once every thread holds its B values, so the scaled
-    // q / k copies reuse its storage (and k^ reuses q~ once P is done)
-    union {
-        __align__(16) float bg[C * PB];
-        struct {
-            __align__(16) uint16_t qt[C * PQ];   // q~ (row block's own reference)
-            __align__(16) uint16_t kt[C * PQ];   // k~ (row block's own reference)
-        } s;
-    } u;
-    __align__(16) float rho[4][DK];
-    __align__(16) float fq[4][DK];    // exp(rho_b)
-    __align__(16) float fk[4][DK];    // exp(B_last - rho_b)
-    __align__(16) float fe[6][DK];    // exp(rho_bb - rho_b), b < bb
-    __align__(16) float dec[DK];      // exp(B_last)
+    __align__(16) uint16_t qo[C * PQ];      // q~, own row block's reference
+    __align__(16) uint16_t ko[C * PQ];      // k~, own row block's reference
+    __align__(16) uint16_t pc[6][16 * PQ];  // rescaled copy for each off-diagonal pair
+    __align__(16) float T[8][DK];           // gate product of each 8-row group
 };
 
 template <bool GB>
-__global__ __launch_bounds__(NT) void gla_prep_kernel(GlaArgs a) {
+__global__ __launch_bounds__(NTP) void gla_prep_kernel(GlaArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
@@ -98,192 +106,175 @@ __global__ __launch_bounds__(NT) void gla_prep_kernel(GlaArgs a) {
     if (!mp.valid) return;
     const size_t seq = size_t(mp.seq);
     const int ch = mp.tile;
-    const int t0 = ch * C, n = min(C, a.N - t0);
+    const int t0 = ch * C;
     const size_t tok0 = seq * size_t(a.N);
+    const int rg = w, b = w >> 1;
+    const bool upper = (w & 1) != 0;
+    const int col = 2 * lane;
 
     // rows past the end of the sequence read as zero
     const uint32_t rows_left = uint32_t(a.N - t0);
     const rsrc_t rq = make_rsrc(a.q + (tok0 + t0) * DK, rows_left * DK * 2u);
     const rsrc_t rk = make_rsrc(a.k + (tok0 + t0) * DK, rows_left * DK * 2u);
     constexpr uint32_t GS = GB ? 2u : 4u;
-    const rsrc_t rg = make_rsrc(static_cast<const char*>(a.g) + (tok0 + t0) * DK * GS,
-                                rows_left * DK * GS);
-    uint4 qv[4], kv[4], gv[4][2];
+    const rsrc_t rg_ = make_rsrc(static_cast<const char*>(a.g) + (tok0 + t0) * DK * GS,
+                                 rows_left * DK * GS);
+    uint32_t qv[8], kv[8], gv[GB ? 8 : 16];
 #pragma unroll
-    for (int x4 = 0; x4 < 4; ++x4) {
-        const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
-        const uint32_t e = uint32_t(r * DK + col);
-        qv[x4] = buf_ld16(rq, e * 2u);
-        kv[x4] = buf_ld16(rk, e * 2u);
+    for (int r = 0; r < 8; ++r) {
+        const uint32_t e = uint32_t((8 * rg + r) * DK + col);
+        qv[r] = buf_ld4(rq, e * 2u);
+        kv[r] = buf_ld4(rk, e * 2u);
         if constexpr (GB) {
-            gv[x4][0] = buf_ld16(rg, e * 2u);
+            gv[r] = buf_ld4(rg_, e * 2u);
         } else {
-            gv[x4][0] = buf_ld16(rg, e * 4u);
-            gv[x4][1] = buf_ld16(rg, e * 4u + 16u);
+            const uint2 x = buf_ld8(rg_, e * 4u);
+            gv[2 * r] = x.x;
+            gv[2 * r + 1] = x.y;
         }
     }
-    // log g, clamped, zero on padding rows
-#pragma unroll
-    for (int x4 = 0; x4 < 4; ++x4) {
-        const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
-        float f[8];
-        gate8_val<GB>(gv[x4], f);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const float lg = fmaxf(fast_log(f[q]), kLogGateMin);
-            f[q] = r < n ? lg : 0.f;
-        }
-        *reinterpret_cast<float4*>(sm.u.bg + r * PB + col) = make_float4(f[0], f[1], f[2], f[3]);
-        *reinterpret_cast<float4*>(sm.u.bg + r * PB + col + 4) = make_float4(f[4], f[5], f[6], f[7]);
-    }
-    lds_barrier();
-    // inclusive scan down each column: a thread takes 4 columns x 8 rows (16-byte LDS
-    // accesses), scans them, then adds the totals of the row groups above it
+    float pp[8][2], ss[8][2];
     {
-        const int c4 = (tid & 31) * 4, rg = tid >> 5;
-        float4 x[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) x[r] = *reinterpret_cast<const float4*>(sm.u.bg + (8 * rg + r) * PB + c4);
-#pragma unroll
-        for (int r = 1; r < 8; ++r) {
-            x[r].x += x[r - 1].x; x[r].y += x[r - 1].y; x[r].z += x[r - 1].z; x[r].w += x[r - 1].w;
-        }
-        __shared__ float4 part[8][DK / 4];
-        part[rg][tid & 31] = x[7];
-        lds_barrier();
-        float4 add = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int q = 0; q < rg; ++q) {
-            const float4 t = part[q][tid & 31];
-            add.x += t.x; add.y += t.y; add.z += t.z; add.w += t.w;
-        }
+        float gf[8][2];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            x[r].x += add.x; x[r].y += add.y; x[r].z += add.z; x[r].w += add.w;
-            *reinterpret_cast<float4*>(sm.u.bg + (8 * rg + r) * PB + c4) = x[r];
-        }
-    }
-    lds_barrier();
-    if (tid < DK) {
-        const float bl = sm.u.bg[(C - 1) * PB + tid];
-        float rb[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            rb[b] = sm.u.bg[(16 * b + 7) * PB + tid];
-            sm.rho[b][tid] = rb[b];
-            sm.fq[b][tid] = fast_exp(rb[b]);
-            sm.fk[b][tid] = fast_exp(bl - rb[b]);
+            float g0, g1;
+            if constexpr (GB) {
+                g0 = __uint_as_float(gv[r] << 16);
+                g1 = __uint_as_float(gv[r] & 0xffff0000u);
+            } else {
+                g0 = __uint_as_float(gv[2 * r]);
+                g1 = __uint_as_float(gv[2 * r + 1]);
+            }
+            const bool live = uint32_t(8 * rg + r) < rows_left;   // padding rows: identity steps
+            gf[r][0] = live ? fmaxf(g0, kGateMin) : 1.f;
+            gf[r][1] = live ? fmaxf(g1, kGateMin) : 1.f;
         }
 #pragma unroll
-        for (int b = 0; b < 3; ++b)
+        for (int c = 0; c < 2; ++c) {
+            pp[0][c] = gf[0][c];
 #pragma unroll
-            for (int bb = b + 1; bb < 4; ++bb) sm.fe[pair_index(b, bb)][tid] = fast_exp(rb[bb] - rb[b]);
-        sm.dec[tid] = fast_exp(bl);
-    }
-    // every thread takes its B values before the gate tile is overwritten
-    float br[4][8];
-    uint4 khp[4];
+            for (int r = 1; r < 8; ++r) pp[r][c] = pp[r - 1][c] * gf[r][c];
+            ss[7][c] = 1.f;
 #pragma unroll
-    for (int x4 = 0; x4 < 4; ++x4) {
-        const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
-        const float4 u0 = *reinterpret_cast<const float4*>(sm.u.bg + r * PB + col);
-        const float4 u1 = *reinterpret_cast<const float4*>(sm.u.bg + r * PB + col + 4);
-        br[x4][0] = u0.x; br[x4][1] = u0.y; br[x4][2] = u0.z; br[x4][3] = u0.w;
-        br[x4][4] = u1.x; br[x4][5] = u1.y; br[x4][6] = u1.z; br[x4][7] = u1.w;
+            for (int r = 6; r >= 0; --r) ss[r][c] = ss[r + 1][c] * gf[r + 1][c];
+        }
     }
+    *reinterpret_cast<float2*>(&sm.T[rg][col]) = make_float2(pp[7][0], pp[7][1]);
     lds_barrier();
 
-    unsigned char* wsc = a.ws + (seq * a.nchunks + ch) * size_t(kWsChunk);
-    auto ld8 = [&](const float* src, float (&dst)[8]) {
-        const float4 u0 = *reinterpret_cast<const float4*>(src);
-        const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
-        dst[0] = u0.x; dst[1] = u0.y; dst[2] = u0.z; dst[3] = u0.w;
-        dst[4] = u1.x; dst[5] = u1.y; dst[6] = u1.z; dst[7] = u1.w;
-    };
+    float Tv[8][2];
 #pragma unroll
-    for (int x4 = 0; x4 < 4; ++x4) {
-        const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
-        const int b = x4;   // rows (tid >> 4) + 16 x4 lie in row block x4
-        float q8[8], k8[8], rho[8], fq[8], fk[8];
-        unpack8(qv[x4], q8);   // padding rows read as zero
-        unpack8(kv[x4], k8);
-        ld8(sm.rho[b] + col, rho);
-        ld8(sm.fq[b] + col, fq);
-        ld8(sm.fk[b] + col, fk);
-        float qt[8], qh[8], kt[8], kh[8];   // k^ stays in registers until after P
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const float e = fast_exp(br[x4][q] - rho[q]);   // exp(B_r - rho_b)
-            const float inv = __builtin_amdgcn_rcpf(e);      // exp(rho_b - B_r)
-            qt[q] = q8[q] * e;
-            qh[q] = qt[q] * fq[q];                          // q exp(B_r)
-            kt[q] = k8[q] * inv;                            // k exp(rho_b - B_r)
-            kh[q] = kt[q] * fk[q];                          // k exp(B_last - B_r)
-        }
-        *reinterpret_cast<uint4*>(sm.u.s.qt + r * PQ + col) = pack8(qt);
-        *reinterpret_cast<uint4*>(sm.u.s.kt + r * PQ + col) = pack8(kt);
-        // q^ in fragment order, k^ row-major
-        const int jr = r & 15, kk = col >> 5, gg = (col & 31) >> 3;
-        *reinterpret_cast<uint4*>(wsc + kWsQ + (((r >> 4) * 4 + kk) * 64 + 16 * gg + jr) * 16) = pack8(qh);
-        khp[x4] = pack8(kh);
+    for (int hh = 0; hh < 8; ++hh) {
+        const float2 t = *reinterpret_cast<const float2*>(&sm.T[hh][col]);
+        Tv[hh][0] = t.x;
+        Tv[hh][1] = t.y;
     }
-    if (tid < DK / 4)
-        *reinterpret_cast<float4*>(wsc + kWsA + tid * 16) = *reinterpret_cast<const float4*>(sm.dec + 4 * tid);
-    lds_barrier();
-    // P: ten lower tiles, D'[s][r] = k~_s . q~_r exp(rho_rb - rho_sb) for key block sb <
-    // row block rb (the q~ fragment rescaled on the fly, a factor <= 1), stored straight
-    // from the accumulators as half pieces; the two upper half pieces the forward
-    // kernel reads, (0, 1) and (2, 3), are written as zeros
-    // (unrolled over a wave's up to three tiles so that their MFMA chains interleave)
+    // products of the groups before / after this one, and the pair factors: this wave
+    // rescales k~ for the k-side pairs (b, rb > b) and q~ for the q-side pairs (sb, b)
+    float pre[2], suf[2], fk[4][2], fq[4][2];
 #pragma unroll
-    for (int tt = 0; tt < 3; ++tt) {
-        const int ti = w + 4 * tt;
+    for (int c = 0; c < 2; ++c) {
+        pre[c] = 1.f;
+        suf[c] = 1.f;
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+            if (hh < rg) pre[c] *= Tv[hh][c];
+            if (hh > rg) suf[c] *= Tv[hh][c];
+        }
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {   // exp(rho_o - rho_b) (o > b), exp(rho_b - rho_o) (o < b)
+            const int lo = o < b ? o : b, hi = o < b ? b : o;
+            float f = 1.f;
+#pragma unroll
+            for (int hh = 1; hh < 7; ++hh)
+                if (hh >= 2 * lo + 1 && hh <= 2 * hi) f *= Tv[hh][c];
+            fk[o][c] = f;
+            fq[o][c] = f;
+        }
+    }
+    unsigned char* wsc = a.ws + (seq * a.nchunks + ch) * size_t(kWsChunk);
+    if (rg == 0 && lane < DK / 2) {
+        *reinterpret_cast<float2*>(wsc + kWsA + col * 4) = make_float2(Tv[0][0] * suf[0], Tv[0][1] * suf[1]);
+    }
+    float kh[8][2];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int rr = 8 * rg + r;
+        const float q0 = __uint_as_float(qv[r] << 16), q1 = __uint_as_float(qv[r] & 0xffff0000u);
+        const float k0 = __uint_as_float(kv[r] << 16), k1 = __uint_as_float(kv[r] & 0xffff0000u);
+        float e0, e1, i0, i1;
+        if (upper) {
+            e0 = pp[r][0]; e1 = pp[r][1];
+            i0 = __builtin_amdgcn_rcpf(e0); i1 = __builtin_amdgcn_rcpf(e1);
+        } else {
+            i0 = ss[r][0]; i1 = ss[r][1];
+            e0 = __builtin_amdgcn_rcpf(i0); e1 = __builtin_amdgcn_rcpf(i1);
+        }
+        const float qt0 = q0 * e0, qt1 = q1 * e1, kt0 = k0 * i0, kt1 = k1 * i1;
+        *reinterpret_cast<uint32_t*>(sm.qo + rr * PQ + col) = pack_bf16x2(qt0, qt1);
+        *reinterpret_cast<uint32_t*>(sm.ko + rr * PQ + col) = pack_bf16x2(kt0, kt1);
+        const int pr = rr & 15;
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {
+            if (o > b && !pair_on_q(b, o))
+                *reinterpret_cast<uint32_t*>(sm.pc[pair_index(b, o)] + pr * PQ + col) =
+                    pack_bf16x2(kt0 * fk[o][0], kt1 * fk[o][1]);
+            if (o < b && pair_on_q(o, b))
+                *reinterpret_cast<uint32_t*>(sm.pc[pair_index(o, b)] + pr * PQ + col) =
+                    pack_bf16x2(qt0 * fq[o][0], qt1 * fq[o][1]);
+        }
+        // q^ in fragment order: row rr, columns col, col + 1 are a quarter piece
+        const int kk = col >> 5, gg = (col & 31) >> 3;
+        *reinterpret_cast<uint32_t*>(wsc + kWsQ + (((rr >> 4) * 4 + kk) * 64 + 16 * gg + pr) * 16 +
+                                     (col & 7) * 2) =
+            pack_bf16x2(q0 * (pre[0] * pp[r][0]), q1 * (pre[1] * pp[r][1]));
+        kh[r][0] = k0 * (ss[r][0] * suf[0]);
+        kh[r][1] = k1 * (ss[r][1] * suf[1]);
+    }
+    // k^ transposed: this thread's 8 tokens of key i are one fragment piece
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int i = col + c;
+        float f[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) f[r] = kh[r][c];
+        *reinterpret_cast<uint4*>(wsc + kWsK + (((i >> 4) * 2 + (rg >> 2)) * 64 + 16 * (rg & 3) + (i & 15)) * 16) =
+            pack8(f);
+    }
+    lds_barrier();
+    // P: ten lower tiles, D'[s][r] = sum_i K~_si Q~_ri over key block sb and row block rb,
+    // stored straight from the accumulators as half pieces; the two upper half pieces
+    // the forward kernel reads, (0, 1) and (2, 3), are written as zeros. Waves 0 and 1
+    // take two tiles, the others one.
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const int ti = w + 8 * tt;
         if (ti >= 10) continue;
         const int rb = ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3;
         const int sb = ti - (rb * (rb + 1)) / 2;
+        const uint16_t* At = sm.ko;
+        const uint16_t* Bt = sm.qo;
+        int ar = 16 * sb, br = 16 * rb;
+        if (sb < rb) {
+            if (pair_on_q(sb, rb)) { Bt = sm.pc[pair_index(sb, rb)]; br = 0; }
+            else { At = sm.pc[pair_index(sb, rb)]; ar = 0; }
+        }
         f32x4_t acc = zero4();
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) {
-            bf16x8_t qb = frag_kc(sm.u.s.qt, PQ, 16 * rb, 32 * kk, lane);
-            if (sb < rb) {
-                float f[8], fe[8];
-                unpack8(__builtin_bit_cast(uint4, qb), f);
-                ld8(sm.fe[pair_index(sb, rb)] + 32 * kk + 8 * g, fe);
-#pragma unroll
-                for (int q = 0; q < 8; ++q) f[q] *= fe[q];
-                qb = __builtin_bit_cast(bf16x8_t, pack8(f));
-            }
-            acc = mfma16(frag_kc(sm.u.s.kt, PQ, 16 * sb, 32 * kk, lane), qb, acc);
-        }
+        for (int kk = 0; kk < DK / 32; ++kk)
+            acc = mfma16(frag_kc(At, PQ, ar, 32 * kk, lane), frag_kc(Bt, PQ, br, 32 * kk, lane), acc);
         const int r = 16 * rb + jl;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int s = 16 * sb + 4 * g + j;
-            acc[j] = s <= r ? acc[j] : 0.f;
+            const int s_ = 16 * sb + 4 * g + j;
+            acc[j] = s_ <= r ? acc[j] : 0.f;
         }
         unsigned char* piece = wsc + kWsP + ((rb * 2 + (sb >> 1)) * 64 + lane) * 16;
         *reinterpret_cast<uint2*>(piece + (sb & 1) * 8) =
             make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
         if (sb == rb && (rb & 1) == 0) *reinterpret_cast<uint2*>(piece + 8) = make_uint2(0, 0);
     }
-    lds_barrier();
-    // k^ row-major into the (now dead) q~ storage, then transposed out
-    uint16_t* kht = sm.u.s.qt;
-#pragma unroll
-    for (int x4 = 0; x4 < 4; ++x4) {
-        const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
-        *reinterpret_cast<uint4*>(kht + r * PQ + col) = khp[x4];
-    }
-    lds_barrier();
-    // k^ transposed, in fragment order: wave w writes key blocks 2 w, 2 w + 1
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int blk = 2 * w + ib;
-            const bf16x8_t f = frag_kr(kht, PQ, 32 * kk, 16 * blk, lane);
-            *reinterpret_cast<uint4*>(wsc + kWsK + ((blk * 2 + kk) * 64 + lane) * 16) =
-                __builtin_bit_cast(uint4, f);
-        }
 }
 
 // ---------------------------------------------------------------------------
@@ -481,7 +472,7 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
             }
         } else {
             // state entering segment seg, from the summaries of the segments before it:
-            // S_in = sum_m (prod_{l > m} A_l) dS_m + (prod_l A_l) S0, newest first, two
+            // S_in = sum_m (prod_{l > m} A_l) dS_m + (prod_l A_l) S0, newest first, four
             // summaries per batch of loads
             float dcur[2][4];
 #pragma unroll
@@ -489,10 +480,10 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) dcur[ib][j] = 1.f;
             const float* Abase = a.A + size_t(seq) * (a.nseg - 1) * DK + 16 * (2 * w) + 4 * g;
-            for (int m = seg - 1; m >= 0; m -= 2) {
-                float4 ds[2][2][NVT], am[2][2];
+            for (int m = seg - 1; m >= 0; m -= 4) {
+                float4 ds[4][2][NVT], am[4][2];
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
+                for (int u = 0; u < 4; ++u) {
                     const int mm = max(m - u, 0);
 #pragma unroll
                     for (int ib = 0; ib < 2; ++ib) {
@@ -503,7 +494,7 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
                     }
                 }
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
+                for (int u = 0; u < 4; ++u) {
                     if (m - u < 0) break;
 #pragma unroll
                     for (int ib = 0; ib < 2; ++ib) {
@@ -633,7 +624,7 @@ hipError_t launch_nvt(const Problem& p) {
         if (e != hipSuccess) return e;
         const size_t blocks = size_t(xcd_grid(a.nchunks, (a.nseq + 7) & ~7));
         if (size_t(a.nseq + 7) * size_t(a.nchunks) > 0x7fffffffull) return hipErrorInvalidValue;
-        gla_prep_kernel<GB><<<dim3(unsigned(blocks)), dim3(NT), smem, p.stream>>>(a);
+        gla_prep_kernel<GB><<<dim3(unsigned(blocks)), dim3(NTP), smem, p.stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const size_t smem = sizeof(ChainSmem<VT>);
