@@ -38,8 +38,8 @@ struct KathArgs {
     const float *S0, *z0;
     uint16_t* o;
     float *S, *z;
-    float* dS;   // [nseq][nseg - 1][DK][DV]: summaries, then S_in[1 ..]
-    float* dz;   // [nseq][nseg - 1][DK]: likewise for z
+    float* dS;   // [nseq][nseg][DK][DV]: S0, then the summaries; after the scan S_in[j]
+    float* dz;   // [nseq][nseg][DK]: likewise for z
     float eps;
     int N, nseq, nchunks, nseg, cps, ntiles, DV;
 };
@@ -101,10 +101,13 @@ __global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
     const float* Sinit = nullptr;
     const float* zinit = nullptr;
     if (OUT) {
-        Sinit = seg == 0 ? (a.S0 ? a.S0 + size_t(seq) * DK * DV : nullptr)
-                         : a.dS + (size_t(seq) * nsum + seg - 1) * DK * DV;
-        zinit = seg == 0 ? (a.z0 ? a.z0 + size_t(seq) * DK : nullptr)
-                         : a.dz + (size_t(seq) * nsum + seg - 1) * DK;
+        // with several segments every entering state comes from the scan's slots (slot 0
+        // holds the copy of S0, z0), so no workgroup here reads S0 while the last
+        // segment writes S_final over it
+        Sinit = nsum == 0 ? (a.S0 ? a.S0 + size_t(seq) * DK * DV : nullptr)
+                          : a.dS + (size_t(seq) * a.nseg + seg) * DK * DV;
+        zinit = nsum == 0 ? (a.z0 ? a.z0 + size_t(seq) * DK : nullptr)
+                          : a.dz + (size_t(seq) * a.nseg + seg) * DK;
     }
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
@@ -338,7 +341,7 @@ __global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
             if (tile == 0 && tid < DK) a.z[size_t(seq) * DK + tid] = sm.z[tid];
         }
     } else {
-        float* dS = a.dS + (size_t(seq) * nsum + seg) * DK * DV;
+        float* dS = a.dS + (size_t(seq) * a.nseg + seg + 1) * DK * DV;
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
@@ -349,13 +352,14 @@ __global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
                     const int c = c0 + cw + colmap<NVT>(ct, jl);
                     dS[size_t(i) * DV + c] = S[ib][ct][j];
                 }
-        if (tile == 0 && tid < DK) a.dz[(size_t(seq) * nsum + seg) * DK + tid] = sm.z[tid];
+        if (tile == 0 && tid < DK) a.dz[(size_t(seq) * a.nseg + seg + 1) * DK + tid] = sm.z[tid];
     }
 }
 
 // S_in[j + 1] = S_in[j] + dS_j and z_in[j + 1] = z_in[j] + dz_j, in place over the
-// summaries; one thread per 4 consecutive elements of S (the z row rides along with
-// the threads of column group 0).
+// summaries in slot j + 1; slot 0 receives S_in[0] = S0 and z_in[0] = z0 (or zeros).
+// One thread per 4 consecutive elements of S (the z row rides along with the threads
+// of column group 0).
 __global__ __launch_bounds__(256) void kath_scan_kernel(KathArgs a) {
     const int per_seq = DK * (a.DV / 4);
     const XcdMap mp = xcd_map(blockIdx.x, (per_seq + 255) / 256, a.nseq);
@@ -366,10 +370,15 @@ __global__ __launch_bounds__(256) void kath_scan_kernel(KathArgs a) {
     const int i = e / (a.DV / 4), c = (e % (a.DV / 4)) * 4;
     const size_t so = size_t(i) * a.DV + c;
     const int nsum = a.nseg - 1;
+    const size_t slot = size_t(DK) * a.DV;
+    float* Sb = a.dS + seq * a.nseg * slot + so;
+    float* zb = a.dz + seq * a.nseg * DK + i;
     float4 s = a.S0 ? *reinterpret_cast<const float4*>(a.S0 + seq * DK * a.DV + so)
                     : make_float4(0.f, 0.f, 0.f, 0.f);
     const bool zrow = c == 0;
     float z = zrow && a.z0 ? a.z0[seq * DK + i] : 0.f;
+    *reinterpret_cast<float4*>(Sb) = s;
+    if (zrow) zb[0] = z;
     constexpr int kBatch = 16;
     for (int j0 = 0; j0 < nsum; j0 += kBatch) {
         float4 ds[kBatch];
@@ -377,17 +386,17 @@ __global__ __launch_bounds__(256) void kath_scan_kernel(KathArgs a) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int j = min(j0 + u, nsum - 1);
-            ds[u] = *reinterpret_cast<const float4*>(a.dS + (seq * nsum + j) * DK * a.DV + so);
-            dz[u] = zrow ? a.dz[(seq * nsum + j) * DK + i] : 0.f;
+            ds[u] = *reinterpret_cast<const float4*>(Sb + (j + 1) * slot);
+            dz[u] = zrow ? zb[(j + 1) * DK] : 0.f;
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             if (j0 + u < nsum) {
                 s.x += ds[u].x; s.y += ds[u].y; s.z += ds[u].z; s.w += ds[u].w;
-                *reinterpret_cast<float4*>(a.dS + (seq * nsum + j0 + u) * DK * a.DV + so) = s;
+                *reinterpret_cast<float4*>(Sb + (j0 + u + 1) * slot) = s;
                 if (zrow) {
                     z += dz[u];
-                    a.dz[(seq * nsum + j0 + u) * DK + i] = z;
+                    zb[(j0 + u + 1) * DK] = z;
                 }
             }
         }
@@ -399,14 +408,14 @@ struct WsLayout {
 };
 WsLayout ws_layout(const Problem& p) {
     const size_t nseq = size_t(p.B) * size_t(p.H);
-    const size_t nsum = size_t(p.segments > 1 ? p.segments - 1 : 0);
+    const size_t nslot = size_t(p.segments > 1 ? p.segments : 0);
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
     WsLayout L{};
     L.dS = 0;
-    size_t off = al(nseq * nsum * DK * size_t(p.dv) * 4);
+    size_t off = al(nseq * nslot * DK * size_t(p.dv) * 4);
     L.dz = off;
-    off += al(nseq * nsum * DK * 4);
-    L.total = nsum ? off : 0;
+    off += al(nseq * nslot * DK * 4);
+    L.total = nslot ? off : 0;
     return L;
 }
 

@@ -185,6 +185,27 @@ def test_mfma_split_at_chunk_boundary_is_exact(variant):
             assert relerr(torch.cat([oL, oR], 2), f64(o)) < 2e-2 and relerr(SR, f64(S)) < 1e-2
 
 
+@pytest.mark.parametrize("variant", ["kath", "gla", "gdn"])
+@pytest.mark.parametrize("segments", [1, 5])
+def test_mfma_in_place_state(variant, segments):
+    """S_final (and z_final) may be the very buffers of S0 (z0), also when the sequence
+    is cut into segments that run side by side: the result equals the separate-buffer
+    run bit for bit."""
+    inp = W.make_inputs(wl_for(variant, 1, 3, 64 * 9 + 17, 64, seed=12), with_state=True)
+    d = inputs_to_device(inp)
+    banner(f"in-place state {variant} segments={segments}")
+    o, S, z = run_gpu(inp, d, segments=segments)
+    Sx = d["S0"].clone()
+    zx = d["z0"].clone() if variant == "kath" else None
+    d2 = dict(d, S0=Sx, z0=zx)
+    o2, S2, z2 = run_gpu(inp, d2, segments=segments, S_final=Sx, z_final=zx)
+    assert S2.data_ptr() == Sx.data_ptr()
+    assert torch.equal(o2, o) and torch.equal(S2, S)
+    if variant == "kath":
+        assert z2.data_ptr() == zx.data_ptr() and torch.equal(z2, z)
+    check(inp, (o2, S2, z2), run_oracle(inp))
+
+
 @pytest.mark.parametrize("variant", ["gla", "gdn", "kath"])
 def test_prefill_then_decode_equals_longer_prefill(variant):
     N, extra = 192, 5
