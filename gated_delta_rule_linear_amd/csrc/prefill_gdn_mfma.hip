@@ -324,32 +324,43 @@ __global__ __launch_bounds__(NT * CG) void gdn_fwd_kernel(GdnArgs a) {
 
     // loads of one chunk, all unconditional (a chunk index past the end reads zeros);
     // K first, since its LDS copy is written before the other operands are needed
-    auto load_chunk = [&](ChunkRegs<NVT, KST>& R, int ch) {
+    // A chunk's loads go out in three parts spread over the processing of the chunk two
+    // before it (gates and K, then q, then T and V), so that the memory unit's queue is
+    // not handed all of them at once. Each part stays together and in program order:
+    // the memory-counter waits before a chunk is used count the loads issued after it.
+    auto load_part = [&](ChunkRegs<NVT, KST>& R, int ch, int part) {
         const uint32_t t0 = uint32_t(ch) * C;
+        if (part == 0) {
+            R.ga = buf_ld_gate<GB>(ra, t0 + lane);
+            R.gb = buf_ld_gate<GB>(rb_, t0 + lane);
 #pragma unroll
-        for (int x4 = 0; x4 < KST; ++x4) {
-            const int x = tid + NTW * x4, r = x >> 4, col = (x & 15) * 8;
-            R.kst[x4] = buf_ld16(rk, ((t0 + r) * DK + col) * 2u);
-        }
-        const uint32_t oq = ((t0 + rw) * DK + 8 * g) * 2u;
+            for (int x4 = 0; x4 < KST; ++x4) {
+                const int x = tid + NTW * x4, r = x >> 4, col = (x & 15) * 8;
+                R.kst[x4] = buf_ld16(rk, ((t0 + r) * DK + col) * 2u);
+            }
+        } else if (part == 1) {
+            const uint32_t oq = ((t0 + rw) * DK + 8 * g) * 2u;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) R.q[kk] = buf_ld16(rq, oq + 64u * kk);
-        const uint32_t ot = (uint32_t(ch) * (C * C) + (2 * rb * 64 + lane) * 8) * 2u;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) R.t[kk] = buf_ld16(rt, ot + 1024u * kk);
-        const uint32_t ov = ((t0 + rw) * uint32_t(DV) + c0 + colmap<NVT>(0, 4 * g)) * 2u;
-        if constexpr (NVT == 2) {
-            const uint4 v4 = buf_ld16(rv, ov);
-            R.v[0] = make_uint2(v4.x, v4.y);
-            R.v[1] = make_uint2(v4.z, v4.w);
+            for (int kk = 0; kk < 4; ++kk) R.q[kk] = buf_ld16(rq, oq + 64u * kk);
         } else {
-            R.v[0] = buf_ld8(rv, ov);
+            const uint32_t ot = (uint32_t(ch) * (C * C) + (2 * rb * 64 + lane) * 8) * 2u;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) R.t[kk] = buf_ld16(rt, ot + 1024u * kk);
+            const uint32_t ov = ((t0 + rw) * uint32_t(DV) + c0 + colmap<NVT>(0, 4 * g)) * 2u;
+            if constexpr (NVT == 2) {
+                const uint4 v4 = buf_ld16(rv, ov);
+                R.v[0] = make_uint2(v4.x, v4.y);
+                R.v[1] = make_uint2(v4.z, v4.w);
+            } else {
+                R.v[0] = buf_ld8(rv, ov);
+            }
         }
-        R.ga = buf_ld_gate<GB>(ra, t0 + lane);
-        R.gb = buf_ld_gate<GB>(rb_, t0 + lane);
-        // keep each chunk's loads together and in program order: the memory-counter
-        // waits before a chunk is used count the loads issued after it
         __builtin_amdgcn_sched_barrier(0);
+    };
+    auto load_chunk = [&](ChunkRegs<NVT, KST>& R, int ch) {
+        load_part(R, ch, 0);
+        load_part(R, ch, 1);
+        load_part(R, ch, 2);
     };
     auto stage_k = [&](const ChunkRegs<NVT, KST>& R, uint16_t* kb) {
 #pragma unroll
@@ -359,8 +370,9 @@ __global__ __launch_bounds__(NT * CG) void gdn_fwd_kernel(GdnArgs a) {
         }
     };
 
-    auto process = [&](const ChunkRegs<NVT, KST>& R, const ChunkRegs<NVT, KST>& Rn, int ch,
-                       int cur) {
+    auto process = [&](const ChunkRegs<NVT, KST>& R, const ChunkRegs<NVT, KST>& Rn,
+                       ChunkRegs<NVT, KST>& Rl, int ch, int cur) {
+        load_part(Rl, ch + 2, 0);
         const int t0 = ch * C, n = min(C, a.N - t0);
         const uint16_t* kc = sm.k[cur];
         // gates: every wave scans log alpha itself (lane = token); lane (g, j) then
@@ -404,6 +416,7 @@ __global__ __launch_bounds__(NT * CG) void gdn_fwd_kernel(GdnArgs a) {
             store_rows<NVT>(sm.x, PV, cw, ct, 16 * rb, x_, lane);   // X[s][c]
         }
         lds_barrier();
+        load_part(Rl, ch + 2, 1);
 
         // ---- U^T = X^T T^T for rows 16 rb .. : D[c][r] -> U[r][c], U^[r][c]
 #pragma unroll
@@ -439,6 +452,7 @@ __global__ __launch_bounds__(NT * CG) void gdn_fwd_kernel(GdnArgs a) {
         }
         const bf16x8_t pf0 = pack_pk(pt[0], pt[1]), pf1 = pack_pk(pt[2], pt[3]);
         lds_barrier();
+        load_part(Rl, ch + 2, 2);
 
         // ---- O^T = gamma_r (S^T Q^T) + U^T P^T -> o rows 16 rb ..
         uint2 ow[NVT];
@@ -492,12 +506,9 @@ __global__ __launch_bounds__(NT * CG) void gdn_fwd_kernel(GdnArgs a) {
     // the identity step, T = 0), leaves the state unchanged and stores nothing, so no
     // exit sits between the triple's memory operations
     for (int ch = 0; ch < nchunks; ch += 3) {
-        load_chunk(RC, ch + 2);
-        process(RA, RB, ch, ch & 1);
-        load_chunk(RA, ch + 3);
-        process(RB, RC, ch + 1, (ch + 1) & 1);
-        load_chunk(RB, ch + 4);
-        process(RC, RA, ch + 2, ch & 1);
+        process(RA, RB, RC, ch, ch & 1);
+        process(RB, RC, RA, ch + 1, (ch + 1) & 1);
+        process(RC, RA, RB, ch + 2, ch & 1);
     }
 
 #pragma unroll
