@@ -357,15 +357,25 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
                                                                 S0_elem(ib, ct, 2), S0_elem(ib, ct, 3));
     }
 
-    auto load_chunk = [&](ChainRegs<KV>& R, int lc) {   // lc: chunk index within the segment
+    // A chunk's loads (lc: chunk index within the segment) go out in two parts, at the
+    // start and in the middle of the processing of the chunk two before it, so that the
+    // memory unit's queue is not handed all of them at once; each part stays in program
+    // order (the memory-counter waits before a chunk is used count the loads after it).
+    auto load_part = [&](ChainRegs<KV>& R, int lc, int part) {
         const uint32_t cb = uint32_t(lc) * kWsChunk;
         const uint32_t t0 = uint32_t(ch0 + lc) * C;
+        if (part == 0) {
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
+            for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                R.kt[2 * ib + kk] =
-                    buf_ld16(rw_, cb + kWsK + uint32_t(((2 * w + ib) * 2 + kk) * 64 + lane) * 16u);
+                for (int kk = 0; kk < 2; ++kk)
+                    R.kt[2 * ib + kk] =
+                        buf_ld16(rw_, cb + kWsK + uint32_t(((2 * w + ib) * 2 + kk) * 64 + lane) * 16u);
+            R.ast = buf_ld16(rw_, tid < DK / 4 ? cb + kWsA + uint32_t(tid) * 16u
+                                               : uint32_t(nloc) * kWsChunk);
+            __builtin_amdgcn_sched_barrier(0);
+            return;
+        }
 #pragma unroll
         for (int x = 0; x < KV; ++x) {
             // V pieces: 64 rows x VT columns in 16-byte pieces, VT / 8 per row; with
@@ -375,8 +385,6 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
                                      ? ((t0 + r) * uint32_t(DV) + c0 + col) * 2u : obytes;
             R.vst[x] = buf_ld16(rv, off);
         }
-        R.ast = buf_ld16(rw_, tid < DK / 4 ? cb + kWsA + uint32_t(tid) * 16u
-                                           : uint32_t(nloc) * kWsChunk);
         if (OUT) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
@@ -386,6 +394,10 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
                 R.pf[kk] = buf_ld16(rw_, cb + kWsP + uint32_t((w * 2 + kk) * 64 + lane) * 16u);
         }
         __builtin_amdgcn_sched_barrier(0);
+    };
+    auto load_chunk = [&](ChainRegs<KV>& R, int lc) {
+        load_part(R, lc, 0);
+        load_part(R, lc, 1);
     };
     auto stage = [&](const ChainRegs<KV>& R, int buf) {
 #pragma unroll
@@ -397,7 +409,9 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
         if (tid < DK / 4) *reinterpret_cast<uint4*>(sm.a[buf] + 4 * tid) = R.ast;
     };
 
-    auto process = [&](const ChainRegs<KV>& R, const ChainRegs<KV>& Rn, int lc, int cur) {
+    auto process = [&](const ChainRegs<KV>& R, const ChainRegs<KV>& Rn, ChainRegs<KV>& Rl, int lc,
+                       int cur) {
+        load_part(Rl, lc + 2, 0);
         const uint16_t* vv = sm.v[cur];
         if (OUT) {
             // O^T = S^T q^^T + V^T P^T for rows 16 w ..; 4 NVT contiguous columns per lane
@@ -427,6 +441,7 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
                 buf_st8(ro, orow, ow[0]);
             }
         }
+        load_part(Rl, lc + 2, 1);
         // S = diag(a) S + K^^T V (key rows 32 w ..)
         bf16x8_t vf[2][NVT];
 #pragma unroll
@@ -532,14 +547,11 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
     stage(RA, 0);
     lds_barrier();
     for (int lc = 0; lc < nloc; lc += 3) {
-        load_chunk(RC, lc + 2);
-        process(RA, RB, lc, lc & 1);
+        process(RA, RB, RC, lc, lc & 1);
         if (lc + 1 >= nloc) break;
-        load_chunk(RA, lc + 3);
-        process(RB, RC, lc + 1, (lc + 1) & 1);
+        process(RB, RC, RA, lc + 1, (lc + 1) & 1);
         if (lc + 2 >= nloc) break;
-        load_chunk(RB, lc + 4);
-        process(RC, RA, lc + 2, lc & 1);
+        process(RC, RA, RB, lc + 2, lc & 1);
     }
 
     if (OUT) {

@@ -141,22 +141,37 @@ __global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
     const rsrc_t rv = make_rsrc(a.v + tok0 * DV, obytes);
     const rsrc_t ro = make_rsrc(a.o + tok0 * DV, obytes);
 
-    auto load_chunk = [&](ChainRegs<KST, KV>& R, int lc) {
+    // A chunk's loads go out in two parts (K and V, then q) over the processing of the
+    // chunk two before it, so that the memory unit's queue is not handed all of them at
+    // once; each part stays in program order (the memory-counter waits before a chunk
+    // is used count the loads issued after it).
+    auto load_part = [&](ChainRegs<KST, KV>& R, int lc, int part) {
         const uint32_t t0 = uint32_t(ch0 + lc) * C;
+        if (part == 0) {
 #pragma unroll
-        for (int x4 = 0; x4 < KST; ++x4) {
-            const int x = tid + NTW * x4, r = x >> 4, col = (x & 15) * 8;
-            R.kst[x4] = buf_ld16(rk, ((t0 + r) * DK + col) * 2u);
-            if (OUT) R.qst[x4] = buf_ld16(rq, ((t0 + r) * DK + col) * 2u);
-        }
+            for (int x4 = 0; x4 < KST; ++x4) {
+                const int x = tid + NTW * x4, r = x >> 4, col = (x & 15) * 8;
+                R.kst[x4] = buf_ld16(rk, ((t0 + r) * DK + col) * 2u);
+            }
 #pragma unroll
-        for (int x = 0; x < KV; ++x) {
-            // V pieces, VT / 8 per row; threads past the pieces read past the range
-            const int id = tid + NTW * x, r = id / (VT / 8), col = (id % (VT / 8)) * 8;
-            const uint32_t off = id < VP ? ((t0 + r) * uint32_t(DV) + c0 + col) * 2u : obytes;
-            R.vst[x] = buf_ld16(rv, off);
+            for (int x = 0; x < KV; ++x) {
+                // V pieces, VT / 8 per row; threads past the pieces read past the range
+                const int id = tid + NTW * x, r = id / (VT / 8), col = (id % (VT / 8)) * 8;
+                const uint32_t off = id < VP ? ((t0 + r) * uint32_t(DV) + c0 + col) * 2u : obytes;
+                R.vst[x] = buf_ld16(rv, off);
+            }
+        } else if (OUT) {
+#pragma unroll
+            for (int x4 = 0; x4 < KST; ++x4) {
+                const int x = tid + NTW * x4, r = x >> 4, col = (x & 15) * 8;
+                R.qst[x4] = buf_ld16(rq, ((t0 + r) * DK + col) * 2u);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
+    };
+    auto load_chunk = [&](ChainRegs<KST, KV>& R, int lc) {
+        load_part(R, lc, 0);
+        load_part(R, lc, 1);
     };
     // phi of one chunk's q and k (zero on padding rows), V, and per-wave column sums
     // of phi(k)
@@ -202,7 +217,8 @@ __global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
         }
     };
 
-    auto process = [&](const ChainRegs<KST, KV>& Rn, int lc, int cur) {
+    auto process = [&](const ChainRegs<KST, KV>& Rn, ChainRegs<KST, KV>& Rl, int lc, int cur) {
+        load_part(Rl, lc + 2, 0);
         const uint16_t* kt = sm.kt[cur];
         const uint16_t* vv = sm.v[cur];
         if (OUT) {
@@ -249,6 +265,7 @@ __global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
                 if (part == 0) sm.qz[r] = acc;
             }
             lds_barrier();
+            load_part(Rl, lc + 2, 1);
             // ---- O^T = S^T phi(Q)^T + V^T P^T, divided by the row's denominator
             float den = sm.qz[rw] + a.eps;
             const int tb = (rb * (rb + 1)) / 2;
@@ -316,14 +333,11 @@ __global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
     stage(RA, 0, 0);
     lds_barrier();
     for (int lc = 0; lc < nloc; lc += 3) {
-        load_chunk(RC, lc + 2);
-        process(RB, lc, lc & 1);
+        process(RB, RC, lc, lc & 1);
         if (lc + 1 >= nloc) break;
-        load_chunk(RA, lc + 3);
-        process(RC, lc + 1, (lc + 1) & 1);
+        process(RC, RA, lc + 1, (lc + 1) & 1);
         if (lc + 2 >= nloc) break;
-        load_chunk(RB, lc + 4);
-        process(RA, lc + 2, lc & 1);
+        process(RA, RB, lc + 2, lc & 1);
     }
 
     if (OUT) {
