@@ -20,9 +20,13 @@ Gate parameterisations (input distributions, per workload):
   * GDN: alpha = exp(-softplus(u)) = sigmoid(-u), beta = sigmoid(w), u, w ~
     N(0, 1) per (token, head) (scalar gates in (0, 1), "线性注意力与 SSM"
     section GDN);
+  * KDA: a retention per (token, key channel) from the bounded log-decay of
+    "状态空间与线性注意力" section KDA, alpha = exp(g_min sigmoid(e^A z)) with
+    g_min = -5 and A = 0 (the page's own example), z ~ N(0, 1), so alpha lies
+    in (e^-5, 1); beta = sigmoid(w), w ~ N(0, 1) per (token, head);
   * extra gate kinds for carry-sensitive tests: "slow" (alpha or g =
-    exp(logsigmoid(u) / 16), about 0.95), "ones" (g = 1 or alpha = 1),
-    "beta0" (beta = 0), "beta1" (beta = 1).
+    exp(logsigmoid(u) / 16), about 0.95; KDA: exp(-5 sigmoid(z - 6)), about
+    0.99), "ones" (g = 1 or alpha = 1), "beta0" (beta = 0), "beta1" (beta = 1).
 """
 from __future__ import annotations
 
@@ -80,7 +84,7 @@ def _sigmoid(u):
 @dataclass(frozen=True)
 class Workload:
     name: str
-    variant: str            # "kath" | "gla" | "gdn"
+    variant: str            # "kath" | "gla" | "gdn" | "kda"
     B: int
     H: int
     N: int
@@ -121,6 +125,10 @@ WORKLOADS = {
         "gdn_bf16_b4h16_n8192_d128", "gdn", 4, 16, 8192, 128, 128, "bf16", "bf16", seed=4,
         l2norm_qk=True, description="Gated DeltaNet forward, B=4 H=16 N=8192 d=128, bf16, "
                                     "q/k L2-normalized"),
+    "kda_bf16_b4h16_n8192_d128": Workload(
+        "kda_bf16_b4h16_n8192_d128", "kda", 4, 16, 8192, 128, 128, "bf16", "bf16", seed=6,
+        l2norm_qk=True, description="Kimi Delta Attention forward, B=4 H=16 N=8192 d=128, bf16, "
+                                    "q/k L2-normalized, bounded per-channel retention"),
     "decode_gdn_256x32_d128": Workload(
         "decode_gdn_256x32_d128", "gdn", 256, 32, 1, 128, 128, "bf16", "bf16", seed=5,
         l2norm_qk=True, decode=True,
@@ -129,7 +137,13 @@ WORKLOADS = {
         "decode_gla_256x32_d128", "gla", 256, 32, 1, 128, 128, "bf16", "bf16", seed=5,
         qk_scale=1.0 / np.sqrt(128.0), v_scale=1.0 / np.sqrt(128.0), decode=True,
         description="GLA decode step, 256 sequences x 32 heads, d=128, fp32 state"),
+    "decode_kda_256x32_d128": Workload(
+        "decode_kda_256x32_d128", "kda", 256, 32, 1, 128, 128, "bf16", "bf16", seed=7,
+        l2norm_qk=True, decode=True,
+        description="KDA decode step, 256 sequences x 32 heads, d=128, fp32 state"),
 }
+
+KDA_LOG_DECAY_MIN = -5.0   # g_min of the bounded log-decay
 
 DECODE_STATE_STD = 0.02   # decode state S ~ N(0, 0.02^2): std 0.02 (torch normal(mean, std))
 DECODE_POOL = 8           # distinct token sets cycled through by repeated decode steps
@@ -181,6 +195,26 @@ def _draw_gates(rng, wl: Workload, shape_tok):
             beta = np.zeros_like(w)
         elif kind == "beta1":
             alpha = _sigmoid(-u)
+            beta = np.ones_like(w)
+        else:
+            raise ValueError(kind)
+        out["g"] = alpha
+        out["beta"] = beta
+    elif wl.variant == "kda":
+        z = rng.standard_normal((B, H, N, wl.dk))
+        w = rng.standard_normal((B, H, N))
+        beta = _sigmoid(w)
+        if kind == "default":
+            alpha = np.exp(KDA_LOG_DECAY_MIN * _sigmoid(z))
+        elif kind == "slow":
+            alpha = np.exp(KDA_LOG_DECAY_MIN * _sigmoid(z - 6.0))
+        elif kind == "ones":
+            alpha = np.ones_like(z)
+        elif kind == "beta0":
+            alpha = np.exp(KDA_LOG_DECAY_MIN * _sigmoid(z - 6.0))
+            beta = np.zeros_like(w)
+        elif kind == "beta1":
+            alpha = np.exp(KDA_LOG_DECAY_MIN * _sigmoid(z))
             beta = np.ones_like(w)
         else:
             raise ValueError(kind)
@@ -267,6 +301,8 @@ def algorithmic_bytes_per_token_head(wl: Workload) -> int:
         b += wl.dk * gsz
     elif wl.variant == "gdn":
         b += 2 * gsz
+    elif wl.variant == "kda":
+        b += wl.dk * gsz + gsz
     return b
 
 
@@ -288,12 +324,13 @@ def algorithmic_flops(wl: Workload, chunk: int = 64) -> int:
     (2 x 2*dk*dv); KATH adds the normaliser column (2*C + 2*dk for P 1, phi(q) z,
     and dk for z += phi(k)). GDN: K K^T, Q K^T (2 x 2*C*dk), T (beta gamma K)
     (2*C*dk), T (beta V) and P U (2 x 2*C*dv), Q S, W S and K^T U
-    (3 x 2*dk*dv) and the triangular inverse (C^2/3 per token).
+    (3 x 2*dk*dv) and the triangular inverse (C^2/3 per token). KDA counts as GDN
+    (its decay sits inside the same products).
     Decode: 2*dk*dv per state read or write product (GLA 5, GDN 7, KATH 4 dk*dv).
     """
     dk, dv, C = wl.dk, wl.dv, chunk
     if wl.decode:
-        per = {"gla": 5, "gdn": 7, "kath": 4}[wl.variant] * dk * dv
+        per = {"gla": 5, "gdn": 7, "kda": 7, "kath": 4}[wl.variant] * dk * dv
         return wl.B * wl.H * per
     if wl.variant == "gla":
         per = 2 * C * dk + 2 * C * dv + 4 * dk * dv

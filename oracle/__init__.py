@@ -28,8 +28,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-KATH, GLA, GDN = 0, 1, 2
-VARIANTS = {"kath": KATH, "gla": GLA, "gdn": GDN}
+KATH, GLA, GDN, KDA = 0, 1, 2, 3
+VARIANTS = {"kath": KATH, "gla": GLA, "gdn": GDN, "kda": KDA}
 
 
 class _Counts(ctypes.Structure):
@@ -106,8 +106,9 @@ def prefill(variant, q, k, v, g=None, beta=None, S0=None, z0=None, eps=1e-6,
             threads: int = 0, lib_path: str | None = None, with_counts: bool = False):
     """Run the token recurrence over whole sequences.
 
-    q, k: [B,H,N,dk]; v: [B,H,N,dv]; g: GLA [B,H,N,dk] or GDN alpha [B,H,N];
-    beta: GDN [B,H,N]; S0: [B,H,dk,dv] or None; z0: [B,H,dk] or None (KATH).
+    q, k: [B,H,N,dk]; v: [B,H,N,dv]; g: GLA [B,H,N,dk], GDN alpha [B,H,N] or KDA
+    alpha [B,H,N,dk]; beta: GDN / KDA [B,H,N]; S0: [B,H,dk,dv] or None; z0:
+    [B,H,dk] or None (KATH).
     Returns (o [B,H,N,dv], S [B,H,dk,dv], z [B,H,dk] or None[, Counts]).
     """
     lib = load(lib_path)
@@ -120,6 +121,9 @@ def prefill(variant, q, k, v, g=None, beta=None, S0=None, z0=None, eps=1e-6,
         assert g is not None and g.shape == (B, H, N, dk)
     if vt == GDN:
         assert g is not None and g.shape == (B, H, N)
+        assert beta is not None and beta.shape == (B, H, N)
+    if vt == KDA:
+        assert g is not None and g.shape == (B, H, N, dk)
         assert beta is not None and beta.shape == (B, H, N)
     if S0 is not None:
         assert S0.shape == (B, H, dk, dv)
@@ -144,7 +148,8 @@ def decode_step(variant, q, k, v, S, g=None, beta=None, z=None, eps=1e-6, thread
                 lib_path: str | None = None):
     """One in-place decode step on float64 arrays S [B,H,dk,dv] (and z [B,H,dk] for KATH).
 
-    q, k: [B,H,dk]; v: [B,H,dv]; g: GLA [B,H,dk] or GDN alpha [B,H]; beta: GDN [B,H].
+    q, k: [B,H,dk]; v: [B,H,dv]; g: GLA [B,H,dk], GDN alpha [B,H] or KDA alpha
+    [B,H,dk]; beta: GDN / KDA [B,H].
     Returns o [B,H,dv]. S and z must be C-contiguous float64 and are updated in place.
     """
     lib = load(lib_path)

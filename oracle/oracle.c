@@ -25,9 +25,14 @@
  *        and notes that the write equals a correction by v_t - a_t S_{t-1} k_t.
  *        Key-major this is S_t = a_t S_{t-1} + k_t u_t^T with
  *          u_t = b_t (v_t - a_t S_{t-1}^T k_t),   o_t = S_t^T q_t.
+ *  KDA   "状态空间与线性注意力" (wineandchord), section KDA: a retention per key
+ *        channel a_t in (0,1)^{d_k} decays the old state first, then the current
+ *        key asks what the decayed state already predicts and writes the error:
+ *          Sbar = Diag(a_t) S_{t-1}        [row i scaled by a_{t,i}]
+ *          S_t = Sbar + b_t k_t (v_t - Sbar^T k_t)^T,   o_t = S_t^T q_t.
  *
  * Every variant reads the state after the token's update (the post-update
- * read of all three pages' output equations).
+ * read of the output equations on every page).
  *
  * Decode is the same per-token body applied once, in place.
  *
@@ -43,7 +48,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_KATH = 0, OR_GLA = 1, OR_GDN = 2 };
+enum { OR_KATH = 0, OR_GLA = 1, OR_GDN = 2, OR_KDA = 3 };
 
 typedef struct {
     uint64_t state_update_macs; /* multiply-adds that write S */
@@ -97,6 +102,25 @@ static void token_step(int variant, int dk, int dv, const double *q, const doubl
             o[j] = acc;
         }
         c->state_read_macs += (uint64_t)dk * (uint64_t)dv;
+    } else if (variant == OR_KDA) { /* g: retention per key channel */
+        double *u = work; /* dv */
+        for (i = 0; i < dk; ++i)
+            for (j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= g[i];   /* decay first */
+        for (j = 0; j < dv; ++j) {
+            double pred = 0.0; /* (Sbar^T k_t)_j: what the decayed state recalls for k_t */
+            for (i = 0; i < dk; ++i) pred += S[(size_t)i * dv + j] * k[i];
+            u[j] = beta * (v[j] - pred);
+        }
+        for (i = 0; i < dk; ++i) {
+            for (j = 0; j < dv; ++j) S[(size_t)i * dv + j] += k[i] * u[j];
+            c->state_update_macs += (uint64_t)dv;
+        }
+        for (j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (i = 0; i < dk; ++i) acc += q[i] * S[(size_t)i * dv + j];
+            o[j] = acc;
+        }
+        c->state_read_macs += (uint64_t)dk * (uint64_t)dv;
     } else { /* OR_GDN: alpha is g[0] */
         double alpha = g[0];
         double *u = work; /* dv */
@@ -122,7 +146,7 @@ static void token_step(int variant, int dk, int dv, const double *q, const doubl
 
 static int check_args(int variant, int B, int H, int N, int dk, int dv)
 {
-    if (variant < OR_KATH || variant > OR_GDN) return 1;
+    if (variant < OR_KATH || variant > OR_KDA) return 1;
     if (B < 0 || H < 0 || N < 0 || dk < 1 || dv < 1) return 1;
     return 0;
 }
@@ -130,8 +154,8 @@ static int check_args(int variant, int B, int H, int N, int dk, int dv)
 /*
  * Whole-sequence forward.
  *   q, k: [B,H,N,dk]   v: [B,H,N,dv]
- *   g:    GLA [B,H,N,dk]; GDN alpha [B,H,N]; KATH unused (may be NULL)
- *   beta: GDN [B,H,N]; otherwise unused
+ *   g:    GLA [B,H,N,dk]; GDN alpha [B,H,N]; KDA alpha [B,H,N,dk]; KATH unused (may be NULL)
+ *   beta: GDN and KDA [B,H,N]; otherwise unused
  *   S0:   [B,H,dk,dv] or NULL (zeros);   z0: [B,H,dk] or NULL (zeros), KATH only
  *   o:    [B,H,N,dv] out;  S: [B,H,dk,dv] out (final state);  z: [B,H,dk] out (KATH, may be NULL otherwise)
  *   counts: optional, summed over all sequences.
@@ -149,7 +173,7 @@ int oracle_prefill(int variant, int B, int H, int N, int dk, int dv,
     if (check_args(variant, B, H, N, dk, dv)) return 1;
     if (variant == OR_KATH && z == NULL) return 1;
     if (variant != OR_KATH && g == NULL) return 1;
-    if (variant == OR_GDN && beta == NULL) return 1;
+    if ((variant == OR_GDN || variant == OR_KDA) && beta == NULL) return 1;
     memset(&total, 0, sizeof(total));
     nseq = (long long)B * H;
 #ifdef _OPENMP
@@ -179,6 +203,7 @@ int oracle_prefill(int variant, int B, int H, int N, int dk, int dv,
                 double bt = 0.0;
                 if (variant == OR_GLA) gt = g + tok * dk;
                 if (variant == OR_GDN) { gt = g + tok; bt = beta[tok]; }
+                if (variant == OR_KDA) { gt = g + tok * dk; bt = beta[tok]; }
                 token_step(variant, dk, dv, q + tok * dk, k + tok * dk, v + tok * dv, gt, bt,
                            eps, Sh, zh, o + tok * dv, work, &c);
             }
@@ -199,7 +224,8 @@ int oracle_prefill(int variant, int B, int H, int N, int dk, int dv,
 
 /*
  * One decode step for B*H independent states, in place.
- *   q, k: [B,H,dk]  v: [B,H,dv]  g: GLA [B,H,dk] / GDN alpha [B,H]  beta: GDN [B,H]
+ *   q, k: [B,H,dk]  v: [B,H,dv]  g: GLA [B,H,dk] / GDN alpha [B,H] / KDA alpha [B,H,dk]
+ *   beta: GDN and KDA [B,H]
  *   S: [B,H,dk,dv] in/out;  z: [B,H,dk] in/out (KATH);  o: [B,H,dv] out.
  */
 int oracle_decode_step(int variant, int B, int H, int dk, int dv,
@@ -211,7 +237,7 @@ int oracle_decode_step(int variant, int B, int H, int dk, int dv,
     if (check_args(variant, B, H, 1, dk, dv)) return 1;
     if (variant == OR_KATH && z == NULL) return 1;
     if (variant != OR_KATH && g == NULL) return 1;
-    if (variant == OR_GDN && beta == NULL) return 1;
+    if ((variant == OR_GDN || variant == OR_KDA) && beta == NULL) return 1;
     nseq = (long long)B * H;
 #ifdef _OPENMP
     if (threads > 0) omp_set_num_threads(threads);
@@ -229,6 +255,7 @@ int oracle_decode_step(int variant, int B, int H, int dk, int dv,
             double bt = 0.0;
             if (variant == OR_GLA) gt = g + (size_t)seq * dk;
             if (variant == OR_GDN) { gt = g + seq; bt = beta[seq]; }
+            if (variant == OR_KDA) { gt = g + (size_t)seq * dk; bt = beta[seq]; }
             token_step(variant, dk, dv, q + (size_t)seq * dk, k + (size_t)seq * dk,
                        v + (size_t)seq * dv, gt, bt, eps, S + (size_t)seq * dk * dv,
                        variant == OR_KATH ? z + (size_t)seq * dk : NULL,

@@ -12,7 +12,9 @@ not come from the oracle itself:
     implementation: split anywhere, carry the state, equal the whole scan);
   * the gated delta rule written in its value-major matrix form
     ("线性注意力与 SSM", section GDN) and the KDA recurrence with a broadcast
-    gate ("状态空间与线性注意力", section KDA);
+    gate ("状态空间与线性注意力", section KDA); KDA's expanded transition
+    (I - b k k^T) Diag(a), its reduction to the gated delta rule, and its
+    per-channel closed form;
   * the worked delta-rule example (golden fixture);
   * the single-head hand count (golden fixture);
   * closed forms for constant inputs; special cases that reduce to known
@@ -57,6 +59,9 @@ def rand_case(variant, B=1, H=2, N=12, dk=5, dv=4, seed=0, with_state=True, unit
         g = rng.uniform(0.5, 1.0, (B, H, N, dk))
     elif variant == "gdn":
         g = rng.uniform(0.5, 1.0, (B, H, N))
+        beta = rng.uniform(0.05, 0.95, (B, H, N))
+    elif variant == "kda":
+        g = rng.uniform(0.5, 1.0, (B, H, N, dk))
         beta = rng.uniform(0.05, 0.95, (B, H, N))
     S0 = rng.standard_normal((B, H, dk, dv)) * 0.7 if with_state else None
     z0 = (rng.uniform(0.5, 2.0, (B, H, dk)) if (with_state and variant == "kath") else None)
@@ -109,6 +114,22 @@ def quad_gdn(q, k, v, alpha, beta, S0):
     T, dk = q.shape
     I = np.eye(dk)
     F = [alpha[t] * (I - beta[t] * np.outer(k[t], k[t])) for t in range(T)]
+    return _quad_delta(q, k, v, beta, S0, F)
+
+
+def quad_kda(q, k, v, alpha, beta, S0):
+    """KDA's expanded transition F_t = (I - beta_t k_t k_t^T) Diag(alpha_t) ("状态空间与线性
+    注意力", section KDA, the second form), later factors on the left."""
+    T, dk = q.shape
+    I = np.eye(dk)
+    F = [(I - beta[t] * np.outer(k[t], k[t])) @ np.diag(alpha[t]) for t in range(T)]
+    return _quad_delta(q, k, v, beta, S0, F)
+
+
+def _quad_delta(q, k, v, beta, S0, F):
+    """S_t = F_t S_{t-1} + beta_t k_t v_t^T unrolled into products of the F's."""
+    T, dk = q.shape
+    I = np.eye(dk)
 
     def chain(t, s):  # F_t F_{t-1} ... F_{s+1}   (identity when t == s)
         P = I.copy()
@@ -132,7 +153,8 @@ def quad_gdn(q, k, v, alpha, beta, S0):
 # ---------------------------------------------------------------------------
 
 def pin_quadratic_form(lib=None):
-    for variant, dk, dv in (("kath", 5, 3), ("gla", 5, 3), ("gdn", 4, 6), ("gdn", 6, 4)):
+    for variant, dk, dv in (("kath", 5, 3), ("gla", 5, 3), ("gdn", 4, 6), ("gdn", 6, 4),
+                            ("kda", 5, 3), ("kda", 3, 6)):
         case = rand_case(variant, B=2, H=1, N=11, dk=dk, dv=dv, seed=7, with_state=True)
         eps = 0.3 if variant == "kath" else 1e-6
         o, S, z = run(variant, case, lib, eps=eps)
@@ -145,15 +167,18 @@ def pin_quadratic_form(lib=None):
             elif variant == "gla":
                 O_ref, S_ref = quad_gla(case["q"][sl], case["k"][sl], case["v"][sl],
                                         case["g"][sl], case["S0"][sl])
-            else:
+            elif variant == "gdn":
                 O_ref, S_ref = quad_gdn(case["q"][sl], case["k"][sl], case["v"][sl],
+                                        case["g"][sl], case["beta"][sl], case["S0"][sl])
+            else:
+                O_ref, S_ref = quad_kda(case["q"][sl], case["k"][sl], case["v"][sl],
                                         case["g"][sl], case["beta"][sl], case["S0"][sl])
             assert rel(o[sl], O_ref) < 1e-12, f"{variant} o vs quadratic form: {rel(o[sl], O_ref)}"
             assert rel(S[sl], S_ref) < 1e-12, f"{variant} S vs quadratic form"
 
 
 def pin_split_invariance(lib=None):
-    for variant in ("kath", "gla", "gdn"):
+    for variant in ("kath", "gla", "gdn", "kda"):
         case = rand_case(variant, B=1, H=3, N=23, dk=6, dv=5, seed=11, with_state=True)
         o, S, z = run(variant, case, lib)
         for m in (1, 7, 16, 22):
@@ -186,6 +211,37 @@ def pin_gdn_page_forms(lib=None):
         assert rel(o[0, 0, t], Sv @ q[t]) < 1e-12, "GDN o vs value-major form"
         assert rel(o[0, 0, t], Sk.T @ q[t]) < 1e-12, "GDN o vs KDA form"
     assert rel(S[0, 0], Sv.T) < 1e-12 and rel(S[0, 0], Sk) < 1e-12
+
+
+def pin_kda_forms(lib=None):
+    """KDA: decay-then-correct and the expanded (I - b k k^T) Diag(a) S + b k v^T form agree
+    with the oracle at every step; with the retention broadcast over the key channels KDA
+    is the gated delta rule (pinned on its own above); a channel the keys never touch
+    only decays."""
+    case = rand_case("kda", B=1, H=1, N=9, dk=5, dv=3, seed=15, with_state=True, unit_keys=True)
+    q, k, v = case["q"][0, 0], case["k"][0, 0], case["v"][0, 0]
+    a, b = case["g"][0, 0], case["beta"][0, 0]
+    o, S, _ = run("kda", case, lib)
+    Sx = case["S0"][0, 0].copy()
+    I = np.eye(5)
+    for t in range(9):
+        Sx = (I - b[t] * np.outer(k[t], k[t])) @ np.diag(a[t]) @ Sx + b[t] * np.outer(k[t], v[t])
+        assert rel(o[0, 0, t], Sx.T @ q[t]) < 1e-12, "KDA o vs expanded form"
+    assert rel(S[0, 0], Sx) < 1e-12
+    # broadcast retention: equal to GDN with the scalar alpha
+    g_case = rand_case("gdn", B=1, H=2, N=12, dk=4, dv=3, seed=16, with_state=True)
+    k_case = dict(g_case)
+    k_case["g"] = np.repeat(g_case["g"][..., None], 4, axis=-1)
+    og, Sg, _ = run("gdn", g_case, lib)
+    ok, Sk, _ = run("kda", k_case, lib)
+    assert rel(ok, og) < 1e-12 and rel(Sk, Sg) < 1e-12, "KDA with broadcast retention vs GDN"
+    # keys confined to channels 0..2: rows 3, 4 of S0 decay by the product of their
+    # retentions and never mix with the others
+    case = rand_case("kda", B=1, H=1, N=10, dk=5, dv=3, seed=18, with_state=True)
+    case["k"][..., 3:] = 0.0
+    o, S, _ = run("kda", case, lib)
+    pref = np.prod(case["g"][0, 0], axis=0)
+    assert rel(S[0, 0, 3:], pref[3:, None] * case["S0"][0, 0, 3:]) < 1e-13, "KDA idle channels"
 
 
 def pin_delta_identity(lib=None):
@@ -277,6 +333,21 @@ def pin_closed_forms(lib=None):
         p = be * vv * (1 - rho ** tt) / (1 - rho)
         assert rel(o[0, 0, tt - 1], (ku @ qv) * p) < 1e-13, "GDN closed form o"
     assert rel(S[0, 0], np.outer(ku, be * vv * (1 - rho ** T) / (1 - rho))) < 1e-13
+    # KDA, constant tokens with k = e_0 and a constant retention per channel: row 0 of the
+    # state follows r_t = rho r_{t-1} + beta v with rho = a_0 (1 - beta); the other rows
+    # only decay, row i by a_i^t
+    e0 = np.array([1.0, 0.0, 0.0, 0.0, 0.0])
+    av = np.array([0.9, 0.5, 0.99, 0.7, 0.3])
+    be = 0.35
+    rho = av[0] * (1 - be)
+    S0 = np.arange(15, dtype=np.float64).reshape(1, 1, 5, 3) / 7.0 - 1.0
+    o, S, _ = oracle.prefill("kda", tile(qv), tile(e0), tile(vv), g=tile(av),
+                             beta=np.full((1, 1, T), be), S0=S0, lib_path=lib)
+    for tt in (1, 2, 9, T):
+        St = (av[:, None] ** tt) * S0[0, 0]
+        St[0] = rho ** tt * S0[0, 0, 0] + be * vv * (1 - rho ** tt) / (1 - rho)
+        assert rel(o[0, 0, tt - 1], St.T @ qv) < 1e-13, "KDA closed form o"
+    assert rel(S[0, 0], St) < 1e-13
 
 
 def pin_special_cases(lib=None):
@@ -315,10 +386,28 @@ def pin_special_cases(lib=None):
     tt = np.arange(13)
     D = np.where(tt[:, None] >= tt[None, :], gam ** (tt[:, None] - tt[None, :]).clip(0), 0.0)
     assert rel(o[0, 0], ((Q @ K.T) * D) @ V) < 1e-12, "RetNet form"
+    # KDA beta = 0: every channel of S0 decays by its own retention, nothing is written
+    case = rand_case("kda", B=1, H=2, N=10, dk=4, dv=3, seed=19, with_state=True)
+    case["beta"] = np.zeros_like(case["beta"])
+    o, S, _ = run("kda", case, lib)
+    pref = np.cumprod(case["g"], axis=2)
+    for h in range(2):
+        for t in range(10):
+            ref = (pref[0, h, t][:, None] * case["S0"][0, h]).T @ case["q"][0, h, t]
+            assert rel(o[0, h, t], ref) < 1e-13, "KDA beta=0"
+    # KDA retention 1: DeltaNet
+    case = rand_case("kda", B=1, H=1, N=10, dk=4, dv=3, seed=20, with_state=True)
+    case["g"] = np.ones_like(case["g"])
+    o, S, _ = run("kda", case, lib)
+    St = case["S0"][0, 0].copy()
+    for t in range(10):
+        kk = case["k"][0, 0, t]
+        St = St + case["beta"][0, 0, t] * np.outer(kk, case["v"][0, 0, t] - St.T @ kk)
+        assert rel(o[0, 0, t], St.T @ case["q"][0, 0, t]) < 1e-12, "KDA retention 1 (DeltaNet)"
 
 
 def pin_causality(lib=None):
-    for variant in ("kath", "gla", "gdn"):
+    for variant in ("kath", "gla", "gdn", "kda"):
         case = rand_case(variant, B=1, H=2, N=16, dk=4, dv=3, seed=13, with_state=True)
         o, _, _ = run(variant, case, lib)
         for tp in (0, 5, 15):
@@ -334,7 +423,7 @@ def pin_causality(lib=None):
 
 
 def pin_linearity(lib=None):
-    for variant in ("gla", "gdn"):
+    for variant in ("gla", "gdn", "kda"):
         case = rand_case(variant, B=1, H=2, N=14, dk=5, dv=4, seed=17, with_state=False)
         rng = np.random.default_rng(1)
         v1, v2 = rng.standard_normal(case["v"].shape), rng.standard_normal(case["v"].shape)
@@ -349,7 +438,7 @@ def pin_linearity(lib=None):
 
 
 def pin_decode_matches_prefill(lib=None):
-    for variant in ("kath", "gla", "gdn"):
+    for variant in ("kath", "gla", "gdn", "kda"):
         case = rand_case(variant, B=2, H=2, N=6, dk=4, dv=3, seed=21, with_state=True)
         o, S, z = run(variant, case, lib)
         St = case["S0"].copy()
@@ -365,6 +454,7 @@ def pin_decode_matches_prefill(lib=None):
             assert np.array_equal(zt, z)
 
 
-ALL_PINS = [pin_quadratic_form, pin_split_invariance, pin_gdn_page_forms, pin_delta_identity,
+ALL_PINS = [pin_quadratic_form, pin_split_invariance, pin_gdn_page_forms, pin_kda_forms,
+            pin_delta_identity,
             pin_worked_example, pin_closed_forms, pin_special_cases, pin_causality,
             pin_linearity, pin_decode_matches_prefill]

@@ -29,6 +29,27 @@ MUTATIONS = {
     "gdn_transposed_read": ("pred += S[(size_t)i * dv + j] * k[i];",
                             "pred += S[(size_t)j * dv + i] * k[i];"),
     "initial_state_ignored": ("if (S0) memcpy", "if (0) memcpy"),
+    "kda_no_decay": ("for (j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= g[i];   /* decay first */",
+                     "for (j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= 1.0;"),
+    "kda_prediction_before_decay": (
+        "        for (i = 0; i < dk; ++i)\n"
+        "            for (j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= g[i];   /* decay first */\n"
+        "        for (j = 0; j < dv; ++j) {\n"
+        "            double pred = 0.0; /* (Sbar^T k_t)_j: what the decayed state recalls for k_t */\n"
+        "            for (i = 0; i < dk; ++i) pred += S[(size_t)i * dv + j] * k[i];\n"
+        "            u[j] = beta * (v[j] - pred);\n"
+        "        }\n",
+        "        for (j = 0; j < dv; ++j) {\n"
+        "            double pred = 0.0;\n"
+        "            for (i = 0; i < dk; ++i) pred += S[(size_t)i * dv + j] * k[i];\n"
+        "            u[j] = beta * (v[j] - pred);\n"
+        "        }\n"
+        "        for (i = 0; i < dk; ++i)\n"
+        "            for (j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= g[i];\n"),
+    "kda_decay_transposed": ("S[(size_t)i * dv + j] *= g[i];", "S[(size_t)i * dv + j] *= g[j % dk];"),
+    "kda_no_beta": ("u[j] = beta * (v[j] - pred);", "u[j] = (v[j] - pred);"),
+    "kda_gate_previous_token": ("if (variant == OR_KDA) { gt = g + tok * dk;",
+                                "if (variant == OR_KDA) { gt = g + (t > 0 ? tok - 1 : tok) * dk;"),
     "read_uses_key": ("for (i = 0; i < dk; ++i) acc += q[i] * S[(size_t)i * dv + j];\n            o[j] = acc;\n        }\n        c->state_read_macs += (uint64_t)dk * (uint64_t)dv;\n    } else {",
                       "for (i = 0; i < dk; ++i) acc += k[i] * S[(size_t)i * dv + j];\n            o[j] = acc;\n        }\n        c->state_read_macs += (uint64_t)dk * (uint64_t)dv;\n    } else {"),
 }
