@@ -13,11 +13,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblinattn.so")
 
 LA_OK, LA_ERR_INVALID, LA_ERR_UNSUPPORTED, LA_ERR_HIP, LA_ERR_WORKSPACE = 0, 1, 2, 3, 4
-LA_KATH, LA_GLA, LA_GDN = 0, 1, 2
+LA_KATH, LA_GLA, LA_GDN, LA_KDA = 0, 1, 2, 3
 LA_F32, LA_BF16 = 0, 1
 LA_PATH_AUTO, LA_PATH_VALU, LA_PATH_MFMA = 0, 1, 2
 
-VARIANTS = {"kath": LA_KATH, "gla": LA_GLA, "gdn": LA_GDN}
+VARIANTS = {"kath": LA_KATH, "gla": LA_GLA, "gdn": LA_GDN, "kda": LA_KDA}
 PATHS = {"auto": LA_PATH_AUTO, "valu": LA_PATH_VALU, "mfma": LA_PATH_MFMA}
 EXPORTS = ("la_prefill", "la_prefill_workspace_size", "la_decode_step", "la_status_str",
            "la_abi_version")
@@ -120,7 +120,8 @@ def prefill(q, k, v, g=None, beta=None, *, variant: str, S0=None, z0=None, eps: 
     """Chunked prefill through ``la_prefill``.
 
     q, k [B,H,N,dk], v [B,H,N,dv] (float32 or bfloat16, one dtype); g (GLA
-    [B,H,N,dk] / GDN alpha [B,H,N]) and beta (GDN [B,H,N]) float32 or bfloat16;
+    [B,H,N,dk] / GDN alpha [B,H,N] / KDA alpha [B,H,N,dk]) and beta (GDN / KDA
+    [B,H,N]) float32 or bfloat16;
     S0 [B,H,dk,dv] and z0 [B,H,dk] float32 or None. Outputs are allocated with
     torch unless given. Returns (o, S_final, z_final or None).
     """
@@ -158,7 +159,7 @@ def decode_step(q, k, v, S, g=None, beta=None, *, variant: str, z=None, eps: flo
     """One in-place decode step through ``la_decode_step``.
 
     q, k [B,H,dk]; v [B,H,dv]; S [B,H,dk,dv] float32 (updated in place);
-    g (GLA [B,H,dk] / GDN alpha [B,H]); beta (GDN [B,H]); z [B,H,dk] (KATH,
+    g (GLA [B,H,dk] / GDN alpha [B,H] / KDA alpha [B,H,dk]); beta (GDN / KDA [B,H]); z [B,H,dk] (KATH,
     updated in place). Returns o [B,H,dv].
     """
     import torch

@@ -28,7 +28,7 @@ COMMON = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
-SOURCES = ["la_api.cpp", "decode.hip", "prefill_valu.hip", "prefill_kath_mfma.hip",
+SOURCES = ["la_api.cpp", "decode.hip", "prefill_valu.hip", "prefill_kath_mfma.hip", "prefill_kda_mfma.hip",
            "prefill_gla_mfma.hip", "prefill_gdn_mfma.hip"]
 
 

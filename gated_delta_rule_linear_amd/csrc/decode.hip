@@ -14,7 +14,10 @@
 //   GLA  r = S^T (q * g);  S <- diag(g) S + k v^T;  o = r + (q . k) v
 //   KATH r = S^T phi(q);  S <- S + phi(k) v^T;  z <- z + phi(k);
 //        o = (r + (phi(q) . phi(k)) v) / (phi(q) . z_new + eps)
-// ("Linear / RNN 路线", sections 2.1 and 2.2; "线性注意力与 SSM", section GDN.)
+//   KDA  p = S^T (a * k), r = S^T (a * q) (the decayed state Diag(a) S read through
+//        k and q); u = beta (v - p);  S <- Diag(a) S + k u^T;  o = r + (k . q) u
+// ("Linear / RNN 路线", sections 2.1 and 2.2; "线性注意力与 SSM", section GDN;
+// "状态空间与线性注意力", section KDA.)
 #include "common.hpp"
 #include "la_internal.h"
 
@@ -35,6 +38,10 @@ struct DecodeArgs {
 // threads; GDN, with twice the registers per thread, slower.
 template <int VAR>
 constexpr int decode_nthreads() { return VAR == LA_GLA ? 1024 : 512; }
+template <int VAR>
+constexpr bool has_delta() { return VAR == LA_GDN || VAR == LA_KDA; }
+template <int VAR>
+constexpr bool has_channel_gate() { return VAR == LA_GLA || VAR == LA_KDA; }
 
 template <int DK, int DV, int NTH>
 struct DecodeShape {
@@ -60,7 +67,7 @@ __global__ __launch_bounds__(decode_threads(DK, DV, decode_nthreads<VAR>())) voi
     const size_t seq = blockIdx.x;
     float* S = a.S + seq * (size_t(DK) * DV);
 
-    __shared__ float sq[DK], sk[DK], sw[DK];  // sw: q*g (GLA)
+    __shared__ float sq[DK], sk[DK], sw[DK];  // sw: the gate per key dim (GLA, KDA)
     __shared__ float sv[DV];
     __shared__ float4 red[2][RG][NCG];
     __shared__ float scal[4];
@@ -83,7 +90,7 @@ __global__ __launch_bounds__(decode_threads(DK, DV, decode_nthreads<VAR>())) voi
         }
         sq[i] = qi;
         sk[i] = ki;
-        if (VAR == LA_GLA) sw[i] = load_elem(a.g, seq * DK + i, gb);
+        if (has_channel_gate<VAR>()) sw[i] = load_elem(a.g, seq * DK + i, gb);
     }
     for (int j = tid; j < DV; j += NT) sv[j] = load_elem(a.v, seq * DV + j, iob);
     __syncthreads();
@@ -100,10 +107,8 @@ __global__ __launch_bounds__(decode_threads(DK, DV, decode_nthreads<VAR>())) voi
         if (tid == 0) {
             scal[0] = qk;
             scal[1] = qz + a.eps;
-            if (VAR == LA_GDN) {
-                scal[2] = load_elem(a.g, seq, gb);
-                scal[3] = load_elem(a.beta, seq, gb);
-            }
+            if (VAR == LA_GDN) scal[2] = load_elem(a.g, seq, gb);
+            if (has_delta<VAR>()) scal[3] = load_elem(a.beta, seq, gb);
         }
     }
 
@@ -113,22 +118,22 @@ __global__ __launch_bounds__(decode_threads(DK, DV, decode_nthreads<VAR>())) voi
     for (int r = 0; r < RPT; ++r) {
         const int i = rg + RG * r;
         float wq = sq[i];
-        if (VAR == LA_GLA) wq *= sw[i];
+        if (has_channel_gate<VAR>()) wq *= sw[i];
         rr.x += s[r].x * wq; rr.y += s[r].y * wq; rr.z += s[r].z * wq; rr.w += s[r].w * wq;
-        if (VAR == LA_GDN) {
-            const float ki = sk[i];
+        if (has_delta<VAR>()) {
+            const float ki = VAR == LA_KDA ? sk[i] * sw[i] : sk[i];
             pr.x += s[r].x * ki; pr.y += s[r].y * ki; pr.z += s[r].z * ki; pr.w += s[r].w * ki;
         }
     }
     red[0][rg][cg] = rr;
-    if (VAR == LA_GDN) red[1][rg][cg] = pr;
+    if (has_delta<VAR>()) red[1][rg][cg] = pr;
     __syncthreads();
     float4 R = make_float4(0.f, 0.f, 0.f, 0.f), P = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 8
     for (int x = 0; x < RG; ++x) {
         const float4 t = red[0][x][cg];
         R.x += t.x; R.y += t.y; R.z += t.z; R.w += t.w;
-        if (VAR == LA_GDN) {
+        if (has_delta<VAR>()) {
             const float4 t2 = red[1][x][cg];
             P.x += t2.x; P.y += t2.y; P.z += t2.z; P.w += t2.w;
         }
@@ -136,7 +141,23 @@ __global__ __launch_bounds__(decode_threads(DK, DV, decode_nthreads<VAR>())) voi
     const float qk = scal[0];
     const float4 v4 = make_float4(sv[cg * 4], sv[cg * 4 + 1], sv[cg * 4 + 2], sv[cg * 4 + 3]);
     float4 o4;
-    if (VAR == LA_GDN) {
+    if (VAR == LA_KDA) {
+        const float be = scal[3];
+        float4 u;
+        u.x = be * (v4.x - P.x); u.y = be * (v4.y - P.y);
+        u.z = be * (v4.z - P.z); u.w = be * (v4.w - P.w);
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int i = rg + RG * r;
+            const float ki = sk[i], ai = sw[i];
+            float4 n;
+            n.x = ai * s[r].x + ki * u.x; n.y = ai * s[r].y + ki * u.y;
+            n.z = ai * s[r].z + ki * u.z; n.w = ai * s[r].w + ki * u.w;
+            store_nt4(S + size_t(i) * DV + cg * 4, n);
+        }
+        o4.x = R.x + qk * u.x; o4.y = R.y + qk * u.y;
+        o4.z = R.z + qk * u.z; o4.w = R.w + qk * u.w;
+    } else if (VAR == LA_GDN) {
         const float al = scal[2], be = scal[3];
         float4 u;
         u.x = be * (v4.x - al * P.x); u.y = be * (v4.y - al * P.y);
@@ -217,6 +238,7 @@ hipError_t launch_decode(const Problem& p) {
         case LA_KATH: return dispatch_dk<LA_KATH>(p, a);
         case LA_GLA: return dispatch_dk<LA_GLA>(p, a);
         case LA_GDN: return dispatch_dk<LA_GDN>(p, a);
+        case LA_KDA: return dispatch_dk<LA_KDA>(p, a);
     }
     return hipErrorInvalidValue;
 }

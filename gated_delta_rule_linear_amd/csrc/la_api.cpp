@@ -48,9 +48,10 @@ bool check_alignment(const la_desc& d, const void* q, const void* k, const void*
     for (const void* ptr : vec)
         if (ptr && !aligned(ptr, 16)) return false;
     const uintptr_t gsz = d.gate_dtype == LA_BF16 ? 2 : 4;
-    if (d.variant == LA_GLA && g && !aligned(g, 16)) return false;
+    if ((d.variant == LA_GLA || d.variant == LA_KDA) && g && !aligned(g, 16)) return false;
     if (d.variant == LA_GDN && ((g && !aligned(g, gsz)) || (beta && !aligned(beta, gsz))))
         return false;
+    if (d.variant == LA_KDA && beta && !aligned(beta, gsz)) return false;
     return true;
 }
 
@@ -66,8 +67,10 @@ Sizes sizes_of(const la_desc& d) {
     const uint64_t seq = mul(uint64_t(d.B), uint64_t(d.H));
     s.q = s.k = mul(mul(tok, d.dk), isz);
     s.v = s.o = mul(mul(tok, d.dv), isz);
-    s.g = d.variant == LA_GLA ? mul(mul(tok, d.dk), gsz) : d.variant == LA_GDN ? mul(tok, gsz) : 0;
-    s.beta = d.variant == LA_GDN ? mul(tok, gsz) : 0;
+    s.g = (d.variant == LA_GLA || d.variant == LA_KDA) ? mul(mul(tok, d.dk), gsz)
+          : d.variant == LA_GDN                         ? mul(tok, gsz)
+                                                        : 0;
+    s.beta = (d.variant == LA_GDN || d.variant == LA_KDA) ? mul(tok, gsz) : 0;
     s.S = mul(mul(mul(seq, d.dk), d.dv), 4);
     s.z = d.variant == LA_KATH ? mul(mul(seq, d.dk), 4) : 0;
     return s;
@@ -76,7 +79,7 @@ Sizes sizes_of(const la_desc& d) {
 // Descriptor checks shared by prefill, decode and the workspace query.
 int check_desc(const la_desc* d, bool decode) {
     if (!d) return LA_ERR_INVALID;
-    if (d->variant < LA_KATH || d->variant > LA_GDN) return LA_ERR_INVALID;
+    if (d->variant < LA_KATH || d->variant > LA_KDA) return LA_ERR_INVALID;
     if (d->io_dtype != LA_F32 && d->io_dtype != LA_BF16) return LA_ERR_INVALID;
     if (d->variant != LA_KATH && d->gate_dtype != LA_F32 && d->gate_dtype != LA_BF16)
         return LA_ERR_INVALID;
@@ -101,6 +104,7 @@ int plan_prefill(const la_desc& d, Problem& p) {
     p.gate_bf16 = d.gate_dtype == LA_BF16;
     p.eps = d.eps;
     const bool mfma_ok = d.variant == LA_GDN   ? la::gdn_mfma_supported(d.dk, d.dv, p.io_bf16)
+                         : d.variant == LA_KDA ? la::kda_mfma_supported(d.dk, d.dv, p.io_bf16)
                          : d.variant == LA_GLA ? la::gla_mfma_supported(d.dk, d.dv, p.io_bf16)
                                                : la::kath_mfma_supported(d.dk, d.dv, p.io_bf16);
     int path = d.path;
@@ -110,7 +114,7 @@ int plan_prefill(const la_desc& d, Problem& p) {
     p.chunk = path == LA_PATH_MFMA ? la::kMfmaChunk : la::kValuChunk;
     if (d.chunk != 0 && d.chunk != p.chunk) return LA_ERR_UNSUPPORTED;
     p.segments = 1;
-    if (path == LA_PATH_MFMA && d.variant != LA_GDN && d.N > 0) {
+    if (path == LA_PATH_MFMA && (d.variant == LA_KATH || d.variant == LA_GLA) && d.N > 0) {
         const int nchunks = (d.N + p.chunk - 1) / p.chunk;
         int segs = d.segments > 0                 ? d.segments
                    : d.variant == LA_GLA ? la::gla_mfma_auto_segments(p)
@@ -128,6 +132,7 @@ size_t workspace_for(const Problem& p) {
     if (p.N == 0 || p.B == 0 || p.H == 0) return 0;
     if (p.path == LA_PATH_MFMA)
         return p.variant == LA_GDN   ? la::gdn_mfma_workspace_bytes(p)
+               : p.variant == LA_KDA ? la::kda_mfma_workspace_bytes(p)
                : p.variant == LA_GLA ? la::gla_mfma_workspace_bytes(p)
                                      : la::kath_mfma_workspace_bytes(p);
     return 0;
@@ -170,7 +175,7 @@ int la_prefill(const la_desc* d, const void* q, const void* k, const void* v, co
     rc = plan_prefill(*d, p);
     if (rc != LA_OK) return rc;
     const bool kath = d->variant == LA_KATH, gla = d->variant == LA_GLA,
-               gdn = d->variant == LA_GDN;
+               gdn = d->variant == LA_GDN, kda = d->variant == LA_KDA;
     const bool empty_seq = (uint64_t(d->B) * uint64_t(d->H)) == 0;
     const bool tokens = !empty_seq && d->N > 0;
     // presence rules
@@ -183,8 +188,8 @@ int la_prefill(const la_desc* d, const void* q, const void* k, const void* v, co
     }
     if (tokens) {
         if (!q || !k || !v || !o) return LA_ERR_INVALID;
-        if ((gla || gdn) && !g) return LA_ERR_INVALID;
-        if (gdn && !beta) return LA_ERR_INVALID;
+        if ((gla || gdn || kda) && !g) return LA_ERR_INVALID;
+        if ((gdn || kda) && !beta) return LA_ERR_INVALID;
     }
     // alignment: 16 bytes for the arrays read or written with 128-bit accesses; the
     // per-token scalar gates of GDN (alpha, beta) only need element alignment
@@ -232,6 +237,7 @@ int la_prefill(const la_desc* d, const void* q, const void* k, const void* v, co
         err = la::launch_state_init(p);
     else if (p.path == LA_PATH_MFMA)
         err = gdn                     ? la::launch_prefill_gdn_mfma(p)
+              : kda                   ? la::launch_prefill_kda_mfma(p)
               : p.variant == LA_GLA ? la::launch_prefill_gla_mfma(p)
                                     : la::launch_prefill_kath_mfma(p);
     else
@@ -245,15 +251,15 @@ int la_decode_step(const la_desc* d, const void* q, const void* k, const void* v
     int rc = check_desc(d, true);
     if (rc != LA_OK) return rc;
     const bool kath = d->variant == LA_KATH, gla = d->variant == LA_GLA,
-               gdn = d->variant == LA_GDN;
+               gdn = d->variant == LA_GDN, kda = d->variant == LA_KDA;
     if (kath && (g || beta)) return LA_ERR_INVALID;
     if (gla && beta) return LA_ERR_INVALID;
     if (!kath && z) return LA_ERR_INVALID;
     const bool empty_seq = (uint64_t(d->B) * uint64_t(d->H)) == 0;
     if (!empty_seq) {
         if (!q || !k || !v || !o || !S) return LA_ERR_INVALID;
-        if ((gla || gdn) && !g) return LA_ERR_INVALID;
-        if (gdn && !beta) return LA_ERR_INVALID;
+        if ((gla || gdn || kda) && !g) return LA_ERR_INVALID;
+        if ((gdn || kda) && !beta) return LA_ERR_INVALID;
         if (kath && !z) return LA_ERR_INVALID;
     }
     if (!check_alignment(*d, q, k, v, g, beta, nullptr, nullptr, o, S, z)) return LA_ERR_INVALID;

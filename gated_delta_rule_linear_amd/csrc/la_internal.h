@@ -43,6 +43,10 @@ bool kath_mfma_supported(int dk, int dv, bool io_bf16);
 size_t kath_mfma_workspace_bytes(const Problem& p);
 int kath_mfma_auto_segments(const Problem& p);
 hipError_t launch_prefill_kath_mfma(const Problem& p);
+// prefill_kda_mfma.hip (KDA)
+bool kda_mfma_supported(int dk, int dv, bool io_bf16);
+size_t kda_mfma_workspace_bytes(const Problem& p);
+hipError_t launch_prefill_kda_mfma(const Problem& p);
 // prefill_gla_mfma.hip (GLA)
 bool gla_mfma_supported(int dk, int dv, bool io_bf16);
 size_t gla_mfma_workspace_bytes(const Problem& p);

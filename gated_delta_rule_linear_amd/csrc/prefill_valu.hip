@@ -22,6 +22,12 @@
 //        (I + L) U = X,  X_r = beta_r (v_r - gamma_r S^T k_r)     [forward substitution]
 //        o_r  = gamma_r S^T q_r + sum_{s<=r} exp(c_r - c_s) (q_r.k_s) u_s
 //        S    = gamma_last S + sum_s exp(c_last - c_s) k_s u_s^T
+//  KDA   B_r  = sum_{s<=r} log alpha_s (per key dim), the delta rule of GDN with the
+//        decay inside the products:
+//        L_rs = beta_r sum_i k_ri k_si exp(B_ri - B_si) (s < r)
+//        (I + L) U = X,  X_r = beta_r (v_r - S^T (k_r * exp(B_r)))
+//        o_r  = S^T (q_r * exp(B_r)) + sum_{s<=r} P_rs u_s,  P as for GLA
+//        S    = diag(exp(B_last)) S + sum_s diag(exp(B_last - B_s)) k_s u_s^T
 // These are exact rewrites of the token recurrences (the state after token r of
 // the chunk, unrolled back to the chunk start). Padding tokens past N are
 // identity steps: zero key and value, gate 1, beta 0.
@@ -48,10 +54,12 @@ struct ValuArgs {
 template <int VAR, int DK, int DV>
 __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
     constexpr int DKP = DK + 1;  // padded row pitch
+    constexpr bool CHG = VAR == LA_GLA || VAR == LA_KDA;   // gate per key dim
+    constexpr bool DLT = VAR == LA_GDN || VAR == LA_KDA;   // delta rule
     __shared__ float sS[DK][VT];
     __shared__ float sz[DK];
     __shared__ float sQ[C][DKP], sK[C][DKP];
-    __shared__ float sLg[VAR == LA_GLA ? C : 1][VAR == LA_GLA ? DKP : 1];
+    __shared__ float sLg[CHG ? C : 1][CHG ? DKP : 1];
     __shared__ float sV[C][VT];
     __shared__ float sP[C][C + 1], sL[C][C + 1];
     __shared__ float sX[C][VT], sU[C][VT];
@@ -89,24 +97,24 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
                     qv = elu_plus_one(qv);
                     kv = elu_plus_one(kv);
                 }
-                if (VAR == LA_GLA) lg = logf(load_elem(a.g, e, gb));
+                if (CHG) lg = logf(load_elem(a.g, e, gb));
             }
             sQ[r][i] = qv;
             sK[r][i] = kv;
-            if (VAR == LA_GLA) sLg[r][i] = lg;
+            if (CHG) sLg[r][i] = lg;
         }
         {
             const int r = r_me, c = c_me;
             sV[r][c] = r < n ? load_elem(a.v, (tok0 + t0 + r) * DV + c0 + c, iob) : 0.f;
         }
-        if (VAR == LA_GDN && tid < C) {
+        if (DLT && tid < C) {
             const int r = tid;
-            sc[r] = r < n ? logf(load_elem(a.g, tok0 + t0 + r, gb)) : 0.f;
+            if (VAR == LA_GDN) sc[r] = r < n ? logf(load_elem(a.g, tok0 + t0 + r, gb)) : 0.f;
             sbeta[r] = r < n ? load_elem(a.beta, tok0 + t0 + r, gb) : 0.f;
         }
         __syncthreads();
         // in-chunk cumulative log gates
-        if (VAR == LA_GLA) {
+        if (CHG) {
             for (int i = tid; i < DK; i += NT) {
                 float acc = 0.f;
                 for (int r = 0; r < C; ++r) {
@@ -128,10 +136,14 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
             const int r = tid / C, s = tid % C;
             float p = 0.f, l = 0.f;
             if (s <= r) {
-                if (VAR == LA_GLA) {
+                if (CHG) {
                     for (int i = 0; i < DK; ++i) p += sQ[r][i] * sK[s][i] * expf(sLg[r][i] - sLg[s][i]);
                 } else {
                     for (int i = 0; i < DK; ++i) p += sQ[r][i] * sK[s][i];
+                }
+                if (VAR == LA_KDA && s < r) {
+                    for (int i = 0; i < DK; ++i) l += sK[r][i] * sK[s][i] * expf(sLg[r][i] - sLg[s][i]);
+                    l *= sbeta[r];
                 }
                 if (VAR == LA_GDN) {
                     const float d = expf(sc[r] - sc[s]);
@@ -143,7 +155,7 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
                 }
             }
             sP[r][s] = p;
-            if (VAR == LA_GDN) sL[r][s] = l;
+            if (DLT) sL[r][s] = l;
         }
         if (VAR == LA_KATH && tid < C) {
             float d = 0.f;
@@ -156,8 +168,14 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
             for (int i = 0; i < DK; ++i) ks += sK[r][i] * sS[i][c];
             sX[r][c] = sbeta[r] * (sV[r][c] - expf(sc[r]) * ks);
         }
+        if (VAR == LA_KDA) {
+            const int r = r_me, c = c_me;
+            float ks = 0.f;
+            for (int i = 0; i < DK; ++i) ks += sK[r][i] * expf(sLg[r][i]) * sS[i][c];
+            sX[r][c] = sbeta[r] * (sV[r][c] - ks);
+        }
         __syncthreads();
-        if (VAR == LA_GDN) {
+        if (DLT) {
             // forward substitution (I + L) U = X, one thread per column
             if (tid < VT) {
                 const int c = tid;
@@ -173,7 +191,7 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
         {
             const int r = r_me, c = c_me;
             float acc = 0.f;
-            if (VAR == LA_GLA) {
+            if (CHG) {
                 for (int i = 0; i < DK; ++i) acc += sQ[r][i] * expf(sLg[r][i]) * sS[i][c];
             } else {
                 for (int i = 0; i < DK; ++i) acc += sQ[r][i] * sS[i][c];
@@ -182,7 +200,7 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
             float intra = 0.f, psum = 0.f;
             for (int s = 0; s <= r; ++s) {
                 const float p = sP[r][s];
-                intra += p * (VAR == LA_GDN ? sU[s][c] : sV[s][c]);
+                intra += p * (DLT ? sU[s][c] : sV[s][c]);
                 psum += p;
             }
             float out = acc + intra;
@@ -197,6 +215,10 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
             if (VAR == LA_GLA) {
                 const float bl = sLg[C - 1][i];
                 for (int s = 0; s < C; ++s) acc += sK[s][i] * expf(bl - sLg[s][i]) * sV[s][c];
+                sS[i][c] = expf(bl) * sS[i][c] + acc;
+            } else if (VAR == LA_KDA) {
+                const float bl = sLg[C - 1][i];
+                for (int s = 0; s < C; ++s) acc += sK[s][i] * expf(bl - sLg[s][i]) * sU[s][c];
                 sS[i][c] = expf(bl) * sS[i][c] + acc;
             } else if (VAR == LA_GDN) {
                 const float cl = sc[C - 1];
@@ -272,6 +294,7 @@ hipError_t launch_prefill_valu(const Problem& p) {
         case LA_KATH: return dispatch_dk<LA_KATH>(p, a);
         case LA_GLA: return dispatch_dk<LA_GLA>(p, a);
         case LA_GDN: return dispatch_dk<LA_GDN>(p, a);
+        case LA_KDA: return dispatch_dk<LA_KDA>(p, a);
     }
     return hipErrorInvalidValue;
 }

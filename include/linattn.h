@@ -17,6 +17,10 @@
  *            symmetric): S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T, that is
  *              u_t = b_t (v_t - a_t S_{t-1}^T k_t),  S_t = a_t S_{t-1} + k_t u_t^T,
  *              o_t = S_t^T q_t
+ *   LA_KDA   Kimi Delta Attention ("状态空间与线性注意力", section KDA): a retention
+ *            per key channel decays the old state first, then the delta write reads
+ *            the decayed state:  Sbar = Diag(a_t) S_{t-1},
+ *              S_t = Sbar + b_t k_t (v_t - Sbar^T k_t)^T,   o_t = S_t^T q_t
  *
  * Every variant reads the state after the token's update. Prefill runs the
  * recurrence over N tokens with the chunkwise-parallel method (quadratic, causally
@@ -28,7 +32,8 @@
  *   q, k     [B, H, N, d_k]  io        v, o  [B, H, N, d_v]  io
  *   g        LA_GLA: [B, H, N, d_k] gate, values in (0, 1]
  *            LA_GDN: alpha [B, H, N] gate, values in (0, 1]
- *   beta     LA_GDN: [B, H, N] gate, values in [0, 1]
+ *            LA_KDA: alpha [B, H, N, d_k] gate (retention per key channel), in (0, 1]
+ *   beta     LA_GDN, LA_KDA: [B, H, N] gate, values in [0, 1]
  *   S0, S    [B, H, d_k, d_v] fp32 (key-major)
  *   z0, z    [B, H, d_k] fp32 (LA_KATH only)
  * For decode N = 1 and the token arrays are [B, H, d] (respectively [B, H]).
@@ -61,7 +66,7 @@ enum {
     LA_OK = 0,
     LA_ERR_INVALID = 1,      /* null required pointer, bad enum, negative size, misaligned
                                 pointer (16 bytes for q, k, v, o, GLA g, S and z; element
-                                alignment for GDN alpha and beta; 256 bytes for the
+                                alignment for GDN alpha and GDN / KDA beta; 256 bytes for the
                                 workspace), overlap of an output with any other buffer,
                                 gate passed / missing for the variant, N != 1 for decode */
     LA_ERR_UNSUPPORTED = 2,  /* d_k or d_v not in {16, 32, 64, 128}, or a requested path /
@@ -71,7 +76,7 @@ enum {
 };
 
 /* variants */
-enum { LA_KATH = 0, LA_GLA = 1, LA_GDN = 2 };
+enum { LA_KATH = 0, LA_GLA = 1, LA_GDN = 2, LA_KDA = 3 };
 
 /* storage dtypes */
 enum { LA_F32 = 0, LA_BF16 = 1 };
@@ -81,13 +86,13 @@ enum {
     LA_PATH_AUTO = 0, /* bf16 MFMA kernels where the shape allows, else the fp32 VALU kernels */
     LA_PATH_VALU = 1, /* fp32 arithmetic on the vector ALUs (chunk 16) */
     LA_PATH_MFMA = 2  /* bf16 matrix cores with fp32 accumulation and fp32 state (chunk 64);
-                         needs d_k = 128 and d_v in {64, 128} */
+                         needs bf16 q / k / v and d_k = 128 */
 };
 
 typedef struct la_desc {
     int32_t B, H, N;      /* batch, heads, tokens per sequence (N = 1 for decode) */
     int32_t dk, dv;       /* key and value dims, each in {16, 32, 64, 128} */
-    int32_t variant;      /* LA_KATH | LA_GLA | LA_GDN */
+    int32_t variant;      /* LA_KATH | LA_GLA | LA_GDN | LA_KDA */
     int32_t io_dtype;     /* LA_F32 | LA_BF16: q, k, v, o */
     int32_t gate_dtype;   /* LA_F32 | LA_BF16: g / alpha, beta (ignored for LA_KATH) */
     float eps;            /* LA_KATH denominator epsilon, finite and >= 0 */
@@ -127,7 +132,8 @@ int la_prefill(const la_desc* d, const void* q, const void* k, const void* v,
  * the final recurrent state only, so the cost of a step does not depend on how many
  * tokens came before.
  *   d->N must be 1. q, k [B, H, d_k]; v [B, H, d_v]; g (GLA [B, H, d_k], GDN alpha
- *   [B, H]); beta (GDN [B, H]); S [B, H, d_k, d_v] fp32 read and overwritten;
+ *   [B, H], KDA alpha [B, H, d_k]); beta (GDN / KDA [B, H]); S [B, H, d_k, d_v] fp32
+ *   read and overwritten;
  *   z [B, H, d_k] fp32 read and overwritten (LA_KATH, NULL otherwise);
  *   o [B, H, d_v] io written. o must not overlap S, z or any input. */
 int la_decode_step(const la_desc* d, const void* q, const void* k, const void* v,

@@ -73,9 +73,9 @@ def good(variant="gla", **kw):
 
 def ptrs(variant):
     p = dict(q=addr(0), k=addr(1), v=addr(2), o=addr(7), S=addr(8))
-    if variant in ("gla", "gdn"):
+    if variant in ("gla", "gdn", "kda"):
         p["g"] = addr(3)
-    if variant == "gdn":
+    if variant in ("gdn", "kda"):
         p["beta"] = addr(4)
     if variant == "kath":
         p["z"] = addr(9)
@@ -103,13 +103,17 @@ def ptrs(variant):
     ("gla_missing_gate", bd.LA_ERR_INVALID),
     ("gla_with_beta", bd.LA_ERR_INVALID),
     ("gdn_missing_beta", bd.LA_ERR_INVALID),
+    ("kda_missing_beta", bd.LA_ERR_INVALID),
+    ("kda_missing_gate", bd.LA_ERR_INVALID),
+    ("misaligned_kda_gate", bd.LA_ERR_INVALID),
     ("kath_with_gate", bd.LA_ERR_INVALID),
     ("kath_missing_z", bd.LA_ERR_INVALID),
     ("gla_with_z", bd.LA_ERR_INVALID),
 ])
 def test_prefill_rejects(lib, case, expect):
-    variant = {"gdn_missing_beta": "gdn", "kath_with_gate": "kath", "kath_missing_z": "kath"}.get(
-        case, "gla")
+    variant = {"gdn_missing_beta": "gdn", "kath_with_gate": "kath", "kath_missing_z": "kath",
+               "kda_missing_beta": "kda", "kda_missing_gate": "kda",
+               "misaligned_kda_gate": "kda"}.get(case, "gla")
     d = good(variant)
     p = ptrs(variant)
     if case == "null_desc":
@@ -152,8 +156,12 @@ def test_prefill_rejects(lib, case, expect):
         p.pop("g")
     elif case == "gla_with_beta":
         p["beta"] = addr(4)
-    elif case == "gdn_missing_beta":
+    elif case in ("gdn_missing_beta", "kda_missing_beta"):
         p.pop("beta")
+    elif case == "kda_missing_gate":
+        p.pop("g")
+    elif case == "misaligned_kda_gate":
+        p["g"] = addr(3, 2)
     elif case == "kath_with_gate":
         p["g"] = addr(3)
     elif case == "kath_missing_z":

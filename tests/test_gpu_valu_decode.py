@@ -42,27 +42,29 @@ def test_config_kath_f32_n256_d16():
 SHAPES = [(16, 16), (32, 64), (64, 32), (128, 128), (128, 64)]
 
 
-@pytest.mark.parametrize("variant", ["kath", "gla", "gdn"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", SHAPES)
 def test_valu_prefill_shapes(variant, io, dk, dv):
     wl = W.Workload("t", variant, 2, 2, 37, dk, dv, io, io, seed=dk * 7 + dv,
                     qk_scale=(1.0 if variant == "kath" else dk ** -0.5),
-                    l2norm_qk=(variant == "gdn"))
+                    l2norm_qk=(variant in ("gdn", "kda")))
     run_prefill_case(wl)
 
 
-@pytest.mark.parametrize("variant", ["kath", "gla", "gdn"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda"])
 @pytest.mark.parametrize("N", [1, 15, 16, 17, 64, 129])
 def test_valu_prefill_lengths(variant, N):
     wl = W.Workload("t", variant, 1, 3, N, 32, 16, "f32", "f32", seed=N,
-                    l2norm_qk=(variant == "gdn"), gate_kind="slow" if variant != "kath" else "default")
+                    l2norm_qk=(variant in ("gdn", "kda")),
+                    gate_kind="slow" if variant != "kath" else "default")
     run_prefill_case(wl)
 
 
-@pytest.mark.parametrize("kind", ["ones", "beta0", "beta1", "slow"])
-def test_valu_gdn_gate_kinds(kind):
-    wl = W.Workload("t", "gdn", 1, 2, 80, 64, 32, "f32", "f32", seed=3, l2norm_qk=True,
+@pytest.mark.parametrize("variant", ["gdn", "kda"])
+@pytest.mark.parametrize("kind", ["default", "ones", "beta0", "beta1", "slow"])
+def test_valu_delta_gate_kinds(variant, kind):
+    wl = W.Workload("t", variant, 1, 2, 80, 64, 32, "f32", "f32", seed=3, l2norm_qk=True,
                     gate_kind=kind)
     run_prefill_case(wl)
 
@@ -123,7 +125,7 @@ def test_valu_split_carry_matches_whole():
 def decode_case(variant, io, B, H, dk, dv, seed=0, steps=1, gate_kind="default"):
     wl = W.Workload("dec", variant, B, H, 1, dk, dv, io, io, seed=seed, decode=True,
                     qk_scale=(1.0 if variant == "kath" else dk ** -0.5),
-                    l2norm_qk=(variant == "gdn"), gate_kind=gate_kind)
+                    l2norm_qk=(variant in ("gdn", "kda")), gate_kind=gate_kind)
     rng = np.random.default_rng(seed + 100)
     S64 = (rng.standard_normal((B, H, dk, dv)) * 0.5).astype(np.float32).astype(np.float64)
     z64 = (np.abs(rng.standard_normal((B, H, dk))) + 1.0).astype(np.float32).astype(np.float64)
@@ -149,7 +151,7 @@ def decode_case(variant, io, B, H, dk, dv, seed=0, steps=1, gate_kind="default")
     return errs
 
 
-@pytest.mark.parametrize("variant", ["kath", "gla", "gdn"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 128), (128, 16), (64, 64), (128, 128)])
 def test_decode_shapes(variant, io, dk, dv):
@@ -158,7 +160,7 @@ def test_decode_shapes(variant, io, dk, dv):
         assert eo <= TOL[io] and eS <= 1e-5, errs
 
 
-@pytest.mark.parametrize("variant", ["gdn", "gla"])
+@pytest.mark.parametrize("variant", ["gdn", "gla", "kda"])
 def test_decode_many_steps(variant):
     errs = decode_case(variant, "bf16", 4, 8, 128, 128, seed=5, steps=40, gate_kind="default")
     eo, eS = errs[-1]
