@@ -35,9 +35,10 @@ PEAK_BF16_TFLOPS = 2516.6    # dense bf16 MFMA, 256 CU x 4096 flop/clk x 2.4 GHz
 PROFILES = os.path.join(ROOT, "profiles")
 # the kernels one prefill step launches, per variant (the roofline covers the whole step)
 STEP_KERNELS = {
-    "gla": "gla_prep_kernel + gla_chain_kernel (summary) + gla_scan_kernel + gla_chain_kernel",
+    "gla": "gla_prep_kernel + gla_chain_kernel (summary) + gla_chain_kernel (forward)",
     "kath": "kath_chain_kernel (summary) + kath_scan_kernel + kath_chain_kernel",
     "gdn": "gdn_prep_kernel + gdn_fwd_kernel",
+    "kda": "kda_prep_kernel + kda_fwd_kernel",
 }
 
 
@@ -326,13 +327,13 @@ def main():
 
     if not args.no_extras and not args.only:
         for name in ("gdn_bf16_b4h16_n8192_d128", "kath_bf16_b1h16_n32768_dk128_dv64",
-                     "kath_f32_n256_d16"):
+                     "kath_f32_n256_d16", "kda_bf16_b4h16_n8192_d128"):
             r, c = bench_prefill(name, max(20, args.steps // 8), 5, 2, torch, bd, W, device,
                                  stream, graph=use_graph)
             results[name] = r
             del c
             torch.cuda.empty_cache()
-        for name in ("decode_gdn_256x32_d128", "decode_gla_256x32_d128"):
+        for name in ("decode_gdn_256x32_d128", "decode_gla_256x32_d128", "decode_kda_256x32_d128"):
             results[name] = bench_decode(name, 1000, 10, torch, bd, W, device, stream)
             torch.cuda.empty_cache()
 

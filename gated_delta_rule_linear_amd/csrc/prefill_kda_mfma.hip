@@ -39,8 +39,8 @@ constexpr int C = kMfmaChunk;  // 64
 constexpr int NTP = 512;       // prep: 8 waves
 constexpr int NTF = 256;       // forward: 4 waves
 constexpr int PQ = DK + 8;     // pitch of [*][128] bf16 tiles
-constexpr int PC = C + 8;      // pitch of [*][64] bf16 tiles
-constexpr int PD = 16 + 4;     // pitch of the fp32 16 x 16 diagonal L blocks
+constexpr int PC = C + 8;      // pitch of [*][64] bf16 tiles (rows 16-byte aligned)
+constexpr int PD = 16;         // pitch of the fp32 16 x 16 diagonal L blocks
 constexpr int PY = 32 + 8;     // pitch of the bf16 32-row scratch tiles
 constexpr float kGateMin = 4.539993e-05f;   // exp(-10)
 
@@ -88,19 +88,26 @@ __device__ __forceinline__ bf16x8_t k16(bf16x8_t f, int lane) {
 // every factor: lower group G_rho / G_r = ss_r, upper group G_r / G_rho = pp_r (each in
 // [e^-80, 1]), the other of the pair one reciprocal; G_r = Pre pp_r and G_last / G_r =
 // ss_r Suf with Pre / Suf the products of the groups before / after.
+// 80 KiB, so that two workgroups share a CU: the off-diagonal key fragments are
+// rescaled as they are read (from the per-pair factor table fe) instead of being stored
+// as copies, and the inverse's scratch reuses q~, which is dead by then.
 struct __align__(16) PrepSmem {
-    __align__(16) uint16_t qo[C * PQ];      // q~ (own row block's reference)
+    union {
+        __align__(16) uint16_t qo[C * PQ];  // q~ (own row block's reference)
+        struct {
+            __align__(16) uint16_t ya[2][32 * PY];  // level-a scratch (rows 0..15 used)
+            __align__(16) uint16_t yb[32 * PY];     // level-b scratch
+        } y;
+    } u;
     __align__(16) uint16_t ko[C * PQ];      // k- side: k_s G_rho / G_s
     __align__(16) uint16_t kr[C * PQ];      // k~ row side: k_r G_r / G_rho
-    __align__(16) uint16_t pc[6][16 * PQ];  // key side rescaled to a later block's reference
     __align__(16) uint16_t t[C * PC];       // T [r][s]
     __align__(16) uint16_t lo[C * PC];      // off-diagonal blocks of L [r][s]
-    __align__(16) uint16_t ya[2][32 * PY];  // level-a scratch (16 rows used)
-    __align__(16) uint16_t yb[32 * PY];     // level-b scratch
     __align__(16) float ld[4][16 * PD];     // diagonal blocks of L, fp32
     __align__(16) float T[8][DK];           // retention product of each 8-row group
-    float beta[C];
+    __align__(16) float fe[6][DK];          // G_rho_rb / G_rho_sb per key, pair (sb, rb)
 };
+static_assert(sizeof(PrepSmem) <= 80 * 1024, "two prep workgroups per CU");
 
 template <bool GB>
 __global__ __launch_bounds__(NTP) void kda_prep_kernel(KdaArgs a) {
@@ -140,19 +147,21 @@ __global__ __launch_bounds__(NTP) void kda_prep_kernel(KdaArgs a) {
             gv[2 * r + 1] = x.y;
         }
     }
-    if (w == 7) sm.beta[lane] = gate_val<GB>(buf_ld_gate<GB>(rb_, uint32_t(lane)));   // 0 past the end
+    // beta of rows 16 bb + jl, for the waves that form L (zero past the end)
+    float bet[4] = {0.f, 0.f, 0.f, 0.f};
+    if (w < 4) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) bet[bb] = gate_val<GB>(buf_ld_gate<GB>(rb_, uint32_t(16 * bb + jl)));
+    }
     if (w >= 4) {
-        // zero the six upper blocks of T and the level-a scratch
+        // zero the six upper blocks of T (the level-a scratch needs none: its rows 16..31
+        // only reach lanes whose fragment is replaced by zeros)
         const int x = w - 4;
         const int ub[6][2] = {{0, 1}, {0, 2}, {0, 3}, {1, 2}, {1, 3}, {2, 3}};
         const int r = lane >> 2, cc = (lane & 3) * 4;
         for (int y = x; y < 6; y += 4)
             *reinterpret_cast<uint2*>(sm.t + (16 * ub[y][0] + r) * PC + 16 * ub[y][1] + cc) =
                 make_uint2(0, 0);
-        if (x < 2) {
-            uint16_t* y = sm.ya[x];
-            for (int z = lane; z < 32 * PY / 4; z += 64) *reinterpret_cast<uint2*>(y + 4 * z) = make_uint2(0, 0);
-        }
     }
     float pp[8][2], ss[8][2];
     {
@@ -191,8 +200,8 @@ __global__ __launch_bounds__(NTP) void kda_prep_kernel(KdaArgs a) {
         Tv[hh][0] = t.x;
         Tv[hh][1] = t.y;
     }
-    // products of the groups before / after this one; fe[o] = G_rho_o / G_rho_b (o > b)
-    float pre[2], suf[2], fe[4][2];
+    // products of the groups before / after this one
+    float pre[2], suf[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         pre[c] = 1.f;
@@ -202,14 +211,21 @@ __global__ __launch_bounds__(NTP) void kda_prep_kernel(KdaArgs a) {
             if (hh < rg) pre[c] *= Tv[hh][c];
             if (hh > rg) suf[c] *= Tv[hh][c];
         }
-        float run = 1.f;
+    }
+    if (rg == 1) {
+        // pair factors G_rho_rb / G_rho_sb = product of groups 2 sb + 1 .. 2 rb
 #pragma unroll
-        for (int o = 1; o < 4; ++o) {
-            if (o > b) {
-                if (2 * o - 1 > 2 * b) run *= Tv[2 * o - 1][c];
-                run *= Tv[2 * o][c];
+        for (int sb = 0; sb < 3; ++sb) {
+            float run[2] = {1.f, 1.f};
+#pragma unroll
+            for (int rb = sb + 1; rb < 4; ++rb) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    if (2 * rb - 1 > 2 * sb) run[c] *= Tv[2 * rb - 1][c];
+                    run[c] *= Tv[2 * rb][c];
+                }
+                *reinterpret_cast<float2*>(&sm.fe[pair_index(sb, rb)][col]) = make_float2(run[0], run[1]);
             }
-            fe[o][c] = run;
         }
     }
     unsigned char* wsc = a.ws + (seq * a.nchunks + ch) * size_t(kWsChunk);
@@ -230,14 +246,9 @@ __global__ __launch_bounds__(NTP) void kda_prep_kernel(KdaArgs a) {
             e0 = __builtin_amdgcn_rcpf(i0); e1 = __builtin_amdgcn_rcpf(i1);
         }
         const float kt0 = k0 * i0, kt1 = k1 * i1;
-        *reinterpret_cast<uint32_t*>(sm.qo + rr * PQ + col) = pack_bf16x2(q0 * e0, q1 * e1);
+        *reinterpret_cast<uint32_t*>(sm.u.qo + rr * PQ + col) = pack_bf16x2(q0 * e0, q1 * e1);
         *reinterpret_cast<uint32_t*>(sm.kr + rr * PQ + col) = pack_bf16x2(k0 * e0, k1 * e1);
         *reinterpret_cast<uint32_t*>(sm.ko + rr * PQ + col) = pack_bf16x2(kt0, kt1);
-#pragma unroll
-        for (int o = 1; o < 4; ++o)
-            if (o > b)
-                *reinterpret_cast<uint32_t*>(sm.pc[pair_index(b, o)] + pr * PQ + col) =
-                    pack_bf16x2(kt0 * fe[o][0], kt1 * fe[o][1]);
         // Q~ and K~ in fragment order: row rr, columns col, col + 1 are a quarter piece
         const int kk = col >> 5, gg = (col & 31) >> 3;
         const uint32_t piece = (((rr >> 4) * 4 + kk) * 64 + 16 * gg + pr) * 16 + (col & 7) * 2;
@@ -259,12 +270,19 @@ __global__ __launch_bounds__(NTP) void kda_prep_kernel(KdaArgs a) {
     }
     lds_barrier();
 
-    // key-side operand of tile (rb, sb): the own-reference k- rows, or their copy rescaled
-    // to row block rb's reference
-    auto key_side = [&](int rb, int sb, int& row0) -> const uint16_t* {
-        if (sb == rb) { row0 = 16 * rb; return sm.ko; }
-        row0 = 0;
-        return sm.pc[pair_index(sb, rb)];
+    // key-side fragment of tile (rb, sb), keys 32 kk ..: the own-reference k- rows of
+    // block sb, rescaled to row block rb's reference for sb < rb (a factor <= 1)
+    auto key_frag = [&](int rb, int sb, int kk) -> bf16x8_t {
+        const bf16x8_t f = frag_kc(sm.ko, PQ, 16 * sb, 32 * kk, lane);
+        if (sb == rb) return f;
+        const float* fp = sm.fe[pair_index(sb, rb)] + 32 * kk + 8 * g;
+        const float4 f0 = *reinterpret_cast<const float4*>(fp);
+        const float4 f1 = *reinterpret_cast<const float4*>(fp + 4);
+        float x[8];
+        unpack8(__builtin_bit_cast(uint4, f), x);
+        x[0] *= f0.x; x[1] *= f0.y; x[2] *= f0.z; x[3] *= f0.w;
+        x[4] *= f1.x; x[5] *= f1.y; x[6] *= f1.z; x[7] *= f1.w;
+        return __builtin_bit_cast(bf16x8_t, pack8(x));
     };
     if (w == 0) {
         // diagonal blocks of L (fp32): D'[s][r] = beta_r sum_i k-_si k~_ri, s < r
@@ -276,7 +294,7 @@ __global__ __launch_bounds__(NTP) void kda_prep_kernel(KdaArgs a) {
                 d = mfma16(frag_kc(sm.ko, PQ, 16 * bb, 32 * kk, lane),
                            frag_kc(sm.kr, PQ, 16 * bb, 32 * kk, lane), d);
             const int r = 16 * bb + jl;
-            const float br = sm.beta[r];
+            const float br = bet[bb];
             float4 val;
             float* vv = reinterpret_cast<float*>(&val);
 #pragma unroll
@@ -313,13 +331,11 @@ __global__ __launch_bounds__(NTP) void kda_prep_kernel(KdaArgs a) {
         for (int task = w - 1; task < 6; task += 3) {
             const int rb = task < 1 ? 1 : task < 3 ? 2 : 3;
             const int sb = task - (rb * (rb - 1)) / 2;
-            int ar;
-            const uint16_t* At = key_side(rb, sb, ar);
             f32x4_t d = zero4();
 #pragma unroll
             for (int kk = 0; kk < DK / 32; ++kk)
-                d = mfma16(frag_kc(At, PQ, ar, 32 * kk, lane), frag_kc(sm.kr, PQ, 16 * rb, 32 * kk, lane), d);
-            const float br = sm.beta[16 * rb + jl];
+                d = mfma16(key_frag(rb, sb, kk), frag_kc(sm.kr, PQ, 16 * rb, 32 * kk, lane), d);
+            const float br = rb == 1 ? bet[1] : rb == 2 ? bet[2] : bet[3];
             store_dT(sm.lo, PC, 16 * sb, 16 * rb, d * br, lane);
         }
     } else {
@@ -329,12 +345,10 @@ __global__ __launch_bounds__(NTP) void kda_prep_kernel(KdaArgs a) {
         for (int ti = w - 4; ti < 10; ti += 4) {
             const int rb = ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3;
             const int sb = ti - (rb * (rb + 1)) / 2;
-            int ar;
-            const uint16_t* At = key_side(rb, sb, ar);
             f32x4_t acc = zero4();
 #pragma unroll
             for (int kk = 0; kk < DK / 32; ++kk)
-                acc = mfma16(frag_kc(At, PQ, ar, 32 * kk, lane), frag_kc(sm.qo, PQ, 16 * rb, 32 * kk, lane), acc);
+                acc = mfma16(key_frag(rb, sb, kk), frag_kc(sm.u.qo, PQ, 16 * rb, 32 * kk, lane), acc);
             const int r = 16 * rb + jl;
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[j] = 16 * sb + 4 * g + j <= r ? acc[j] : 0.f;
@@ -348,7 +362,7 @@ __global__ __launch_bounds__(NTP) void kda_prep_kernel(KdaArgs a) {
     // level a: T_10 = -T_11 L_10 T_00 (wave 1), T_32 = -T_33 L_32 T_22 (wave 2)
     if (w == 1 || w == 2) {
         const int i = w == 1 ? 1 : 3, j = i - 1;
-        uint16_t* y = sm.ya[w - 1];
+        uint16_t* y = sm.u.y.ya[w - 1];
         f32x4_t d = mfma16(k16(frag_kr(sm.t, PC, 16 * j, 16 * j, lane), lane),
                            k16(frag_kc(sm.lo, PC, 16 * i, 16 * j, lane), lane), zero4());
         store_dT(y, PY, 0, 0, d, lane);
@@ -363,13 +377,13 @@ __global__ __launch_bounds__(NTP) void kda_prep_kernel(KdaArgs a) {
         const int jb = w & 1, rb = w >> 1;
         const f32x4_t d = mfma16(frag_kr(sm.t, PC, 0, 16 * jb, lane),
                                  frag_kc(sm.lo, PC, 32 + 16 * rb, 0, lane), zero4());
-        store_dT(sm.yb, PY, 16 * jb, 16 * rb, d, lane);
+        store_dT(sm.u.y.yb, PY, 16 * jb, 16 * rb, d, lane);
     }
     lds_barrier();
     // level c: T[32:64, 0:32] = -B^{-1} Y
     if (w < 4) {
         const int jb = w & 1, rb = w >> 1;
-        const f32x4_t d = mfma16(frag_kr(sm.yb, PY, 0, 16 * jb, lane),
+        const f32x4_t d = mfma16(frag_kr(sm.u.y.yb, PY, 0, 16 * jb, lane),
                                  frag_kc(sm.t, PC, 32 + 16 * rb, 32, lane), zero4());
         store_dT(sm.t, PC, 16 * jb, 32 + 16 * rb, -d, lane);
     }

@@ -29,12 +29,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # kernels that make up one step of each workload (matched on the demangled name)
 STEP_KERNELS = {
-    "gla_bf16_b2h8_n2048_d128": [r"gla_prep_kernel<", r"gla_chain_kernel<", r"gla_scan_kernel"],
+    "gla_bf16_b2h8_n2048_d128": [r"gla_prep_kernel<", r"gla_chain_kernel<"],
     "kath_bf16_b1h16_n32768_dk128_dv64": [r"kath_chain_kernel<", r"kath_scan_kernel"],
     "gdn_bf16_b4h16_n8192_d128": [r"gdn_prep_kernel<", r"gdn_fwd_kernel<"],
+    "kda_bf16_b4h16_n8192_d128": [r"kda_prep_kernel<", r"kda_fwd_kernel<"],
     "kath_f32_n256_d16": [r"prefill_valu_kernel<0,"],
     "decode_gdn_256x32_d128": [r"decode_kernel<2,"],
     "decode_gla_256x32_d128": [r"decode_kernel<1,"],
+    "decode_kda_256x32_d128": [r"decode_kernel<3,"],
 }
 COPY_BYTES = 512 << 20
 
