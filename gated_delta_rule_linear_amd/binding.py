@@ -19,7 +19,8 @@ LA_PATH_AUTO, LA_PATH_VALU, LA_PATH_MFMA = 0, 1, 2
 
 VARIANTS = {"kath": LA_KATH, "gla": LA_GLA, "gdn": LA_GDN, "kda": LA_KDA}
 PATHS = {"auto": LA_PATH_AUTO, "valu": LA_PATH_VALU, "mfma": LA_PATH_MFMA}
-EXPORTS = ("la_prefill", "la_prefill_workspace_size", "la_decode_step", "la_status_str",
+EXPORTS = ("la_prefill", "la_prefill_workspace_size", "la_prefill_varlen",
+           "la_prefill_varlen_workspace_size", "la_decode_step", "la_status_str",
            "la_abi_version")
 
 
@@ -57,6 +58,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.la_prefill.restype = ctypes.c_int
     lib.la_prefill_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
     lib.la_prefill_workspace_size.restype = ctypes.c_int
+    i32 = ctypes.c_int32
+    lib.la_prefill_varlen.argtypes = [dp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, sz, vp]
+    lib.la_prefill_varlen.restype = ctypes.c_int
+    lib.la_prefill_varlen_workspace_size.argtypes = [dp, i32, i32, ctypes.POINTER(sz)]
+    lib.la_prefill_varlen_workspace_size.restype = ctypes.c_int
     lib.la_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.la_decode_step.restype = ctypes.c_int
     lib.la_status_str.argtypes = [ctypes.c_int]
@@ -151,6 +158,54 @@ def prefill(q, k, v, g=None, beta=None, *, variant: str, S0=None, z0=None, eps: 
                         _ptr(S0), _ptr(z0), _ptr(o), _ptr(S_final), _ptr(z_final),
                         _ptr(workspace if ws_bytes else None), wsz, _stream_handle(stream, dev))
     _check(rc, "la_prefill")
+    return o, S_final, z_final
+
+
+def prefill_varlen(q, k, v, g=None, beta=None, *, variant: str, cu_seqlens, max_seqlen: int,
+                   S0=None, z0=None, eps: float = 1e-6, path: str = "auto", segments: int = 0,
+                   o=None, S_final=None, z_final=None, workspace=None, stream=None):
+    """Packed variable-length prefill through ``la_prefill_varlen``.
+
+    q, k [1,H,N,dk], v [1,H,N,dv] with the sequences concatenated along N; cu_seqlens an
+    int32 device tensor [nseq + 1] of cumulative lengths; max_seqlen >= every length.
+    g / beta as for ``prefill`` with B = 1. S0 / S_final [nseq,H,dk,dv], z0 / z_final
+    [nseq,H,dk]. Returns (o, S_final, z_final or None).
+    """
+    import torch
+    lib = load()
+    one, H, N, dk = q.shape
+    dv = v.shape[-1]
+    nseq = cu_seqlens.numel() - 1
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("S0", S0),
+                    ("z0", z0), ("o", o), ("S_final", S_final), ("z_final", z_final),
+                    ("cu_seqlens", cu_seqlens)):
+        _require_contig(name, t)
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    io = _dtype_code(q)
+    gate_t = g if g is not None else beta
+    gd = _dtype_code(gate_t) if gate_t is not None else LA_F32
+    desc = make_desc(variant, one, H, N, dk, dv, io, gd, eps, path, 0, segments)
+    dev = q.device
+    if o is None:
+        o = torch.empty((one, H, N, dv), dtype=q.dtype, device=dev)
+    if S_final is None:
+        S_final = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=dev)
+    if z_final is None and desc.variant == LA_KATH:
+        z_final = torch.empty((nseq, H, dk), dtype=torch.float32, device=dev)
+    n = ctypes.c_size_t(0)
+    _check(lib.la_prefill_varlen_workspace_size(ctypes.byref(desc), nseq, int(max_seqlen),
+                                                ctypes.byref(n)), "la_prefill_varlen_workspace_size")
+    ws_bytes = int(n.value)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.la_prefill_varlen(ctypes.byref(desc), nseq, _ptr(cu_seqlens), int(max_seqlen),
+                               _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(z0),
+                               _ptr(o), _ptr(S_final), _ptr(z_final),
+                               _ptr(workspace if ws_bytes else None), wsz,
+                               _stream_handle(stream, dev))
+    _check(rc, "la_prefill_varlen")
     return o, S_final, z_final
 
 

@@ -94,6 +94,24 @@ __device__ __forceinline__ float elu_plus_one(float x) { return x > 0.f ? x + 1.
 
 // Index of this thread's wave in the workgroup, as a wave-uniform (scalar) value so
 // that control flow depending on it compiles to scalar branches.
+// Tokens of sequence seq = s H + h. A dense [B, H, N, d] layout holds them at seq N,
+// N of them. A packed variable-length batch (one [1, H, N, d] layout, cu the nseq + 1
+// cumulative sequence lengths) holds sequence s of head h at h N + cu[s], cu[s + 1] -
+// cu[s] of them: the state restarts at every boundary. Offsets are clamped to the
+// head's N tokens and lengths to maxlen, so no access leaves the buffers whatever cu
+// holds.
+struct SeqSpan {
+    size_t base;
+    int len;
+};
+__device__ __forceinline__ SeqSpan seq_span(int seq, int H, int N, int maxlen, const int32_t* cu) {
+    if (cu == nullptr) return SeqSpan{size_t(seq) * size_t(N), N};
+    const int s = seq / H, h = seq - s * H;
+    const int st = min(max(cu[s], 0), N);
+    const int en = min(max(cu[s + 1], st), N);
+    return SeqSpan{size_t(h) * size_t(N) + size_t(st), min(en - st, maxlen)};
+}
+
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Natural log and exp on the hardware transcendental units (log2 / exp2), a few ulp.

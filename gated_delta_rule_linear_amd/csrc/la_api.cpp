@@ -96,9 +96,12 @@ int check_desc(const la_desc* d, bool decode) {
     return LA_OK;
 }
 
-// Resolve path, chunk and segments for a prefill descriptor.
-int plan_prefill(const la_desc& d, Problem& p) {
-    p.B = d.B; p.H = d.H; p.N = d.N; p.dk = d.dk; p.dv = d.dv;
+// Resolve path, chunk and segments for a prefill over nseq sequences per head whose
+// longest has max_len tokens (a dense batch: nseq = B, max_len = N, cu = null).
+int plan_prefill(const la_desc& d, Problem& p, int nseq, int max_len, const int32_t* cu) {
+    p.B = nseq; p.H = d.H; p.N = d.N; p.dk = d.dk; p.dv = d.dv;
+    p.L = max_len;
+    p.cu = cu;
     p.variant = d.variant;
     p.io_bf16 = d.io_dtype == LA_BF16;
     p.gate_bf16 = d.gate_dtype == LA_BF16;
@@ -114,8 +117,8 @@ int plan_prefill(const la_desc& d, Problem& p) {
     p.chunk = path == LA_PATH_MFMA ? la::kMfmaChunk : la::kValuChunk;
     if (d.chunk != 0 && d.chunk != p.chunk) return LA_ERR_UNSUPPORTED;
     p.segments = 1;
-    if (path == LA_PATH_MFMA && (d.variant == LA_KATH || d.variant == LA_GLA) && d.N > 0) {
-        const int nchunks = (d.N + p.chunk - 1) / p.chunk;
+    if (path == LA_PATH_MFMA && (d.variant == LA_KATH || d.variant == LA_GLA) && p.L > 0) {
+        const int nchunks = (p.L + p.chunk - 1) / p.chunk;
         int segs = d.segments > 0                 ? d.segments
                    : d.variant == LA_GLA ? la::gla_mfma_auto_segments(p)
                                          : la::kath_mfma_auto_segments(p);
@@ -129,7 +132,7 @@ int plan_prefill(const la_desc& d, Problem& p) {
 }
 
 size_t workspace_for(const Problem& p) {
-    if (p.N == 0 || p.B == 0 || p.H == 0) return 0;
+    if (p.N == 0 || p.L == 0 || p.B == 0 || p.H == 0) return 0;
     if (p.path == LA_PATH_MFMA)
         return p.variant == LA_GDN   ? la::gdn_mfma_workspace_bytes(p)
                : p.variant == LA_KDA ? la::kda_mfma_workspace_bytes(p)
@@ -160,24 +163,43 @@ int la_prefill_workspace_size(const la_desc* d, size_t* bytes) {
     if (rc != LA_OK) return rc;
     if (!bytes) return LA_ERR_INVALID;
     Problem p;
-    rc = plan_prefill(*d, p);
+    rc = plan_prefill(*d, p, d->B, d->N, nullptr);
     if (rc != LA_OK) return rc;
     *bytes = workspace_for(p);
     return LA_OK;
 }
 
-int la_prefill(const la_desc* d, const void* q, const void* k, const void* v, const void* g,
-               const void* beta, const float* S0, const float* z0, void* o, float* S_final,
-               float* z_final, void* workspace, size_t workspace_bytes, void* stream) {
+int la_prefill_varlen_workspace_size(const la_desc* d, int32_t nseq, int32_t max_seqlen,
+                                     size_t* bytes) {
+    int rc = check_desc(d, false);
+    if (rc != LA_OK) return rc;
+    if (!bytes || d->B != 1 || nseq < 0 || max_seqlen < 0 || max_seqlen > d->N) return LA_ERR_INVALID;
+    Problem p;
+    rc = plan_prefill(*d, p, nseq, max_seqlen, nullptr);
+    if (rc != LA_OK) return rc;
+    *bytes = workspace_for(p);
+    return LA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared by la_prefill (nseq = B, cu = null, max_len = N) and la_prefill_varlen.
+int prefill_impl(const la_desc* d, int nseq, const int32_t* cu, int max_len, const void* q,
+                 const void* k, const void* v, const void* g, const void* beta, const float* S0,
+                 const float* z0, void* o, float* S_final, float* z_final, void* workspace,
+                 size_t workspace_bytes, void* stream) {
     int rc = check_desc(d, false);
     if (rc != LA_OK) return rc;
     Problem p;
-    rc = plan_prefill(*d, p);
+    rc = plan_prefill(*d, p, nseq, max_len, cu);
     if (rc != LA_OK) return rc;
     const bool kath = d->variant == LA_KATH, gla = d->variant == LA_GLA,
                gdn = d->variant == LA_GDN, kda = d->variant == LA_KDA;
-    const bool empty_seq = (uint64_t(d->B) * uint64_t(d->H)) == 0;
-    const bool tokens = !empty_seq && d->N > 0;
+    const bool varlen = cu != nullptr;
+    const bool empty_seq = (uint64_t(nseq) * uint64_t(d->H)) == 0;
+    const bool tokens = !empty_seq && d->N > 0 && (uint64_t(d->B) * uint64_t(d->H)) > 0;
     // presence rules
     if (kath && (g || beta)) return LA_ERR_INVALID;
     if (gla && beta) return LA_ERR_INVALID;
@@ -196,13 +218,20 @@ int la_prefill(const la_desc* d, const void* q, const void* k, const void* v, co
     if (!check_alignment(*d, q, k, v, g, beta, S0, z0, o, S_final, z_final))
         return LA_ERR_INVALID;
     // aliasing: outputs overlap nothing, except S_final == S0 and z_final == z0 exactly
-    const Sizes s = sizes_of(*d);
+    Sizes s = sizes_of(*d);
+    if (varlen) {   // states are per (sequence, head), not per (batch row, head)
+        const uint64_t states = mul(uint64_t(nseq), uint64_t(d->H));
+        s.S = mul(mul(mul(states, d->dk), d->dv), 4);
+        s.z = d->variant == LA_KATH ? mul(mul(states, d->dk), 4) : 0;
+        if (s.S == UINT64_MAX || s.z == UINT64_MAX) return LA_ERR_INVALID;
+    }
     const Range rq = range(q, tokens ? s.q : 0), rk = range(k, tokens ? s.k : 0),
                 rv = range(v, tokens ? s.v : 0), rg = range(g, tokens ? s.g : 0),
                 rb = range(beta, tokens ? s.beta : 0), rS0 = range(S0, s.S), rz0 = range(z0, s.z),
                 ro = range(o, tokens ? s.o : 0), rS = range(S_final, s.S),
-                rz = range(z_final, s.z);
-    const Range inputs[] = {rq, rk, rv, rg, rb, rS0, rz0};
+                rz = range(z_final, s.z),
+                rc_ = range(cu, varlen ? (uint64_t(nseq) + 1) * 4 : 0);
+    const Range inputs[] = {rq, rk, rv, rg, rb, rS0, rz0, rc_};
     for (const Range& in : inputs) {
         if (overlap(ro, in)) return LA_ERR_INVALID;
     }
@@ -213,6 +242,7 @@ int la_prefill(const la_desc* d, const void* q, const void* k, const void* v, co
     }
     if (overlap(rS, rS0) && S_final != S0) return LA_ERR_INVALID;
     if (overlap(rS, rz0) || overlap(rz, rS0)) return LA_ERR_INVALID;
+    if (overlap(rS, rc_) || overlap(rz, rc_)) return LA_ERR_INVALID;
     if (overlap(rz, rz0) && z_final != z0) return LA_ERR_INVALID;
     // workspace
     const size_t need = workspace_for(p);
@@ -220,7 +250,7 @@ int la_prefill(const la_desc* d, const void* q, const void* k, const void* v, co
         if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
             return LA_ERR_WORKSPACE;
         const Range rw = range(workspace, need);
-        const Range every[] = {rq, rk, rv, rg, rb, rS0, rz0, ro, rS, rz};
+        const Range every[] = {rq, rk, rv, rg, rb, rS0, rz0, ro, rS, rz, rc_};
         for (const Range& x : every)
             if (overlap(rw, x)) return LA_ERR_INVALID;
     }
@@ -233,7 +263,7 @@ int la_prefill(const la_desc* d, const void* q, const void* k, const void* v, co
 
     (void)hipGetLastError();  // clear a stale error so the check below sees this call's
     hipError_t err;
-    if (p.N == 0)
+    if (p.N == 0 || p.L == 0)
         err = la::launch_state_init(p);
     else if (p.path == LA_PATH_MFMA)
         err = gdn                     ? la::launch_prefill_gdn_mfma(p)
@@ -244,6 +274,36 @@ int la_prefill(const la_desc* d, const void* q, const void* k, const void* v, co
         err = la::launch_prefill_valu(p);
     if (err == hipSuccess) err = hipGetLastError();
     return err == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int la_prefill(const la_desc* d, const void* q, const void* k, const void* v, const void* g,
+               const void* beta, const float* S0, const float* z0, void* o, float* S_final,
+               float* z_final, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!d) return LA_ERR_INVALID;
+    return prefill_impl(d, d->B, nullptr, d->N, q, k, v, g, beta, S0, z0, o, S_final, z_final,
+                        workspace, workspace_bytes, stream);
+}
+
+int la_prefill_varlen(const la_desc* d, int32_t nseq, const int32_t* cu_seqlens,
+                      int32_t max_seqlen, const void* q, const void* k, const void* v,
+                      const void* g, const void* beta, const float* S0, const float* z0, void* o,
+                      float* S_final, float* z_final, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+    if (!d) return LA_ERR_INVALID;
+    if (d->B != 1 || nseq < 0 || max_seqlen < 0 || max_seqlen > d->N) return LA_ERR_INVALID;
+    if (nseq > 0 && (!cu_seqlens || !aligned(cu_seqlens, 4))) return LA_ERR_INVALID;
+    if (nseq == 0) cu_seqlens = nullptr;
+    if (nseq > 0) {
+        return prefill_impl(d, nseq, cu_seqlens, max_seqlen, q, k, v, g, beta, S0, z0, o,
+                            S_final, z_final, workspace, workspace_bytes, stream);
+    }
+    // no sequences: only the descriptor and argument presence are checked
+    return prefill_impl(d, 0, nullptr, 0, q, k, v, g, beta, S0, z0, o, S_final, z_final,
+                        workspace, workspace_bytes, stream);
 }
 
 int la_decode_step(const la_desc* d, const void* q, const void* k, const void* v, const void* g,

@@ -20,6 +20,11 @@ struct Problem {
     int path = LA_PATH_VALU;  // resolved: VALU or MFMA
     int chunk = 16;           // resolved chunk size
     int segments = 1;         // resolved segment count (KATH / GLA matrix-core path)
+    // Sequences: B * H of them (B = the batch, or the number of packed sequences). N is
+    // the token count of one head's rows in the layout, L the longest sequence (N for a
+    // dense batch), cu the packed batch's cumulative lengths (device, B + 1) or null.
+    int L = 0;
+    const int32_t* cu = nullptr;
     const void *q = nullptr, *k = nullptr, *v = nullptr, *g = nullptr, *beta = nullptr;
     const float *S0 = nullptr, *z0 = nullptr;
     void* o = nullptr;

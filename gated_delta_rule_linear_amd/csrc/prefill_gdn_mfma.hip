@@ -82,6 +82,8 @@ struct GdnArgs {
     float* S;
     uint16_t* T;   // workspace: [nseq][nchunks][64][64] bf16, T per chunk
     int N, nseq, ntiles, nchunks, gate_bf16;
+    const int32_t* cu;   // packed variable-length batch, or null
+    int H, L;            // heads; longest sequence (chunk counts are sized for it)
 };
 
 // bf16 fragment with the K half 16..31 (lane groups 2, 3) forced to zero: 16 x 16 x 16
@@ -109,8 +111,10 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
     const int g = lane >> 4, jl = lane & 15;
     const size_t seq = blockIdx.x / a.nchunks;
     const int ch = blockIdx.x % a.nchunks;
-    const int t0 = ch * C, n = min(C, a.N - t0);
-    const size_t tok0 = seq * size_t(a.N);
+    const SeqSpan sp = seq_span(int(seq), a.H, a.N, a.L, a.cu);
+    const int t0 = ch * C, n = min(C, sp.len - t0);
+    const size_t tok0 = sp.base;
+    if (n <= 0) return;   // past this sequence's end: the forward reads zeros instead
 
     // loads from clamped rows (always valid), padding applied when staging
     uint4 kv[4];
@@ -288,8 +292,9 @@ __global__ __launch_bounds__(NT * CG) void gdn_fwd_kernel(GdnArgs a) {
     const int cw = 16 * NVT * cg;      // first column of this wave, within the tile
     const int c0 = mp.tile * VT + cw;  // ... and within the row
     const size_t seq = size_t(mp.seq);
-    const size_t tok0 = seq * size_t(a.N);
-    const int nchunks = a.nchunks;
+    const SeqSpan sp = seq_span(int(seq), a.H, a.N, a.L, a.cu);
+    const size_t tok0 = sp.base;
+    const int nchunks = (sp.len + C - 1) / C;   // this sequence's chunks
     const int rw = 16 * rb + jl;       // this lane's row of the wave's 16-row block
     const int nk = rb < 2 ? 1 : 2;     // T and P vanish for s >= 16 (rb + 1)
 
@@ -312,15 +317,15 @@ __global__ __launch_bounds__(NT * CG) void gdn_fwd_kernel(GdnArgs a) {
 
     // Per-sequence buffer resources: rows past the end of the sequence read as zero
     // (the ragged last chunk's padding) and o rows past it are dropped on store.
-    const rsrc_t rq = make_rsrc(a.q + tok0 * DK, uint32_t(a.N) * DK * 2u);
-    const rsrc_t rk = make_rsrc(a.k + tok0 * DK, uint32_t(a.N) * DK * 2u);
-    const rsrc_t rv = make_rsrc(a.v + tok0 * DV, uint32_t(a.N) * uint32_t(DV) * 2u);
-    const rsrc_t ro = make_rsrc(a.o + tok0 * DV, uint32_t(a.N) * uint32_t(DV) * 2u);
-    const rsrc_t rt = make_rsrc(a.T + seq * nchunks * size_t(C * C),
+    const rsrc_t rq = make_rsrc(a.q + tok0 * DK, uint32_t(sp.len) * DK * 2u);
+    const rsrc_t rk = make_rsrc(a.k + tok0 * DK, uint32_t(sp.len) * DK * 2u);
+    const rsrc_t rv = make_rsrc(a.v + tok0 * DV, uint32_t(sp.len) * uint32_t(DV) * 2u);
+    const rsrc_t ro = make_rsrc(a.o + tok0 * DV, uint32_t(sp.len) * uint32_t(DV) * 2u);
+    const rsrc_t rt = make_rsrc(a.T + seq * size_t(a.nchunks) * size_t(C * C),
                                 uint32_t(nchunks) * (C * C * 2u));
     constexpr uint32_t GS = GB ? 2u : 4u;
-    const rsrc_t ra = make_rsrc(static_cast<const char*>(a.alpha) + tok0 * GS, uint32_t(a.N) * GS);
-    const rsrc_t rb_ = make_rsrc(static_cast<const char*>(a.beta) + tok0 * GS, uint32_t(a.N) * GS);
+    const rsrc_t ra = make_rsrc(static_cast<const char*>(a.alpha) + tok0 * GS, uint32_t(sp.len) * GS);
+    const rsrc_t rb_ = make_rsrc(static_cast<const char*>(a.beta) + tok0 * GS, uint32_t(sp.len) * GS);
 
     // loads of one chunk, all unconditional (a chunk index past the end reads zeros);
     // K first, since its LDS copy is written before the other operands are needed
@@ -373,7 +378,7 @@ __global__ __launch_bounds__(NT * CG) void gdn_fwd_kernel(GdnArgs a) {
     auto process = [&](const ChunkRegs<NVT, KST>& R, const ChunkRegs<NVT, KST>& Rn,
                        ChunkRegs<NVT, KST>& Rl, int ch, int cur) {
         load_part(Rl, ch + 2, 0);
-        const int t0 = ch * C, n = min(C, a.N - t0);
+        const int t0 = ch * C, n = min(C, sp.len - t0);
         const uint16_t* kc = sm.k[cur];
         // gates: every wave scans log alpha itself (lane = token); lane (g, j) then
         // takes the values of token 16 rb + j
@@ -535,8 +540,11 @@ GdnArgs make_args(const Problem& p) {
     a.T = static_cast<uint16_t*>(p.ws);
     a.N = p.N;
     a.nseq = int(size_t(p.B) * size_t(p.H));
-    a.nchunks = (p.N + C - 1) / C;
+    a.nchunks = (p.L + C - 1) / C;
     a.gate_bf16 = p.gate_bf16;
+    a.cu = p.cu;
+    a.H = p.H;
+    a.L = p.L;
     return a;
 }
 
@@ -577,13 +585,15 @@ bool gdn_mfma_supported(int dk, int dv, bool io_bf16) {
 }
 
 size_t gdn_mfma_workspace_bytes(const Problem& p) {
-    const size_t nchunks = size_t((p.N + C - 1) / C);
+    const size_t nchunks = size_t((p.L + C - 1) / C);
     return size_t(p.B) * size_t(p.H) * nchunks * C * C * sizeof(uint16_t);
 }
 
 hipError_t launch_prefill_gdn_mfma(const Problem& p) {
     const size_t nseq = size_t(p.B) * size_t(p.H);
     if (nseq > (1u << 26) || !p.ws) return hipErrorInvalidValue;
+    // buffer offsets are 32-bit: one sequence's rows and its chunk transforms
+    if (size_t(p.L) * DK * 4 >= (size_t(1) << 31)) return hipErrorInvalidValue;
     // Forward shape: each value tile is an independent chain of chunks, so the tile
     // count sets the parallelism, while every tile re-reads the chunk's q, K, T and P
     // through the vector memory path, whose request rate bounds the loop. 32-column

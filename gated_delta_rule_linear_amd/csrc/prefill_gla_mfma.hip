@@ -64,6 +64,8 @@ struct GlaArgs {
     float* dS;           // [nseq][nseg][tile][DK x VT]: S0, then the segment summaries
     float* A;            // [nseq][nseg - 1][DK]
     int N, nseq, nchunks, nseg, cps, ntiles, DV;
+    const int32_t* cu;   // packed variable-length batch, or null
+    int H, L;            // heads; longest sequence (chunk counts are sized for it)
 };
 
 // ---------------------------------------------------------------------------
@@ -107,13 +109,15 @@ __global__ __launch_bounds__(NTP) void gla_prep_kernel(GlaArgs a) {
     const size_t seq = size_t(mp.seq);
     const int ch = mp.tile;
     const int t0 = ch * C;
-    const size_t tok0 = seq * size_t(a.N);
+    const SeqSpan sp = seq_span(int(seq), a.H, a.N, a.L, a.cu);
+    const size_t tok0 = sp.base;
+    if (t0 >= sp.len) return;   // past this sequence's end: nothing reads this chunk
     const int rg = w, b = w >> 1;
     const bool upper = (w & 1) != 0;
     const int col = 2 * lane;
 
     // rows past the end of the sequence read as zero
-    const uint32_t rows_left = uint32_t(a.N - t0);
+    const uint32_t rows_left = uint32_t(sp.len - t0);
     const rsrc_t rq = make_rsrc(a.q + (tok0 + t0) * DK, rows_left * DK * 2u);
     const rsrc_t rk = make_rsrc(a.k + (tok0 + t0) * DK, rows_left * DK * 2u);
     constexpr uint32_t GS = GB ? 2u : 4u;
@@ -313,9 +317,11 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
     const int g = lane >> 4, jl = lane & 15;
     const int DV = a.DV;
     const int c0 = tile * VT;
-    const size_t tok0 = size_t(seq) * size_t(a.N);
-    const int ch0 = seg * a.cps, ch1 = min(a.nchunks, ch0 + a.cps);
-    const int nloc = ch1 - ch0;
+    const SeqSpan sp = seq_span(seq, a.H, a.N, a.L, a.cu);
+    const size_t tok0 = sp.base;
+    const int nch = (sp.len + C - 1) / C;   // this sequence's chunks
+    const int ch0 = seg * a.cps, ch1 = min(nch, ch0 + a.cps);
+    const int nloc = max(ch1 - ch0, 0);     // a segment past the end is an identity step
     const int nk = w < 2 ? 1 : 2;   // P rows 16 w .. vanish for s >= 16 (w + 1)
     const int rw = 16 * w + jl;
 
@@ -344,8 +350,8 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
     // only, so a prefetch past the segment reads zeros.
     const rsrc_t rw_ = make_rsrc(a.ws + (size_t(seq) * a.nchunks + ch0) * kWsChunk,
                                  uint32_t(nloc) * kWsChunk);
-    const rsrc_t rv = make_rsrc(a.v + tok0 * DV, uint32_t(a.N) * uint32_t(DV) * 2u);
-    const uint32_t obytes = uint32_t(a.N) * uint32_t(DV) * 2u;
+    const rsrc_t rv = make_rsrc(a.v + tok0 * DV, uint32_t(sp.len) * uint32_t(DV) * 2u);
+    const uint32_t obytes = uint32_t(sp.len) * uint32_t(DV) * 2u;
     const rsrc_t ro = make_rsrc(a.o + tok0 * DV, obytes);
     if (!OUT && seg == 0 && a.S0) {
         // the forward reads S0 from slot 0, so S_final may alias S0
@@ -588,7 +594,7 @@ struct WsLayout {
 };
 WsLayout ws_layout(const Problem& p) {
     const size_t nseq = size_t(p.B) * size_t(p.H);
-    const size_t nchunks = size_t((p.N + C - 1) / C);
+    const size_t nchunks = size_t((p.L + C - 1) / C);
     const size_t nsum = size_t(p.segments > 1 ? p.segments - 1 : 0);
     const size_t nslot = p.segments > 1 ? size_t(p.segments) : 0;
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
@@ -622,8 +628,11 @@ hipError_t launch_nvt(const Problem& p) {
     a.dS = reinterpret_cast<float*>(ws + L.dS);
     a.A = reinterpret_cast<float*>(ws + L.A);
     a.N = p.N;
+    a.cu = p.cu;
+    a.H = p.H;
+    a.L = p.L;
     a.nseq = int(size_t(p.B) * size_t(p.H));
-    a.nchunks = (p.N + C - 1) / C;
+    a.nchunks = (p.L + C - 1) / C;
     a.nseg = p.segments;
     a.cps = (a.nchunks + a.nseg - 1) / a.nseg;
     a.DV = p.dv;
@@ -678,7 +687,7 @@ int gla_mfma_auto_segments(const Problem& p) {
     // least two chunks per segment
     const size_t nseq = size_t(p.B) * size_t(p.H);
     const size_t ntiles = size_t(p.dv / (16 * pick_nvt(p.dv)));
-    const size_t nchunks = size_t((p.N + C - 1) / C);
+    const size_t nchunks = size_t((p.L + C - 1) / C);
     const size_t units = nseq * ntiles;
     size_t want = (256 + units - 1) / units;
     const size_t cap = nchunks / 2;
@@ -690,8 +699,8 @@ hipError_t launch_prefill_gla_mfma(const Problem& p) {
     const size_t nseq = size_t(p.B) * size_t(p.H);
     if (nseq > (1u << 24) || !p.ws) return hipErrorInvalidValue;
     // buffer offsets are 32-bit: one sequence's v / o rows and its chunk workspace
-    if (size_t(p.N) * size_t(p.dv) * 2 >= (size_t(1) << 31)) return hipErrorInvalidValue;
-    if (size_t((p.N + C - 1) / C) * kWsChunk >= (size_t(1) << 31)) return hipErrorInvalidValue;
+    if (size_t(p.L) * size_t(DK) * 4 >= (size_t(1) << 31)) return hipErrorInvalidValue;
+    if (size_t((p.L + C - 1) / C) * kWsChunk >= (size_t(1) << 31)) return hipErrorInvalidValue;
     return p.gate_bf16 ? launch_gb<true>(p) : launch_gb<false>(p);
 }
 

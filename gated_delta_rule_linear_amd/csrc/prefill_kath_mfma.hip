@@ -42,6 +42,8 @@ struct KathArgs {
     float* dz;   // [nseq][nseg][DK]: likewise for z
     float eps;
     int N, nseq, nchunks, nseg, cps, ntiles, DV;
+    const int32_t* cu;   // packed variable-length batch, or null
+    int H, L;            // heads; longest sequence (chunk counts are sized for it)
 };
 
 // The summary kernel uses only the fields up to `qt`, and is launched with that much
@@ -90,9 +92,11 @@ __global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
     const int DV = a.DV;
     const int cw = 16 * NVT * cg;              // the wave's first column in the tile
     const int c0 = tile * VT;
-    const size_t tok0 = size_t(seq) * size_t(a.N);
-    const int ch0 = seg * a.cps, ch1 = min(a.nchunks, ch0 + a.cps);
-    const int nloc = ch1 - ch0;
+    const SeqSpan sp = seq_span(seq, a.H, a.N, a.L, a.cu);
+    const size_t tok0 = sp.base;
+    const int nch = (sp.len + C - 1) / C;   // this sequence's chunks
+    const int ch0 = seg * a.cps, ch1 = min(nch, ch0 + a.cps);
+    const int nloc = max(ch1 - ch0, 0);     // a segment past the end is an identity step
     const int nsum = a.nseg - 1;
     const int rw = 16 * rb + jl;
 
@@ -135,9 +139,9 @@ __global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
 
     // Per-sequence resources: rows past the end of the sequence read as zero and
     // output rows past it are dropped. Every load is unconditional.
-    const uint32_t obytes = uint32_t(a.N) * uint32_t(DV) * 2u;
-    const rsrc_t rq = make_rsrc(a.q + tok0 * DK, uint32_t(a.N) * DK * 2u);
-    const rsrc_t rk = make_rsrc(a.k + tok0 * DK, uint32_t(a.N) * DK * 2u);
+    const uint32_t obytes = uint32_t(sp.len) * uint32_t(DV) * 2u;
+    const rsrc_t rq = make_rsrc(a.q + tok0 * DK, uint32_t(sp.len) * DK * 2u);
+    const rsrc_t rk = make_rsrc(a.k + tok0 * DK, uint32_t(sp.len) * DK * 2u);
     const rsrc_t rv = make_rsrc(a.v + tok0 * DV, obytes);
     const rsrc_t ro = make_rsrc(a.o + tok0 * DV, obytes);
 
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
     // phi of one chunk's q and k (zero on padding rows), V, and per-wave column sums
     // of phi(k)
     auto stage = [&](const ChainRegs<KST, KV>& R, int buf, int lc) {
-        const int n = min(C, a.N - (ch0 + lc) * C);
+        const int n = min(C, sp.len - (ch0 + lc) * C);
         float zpart[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) zpart[q] = 0.f;
@@ -462,8 +466,11 @@ hipError_t launch_cfg(const Problem& p) {
     a.dz = ws ? reinterpret_cast<float*>(ws + L.dz) : nullptr;
     a.eps = p.eps;
     a.N = p.N;
+    a.cu = p.cu;
+    a.H = p.H;
+    a.L = p.L;
     a.nseq = int(size_t(p.B) * size_t(p.H));
-    a.nchunks = (p.N + C - 1) / C;
+    a.nchunks = (p.L + C - 1) / C;
     a.nseg = p.segments;
     a.cps = (a.nchunks + a.nseg - 1) / a.nseg;
     a.DV = p.dv;
@@ -505,7 +512,7 @@ int kath_mfma_auto_segments(const Problem& p) {
     const size_t nseq = size_t(p.B) * size_t(p.H);
     const TileCfg t = pick_tile(p.dv);
     const size_t ntiles = size_t(p.dv / (16 * t.nvt * t.cg));
-    const size_t nchunks = size_t((p.N + C - 1) / C);
+    const size_t nchunks = size_t((p.L + C - 1) / C);
     const size_t units = nseq * ntiles;
     size_t want = (256 + units - 1) / units;
     const size_t cap = nchunks / 4;
@@ -518,7 +525,7 @@ hipError_t launch_prefill_kath_mfma(const Problem& p) {
     if (nseq > (1u << 24)) return hipErrorInvalidValue;
     if (p.segments > 1 && !p.ws) return hipErrorInvalidValue;
     // buffer offsets are 32-bit: one sequence's q / k / v / o rows
-    if (size_t(p.N) * DK * 2 >= (size_t(1) << 31)) return hipErrorInvalidValue;
+    if (size_t(p.L) * DK * 2 >= (size_t(1) << 31)) return hipErrorInvalidValue;
     const TileCfg t = pick_tile(p.dv);
     if (t.cg == 2) return launch_cfg<2, 2>(p);
     return t.nvt == 1 ? launch_cfg<1, 1>(p) : launch_cfg<2, 1>(p);

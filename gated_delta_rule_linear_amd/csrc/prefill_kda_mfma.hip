@@ -67,6 +67,8 @@ struct KdaArgs {
     float* S;
     unsigned char* ws;
     int N, nseq, ntiles, nchunks;
+    const int32_t* cu;   // packed variable-length batch, or null
+    int H, L;            // heads; longest sequence (chunk counts are sized for it)
 };
 
 // bf16 fragment with the K half 16..31 (lane groups 2, 3) forced to zero: 16 x 16 x 16
@@ -120,13 +122,15 @@ __global__ __launch_bounds__(NTP) void kda_prep_kernel(KdaArgs a) {
     const size_t seq = size_t(mp.seq);
     const int ch = mp.tile;
     const int t0 = ch * C;
-    const size_t tok0 = seq * size_t(a.N);
+    const SeqSpan sp = seq_span(int(seq), a.H, a.N, a.L, a.cu);
+    const size_t tok0 = sp.base;
+    if (t0 >= sp.len) return;   // past this sequence's end: the forward reads zeros instead
     const int rg = w, b = w >> 1;
     const bool upper = (w & 1) != 0;
     const int col = 2 * lane;
 
     // rows past the end of the sequence read as zero
-    const uint32_t rows_left = uint32_t(a.N - t0);
+    const uint32_t rows_left = uint32_t(sp.len - t0);
     const rsrc_t rq = make_rsrc(a.q + (tok0 + t0) * DK, rows_left * DK * 2u);
     const rsrc_t rk = make_rsrc(a.k + (tok0 + t0) * DK, rows_left * DK * 2u);
     constexpr uint32_t GS = GB ? 2u : 4u;
@@ -432,8 +436,9 @@ __global__ __launch_bounds__(NTF) void kda_fwd_kernel(KdaArgs a) {
     const int DV = a.ntiles * VT;
     const int c0 = mp.tile * VT;
     const size_t seq = size_t(mp.seq);
-    const size_t tok0 = seq * size_t(a.N);
-    const int nchunks = a.nchunks;
+    const SeqSpan sp = seq_span(int(seq), a.H, a.N, a.L, a.cu);
+    const size_t tok0 = sp.base;
+    const int nchunks = (sp.len + C - 1) / C;   // this sequence's chunks
     const int rw = 16 * rb + jl;
     const int nk = rb < 2 ? 1 : 2;   // T and P vanish for s >= 16 (rb + 1)
 
@@ -453,12 +458,12 @@ __global__ __launch_bounds__(NTF) void kda_fwd_kernel(KdaArgs a) {
 #pragma unroll
         for (int ct = 0; ct < NVT; ++ct) store_st<NVT>(sm.st, PQ, 16 * (2 * rb + ib), 0, ct, S[ib][ct], lane);
 
-    const rsrc_t rw_ = make_rsrc(a.ws + seq * size_t(nchunks) * kWsChunk, uint32_t(nchunks) * kWsChunk);
-    const uint32_t vbytes = uint32_t(a.N) * uint32_t(DV) * 2u;
+    const rsrc_t rw_ = make_rsrc(a.ws + seq * size_t(a.nchunks) * kWsChunk, uint32_t(nchunks) * kWsChunk);
+    const uint32_t vbytes = uint32_t(sp.len) * uint32_t(DV) * 2u;
     const rsrc_t rv = make_rsrc(a.v + tok0 * DV, vbytes);
     const rsrc_t ro = make_rsrc(a.o + tok0 * DV, vbytes);
     constexpr uint32_t GS = GB ? 2u : 4u;
-    const rsrc_t rbeta = make_rsrc(static_cast<const char*>(a.beta) + tok0 * GS, uint32_t(a.N) * GS);
+    const rsrc_t rbeta = make_rsrc(static_cast<const char*>(a.beta) + tok0 * GS, uint32_t(sp.len) * GS);
 
     // a chunk's loads go out in three parts over the processing of the chunk two before
     // it (each part in program order: the memory-counter waits count the loads after it)
@@ -590,7 +595,11 @@ __global__ __launch_bounds__(NTF) void kda_fwd_kernel(KdaArgs a) {
     load_chunk(RA, 0);
     load_chunk(RB, 1);
     lds_barrier();
-    f32x4_t Sfin[2][NVT];
+    f32x4_t Sfin[2][NVT];   // the state after the sequence's last chunk (S0 if it has none)
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int ct = 0; ct < NVT; ++ct) Sfin[ib][ct] = S[ib][ct];
     for (int ch = 0; ch < nchunks; ch += 3) {
         process(RA, RC, ch);
         if (ch + 1 == nchunks) { for (int ib = 0; ib < 2; ++ib) for (int ct = 0; ct < NVT; ++ct) Sfin[ib][ct] = S[ib][ct]; }
@@ -624,7 +633,10 @@ hipError_t launch_gb(const Problem& p) {
     a.ws = static_cast<unsigned char*>(p.ws);
     a.N = p.N;
     a.nseq = int(size_t(p.B) * size_t(p.H));
-    a.nchunks = (p.N + C - 1) / C;
+    a.nchunks = (p.L + C - 1) / C;
+    a.cu = p.cu;
+    a.H = p.H;
+    a.L = p.L;
     const bool wide = p.dv >= 32;
     a.ntiles = p.dv / (wide ? 32 : 16);
     {
@@ -655,7 +667,7 @@ bool kda_mfma_supported(int dk, int dv, bool io_bf16) {
 
 size_t kda_mfma_workspace_bytes(const Problem& p) {
     const size_t nseq = size_t(p.B) * size_t(p.H);
-    const size_t nchunks = size_t((p.N + C - 1) / C);
+    const size_t nchunks = size_t((p.L + C - 1) / C);
     return nseq * nchunks * kWsChunk;
 }
 
@@ -663,8 +675,8 @@ hipError_t launch_prefill_kda_mfma(const Problem& p) {
     const size_t nseq = size_t(p.B) * size_t(p.H);
     if (nseq > (1u << 24) || !p.ws) return hipErrorInvalidValue;
     // buffer offsets are 32-bit: one sequence's v / o rows and its chunk workspace
-    if (size_t(p.N) * size_t(p.dv) * 2 >= (size_t(1) << 31)) return hipErrorInvalidValue;
-    if (size_t((p.N + C - 1) / C) * kWsChunk >= (size_t(1) << 31)) return hipErrorInvalidValue;
+    if (size_t(p.L) * DK * 4 >= (size_t(1) << 31)) return hipErrorInvalidValue;
+    if (size_t((p.L + C - 1) / C) * kWsChunk >= (size_t(1) << 31)) return hipErrorInvalidValue;
     return p.gate_bf16 ? launch_gb<true>(p) : launch_gb<false>(p);
 }
 

@@ -49,6 +49,8 @@ struct ValuArgs {
     int N, ntiles;
     float eps;
     int io_bf16, gate_bf16;
+    const int32_t* cu;   // packed variable-length batch, or null
+    int H, L;
 };
 
 template <int VAR, int DK, int DV>
@@ -70,7 +72,9 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
     const int tile = blockIdx.x % a.ntiles;
     const int c0 = tile * VT;
     const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
-    const size_t tok0 = seq * size_t(a.N);
+    const SeqSpan sp = seq_span(int(seq), a.H, a.N, a.L, a.cu);
+    const size_t tok0 = sp.base;
+    const int len = sp.len;
 
     // initial state tile
     for (int idx = tid; idx < DK * VT; idx += NT) {
@@ -81,10 +85,10 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
         for (int i = tid; i < DK; i += NT) sz[i] = a.z0 ? a.z0[seq * DK + i] : 0.f;
 
     const int r_me = tid / VT, c_me = tid % VT;  // (row, column) of this thread's output
-    const int nchunks = (a.N + C - 1) / C;
+    const int nchunks = (len + C - 1) / C;
     for (int ch = 0; ch < nchunks; ++ch) {
         const int t0 = ch * C;
-        const int n = min(C, a.N - t0);
+        const int n = min(C, len - t0);
         __syncthreads();  // previous chunk's readers of sQ/sK/sV/sS are done
         for (int idx = tid; idx < C * DK; idx += NT) {
             const int r = idx / DK, i = idx % DK;
@@ -289,7 +293,7 @@ __global__ void state_init_kernel(const float* S0, const float* z0, float* S, fl
 
 hipError_t launch_prefill_valu(const Problem& p) {
     ValuArgs a{p.q, p.k, p.v, p.g, p.beta, p.S0, p.z0, p.o, p.S, p.z, p.N, 1, p.eps,
-               p.io_bf16, p.gate_bf16};
+               p.io_bf16, p.gate_bf16, p.cu, p.H, p.L};
     switch (p.variant) {
         case LA_KATH: return dispatch_dk<LA_KATH>(p, a);
         case LA_GLA: return dispatch_dk<LA_GLA>(p, a);

@@ -127,6 +127,34 @@ int la_prefill(const la_desc* d, const void* q, const void* k, const void* v,
                void* o, float* S_final, float* z_final,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Variable-length batch. The implementation checklist of "状态空间与线性注意力" asks
+ * whether sequence resets and padding positions update the state, and its failure modes
+ * name state carried across request boundaries; here sequences are packed (no padding
+ * is stored) and the state restarts at every boundary. nseq
+ * sequences concatenated along the token axis of one [1, H, N, d] layout. Sequence s
+ * occupies tokens cu_seqlens[s] .. cu_seqlens[s + 1] - 1 of every head, starts from
+ * S0[s] (z0[s]) or zeros, and ends in S_final[s] (z_final[s]): the state resets at
+ * every boundary, and the result for each sequence is that of la_prefill on it alone.
+ *   d->B must be 1; d->N is the total token count; q, k, v, o, g, beta as in la_prefill
+ *   with B = 1.
+ *   cu_seqlens   device int32 [nseq + 1], nondecreasing, cu_seqlens[0] = 0,
+ *                cu_seqlens[nseq] <= N; 4-byte aligned. Read only by the kernels: the
+ *                host does not check its contents. Offsets outside [0, N] are clamped
+ *                and lengths capped at max_seqlen, so no access leaves the buffers, but
+ *                the results for such values are unspecified.
+ *   max_seqlen   host value >= every sequence length, <= N; sizes the launch and the
+ *                workspace.
+ *   S0, S_final  [nseq, H, d_k, d_v] fp32; z0, z_final [nseq, H, d_k] fp32 (LA_KATH).
+ *   workspace    at least la_prefill_varlen_workspace_size bytes (as for la_prefill).
+ * Errors as for la_prefill; nseq = 0 does nothing. */
+int la_prefill_varlen_workspace_size(const la_desc* d, int32_t nseq, int32_t max_seqlen,
+                                     size_t* bytes);
+int la_prefill_varlen(const la_desc* d, int32_t nseq, const int32_t* cu_seqlens,
+                      int32_t max_seqlen, const void* q, const void* k, const void* v,
+                      const void* g, const void* beta, const float* S0, const float* z0, void* o,
+                      float* S_final, float* z_final, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
 /* One decode step, in place: the per-token step of "Linear / RNN 路线", section 2.1,
  * applied to the carried state; the decode carry of "线性注意力与 SSM", section 01, is
  * the final recurrent state only, so the cost of a step does not depend on how many

@@ -241,3 +241,27 @@ def test_empty_batch_is_noop(lib):
     d = good("gdn", B=2, H=0, N=1)
     assert lib.la_decode_step(ctypes.byref(d), None, None, None, None, None, None, None, None,
                               None) == bd.LA_OK
+
+
+@pytest.mark.parametrize("case", ["B_not_1", "max_over_N", "negative_nseq", "null_cu", "misaligned_cu",
+                                  "S_overlaps_cu"])
+def test_prefill_varlen_rejects(lib, case):
+    d = good("gdn", B=1, N=40)
+    p = ptrs("gdn")
+    nseq, cu, maxlen = 3, addr(5), 20
+    if case == "B_not_1":
+        d.B = 2
+    elif case == "max_over_N":
+        maxlen = 41
+    elif case == "negative_nseq":
+        nseq = -1
+    elif case == "null_cu":
+        cu = None
+    elif case == "misaligned_cu":
+        cu = addr(5, 2)
+    elif case == "S_overlaps_cu":
+        cu = addr(8, 16)
+    rc = lib.la_prefill_varlen(ctypes.byref(d), nseq, cu, maxlen, p["q"], p["k"], p["v"],
+                               p.get("g"), p.get("beta"), None, None, p["o"], p["S"], None,
+                               None, 0, None)
+    assert rc == bd.LA_ERR_INVALID, (case, rc)
