@@ -203,6 +203,55 @@ def bench_prefill(name, steps, warmup, rotate, torch, bd, W, device, stream, gra
     return rec, case
 
 
+def bench_varlen(name, steps, warmup, torch, bd, W, device, stream):
+    """Packed variable-length prefill: sum of the sequence lengths per second."""
+    import ctypes
+    wl, inp, cu, lengths = W.make_varlen_inputs(name)
+    log(f"varlen {name}: {len(lengths)} sequences, {int(cu[-1])} tokens per head")
+    sets = [{k: to_dev(v, torch, device) for k, v in inp.dev.items()}]
+    sets.append({k: torch.roll(v, shifts=97, dims=2).contiguous() for k, v in sets[0].items()})
+    cu_t = torch.from_numpy(cu).to(device)
+    nseq, maxlen = len(lengths), int(lengths.max())
+    io = bd.LA_BF16 if wl.io == "bf16" else bd.LA_F32
+    desc = bd.make_desc(wl.variant, 1, wl.H, wl.N, wl.dk, wl.dv, io, io, wl.eps)
+    lib = bd.load()
+    n = ctypes.c_size_t(0)
+    rc = lib.la_prefill_varlen_workspace_size(ctypes.byref(desc), nseq, maxlen, ctypes.byref(n))
+    if rc != 0:
+        raise bd.LinAttnError(rc, "la_prefill_varlen_workspace_size")
+    ws = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=device)
+    dt = torch.bfloat16 if wl.io == "bf16" else torch.float32
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    args = []
+    for s in sets:
+        o = torch.empty((1, wl.H, wl.N, wl.dv), dtype=dt, device=device)
+        S = torch.empty((nseq, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=device)
+        args.append(((P(s["q"]), P(s["k"]), P(s["v"]), P(s.get("g")), P(s.get("beta")), None, None,
+                      P(o), P(S), None, P(ws) if n.value else None, int(n.value)), o))
+    pd = ctypes.byref(desc)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    pcu = P(cu_t)
+
+    def fn(i):
+        a = args[i % len(args)][0]
+        rc = lib.la_prefill_varlen(pd, nseq, pcu, maxlen, *a, sh)
+        if rc != 0:
+            raise bd.LinAttnError(rc, "la_prefill_varlen")
+
+    ms = time_eager(fn, steps, warmup, torch, stream)
+    tokens = int(cu[-1])
+    per = W.algorithmic_bytes_per_token_head(wl)
+    byts = tokens * wl.H * per + nseq * wl.H * wl.dk * wl.dv * 4
+    flops = W.algorithmic_flops(wl)   # the packed layout's token count, B = 1
+    s = ms / 1e3
+    gbs = byts / s / 1e9
+    return {"workload": name, "ms": ms, "sequences": nseq, "tokens": tokens,
+            "length_min": int(lengths.min()), "length_max": maxlen,
+            "Mtok_per_s": tokens / s / 1e6, "GB_per_s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+            "TFLOP_per_s": flops / s / 1e12, "mfma_frac": flops / s / 1e12 / PEAK_BF16_TFLOPS,
+            "finite": bool(torch.isfinite(args[0][1].float()).all().item())}
+
+
 def bench_decode(name, steps, warmup, torch, bd, W, device, stream):
     import ctypes
     wl = W.WORKLOADS[name]
@@ -278,6 +327,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the packed variable-length lines (they launch the same kernels as "
+                         "the dense workloads, which per-kernel counter passes must not mix)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -332,6 +384,10 @@ def main():
                                  stream, graph=use_graph)
             results[name] = r
             del c
+            torch.cuda.empty_cache()
+        for name in ([] if args.no_varlen else W.VARLEN):
+            results[name] = bench_varlen(name, max(20, args.steps // 8), 5, torch, bd, W, device,
+                                         stream)
             torch.cuda.empty_cache()
         for name in ("decode_gdn_256x32_d128", "decode_gla_256x32_d128", "decode_kda_256x32_d128"):
             results[name] = bench_decode(name, 1000, 10, torch, bd, W, device, stream)

@@ -98,10 +98,12 @@ int check_desc(const la_desc* d, bool decode) {
 
 // Resolve path, chunk and segments for a prefill over nseq sequences per head whose
 // longest has max_len tokens (a dense batch: nseq = B, max_len = N, cu = null).
-int plan_prefill(const la_desc& d, Problem& p, int nseq, int max_len, const int32_t* cu) {
+int plan_prefill(const la_desc& d, Problem& p, int nseq, int max_len, const int32_t* cu,
+                 bool packed) {
     p.B = nseq; p.H = d.H; p.N = d.N; p.dk = d.dk; p.dv = d.dv;
     p.L = max_len;
     p.cu = cu;
+    p.packed = packed;
     p.variant = d.variant;
     p.io_bf16 = d.io_dtype == LA_BF16;
     p.gate_bf16 = d.gate_dtype == LA_BF16;
@@ -163,7 +165,7 @@ int la_prefill_workspace_size(const la_desc* d, size_t* bytes) {
     if (rc != LA_OK) return rc;
     if (!bytes) return LA_ERR_INVALID;
     Problem p;
-    rc = plan_prefill(*d, p, d->B, d->N, nullptr);
+    rc = plan_prefill(*d, p, d->B, d->N, nullptr, false);
     if (rc != LA_OK) return rc;
     *bytes = workspace_for(p);
     return LA_OK;
@@ -175,7 +177,7 @@ int la_prefill_varlen_workspace_size(const la_desc* d, int32_t nseq, int32_t max
     if (rc != LA_OK) return rc;
     if (!bytes || d->B != 1 || nseq < 0 || max_seqlen < 0 || max_seqlen > d->N) return LA_ERR_INVALID;
     Problem p;
-    rc = plan_prefill(*d, p, nseq, max_seqlen, nullptr);
+    rc = plan_prefill(*d, p, nseq, max_seqlen, nullptr, true);
     if (rc != LA_OK) return rc;
     *bytes = workspace_for(p);
     return LA_OK;
@@ -193,7 +195,7 @@ int prefill_impl(const la_desc* d, int nseq, const int32_t* cu, int max_len, con
     int rc = check_desc(d, false);
     if (rc != LA_OK) return rc;
     Problem p;
-    rc = plan_prefill(*d, p, nseq, max_len, cu);
+    rc = plan_prefill(*d, p, nseq, max_len, cu, cu != nullptr);
     if (rc != LA_OK) return rc;
     const bool kath = d->variant == LA_KATH, gla = d->variant == LA_GLA,
                gdn = d->variant == LA_GDN, kda = d->variant == LA_KDA;

@@ -25,6 +25,7 @@ struct Problem {
     // dense batch), cu the packed batch's cumulative lengths (device, B + 1) or null.
     int L = 0;
     const int32_t* cu = nullptr;
+    bool packed = false;      // a packed variable-length batch (set for its size query too)
     const void *q = nullptr, *k = nullptr, *v = nullptr, *g = nullptr, *beta = nullptr;
     const float *S0 = nullptr, *z0 = nullptr;
     void* o = nullptr;

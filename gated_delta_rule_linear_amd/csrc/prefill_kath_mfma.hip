@@ -515,6 +515,12 @@ int kath_mfma_auto_segments(const Problem& p) {
     const size_t nchunks = size_t((p.L + C - 1) / C);
     const size_t units = nseq * ntiles;
     size_t want = (256 + units - 1) / units;
+    // a packed batch: cut the longest sequence into pieces about the mean length, so that
+    // it does not outlast the others (B sequences share the N tokens of each head)
+    if (p.packed && p.N > 0) {
+        const size_t even = (size_t(p.L) * size_t(p.B) + size_t(p.N) - 1) / size_t(p.N);
+        if (even > want) want = even;
+    }
     const size_t cap = nchunks / 4;
     if (want > cap) want = cap;
     return want < 1 ? 1 : int(want);

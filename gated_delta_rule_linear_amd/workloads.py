@@ -145,6 +145,33 @@ WORKLOADS = {
 
 KDA_LOG_DECAY_MIN = -5.0   # g_min of the bounded log-decay
 
+# Packed variable-length batches: a base workload (its H, d, dtypes and gate recipe),
+# the number of sequences, and lengths drawn log-uniformly in [lo, hi] (seeded): a
+# serving-like mix of short and long prompts.
+VARLEN = {
+    "gla_varlen_bf16_h8_d128": dict(base="gla_bf16_b2h8_n2048_d128", nseq=16, lo=64, hi=4096,
+                                    seed=21),
+    "gdn_varlen_bf16_h16_d128": dict(base="gdn_bf16_b4h16_n8192_d128", nseq=64, lo=256, hi=16384,
+                                     seed=22),
+}
+
+
+def varlen_lengths(nseq: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Sequence lengths, log-uniform in [lo, hi] (int32)."""
+    rng = np.random.default_rng(seed)
+    return np.exp(rng.uniform(np.log(lo), np.log(hi), nseq)).astype(np.int32)
+
+
+def make_varlen_inputs(name: str):
+    """(Workload of the packed layout [1, H, total, d], Inputs, cu_seqlens int32, lengths)."""
+    spec = VARLEN[name]
+    base = WORKLOADS[spec["base"]]
+    lengths = varlen_lengths(spec["nseq"], spec["lo"], spec["hi"], spec["seed"])
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    wl = base.with_(name=name, B=1, N=int(cu[-1]), seed=spec["seed"])
+    return wl, make_inputs(wl), cu, lengths
+
+
 DECODE_STATE_STD = 0.02   # decode state S ~ N(0, 0.02^2): std 0.02 (torch normal(mean, std))
 DECODE_POOL = 8           # distinct token sets cycled through by repeated decode steps
 

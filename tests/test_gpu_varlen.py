@@ -106,3 +106,24 @@ def test_varlen_all_empty_copies_state():
                                 cu_seqlens=cu_t, max_seqlen=0, S0=S0)
     torch.cuda.synchronize()
     assert torch.equal(S, S0)
+
+
+@pytest.mark.parametrize("name", list(W.VARLEN))
+def test_varlen_workload_sampled(name):
+    """The benchmark's packed batches at full size; sampled sequences against the oracle."""
+    wl, inp, cu, lengths = W.make_varlen_inputs(name)
+    d = inputs_to_device(inp)
+    cu_t = torch.from_numpy(cu).cuda()
+    banner(f"varlen workload {name}: {len(lengths)} sequences, {int(cu[-1])} tokens")
+    o, S, _ = bd.prefill_varlen(d["q"], d["k"], d["v"], d.get("g"), d.get("beta"),
+                                variant=wl.variant, cu_seqlens=cu_t, max_seqlen=int(lengths.max()))
+    torch.cuda.synchronize()
+    e = inp.exact
+    for i in (0, int(np.argmax(lengths)), len(lengths) - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        sl = lambda x: None if x is None else x[:, :, a:b]
+        o_ref, S_ref, _ = oracle.prefill(wl.variant, sl(e["q"]), sl(e["k"]), sl(e["v"]),
+                                         sl(e.get("g")), sl(e.get("beta")), eps=wl.eps)
+        eo, eS = relerr(o[:, :, a:b], o_ref), relerr(S[i:i + 1], S_ref)
+        print(name, i, b - a, eo, eS, flush=True)
+        assert eo <= TOL["bf16"] and eS <= TOL["bf16"], (i, eo, eS)
