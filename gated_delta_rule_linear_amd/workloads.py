@@ -24,6 +24,12 @@ Gate parameterisations (input distributions, per workload):
     "状态空间与线性注意力" section KDA, alpha = exp(g_min sigmoid(e^A z)) with
     g_min = -5 and A = 0 (the page's own example), z ~ N(0, 1), so alpha lies
     in (e^-5, 1); beta = sigmoid(w), w ~ N(0, 1) per (token, head);
+  * SSD (Mamba-2, one decay per token and head, "Linear / RNN 路线" sections 3.6
+    and 4.1): a = exp(Delta A_h) with A_h = -(1 + h mod 16) (the page's A =
+    -arange(1, ..) initialisation, one value per head) and Delta = softplus(u),
+    u ~ N(-3, 1) per (token, head); q = C and k = B ~ N(0, 1/d_k), v = Delta x
+    with x ~ N(0, 1) (the step scales the written input), so a lies in about
+    (0.4, 1);
   * extra gate kinds for carry-sensitive tests: "slow" (alpha or g =
     exp(logsigmoid(u) / 16), about 0.95; KDA: exp(-5 sigmoid(z - 6)), about
     0.99), "ones" (g = 1 or alpha = 1), "beta0" (beta = 0), "beta1" (beta = 1).
@@ -84,7 +90,7 @@ def _sigmoid(u):
 @dataclass(frozen=True)
 class Workload:
     name: str
-    variant: str            # "kath" | "gla" | "gdn" | "kda"
+    variant: str            # "kath" | "gla" | "gdn" | "kda" | "ssd"
     B: int
     H: int
     N: int
@@ -129,6 +135,11 @@ WORKLOADS = {
         "kda_bf16_b4h16_n8192_d128", "kda", 4, 16, 8192, 128, 128, "bf16", "bf16", seed=6,
         l2norm_qk=True, description="Kimi Delta Attention forward, B=4 H=16 N=8192 d=128, bf16, "
                                     "q/k L2-normalized, bounded per-channel retention"),
+    "ssd_bf16_b2h32_n4096_dk128_dv64": Workload(
+        "ssd_bf16_b2h32_n4096_dk128_dv64", "ssd", 2, 32, 4096, 128, 64, "bf16", "bf16", seed=8,
+        qk_scale=1.0 / np.sqrt(128.0),
+        description="Mamba-2 SSD forward (scalar decay per token and head), B=2 H=32 N=4096 "
+                    "d_state=128 head dim 64, bf16"),
     "decode_gdn_256x32_d128": Workload(
         "decode_gdn_256x32_d128", "gdn", 256, 32, 1, 128, 128, "bf16", "bf16", seed=5,
         l2norm_qk=True, decode=True,
@@ -141,7 +152,14 @@ WORKLOADS = {
         "decode_kda_256x32_d128", "kda", 256, 32, 1, 128, 128, "bf16", "bf16", seed=7,
         l2norm_qk=True, decode=True,
         description="KDA decode step, 256 sequences x 32 heads, d=128, fp32 state"),
+    "decode_ssd_256x64_dk128_dv64": Workload(
+        "decode_ssd_256x64_dk128_dv64", "ssd", 256, 64, 1, 128, 64, "bf16", "bf16", seed=9,
+        qk_scale=1.0 / np.sqrt(128.0), decode=True,
+        description="SSD decode step, 256 sequences x 64 heads, d_state=128 head dim 64, "
+                    "fp32 state"),
 }
+
+SSD_DT_MEAN = -3.0   # Delta = softplus(u), u ~ N(SSD_DT_MEAN, 1)
 
 KDA_LOG_DECAY_MIN = -5.0   # g_min of the bounded log-decay
 
@@ -247,6 +265,22 @@ def _draw_gates(rng, wl: Workload, shape_tok):
             raise ValueError(kind)
         out["g"] = alpha
         out["beta"] = beta
+    elif wl.variant == "ssd":
+        u = rng.standard_normal((B, H, N)) + SSD_DT_MEAN
+        delta = np.logaddexp(0.0, u)
+        A_h = -(1.0 + (np.arange(H) % 16))[None, :, None]
+        if kind == "default":
+            a = np.exp(delta * A_h)
+        elif kind == "slow":
+            a = np.exp(delta * A_h / 16.0)
+        elif kind == "ones":
+            a = np.ones_like(delta)
+        elif kind == "fast":
+            a = np.exp(delta * A_h * 16.0)
+        else:
+            raise ValueError(kind)
+        out["g"] = a
+        out["_v_step"] = delta   # v = Delta x: the step scales the written input
     return out
 
 
@@ -272,6 +306,8 @@ def make_inputs(wl: Workload | str, *, with_state: bool = False, state_std: floa
         k = k / np.linalg.norm(k, axis=-1, keepdims=True)
     raw = {"q": q, "k": k, "v": v}
     gates = _draw_gates(rng, wl, (B, H, N))
+    if "_v_step" in gates:
+        raw["v"] = raw["v"] * gates.pop("_v_step")[..., None]
     dev, exact = {}, {}
     for name, arr in raw.items():
         dev[name], exact[name] = round_to(arr, wl.io)
@@ -330,6 +366,8 @@ def algorithmic_bytes_per_token_head(wl: Workload) -> int:
         b += 2 * gsz
     elif wl.variant == "kda":
         b += wl.dk * gsz + gsz
+    elif wl.variant == "ssd":
+        b += gsz
     return b
 
 
@@ -357,12 +395,89 @@ def algorithmic_flops(wl: Workload, chunk: int = 64) -> int:
     """
     dk, dv, C = wl.dk, wl.dv, chunk
     if wl.decode:
-        per = {"gla": 5, "gdn": 7, "kda": 7, "kath": 4}[wl.variant] * dk * dv
+        per = {"gla": 5, "gdn": 7, "kda": 7, "kath": 4, "ssd": 5}[wl.variant] * dk * dv
         return wl.B * wl.H * per
-    if wl.variant == "gla":
+    if wl.variant in ("gla", "ssd"):
         per = 2 * C * dk + 2 * C * dv + 4 * dk * dv
     elif wl.variant == "kath":
         per = 2 * C * dk + 2 * C * (dv + 1) + 4 * dk * dv + 3 * dk
     else:
         per = 6 * C * dk + 4 * C * dv + 6 * dk * dv + (C * C) // 3
     return wl.token_heads * per
+
+
+# ---------------------------------------------------------------------------
+# Selective scan (Mamba-1)
+# ---------------------------------------------------------------------------
+# Recipe ("Linear / RNN 路线" section 3.6, the simplified block's parameters):
+#   * A = -arange(1, n + 1) for every channel (the block's initialisation, fp32);
+#   * dt ~ N(0, 0.5^2) per (token, channel) and dt_bias ~ U(-1, 1) per channel, the
+#     step being Delta = softplus(dt + dt_bias) inside the scan (the block's dt_proj
+#     output with its bias split off);
+#   * B, C ~ N(0, 1) per (token, state entry), x ~ N(0, 1) per (token, channel);
+#   * D = 1 per channel (the skip at its usual initialisation);
+#   * drawn in the order dt, dt_bias, B, C, x (then h0 ~ N(0, 0.5^2) when asked for),
+#     rounded like the other inputs: dt, B, C, x to the storage dtype, A, D, dt_bias
+#     and h0 to fp32.
+
+
+@dataclass(frozen=True)
+class SelScan:
+    name: str
+    Bt: int       # batch rows
+    T: int        # tokens per row
+    D: int        # channels (the block's inner width)
+    n: int        # state entries per channel
+    io: str       # storage dtype of dt, B, C, x, y
+    seed: int
+    description: str = field(default="", compare=False)
+
+    def with_(self, **kw) -> "SelScan":
+        return replace(self, **kw)
+
+
+SELSCAN = {
+    "selscan_bf16_b2_t4096_d2048_n128": SelScan(
+        "selscan_bf16_b2_t4096_d2048_n128", 2, 4096, 2048, 128, "bf16", seed=11,
+        description="Mamba-1 selective scan, 2 rows x 4096 tokens, 2048 channels, "
+                    "128 state entries per channel, bf16 inputs, fp32 state"),
+    "selscan_bf16_b2_t4096_d2048_n16": SelScan(
+        "selscan_bf16_b2_t4096_d2048_n16", 2, 4096, 2048, 16, "bf16", seed=12,
+        description="Mamba-1 selective scan with 16 state entries per channel"),
+}
+
+
+def make_selscan_inputs(wl: SelScan | str, *, with_state: bool = False, seed: int | None = None,
+                        T: int | None = None):
+    """(dev, exact) dicts for a selective-scan workload: dt, dt_bias, A, Bm, Cm, x, Dskip
+    (and h0). ``dev`` holds the stored arrays (bf16 bits or fp32), ``exact`` their fp64
+    values."""
+    if isinstance(wl, str):
+        wl = SELSCAN[wl]
+    if T is not None:
+        wl = wl.with_(T=T)
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    Bt, T, D, n = wl.Bt, wl.T, wl.D, wl.n
+    raw_io = {"dt": rng.normal(0.0, 0.5, (Bt, T, D))}
+    raw_f32 = {"dt_bias": rng.uniform(-1.0, 1.0, D)}
+    raw_io["Bm"] = rng.standard_normal((Bt, T, n))
+    raw_io["Cm"] = rng.standard_normal((Bt, T, n))
+    raw_io["x"] = rng.standard_normal((Bt, T, D))
+    raw_f32["A"] = -np.broadcast_to(np.arange(1.0, n + 1.0), (D, n)).copy()
+    raw_f32["Dskip"] = np.ones(D)
+    if with_state:
+        raw_f32["h0"] = rng.normal(0.0, 0.5, (Bt, D, n))
+    dev, exact = {}, {}
+    for k_, a in raw_io.items():
+        dev[k_], exact[k_] = round_to(a, wl.io)
+    for k_, a in raw_f32.items():
+        dev[k_], exact[k_] = round_to(a, "f32")
+    return dev, exact
+
+
+def selscan_algorithmic_bytes(wl: SelScan) -> int:
+    """Minimum bytes of one scan: dt, x read and y written per (token, channel), B and C
+    per (token, state entry), A, D and dt_bias once, the final state written once."""
+    isz = 4 if wl.io == "f32" else 2
+    return (wl.Bt * wl.T * (3 * wl.D + 2 * wl.n) * isz + wl.D * (wl.n + 2) * 4
+            + wl.Bt * wl.D * wl.n * 4)

@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the causal linear-attention state recurrence.
+"""fp64 CPU oracle for the causal linear-attention state recurrence and the selective scan.
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg are the only callers. The GPU library never imports this
@@ -28,8 +28,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-KATH, GLA, GDN, KDA = 0, 1, 2, 3
-VARIANTS = {"kath": KATH, "gla": GLA, "gdn": GDN, "kda": KDA}
+KATH, GLA, GDN, KDA, SSD = 0, 1, 2, 3, 4
+VARIANTS = {"kath": KATH, "gla": GLA, "gdn": GDN, "kda": KDA, "ssd": SSD}
 
 
 class _Counts(ctypes.Structure):
@@ -80,6 +80,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.oracle_decode_step.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp, ctypes.c_double,
                                        dp, dp, dp, i]
     lib.oracle_decode_step.restype = i
+    lib.oracle_selective_scan.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp, dp, i, dp, dp, dp,
+                                          i]
+    lib.oracle_selective_scan.restype = i
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i
     _lib_cache[path] = lib
@@ -107,7 +110,7 @@ def prefill(variant, q, k, v, g=None, beta=None, S0=None, z0=None, eps=1e-6,
     """Run the token recurrence over whole sequences.
 
     q, k: [B,H,N,dk]; v: [B,H,N,dv]; g: GLA [B,H,N,dk], GDN alpha [B,H,N] or KDA
-    alpha [B,H,N,dk]; beta: GDN / KDA [B,H,N]; S0: [B,H,dk,dv] or None; z0:
+    alpha [B,H,N,dk] or SSD decay [B,H,N]; beta: GDN / KDA [B,H,N]; S0: [B,H,dk,dv] or None; z0:
     [B,H,dk] or None (KATH).
     Returns (o [B,H,N,dv], S [B,H,dk,dv], z [B,H,dk] or None[, Counts]).
     """
@@ -125,6 +128,8 @@ def prefill(variant, q, k, v, g=None, beta=None, S0=None, z0=None, eps=1e-6,
     if vt == KDA:
         assert g is not None and g.shape == (B, H, N, dk)
         assert beta is not None and beta.shape == (B, H, N)
+    if vt == SSD:
+        assert g is not None and g.shape == (B, H, N)
     if S0 is not None:
         assert S0.shape == (B, H, dk, dv)
     if z0 is not None:
@@ -167,6 +172,35 @@ def decode_step(variant, q, k, v, S, g=None, beta=None, z=None, eps=1e-6, thread
     if rc != 0:
         raise ValueError("oracle_decode_step rejected its arguments")
     return o
+
+
+def selective_scan(dt, A, Bm, Cm, x, Dskip=None, dt_bias=None, dt_softplus: bool = False,
+                   h0=None, threads: int = 0, lib_path: str | None = None):
+    """Mamba-1 selective scan over whole sequences (equations in the header of oracle.c).
+
+    dt, x: [Bt,T,D]; A: [D,n]; Bm, Cm: [Bt,T,n]; Dskip, dt_bias: [D] or None;
+    h0: [Bt,D,n] or None. Returns (y [Bt,T,D], hT [Bt,D,n]).
+    """
+    lib = load(lib_path)
+    dt, A, Bm, Cm, x, Dskip, dt_bias, h0 = map(_f64, (dt, A, Bm, Cm, x, Dskip, dt_bias, h0))
+    Bt, T, D = x.shape
+    n = A.shape[1]
+    assert dt.shape == (Bt, T, D) and A.shape == (D, n)
+    assert Bm.shape == (Bt, T, n) and Cm.shape == (Bt, T, n)
+    if Dskip is not None:
+        assert Dskip.shape == (D,)
+    if dt_bias is not None:
+        assert dt_bias.shape == (D,)
+    if h0 is not None:
+        assert h0.shape == (Bt, D, n)
+    y = np.zeros((Bt, T, D), np.float64)
+    hT = np.zeros((Bt, D, n), np.float64)
+    rc = lib.oracle_selective_scan(Bt, T, D, n, _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(x),
+                                   _ptr(Dskip), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(h0),
+                                   _ptr(y), _ptr(hT), int(threads))
+    if rc != 0:
+        raise ValueError("oracle_selective_scan rejected its arguments")
+    return y, hT
 
 
 def max_threads(lib_path: str | None = None) -> int:

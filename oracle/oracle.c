@@ -25,6 +25,10 @@
  *        and notes that the write equals a correction by v_t - a_t S_{t-1} k_t.
  *        Key-major this is S_t = a_t S_{t-1} + k_t u_t^T with
  *          u_t = b_t (v_t - a_t S_{t-1}^T k_t),   o_t = S_t^T q_t.
+ *  SSD   "Linear / RNN 路线", sections 3.6 and 4.1 (Mamba-2): the selective state
+ *        space recurrence h_t = A_t h_{t-1} + B_t x_t, y_t = C_t h_t with a scalar
+ *        A_t per head, unrolled into linear attention with k = B, v = x, q = C:
+ *          S_t = a_t S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t.
  *  KDA   "状态空间与线性注意力" (wineandchord), section KDA: a retention per key
  *        channel a_t in (0,1)^{d_k} decays the old state first, then the current
  *        key asks what the decayed state already predicts and writes the error:
@@ -33,6 +37,16 @@
  *
  * Every variant reads the state after the token's update (the post-update
  * read of the output equations on every page).
+ *
+ * Selective scan (Mamba-1, S6), a separate entry point: "Linear / RNN 路线"
+ * section 3.5 (boxed discretisation) and the Mamba2Block forward of section 3.6;
+ * "状态空间与线性注意力" sections Selective SSM and 卷积与递推的等价 (the D x_t skip).
+ * For each batch row b and channel d, a state h_d in R^{n} (one entry per state
+ * dimension), with
+ *     Delta_t = softplus(dt_t + bias_d)    (or dt_t itself when no softplus is asked)
+ *     h_d <- exp(Delta_t A_{d,i}) h_{d,i} + Delta_t B_{t,i} x_{t,d}     for each i < n
+ *     y_{t,d} = sum_i C_{t,i} h_{d,i} + D_d x_{t,d}.
+ * B_t and C_t are shared by all channels of a row; A is fixed per (channel, state).
  *
  * Decode is the same per-token body applied once, in place.
  *
@@ -48,7 +62,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_KATH = 0, OR_GLA = 1, OR_GDN = 2, OR_KDA = 3 };
+enum { OR_KATH = 0, OR_GLA = 1, OR_GDN = 2, OR_KDA = 3, OR_SSD = 4 };
 
 typedef struct {
     uint64_t state_update_macs; /* multiply-adds that write S */
@@ -102,6 +116,19 @@ static void token_step(int variant, int dk, int dv, const double *q, const doubl
             o[j] = acc;
         }
         c->state_read_macs += (uint64_t)dk * (uint64_t)dv;
+    } else if (variant == OR_SSD) { /* g[0]: the token's scalar decay */
+        const double a = g[0];
+        for (i = 0; i < dk; ++i) {
+            for (j = 0; j < dv; ++j)
+                S[(size_t)i * dv + j] = a * S[(size_t)i * dv + j] + k[i] * v[j];
+            c->state_update_macs += (uint64_t)dv;
+        }
+        for (j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (i = 0; i < dk; ++i) acc += q[i] * S[(size_t)i * dv + j];
+            o[j] = acc;
+        }
+        c->state_read_macs += (uint64_t)dk * (uint64_t)dv;
     } else if (variant == OR_KDA) { /* g: retention per key channel */
         double *u = work; /* dv */
         for (i = 0; i < dk; ++i)
@@ -146,7 +173,7 @@ static void token_step(int variant, int dk, int dv, const double *q, const doubl
 
 static int check_args(int variant, int B, int H, int N, int dk, int dv)
 {
-    if (variant < OR_KATH || variant > OR_KDA) return 1;
+    if (variant < OR_KATH || variant > OR_SSD) return 1;
     if (B < 0 || H < 0 || N < 0 || dk < 1 || dv < 1) return 1;
     return 0;
 }
@@ -154,7 +181,8 @@ static int check_args(int variant, int B, int H, int N, int dk, int dv)
 /*
  * Whole-sequence forward.
  *   q, k: [B,H,N,dk]   v: [B,H,N,dv]
- *   g:    GLA [B,H,N,dk]; GDN alpha [B,H,N]; KDA alpha [B,H,N,dk]; KATH unused (may be NULL)
+ *   g:    GLA [B,H,N,dk]; GDN alpha [B,H,N]; KDA alpha [B,H,N,dk]; SSD decay [B,H,N];
+ *         KATH unused (may be NULL)
  *   beta: GDN and KDA [B,H,N]; otherwise unused
  *   S0:   [B,H,dk,dv] or NULL (zeros);   z0: [B,H,dk] or NULL (zeros), KATH only
  *   o:    [B,H,N,dv] out;  S: [B,H,dk,dv] out (final state);  z: [B,H,dk] out (KATH, may be NULL otherwise)
@@ -204,6 +232,7 @@ int oracle_prefill(int variant, int B, int H, int N, int dk, int dv,
                 if (variant == OR_GLA) gt = g + tok * dk;
                 if (variant == OR_GDN) { gt = g + tok; bt = beta[tok]; }
                 if (variant == OR_KDA) { gt = g + tok * dk; bt = beta[tok]; }
+                if (variant == OR_SSD) gt = g + tok;
                 token_step(variant, dk, dv, q + tok * dk, k + tok * dk, v + tok * dv, gt, bt,
                            eps, Sh, zh, o + tok * dv, work, &c);
             }
@@ -224,7 +253,8 @@ int oracle_prefill(int variant, int B, int H, int N, int dk, int dv,
 
 /*
  * One decode step for B*H independent states, in place.
- *   q, k: [B,H,dk]  v: [B,H,dv]  g: GLA [B,H,dk] / GDN alpha [B,H] / KDA alpha [B,H,dk]
+ *   q, k: [B,H,dk]  v: [B,H,dv]  g: GLA [B,H,dk] / GDN alpha [B,H] / KDA alpha [B,H,dk] /
+ *   SSD decay [B,H]
  *   beta: GDN and KDA [B,H]
  *   S: [B,H,dk,dv] in/out;  z: [B,H,dk] in/out (KATH);  o: [B,H,dv] out.
  */
@@ -256,12 +286,63 @@ int oracle_decode_step(int variant, int B, int H, int dk, int dv,
             if (variant == OR_GLA) gt = g + (size_t)seq * dk;
             if (variant == OR_GDN) { gt = g + seq; bt = beta[seq]; }
             if (variant == OR_KDA) { gt = g + (size_t)seq * dk; bt = beta[seq]; }
+            if (variant == OR_SSD) gt = g + seq;
             token_step(variant, dk, dv, q + (size_t)seq * dk, k + (size_t)seq * dk,
                        v + (size_t)seq * dv, gt, bt, eps, S + (size_t)seq * dk * dv,
                        variant == OR_KATH ? z + (size_t)seq * dk : NULL,
                        o + (size_t)seq * dv, work, &c);
         }
         free(work);
+    }
+    return 0;
+}
+
+static double softplus(double u) { return u > 30.0 ? u : log1p(exp(u)); }
+
+/*
+ * Selective scan over whole sequences (see the header for the equations).
+ *   dt, x: [Bt,T,D]   A: [D,n]   Bm, Cm: [Bt,T,n]
+ *   Dskip: [D] or NULL (no skip)   dt_bias: [D] or NULL (zero)   dt_softplus: 0 or 1
+ *   h0: [Bt,D,n] or NULL (zeros)
+ *   y: [Bt,T,D] out;   hT: [Bt,D,n] out (final state).
+ * Returns 0, or 1 on a bad argument.
+ */
+int oracle_selective_scan(int Bt, int T, int D, int n, const double *dt, const double *A,
+                          const double *Bm, const double *Cm, const double *x,
+                          const double *Dskip, const double *dt_bias, int dt_softplus,
+                          const double *h0, double *y, double *hT, int threads)
+{
+    long long row;
+    if (Bt < 0 || T < 0 || D < 1 || n < 1 || dt == NULL || A == NULL || Bm == NULL ||
+        Cm == NULL || x == NULL || y == NULL || hT == NULL)
+        return 1;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (row = 0; row < (long long)Bt * D; ++row) {
+        const long long b = row / D;
+        const int d = (int)(row % D);
+        double *h = hT + (size_t)row * n;
+        int t, i;
+        if (h0) memcpy(h, h0 + (size_t)row * n, sizeof(double) * (size_t)n);
+        else memset(h, 0, sizeof(double) * (size_t)n);
+        for (t = 0; t < T; ++t) {
+            const size_t tok = (size_t)b * T + t;
+            const double xt = x[tok * D + d];
+            double delta = dt[tok * D + d] + (dt_bias ? dt_bias[d] : 0.0);
+            double acc = 0.0;
+            if (dt_softplus) delta = softplus(delta);
+            for (i = 0; i < n; ++i) {
+                const double abar = exp(delta * A[(size_t)d * n + i]);
+                const double bbar = delta * Bm[tok * n + i];
+                h[i] = abar * h[i] + bbar * xt;
+            }
+            for (i = 0; i < n; ++i) acc += Cm[tok * n + i] * h[i];
+            y[tok * D + d] = acc + (Dskip ? Dskip[d] * xt : 0.0);
+        }
     }
     return 0;
 }

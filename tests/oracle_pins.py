@@ -63,6 +63,8 @@ def rand_case(variant, B=1, H=2, N=12, dk=5, dv=4, seed=0, with_state=True, unit
     elif variant == "kda":
         g = rng.uniform(0.5, 1.0, (B, H, N, dk))
         beta = rng.uniform(0.05, 0.95, (B, H, N))
+    elif variant == "ssd":
+        g = rng.uniform(0.5, 1.0, (B, H, N))
     S0 = rng.standard_normal((B, H, dk, dv)) * 0.7 if with_state else None
     z0 = (rng.uniform(0.5, 2.0, (B, H, dk)) if (with_state and variant == "kath") else None)
     return dict(q=q, k=k, v=v, g=g, beta=beta, S0=S0, z0=z0)
@@ -154,7 +156,7 @@ def _quad_delta(q, k, v, beta, S0, F):
 
 def pin_quadratic_form(lib=None):
     for variant, dk, dv in (("kath", 5, 3), ("gla", 5, 3), ("gdn", 4, 6), ("gdn", 6, 4),
-                            ("kda", 5, 3), ("kda", 3, 6)):
+                            ("kda", 5, 3), ("kda", 3, 6), ("ssd", 5, 3)):
         case = rand_case(variant, B=2, H=1, N=11, dk=dk, dv=dv, seed=7, with_state=True)
         eps = 0.3 if variant == "kath" else 1e-6
         o, S, z = run(variant, case, lib, eps=eps)
@@ -167,6 +169,10 @@ def pin_quadratic_form(lib=None):
             elif variant == "gla":
                 O_ref, S_ref = quad_gla(case["q"][sl], case["k"][sl], case["v"][sl],
                                         case["g"][sl], case["S0"][sl])
+            elif variant == "ssd":   # the semiseparable form with a scalar decay per token
+                O_ref, S_ref = quad_gla(case["q"][sl], case["k"][sl], case["v"][sl],
+                                        np.repeat(case["g"][sl][:, None], dk, axis=1),
+                                        case["S0"][sl])
             elif variant == "gdn":
                 O_ref, S_ref = quad_gdn(case["q"][sl], case["k"][sl], case["v"][sl],
                                         case["g"][sl], case["beta"][sl], case["S0"][sl])
@@ -178,7 +184,7 @@ def pin_quadratic_form(lib=None):
 
 
 def pin_split_invariance(lib=None):
-    for variant in ("kath", "gla", "gdn", "kda"):
+    for variant in ("kath", "gla", "gdn", "kda", "ssd"):
         case = rand_case(variant, B=1, H=3, N=23, dk=6, dv=5, seed=11, with_state=True)
         o, S, z = run(variant, case, lib)
         for m in (1, 7, 16, 22):
@@ -386,6 +392,18 @@ def pin_special_cases(lib=None):
     tt = np.arange(13)
     D = np.where(tt[:, None] >= tt[None, :], gam ** (tt[:, None] - tt[None, :]).clip(0), 0.0)
     assert rel(o[0, 0], ((Q @ K.T) * D) @ V) < 1e-12, "RetNet form"
+    # SSD with a constant decay: the same parallel form (Mamba-2's 1-semiseparable mask)
+    case = rand_case("ssd", B=1, H=1, N=13, dk=5, dv=4, seed=6, with_state=False)
+    case["g"] = np.full_like(case["g"], gam)
+    o, S, _ = run("ssd", case, lib)
+    assert rel(o[0, 0], ((Q @ K.T) * D) @ V) < 1e-12, "SSD constant decay vs RetNet form"
+    # SSD with its decay broadcast over the key dims is GLA, operation for operation
+    case = rand_case("ssd", B=1, H=2, N=17, dk=4, dv=3, seed=23, with_state=True)
+    o, S, _ = run("ssd", case, lib)
+    g_case = dict(case)
+    g_case["g"] = np.repeat(case["g"][..., None], 4, axis=-1)
+    og, Sg, _ = run("gla", g_case, lib)
+    assert np.array_equal(o, og) and np.array_equal(S, Sg), "SSD vs GLA with a broadcast gate"
     # KDA beta = 0: every channel of S0 decays by its own retention, nothing is written
     case = rand_case("kda", B=1, H=2, N=10, dk=4, dv=3, seed=19, with_state=True)
     case["beta"] = np.zeros_like(case["beta"])
@@ -407,7 +425,7 @@ def pin_special_cases(lib=None):
 
 
 def pin_causality(lib=None):
-    for variant in ("kath", "gla", "gdn", "kda"):
+    for variant in ("kath", "gla", "gdn", "kda", "ssd"):
         case = rand_case(variant, B=1, H=2, N=16, dk=4, dv=3, seed=13, with_state=True)
         o, _, _ = run(variant, case, lib)
         for tp in (0, 5, 15):
@@ -423,7 +441,7 @@ def pin_causality(lib=None):
 
 
 def pin_linearity(lib=None):
-    for variant in ("gla", "gdn", "kda"):
+    for variant in ("gla", "gdn", "kda", "ssd"):
         case = rand_case(variant, B=1, H=2, N=14, dk=5, dv=4, seed=17, with_state=False)
         rng = np.random.default_rng(1)
         v1, v2 = rng.standard_normal(case["v"].shape), rng.standard_normal(case["v"].shape)
@@ -438,7 +456,7 @@ def pin_linearity(lib=None):
 
 
 def pin_decode_matches_prefill(lib=None):
-    for variant in ("kath", "gla", "gdn", "kda"):
+    for variant in ("kath", "gla", "gdn", "kda", "ssd"):
         case = rand_case(variant, B=2, H=2, N=6, dk=4, dv=3, seed=21, with_state=True)
         o, S, z = run(variant, case, lib)
         St = case["S0"].copy()
@@ -454,7 +472,182 @@ def pin_decode_matches_prefill(lib=None):
             assert np.array_equal(zt, z)
 
 
+def pin_ssd_selective_ssm(lib=None):
+    """SSD against the selective state space model it is ("Linear / RNN 路线", sections 3.6 and
+    4.1; "状态空间与线性注意力", the Mamba section): every channel p of the head input x runs its
+    own diagonal SSM with state h_p in R^n, h_p <- exp(dt*A) h_p + dt * B x_p, y_p = C . h_p,
+    with one scalar A per head (Mamba-2).  Written here as P independent scalar-input recurrences,
+    it must equal the oracle's SSD with q = C, k = B, v = dt*x and decay exp(dt*A): this fixes
+    which axis of S is the state and which is the channel, and that the output reads S after
+    the write."""
+    rng = np.random.default_rng(41)
+    T, n, P = 19, 6, 3
+    A = -rng.uniform(1.0, 4.0)
+    dt = np.log1p(np.exp(rng.normal(-1.0, 1.0, T)))           # softplus, positive steps
+    Bm, Cm, x = rng.normal(size=(T, n)), rng.normal(size=(T, n)), rng.normal(size=(T, P))
+    h0 = rng.normal(size=(P, n))
+    y, h_end = np.zeros((T, P)), np.zeros((P, n))
+    for p in range(P):                                          # one scalar-input SSM per channel
+        h = h0[p].copy()
+        for t in range(T):
+            h = np.exp(dt[t] * A) * h + dt[t] * Bm[t] * x[t, p]
+            y[t, p] = Cm[t] @ h
+        h_end[p] = h
+    case = {"q": Cm[None, None], "k": Bm[None, None], "v": (dt[:, None] * x)[None, None],
+            "g": np.exp(dt * A)[None, None], "beta": None, "S0": h0.T[None, None].copy(),
+            "z0": None}
+    o, S, _ = run("ssd", case, lib)
+    assert rel(o[0, 0], y) < 1e-12, "SSD output vs per-channel selective SSM"
+    assert rel(S[0, 0], h_end.T) < 1e-12, "SSD state vs per-channel selective SSM"
+
+
+# ---------------------------------------------------------------------------
+# Selective scan (Mamba-1)
+# ---------------------------------------------------------------------------
+
+def ss_case(Bt=2, T=11, D=3, n=4, seed=0, with_state=True, softplus=True):
+    """Random selective-scan inputs: A < 0 per (channel, state), raw steps around softplus(-1)."""
+    rng = np.random.default_rng(seed)
+    return dict(dt=rng.normal(-1.0, 1.0, (Bt, T, D)),
+                A=-rng.uniform(0.5, 4.0, (D, n)),
+                Bm=rng.standard_normal((Bt, T, n)), Cm=rng.standard_normal((Bt, T, n)),
+                x=rng.standard_normal((Bt, T, D)), Dskip=rng.standard_normal(D),
+                dt_bias=rng.normal(0.0, 0.5, D), dt_softplus=softplus,
+                h0=rng.standard_normal((Bt, D, n)) if with_state else None)
+
+
+def ss_run(case, lib=None, **over):
+    c = dict(case, **over)
+    return oracle.selective_scan(c["dt"], c["A"], c["Bm"], c["Cm"], c["x"], c["Dskip"],
+                                 c["dt_bias"], c["dt_softplus"], c["h0"], lib_path=lib)
+
+
+def _softplus(u):
+    return np.logaddexp(0.0, u)
+
+
+def pin_selective_scan_unrolled(lib=None):
+    """The selective scan against its unrolled sum ("Linear / RNN 路线" section 4.1, with the
+    discretisation of section 3.5): h_t = (prod_{0<i<=t} Abar_i) h_0
+    + sum_{tau<=t} (prod_{tau<i<=t} Abar_i) Bbar_tau x_tau, per channel and state entry, with
+    Abar = exp(Delta A), Bbar = Delta B and Delta = softplus(dt + bias); y_t = C_t . h_t + D x_t
+    ("状态空间与线性注意力", section 卷积与递推的等价, for the skip). Every token has its own step."""
+    case = ss_case(Bt=2, T=9, D=3, n=4, seed=31)
+    y, hT = ss_run(case, lib)
+    Bt, T, D = case["x"].shape
+    n = case["A"].shape[1]
+    delta = _softplus(case["dt"] + case["dt_bias"])                       # [Bt,T,D]
+    for b in range(Bt):
+        for d in range(D):
+            abar = np.exp(delta[b, :, d, None] * case["A"][d][None, :])    # [T,n]
+            bbar = delta[b, :, d, None] * case["Bm"][b]                    # [T,n]
+            for t in range(T):
+                h = np.prod(abar[:t + 1], axis=0) * case["h0"][b, d]
+                for tau in range(t + 1):
+                    h = h + np.prod(abar[tau + 1:t + 1], axis=0) * bbar[tau] * case["x"][b, tau, d]
+                want = case["Cm"][b, t] @ h + case["Dskip"][d] * case["x"][b, t, d]
+                assert abs(y[b, t, d] - want) <= 1e-12 * (1 + abs(want)), "unrolled output"
+            assert rel(hT[b, d], h) < 1e-12, "unrolled final state"
+    # without softplus the step is the raw value itself, bias included
+    case["dt"] = np.abs(case["dt"])
+    case["dt_bias"] = np.zeros(D)
+    y1, _ = ss_run(case, lib, dt_softplus=False)
+    y2, _ = ss_run(case, lib, dt=np.log(np.expm1(case["dt"])), dt_softplus=True)
+    assert rel(y1, y2) < 1e-10, "softplus off: the raw step is Delta"
+
+
+def pin_selective_scan_convolution(lib=None):
+    """Time-invariant parameters turn the scan into a causal convolution ("状态空间与线性注意力",
+    section 卷积与递推的等价): with one Delta, B, C for all tokens, y_t = sum_{i<=t} K_{t-i} x_i
+    + D x_t with the kernel K_j = C . (Abar^j Bbar) per channel."""
+    rng = np.random.default_rng(32)
+    Bt, T, D, n = 1, 15, 3, 5
+    A = -rng.uniform(0.2, 2.0, (D, n))
+    delta = rng.uniform(0.05, 0.6, D)
+    Bv, Cv = rng.standard_normal(n), rng.standard_normal(n)
+    x = rng.standard_normal((Bt, T, D))
+    Dskip = rng.standard_normal(D)
+    y, _ = oracle.selective_scan(np.broadcast_to(delta, (Bt, T, D)), A,
+                                 np.broadcast_to(Bv, (Bt, T, n)), np.broadcast_to(Cv, (Bt, T, n)),
+                                 x, Dskip, None, False, None, lib_path=lib)
+    for d in range(D):
+        abar, bbar = np.exp(delta[d] * A[d]), delta[d] * Bv
+        K = np.array([Cv @ (abar ** j * bbar) for j in range(T)])
+        want = np.convolve(x[0, :, d], K)[:T] + Dskip[d] * x[0, :, d]
+        assert rel(y[0, :, d], want) < 1e-12, "convolution form"
+
+
+def pin_selective_scan_split(lib=None):
+    """Split anywhere, carry the state, and the pieces equal the whole scan ("状态空间与线性注意力",
+    the split check under its minimal selective_scan): bit for bit, at every split point."""
+    case = ss_case(Bt=2, T=7, D=4, n=4, seed=0)
+    y, hT = ss_run(case, lib)
+    for cut in range(0, 8):
+        left = dict(case, dt=case["dt"][:, :cut], Bm=case["Bm"][:, :cut], Cm=case["Cm"][:, :cut],
+                    x=case["x"][:, :cut])
+        yl, hm = ss_run(left, lib)
+        right = dict(case, dt=case["dt"][:, cut:], Bm=case["Bm"][:, cut:], Cm=case["Cm"][:, cut:],
+                     x=case["x"][:, cut:], h0=hm)
+        yr, hr = ss_run(right, lib)
+        assert np.array_equal(np.concatenate([yl, yr], axis=1), y), "split outputs"
+        assert np.array_equal(hr, hT), "split final state"
+
+
+def pin_selective_scan_special_cases(lib=None):
+    """Degenerate cases with exact answers, and the pages' minimal elementwise scan."""
+    case = ss_case(Bt=2, T=6, D=3, n=4, seed=33)
+    # a zero step keeps the state (Abar = 1, Bbar = 0): y = C h0 + D x, h_T = h0 exactly
+    y, hT = ss_run(case, lib, dt=np.zeros_like(case["dt"]), dt_bias=None, dt_softplus=False)
+    assert np.array_equal(hT, case["h0"]), "zero step keeps the state"
+    want = np.einsum("btn,bdn->btd", case["Cm"], case["h0"]) + case["Dskip"] * case["x"]
+    assert rel(y, want) < 1e-13, "zero step output"
+    # C = 0 and no initial state: only the skip remains
+    y, _ = ss_run(case, lib, Cm=np.zeros_like(case["Cm"]))
+    assert np.array_equal(y, case["Dskip"] * case["x"]), "C = 0 leaves D x"
+    # one state entry: the minimal elementwise scan of the pages, state = a state + b x,
+    # out = c state, with a = exp(Delta A), b = Delta B, c = C per channel
+    case = ss_case(Bt=1, T=8, D=5, n=1, seed=34)
+    y, hT = ss_run(case, lib, Dskip=None)
+    delta = _softplus(case["dt"][0] + case["dt_bias"])                    # [T,D]
+    a = np.exp(delta * case["A"][:, 0])
+    b = delta * case["Bm"][0]                                             # [T,1] broadcast
+    c = np.broadcast_to(case["Cm"][0], a.shape)
+    state = case["h0"][0, :, 0].copy()
+    for t in range(8):
+        state = a[t] * state + b[t] * case["x"][0, t]
+        assert rel(y[0, t], c[t] * state) < 1e-13, "elementwise scan output"
+    assert rel(hT[0, :, 0], state) < 1e-13
+
+
+def pin_selective_scan_is_ssd(lib=None):
+    """Mamba-1 with one A per head (equal over the state entries) and one step per head and token
+    is the SSD recurrence ("Linear / RNN 路线", section 4.1): per head, k = B, v = Delta x, q = C
+    and the scalar decay exp(Delta A); the head's channel block of h is S^T."""
+    rng = np.random.default_rng(35)
+    Bt, T, Hh, P, n = 2, 10, 3, 2, 4
+    D = Hh * P
+    A_h = -rng.uniform(0.5, 3.0, Hh)
+    delta_h = rng.uniform(0.05, 0.8, (Bt, T, Hh))
+    A = np.repeat(A_h, P)[:, None] * np.ones((1, n))
+    dt = np.repeat(delta_h, P, axis=2)
+    Bm, Cm = rng.standard_normal((Bt, T, n)), rng.standard_normal((Bt, T, n))
+    x = rng.standard_normal((Bt, T, D))
+    h0 = rng.standard_normal((Bt, D, n))
+    y, hT = oracle.selective_scan(dt, A, Bm, Cm, x, None, None, False, h0, lib_path=lib)
+    q = np.repeat(Cm[:, None], Hh, axis=1)
+    k = np.repeat(Bm[:, None], Hh, axis=1)
+    xv = x.reshape(Bt, T, Hh, P).transpose(0, 2, 1, 3)
+    v = delta_h.transpose(0, 2, 1)[..., None] * xv
+    g = np.exp(delta_h.transpose(0, 2, 1) * A_h[None, :, None])
+    S0 = h0.reshape(Bt, Hh, P, n).transpose(0, 1, 3, 2)
+    o, S, _ = oracle.prefill("ssd", q, k, v, g, None, S0, None, lib_path=lib)
+    assert rel(y, o.transpose(0, 2, 1, 3).reshape(Bt, T, D)) < 1e-12, "selective scan vs SSD"
+    assert rel(hT, S.transpose(0, 1, 3, 2).reshape(Bt, D, n)) < 1e-12
+
+
 ALL_PINS = [pin_quadratic_form, pin_split_invariance, pin_gdn_page_forms, pin_kda_forms,
-            pin_delta_identity,
+            pin_ssd_selective_ssm, pin_delta_identity,
             pin_worked_example, pin_closed_forms, pin_special_cases, pin_causality,
-            pin_linearity, pin_decode_matches_prefill]
+            pin_linearity, pin_decode_matches_prefill,
+            pin_selective_scan_unrolled, pin_selective_scan_convolution, pin_selective_scan_split,
+            pin_selective_scan_special_cases, pin_selective_scan_is_ssd]

@@ -48,6 +48,26 @@ MUTATIONS = {
         "            for (j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= g[i];\n"),
     "kda_decay_transposed": ("S[(size_t)i * dv + j] *= g[i];", "S[(size_t)i * dv + j] *= g[j % dk];"),
     "kda_no_beta": ("u[j] = beta * (v[j] - pred);", "u[j] = (v[j] - pred);"),
+    "ssd_decay_after_write": ("S[(size_t)i * dv + j] = a * S[(size_t)i * dv + j] + k[i] * v[j];",
+                              "S[(size_t)i * dv + j] = a * (S[(size_t)i * dv + j] + k[i] * v[j]);"),
+    "ssd_gate_next_token": ("if (variant == OR_SSD) gt = g + tok;",
+                            "if (variant == OR_SSD) gt = g + (t + 1 < N ? tok + 1 : tok);"),
+    "ss_bbar_without_step": ("const double bbar = delta * Bm[tok * n + i];",
+                             "const double bbar = Bm[tok * n + i];"),
+    "ss_decay_sign": ("exp(delta * A[(size_t)d * n + i])", "exp(-delta * A[(size_t)d * n + i])"),
+    "ss_state_index_reversed": ("exp(delta * A[(size_t)d * n + i])",
+                                "exp(delta * A[(size_t)d * n + (n - 1 - i)])"),
+    "ss_read_before_write": (
+        "                h[i] = abar * h[i] + bbar * xt;\n            }\n"
+        "            for (i = 0; i < n; ++i) acc += Cm[tok * n + i] * h[i];\n",
+        "                acc += Cm[tok * n + i] * h[i];\n                h[i] = abar * h[i] + bbar * xt;\n"
+        "            }\n"),
+    "ss_output_reads_B": ("acc += Cm[tok * n + i] * h[i];", "acc += Bm[tok * n + i] * h[i];"),
+    "ss_no_skip": ("y[tok * D + d] = acc + (Dskip ? Dskip[d] * xt : 0.0);", "y[tok * D + d] = acc;"),
+    "ss_bias_dropped": ("double delta = dt[tok * D + d] + (dt_bias ? dt_bias[d] : 0.0);",
+                        "double delta = dt[tok * D + d];"),
+    "ss_softplus_ignored": ("if (dt_softplus) delta = softplus(delta);", "(void)dt_softplus;"),
+    "ss_initial_state_ignored": ("if (h0) memcpy(h, h0", "if (0) memcpy(h, h0"),
     "kda_gate_previous_token": ("if (variant == OR_KDA) { gt = g + tok * dk;",
                                 "if (variant == OR_KDA) { gt = g + (t > 0 ? tok - 1 : tok) * dk;"),
     "read_uses_key": ("for (i = 0; i < dk; ++i) acc += q[i] * S[(size_t)i * dv + j];\n            o[j] = acc;\n        }\n        c->state_read_macs += (uint64_t)dk * (uint64_t)dv;\n    } else {",
