@@ -11,8 +11,9 @@ timed loop replays a HIP graph of those launches (same kernels and work as an
 eager call, without host launch gaps); the graph's output is checked bit for bit
 against an eager call first, and the eager time is reported beside it.
 
-The other workloads (Gated DeltaNet prefill, long normalized-attention prefill,
-decode steps for GDN and GLA, the small fp32 case) are timed the same way and
+The other workloads (Gated DeltaNet, KDA and Mamba-2 SSD prefill, long
+normalized-attention prefill, packed variable-length batches, decode steps, the
+small fp32 case) are timed the same way and
 reported under "workloads", each with its roofline. One JSON line is printed.
 """
 from __future__ import annotations
@@ -39,6 +40,7 @@ STEP_KERNELS = {
     "kath": "kath_chain_kernel (summary) + kath_scan_kernel + kath_chain_kernel",
     "gdn": "gdn_prep_kernel + gdn_fwd_kernel",
     "kda": "kda_prep_kernel + kda_fwd_kernel",
+    "ssd": "gla_prep_kernel (one decay per token) + gla_chain_kernel (summary, forward)",
 }
 
 
@@ -379,7 +381,8 @@ def main():
 
     if not args.no_extras and not args.only:
         for name in ("gdn_bf16_b4h16_n8192_d128", "kath_bf16_b1h16_n32768_dk128_dv64",
-                     "kath_f32_n256_d16", "kda_bf16_b4h16_n8192_d128"):
+                     "kath_f32_n256_d16", "kda_bf16_b4h16_n8192_d128",
+                     "ssd_bf16_b2h32_n4096_dk128_dv64"):
             r, c = bench_prefill(name, max(20, args.steps // 8), 5, 2, torch, bd, W, device,
                                  stream, graph=use_graph)
             results[name] = r
@@ -389,7 +392,8 @@ def main():
             results[name] = bench_varlen(name, max(20, args.steps // 8), 5, torch, bd, W, device,
                                          stream)
             torch.cuda.empty_cache()
-        for name in ("decode_gdn_256x32_d128", "decode_gla_256x32_d128", "decode_kda_256x32_d128"):
+        for name in ("decode_gdn_256x32_d128", "decode_gla_256x32_d128", "decode_kda_256x32_d128",
+                     "decode_ssd_256x64_dk128_dv64"):
             results[name] = bench_decode(name, 1000, 10, torch, bd, W, device, stream)
             torch.cuda.empty_cache()
 

@@ -13,11 +13,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblinattn.so")
 
 LA_OK, LA_ERR_INVALID, LA_ERR_UNSUPPORTED, LA_ERR_HIP, LA_ERR_WORKSPACE = 0, 1, 2, 3, 4
-LA_KATH, LA_GLA, LA_GDN, LA_KDA = 0, 1, 2, 3
+LA_KATH, LA_GLA, LA_GDN, LA_KDA, LA_SSD = 0, 1, 2, 3, 4
 LA_F32, LA_BF16 = 0, 1
 LA_PATH_AUTO, LA_PATH_VALU, LA_PATH_MFMA = 0, 1, 2
 
-VARIANTS = {"kath": LA_KATH, "gla": LA_GLA, "gdn": LA_GDN, "kda": LA_KDA}
+VARIANTS = {"kath": LA_KATH, "gla": LA_GLA, "gdn": LA_GDN, "kda": LA_KDA, "ssd": LA_SSD}
 PATHS = {"auto": LA_PATH_AUTO, "valu": LA_PATH_VALU, "mfma": LA_PATH_MFMA}
 EXPORTS = ("la_prefill", "la_prefill_workspace_size", "la_prefill_varlen",
            "la_prefill_varlen_workspace_size", "la_decode_step", "la_status_str",

@@ -16,7 +16,8 @@
 //        o = (r + (phi(q) . phi(k)) v) / (phi(q) . z_new + eps)
 //   KDA  p = S^T (a * k), r = S^T (a * q) (the decayed state Diag(a) S read through
 //        k and q); u = beta (v - p);  S <- Diag(a) S + k u^T;  o = r + (k . q) u
-// ("Linear / RNN 路线", sections 2.1 and 2.2; "线性注意力与 SSM", section GDN;
+//   SSD  r = S^T q;  S <- a S + k v^T;  o = a r + (q . k) v
+// ("Linear / RNN 路线", sections 2.1, 2.2, 3.6 and 4.1; "线性注意力与 SSM", section GDN;
 // "状态空间与线性注意力", section KDA.)
 #include "common.hpp"
 #include "la_internal.h"
@@ -37,7 +38,7 @@ struct DecodeArgs {
 // 5.8 TB/s with 256 threads. GLA (the lighter kernel) measured faster still with 1024
 // threads; GDN, with twice the registers per thread, slower.
 template <int VAR>
-constexpr int decode_nthreads() { return VAR == LA_GLA ? 1024 : 512; }
+constexpr int decode_nthreads() { return VAR == LA_GLA || VAR == LA_SSD ? 1024 : 512; }
 template <int VAR>
 constexpr bool has_delta() { return VAR == LA_GDN || VAR == LA_KDA; }
 template <int VAR>
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(decode_threads(DK, DV, decode_nthreads<VAR>())) voi
         if (tid == 0) {
             scal[0] = qk;
             scal[1] = qz + a.eps;
-            if (VAR == LA_GDN) scal[2] = load_elem(a.g, seq, gb);
+            if (VAR == LA_GDN || VAR == LA_SSD) scal[2] = load_elem(a.g, seq, gb);
             if (has_delta<VAR>()) scal[3] = load_elem(a.beta, seq, gb);
         }
     }
@@ -174,18 +175,19 @@ __global__ __launch_bounds__(decode_threads(DK, DV, decode_nthreads<VAR>())) voi
         o4.x = al * R.x + qk * u.x; o4.y = al * R.y + qk * u.y;
         o4.z = al * R.z + qk * u.z; o4.w = al * R.w + qk * u.w;
     } else {
+        const float as = VAR == LA_SSD ? scal[2] : 1.f;   // SSD: the token's decay
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
             const int i = rg + RG * r;
             const float ki = sk[i];
-            const float gi = VAR == LA_GLA ? sw[i] : 1.f;
+            const float gi = VAR == LA_GLA ? sw[i] : as;
             float4 n;
             n.x = gi * s[r].x + ki * v4.x; n.y = gi * s[r].y + ki * v4.y;
             n.z = gi * s[r].z + ki * v4.z; n.w = gi * s[r].w + ki * v4.w;
             store_nt4(S + size_t(i) * DV + cg * 4, n);
         }
-        o4.x = R.x + qk * v4.x; o4.y = R.y + qk * v4.y;
-        o4.z = R.z + qk * v4.z; o4.w = R.w + qk * v4.w;
+        o4.x = as * R.x + qk * v4.x; o4.y = as * R.y + qk * v4.y;
+        o4.z = as * R.z + qk * v4.z; o4.w = as * R.w + qk * v4.w;
         if (VAR == LA_KATH) {
             const float inv = 1.f / scal[1];
             o4.x *= inv; o4.y *= inv; o4.z *= inv; o4.w *= inv;
@@ -239,6 +241,7 @@ hipError_t launch_decode(const Problem& p) {
         case LA_GLA: return dispatch_dk<LA_GLA>(p, a);
         case LA_GDN: return dispatch_dk<LA_GDN>(p, a);
         case LA_KDA: return dispatch_dk<LA_KDA>(p, a);
+        case LA_SSD: return dispatch_dk<LA_SSD>(p, a);
     }
     return hipErrorInvalidValue;
 }

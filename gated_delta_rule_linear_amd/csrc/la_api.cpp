@@ -51,6 +51,7 @@ bool check_alignment(const la_desc& d, const void* q, const void* k, const void*
     if ((d.variant == LA_GLA || d.variant == LA_KDA) && g && !aligned(g, 16)) return false;
     if (d.variant == LA_GDN && ((g && !aligned(g, gsz)) || (beta && !aligned(beta, gsz))))
         return false;
+    if (d.variant == LA_SSD && g && !aligned(g, gsz)) return false;
     if (d.variant == LA_KDA && beta && !aligned(beta, gsz)) return false;
     return true;
 }
@@ -68,7 +69,7 @@ Sizes sizes_of(const la_desc& d) {
     s.q = s.k = mul(mul(tok, d.dk), isz);
     s.v = s.o = mul(mul(tok, d.dv), isz);
     s.g = (d.variant == LA_GLA || d.variant == LA_KDA) ? mul(mul(tok, d.dk), gsz)
-          : d.variant == LA_GDN                         ? mul(tok, gsz)
+          : (d.variant == LA_GDN || d.variant == LA_SSD) ? mul(tok, gsz)
                                                         : 0;
     s.beta = (d.variant == LA_GDN || d.variant == LA_KDA) ? mul(tok, gsz) : 0;
     s.S = mul(mul(mul(seq, d.dk), d.dv), 4);
@@ -79,7 +80,7 @@ Sizes sizes_of(const la_desc& d) {
 // Descriptor checks shared by prefill, decode and the workspace query.
 int check_desc(const la_desc* d, bool decode) {
     if (!d) return LA_ERR_INVALID;
-    if (d->variant < LA_KATH || d->variant > LA_KDA) return LA_ERR_INVALID;
+    if (d->variant < LA_KATH || d->variant > LA_SSD) return LA_ERR_INVALID;
     if (d->io_dtype != LA_F32 && d->io_dtype != LA_BF16) return LA_ERR_INVALID;
     if (d->variant != LA_KATH && d->gate_dtype != LA_F32 && d->gate_dtype != LA_BF16)
         return LA_ERR_INVALID;
@@ -110,7 +111,8 @@ int plan_prefill(const la_desc& d, Problem& p, int nseq, int max_len, const int3
     p.eps = d.eps;
     const bool mfma_ok = d.variant == LA_GDN   ? la::gdn_mfma_supported(d.dk, d.dv, p.io_bf16)
                          : d.variant == LA_KDA ? la::kda_mfma_supported(d.dk, d.dv, p.io_bf16)
-                         : d.variant == LA_GLA ? la::gla_mfma_supported(d.dk, d.dv, p.io_bf16)
+                         : (d.variant == LA_GLA || d.variant == LA_SSD)
+                             ? la::gla_mfma_supported(d.dk, d.dv, p.io_bf16)
                                                : la::kath_mfma_supported(d.dk, d.dv, p.io_bf16);
     int path = d.path;
     if (path == LA_PATH_AUTO) path = mfma_ok ? LA_PATH_MFMA : LA_PATH_VALU;
@@ -119,11 +121,12 @@ int plan_prefill(const la_desc& d, Problem& p, int nseq, int max_len, const int3
     p.chunk = path == LA_PATH_MFMA ? la::kMfmaChunk : la::kValuChunk;
     if (d.chunk != 0 && d.chunk != p.chunk) return LA_ERR_UNSUPPORTED;
     p.segments = 1;
-    if (path == LA_PATH_MFMA && (d.variant == LA_KATH || d.variant == LA_GLA) && p.L > 0) {
+    const bool diag = d.variant == LA_GLA || d.variant == LA_SSD;   // diagonal transition
+    if (path == LA_PATH_MFMA && (d.variant == LA_KATH || diag) && p.L > 0) {
         const int nchunks = (p.L + p.chunk - 1) / p.chunk;
-        int segs = d.segments > 0                 ? d.segments
-                   : d.variant == LA_GLA ? la::gla_mfma_auto_segments(p)
-                                         : la::kath_mfma_auto_segments(p);
+        int segs = d.segments > 0 ? d.segments
+                   : diag         ? la::gla_mfma_auto_segments(p)
+                                  : la::kath_mfma_auto_segments(p);
         if (segs > nchunks) segs = nchunks;
         if (segs < 1) segs = 1;
         // equal segments of cps chunks; drop segments that would be empty
@@ -138,7 +141,7 @@ size_t workspace_for(const Problem& p) {
     if (p.path == LA_PATH_MFMA)
         return p.variant == LA_GDN   ? la::gdn_mfma_workspace_bytes(p)
                : p.variant == LA_KDA ? la::kda_mfma_workspace_bytes(p)
-               : p.variant == LA_GLA ? la::gla_mfma_workspace_bytes(p)
+               : (p.variant == LA_GLA || p.variant == LA_SSD) ? la::gla_mfma_workspace_bytes(p)
                                      : la::kath_mfma_workspace_bytes(p);
     return 0;
 }
@@ -198,13 +201,13 @@ int prefill_impl(const la_desc* d, int nseq, const int32_t* cu, int max_len, con
     rc = plan_prefill(*d, p, nseq, max_len, cu, cu != nullptr);
     if (rc != LA_OK) return rc;
     const bool kath = d->variant == LA_KATH, gla = d->variant == LA_GLA,
-               gdn = d->variant == LA_GDN, kda = d->variant == LA_KDA;
+               gdn = d->variant == LA_GDN, kda = d->variant == LA_KDA, ssd = d->variant == LA_SSD;
     const bool varlen = cu != nullptr;
     const bool empty_seq = (uint64_t(nseq) * uint64_t(d->H)) == 0;
     const bool tokens = !empty_seq && d->N > 0 && (uint64_t(d->B) * uint64_t(d->H)) > 0;
     // presence rules
     if (kath && (g || beta)) return LA_ERR_INVALID;
-    if (gla && beta) return LA_ERR_INVALID;
+    if ((gla || ssd) && beta) return LA_ERR_INVALID;
     if (!kath && (z0 || z_final)) return LA_ERR_INVALID;
     if (!empty_seq) {
         if (!S_final) return LA_ERR_INVALID;
@@ -212,7 +215,7 @@ int prefill_impl(const la_desc* d, int nseq, const int32_t* cu, int max_len, con
     }
     if (tokens) {
         if (!q || !k || !v || !o) return LA_ERR_INVALID;
-        if ((gla || gdn || kda) && !g) return LA_ERR_INVALID;
+        if ((gla || gdn || kda || ssd) && !g) return LA_ERR_INVALID;
         if ((gdn || kda) && !beta) return LA_ERR_INVALID;
     }
     // alignment: 16 bytes for the arrays read or written with 128-bit accesses; the
@@ -270,7 +273,7 @@ int prefill_impl(const la_desc* d, int nseq, const int32_t* cu, int max_len, con
     else if (p.path == LA_PATH_MFMA)
         err = gdn                     ? la::launch_prefill_gdn_mfma(p)
               : kda                   ? la::launch_prefill_kda_mfma(p)
-              : p.variant == LA_GLA ? la::launch_prefill_gla_mfma(p)
+              : (gla || ssd)          ? la::launch_prefill_gla_mfma(p)
                                     : la::launch_prefill_kath_mfma(p);
     else
         err = la::launch_prefill_valu(p);
@@ -313,14 +316,14 @@ int la_decode_step(const la_desc* d, const void* q, const void* k, const void* v
     int rc = check_desc(d, true);
     if (rc != LA_OK) return rc;
     const bool kath = d->variant == LA_KATH, gla = d->variant == LA_GLA,
-               gdn = d->variant == LA_GDN, kda = d->variant == LA_KDA;
+               gdn = d->variant == LA_GDN, kda = d->variant == LA_KDA, ssd = d->variant == LA_SSD;
     if (kath && (g || beta)) return LA_ERR_INVALID;
-    if (gla && beta) return LA_ERR_INVALID;
+    if ((gla || ssd) && beta) return LA_ERR_INVALID;
     if (!kath && z) return LA_ERR_INVALID;
     const bool empty_seq = (uint64_t(d->B) * uint64_t(d->H)) == 0;
     if (!empty_seq) {
         if (!q || !k || !v || !o || !S) return LA_ERR_INVALID;
-        if ((gla || gdn || kda) && !g) return LA_ERR_INVALID;
+        if ((gla || gdn || kda || ssd) && !g) return LA_ERR_INVALID;
         if ((gdn || kda) && !beta) return LA_ERR_INVALID;
         if (kath && !z) return LA_ERR_INVALID;
     }

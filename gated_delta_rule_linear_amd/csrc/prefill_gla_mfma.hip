@@ -30,6 +30,11 @@
 // side. Gates are clamped at g >= exp(-10) (a gate below that keeps less than 4.5e-5
 // of the state, so the clamp changes no result beyond bf16 rounding), which keeps
 // every factor within [exp(-80), exp(80)], inside fp32's normal range.
+//
+// Mamba-2's SSD ("Linear / RNN 路线", sections 3.6 and 4.1: one decay a_t per token and
+// head, S_t = a_t S_{t-1} + k_t v_t^T) is this recurrence with the gate equal over the
+// key dims; the prep kernel then reads one gate per row and broadcasts it, and
+// everything after it is shared.
 #include "la_internal.h"
 #include "mfma.hpp"
 
@@ -97,7 +102,7 @@ struct __align__(16) PrepSmem {
     __align__(16) float T[8][DK];           // gate product of each 8-row group
 };
 
-template <bool GB>
+template <bool GB, bool SG>   // SG: one gate per token (SSD) instead of one per key dim
 __global__ __launch_bounds__(NTP) void gla_prep_kernel(GlaArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
@@ -121,15 +126,18 @@ __global__ __launch_bounds__(NTP) void gla_prep_kernel(GlaArgs a) {
     const rsrc_t rq = make_rsrc(a.q + (tok0 + t0) * DK, rows_left * DK * 2u);
     const rsrc_t rk = make_rsrc(a.k + (tok0 + t0) * DK, rows_left * DK * 2u);
     constexpr uint32_t GS = GB ? 2u : 4u;
-    const rsrc_t rg_ = make_rsrc(static_cast<const char*>(a.g) + (tok0 + t0) * DK * GS,
-                                 rows_left * DK * GS);
-    uint32_t qv[8], kv[8], gv[GB ? 8 : 16];
+    constexpr uint32_t GW = SG ? 1u : uint32_t(DK);   // gate elements per token
+    const rsrc_t rg_ = make_rsrc(static_cast<const char*>(a.g) + (tok0 + t0) * GW * GS,
+                                 rows_left * GW * GS);
+    uint32_t qv[8], kv[8], gv[GB || SG ? 8 : 16];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         const uint32_t e = uint32_t((8 * rg + r) * DK + col);
         qv[r] = buf_ld4(rq, e * 2u);
         kv[r] = buf_ld4(rk, e * 2u);
-        if constexpr (GB) {
+        if constexpr (SG) {
+            gv[r] = buf_ld_gate<GB>(rg_, uint32_t(8 * rg + r));
+        } else if constexpr (GB) {
             gv[r] = buf_ld4(rg_, e * 2u);
         } else {
             const uint2 x = buf_ld8(rg_, e * 4u);
@@ -143,7 +151,9 @@ __global__ __launch_bounds__(NTP) void gla_prep_kernel(GlaArgs a) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             float g0, g1;
-            if constexpr (GB) {
+            if constexpr (SG) {
+                g0 = g1 = gate_val<GB>(gv[r]);
+            } else if constexpr (GB) {
                 g0 = __uint_as_float(gv[r] << 16);
                 g1 = __uint_as_float(gv[r] & 0xffff0000u);
             } else {
@@ -300,7 +310,9 @@ struct ChainRegs {
     uint4 kt[4], qf[4], pf[2], vst[KV], ast;
 };
 
-template <bool OUT, int NVT>
+// SG only names the instantiation (one decay per token: the SSD workload), so that
+// profiles tell the two workloads apart; the chunk walk itself is the same.
+template <bool OUT, int NVT, bool SG>
 __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
     constexpr int VT = 16 * NVT;
     constexpr int PV = ChainSmem<VT>::PV;
@@ -611,7 +623,7 @@ WsLayout ws_layout(const Problem& p) {
 
 int pick_nvt(int dv) { return dv >= 64 ? 4 : dv / 16; }
 
-template <bool GB, int NVT>
+template <bool GB, bool SG, int NVT>
 hipError_t launch_nvt(const Problem& p) {
     constexpr int VT = 16 * NVT;
     const WsLayout L = ws_layout(p);
@@ -640,37 +652,37 @@ hipError_t launch_nvt(const Problem& p) {
     hipError_t e;
     {
         const size_t smem = sizeof(PrepSmem);
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_prep_kernel<GB>),
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_prep_kernel<GB, SG>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
         if (e != hipSuccess) return e;
         const size_t blocks = size_t(xcd_grid(a.nchunks, (a.nseq + 7) & ~7));
         if (size_t(a.nseq + 7) * size_t(a.nchunks) > 0x7fffffffull) return hipErrorInvalidValue;
-        gla_prep_kernel<GB><<<dim3(unsigned(blocks)), dim3(NTP), smem, p.stream>>>(a);
+        gla_prep_kernel<GB, SG><<<dim3(unsigned(blocks)), dim3(NTP), smem, p.stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const size_t smem = sizeof(ChainSmem<VT>);
     if (a.nseg > 1) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_chain_kernel<false, NVT>),
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_chain_kernel<false, NVT, SG>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
         if (e != hipSuccess) return e;
-        gla_chain_kernel<false, NVT><<<dim3(xcd_grid(a.ntiles * (a.nseg - 1), a.nseq)), dim3(NT),
+        gla_chain_kernel<false, NVT, SG><<<dim3(xcd_grid(a.ntiles * (a.nseg - 1), a.nseq)), dim3(NT),
                                        smem, p.stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_chain_kernel<true, NVT>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_chain_kernel<true, NVT, SG>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
     if (e != hipSuccess) return e;
-    gla_chain_kernel<true, NVT><<<dim3(xcd_grid(a.ntiles * a.nseg, a.nseq)), dim3(NT), smem,
+    gla_chain_kernel<true, NVT, SG><<<dim3(xcd_grid(a.ntiles * a.nseg, a.nseq)), dim3(NT), smem,
                                   p.stream>>>(a);
     return hipGetLastError();
 }
 
-template <bool GB>
+template <bool GB, bool SG>
 hipError_t launch_gb(const Problem& p) {
     switch (pick_nvt(p.dv)) {
-        case 1: return launch_nvt<GB, 1>(p);
-        case 2: return launch_nvt<GB, 2>(p);
-        default: return launch_nvt<GB, 4>(p);
+        case 1: return launch_nvt<GB, SG, 1>(p);
+        case 2: return launch_nvt<GB, SG, 2>(p);
+        default: return launch_nvt<GB, SG, 4>(p);
     }
 }
 
@@ -707,7 +719,9 @@ hipError_t launch_prefill_gla_mfma(const Problem& p) {
     // buffer offsets are 32-bit: one sequence's v / o rows and its chunk workspace
     if (size_t(p.L) * size_t(DK) * 4 >= (size_t(1) << 31)) return hipErrorInvalidValue;
     if (size_t((p.L + C - 1) / C) * kWsChunk >= (size_t(1) << 31)) return hipErrorInvalidValue;
-    return p.gate_bf16 ? launch_gb<true>(p) : launch_gb<false>(p);
+    if (p.variant == LA_SSD)
+        return p.gate_bf16 ? launch_gb<true, true>(p) : launch_gb<false, true>(p);
+    return p.gate_bf16 ? launch_gb<true, false>(p) : launch_gb<false, false>(p);
 }
 
 }  // namespace la

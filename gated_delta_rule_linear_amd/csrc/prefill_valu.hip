@@ -28,6 +28,9 @@
 //        (I + L) U = X,  X_r = beta_r (v_r - S^T (k_r * exp(B_r)))
 //        o_r  = S^T (q_r * exp(B_r)) + sum_{s<=r} P_rs u_s,  P as for GLA
 //        S    = diag(exp(B_last)) S + sum_s diag(exp(B_last - B_s)) k_s u_s^T
+//  SSD   c_r  = sum_{s<=r} log a_s (one decay per token), GLA with that decay on every
+//        key dim: P_rs = exp(c_r - c_s) q_r.k_s, o_r = exp(c_r) S^T q_r + sum_s P_rs v_s,
+//        S    = exp(c_last) S + sum_s exp(c_last - c_s) k_s v_s^T
 // These are exact rewrites of the token recurrences (the state after token r of
 // the chunk, unrolled back to the chunk start). Padding tokens past N are
 // identity steps: zero key and value, gate 1, beta 0.
@@ -58,6 +61,7 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
     constexpr int DKP = DK + 1;  // padded row pitch
     constexpr bool CHG = VAR == LA_GLA || VAR == LA_KDA;   // gate per key dim
     constexpr bool DLT = VAR == LA_GDN || VAR == LA_KDA;   // delta rule
+    constexpr bool SCL = VAR == LA_GDN || VAR == LA_SSD;   // one gate per token
     __shared__ float sS[DK][VT];
     __shared__ float sz[DK];
     __shared__ float sQ[C][DKP], sK[C][DKP];
@@ -111,10 +115,10 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
             const int r = r_me, c = c_me;
             sV[r][c] = r < n ? load_elem(a.v, (tok0 + t0 + r) * DV + c0 + c, iob) : 0.f;
         }
-        if (DLT && tid < C) {
+        if ((DLT || SCL) && tid < C) {
             const int r = tid;
-            if (VAR == LA_GDN) sc[r] = r < n ? logf(load_elem(a.g, tok0 + t0 + r, gb)) : 0.f;
-            sbeta[r] = r < n ? load_elem(a.beta, tok0 + t0 + r, gb) : 0.f;
+            if (SCL) sc[r] = r < n ? logf(load_elem(a.g, tok0 + t0 + r, gb)) : 0.f;
+            if (DLT) sbeta[r] = r < n ? load_elem(a.beta, tok0 + t0 + r, gb) : 0.f;
         }
         __syncthreads();
         // in-chunk cumulative log gates
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
                 }
             }
         }
-        if (VAR == LA_GDN && tid == 0) {
+        if (SCL && tid == 0) {
             float acc = 0.f;
             for (int r = 0; r < C; ++r) {
                 acc += sc[r];
@@ -149,10 +153,10 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
                     for (int i = 0; i < DK; ++i) l += sK[r][i] * sK[s][i] * expf(sLg[r][i] - sLg[s][i]);
                     l *= sbeta[r];
                 }
-                if (VAR == LA_GDN) {
+                if (SCL) {
                     const float d = expf(sc[r] - sc[s]);
                     p *= d;
-                    if (s < r) {
+                    if (DLT && s < r) {
                         for (int i = 0; i < DK; ++i) l += sK[r][i] * sK[s][i];
                         l *= sbeta[r] * d;
                     }
@@ -200,7 +204,7 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
             } else {
                 for (int i = 0; i < DK; ++i) acc += sQ[r][i] * sS[i][c];
             }
-            if (VAR == LA_GDN) acc *= expf(sc[r]);
+            if (SCL) acc *= expf(sc[r]);
             float intra = 0.f, psum = 0.f;
             for (int s = 0; s <= r; ++s) {
                 const float p = sP[r][s];
@@ -224,9 +228,10 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
                 const float bl = sLg[C - 1][i];
                 for (int s = 0; s < C; ++s) acc += sK[s][i] * expf(bl - sLg[s][i]) * sU[s][c];
                 sS[i][c] = expf(bl) * sS[i][c] + acc;
-            } else if (VAR == LA_GDN) {
+            } else if (SCL) {
                 const float cl = sc[C - 1];
-                for (int s = 0; s < C; ++s) acc += sK[s][i] * expf(cl - sc[s]) * sU[s][c];
+                for (int s = 0; s < C; ++s)
+                    acc += sK[s][i] * expf(cl - sc[s]) * (DLT ? sU[s][c] : sV[s][c]);
                 sS[i][c] = expf(cl) * sS[i][c] + acc;
             } else {
                 for (int s = 0; s < C; ++s) acc += sK[s][i] * sV[s][c];
@@ -299,6 +304,7 @@ hipError_t launch_prefill_valu(const Problem& p) {
         case LA_GLA: return dispatch_dk<LA_GLA>(p, a);
         case LA_GDN: return dispatch_dk<LA_GDN>(p, a);
         case LA_KDA: return dispatch_dk<LA_KDA>(p, a);
+        case LA_SSD: return dispatch_dk<LA_SSD>(p, a);
     }
     return hipErrorInvalidValue;
 }

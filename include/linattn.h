@@ -21,6 +21,13 @@
  *            per key channel decays the old state first, then the delta write reads
  *            the decayed state:  Sbar = Diag(a_t) S_{t-1},
  *              S_t = Sbar + b_t k_t (v_t - Sbar^T k_t)^T,   o_t = S_t^T q_t
+ *   LA_SSD   Mamba-2's structured state space duality ("Linear / RNN 路线", sections 3.6
+ *            and 4.1): the selective SSM h_t = A_t h_{t-1} + B_t x_t, y_t = C_t h_t with
+ *            one scalar decay per token and head is linear attention with k = B,
+ *            v = x (already scaled by the step), q = C:
+ *              S_t = a_t S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t
+ *            d_k is the state size and d_v the head dim; the caller passes a_t =
+ *            exp(Delta_t A_h). (The per-channel Mamba-1 scan is la_selective_scan.)
  *
  * Every variant reads the state after the token's update. Prefill runs the
  * recurrence over N tokens with the chunkwise-parallel method (quadratic, causally
@@ -33,6 +40,7 @@
  *   g        LA_GLA: [B, H, N, d_k] gate, values in (0, 1]
  *            LA_GDN: alpha [B, H, N] gate, values in (0, 1]
  *            LA_KDA: alpha [B, H, N, d_k] gate (retention per key channel), in (0, 1]
+ *            LA_SSD: a [B, H, N] decay, values in (0, 1]
  *   beta     LA_GDN, LA_KDA: [B, H, N] gate, values in [0, 1]
  *   S0, S    [B, H, d_k, d_v] fp32 (key-major)
  *   z0, z    [B, H, d_k] fp32 (LA_KATH only)
@@ -66,7 +74,7 @@ enum {
     LA_OK = 0,
     LA_ERR_INVALID = 1,      /* null required pointer, bad enum, negative size, misaligned
                                 pointer (16 bytes for q, k, v, o, GLA g, S and z; element
-                                alignment for GDN alpha and GDN / KDA beta; 256 bytes for the
+                                alignment for GDN alpha, SSD a and GDN / KDA beta; 256 bytes for the
                                 workspace), overlap of an output with any other buffer,
                                 gate passed / missing for the variant, N != 1 for decode */
     LA_ERR_UNSUPPORTED = 2,  /* d_k or d_v not in {16, 32, 64, 128}, or a requested path /
@@ -76,7 +84,7 @@ enum {
 };
 
 /* variants */
-enum { LA_KATH = 0, LA_GLA = 1, LA_GDN = 2, LA_KDA = 3 };
+enum { LA_KATH = 0, LA_GLA = 1, LA_GDN = 2, LA_KDA = 3, LA_SSD = 4 };
 
 /* storage dtypes */
 enum { LA_F32 = 0, LA_BF16 = 1 };
@@ -92,13 +100,13 @@ enum {
 typedef struct la_desc {
     int32_t B, H, N;      /* batch, heads, tokens per sequence (N = 1 for decode) */
     int32_t dk, dv;       /* key and value dims, each in {16, 32, 64, 128} */
-    int32_t variant;      /* LA_KATH | LA_GLA | LA_GDN | LA_KDA */
+    int32_t variant;      /* LA_KATH | LA_GLA | LA_GDN | LA_KDA | LA_SSD */
     int32_t io_dtype;     /* LA_F32 | LA_BF16: q, k, v, o */
     int32_t gate_dtype;   /* LA_F32 | LA_BF16: g / alpha, beta (ignored for LA_KATH) */
     float eps;            /* LA_KATH denominator epsilon, finite and >= 0 */
     int32_t path;         /* LA_PATH_* */
     int32_t chunk;        /* 0 = the path's chunk size; otherwise it must equal it */
-    int32_t segments;     /* 0 = automatic. LA_KATH / LA_GLA on the MFMA path split each
+    int32_t segments;     /* 0 = automatic. LA_KATH / LA_GLA / LA_SSD on the MFMA path split each
                              sequence into this many segments that run in parallel and
                              are joined by a scan of their state summaries */
 } la_desc;

@@ -73,7 +73,7 @@ def good(variant="gla", **kw):
 
 def ptrs(variant):
     p = dict(q=addr(0), k=addr(1), v=addr(2), o=addr(7), S=addr(8))
-    if variant in ("gla", "gdn", "kda"):
+    if variant in ("gla", "gdn", "kda", "ssd"):
         p["g"] = addr(3)
     if variant in ("gdn", "kda"):
         p["beta"] = addr(4)
@@ -106,6 +106,9 @@ def ptrs(variant):
     ("kda_missing_beta", bd.LA_ERR_INVALID),
     ("kda_missing_gate", bd.LA_ERR_INVALID),
     ("misaligned_kda_gate", bd.LA_ERR_INVALID),
+    ("ssd_missing_gate", bd.LA_ERR_INVALID),
+    ("ssd_with_beta", bd.LA_ERR_INVALID),
+    ("misaligned_ssd_gate", bd.LA_ERR_INVALID),
     ("kath_with_gate", bd.LA_ERR_INVALID),
     ("kath_missing_z", bd.LA_ERR_INVALID),
     ("gla_with_z", bd.LA_ERR_INVALID),
@@ -113,7 +116,8 @@ def ptrs(variant):
 def test_prefill_rejects(lib, case, expect):
     variant = {"gdn_missing_beta": "gdn", "kath_with_gate": "kath", "kath_missing_z": "kath",
                "kda_missing_beta": "kda", "kda_missing_gate": "kda",
-               "misaligned_kda_gate": "kda"}.get(case, "gla")
+               "misaligned_kda_gate": "kda", "ssd_missing_gate": "ssd", "ssd_with_beta": "ssd",
+               "misaligned_ssd_gate": "ssd"}.get(case, "gla")
     d = good(variant)
     p = ptrs(variant)
     if case == "null_desc":
@@ -158,8 +162,12 @@ def test_prefill_rejects(lib, case, expect):
         p["beta"] = addr(4)
     elif case in ("gdn_missing_beta", "kda_missing_beta"):
         p.pop("beta")
-    elif case == "kda_missing_gate":
+    elif case in ("kda_missing_gate", "ssd_missing_gate"):
         p.pop("g")
+    elif case == "ssd_with_beta":
+        p["beta"] = addr(4)
+    elif case == "misaligned_ssd_gate":
+        p["g"] = addr(3, 1)
     elif case == "misaligned_kda_gate":
         p["g"] = addr(3, 2)
     elif case == "kath_with_gate":

@@ -19,6 +19,9 @@ def wl_for(variant, B, H, N, dv, seed, gate_kind="default", dk=128):
     if variant in ("gdn", "kda"):
         return W.Workload("t", variant, B, H, N, dk, dv, "bf16", "bf16", seed=seed,
                           l2norm_qk=True, gate_kind=gate_kind)
+    if variant == "ssd":
+        return W.Workload("t", "ssd", B, H, N, dk, dv, "bf16", "bf16", seed=seed,
+                          qk_scale=dk ** -0.5, gate_kind=gate_kind)
     return W.Workload("t", "kath", B, H, N, dk, dv, "bf16", "bf16", seed=seed)
 
 
@@ -55,7 +58,7 @@ def check(inp, got, ref, tol=TOL["bf16"], seqs=None):
     return errs
 
 
-@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda", "ssd"])
 @pytest.mark.parametrize("dv", [16, 32, 64, 128])
 def test_mfma_shapes(variant, dv):
     inp = W.make_inputs(wl_for(variant, 2, 3, 200, dv, seed=dv + 1), with_state=True)
@@ -64,7 +67,7 @@ def test_mfma_shapes(variant, dv):
     print(errs)
 
 
-@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda", "ssd"])
 @pytest.mark.parametrize("N", [1, 63, 64, 65, 130, 447])
 def test_mfma_lengths(variant, N):
     inp = W.make_inputs(wl_for(variant, 1, 2, N, 64, seed=N), with_state=(N % 2 == 1))
@@ -83,14 +86,15 @@ def test_mfma_segments(variant, segments):
 @pytest.mark.parametrize("variant,kind", [("gla", "fast"), ("gla", "ones"), ("gla", "slow"),
                                           ("gdn", "slow"), ("gdn", "ones"), ("gdn", "beta0"),
                                           ("gdn", "beta1"), ("kda", "slow"), ("kda", "ones"),
-                                          ("kda", "beta0"), ("kda", "beta1")])
+                                          ("kda", "beta0"), ("kda", "beta1"), ("ssd", "slow"),
+                                          ("ssd", "ones"), ("ssd", "fast")])
 def test_mfma_gate_kinds(variant, kind):
     inp = W.make_inputs(wl_for(variant, 1, 2, 300, 64, seed=7, gate_kind=kind), with_state=True)
     banner(f"mfma {variant} gates={kind}")
     check(inp, run_gpu(inp), run_oracle(inp))
 
 
-@pytest.mark.parametrize("variant", ["gla", "gdn", "kda"])
+@pytest.mark.parametrize("variant", ["gla", "gdn", "kda", "ssd"])
 @pytest.mark.parametrize("N", [70, 449])
 def test_mfma_fp32_gates(variant, N):
     """bf16 q, k, v with fp32 gates (the other gate storage the ABI accepts)."""
@@ -101,7 +105,7 @@ def test_mfma_fp32_gates(variant, N):
     check(inp, run_gpu(inp), run_oracle(inp))
 
 
-@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda", "ssd"])
 @pytest.mark.parametrize("segments", [3, 7])
 def test_mfma_wide_tiles_segments(variant, segments):
     """d_v = 128 (the widest value tiles) with an explicit segment count and a ragged
@@ -123,7 +127,7 @@ def test_gla_tiny_gates_clamped():
     check(inp, run_gpu(inp), run_oracle(inp))
 
 
-@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda", "ssd"])
 def test_mfma_matches_valu_path(variant):
     inp = W.make_inputs(wl_for(variant, 2, 2, 333, 64, seed=11), with_state=True)
     d = inputs_to_device(inp)
@@ -133,7 +137,7 @@ def test_mfma_matches_valu_path(variant):
     assert relerr(a[0], f64(b[0])) < 2e-2 and relerr(a[1], f64(b[1])) < 2e-2
 
 
-@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda", "ssd"])
 def test_mfma_deterministic_and_batch_invariant(variant):
     inp = W.make_inputs(wl_for(variant, 2, 3, 257, 64, seed=5), with_state=True)
     d = inputs_to_device(inp)
@@ -147,7 +151,7 @@ def test_mfma_deterministic_and_batch_invariant(variant):
     assert torch.equal(o3[0, 0], o1[1, 2]) and torch.equal(S3[0, 0], S1[1, 2])
 
 
-@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda", "ssd"])
 def test_mfma_causality(variant):
     inp = W.make_inputs(wl_for(variant, 1, 2, 200, 32, seed=6), with_state=True)
     d = inputs_to_device(inp)
@@ -165,7 +169,7 @@ def test_mfma_causality(variant):
         assert not torch.equal(o2[:, :, tp], o[:, :, tp])
 
 
-@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda", "ssd"])
 def test_mfma_split_at_chunk_boundary_is_exact(variant):
     inp = W.make_inputs(wl_for(variant, 1, 2, 320, 64, seed=8), with_state=True)
     d = inputs_to_device(inp)
@@ -186,7 +190,7 @@ def test_mfma_split_at_chunk_boundary_is_exact(variant):
             assert relerr(torch.cat([oL, oR], 2), f64(o)) < 2e-2 and relerr(SR, f64(S)) < 1e-2
 
 
-@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda", "ssd"])
 @pytest.mark.parametrize("segments", [1, 5])
 def test_mfma_in_place_state(variant, segments):
     """S_final (and z_final) may be the very buffers of S0 (z0), also when the sequence
@@ -207,7 +211,7 @@ def test_mfma_in_place_state(variant, segments):
     check(inp, (o2, S2, z2), run_oracle(inp))
 
 
-@pytest.mark.parametrize("variant", ["gla", "gdn", "kath", "kda"])
+@pytest.mark.parametrize("variant", ["gla", "gdn", "kath", "kda", "ssd"])
 def test_prefill_then_decode_equals_longer_prefill(variant):
     N, extra = 192, 5
     inp = W.make_inputs(wl_for(variant, 1, 2, N + extra, 64, seed=12))
@@ -230,7 +234,8 @@ def test_prefill_then_decode_equals_longer_prefill(variant):
 # ---------------------------------------------------------------- full-size workloads
 
 FULL = ["gla_bf16_b2h8_n2048_d128", "kath_bf16_b1h16_n32768_dk128_dv64",
-        "gdn_bf16_b4h16_n8192_d128", "kda_bf16_b4h16_n8192_d128"]
+        "gdn_bf16_b4h16_n8192_d128", "kda_bf16_b4h16_n8192_d128",
+        "ssd_bf16_b2h32_n4096_dk128_dv64"]
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -42,7 +42,7 @@ def test_config_kath_f32_n256_d16():
 SHAPES = [(16, 16), (32, 64), (64, 32), (128, 128), (128, 64)]
 
 
-@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda", "ssd"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", SHAPES)
 def test_valu_prefill_shapes(variant, io, dk, dv):
@@ -52,7 +52,7 @@ def test_valu_prefill_shapes(variant, io, dk, dv):
     run_prefill_case(wl)
 
 
-@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda", "ssd"])
 @pytest.mark.parametrize("N", [1, 15, 16, 17, 64, 129])
 def test_valu_prefill_lengths(variant, N):
     wl = W.Workload("t", variant, 1, 3, N, 32, 16, "f32", "f32", seed=N,
@@ -151,7 +151,7 @@ def decode_case(variant, io, B, H, dk, dv, seed=0, steps=1, gate_kind="default")
     return errs
 
 
-@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "gdn", "kda", "ssd"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 128), (128, 16), (64, 64), (128, 128)])
 def test_decode_shapes(variant, io, dk, dv):
@@ -160,7 +160,7 @@ def test_decode_shapes(variant, io, dk, dv):
         assert eo <= TOL[io] and eS <= 1e-5, errs
 
 
-@pytest.mark.parametrize("variant", ["gdn", "gla", "kda"])
+@pytest.mark.parametrize("variant", ["gdn", "gla", "kda", "ssd"])
 def test_decode_many_steps(variant):
     errs = decode_case(variant, "bf16", 4, 8, 128, 128, seed=5, steps=40, gate_kind="default")
     eo, eS = errs[-1]

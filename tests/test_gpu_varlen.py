@@ -18,6 +18,8 @@ def seq_workload(variant, H, n, dk, dv, io, seed):
     kw = dict(seed=seed)
     if variant in ("gla",):
         kw.update(qk_scale=dk ** -0.5, v_scale=dk ** -0.5, gate_kind="slow")
+    if variant == "ssd":
+        kw.update(qk_scale=dk ** -0.5, v_scale=dk ** -0.5, gate_kind="slow")
     if variant in ("gdn", "kda"):
         kw.update(l2norm_qk=True, gate_kind="slow")
     return W.Workload("v", variant, 1, H, n, dk, dv, io, io, **kw)
@@ -37,14 +39,15 @@ def build_case(variant, H, dk, dv, io, lengths, seed=0):
 
 @pytest.mark.parametrize("variant,io,path", [
     ("kath", "bf16", "mfma"), ("gla", "bf16", "mfma"), ("gdn", "bf16", "mfma"), ("kda", "bf16", "mfma"),
-    ("kath", "f32", "valu"), ("gla", "f32", "valu"), ("gdn", "f32", "valu"), ("kda", "f32", "valu")])
+    ("ssd", "bf16", "mfma"), ("kath", "f32", "valu"), ("gla", "f32", "valu"), ("gdn", "f32", "valu"),
+    ("kda", "f32", "valu"), ("ssd", "f32", "valu")])
 def test_varlen_matches_each_sequence(variant, io, path):
     H, dk, dv = 2, 128, 64
     seqs, packed, state, cu = build_case(variant, H, dk, dv, io, LENGTHS)
     d = inputs_to_device(type(seqs[0])(seqs[0].wl, {**packed, **state}, {}))
     cu_t = torch.from_numpy(cu).cuda()
     banner(f"varlen {variant} {io} path={path} lengths={LENGTHS}")
-    segs = 1 if variant in ("kath", "gla") else 0
+    segs = 1 if variant in ("kath", "gla", "ssd") else 0
     o, S, z = bd.prefill_varlen(d["q"], d["k"], d["v"], d.get("g"), d.get("beta"), variant=variant,
                                 cu_seqlens=cu_t, max_seqlen=max(LENGTHS), S0=d["S0"],
                                 z0=d.get("z0"), path=path, segments=segs)
@@ -71,7 +74,7 @@ def test_varlen_matches_each_sequence(variant, io, path):
             assert torch.equal(Si, S[i:i + 1]), i
 
 
-@pytest.mark.parametrize("variant", ["kath", "gla"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "ssd"])
 def test_varlen_segments(variant):
     """Sequences of different lengths cut into several segments each (segments past a
     short sequence's end are identity steps)."""
