@@ -33,6 +33,13 @@ METRIC = "prefill Mtok/s & MFMA util (GLA/GDN chunked); decode state-update HBM 
 MAIN = "gla_bf16_b2h8_n2048_d128"
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2516.6    # dense bf16 MFMA, 256 CU x 4096 flop/clk x 2.4 GHz
+# Selective scan: each state update needs one exponential (v_exp_f32, which takes two issue
+# slots: half the fp32 rate on gfx950, as a throughput probe of independent exponentials
+# measures) and four other fp32 operations (two multiplies, two fused multiply-adds): six
+# slots of a 16-lane SIMD. The chip issues 256 CU x 4 SIMD x 16 lanes x 2.4 GHz = 39.3 T
+# fp32 lane operations per second without packed fp32 (157.3 TFLOP/s counts packed
+# fused multiply-adds), so at most 39.3 T / 6 = 6.55 T state updates per second.
+PEAK_SCAN_UPDATES = 256 * 4 * 16 * 2.4e9 / 6
 PROFILES = os.path.join(ROOT, "profiles")
 # the kernels one prefill step launches, per variant (the roofline covers the whole step)
 STEP_KERNELS = {
@@ -287,6 +294,74 @@ def bench_decode(name, steps, warmup, torch, bd, W, device, stream):
             "finite": bool(torch.isfinite(S).all().item())}
 
 
+def bench_selscan(name, steps, warmup, torch, bd, W, device, stream, graph=True):
+    """Mamba-1 selective scan: state updates (Bt T D n) and tokens per second."""
+    import ctypes
+    wl = W.SELSCAN[name]
+    log(f"selective scan {name}: generating inputs")
+    sets = []
+    for r in range(2):
+        d, _ = W.make_selscan_inputs(wl, with_state=True, seed=wl.seed + 100 * r)
+        sets.append({k: to_dev(v, torch, device) for k, v in d.items()})
+    dt = torch.bfloat16 if wl.io == "bf16" else torch.float32
+    io = bd.LA_BF16 if wl.io == "bf16" else bd.LA_F32
+    desc = bd.ScanDesc(wl.Bt, wl.T, wl.D, wl.n, io, 1)
+    lib = bd.load()
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    outs, args = [], []
+    for s_ in sets:
+        y = torch.empty((wl.Bt, wl.T, wl.D), dtype=dt, device=device)
+        h = torch.empty((wl.Bt, wl.D, wl.n), dtype=torch.float32, device=device)
+        outs.append((y, h))
+        args.append((P(s_["dt"]), P(s_["A"]), P(s_["Bm"]), P(s_["Cm"]), P(s_["x"]),
+                     P(s_["Dskip"]), P(s_["dt_bias"]), P(s_["h0"]), P(y), P(h)))
+    pd = ctypes.byref(desc)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def fn(i):
+        rc = lib.la_selective_scan(pd, *args[i % len(args)], sh)
+        if rc != 0:
+            raise bd.LinAttnError(rc, "la_selective_scan")
+
+    ms = time_eager(fn, steps, warmup, torch, stream)
+    rec = {"workload": name, "eager_ms": ms}
+    if graph:
+        fn(0)
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in outs[0]]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(len(args)):
+                fn(i)
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(1, steps // len(args))
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gms = e0.elapsed_time(e1) / (reps * len(args))
+        same = all(torch.equal(a, b) for a, b in zip(outs[0], ref))
+        rec["graph_replay_matches_eager"] = bool(same)
+        if same:
+            rec["graph_ms"] = gms
+            ms = gms
+        del g
+    s = ms / 1e3
+    updates = wl.Bt * wl.T * wl.D * wl.n
+    byts = W.selscan_algorithmic_bytes(wl)
+    rec.update({"ms": ms, "Mtok_per_s": wl.Bt * wl.T / s / 1e6,
+                "G_state_updates_per_s": updates / s / 1e9,
+                "alu_frac": updates / s / PEAK_SCAN_UPDATES,
+                "GB_per_s": byts / s / 1e9, "hbm_frac": byts / s / 1e9 / PEAK_HBM_GBS,
+                "algorithmic_bytes": byts, "state_updates": updates,
+                "finite": bool(torch.isfinite(outs[0][0].float()).all().item())})
+    return rec
+
+
 def cpu_baseline(case, wl, budget_s=8.0):
     """Time the fp64 oracle on a bounded sample of the workload's sequences."""
     import numpy as np
@@ -373,6 +448,10 @@ def main():
     if main_name.startswith("decode"):
         rec = bench_decode(main_name, args.steps, args.warmup, torch, bd, W, device, stream)
         main_case = None
+    elif main_name.startswith("selscan"):
+        rec = bench_selscan(main_name, args.steps, args.warmup, torch, bd, W, device, stream,
+                            graph=use_graph)
+        main_case = None
     else:
         rotate = 8 if main_name == MAIN else 2
         rec, main_case = bench_prefill(main_name, args.steps, args.warmup, rotate, torch, bd, W,
@@ -396,10 +475,21 @@ def main():
                      "decode_ssd_256x64_dk128_dv64"):
             results[name] = bench_decode(name, 1000, 10, torch, bd, W, device, stream)
             torch.cuda.empty_cache()
+        for name in W.SELSCAN:
+            results[name] = bench_selscan(name, max(10, args.steps // 40), 3, torch, bd, W, device,
+                                          stream, graph=use_graph)
+            torch.cuda.empty_cache()
 
-    wl = W.WORKLOADS[main_name]
+    scan = main_name.startswith("selscan")
+    wl = W.SELSCAN[main_name] if scan else W.WORKLOADS[main_name]
     m = results[main_name]
-    if main_name.startswith("decode"):
+    if scan:
+        value, unit = m["Mtok_per_s"], "Mtok/s"
+        roof = {"bound": "alu", "achieved": m["G_state_updates_per_s"],
+                "peak": PEAK_SCAN_UPDATES / 1e9, "unit": "G state updates/s",
+                "frac": m["alu_frac"], "traffic": load_traffic(main_name),
+                "kernel": "selective_scan_kernel", "duration_us": m["ms"] * 1e3}
+    elif main_name.startswith("decode"):
         value, unit = m["GB_per_s"], "GB/s"
         roof = {"bound": "hbm", "achieved": m["GB_per_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": m["hbm_frac"], "traffic": load_traffic(main_name),
@@ -421,9 +511,11 @@ def main():
         "warmup": args.warmup, "ms_per_step": m["ms"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.io == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": main_name, "variant": wl.variant, "B": wl.B, "H": wl.H, "N": wl.N,
-                   "dk": wl.dk, "dv": wl.dv, "chunk": 64, "state": "fp32",
-                   "parallelism": "single GPU"},
+        "config": ({"workload": main_name, "variant": "selective_scan", "Bt": wl.Bt, "T": wl.T,
+                    "D": wl.D, "n": wl.n, "state": "fp32", "parallelism": "single GPU"} if scan else
+                   {"workload": main_name, "variant": wl.variant, "B": wl.B, "H": wl.H, "N": wl.N,
+                    "dk": wl.dk, "dv": wl.dv, "chunk": 64, "state": "fp32",
+                    "parallelism": "single GPU"}),
         "roofline": roof,
         "cpu_baseline": cpu,
         "workloads": results,

@@ -20,8 +20,8 @@ LA_PATH_AUTO, LA_PATH_VALU, LA_PATH_MFMA = 0, 1, 2
 VARIANTS = {"kath": LA_KATH, "gla": LA_GLA, "gdn": LA_GDN, "kda": LA_KDA, "ssd": LA_SSD}
 PATHS = {"auto": LA_PATH_AUTO, "valu": LA_PATH_VALU, "mfma": LA_PATH_MFMA}
 EXPORTS = ("la_prefill", "la_prefill_workspace_size", "la_prefill_varlen",
-           "la_prefill_varlen_workspace_size", "la_decode_step", "la_status_str",
-           "la_abi_version")
+           "la_prefill_varlen_workspace_size", "la_decode_step", "la_selective_scan",
+           "la_status_str", "la_abi_version")
 
 
 class LinAttnError(RuntimeError):
@@ -37,6 +37,13 @@ class Desc(ctypes.Structure):
         ("variant", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
         ("gate_dtype", ctypes.c_int32), ("eps", ctypes.c_float),
         ("path", ctypes.c_int32), ("chunk", ctypes.c_int32), ("segments", ctypes.c_int32),
+    ]
+
+
+class ScanDesc(ctypes.Structure):
+    _fields_ = [
+        ("Bt", ctypes.c_int32), ("T", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("n", ctypes.c_int32), ("io_dtype", ctypes.c_int32), ("dt_softplus", ctypes.c_int32),
     ]
 
 
@@ -66,6 +73,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.la_prefill_varlen_workspace_size.restype = ctypes.c_int
     lib.la_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.la_decode_step.restype = ctypes.c_int
+    lib.la_selective_scan.argtypes = [ctypes.POINTER(ScanDesc), vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, vp, vp]
+    lib.la_selective_scan.restype = ctypes.c_int
     lib.la_status_str.argtypes = [ctypes.c_int]
     lib.la_status_str.restype = ctypes.c_char_p
     lib.la_abi_version.argtypes = []
@@ -234,3 +244,31 @@ def decode_step(q, k, v, S, g=None, beta=None, *, variant: str, z=None, eps: flo
                             _ptr(S), _ptr(z), _ptr(o), _stream_handle(stream, q.device))
     _check(rc, "la_decode_step")
     return o
+
+
+def selective_scan(dt, A, Bm, Cm, x, Dskip=None, dt_bias=None, *, dt_softplus: bool = True,
+                   h0=None, y=None, h_final=None, stream=None):
+    """Mamba-1 selective scan through ``la_selective_scan``.
+
+    dt, x [Bt,T,D] and Bm, Cm [Bt,T,n] (float32 or bfloat16, one dtype); A [D,n],
+    Dskip [D], dt_bias [D] and h0 [Bt,D,n] float32 (the last three optional).
+    h_final may be h0 (in place). Returns (y [Bt,T,D], h_final [Bt,D,n]).
+    """
+    import torch
+    lib = load()
+    Bt, T, D = x.shape
+    n = A.shape[1]
+    for name, t in (("dt", dt), ("A", A), ("Bm", Bm), ("Cm", Cm), ("x", x), ("Dskip", Dskip),
+                    ("dt_bias", dt_bias), ("h0", h0), ("y", y), ("h_final", h_final)):
+        _require_contig(name, t)
+    desc = ScanDesc(Bt, T, D, n, _dtype_code(x), 1 if dt_softplus else 0)
+    dev = x.device
+    if y is None:
+        y = torch.empty((Bt, T, D), dtype=x.dtype, device=dev)
+    if h_final is None:
+        h_final = torch.empty((Bt, D, n), dtype=torch.float32, device=dev)
+    rc = lib.la_selective_scan(ctypes.byref(desc), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(x),
+                               _ptr(Dskip), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final),
+                               _stream_handle(stream, dev))
+    _check(rc, "la_selective_scan")
+    return y, h_final

@@ -29,6 +29,7 @@ COMMON = [
 ]
 
 SOURCES = ["la_api.cpp", "decode.hip", "prefill_valu.hip", "prefill_kath_mfma.hip", "prefill_kda_mfma.hip",
+           "selective_scan.hip",
            "prefill_gla_mfma.hip", "prefill_gdn_mfma.hip"]
 
 

@@ -356,4 +356,63 @@ int la_decode_step(const la_desc* d, const void* q, const void* k, const void* v
     return err == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
+int la_selective_scan(const la_scan_desc* d, const void* dt, const float* A, const void* Bm,
+                      const void* Cm, const void* x, const float* Dskip, const float* dt_bias,
+                      const float* h0, void* y, float* h_final, void* stream) {
+    if (!d) return LA_ERR_INVALID;
+    if (d->io_dtype != LA_F32 && d->io_dtype != LA_BF16) return LA_ERR_INVALID;
+    if (d->Bt < 0 || d->T < 0 || d->D < 0 || d->n < 0) return LA_ERR_INVALID;
+    if (d->dt_softplus != 0 && d->dt_softplus != 1) return LA_ERR_INVALID;
+    if (!la::selective_scan_supported(d->n)) return LA_ERR_UNSUPPORTED;
+    const uint64_t isz = d->io_dtype == LA_BF16 ? 2 : 4;
+    const uint64_t rows = uint64_t(d->Bt), T = uint64_t(d->T), D = uint64_t(d->D),
+                   n = uint64_t(d->n);
+    const uint64_t s_tok = mul(mul(mul(rows, T), D), isz);   // dt, x, y
+    const uint64_t s_bc = mul(mul(mul(rows, T), n), isz);    // B, C
+    const uint64_t s_A = mul(mul(D, n), 4), s_ch = mul(D, 4);
+    const uint64_t s_h = mul(mul(mul(rows, D), n), 4);
+    if (s_tok == UINT64_MAX || s_bc == UINT64_MAX || s_A == UINT64_MAX || s_h == UINT64_MAX)
+        return LA_ERR_INVALID;
+    const bool states = rows * D > 0;
+    const bool tokens = states && T > 0;
+    if (states && (!A || !h_final)) return LA_ERR_INVALID;
+    if (tokens && (!dt || !Bm || !Cm || !x || !y)) return LA_ERR_INVALID;
+    // alignment: element alignment for the per-channel token arrays, 16 bytes for the rows
+    // of B and C and for A and the states (read as 16-byte pieces)
+    const void* a16[] = {Bm, Cm, A, h0, h_final};
+    for (const void* ptr : a16)
+        if (ptr && !aligned(ptr, 16)) return LA_ERR_INVALID;
+    const void* ael[] = {dt, x, y};
+    for (const void* ptr : ael)
+        if (ptr && !aligned(ptr, isz)) return LA_ERR_INVALID;
+    if ((Dskip && !aligned(Dskip, 4)) || (dt_bias && !aligned(dt_bias, 4))) return LA_ERR_INVALID;
+    // aliasing: y overlaps nothing; h_final overlaps only h0, and only exactly
+    const uint64_t tk = tokens ? 1 : 0;
+    const Range rdt = range(dt, s_tok * tk), rx = range(x, s_tok * tk), ry = range(y, s_tok * tk),
+                rB = range(Bm, s_bc * tk), rC = range(Cm, s_bc * tk), rA = range(A, s_A),
+                rD = range(Dskip, s_ch), rb = range(dt_bias, s_ch), rh0 = range(h0, s_h),
+                rh = range(h_final, s_h);
+    const Range ins[] = {rdt, rx, rB, rC, rA, rD, rb, rh0, rh};
+    for (const Range& r : ins)
+        if (overlap(ry, r)) return LA_ERR_INVALID;
+    const Range others[] = {rdt, rx, rB, rC, rA, rD, rb};
+    for (const Range& r : others)
+        if (overlap(rh, r)) return LA_ERR_INVALID;
+    if (overlap(rh, rh0) && h_final != h0) return LA_ERR_INVALID;
+    if (!states) return LA_OK;
+
+    la::ScanProblem p;
+    p.Bt = d->Bt; p.T = d->T; p.D = d->D; p.n = d->n;
+    p.io_bf16 = d->io_dtype == LA_BF16;
+    p.dt_softplus = d->dt_softplus;
+    p.dt = dt; p.Bm = Bm; p.Cm = Cm; p.x = x;
+    p.A = A; p.Dskip = Dskip; p.dt_bias = dt_bias; p.h0 = h0;
+    p.y = y; p.hT = h_final;
+    p.stream = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    hipError_t err = la::launch_selective_scan(p);
+    if (err == hipSuccess) err = hipGetLastError();
+    return err == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
 }  // extern "C"

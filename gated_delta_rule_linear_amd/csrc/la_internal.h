@@ -63,4 +63,18 @@ bool gdn_mfma_supported(int dk, int dv, bool io_bf16);
 size_t gdn_mfma_workspace_bytes(const Problem& p);
 hipError_t launch_prefill_gdn_mfma(const Problem& p);
 
+// selective_scan.hip (Mamba-1 selective scan), a validated call
+struct ScanProblem {
+    int Bt = 0, T = 0, D = 0, n = 0;
+    bool io_bf16 = false;
+    int dt_softplus = 0;
+    const void *dt = nullptr, *Bm = nullptr, *Cm = nullptr, *x = nullptr;
+    const float *A = nullptr, *Dskip = nullptr, *dt_bias = nullptr, *h0 = nullptr;
+    void* y = nullptr;
+    float* hT = nullptr;
+    hipStream_t stream = nullptr;
+};
+bool selective_scan_supported(int n);
+hipError_t launch_selective_scan(const ScanProblem& p);
+
 }  // namespace la

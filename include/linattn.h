@@ -176,6 +176,44 @@ int la_decode_step(const la_desc* d, const void* q, const void* k, const void* v
                    const void* g, const void* beta, float* S, float* z, void* o,
                    void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * Selective scan (Mamba-1 / S6): "Linear / RNN 路线", section 3.5 (the boxed
+ * discretisation Abar_t = exp(Delta_t A), Bbar_t = Delta_t B_t with Delta, B and C
+ * computed from the input) and the simplified block's forward in section 3.6;
+ * "状态空间与线性注意力", sections Selective SSM (h_t = Abar_t h_{t-1} + Bbar_t x_t,
+ * y_t = C_t h_t) and 卷积与递推的等价 (the D x_t skip). Every batch row b and channel d
+ * carries a state h_{b,d} in R^n, one decay rate per (channel, state entry):
+ *   Delta = softplus(dt_{t,d} + dt_bias_d)      (dt_softplus = 1; dt + dt_bias when 0)
+ *   h_{d,i} <- exp(Delta A_{d,i}) h_{d,i} + Delta B_{t,i} x_{t,d}      (i < n)
+ *   y_{t,d}  = sum_i C_{t,i} h_{d,i} + D_d x_{t,d}
+ * B_t and C_t are shared by all channels of a row. The arithmetic is fp32 with an fp32
+ * state; exp is the hardware base-2 exponential of Delta A log2(e).
+ * ------------------------------------------------------------------------------------ */
+typedef struct la_scan_desc {
+    int32_t Bt;           /* batch rows */
+    int32_t T;            /* tokens per row; T = 1 with h_final == h0 is one decode step */
+    int32_t D;            /* channels */
+    int32_t n;            /* state entries per channel: 16, 32, 64 or 128 */
+    int32_t io_dtype;     /* LA_F32 | LA_BF16: dt, B, C, x and y */
+    int32_t dt_softplus;  /* 1: Delta = softplus(dt + dt_bias); 0: Delta = dt + dt_bias */
+} la_scan_desc;
+
+/* Whole-sequence selective scan.
+ *   dt, x     [Bt, T, D] io            A        [D, n] fp32 (negative for a decay)
+ *   Bm, Cm    [Bt, T, n] io            Dskip    [D] fp32, or NULL for no skip
+ *   dt_bias   [D] fp32, or NULL (zero) h0       [Bt, D, n] fp32, or NULL (zeros)
+ *   y         [Bt, T, D] io, written (bf16: rounded to nearest even from fp32)
+ *   h_final   [Bt, D, n] fp32, written; may be the same pointer as h0 (in place) but
+ *             must not otherwise overlap anything; y must not overlap any buffer.
+ * Alignment: Bm, Cm, A, h0 and h_final 16 bytes; dt, x and y their element size; Dskip
+ * and dt_bias 4 bytes. All buffers are device memory owned by the caller; the call only
+ * enqueues work on the stream. T = 0 copies h0 (or zeros) to h_final; Bt * D = 0 does
+ * nothing. Errors as for la_prefill: LA_ERR_INVALID (null required pointer, bad dtype or
+ * flag, negative size, misalignment, overlap), LA_ERR_UNSUPPORTED (n), LA_ERR_HIP. */
+int la_selective_scan(const la_scan_desc* d, const void* dt, const float* A, const void* Bm,
+                      const void* Cm, const void* x, const float* Dskip, const float* dt_bias,
+                      const float* h0, void* y, float* h_final, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* la_status_str(int status);
 

@@ -273,3 +273,82 @@ def test_prefill_varlen_rejects(lib, case):
                                p.get("g"), p.get("beta"), None, None, p["o"], p["S"], None,
                                None, 0, None)
     assert rc == bd.LA_ERR_INVALID, (case, rc)
+
+
+# ------------------------------------------------------------------ selective scan
+
+
+def scan_args():
+    return dict(dt=addr(0), A=addr(1), Bm=addr(2), Cm=addr(3), x=addr(4), Dskip=addr(5),
+                dt_bias=addr(6), h0=addr(7), y=addr(8), h_final=addr(9))
+
+
+def call_scan(lib, desc, **p):
+    return lib.la_selective_scan(ctypes.byref(desc) if desc is not None else None, p["dt"],
+                                 p["A"], p["Bm"], p["Cm"], p["x"], p["Dskip"], p["dt_bias"],
+                                 p["h0"], p["y"], p["h_final"], None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_desc", bd.LA_ERR_INVALID),
+    ("bad_io", bd.LA_ERR_INVALID),
+    ("bad_softplus_flag", bd.LA_ERR_INVALID),
+    ("negative_T", bd.LA_ERR_INVALID),
+    ("n_48", bd.LA_ERR_UNSUPPORTED),
+    ("n_256", bd.LA_ERR_UNSUPPORTED),
+    ("null_x", bd.LA_ERR_INVALID),
+    ("null_A", bd.LA_ERR_INVALID),
+    ("null_h_final", bd.LA_ERR_INVALID),
+    ("misaligned_B", bd.LA_ERR_INVALID),
+    ("misaligned_h0", bd.LA_ERR_INVALID),
+    ("misaligned_dt_bf16", bd.LA_ERR_INVALID),
+    ("y_overlaps_x", bd.LA_ERR_INVALID),
+    ("h_partial_overlap_h0", bd.LA_ERR_INVALID),
+    ("h_overlaps_A", bd.LA_ERR_INVALID),
+])
+def test_selective_scan_rejects(lib, case, expect):
+    d = bd.ScanDesc(2, 50, 40, 16, bd.LA_BF16, 1)
+    p = scan_args()
+    if case == "null_desc":
+        d = None
+    elif case == "bad_io":
+        d.io_dtype = 5
+    elif case == "bad_softplus_flag":
+        d.dt_softplus = 2
+    elif case == "negative_T":
+        d.T = -1
+    elif case == "n_48":
+        d.n = 48
+    elif case == "n_256":
+        d.n = 256
+    elif case == "null_x":
+        p["x"] = None
+    elif case == "null_A":
+        p["A"] = None
+    elif case == "null_h_final":
+        p["h_final"] = None
+    elif case == "misaligned_B":
+        p["Bm"] = addr(2, 8)
+    elif case == "misaligned_h0":
+        p["h0"] = addr(7, 4)
+    elif case == "misaligned_dt_bf16":
+        p["dt"] = addr(0, 1)
+    elif case == "y_overlaps_x":
+        p["y"] = addr(4, 64)
+    elif case == "h_partial_overlap_h0":
+        p["h_final"] = addr(7, 16)
+    elif case == "h_overlaps_A":
+        p["h_final"] = addr(1, 16)
+    assert call_scan(lib, d, **p) == expect
+
+
+def test_selective_scan_accepts_and_noops(lib):
+    p = scan_args()
+    # no rows or no channels: validated, then nothing to do
+    assert call_scan(lib, bd.ScanDesc(0, 50, 40, 16, bd.LA_BF16, 1), **p) == bd.LA_OK
+    assert call_scan(lib, bd.ScanDesc(2, 50, 0, 16, bd.LA_F32, 0), **p) == bd.LA_OK
+    # optional inputs may be absent; h_final may be h0 exactly (in place)
+    p2 = dict(p, Dskip=None, dt_bias=None, h0=None)
+    assert call_scan(lib, bd.ScanDesc(0, 5, 8, 32, bd.LA_F32, 0), **p2) == bd.LA_OK
+    p3 = dict(p, h_final=p["h0"])
+    assert call_scan(lib, bd.ScanDesc(0, 5, 8, 32, bd.LA_F32, 0), **p3) == bd.LA_OK
