@@ -37,6 +37,8 @@ STEP_KERNELS = {
     "gdn_bf16_b4h16_n8192_d128": [r"gdn_prep_kernel<", r"gdn_fwd_kernel<"],
     "kda_bf16_b4h16_n8192_d128": [r"kda_prep_kernel<", r"kda_fwd_kernel<"],
     "kath_f32_n256_d16": [r"prefill_valu_kernel<0,"],
+    "selscan_bf16_b2_t4096_d2048_n128": [r"selective_scan_kernel<128,"],
+    "selscan_bf16_b2_t4096_d2048_n16": [r"selective_scan_kernel<16,"],
     "decode_gdn_256x32_d128": [r"decode_kernel<2,"],
     "decode_gla_256x32_d128": [r"decode_kernel<1,"],
     "decode_kda_256x32_d128": [r"decode_kernel<3,"],
