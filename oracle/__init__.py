@@ -80,6 +80,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.oracle_decode_step.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp, ctypes.c_double,
                                        dp, dp, dp, i]
     lib.oracle_decode_step.restype = i
+    lib.oracle_prefill_backward.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp,
+                                            ctypes.c_double, dp, dp, dp, dp, dp, dp, dp, dp, dp,
+                                            dp, i]
+    lib.oracle_prefill_backward.restype = i
     lib.oracle_selective_scan.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp, dp, i, dp, dp, dp,
                                           i]
     lib.oracle_selective_scan.restype = i
@@ -172,6 +176,41 @@ def decode_step(variant, q, k, v, S, g=None, beta=None, z=None, eps=1e-6, thread
     if rc != 0:
         raise ValueError("oracle_decode_step rejected its arguments")
     return o
+
+
+def prefill_backward(variant, q, k, v, g=None, beta=None, S0=None, z0=None, dO=None,
+                     dS_final=None, dz_final=None, eps=1e-6, threads: int = 0,
+                     lib_path: str | None = None):
+    """Reverse-mode gradients of ``prefill`` for the loss with dL/do = dO, dL/dS_final =
+    dS_final (and dL/dz_final = dz_final, KATH); None means zero.
+
+    Returns a dict: dq, dk [B,H,N,dk], dv [B,H,N,dv], dg (shaped like g, or None for
+    KATH), dbeta [B,H,N] (GDN, KDA) or None, dS0 [B,H,dk,dv], dz0 [B,H,dk] (KATH) or None.
+    """
+    lib = load(lib_path)
+    vt = _variant(variant)
+    q, k, v, g, beta, S0, z0, dO, dS_final, dz_final = map(
+        _f64, (q, k, v, g, beta, S0, z0, dO, dS_final, dz_final))
+    B, H, N, dk = q.shape
+    dv = v.shape[3]
+    assert dO is not None and dO.shape == (B, H, N, dv)
+    if dS_final is not None:
+        assert dS_final.shape == (B, H, dk, dv)
+    out = {"dq": np.zeros((B, H, N, dk)), "dk": np.zeros((B, H, N, dk)),
+           "dv": np.zeros((B, H, N, dv)),
+           "dg": None if vt == KATH else np.zeros(g.shape),
+           "dbeta": np.zeros((B, H, N)) if vt in (GDN, KDA) else None,
+           "dS0": np.zeros((B, H, dk, dv)),
+           "dz0": np.zeros((B, H, dk)) if vt == KATH else None}
+    rc = lib.oracle_prefill_backward(vt, B, H, N, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                     _ptr(beta), _ptr(S0), _ptr(z0), float(eps), _ptr(dO),
+                                     _ptr(dS_final), _ptr(dz_final), _ptr(out["dq"]),
+                                     _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                                     _ptr(out["dbeta"]), _ptr(out["dS0"]), _ptr(out["dz0"]),
+                                     int(threads))
+    if rc != 0:
+        raise ValueError("oracle_prefill_backward rejected its arguments")
+    return out
 
 
 def selective_scan(dt, A, Bm, Cm, x, Dskip=None, dt_bias=None, dt_softplus: bool = False,

@@ -50,6 +50,27 @@
  *
  * Decode is the same per-token body applied once, in place.
  *
+ * Backward (the training side of the same prefill; the pages note that training keeps
+ * length-N activations and may recompute states): for a loss L with given dL/do_t and
+ * dL/dS_final (and dL/dz_final for KATH), the gradients with respect to every input,
+ * by reverse-mode differentiation of the token recurrence above, step by step in
+ * reverse token order with every state of the forward pass kept. With dS = dL/dS_t
+ * (everything after token t, plus the output path q_t dO_t^T added at token t):
+ *   GLA   dq = S_t dO; dk = dS v; dv = dS^T k; dg_i = sum_j dS_ij S_{t-1,ij};
+ *         dS_{t-1} = diag(g) dS
+ *   SSD   as GLA with one decay: da = sum_ij dS_ij S_{t-1,ij}; dS_{t-1} = a dS
+ *   GDN   p = S_{t-1}^T k, u = b (v - a p): du = dS^T k; dk = dS u + S_{t-1} dp with
+ *         dp = -a b du; dv = b du; db = du . (v - a p); da = <dS, S_{t-1}> - b du . p;
+ *         dS_{t-1} = a dS + k dp^T
+ *   KDA   Sbar = Diag(a) S_{t-1}, p = Sbar^T k, u = b (v - p): du = dS^T k; dv = b du;
+ *         db = du . (v - p); dp = -b du; dSbar = dS + k dp^T; dk = dS u + Sbar dp;
+ *         da_i = sum_j dSbar_ij S_{t-1,ij}; dS_{t-1} = Diag(a) dSbar
+ *   KATH  o = n / d with n = S_t^T phi(q), d = phi(q) . z_t + eps: dn = dO / d,
+ *         dd = -(dO . o) / d; dphi(q) = S_t dn + z_t dd; dS += phi(q) dn^T;
+ *         dz += phi(q) dd; dphi(k) = dS v + dz; dv = dS^T phi(k); dS_{t-1} = dS,
+ *         dz_{t-1} = dz; dq = dphi(q) phi'(q), dk = dphi(k) phi'(k)
+ * and dS0 = dS_0 (dz0 = dz_0).
+ *
  * Counters (work accounting, "线性注意力与 SSM" section 02 hand count): each
  * state-update multiply-add and each state-read multiply-add is counted as it
  * is executed.
@@ -343,6 +364,211 @@ int oracle_selective_scan(int Bt, int T, int D, int n, const double *dt, const d
             for (i = 0; i < n; ++i) acc += Cm[tok * n + i] * h[i];
             y[tok * D + d] = acc + (Dskip ? Dskip[d] * xt : 0.0);
         }
+    }
+    return 0;
+}
+
+/* Backward of one token: S_prev / z_prev the state before the token, S_post / z_post
+ * after it; dS / dz hold dL/dS_post (without this token's output path) on entry and
+ * dL/dS_prev on return. work: at least 2 dk + 3 dv doubles. */
+static void token_backward(int variant, int dk, int dv, const double *q, const double *k,
+                           const double *v, const double *g, double beta, double eps,
+                           const double *S_prev, const double *S_post, const double *z_post,
+                           const double *dO, double *dS, double *dz, double *dq, double *dk_,
+                           double *dv_, double *dg, double *dbeta, double *work)
+{
+    int i, j;
+    if (variant == OR_KATH) {
+        double *fq = work, *fk = work + dk, *dn = work + 2 * dk, *o = work + 2 * dk + dv;
+        double den = eps, dd = 0.0;
+        for (i = 0; i < dk; ++i) {
+            fq[i] = elu_plus_one(q[i]);
+            fk[i] = elu_plus_one(k[i]);
+            den += fq[i] * z_post[i];
+        }
+        for (j = 0; j < dv; ++j) {
+            double num = 0.0;
+            for (i = 0; i < dk; ++i) num += fq[i] * S_post[(size_t)i * dv + j];
+            o[j] = num / den;
+            dn[j] = dO[j] / den;
+            dd -= dO[j] * o[j] / den;
+        }
+        for (i = 0; i < dk; ++i) {
+            double dfq = z_post[i] * dd;
+            for (j = 0; j < dv; ++j) dfq += S_post[(size_t)i * dv + j] * dn[j];
+            dq[i] = dfq * (q[i] > 0.0 ? 1.0 : exp(q[i]));
+            for (j = 0; j < dv; ++j) dS[(size_t)i * dv + j] += fq[i] * dn[j];
+            dz[i] += fq[i] * dd;
+        }
+        for (i = 0; i < dk; ++i) {
+            double dfk = dz[i];
+            for (j = 0; j < dv; ++j) dfk += dS[(size_t)i * dv + j] * v[j];
+            dk_[i] = dfk * (k[i] > 0.0 ? 1.0 : exp(k[i]));
+        }
+        for (j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (i = 0; i < dk; ++i) acc += dS[(size_t)i * dv + j] * fk[i];
+            dv_[j] = acc;
+        }
+        return;   /* dS and dz pass through unchanged: S_t = S_{t-1} + ..., z_t = z_{t-1} + ... */
+    }
+    /* the output read o = S_post^T q */
+    for (i = 0; i < dk; ++i) {
+        double acc = 0.0;
+        for (j = 0; j < dv; ++j) acc += S_post[(size_t)i * dv + j] * dO[j];
+        dq[i] = acc;
+        for (j = 0; j < dv; ++j) dS[(size_t)i * dv + j] += q[i] * dO[j];
+    }
+    if (variant == OR_GLA || variant == OR_SSD) {
+        double dsum = 0.0;
+        for (i = 0; i < dk; ++i) {
+            double acc = 0.0, gi = variant == OR_GLA ? g[i] : g[0];
+            for (j = 0; j < dv; ++j) acc += dS[(size_t)i * dv + j] * v[j];
+            dk_[i] = acc;
+            acc = 0.0;
+            for (j = 0; j < dv; ++j) acc += dS[(size_t)i * dv + j] * S_prev[(size_t)i * dv + j];
+            if (variant == OR_GLA) dg[i] = acc;
+            else dsum += acc;
+            (void)gi;
+        }
+        if (variant == OR_SSD) dg[0] = dsum;
+        for (j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (i = 0; i < dk; ++i) acc += dS[(size_t)i * dv + j] * k[i];
+            dv_[j] = acc;
+        }
+        for (i = 0; i < dk; ++i) {
+            const double gi = variant == OR_GLA ? g[i] : g[0];
+            for (j = 0; j < dv; ++j) dS[(size_t)i * dv + j] *= gi;
+        }
+        return;
+    }
+    {
+        /* delta rule: p = Sdec^T k with Sdec = alpha S_prev (GDN: alpha scalar; KDA:
+         * Diag(alpha) S_prev), u = beta (v - p); S_post = Sdec + k u^T */
+        double *u = work, *du = work + dv, *dp = work + 2 * dv, *p = work + 3 * dv;
+        double da = 0.0, db = 0.0;
+        for (j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (i = 0; i < dk; ++i) {
+                const double ai = variant == OR_GDN ? g[0] : g[i];
+                acc += ai * S_prev[(size_t)i * dv + j] * k[i];
+            }
+            p[j] = acc;
+            u[j] = beta * (v[j] - acc);
+        }
+        for (j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (i = 0; i < dk; ++i) acc += dS[(size_t)i * dv + j] * k[i];
+            du[j] = acc;
+            dv_[j] = beta * acc;
+            db += acc * (v[j] - p[j]);
+            dp[j] = -beta * acc;
+        }
+        *dbeta = db;
+        for (i = 0; i < dk; ++i) {
+            const double ai = variant == OR_GDN ? g[0] : g[i];
+            double acc = 0.0, accp = 0.0;
+            for (j = 0; j < dv; ++j) {
+                acc += dS[(size_t)i * dv + j] * u[j];
+                accp += ai * S_prev[(size_t)i * dv + j] * dp[j];
+            }
+            dk_[i] = acc + accp;
+        }
+        /* dSdec = dS + k dp^T; dalpha from Sdec = alpha S_prev; dS_prev = alpha dSdec */
+        for (i = 0; i < dk; ++i) {
+            const double ai = variant == OR_GDN ? g[0] : g[i];
+            double acc = 0.0;
+            for (j = 0; j < dv; ++j) {
+                const double dsd = dS[(size_t)i * dv + j] + k[i] * dp[j];
+                acc += dsd * S_prev[(size_t)i * dv + j];
+                dS[(size_t)i * dv + j] = ai * dsd;
+            }
+            if (variant == OR_GDN) da += acc;
+            else dg[i] = acc;
+        }
+        if (variant == OR_GDN) dg[0] = da;
+    }
+}
+
+/*
+ * Whole-sequence backward (reverse-mode derivative of oracle_prefill).
+ * Inputs as for oracle_prefill, plus
+ *   dO: [B,H,N,dv]; dS_final: [B,H,dk,dv] or NULL (zero); dz_final: [B,H,dk] or NULL (KATH)
+ * Outputs (all required unless noted):
+ *   dq, dk: [B,H,N,dk]; dv: [B,H,N,dv]; dg: shaped like g (NULL for KATH);
+ *   dbeta: [B,H,N] (GDN, KDA; NULL otherwise); dS0: [B,H,dk,dv]; dz0: [B,H,dk] (KATH)
+ * Returns 0, or 1 on a bad argument.
+ */
+int oracle_prefill_backward(int variant, int B, int H, int N, int dk, int dv,
+                            const double *q, const double *k, const double *v,
+                            const double *g, const double *beta,
+                            const double *S0, const double *z0, double eps,
+                            const double *dO, const double *dS_final, const double *dz_final,
+                            double *dq, double *dk_, double *dv_, double *dg, double *dbeta,
+                            double *dS0, double *dz0, int threads)
+{
+    long long seq, nseq;
+    const int gw = (variant == OR_GLA || variant == OR_KDA) ? dk : 1;
+    if (check_args(variant, B, H, N, dk, dv)) return 1;
+    if (!dO || !dq || !dk_ || !dv_ || !dS0) return 1;
+    if (variant != OR_KATH && (!g || !dg)) return 1;
+    if ((variant == OR_GDN || variant == OR_KDA) && (!beta || !dbeta)) return 1;
+    if (variant == OR_KATH && !dz0) return 1;
+    nseq = (long long)B * H;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel
+    {
+        oracle_counts c;
+        const size_t SS = (size_t)dk * dv;
+        double *work = (double *)malloc(sizeof(double) * (size_t)(2 * dk + 4 * dv + 8));
+        double *states = (double *)malloc(sizeof(double) * SS * (size_t)(N + 1));
+        double *zs = (double *)malloc(sizeof(double) * (size_t)dk * (size_t)(N + 1));
+        double *ot = (double *)malloc(sizeof(double) * (size_t)(dv + 1));
+        double *dS = (double *)malloc(sizeof(double) * SS);
+        double *dz = (double *)malloc(sizeof(double) * (size_t)dk);
+        memset(&c, 0, sizeof(c));
+#pragma omp for schedule(dynamic, 1)
+        for (seq = 0; seq < nseq; ++seq) {
+            int t;
+            if (S0) memcpy(states, S0 + (size_t)seq * SS, sizeof(double) * SS);
+            else memset(states, 0, sizeof(double) * SS);
+            if (variant == OR_KATH && z0) memcpy(zs, z0 + (size_t)seq * dk, sizeof(double) * (size_t)dk);
+            else memset(zs, 0, sizeof(double) * (size_t)dk);
+            /* forward, keeping every state */
+            for (t = 0; t < N; ++t) {
+                const size_t tok = (size_t)seq * N + t;
+                const double *gt = g ? g + tok * gw : NULL;
+                const double bt = beta ? beta[tok] : 0.0;
+                memcpy(states + SS * (size_t)(t + 1), states + SS * (size_t)t, sizeof(double) * SS);
+                memcpy(zs + (size_t)dk * (t + 1), zs + (size_t)dk * t, sizeof(double) * (size_t)dk);
+                token_step(variant, dk, dv, q + tok * dk, k + tok * dk, v + tok * dv, gt, bt, eps,
+                           states + SS * (size_t)(t + 1), zs + (size_t)dk * (t + 1), ot, work, &c);
+            }
+            /* backward */
+            if (dS_final) memcpy(dS, dS_final + (size_t)seq * SS, sizeof(double) * SS);
+            else memset(dS, 0, sizeof(double) * SS);
+            if (variant == OR_KATH && dz_final) memcpy(dz, dz_final + (size_t)seq * dk, sizeof(double) * (size_t)dk);
+            else memset(dz, 0, sizeof(double) * (size_t)dk);
+            for (t = N - 1; t >= 0; --t) {
+                const size_t tok = (size_t)seq * N + t;
+                const double *gt = g ? g + tok * gw : NULL;
+                const double bt = beta ? beta[tok] : 0.0;
+                double dbt = 0.0;
+                token_backward(variant, dk, dv, q + tok * dk, k + tok * dk, v + tok * dv, gt, bt, eps,
+                               states + SS * (size_t)t, states + SS * (size_t)(t + 1),
+                               zs + (size_t)dk * (t + 1), dO + tok * dv, dS, dz, dq + tok * dk,
+                               dk_ + tok * dk, dv_ + tok * dv, dg ? dg + tok * gw : NULL, &dbt, work);
+                if (dbeta) dbeta[tok] = dbt;
+            }
+            memcpy(dS0 + (size_t)seq * SS, dS, sizeof(double) * SS);
+            if (variant == OR_KATH) memcpy(dz0 + (size_t)seq * dk, dz, sizeof(double) * (size_t)dk);
+        }
+        free(work); free(states); free(zs); free(ot); free(dS); free(dz);
     }
     return 0;
 }

@@ -645,9 +645,130 @@ def pin_selective_scan_is_ssd(lib=None):
     assert rel(hT, S.transpose(0, 1, 3, 2).reshape(Bt, D, n)) < 1e-12
 
 
+# ---------------------------------------------------------------------------
+# Backward
+# ---------------------------------------------------------------------------
+
+def _loss(variant, case, dO, dSf, dzf, lib):
+    """L = <dO, o> + <dS_final, S_final> (+ <dz_final, z_final>): its gradients are what the
+    backward returns for that (dO, dS_final, dz_final)."""
+    o, S, z = run(variant, case, lib)
+    L = float(np.sum(dO * o) + np.sum(dSf * S))
+    if variant == "kath":
+        L += float(np.sum(dzf * z))
+    return L
+
+
+def _bwd_case(variant, seed):
+    case = rand_case(variant, B=1, H=2, N=6, dk=3, dv=2, seed=seed, with_state=True)
+    rng = np.random.default_rng(seed + 1000)
+    dO = rng.standard_normal(case["v"].shape)
+    dSf = rng.standard_normal(case["S0"].shape)
+    dzf = rng.standard_normal(case["z0"].shape) if variant == "kath" else None
+    return case, dO, dSf, dzf
+
+
+def _bwd(variant, case, dO, dSf, dzf, lib):
+    return oracle.prefill_backward(variant, case["q"], case["k"], case["v"], case["g"],
+                                   case["beta"], case["S0"], case["z0"], dO, dSf, dzf,
+                                   lib_path=lib)
+
+
+def pin_backward_finite_differences(lib=None):
+    """Every gradient of every variant against central finite differences of the forward
+    (the definition of the derivative): h = 1e-5 in fp64, agreement to 1e-6 of the largest
+    gradient entry. The forward itself is pinned above."""
+    names = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "beta": "dbeta", "S0": "dS0",
+             "z0": "dz0"}
+    for variant in ("kath", "gla", "gdn", "kda", "ssd"):
+        case, dO, dSf, dzf = _bwd_case(variant, seed=51)
+        grads = _bwd(variant, case, dO, dSf, dzf, lib)
+        for arg, gname in names.items():
+            if case.get(arg) is None:
+                continue
+            x = case[arg]
+            fd = np.zeros_like(x)
+            h = 1e-5
+            for idx in np.ndindex(x.shape):
+                old = x[idx]
+                x[idx] = old + h
+                lp = _loss(variant, case, dO, dSf, dzf, lib)
+                x[idx] = old - h
+                lm = _loss(variant, case, dO, dSf, dzf, lib)
+                x[idx] = old
+                fd[idx] = (lp - lm) / (2 * h)
+            got = grads[gname]
+            assert got is not None and got.shape == x.shape, (variant, gname)
+            err = np.max(np.abs(got - fd)) / max(np.max(np.abs(fd)), 1e-12)
+            assert err < 1e-6, f"{variant} {gname} vs finite differences: {err:.2e}"
+
+
+def pin_backward_closed_form(lib=None):
+    """Ungated causal linear attention O = tril(Q K^T) V (GLA with g = 1, no initial state,
+    no final-state gradient): dQ = tril(dO V^T) K, dK = tril(dO V^T)^T Q,
+    dV = tril(Q K^T)^T dO."""
+    case = rand_case("gla", B=1, H=1, N=9, dk=4, dv=3, seed=52, with_state=False)
+    case["g"] = np.ones_like(case["g"])
+    rng = np.random.default_rng(53)
+    dO = rng.standard_normal(case["v"].shape)
+    grads = _bwd("gla", case, dO, None, None, lib)
+    Q, K, V, G = case["q"][0, 0], case["k"][0, 0], case["v"][0, 0], dO[0, 0]
+    M = np.tril(np.ones((9, 9)))
+    A = (G @ V.T) * M
+    assert rel(grads["dq"][0, 0], A @ K) < 1e-13, "dQ closed form"
+    assert rel(grads["dk"][0, 0], A.T @ Q) < 1e-13, "dK closed form"
+    assert rel(grads["dv"][0, 0], ((Q @ K.T) * M).T @ G) < 1e-13, "dV closed form"
+    assert rel(grads["dS0"][0, 0], Q.T @ G) < 1e-13, "dS0 closed form (the zero state's gradient)"
+
+
+def pin_backward_log_gate_identity(lib=None):
+    """For a diagonal transition, o_t depends on the gates only through q_t exp(B_t) and
+    k_s exp(-B_s) with B_t the cumulative log gate, and S_final through exp(B_N); so
+    g_s dL/dg_s = sum_{t >= s} (q_t dq_t - k_t dk_t) + (dS_final * S_final) summed over the
+    value dim (per key dim for GLA; also over the key dims for SSD). The oracle's gate
+    gradient comes from the per-token state products instead."""
+    for variant in ("gla", "ssd"):
+        case, dO, dSf, _ = _bwd_case(variant, seed=54)
+        grads = _bwd(variant, case, dO, dSf, None, lib)
+        _, S, _ = run(variant, case, lib)
+        c = case["q"] * grads["dq"] - case["k"] * grads["dk"]           # [B,H,N,dk]
+        rev = np.flip(np.cumsum(np.flip(c, axis=2), axis=2), axis=2)
+        fin = np.sum(dSf * S, axis=-1)[:, :, None, :]                    # [B,H,1,dk]
+        want = rev + fin
+        if variant == "ssd":
+            want = want.sum(axis=-1)
+        assert rel(case["g"] * grads["dg"], want) < 1e-12, f"{variant} log-gate identity"
+
+
+def pin_backward_split(lib=None):
+    """The chain rule across a split: the backward of the second part with dS_final gives
+    the gradient of its initial state, which is the first part's dS_final; together the two
+    backwards equal the backward of the whole sequence."""
+    for variant in ("kath", "gla", "gdn", "kda", "ssd"):
+        case, dO, dSf, dzf = _bwd_case(variant, seed=55)
+        whole = _bwd(variant, case, dO, dSf, dzf, lib)
+        m = 2
+        left = {kk: (vv[:, :, :m] if (vv is not None and kk in ("q", "k", "v", "g", "beta"))
+                     else vv) for kk, vv in case.items()}
+        _, Sm, zm = run(variant, left, lib)
+        right = {kk: (vv[:, :, m:] if (vv is not None and kk in ("q", "k", "v", "g", "beta"))
+                      else vv) for kk, vv in case.items()}
+        right["S0"], right["z0"] = Sm, zm
+        gr = _bwd(variant, right, dO[:, :, m:], dSf, dzf, lib)
+        gl = _bwd(variant, left, dO[:, :, :m], gr["dS0"], gr["dz0"], lib)
+        for name in ("dq", "dk", "dv", "dg", "dbeta"):
+            if whole[name] is None:
+                continue
+            cat = np.concatenate([gl[name], gr[name]], axis=2)
+            assert rel(cat, whole[name]) < 1e-12, f"{variant} {name} split"
+        assert rel(gl["dS0"], whole["dS0"]) < 1e-12, f"{variant} dS0 split"
+
+
 ALL_PINS = [pin_quadratic_form, pin_split_invariance, pin_gdn_page_forms, pin_kda_forms,
             pin_ssd_selective_ssm, pin_delta_identity,
             pin_worked_example, pin_closed_forms, pin_special_cases, pin_causality,
             pin_linearity, pin_decode_matches_prefill,
             pin_selective_scan_unrolled, pin_selective_scan_convolution, pin_selective_scan_split,
-            pin_selective_scan_special_cases, pin_selective_scan_is_ssd]
+            pin_selective_scan_special_cases, pin_selective_scan_is_ssd,
+            pin_backward_finite_differences, pin_backward_closed_form,
+            pin_backward_log_gate_identity, pin_backward_split]

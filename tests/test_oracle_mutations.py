@@ -68,6 +68,20 @@ MUTATIONS = {
                         "double delta = dt[tok * D + d];"),
     "ss_softplus_ignored": ("if (dt_softplus) delta = softplus(delta);", "(void)dt_softplus;"),
     "ss_initial_state_ignored": ("if (h0) memcpy(h, h0", "if (0) memcpy(h, h0"),
+    "bwd_decay_not_carried": ("for (j = 0; j < dv; ++j) dS[(size_t)i * dv + j] *= gi;",
+                              "for (j = 0; j < dv; ++j) dS[(size_t)i * dv + j] *= 1.0;"),
+    "bwd_output_path_missing": ("for (j = 0; j < dv; ++j) dS[(size_t)i * dv + j] += q[i] * dO[j];",
+                                "for (j = 0; j < dv; ++j) dS[(size_t)i * dv + j] += 0.0 * dO[j];"),
+    "bwd_delta_dp_sign": ("dp[j] = -beta * acc;", "dp[j] = beta * acc;"),
+    "bwd_dbeta_without_prediction": ("db += acc * (v[j] - p[j]);", "db += acc * v[j];"),
+    "bwd_dk_without_state_term": ("dk_[i] = acc + accp;", "dk_[i] = acc;"),
+    "bwd_dalpha_on_decayed_state": ("acc += dsd * S_prev[(size_t)i * dv + j];",
+                                    "acc += dsd * ai * S_prev[(size_t)i * dv + j];"),
+    "bwd_kath_denominator_sign": ("dd -= dO[j] * o[j] / den;", "dd += dO[j] * o[j] / den;"),
+    "bwd_kath_no_phi_derivative": ("dq[i] = dfq * (q[i] > 0.0 ? 1.0 : exp(q[i]));", "dq[i] = dfq;"),
+    "bwd_gate_grad_post_state": (
+        "for (j = 0; j < dv; ++j) acc += dS[(size_t)i * dv + j] * S_prev[(size_t)i * dv + j];",
+        "for (j = 0; j < dv; ++j) acc += dS[(size_t)i * dv + j] * S_post[(size_t)i * dv + j];"),
     "kda_gate_previous_token": ("if (variant == OR_KDA) { gt = g + tok * dk;",
                                 "if (variant == OR_KDA) { gt = g + (t > 0 ? tok - 1 : tok) * dk;"),
     "read_uses_key": ("for (i = 0; i < dk; ++i) acc += q[i] * S[(size_t)i * dv + j];\n            o[j] = acc;\n        }\n        c->state_read_macs += (uint64_t)dk * (uint64_t)dv;\n    } else {",
