@@ -362,6 +362,52 @@ def bench_selscan(name, steps, warmup, torch, bd, W, device, stream, graph=True)
     return rec
 
 
+def bench_backward(name, steps, warmup, torch, bd, W, device, stream):
+    """Backward of the prefill (fp32 VALU kernels): tokens per second of the whole
+    backward (states, reverse chunk walk, partial sums)."""
+    import ctypes
+    import numpy as np
+    wl = W.WORKLOADS[name]
+    log(f"backward {name}: generating inputs")
+    inp = W.make_inputs(wl)
+    d = {k: to_dev(v, torch, device) for k, v in inp.dev.items()}
+    rng = np.random.default_rng(wl.seed + 500)
+    dO = to_dev(W.round_to(rng.standard_normal((wl.B, wl.H, wl.N, wl.dv)), wl.io)[0], torch,
+                device)
+    io = bd.LA_BF16 if wl.io == "bf16" else bd.LA_F32
+    desc = bd.make_desc(wl.variant, wl.B, wl.H, wl.N, wl.dk, wl.dv, io, io, wl.eps, "valu")
+    lib = bd.load()
+    n = ctypes.c_size_t(0)
+    rc = lib.la_prefill_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if rc != 0:
+        raise bd.LinAttnError(rc, "la_prefill_backward_workspace_size")
+    ws = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=device)
+    outs = [torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"]),
+            torch.empty_like(d["g"]),
+            torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=device)]
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    args = (P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), None, None, None, P(dO), None, None,
+            P(outs[0]), P(outs[1]), P(outs[2]), P(outs[3]), None, P(outs[4]), None, P(ws),
+            int(n.value), ctypes.c_void_p(stream.cuda_stream))
+    pd = ctypes.byref(desc)
+
+    def fn(i):
+        rc = lib.la_prefill_backward(pd, *args)
+        if rc != 0:
+            raise bd.LinAttnError(rc, "la_prefill_backward")
+
+    ms = time_eager(fn, steps, warmup, torch, stream)
+    s = ms / 1e3
+    # algorithmic bytes: the forward's inputs and dO read, dq, dk, dv, dg and dS0 written
+    per = W.algorithmic_bytes_per_token_head(wl)
+    isz = 4 if wl.io == "f32" else 2
+    byts = wl.token_heads * (2 * per - wl.dv * isz) + wl.B * wl.H * wl.dk * wl.dv * 4
+    return {"workload": name + " (backward)", "ms": ms, "Mtok_per_s": wl.B * wl.N / s / 1e6,
+            "GB_per_s": byts / s / 1e9, "hbm_frac": byts / s / 1e9 / PEAK_HBM_GBS,
+            "algorithmic_bytes": byts, "workspace_bytes": int(n.value),
+            "finite": bool(torch.isfinite(outs[0].float()).all().item())}
+
+
 def cpu_baseline(case, wl, budget_s=8.0):
     """Time the fp64 oracle on a bounded sample of the workload's sequences."""
     import numpy as np
@@ -474,6 +520,10 @@ def main():
         for name in ("decode_gdn_256x32_d128", "decode_gla_256x32_d128", "decode_kda_256x32_d128",
                      "decode_ssd_256x64_dk128_dv64"):
             results[name] = bench_decode(name, 1000, 10, torch, bd, W, device, stream)
+            torch.cuda.empty_cache()
+        for name in ("gla_bf16_b2h8_n2048_d128", "ssd_bf16_b2h32_n4096_dk128_dv64"):
+            results["backward_" + name] = bench_backward(name, max(5, args.steps // 80), 2,
+                                                         torch, bd, W, device, stream)
             torch.cuda.empty_cache()
         for name in W.SELSCAN:
             results[name] = bench_selscan(name, max(10, args.steps // 40), 3, torch, bd, W, device,

@@ -20,7 +20,8 @@ LA_PATH_AUTO, LA_PATH_VALU, LA_PATH_MFMA = 0, 1, 2
 VARIANTS = {"kath": LA_KATH, "gla": LA_GLA, "gdn": LA_GDN, "kda": LA_KDA, "ssd": LA_SSD}
 PATHS = {"auto": LA_PATH_AUTO, "valu": LA_PATH_VALU, "mfma": LA_PATH_MFMA}
 EXPORTS = ("la_prefill", "la_prefill_workspace_size", "la_prefill_varlen",
-           "la_prefill_varlen_workspace_size", "la_decode_step", "la_selective_scan",
+           "la_prefill_varlen_workspace_size", "la_decode_step", "la_prefill_backward",
+           "la_prefill_backward_workspace_size", "la_selective_scan",
            "la_status_str", "la_abi_version")
 
 
@@ -73,6 +74,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.la_prefill_varlen_workspace_size.restype = ctypes.c_int
     lib.la_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.la_decode_step.restype = ctypes.c_int
+    lib.la_prefill_backward.argtypes = [dp] + [vp] * 18 + [sz, vp]
+    lib.la_prefill_backward.restype = ctypes.c_int
+    lib.la_prefill_backward_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
+    lib.la_prefill_backward_workspace_size.restype = ctypes.c_int
     lib.la_selective_scan.argtypes = [ctypes.POINTER(ScanDesc), vp, vp, vp, vp, vp, vp, vp, vp,
                                       vp, vp, vp]
     lib.la_selective_scan.restype = ctypes.c_int
@@ -244,6 +249,45 @@ def decode_step(q, k, v, S, g=None, beta=None, *, variant: str, z=None, eps: flo
                             _ptr(S), _ptr(z), _ptr(o), _stream_handle(stream, q.device))
     _check(rc, "la_decode_step")
     return o
+
+
+def prefill_backward(q, k, v, g, dO, *, variant: str, S0=None, dS_final=None, dq=None, dk=None,
+                     dv=None, dg=None, dS0=None, workspace=None, stream=None):
+    """Gradients of ``prefill`` through ``la_prefill_backward`` (GLA and SSD).
+
+    q, k, v, g, S0 as given to ``prefill``; dO [B,H,N,dv] (q's dtype); dS_final
+    [B,H,dk,dv] float32 or None. Returns (dq, dk, dv, dg, dS0).
+    """
+    import torch
+    lib = load()
+    B, H, N, dk_ = q.shape
+    dv_ = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("dO", dO), ("S0", S0),
+                    ("dS_final", dS_final), ("dq", dq), ("dk", dk), ("dv", dv), ("dg", dg),
+                    ("dS0", dS0)):
+        _require_contig(name, t)
+    desc = make_desc(variant, B, H, N, dk_, dv_, _dtype_code(q), _dtype_code(g), 1e-6, "auto")
+    dev = q.device
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dg = torch.empty_like(g) if dg is None else dg
+    if dS0 is None:
+        dS0 = torch.empty((B, H, dk_, dv_), dtype=torch.float32, device=dev)
+    n = ctypes.c_size_t(0)
+    _check(lib.la_prefill_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
+           "la_prefill_backward_workspace_size")
+    ws_bytes = int(n.value)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.la_prefill_backward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), None,
+                                 _ptr(S0), None, _ptr(dO), _ptr(dS_final), None, _ptr(dq),
+                                 _ptr(dk), _ptr(dv), _ptr(dg), None, _ptr(dS0), None,
+                                 _ptr(workspace if ws_bytes else None), wsz,
+                                 _stream_handle(stream, dev))
+    _check(rc, "la_prefill_backward")
+    return dq, dk, dv, dg, dS0
 
 
 def selective_scan(dt, A, Bm, Cm, x, Dskip=None, dt_bias=None, *, dt_softplus: bool = True,

@@ -1,0 +1,416 @@
+// Backward of the chunked prefill for the diagonal transitions (GLA: one gate per key
+// dim, "Linear / RNN 路线" section 2.2; SSD: one decay per token, sections 3.6 and 4.1),
+// in fp32 on the vector ALUs with chunk C = 16 and exact per-element decays (as the
+// VALU prefill).
+//
+// For a loss with dL/do = dO and dL/dS_final, with B_r the cumulative log gate inside a
+// chunk (per key dim), S_in the state entering it and dS_out the gradient of the state
+// leaving it (everything after the chunk), the reverse-mode derivative of the chunked
+// forward is, for rows r, s of the chunk (s <= r, mask M):
+//   A    = (dO V^T) o M                       (only this workgroup's value columns)
+//   P_rs = sum_i q_ri k_si exp(B_ri - B_si)    (s <= r)
+//   dV_s = sum_{r>=s} P_rs dO_r + K^_s dS_out,  K^_si = k_si exp(B_last,i - B_si)
+//   dQ_ri = exp(B_ri) (dO_r . S_in[i,:]) + sum_{s<=r} A_rs k_si exp(B_ri - B_si)
+//   dK_si = sum_{r>=s} A_rs q_ri exp(B_ri - B_si) + exp(B_last,i - B_si) (dS_out[i,:] . v_s)
+//   dS_in = diag(exp(B_last)) dS_out + sum_r diag(exp(B_r)) q_r dO_r^T
+// The gate gradient is taken directly, dL/dg_s,i = sum_c dS_s[i,c] S_{s-1}[i,c] (summed
+// over i as well for SSD's one decay), with every element's token states S_{s-1} rebuilt
+// forward from S_in and its gradients dS_s backward from dS_out inside the chunk. (The
+// equivalent closed form g_s dL/dg_s = sum_{t>=s} (q_t dq_t - k_t dk_t) + the final-state
+// term is a reverse cumulative sum whose terms cancel down to O(g_s); dividing by g_s
+// amplifies fp32 rounding by 1/g_s, so it is not used.)
+// dQ, dK and dg sum over all value columns, so each workgroup (one 16-column tile) writes
+// partials that a finishing kernel adds up. Kernels: states (the chunk-entering states,
+// forward), chunks (the reverse walk above), then the finishing sums.
+#include "common.hpp"
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+constexpr int C = kValuChunk;  // 16
+constexpr int VT = 16;         // value columns per workgroup
+constexpr int NT = 256;
+
+struct BwdArgs {
+    const void *q, *k, *v, *g, *dO;
+    const float *S0, *dSf;
+    void *dq, *dk, *dv, *dg;
+    float* dS0;
+    float* Sin;      // [nseq][ntiles][nchunks][DK][VT] chunk-entering states
+    float* dqp;      // [ntiles][nseq * N][DK] partial dq
+    float* dkp;      // [ntiles][nseq * N][DK] partial dk
+    float* dgp;      // [ntiles][nseq * N][DK] partial dg (per key dim)
+    int N, nseq, ntiles, nchunks;
+    int io_bf16, gate_bf16;
+};
+
+template <int VAR>
+constexpr bool scalar_gate() { return VAR == LA_SSD; }
+
+// ---------------------------------------------------------------------------- states
+template <int VAR, int DK, int DV>
+__global__ __launch_bounds__(NT) void bwd_states_kernel(BwdArgs a) {
+    constexpr int DKP = DK + 1;
+    constexpr bool SG = scalar_gate<VAR>();
+    __shared__ float sS[DK][VT];
+    __shared__ float sK[C][DKP];
+    __shared__ float sLg[SG ? 1 : C][SG ? 1 : DKP];
+    __shared__ float sc[C];
+    __shared__ float sV[C][VT];
+    const int tid = threadIdx.x;
+    const size_t seq = blockIdx.x / a.ntiles;
+    const int tile = blockIdx.x % a.ntiles, c0 = tile * VT;
+    const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
+    const size_t tok0 = seq * size_t(a.N);
+    float* Sin = a.Sin + (seq * a.ntiles + tile) * size_t(a.nchunks) * DK * VT;
+
+    for (int idx = tid; idx < DK * VT; idx += NT) {
+        const int i = idx / VT, c = idx % VT;
+        sS[i][c] = a.S0 ? a.S0[seq * DK * DV + size_t(i) * DV + c0 + c] : 0.f;
+    }
+    for (int ch = 0; ch < a.nchunks; ++ch) {
+        const int t0 = ch * C, n = min(C, a.N - t0);
+        __syncthreads();
+        for (int idx = tid; idx < DK * VT; idx += NT)
+            Sin[size_t(ch) * DK * VT + idx] = sS[idx / VT][idx % VT];
+        for (int idx = tid; idx < C * DK; idx += NT) {
+            const int r = idx / DK, i = idx % DK;
+            const size_t e = (tok0 + t0 + r) * DK + i;
+            sK[r][i] = r < n ? load_elem(a.k, e, iob) : 0.f;
+            if (!SG) sLg[r][i] = r < n ? logf(load_elem(a.g, e, gb)) : 0.f;
+        }
+        if (SG && tid < C) sc[tid] = tid < n ? logf(load_elem(a.g, tok0 + t0 + tid, gb)) : 0.f;
+        sV[tid / VT][tid % VT] = tid / VT < n ? load_elem(a.v, (tok0 + t0 + tid / VT) * DV + c0 + tid % VT, iob) : 0.f;
+        __syncthreads();
+        if (!SG) {
+            for (int i = tid; i < DK; i += NT) {
+                float acc = 0.f;
+                for (int r = 0; r < C; ++r) { acc += sLg[r][i]; sLg[r][i] = acc; }
+            }
+        } else if (tid == 0) {
+            float acc = 0.f;
+            for (int r = 0; r < C; ++r) { acc += sc[r]; sc[r] = acc; }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < DK * VT; idx += NT) {
+            const int i = idx / VT, c = idx % VT;
+            const float bl = SG ? sc[C - 1] : sLg[C - 1][i];
+            float acc = 0.f;
+            for (int s = 0; s < C; ++s)
+                acc += sK[s][i] * expf(bl - (SG ? sc[s] : sLg[s][i])) * sV[s][c];
+            sS[i][c] = expf(bl) * sS[i][c] + acc;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------- chunks
+template <int VAR, int DK, int DV>
+__global__ __launch_bounds__(NT) void bwd_chunks_kernel(BwdArgs a) {
+    constexpr int DKP = DK + 1;
+    constexpr bool SG = scalar_gate<VAR>();
+    __shared__ float sdS[DK][VT];    // gradient of the state leaving the chunk
+    __shared__ float sSin[DK][VT];
+    __shared__ float sQ[C][DKP], sK[C][DKP];
+    __shared__ float sLg[SG ? 1 : C][SG ? 1 : DKP];
+    __shared__ float sGt[SG ? 1 : C][SG ? 1 : DKP];   // the gates themselves
+    __shared__ float sc[C], sgt[C];
+    __shared__ float sV[C][VT], sdO[C][VT];
+    __shared__ float sP[C][C + 1], sA[C][C + 1];
+    const int tid = threadIdx.x;
+    const size_t seq = blockIdx.x / a.ntiles;
+    const int tile = blockIdx.x % a.ntiles, c0 = tile * VT;
+    const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
+    const size_t tok0 = seq * size_t(a.N);
+    const float* Sin = a.Sin + (seq * a.ntiles + tile) * size_t(a.nchunks) * DK * VT;
+    float* dqp = a.dqp + size_t(tile) * a.nseq * a.N * DK;
+    float* dkp = a.dkp + size_t(tile) * a.nseq * a.N * DK;
+    float* dgp = a.dgp + size_t(tile) * a.nseq * a.N * DK;
+    auto B = [&](int r, int i) { return SG ? sc[r] : sLg[r][i]; };
+    auto gate = [&](int r, int i) { return SG ? sgt[r] : sGt[r][i]; };
+
+    for (int idx = tid; idx < DK * VT; idx += NT) {
+        const int i = idx / VT, c = idx % VT;
+        sdS[i][c] = a.dSf ? a.dSf[seq * DK * DV + size_t(i) * DV + c0 + c] : 0.f;
+    }
+    for (int ch = a.nchunks - 1; ch >= 0; --ch) {
+        const int t0 = ch * C, n = min(C, a.N - t0);
+        __syncthreads();
+        for (int idx = tid; idx < C * DK; idx += NT) {
+            const int r = idx / DK, i = idx % DK;
+            const size_t e = (tok0 + t0 + r) * DK + i;
+            sQ[r][i] = r < n ? load_elem(a.q, e, iob) : 0.f;
+            sK[r][i] = r < n ? load_elem(a.k, e, iob) : 0.f;
+            if (!SG) {
+                const float gv = r < n ? load_elem(a.g, e, gb) : 1.f;
+                sGt[r][i] = gv;
+                sLg[r][i] = logf(gv);
+            }
+        }
+        if (SG && tid < C) {
+            const float gv = tid < n ? load_elem(a.g, tok0 + t0 + tid, gb) : 1.f;
+            sgt[tid] = gv;
+            sc[tid] = logf(gv);
+        }
+        {
+            const int r = tid / VT, c = tid % VT;
+            const size_t e = (tok0 + t0 + r) * DV + c0 + c;
+            sV[r][c] = r < n ? load_elem(a.v, e, iob) : 0.f;
+            sdO[r][c] = r < n ? load_elem(a.dO, e, iob) : 0.f;
+        }
+        for (int idx = tid; idx < DK * VT; idx += NT) sSin[idx / VT][idx % VT] = Sin[size_t(ch) * DK * VT + idx];
+        __syncthreads();
+        if (!SG) {
+            for (int i = tid; i < DK; i += NT) {
+                float acc = 0.f;
+                for (int r = 0; r < C; ++r) { acc += sLg[r][i]; sLg[r][i] = acc; }
+            }
+        } else if (tid == 0) {
+            float acc = 0.f;
+            for (int r = 0; r < C; ++r) { acc += sc[r]; sc[r] = acc; }
+        }
+        __syncthreads();
+        // P (all key dims) and A (this tile's value columns), lower triangles
+        {
+            const int r = tid / C, s = tid % C;
+            float p = 0.f, av = 0.f;
+            if (s <= r) {
+                if (SG) {
+                    for (int i = 0; i < DK; ++i) p += sQ[r][i] * sK[s][i];
+                    p *= expf(sc[r] - sc[s]);
+                } else {
+                    for (int i = 0; i < DK; ++i) p += sQ[r][i] * sK[s][i] * expf(sLg[r][i] - sLg[s][i]);
+                }
+                for (int c = 0; c < VT; ++c) av += sdO[r][c] * sV[s][c];
+            }
+            sP[r][s] = p;
+            sA[r][s] = av;
+        }
+        __syncthreads();
+        // dV (final for this tile's columns)
+        {
+            const int s = tid / VT, c = tid % VT;
+            float acc = 0.f;
+            for (int r = s; r < C; ++r) acc += sP[r][s] * sdO[r][c];
+            for (int i = 0; i < DK; ++i)
+                acc += sK[s][i] * expf(B(C - 1, i) - B(s, i)) * sdS[i][c];
+            if (s < n) store_elem(a.dv, (tok0 + t0 + s) * DV + c0 + c, acc, iob);
+        }
+        // partial dQ and dK over this tile's columns
+        for (int idx = tid; idx < C * DK; idx += NT) {
+            const int r = idx / DK, i = idx % DK;
+            if (r >= n) continue;
+            float sd = 0.f, kv = 0.f;
+            for (int c = 0; c < VT; ++c) {
+                sd += sdO[r][c] * sSin[i][c];
+                kv += sdS[i][c] * sV[r][c];
+            }
+            float dq = expf(B(r, i)) * sd;
+            for (int s = 0; s <= r; ++s) dq += sA[r][s] * sK[s][i] * expf(B(r, i) - B(s, i));
+            float dk = expf(B(C - 1, i) - B(r, i)) * kv;
+            for (int t = r; t < C; ++t) dk += sA[t][r] * sQ[t][i] * expf(B(t, i) - B(r, i));
+            dqp[(tok0 + t0 + r) * DK + i] = dq;
+            dkp[(tok0 + t0 + r) * DK + i] = dk;
+        }
+        // partial dg: thread (row group rg, column c) owns elements (rg + 16 m, c); for each
+        // it rebuilds S_{s-1} forward and dS_s backward over the chunk, and the products are
+        // summed over the 16 column lanes (consecutive lanes) with DPP
+        {
+            const int c = tid % VT, rg = tid / VT;
+#pragma unroll 1
+            for (int m = 0; m < DK / 16; ++m) {
+                const int i = rg + 16 * m;
+                float sp[C];   // S_{s-1}[i][c]
+                float st = sSin[i][c];
+#pragma unroll
+                for (int s_ = 0; s_ < C; ++s_) {
+                    sp[s_] = st;
+                    st = gate(s_, i) * st + sK[s_][i] * sV[s_][c];
+                }
+                float dsv = sdS[i][c];   // dS_s[i][c], from the chunk's end backward
+                float pr[C];
+#pragma unroll
+                for (int s_ = C - 1; s_ >= 0; --s_) {
+                    if (s_ < C - 1) dsv *= gate(s_ + 1, i);
+                    dsv += sQ[s_][i] * sdO[s_][c];
+                    pr[s_] = dsv * sp[s_];
+                }
+#pragma unroll
+                for (int s_ = 0; s_ < C; ++s_) {
+                    float v_ = pr[s_];
+                    v_ += dpp_f<0xB1, 0xf, 0xf>(v_);
+                    v_ += dpp_f<0x4E, 0xf, 0xf>(v_);
+                    v_ += dpp_f<0x141, 0xf, 0xf>(v_);
+                    v_ += dpp_f<0x140, 0xf, 0xf>(v_);
+                    pr[s_] = v_;
+                }
+                if (c == 0) {
+#pragma unroll
+                    for (int s_ = 0; s_ < C; ++s_)
+                        if (s_ < n) dgp[(tok0 + t0 + s_) * DK + i] = pr[s_];
+                }
+            }
+        }
+        __syncthreads();   // every read of the outgoing gradient is done
+        for (int idx = tid; idx < DK * VT; idx += NT) {
+            const int i = idx / VT, c = idx % VT;
+            float acc = expf(B(C - 1, i)) * sdS[i][c];
+            for (int r = 0; r < C; ++r) acc += expf(B(r, i)) * sQ[r][i] * sdO[r][c];
+            sdS[i][c] = acc;
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < DK * VT; idx += NT) {
+        const int i = idx / VT, c = idx % VT;
+        a.dS0[seq * DK * DV + size_t(i) * DV + c0 + c] = sdS[i][c];
+    }
+}
+
+// ---------------------------------------------------------------------------- finish
+// dq, dk, dg = sums of the tile partials (dg summed over the key dims too for SSD, one
+// wave per token).
+template <int VAR, int DK>
+__global__ __launch_bounds__(NT) void bwd_sum_kernel(BwdArgs a) {
+    constexpr bool SG = scalar_gate<VAR>();
+    const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
+    const size_t ntok = size_t(a.nseq) * a.N;
+    const size_t stride = ntok * DK;
+    if constexpr (!SG) {
+        const size_t e = size_t(blockIdx.x) * NT + threadIdx.x;
+        if (e >= stride) return;
+        float dq = 0.f, dk = 0.f, dg = 0.f;
+        for (int t = 0; t < a.ntiles; ++t) {
+            dq += a.dqp[t * stride + e];
+            dk += a.dkp[t * stride + e];
+            dg += a.dgp[t * stride + e];
+        }
+        store_elem(a.dq, e, dq, iob);
+        store_elem(a.dk, e, dk, iob);
+        store_elem(a.dg, e, dg, gb);
+    } else {
+        const size_t tok = size_t(blockIdx.x) * (NT / kWave) + threadIdx.x / kWave;
+        const int lane = threadIdx.x % kWave;
+        if (tok >= ntok) return;   // a whole wave leaves together
+        float dg = 0.f;
+        for (int i = lane; i < DK; i += kWave) {
+            const size_t e = tok * DK + i;
+            float dq = 0.f, dk = 0.f;
+            for (int t = 0; t < a.ntiles; ++t) {
+                dq += a.dqp[t * stride + e];
+                dk += a.dkp[t * stride + e];
+                dg += a.dgp[t * stride + e];
+            }
+            store_elem(a.dq, e, dq, iob);
+            store_elem(a.dk, e, dk, iob);
+        }
+        dg = wave_sum(dg);
+        if (lane == 0) store_elem(a.dg, tok, dg, gb);
+    }
+}
+
+struct BwdLayout {
+    size_t Sin, dqp, dkp, dgp, total;
+};
+BwdLayout bwd_layout(const Problem& p) {
+    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    const size_t nseq = size_t(p.B) * p.H, ntiles = size_t(p.dv / VT);
+    const size_t nchunks = size_t((p.N + C - 1) / C), ntok = nseq * size_t(p.N);
+    BwdLayout L{};
+    size_t off = 0;
+    L.Sin = off; off += al(nseq * ntiles * nchunks * p.dk * VT * 4);
+    L.dqp = off; off += al(ntiles * ntok * p.dk * 4);
+    L.dkp = off; off += al(ntiles * ntok * p.dk * 4);
+    L.dgp = off; off += al(ntiles * ntok * p.dk * 4);
+    L.total = off;
+    return L;
+}
+
+template <int VAR, int DK, int DV>
+hipError_t launch_dims(const Problem& p, BwdArgs a) {
+    const unsigned units = unsigned(a.nseq * a.ntiles);
+    bwd_states_kernel<VAR, DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    bwd_chunks_kernel<VAR, DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t ntok = size_t(a.nseq) * a.N;
+    const size_t sblocks = scalar_gate<VAR>() ? (ntok + NT / kWave - 1) / (NT / kWave)
+                                              : (ntok * DK + NT - 1) / NT;
+    bwd_sum_kernel<VAR, DK><<<dim3(unsigned(sblocks)), dim3(NT), 0, p.stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int VAR, int DK>
+hipError_t dispatch_dv(const Problem& p, const BwdArgs& a) {
+    switch (p.dv) {
+        case 16: return launch_dims<VAR, DK, 16>(p, a);
+        case 32: return launch_dims<VAR, DK, 32>(p, a);
+        case 64: return launch_dims<VAR, DK, 64>(p, a);
+        case 128: return launch_dims<VAR, DK, 128>(p, a);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int VAR>
+hipError_t dispatch_dk(const Problem& p, const BwdArgs& a) {
+    switch (p.dk) {
+        case 16: return dispatch_dv<VAR, 16>(p, a);
+        case 32: return dispatch_dv<VAR, 32>(p, a);
+        case 64: return dispatch_dv<VAR, 64>(p, a);
+        case 128: return dispatch_dv<VAR, 128>(p, a);
+    }
+    return hipErrorInvalidValue;
+}
+
+// N = 0: the gradient of the initial state is the final-state gradient itself
+__global__ void bwd_copy_kernel(const float* dSf, float* dS0, size_t n) {
+    const size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) dS0[i] = dSf ? dSf[i] : 0.f;
+}
+
+}  // namespace
+
+bool backward_supported(int variant) { return variant == LA_GLA || variant == LA_SSD; }
+
+size_t backward_workspace_bytes(const Problem& p) {
+    if (p.N == 0 || p.B == 0 || p.H == 0) return 0;
+    return bwd_layout(p).total;
+}
+
+hipError_t launch_backward(const BwdProblem& bp) {
+    const Problem& p = bp.p;
+    if (p.N == 0) {
+        const size_t n = size_t(p.B) * p.H * p.dk * p.dv;
+        const size_t blocks = (n + 255) / 256;
+        if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
+        bwd_copy_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, p.stream>>>(bp.dS_final, bp.dS0, n);
+        return hipGetLastError();
+    }
+    const size_t nseq = size_t(p.B) * p.H;
+    if (nseq * size_t(p.dv / VT) > 0x7fffffffull || nseq > 0x7fffffffull ||
+        nseq * size_t(p.N) * p.dk / NT > 0x7fffffffull)
+        return hipErrorInvalidValue;
+    const BwdLayout L = bwd_layout(p);
+    unsigned char* ws = static_cast<unsigned char*>(p.ws);
+    BwdArgs a{};
+    a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.dO = bp.dO;
+    a.S0 = p.S0; a.dSf = bp.dS_final;
+    a.dq = bp.dq; a.dk = bp.dk; a.dv = bp.dv; a.dg = bp.dg; a.dS0 = bp.dS0;
+    a.Sin = reinterpret_cast<float*>(ws + L.Sin);
+    a.dqp = reinterpret_cast<float*>(ws + L.dqp);
+    a.dkp = reinterpret_cast<float*>(ws + L.dkp);
+    a.dgp = reinterpret_cast<float*>(ws + L.dgp);
+    a.N = p.N;
+    a.nseq = int(nseq);
+    a.ntiles = p.dv / VT;
+    a.nchunks = (p.N + C - 1) / C;
+    a.io_bf16 = p.io_bf16;
+    a.gate_bf16 = p.gate_bf16;
+    switch (p.variant) {
+        case LA_GLA: return dispatch_dk<LA_GLA>(p, a);
+        case LA_SSD: return dispatch_dk<LA_SSD>(p, a);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace la

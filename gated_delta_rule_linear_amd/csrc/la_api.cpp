@@ -356,6 +356,84 @@ int la_decode_step(const la_desc* d, const void* q, const void* k, const void* v
     return err == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
+// Backward: the forward's descriptor (path AUTO or VALU; the backward runs in fp32 on the
+// vector ALUs) and a variant with a backward kernel.
+static int check_backward_desc(const la_desc* d, la::Problem& p) {
+    int rc = check_desc(d, false);
+    if (rc != LA_OK) return rc;
+    if (!la::backward_supported(d->variant)) return LA_ERR_UNSUPPORTED;
+    if (d->path == LA_PATH_MFMA || (d->chunk != 0 && d->chunk != la::kValuChunk))
+        return LA_ERR_UNSUPPORTED;
+    p.B = d->B; p.H = d->H; p.N = d->N; p.dk = d->dk; p.dv = d->dv; p.L = d->N;
+    p.variant = d->variant;
+    p.io_bf16 = d->io_dtype == LA_BF16;
+    p.gate_bf16 = d->gate_dtype == LA_BF16;
+    p.path = LA_PATH_VALU;
+    p.chunk = la::kValuChunk;
+    return LA_OK;
+}
+
+int la_prefill_backward_workspace_size(const la_desc* d, size_t* bytes) {
+    if (!bytes) return LA_ERR_INVALID;
+    la::Problem p;
+    const int rc = check_backward_desc(d, p);
+    if (rc != LA_OK) return rc;
+    *bytes = la::backward_workspace_bytes(p);
+    return LA_OK;
+}
+
+int la_prefill_backward(const la_desc* d, const void* q, const void* k, const void* v,
+                        const void* g, const void* beta, const float* S0, const float* z0,
+                        const void* dO, const float* dS_final, const float* dz_final, void* dq,
+                        void* dk, void* dv, void* dg, void* dbeta, float* dS0, float* dz0,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    la::Problem p;
+    int rc = check_backward_desc(d, p);
+    if (rc != LA_OK) return rc;
+    // GLA and SSD take no beta and no normaliser
+    if (beta || z0 || dz_final || dbeta || dz0) return LA_ERR_INVALID;
+    const bool seqs = (uint64_t(d->B) * uint64_t(d->H)) > 0;
+    const bool tokens = seqs && d->N > 0;
+    if (seqs && !dS0) return LA_ERR_INVALID;
+    if (tokens && (!q || !k || !v || !g || !dO || !dq || !dk || !dv || !dg)) return LA_ERR_INVALID;
+    // alignment: dq, dk as q; dv, dO as v; dg as g; the fp32 states 16 bytes
+    if (!check_alignment(*d, q, k, v, g, nullptr, S0, nullptr, dv, dS0, nullptr) ||
+        !check_alignment(*d, dq, dk, dO, dg, nullptr, dS_final, nullptr, nullptr, nullptr, nullptr))
+        return LA_ERR_INVALID;
+    const Sizes s = sizes_of(*d);
+    const uint64_t tk = tokens ? 1 : 0;
+    const Range rq = range(q, s.q * tk), rk = range(k, s.k * tk), rv = range(v, s.v * tk),
+                rg = range(g, s.g * tk), rS0 = range(S0, s.S), rdO = range(dO, s.o * tk),
+                rdSf = range(dS_final, s.S), rdq = range(dq, s.q * tk), rdk = range(dk, s.k * tk),
+                rdv = range(dv, s.v * tk), rdg = range(dg, s.g * tk),
+                rdS0 = range(dS0, s.S);
+    // outputs overlap nothing: not the inputs, not each other
+    const Range outs[] = {rdq, rdk, rdv, rdg, rdS0};
+    const Range all[] = {rq, rk, rv, rg, rS0, rdO, rdSf, rdq, rdk, rdv, rdg, rdS0};
+    for (int a = 0; a < 5; ++a)
+        for (const Range& x : all)
+            if (&x != &all[7 + a] && overlap(outs[a], x)) return LA_ERR_INVALID;
+    const size_t need = la::backward_workspace_bytes(p);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return LA_ERR_WORKSPACE;
+        const Range rw = range(workspace, need);
+        for (const Range& x : all)
+            if (overlap(rw, x)) return LA_ERR_INVALID;
+    }
+    if (!seqs) return LA_OK;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.S0 = S0;
+    p.ws = workspace; p.ws_bytes = workspace_bytes;
+    p.stream = static_cast<hipStream_t>(stream);
+    la::BwdProblem bp;
+    bp.p = p;
+    bp.dO = dO; bp.dS_final = dS_final;
+    bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dS0 = dS0;
+    (void)hipGetLastError();
+    hipError_t err = la::launch_backward(bp);
+    if (err == hipSuccess) err = hipGetLastError();
+    return err == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
 int la_selective_scan(const la_scan_desc* d, const void* dt, const float* A, const void* Bm,
                       const void* Cm, const void* x, const float* Dskip, const float* dt_bias,
                       const float* h0, void* y, float* h_final, void* stream) {

@@ -63,6 +63,18 @@ bool gdn_mfma_supported(int dk, int dv, bool io_bf16);
 size_t gdn_mfma_workspace_bytes(const Problem& p);
 hipError_t launch_prefill_gdn_mfma(const Problem& p);
 
+// backward_valu.hip (backward of the prefill, diagonal transitions), a validated call
+struct BwdProblem {
+    Problem p;                       // the forward call (inputs, shapes, workspace, stream)
+    const void* dO = nullptr;        // dL/do [B,H,N,dv] io
+    const float* dS_final = nullptr; // dL/dS_final [B,H,dk,dv] or null (zero)
+    void *dq = nullptr, *dk = nullptr, *dv = nullptr, *dg = nullptr;
+    float* dS0 = nullptr;
+};
+bool backward_supported(int variant);
+size_t backward_workspace_bytes(const Problem& p);
+hipError_t launch_backward(const BwdProblem& p);
+
 // selective_scan.hip (Mamba-1 selective scan), a validated call
 struct ScanProblem {
     int Bt = 0, T = 0, D = 0, n = 0;

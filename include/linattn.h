@@ -176,6 +176,32 @@ int la_decode_step(const la_desc* d, const void* q, const void* k, const void* v
                    const void* g, const void* beta, float* S, float* z, void* o,
                    void* stream);
 
+/* Backward of la_prefill: the gradients of every input for a loss with dL/do = dO and
+ * dL/dS_final = dS_final (NULL: zero), by reverse-mode differentiation of the recurrence
+ * (the training side of the same prefill; "线性注意力与 SSM" notes that training keeps
+ * length-N activations and may recompute states, which this does: the chunk-entering
+ * states are recomputed into the workspace). Variants: LA_GLA and LA_SSD (the diagonal
+ * transitions); others return LA_ERR_UNSUPPORTED. It runs in fp32 on the vector ALUs
+ * (d->path LA_PATH_AUTO or LA_PATH_VALU, chunk 0 or 16) for any supported d_k, d_v and
+ * either io dtype.
+ *   q, k, v, g, S0     the forward's inputs (S0 may be NULL)
+ *   dO                 [B, H, N, d_v] io
+ *   dq, dk             [B, H, N, d_k] io, written;  dv [B, H, N, d_v] io, written
+ *   dg                 shaped like g (gate dtype), written: dL/dg for the gate as given
+ *   dS0                [B, H, d_k, d_v] fp32, written (also when S0 is NULL: the gradient
+ *                      with respect to the zero initial state)
+ *   beta, z0, dz_final, dbeta, dz0   must be NULL (reserved for the variants with a
+ *                      delta rule or a normaliser)
+ *   workspace          at least la_prefill_backward_workspace_size bytes, 256-byte aligned
+ * Outputs overlap nothing (no input, no other output, not the workspace). Alignment as for
+ * la_prefill (dq, dk as q; dv and dO as v; dg as g). Errors as for la_prefill. */
+int la_prefill_backward_workspace_size(const la_desc* d, size_t* bytes);
+int la_prefill_backward(const la_desc* d, const void* q, const void* k, const void* v,
+                        const void* g, const void* beta, const float* S0, const float* z0,
+                        const void* dO, const float* dS_final, const float* dz_final, void* dq,
+                        void* dk, void* dv, void* dg, void* dbeta, float* dS0, float* dz0,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------------------
  * Selective scan (Mamba-1 / S6): "Linear / RNN 路线", section 3.5 (the boxed
  * discretisation Abar_t = exp(Delta_t A), Bbar_t = Delta_t B_t with Delta, B and C

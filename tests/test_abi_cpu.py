@@ -352,3 +352,76 @@ def test_selective_scan_accepts_and_noops(lib):
     assert call_scan(lib, bd.ScanDesc(0, 5, 8, 32, bd.LA_F32, 0), **p2) == bd.LA_OK
     p3 = dict(p, h_final=p["h0"])
     assert call_scan(lib, bd.ScanDesc(0, 5, 8, 32, bd.LA_F32, 0), **p3) == bd.LA_OK
+
+
+# ------------------------------------------------------------------------------ backward
+
+
+def bwd_args():
+    return dict(q=addr(0), k=addr(1), v=addr(2), g=addr(3), beta=None, S0=addr(5), z0=None,
+                dO=addr(6), dSf=addr(7), dzf=None, dq=addr(10), dk=addr(11), dv=addr(12),
+                dg=addr(13), dbeta=None, dS0=addr(14), dz0=None)
+
+
+def call_bwd(lib, desc, ws=None, ws_bytes=0, **p):
+    return lib.la_prefill_backward(ctypes.byref(desc) if desc is not None else None, p["q"],
+                                   p["k"], p["v"], p["g"], p["beta"], p["S0"], p["z0"], p["dO"],
+                                   p["dSf"], p["dzf"], p["dq"], p["dk"], p["dv"], p["dg"],
+                                   p["dbeta"], p["dS0"], p["dz0"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_desc", bd.LA_ERR_INVALID),
+    ("gdn_unsupported", bd.LA_ERR_UNSUPPORTED),
+    ("kath_unsupported", bd.LA_ERR_UNSUPPORTED),
+    ("mfma_path", bd.LA_ERR_UNSUPPORTED),
+    ("beta_given", bd.LA_ERR_INVALID),
+    ("null_dO", bd.LA_ERR_INVALID),
+    ("null_dS0", bd.LA_ERR_INVALID),
+    ("null_dg", bd.LA_ERR_INVALID),
+    ("misaligned_dq", bd.LA_ERR_INVALID),
+    ("dq_overlaps_dk", bd.LA_ERR_INVALID),
+    ("dv_overlaps_dO", bd.LA_ERR_INVALID),
+    ("dS0_overlaps_S0", bd.LA_ERR_INVALID),
+    ("no_workspace", bd.LA_ERR_WORKSPACE),
+])
+def test_backward_rejects(lib, case, expect):
+    variant = {"gdn_unsupported": "gdn", "kath_unsupported": "kath"}.get(case, "gla")
+    d = good(variant)
+    p = bwd_args()
+    ws, wsb = addr(20), 1 << 32
+    if case == "null_desc":
+        d = None
+    elif case == "mfma_path":
+        d = good("gla", path="mfma")
+    elif case == "beta_given":
+        p["beta"] = addr(4)
+    elif case == "null_dO":
+        p["dO"] = None
+    elif case == "null_dS0":
+        p["dS0"] = None
+    elif case == "null_dg":
+        p["dg"] = None
+    elif case == "misaligned_dq":
+        p["dq"] = addr(10, 4)
+    elif case == "dq_overlaps_dk":
+        p["dk"] = addr(10, 512)
+    elif case == "dv_overlaps_dO":
+        p["dv"] = addr(6, 256)
+    elif case == "dS0_overlaps_S0":
+        p["dS0"] = addr(5)
+    elif case == "no_workspace":
+        ws, wsb = None, 0
+    assert call_bwd(lib, d, ws, wsb, **p) == expect, case
+
+
+def test_backward_workspace_query(lib):
+    n = ctypes.c_size_t(0)
+    d = good("ssd", dk=128, dv=64, N=100)
+    assert lib.la_prefill_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == bd.LA_OK
+    assert n.value > 0
+    d = good("gdn")
+    assert lib.la_prefill_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == \
+        bd.LA_ERR_UNSUPPORTED
+    d = good("gla", B=0)
+    assert call_bwd(lib, d, **bwd_args()) == bd.LA_OK   # no sequences: nothing to do

@@ -1,0 +1,117 @@
+"""Parity of the prefill backward (GLA, SSD) against the fp64 oracle's reverse-mode
+gradients (GPU)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_linear_amd import binding as bd
+from gated_delta_rule_linear_amd import workloads as W
+from gpu_util import TOL, banner, dev, relerr
+
+pytestmark = pytest.mark.gpu
+
+
+def make_case(variant, B, H, N, dk, dv, io, seed, gate_kind="default", with_state=True,
+              with_dsf=True):
+    kw = dict(seed=seed, qk_scale=dk ** -0.5, gate_kind=gate_kind)
+    if variant == "gla":
+        kw["v_scale"] = dk ** -0.5
+    wl = W.Workload("b", variant, B, H, N, dk, dv, io, io, **kw)
+    inp = W.make_inputs(wl, with_state=with_state)
+    rng = np.random.default_rng(seed + 77)
+    dO, dO_x = W.round_to(rng.standard_normal((B, H, N, dv)), io)
+    dSf = dSf_x = None
+    if with_dsf:
+        dSf, dSf_x = W.round_to(rng.standard_normal((B, H, dk, dv)) * 0.1, "f32")
+    return inp, dO, dO_x, dSf, dSf_x
+
+
+def run_both(variant, inp, dO, dO_x, dSf, dSf_x, seqs=None, threads=0):
+    d = {k: dev(v) for k, v in inp.dev.items()}
+    dq, dk, dv, dg, dS0 = bd.prefill_backward(d["q"], d["k"], d["v"], d["g"], dev(dO),
+                                              variant=variant, S0=d.get("S0"),
+                                              dS_final=dev(dSf))
+    torch.cuda.synchronize()
+    e = inp.exact
+    sel = (lambda a: a) if seqs is None else \
+        (lambda a: None if a is None else a.reshape((-1,) + a.shape[2:])[seqs][None])
+    ref = oracle.prefill_backward(variant, sel(e["q"]), sel(e["k"]), sel(e["v"]), sel(e["g"]),
+                                  None, sel(e.get("S0")), None, sel(dO_x), sel(dSf_x),
+                                  threads=threads)
+    got = {"dq": dq, "dk": dk, "dv": dv, "dg": dg, "dS0": dS0}
+    if seqs is not None:
+        got = {k: v.reshape((-1,) + tuple(v.shape[2:]))[seqs][None] for k, v in got.items()}
+    return got, ref
+
+
+def check(got, ref, tol):
+    errs = {k: relerr(got[k], ref[k]) for k in got}
+    for k, v in errs.items():
+        assert v <= tol, f"{k}: {v:.3e} > {tol} ({errs})"
+    return errs
+
+
+@pytest.mark.parametrize("variant", ["gla", "ssd"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (128, 128), (128, 64)])
+def test_backward_shapes(variant, io, dk, dv):
+    case = make_case(variant, 2, 2, 37, dk, dv, io, seed=dk + 3 * dv)
+    banner(f"backward {variant} {io} dk={dk} dv={dv} N=37")
+    check(*run_both(variant, *case), TOL[io])
+
+
+@pytest.mark.parametrize("variant", ["gla", "ssd"])
+@pytest.mark.parametrize("N", [1, 15, 16, 17, 70])
+def test_backward_lengths(variant, N):
+    case = make_case(variant, 1, 3, N, 32, 16, "f32", seed=N, gate_kind="slow")
+    banner(f"backward {variant} N={N}")
+    check(*run_both(variant, *case), TOL["f32"])
+
+
+@pytest.mark.parametrize("variant,kind", [("gla", "fast"), ("gla", "ones"), ("ssd", "fast"),
+                                          ("ssd", "ones")])
+def test_backward_gate_kinds(variant, kind):
+    case = make_case(variant, 1, 2, 50, 64, 32, "f32", seed=9, gate_kind=kind)
+    banner(f"backward {variant} gates={kind}")
+    check(*run_both(variant, *case), TOL["f32"])
+
+
+def test_backward_without_state_or_final_gradient():
+    case = make_case("gla", 1, 2, 40, 64, 32, "bf16", seed=12, with_state=False, with_dsf=False)
+    banner("backward gla no S0, no dS_final")
+    check(*run_both("gla", *case), TOL["bf16"])
+
+
+def test_backward_empty_sequence():
+    """N = 0: the initial state's gradient is the final state's."""
+    inp, dO, dO_x, dSf, dSf_x = make_case("ssd", 2, 3, 0, 32, 16, "f32", seed=3)
+    banner("backward N=0")
+    got, ref = run_both("ssd", inp, dO, dO_x, dSf, dSf_x)
+    assert torch.equal(got["dS0"].cpu(), torch.from_numpy(dSf))
+
+
+@pytest.mark.parametrize("name", ["gla_bf16_b2h8_n2048_d128", "ssd_bf16_b2h32_n4096_dk128_dv64"])
+def test_backward_full_workload_sampled(name):
+    """The full-size workload; the oracle checks sampled sequences one by one."""
+    wl = W.WORKLOADS[name]
+    inp = W.make_inputs(wl)
+    rng = np.random.default_rng(wl.seed + 500)
+    dO, dO_x = W.round_to(rng.standard_normal((wl.B, wl.H, wl.N, wl.dv)), wl.io)
+    banner(f"backward full workload {name}")
+    nseq = wl.B * wl.H
+    for s in (0, nseq - 1):
+        got, ref = run_both(wl.variant, inp, dO, dO_x, None, None, seqs=[s], threads=1)
+        errs = check(got, ref, TOL["bf16"])
+        print(name, s, errs, flush=True)
+
+
+def test_backward_tiny_gates():
+    """Gates down to 1e-7 (5% of them): the gate gradient is taken directly from the states,
+    so tiny gates cost no accuracy (fp32 bound)."""
+    inp, dO, dO_x, dSf, dSf_x = make_case("gla", 1, 2, 60, 64, 32, "f32", seed=21)
+    rng = np.random.default_rng(22)
+    g = np.where(rng.random(inp.exact["g"].shape) < 0.05, 1e-7, inp.exact["g"])
+    inp.dev["g"], inp.exact["g"] = W.round_to(g, "f32")
+    banner("backward gla tiny gates")
+    check(*run_both("gla", inp, dO, dO_x, dSf, dSf_x), TOL["f32"])
