@@ -1,12 +1,13 @@
 // Backward of the chunked prefill for the diagonal transitions (GLA: one gate per key
 // dim, "Linear / RNN 路线" section 2.2; SSD: one decay per token, sections 3.6 and 4.1),
-// in fp32 on the vector ALUs with chunk C = 16 and exact per-element decays (as the
-// VALU prefill).
+// in fp32 on the vector ALUs with chunk C = 16 and per-element decays (cumulative gates
+// in base-2 logarithms, decay factors by the hardware base-2 exponential).
 //
 // For a loss with dL/do = dO and dL/dS_final, with B_r the cumulative log gate inside a
 // chunk (per key dim), S_in the state entering it and dS_out the gradient of the state
 // leaving it (everything after the chunk), the reverse-mode derivative of the chunked
-// forward is, for rows r, s of the chunk (s <= r, mask M):
+// forward is, for rows r, s of the chunk (s <= r, mask M; written with exp, computed
+// as exp2 of base-2 logarithms):
 //   A    = (dO V^T) o M                       (only this workgroup's value columns)
 //   P_rs = sum_i q_ri k_si exp(B_ri - B_si)    (s <= r)
 //   dV_s = sum_{r>=s} P_rs dO_r + K^_s dS_out,  K^_si = k_si exp(B_last,i - B_si)
@@ -78,9 +79,9 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(BwdArgs a) {
             const int r = idx / DK, i = idx % DK;
             const size_t e = (tok0 + t0 + r) * DK + i;
             sK[r][i] = r < n ? load_elem(a.k, e, iob) : 0.f;
-            if (!SG) sLg[r][i] = r < n ? logf(load_elem(a.g, e, gb)) : 0.f;
+            if (!SG) sLg[r][i] = r < n ? __builtin_amdgcn_logf(load_elem(a.g, e, gb)) : 0.f;
         }
-        if (SG && tid < C) sc[tid] = tid < n ? logf(load_elem(a.g, tok0 + t0 + tid, gb)) : 0.f;
+        if (SG && tid < C) sc[tid] = tid < n ? __builtin_amdgcn_logf(load_elem(a.g, tok0 + t0 + tid, gb)) : 0.f;
         sV[tid / VT][tid % VT] = tid / VT < n ? load_elem(a.v, (tok0 + t0 + tid / VT) * DV + c0 + tid % VT, iob) : 0.f;
         __syncthreads();
         if (!SG) {
@@ -98,8 +99,8 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(BwdArgs a) {
             const float bl = SG ? sc[C - 1] : sLg[C - 1][i];
             float acc = 0.f;
             for (int s = 0; s < C; ++s)
-                acc += sK[s][i] * expf(bl - (SG ? sc[s] : sLg[s][i])) * sV[s][c];
-            sS[i][c] = expf(bl) * sS[i][c] + acc;
+                acc += sK[s][i] * __builtin_amdgcn_exp2f(bl - (SG ? sc[s] : sLg[s][i])) * sV[s][c];
+            sS[i][c] = __builtin_amdgcn_exp2f(bl) * sS[i][c] + acc;
         }
     }
 }
@@ -109,8 +110,9 @@ template <int VAR, int DK, int DV>
 __global__ __launch_bounds__(NT) void bwd_chunks_kernel(BwdArgs a) {
     constexpr int DKP = DK + 1;
     constexpr bool SG = scalar_gate<VAR>();
-    __shared__ float sdS[DK][VT];    // gradient of the state leaving the chunk
-    __shared__ float sSin[DK][VT];
+    // rows padded to VT + 1 floats: the dQ / dK step reads a column down consecutive rows
+    __shared__ float sdS[DK][VT + 1];    // gradient of the state leaving the chunk
+    __shared__ float sSin[DK][VT + 1];
     __shared__ float sQ[C][DKP], sK[C][DKP];
     __shared__ float sLg[SG ? 1 : C][SG ? 1 : DKP];
     __shared__ float sGt[SG ? 1 : C][SG ? 1 : DKP];   // the gates themselves
@@ -144,13 +146,13 @@ __global__ __launch_bounds__(NT) void bwd_chunks_kernel(BwdArgs a) {
             if (!SG) {
                 const float gv = r < n ? load_elem(a.g, e, gb) : 1.f;
                 sGt[r][i] = gv;
-                sLg[r][i] = logf(gv);
+                sLg[r][i] = __builtin_amdgcn_logf(gv);
             }
         }
         if (SG && tid < C) {
             const float gv = tid < n ? load_elem(a.g, tok0 + t0 + tid, gb) : 1.f;
             sgt[tid] = gv;
-            sc[tid] = logf(gv);
+            sc[tid] = __builtin_amdgcn_logf(gv);
         }
         {
             const int r = tid / VT, c = tid % VT;
@@ -177,9 +179,9 @@ __global__ __launch_bounds__(NT) void bwd_chunks_kernel(BwdArgs a) {
             if (s <= r) {
                 if (SG) {
                     for (int i = 0; i < DK; ++i) p += sQ[r][i] * sK[s][i];
-                    p *= expf(sc[r] - sc[s]);
+                    p *= __builtin_amdgcn_exp2f(sc[r] - sc[s]);
                 } else {
-                    for (int i = 0; i < DK; ++i) p += sQ[r][i] * sK[s][i] * expf(sLg[r][i] - sLg[s][i]);
+                    for (int i = 0; i < DK; ++i) p += sQ[r][i] * sK[s][i] * __builtin_amdgcn_exp2f(sLg[r][i] - sLg[s][i]);
                 }
                 for (int c = 0; c < VT; ++c) av += sdO[r][c] * sV[s][c];
             }
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(NT) void bwd_chunks_kernel(BwdArgs a) {
             float acc = 0.f;
             for (int r = s; r < C; ++r) acc += sP[r][s] * sdO[r][c];
             for (int i = 0; i < DK; ++i)
-                acc += sK[s][i] * expf(B(C - 1, i) - B(s, i)) * sdS[i][c];
+                acc += sK[s][i] * __builtin_amdgcn_exp2f(B(C - 1, i) - B(s, i)) * sdS[i][c];
             if (s < n) store_elem(a.dv, (tok0 + t0 + s) * DV + c0 + c, acc, iob);
         }
         // partial dQ and dK over this tile's columns
@@ -205,10 +207,10 @@ __global__ __launch_bounds__(NT) void bwd_chunks_kernel(BwdArgs a) {
                 sd += sdO[r][c] * sSin[i][c];
                 kv += sdS[i][c] * sV[r][c];
             }
-            float dq = expf(B(r, i)) * sd;
-            for (int s = 0; s <= r; ++s) dq += sA[r][s] * sK[s][i] * expf(B(r, i) - B(s, i));
-            float dk = expf(B(C - 1, i) - B(r, i)) * kv;
-            for (int t = r; t < C; ++t) dk += sA[t][r] * sQ[t][i] * expf(B(t, i) - B(r, i));
+            float dq = __builtin_amdgcn_exp2f(B(r, i)) * sd;
+            for (int s = 0; s <= r; ++s) dq += sA[r][s] * sK[s][i] * __builtin_amdgcn_exp2f(B(r, i) - B(s, i));
+            float dk = __builtin_amdgcn_exp2f(B(C - 1, i) - B(r, i)) * kv;
+            for (int t = r; t < C; ++t) dk += sA[t][r] * sQ[t][i] * __builtin_amdgcn_exp2f(B(t, i) - B(r, i));
             dqp[(tok0 + t0 + r) * DK + i] = dq;
             dkp[(tok0 + t0 + r) * DK + i] = dk;
         }
@@ -254,8 +256,8 @@ __global__ __launch_bounds__(NT) void bwd_chunks_kernel(BwdArgs a) {
         __syncthreads();   // every read of the outgoing gradient is done
         for (int idx = tid; idx < DK * VT; idx += NT) {
             const int i = idx / VT, c = idx % VT;
-            float acc = expf(B(C - 1, i)) * sdS[i][c];
-            for (int r = 0; r < C; ++r) acc += expf(B(r, i)) * sQ[r][i] * sdO[r][c];
+            float acc = __builtin_amdgcn_exp2f(B(C - 1, i)) * sdS[i][c];
+            for (int r = 0; r < C; ++r) acc += __builtin_amdgcn_exp2f(B(r, i)) * sQ[r][i] * sdO[r][c];
             sdS[i][c] = acc;
         }
     }
