@@ -20,9 +20,16 @@
 // equivalent closed form g_s dL/dg_s = sum_{t>=s} (q_t dq_t - k_t dk_t) + the final-state
 // term is a reverse cumulative sum whose terms cancel down to O(g_s); dividing by g_s
 // amplifies fp32 rounding by 1/g_s, so it is not used.)
-// dQ, dK and dg sum over all value columns, so each workgroup (one 16-column tile) writes
-// partials that a finishing kernel adds up. Kernels: states (the chunk-entering states,
-// forward), chunks (the reverse walk above), then the finishing sums.
+//
+// Only the chunk-to-chunk carries are sequential, and they are elementwise: with the
+// chunk's state contribution dS_c = sum_s diag(exp(B_last - B_s)) k_s v_s^T, its output-
+// gradient contribution G_c = sum_r diag(exp(B_r)) q_r dO_r^T and its decay a_c =
+// exp(B_last),
+//   S_in[c+1] = a_c o S_in[c] + dS_c,    dS_out[c-1] = a_c o dS_out[c] + G_c.
+// So the work runs in four kernels: sums (every chunk in parallel: dS_c, G_c, a_c), scans
+// (one thread per state element walks the chunks forward for S_in and backward for
+// dS_out, in place), grads (every chunk and value tile in parallel: dV, and partials of
+// dQ, dK and dg over the tile's columns), then the finishing sums of the partials.
 #include "common.hpp"
 #include "la_internal.h"
 
@@ -38,7 +45,9 @@ struct BwdArgs {
     const float *S0, *dSf;
     void *dq, *dk, *dv, *dg;
     float* dS0;
-    float* Sin;      // [nseq][ntiles][nchunks][DK][VT] chunk-entering states
+    float* Sst;      // [nseq][nchunks][DK][DV]: dS_c, then S_in (in place)
+    float* dSt;      // [nseq][nchunks][DK][DV]: G_c, then dS_out (in place)
+    float* ac;       // [nseq][nchunks][DK] (GLA) or [nseq][nchunks] (SSD): chunk decay
     float* dqp;      // [ntiles][nseq * N][DK] partial dq
     float* dkp;      // [ntiles][nseq * N][DK] partial dk
     float* dgp;      // [ntiles][nseq * N][DK] partial dg (per key dim)
@@ -49,222 +58,264 @@ struct BwdArgs {
 template <int VAR>
 constexpr bool scalar_gate() { return VAR == LA_SSD; }
 
-// ---------------------------------------------------------------------------- states
-template <int VAR, int DK, int DV>
-__global__ __launch_bounds__(NT) void bwd_states_kernel(BwdArgs a) {
-    constexpr int DKP = DK + 1;
-    constexpr bool SG = scalar_gate<VAR>();
-    __shared__ float sS[DK][VT];
-    __shared__ float sK[C][DKP];
-    __shared__ float sLg[SG ? 1 : C][SG ? 1 : DKP];
-    __shared__ float sc[C];
-    __shared__ float sV[C][VT];
-    const int tid = threadIdx.x;
-    const size_t seq = blockIdx.x / a.ntiles;
-    const int tile = blockIdx.x % a.ntiles, c0 = tile * VT;
-    const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
-    const size_t tok0 = seq * size_t(a.N);
-    float* Sin = a.Sin + (seq * a.ntiles + tile) * size_t(a.nchunks) * DK * VT;
+// One chunk's operands in LDS: q, k, the gates and their cumulative base-2 logarithms,
+// and the value tile of v and dO. Rows past the end are zero with gate 1.
+template <int DK, bool SG>
+struct ChunkSmem {
+    static constexpr int DKP = DK + 1;
+    float q[C][DKP], k[C][DKP];
+    float lg[SG ? 1 : C][SG ? 1 : DKP];   // cumulative log2 gate (per key dim)
+    float gt[SG ? 1 : C][SG ? 1 : DKP];   // the gates themselves
+    float sc[C], sgt[C];                  // the same for one gate per token
+    // decay factors, all <= 1: eq = exp(B_r), ek = exp(B_last - B_s) per (row, key dim), or
+    // per row with one gate per token, and the pair factors exp(B_r - B_s) (s <= r) of the
+    // one-gate case
+    float eq[SG ? 1 : C][SG ? 1 : DKP], ek[SG ? 1 : C][SG ? 1 : DKP];
+    float seq[C], sek[C], pd[SG ? C : 1][SG ? C + 1 : 1];
+    float v[C][VT], dO[C][VT];
+};
 
-    for (int idx = tid; idx < DK * VT; idx += NT) {
-        const int i = idx / VT, c = idx % VT;
-        sS[i][c] = a.S0 ? a.S0[seq * DK * DV + size_t(i) * DV + c0 + c] : 0.f;
+template <int DK, int DV, bool SG>
+__device__ __forceinline__ void load_chunk(ChunkSmem<DK, SG>& sm, const BwdArgs& a, size_t tok0,
+                                           int t0, int n, int c0) {
+    const int tid = threadIdx.x;
+    const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
+    for (int idx = tid; idx < C * DK; idx += NT) {
+        const int r = idx / DK, i = idx % DK;
+        const size_t e = (tok0 + t0 + r) * DK + i;
+        sm.q[r][i] = r < n ? load_elem(a.q, e, iob) : 0.f;
+        sm.k[r][i] = r < n ? load_elem(a.k, e, iob) : 0.f;
+        if (!SG) {
+            const float gv = r < n ? load_elem(a.g, e, gb) : 1.f;
+            sm.gt[r][i] = gv;
+            sm.lg[r][i] = __builtin_amdgcn_logf(gv);
+        }
     }
-    for (int ch = 0; ch < a.nchunks; ++ch) {
-        const int t0 = ch * C, n = min(C, a.N - t0);
-        __syncthreads();
-        for (int idx = tid; idx < DK * VT; idx += NT)
-            Sin[size_t(ch) * DK * VT + idx] = sS[idx / VT][idx % VT];
+    if (SG && tid < C) {
+        const float gv = tid < n ? load_elem(a.g, tok0 + t0 + tid, gb) : 1.f;
+        sm.sgt[tid] = gv;
+        sm.sc[tid] = __builtin_amdgcn_logf(gv);
+    }
+    {
+        const int r = tid / VT, c = tid % VT;
+        const size_t e = (tok0 + t0 + r) * DV + c0 + c;
+        sm.v[r][c] = r < n ? load_elem(a.v, e, iob) : 0.f;
+        sm.dO[r][c] = r < n ? load_elem(a.dO, e, iob) : 0.f;
+    }
+    __syncthreads();
+    if (!SG) {
+        for (int i = tid; i < DK; i += NT) {
+            float acc = 0.f;
+            for (int r = 0; r < C; ++r) { acc += sm.lg[r][i]; sm.lg[r][i] = acc; }
+        }
+    } else if (tid == 0) {
+        float acc = 0.f;
+        for (int r = 0; r < C; ++r) { acc += sm.sc[r]; sm.sc[r] = acc; }
+    }
+    __syncthreads();
+    if (!SG) {
         for (int idx = tid; idx < C * DK; idx += NT) {
             const int r = idx / DK, i = idx % DK;
-            const size_t e = (tok0 + t0 + r) * DK + i;
-            sK[r][i] = r < n ? load_elem(a.k, e, iob) : 0.f;
-            if (!SG) sLg[r][i] = r < n ? __builtin_amdgcn_logf(load_elem(a.g, e, gb)) : 0.f;
+            sm.eq[r][i] = __builtin_amdgcn_exp2f(sm.lg[r][i]);
+            sm.ek[r][i] = __builtin_amdgcn_exp2f(sm.lg[C - 1][i] - sm.lg[r][i]);
         }
-        if (SG && tid < C) sc[tid] = tid < n ? __builtin_amdgcn_logf(load_elem(a.g, tok0 + t0 + tid, gb)) : 0.f;
-        sV[tid / VT][tid % VT] = tid / VT < n ? load_elem(a.v, (tok0 + t0 + tid / VT) * DV + c0 + tid % VT, iob) : 0.f;
-        __syncthreads();
-        if (!SG) {
-            for (int i = tid; i < DK; i += NT) {
-                float acc = 0.f;
-                for (int r = 0; r < C; ++r) { acc += sLg[r][i]; sLg[r][i] = acc; }
-            }
-        } else if (tid == 0) {
-            float acc = 0.f;
-            for (int r = 0; r < C; ++r) { acc += sc[r]; sc[r] = acc; }
+    } else {
+        const int r = tid / C, s = tid % C;   // C * C = NT
+        sm.pd[r][s] = s <= r ? __builtin_amdgcn_exp2f(sm.sc[r] - sm.sc[s]) : 0.f;
+        if (tid < C) {
+            sm.seq[tid] = __builtin_amdgcn_exp2f(sm.sc[tid]);
+            sm.sek[tid] = __builtin_amdgcn_exp2f(sm.sc[C - 1] - sm.sc[tid]);
         }
-        __syncthreads();
-        for (int idx = tid; idx < DK * VT; idx += NT) {
-            const int i = idx / VT, c = idx % VT;
-            const float bl = SG ? sc[C - 1] : sLg[C - 1][i];
-            float acc = 0.f;
-            for (int s = 0; s < C; ++s)
-                acc += sK[s][i] * __builtin_amdgcn_exp2f(bl - (SG ? sc[s] : sLg[s][i])) * sV[s][c];
-            sS[i][c] = __builtin_amdgcn_exp2f(bl) * sS[i][c] + acc;
+    }
+    __syncthreads();
+}
+
+// workgroup -> (sequence, chunk, value tile), the tiles of one chunk adjacent
+struct ChunkUnit {
+    size_t seq;
+    int ch, tile;
+};
+__device__ __forceinline__ ChunkUnit chunk_unit(const BwdArgs& a) {
+    const size_t b = blockIdx.x;
+    ChunkUnit u;
+    u.tile = int(b % a.ntiles);
+    u.ch = int((b / a.ntiles) % a.nchunks);
+    u.seq = b / (size_t(a.ntiles) * a.nchunks);
+    return u;
+}
+
+// ---------------------------------------------------------------------------- sums
+template <int VAR, int DK, int DV>
+__global__ __launch_bounds__(NT) void bwd_sums_kernel(BwdArgs a) {
+    constexpr bool SG = scalar_gate<VAR>();
+    __shared__ ChunkSmem<DK, SG> sm;
+    const ChunkUnit u = chunk_unit(a);
+    const int c0 = u.tile * VT, t0 = u.ch * C, n = min(C, a.N - t0);
+    const size_t tok0 = u.seq * size_t(a.N);
+    load_chunk<DK, DV, SG>(sm, a, tok0, t0, n, c0);
+    auto EQ = [&](int r, int i) { return SG ? sm.seq[r] : sm.eq[r][i]; };
+    auto EK = [&](int r, int i) { return SG ? sm.sek[r] : sm.ek[r][i]; };
+    const size_t sbase = (u.seq * a.nchunks + u.ch) * size_t(DK) * DV;
+    for (int idx = threadIdx.x; idx < DK * VT; idx += NT) {
+        const int i = idx / VT, c = idx % VT;
+        float ds = 0.f, gq = 0.f;
+        for (int s_ = 0; s_ < C; ++s_) {
+            ds += EK(s_, i) * sm.k[s_][i] * sm.v[s_][c];
+            gq += EQ(s_, i) * sm.q[s_][i] * sm.dO[s_][c];
+        }
+        a.Sst[sbase + size_t(i) * DV + c0 + c] = ds;
+        a.dSt[sbase + size_t(i) * DV + c0 + c] = gq;
+    }
+    if (u.tile == 0) {
+        float* ac = a.ac + (u.seq * a.nchunks + u.ch) * (SG ? 1 : DK);
+        if (SG) {
+            if (threadIdx.x == 0) ac[0] = __builtin_amdgcn_exp2f(sm.sc[C - 1]);
+        } else {
+            for (int i = threadIdx.x; i < DK; i += NT) ac[i] = __builtin_amdgcn_exp2f(sm.lg[C - 1][i]);
         }
     }
 }
 
-// ---------------------------------------------------------------------------- chunks
+// ---------------------------------------------------------------------------- scans
+// One thread per state element (sequence, i, j): S_in forward, dS_out backward, in place.
 template <int VAR, int DK, int DV>
-__global__ __launch_bounds__(NT) void bwd_chunks_kernel(BwdArgs a) {
-    constexpr int DKP = DK + 1;
+__global__ __launch_bounds__(NT) void bwd_scans_kernel(BwdArgs a) {
     constexpr bool SG = scalar_gate<VAR>();
+    const size_t e = size_t(blockIdx.x) * NT + threadIdx.x;
+    if (e >= size_t(a.nseq) * DK * DV) return;
+    const size_t seq = e / (size_t(DK) * DV), ij = e % (size_t(DK) * DV);
+    const int i = int(ij / DV);
+    const size_t stride = size_t(DK) * DV;
+    float* Ss = a.Sst + seq * a.nchunks * stride + ij;
+    float* dSs = a.dSt + seq * a.nchunks * stride + ij;
+    const float* ac = a.ac + seq * a.nchunks * (SG ? 1 : DK) + (SG ? 0 : i);
+    float S = a.S0 ? a.S0[e] : 0.f;
+    for (int ch = 0; ch < a.nchunks; ++ch) {
+        const float d = Ss[ch * stride];
+        Ss[ch * stride] = S;
+        S = ac[ch * (SG ? 1 : DK)] * S + d;
+    }
+    float dS = a.dSf ? a.dSf[e] : 0.f;
+    for (int ch = a.nchunks - 1; ch >= 0; --ch) {
+        const float gq = dSs[ch * stride];
+        dSs[ch * stride] = dS;
+        dS = ac[ch * (SG ? 1 : DK)] * dS + gq;
+    }
+    a.dS0[e] = dS;
+}
+
+// ---------------------------------------------------------------------------- grads
+template <int VAR, int DK, int DV>
+__global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
+    constexpr bool SG = scalar_gate<VAR>();
+    __shared__ ChunkSmem<DK, SG> sm;
     // rows padded to VT + 1 floats: the dQ / dK step reads a column down consecutive rows
     __shared__ float sdS[DK][VT + 1];    // gradient of the state leaving the chunk
-    __shared__ float sSin[DK][VT + 1];
-    __shared__ float sQ[C][DKP], sK[C][DKP];
-    __shared__ float sLg[SG ? 1 : C][SG ? 1 : DKP];
-    __shared__ float sGt[SG ? 1 : C][SG ? 1 : DKP];   // the gates themselves
-    __shared__ float sc[C], sgt[C];
-    __shared__ float sV[C][VT], sdO[C][VT];
+    __shared__ float sSin[DK][VT + 1];   // state entering it
     __shared__ float sP[C][C + 1], sA[C][C + 1];
     const int tid = threadIdx.x;
-    const size_t seq = blockIdx.x / a.ntiles;
-    const int tile = blockIdx.x % a.ntiles, c0 = tile * VT;
-    const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
-    const size_t tok0 = seq * size_t(a.N);
-    const float* Sin = a.Sin + (seq * a.ntiles + tile) * size_t(a.nchunks) * DK * VT;
-    float* dqp = a.dqp + size_t(tile) * a.nseq * a.N * DK;
-    float* dkp = a.dkp + size_t(tile) * a.nseq * a.N * DK;
-    float* dgp = a.dgp + size_t(tile) * a.nseq * a.N * DK;
-    auto B = [&](int r, int i) { return SG ? sc[r] : sLg[r][i]; };
-    auto gate = [&](int r, int i) { return SG ? sgt[r] : sGt[r][i]; };
-
+    const ChunkUnit u = chunk_unit(a);
+    const int c0 = u.tile * VT, t0 = u.ch * C, n = min(C, a.N - t0);
+    const bool iob = a.io_bf16 != 0;
+    const size_t tok0 = u.seq * size_t(a.N);
+    const size_t sbase = (u.seq * a.nchunks + u.ch) * size_t(DK) * DV;
     for (int idx = tid; idx < DK * VT; idx += NT) {
         const int i = idx / VT, c = idx % VT;
-        sdS[i][c] = a.dSf ? a.dSf[seq * DK * DV + size_t(i) * DV + c0 + c] : 0.f;
+        sSin[i][c] = a.Sst[sbase + size_t(i) * DV + c0 + c];
+        sdS[i][c] = a.dSt[sbase + size_t(i) * DV + c0 + c];
     }
-    for (int ch = a.nchunks - 1; ch >= 0; --ch) {
-        const int t0 = ch * C, n = min(C, a.N - t0);
-        __syncthreads();
-        for (int idx = tid; idx < C * DK; idx += NT) {
-            const int r = idx / DK, i = idx % DK;
-            const size_t e = (tok0 + t0 + r) * DK + i;
-            sQ[r][i] = r < n ? load_elem(a.q, e, iob) : 0.f;
-            sK[r][i] = r < n ? load_elem(a.k, e, iob) : 0.f;
-            if (!SG) {
-                const float gv = r < n ? load_elem(a.g, e, gb) : 1.f;
-                sGt[r][i] = gv;
-                sLg[r][i] = __builtin_amdgcn_logf(gv);
+    load_chunk<DK, DV, SG>(sm, a, tok0, t0, n, c0);   // ends with a barrier
+    float* dqp = a.dqp + size_t(u.tile) * a.nseq * a.N * DK;
+    float* dkp = a.dkp + size_t(u.tile) * a.nseq * a.N * DK;
+    float* dgp = a.dgp + size_t(u.tile) * a.nseq * a.N * DK;
+    auto EQ = [&](int r, int i) { return SG ? sm.seq[r] : sm.eq[r][i]; };
+    auto EK = [&](int r, int i) { return SG ? sm.sek[r] : sm.ek[r][i]; };
+    // exp(B_r - B_s) for s <= r
+    auto PF = [&](int r, int s, int i) {
+        return SG ? sm.pd[r][s] : __builtin_amdgcn_exp2f(sm.lg[r][i] - sm.lg[s][i]);
+    };
+    auto gate = [&](int r, int i) { return SG ? sm.sgt[r] : sm.gt[r][i]; };
+
+    // P (all key dims) and A (this tile's value columns), lower triangles
+    {
+        const int r = tid / C, s = tid % C;
+        float p = 0.f, av = 0.f;
+        if (s <= r) {
+            if (SG) {
+                for (int i = 0; i < DK; ++i) p += sm.q[r][i] * sm.k[s][i];
+                p *= sm.pd[r][s];
+            } else {
+                for (int i = 0; i < DK; ++i)
+                    p += sm.q[r][i] * sm.k[s][i] * __builtin_amdgcn_exp2f(sm.lg[r][i] - sm.lg[s][i]);
             }
+            for (int c = 0; c < VT; ++c) av += sm.dO[r][c] * sm.v[s][c];
         }
-        if (SG && tid < C) {
-            const float gv = tid < n ? load_elem(a.g, tok0 + t0 + tid, gb) : 1.f;
-            sgt[tid] = gv;
-            sc[tid] = __builtin_amdgcn_logf(gv);
-        }
-        {
-            const int r = tid / VT, c = tid % VT;
-            const size_t e = (tok0 + t0 + r) * DV + c0 + c;
-            sV[r][c] = r < n ? load_elem(a.v, e, iob) : 0.f;
-            sdO[r][c] = r < n ? load_elem(a.dO, e, iob) : 0.f;
-        }
-        for (int idx = tid; idx < DK * VT; idx += NT) sSin[idx / VT][idx % VT] = Sin[size_t(ch) * DK * VT + idx];
-        __syncthreads();
-        if (!SG) {
-            for (int i = tid; i < DK; i += NT) {
-                float acc = 0.f;
-                for (int r = 0; r < C; ++r) { acc += sLg[r][i]; sLg[r][i] = acc; }
-            }
-        } else if (tid == 0) {
-            float acc = 0.f;
-            for (int r = 0; r < C; ++r) { acc += sc[r]; sc[r] = acc; }
-        }
-        __syncthreads();
-        // P (all key dims) and A (this tile's value columns), lower triangles
-        {
-            const int r = tid / C, s = tid % C;
-            float p = 0.f, av = 0.f;
-            if (s <= r) {
-                if (SG) {
-                    for (int i = 0; i < DK; ++i) p += sQ[r][i] * sK[s][i];
-                    p *= __builtin_amdgcn_exp2f(sc[r] - sc[s]);
-                } else {
-                    for (int i = 0; i < DK; ++i) p += sQ[r][i] * sK[s][i] * __builtin_amdgcn_exp2f(sLg[r][i] - sLg[s][i]);
-                }
-                for (int c = 0; c < VT; ++c) av += sdO[r][c] * sV[s][c];
-            }
-            sP[r][s] = p;
-            sA[r][s] = av;
-        }
-        __syncthreads();
-        // dV (final for this tile's columns)
-        {
-            const int s = tid / VT, c = tid % VT;
-            float acc = 0.f;
-            for (int r = s; r < C; ++r) acc += sP[r][s] * sdO[r][c];
-            for (int i = 0; i < DK; ++i)
-                acc += sK[s][i] * __builtin_amdgcn_exp2f(B(C - 1, i) - B(s, i)) * sdS[i][c];
-            if (s < n) store_elem(a.dv, (tok0 + t0 + s) * DV + c0 + c, acc, iob);
-        }
-        // partial dQ and dK over this tile's columns
-        for (int idx = tid; idx < C * DK; idx += NT) {
-            const int r = idx / DK, i = idx % DK;
-            if (r >= n) continue;
-            float sd = 0.f, kv = 0.f;
-            for (int c = 0; c < VT; ++c) {
-                sd += sdO[r][c] * sSin[i][c];
-                kv += sdS[i][c] * sV[r][c];
-            }
-            float dq = __builtin_amdgcn_exp2f(B(r, i)) * sd;
-            for (int s = 0; s <= r; ++s) dq += sA[r][s] * sK[s][i] * __builtin_amdgcn_exp2f(B(r, i) - B(s, i));
-            float dk = __builtin_amdgcn_exp2f(B(C - 1, i) - B(r, i)) * kv;
-            for (int t = r; t < C; ++t) dk += sA[t][r] * sQ[t][i] * __builtin_amdgcn_exp2f(B(t, i) - B(r, i));
-            dqp[(tok0 + t0 + r) * DK + i] = dq;
-            dkp[(tok0 + t0 + r) * DK + i] = dk;
-        }
-        // partial dg: thread (row group rg, column c) owns elements (rg + 16 m, c); for each
-        // it rebuilds S_{s-1} forward and dS_s backward over the chunk, and the products are
-        // summed over the 16 column lanes (consecutive lanes) with DPP
-        {
-            const int c = tid % VT, rg = tid / VT;
-#pragma unroll 1
-            for (int m = 0; m < DK / 16; ++m) {
-                const int i = rg + 16 * m;
-                float sp[C];   // S_{s-1}[i][c]
-                float st = sSin[i][c];
-#pragma unroll
-                for (int s_ = 0; s_ < C; ++s_) {
-                    sp[s_] = st;
-                    st = gate(s_, i) * st + sK[s_][i] * sV[s_][c];
-                }
-                float dsv = sdS[i][c];   // dS_s[i][c], from the chunk's end backward
-                float pr[C];
-#pragma unroll
-                for (int s_ = C - 1; s_ >= 0; --s_) {
-                    if (s_ < C - 1) dsv *= gate(s_ + 1, i);
-                    dsv += sQ[s_][i] * sdO[s_][c];
-                    pr[s_] = dsv * sp[s_];
-                }
-#pragma unroll
-                for (int s_ = 0; s_ < C; ++s_) {
-                    float v_ = pr[s_];
-                    v_ += dpp_f<0xB1, 0xf, 0xf>(v_);
-                    v_ += dpp_f<0x4E, 0xf, 0xf>(v_);
-                    v_ += dpp_f<0x141, 0xf, 0xf>(v_);
-                    v_ += dpp_f<0x140, 0xf, 0xf>(v_);
-                    pr[s_] = v_;
-                }
-                if (c == 0) {
-#pragma unroll
-                    for (int s_ = 0; s_ < C; ++s_)
-                        if (s_ < n) dgp[(tok0 + t0 + s_) * DK + i] = pr[s_];
-                }
-            }
-        }
-        __syncthreads();   // every read of the outgoing gradient is done
-        for (int idx = tid; idx < DK * VT; idx += NT) {
-            const int i = idx / VT, c = idx % VT;
-            float acc = __builtin_amdgcn_exp2f(B(C - 1, i)) * sdS[i][c];
-            for (int r = 0; r < C; ++r) acc += __builtin_amdgcn_exp2f(B(r, i)) * sQ[r][i] * sdO[r][c];
-            sdS[i][c] = acc;
-        }
+        sP[r][s] = p;
+        sA[r][s] = av;
     }
     __syncthreads();
-    for (int idx = tid; idx < DK * VT; idx += NT) {
-        const int i = idx / VT, c = idx % VT;
-        a.dS0[seq * DK * DV + size_t(i) * DV + c0 + c] = sdS[i][c];
+    // dV (final for this tile's columns)
+    {
+        const int s = tid / VT, c = tid % VT;
+        float acc = 0.f;
+        for (int r = s; r < C; ++r) acc += sP[r][s] * sm.dO[r][c];
+        for (int i = 0; i < DK; ++i) acc += sm.k[s][i] * EK(s, i) * sdS[i][c];
+        if (s < n) store_elem(a.dv, (tok0 + t0 + s) * DV + c0 + c, acc, iob);
+    }
+    // partial dQ and dK over this tile's columns
+    for (int idx = tid; idx < C * DK; idx += NT) {
+        const int r = idx / DK, i = idx % DK;
+        if (r >= n) continue;
+        float sd = 0.f, kv = 0.f;
+        for (int c = 0; c < VT; ++c) {
+            sd += sm.dO[r][c] * sSin[i][c];
+            kv += sdS[i][c] * sm.v[r][c];
+        }
+        float dq = EQ(r, i) * sd;
+        for (int s = 0; s <= r; ++s) dq += sA[r][s] * sm.k[s][i] * PF(r, s, i);
+        float dk = EK(r, i) * kv;
+        for (int t = r; t < C; ++t) dk += sA[t][r] * sm.q[t][i] * PF(t, r, i);
+        dqp[(tok0 + t0 + r) * DK + i] = dq;
+        dkp[(tok0 + t0 + r) * DK + i] = dk;
+    }
+    // partial dg: thread (row group rg, column c) owns elements (rg + 16 m, c); for each
+    // it rebuilds S_{s-1} forward and dS_s backward over the chunk, and the products are
+    // summed over the 16 column lanes (consecutive lanes) with DPP
+    {
+        const int c = tid % VT, rg = tid / VT;
+#pragma unroll 1
+        for (int m = 0; m < DK / 16; ++m) {
+            const int i = rg + 16 * m;
+            float sp[C];   // S_{s-1}[i][c]
+            float st = sSin[i][c];
+#pragma unroll
+            for (int s_ = 0; s_ < C; ++s_) {
+                sp[s_] = st;
+                st = gate(s_, i) * st + sm.k[s_][i] * sm.v[s_][c];
+            }
+            float dsv = sdS[i][c];   // dS_s[i][c], from the chunk's end backward
+            float pr[C];
+#pragma unroll
+            for (int s_ = C - 1; s_ >= 0; --s_) {
+                if (s_ < C - 1) dsv *= gate(s_ + 1, i);
+                dsv += sm.q[s_][i] * sm.dO[s_][c];
+                pr[s_] = dsv * sp[s_];
+            }
+#pragma unroll
+            for (int s_ = 0; s_ < C; ++s_) {
+                float v_ = pr[s_];
+                v_ += dpp_f<0xB1, 0xf, 0xf>(v_);
+                v_ += dpp_f<0x4E, 0xf, 0xf>(v_);
+                v_ += dpp_f<0x141, 0xf, 0xf>(v_);
+                v_ += dpp_f<0x140, 0xf, 0xf>(v_);
+                pr[s_] = v_;
+            }
+            if (c == 0) {
+#pragma unroll
+                for (int s_ = 0; s_ < C; ++s_)
+                    if (s_ < n) dgp[(tok0 + t0 + s_) * DK + i] = pr[s_];
+            }
+        }
     }
 }
 
@@ -311,7 +362,7 @@ __global__ __launch_bounds__(NT) void bwd_sum_kernel(BwdArgs a) {
 }
 
 struct BwdLayout {
-    size_t Sin, dqp, dkp, dgp, total;
+    size_t Sst, dSt, ac, dqp, dkp, dgp, total;
 };
 BwdLayout bwd_layout(const Problem& p) {
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
@@ -319,7 +370,9 @@ BwdLayout bwd_layout(const Problem& p) {
     const size_t nchunks = size_t((p.N + C - 1) / C), ntok = nseq * size_t(p.N);
     BwdLayout L{};
     size_t off = 0;
-    L.Sin = off; off += al(nseq * ntiles * nchunks * p.dk * VT * 4);
+    L.Sst = off; off += al(nseq * nchunks * p.dk * p.dv * 4);
+    L.dSt = off; off += al(nseq * nchunks * p.dk * p.dv * 4);
+    L.ac = off; off += al(nseq * nchunks * (p.variant == LA_SSD ? 1 : p.dk) * 4);
     L.dqp = off; off += al(ntiles * ntok * p.dk * 4);
     L.dkp = off; off += al(ntiles * ntok * p.dk * 4);
     L.dgp = off; off += al(ntiles * ntok * p.dk * 4);
@@ -329,11 +382,14 @@ BwdLayout bwd_layout(const Problem& p) {
 
 template <int VAR, int DK, int DV>
 hipError_t launch_dims(const Problem& p, BwdArgs a) {
-    const unsigned units = unsigned(a.nseq * a.ntiles);
-    bwd_states_kernel<VAR, DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
+    const unsigned units = unsigned(size_t(a.nseq) * a.nchunks * a.ntiles);
+    bwd_sums_kernel<VAR, DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    bwd_chunks_kernel<VAR, DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
+    const size_t nel = size_t(a.nseq) * DK * DV;
+    bwd_scans_kernel<VAR, DK, DV><<<dim3(unsigned((nel + NT - 1) / NT)), dim3(NT), 0, p.stream>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    bwd_grads_kernel<VAR, DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t ntok = size_t(a.nseq) * a.N;
     const size_t sblocks = scalar_gate<VAR>() ? (ntok + NT / kWave - 1) / (NT / kWave)
@@ -389,7 +445,9 @@ hipError_t launch_backward(const BwdProblem& bp) {
         return hipGetLastError();
     }
     const size_t nseq = size_t(p.B) * p.H;
-    if (nseq * size_t(p.dv / VT) > 0x7fffffffull || nseq > 0x7fffffffull ||
+    const size_t nchunks = size_t((p.N + C - 1) / C);
+    if (nseq * nchunks * size_t(p.dv / VT) > 0x7fffffffull ||
+        nseq * size_t(p.dk) * p.dv / NT > 0x7fffffffull ||
         nseq * size_t(p.N) * p.dk / NT > 0x7fffffffull)
         return hipErrorInvalidValue;
     const BwdLayout L = bwd_layout(p);
@@ -398,7 +456,9 @@ hipError_t launch_backward(const BwdProblem& bp) {
     a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.dO = bp.dO;
     a.S0 = p.S0; a.dSf = bp.dS_final;
     a.dq = bp.dq; a.dk = bp.dk; a.dv = bp.dv; a.dg = bp.dg; a.dS0 = bp.dS0;
-    a.Sin = reinterpret_cast<float*>(ws + L.Sin);
+    a.Sst = reinterpret_cast<float*>(ws + L.Sst);
+    a.dSt = reinterpret_cast<float*>(ws + L.dSt);
+    a.ac = reinterpret_cast<float*>(ws + L.ac);
     a.dqp = reinterpret_cast<float*>(ws + L.dqp);
     a.dkp = reinterpret_cast<float*>(ws + L.dkp);
     a.dgp = reinterpret_cast<float*>(ws + L.dgp);
