@@ -35,10 +35,11 @@ struct DecodeArgs {
 
 // Threads per workgroup: a 64 KiB state tile streamed by 512 threads with nontemporal
 // 16-byte accesses measured 6.2 TB/s for an in-place read-modify-write on MI355X, against
-// 5.8 TB/s with 256 threads. GLA (the lighter kernel) measured faster still with 1024
-// threads; GDN, with twice the registers per thread, slower.
-template <int VAR>
-constexpr int decode_nthreads() { return VAR == LA_GLA || VAR == LA_SSD ? 1024 : 512; }
+// 5.8 TB/s with 256 threads. GLA and SSD (the lighter kernels) measured faster still
+// with 1024 threads on a 128 x 128 state; GDN, with twice the registers per thread,
+// slower. A narrower state keeps 512 threads, so each thread still has 4 rows in flight.
+template <int VAR, int DV>
+constexpr int decode_nthreads() { return (VAR == LA_GLA || VAR == LA_SSD) && DV >= 128 ? 1024 : 512; }
 template <int VAR>
 constexpr bool has_delta() { return VAR == LA_GDN || VAR == LA_KDA; }
 template <int VAR>
@@ -59,9 +60,9 @@ constexpr int decode_threads(int dk, int dv, int nth) {
 }
 
 template <int VAR, int DK, int DV>
-__global__ __launch_bounds__(decode_threads(DK, DV, decode_nthreads<VAR>())) void decode_kernel(
+__global__ __launch_bounds__(decode_threads(DK, DV, decode_nthreads<VAR, DV>())) void decode_kernel(
     DecodeArgs a) {
-    using Sh = DecodeShape<DK, DV, decode_nthreads<VAR>()>;
+    using Sh = DecodeShape<DK, DV, decode_nthreads<VAR, DV>()>;
     constexpr int NCG = Sh::NCG, RG = Sh::RG, RPT = Sh::RPT, NT = Sh::NT;
     const int tid = threadIdx.x;
     const int cg = tid % NCG, rg = tid / NCG;
@@ -205,7 +206,7 @@ template <int VAR, int DK, int DV>
 hipError_t launch_one(const Problem& p, const DecodeArgs& a) {
     const unsigned nseq = unsigned(size_t(p.B) * size_t(p.H));
     decode_kernel<VAR, DK, DV>
-        <<<dim3(nseq), dim3(DecodeShape<DK, DV, decode_nthreads<VAR>()>::NT), 0, p.stream>>>(a);
+        <<<dim3(nseq), dim3(DecodeShape<DK, DV, decode_nthreads<VAR, DV>()>::NT), 0, p.stream>>>(a);
     return hipGetLastError();
 }
 
