@@ -47,7 +47,7 @@ STEP_KERNELS = {
     "kath": "kath_chain_kernel (summary) + kath_scan_kernel + kath_chain_kernel",
     "gdn": "gdn_prep_kernel + gdn_fwd_kernel",
     "kda": "kda_prep_kernel + kda_fwd_kernel",
-    "ssd": "gla_prep_kernel (one decay per token) + gla_chain_kernel (summary, forward)",
+    "ssd": "ssd_prep_kernel + gla_chain_kernel (summary, forward; q read as given)",
 }
 
 

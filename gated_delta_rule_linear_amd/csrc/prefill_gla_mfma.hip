@@ -33,8 +33,10 @@
 //
 // Mamba-2's SSD ("Linear / RNN 路线", sections 3.6 and 4.1: one decay a_t per token and
 // head, S_t = a_t S_{t-1} + k_t v_t^T) is this recurrence with the gate equal over the
-// key dims; the prep kernel then reads one gate per row and broadcasts it, and
-// everything after it is shared.
+// key dims. With one decay per row every factor is bounded by itself (exp(c_r - c_s) <= 1
+// for s <= r), so SSD has a prep of its own: P = (Q K^T) o D from the raw q and k, k^
+// and the row factors exp(c_r), and no q^; its forward reads q's fragments straight from
+// q and scales the state part of each output row by exp(c_r).
 #include "la_internal.h"
 #include "mfma.hpp"
 
@@ -102,7 +104,7 @@ struct __align__(16) PrepSmem {
     __align__(16) float T[8][DK];           // gate product of each 8-row group
 };
 
-template <bool GB, bool SG>   // SG: one gate per token (SSD) instead of one per key dim
+template <bool GB>
 __global__ __launch_bounds__(NTP) void gla_prep_kernel(GlaArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
@@ -126,18 +128,15 @@ __global__ __launch_bounds__(NTP) void gla_prep_kernel(GlaArgs a) {
     const rsrc_t rq = make_rsrc(a.q + (tok0 + t0) * DK, rows_left * DK * 2u);
     const rsrc_t rk = make_rsrc(a.k + (tok0 + t0) * DK, rows_left * DK * 2u);
     constexpr uint32_t GS = GB ? 2u : 4u;
-    constexpr uint32_t GW = SG ? 1u : uint32_t(DK);   // gate elements per token
-    const rsrc_t rg_ = make_rsrc(static_cast<const char*>(a.g) + (tok0 + t0) * GW * GS,
-                                 rows_left * GW * GS);
-    uint32_t qv[8], kv[8], gv[GB || SG ? 8 : 16];
+    const rsrc_t rg_ = make_rsrc(static_cast<const char*>(a.g) + (tok0 + t0) * DK * GS,
+                                 rows_left * DK * GS);
+    uint32_t qv[8], kv[8], gv[GB ? 8 : 16];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         const uint32_t e = uint32_t((8 * rg + r) * DK + col);
         qv[r] = buf_ld4(rq, e * 2u);
         kv[r] = buf_ld4(rk, e * 2u);
-        if constexpr (SG) {
-            gv[r] = buf_ld_gate<GB>(rg_, uint32_t(8 * rg + r));
-        } else if constexpr (GB) {
+        if constexpr (GB) {
             gv[r] = buf_ld4(rg_, e * 2u);
         } else {
             const uint2 x = buf_ld8(rg_, e * 4u);
@@ -151,9 +150,7 @@ __global__ __launch_bounds__(NTP) void gla_prep_kernel(GlaArgs a) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             float g0, g1;
-            if constexpr (SG) {
-                g0 = g1 = gate_val<GB>(gv[r]);
-            } else if constexpr (GB) {
+            if constexpr (GB) {
                 g0 = __uint_as_float(gv[r] << 16);
                 g1 = __uint_as_float(gv[r] & 0xffff0000u);
             } else {
@@ -292,6 +289,116 @@ __global__ __launch_bounds__(NTP) void gla_prep_kernel(GlaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// SSD prep: one decay per row
+// ---------------------------------------------------------------------------
+// One workgroup of 8 waves per (sequence, chunk). Wave 0 turns the 64 decays (clamped at
+// exp(-10) like GLA's gates) into the cumulative base-2 log c_r by a wave scan; wave w
+// loads rows 8 w .. 8 w + 7 of q and k (two columns per lane) into LDS as they are, and
+// writes its rows of k^ = k exp(c_last - c_r) transposed in fragment order. The ten lower
+// score tiles P_rs = (q_r . k_s) exp(c_r - c_s) (s <= r) come from the raw q, k on the
+// matrix cores, scaled in the accumulators. The workspace gets exp(c_r) per row (in q^'s
+// place), k^T, P and the chunk decay exp(c_last).
+struct __align__(16) SsdPrepSmem {
+    __align__(16) uint16_t qo[C * PQ];   // q as given
+    __align__(16) uint16_t ko[C * PQ];   // k as given
+    float c[C];                          // cumulative log2 decay
+};
+
+template <bool GB>
+__global__ __launch_bounds__(NTP) void ssd_prep_kernel(GlaArgs a) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    SsdPrepSmem& sm = *reinterpret_cast<SsdPrepSmem*>(smem_raw);
+    const int lane = threadIdx.x & 63, w = wave_id();
+    const int g = lane >> 4, jl = lane & 15;
+    const XcdMap mp = xcd_map(blockIdx.x, a.nchunks, a.nseq);
+    if (!mp.valid) return;
+    const size_t seq = size_t(mp.seq);
+    const int ch = mp.tile;
+    const int t0 = ch * C;
+    const SeqSpan sp = seq_span(int(seq), a.H, a.N, a.L, a.cu);
+    const size_t tok0 = sp.base;
+    if (t0 >= sp.len) return;   // past this sequence's end: nothing reads this chunk
+    const uint32_t rows_left = uint32_t(sp.len - t0);
+    const rsrc_t rq = make_rsrc(a.q + (tok0 + t0) * DK, rows_left * DK * 2u);
+    const rsrc_t rk = make_rsrc(a.k + (tok0 + t0) * DK, rows_left * DK * 2u);
+    constexpr uint32_t GS = GB ? 2u : 4u;
+    const rsrc_t rg_ = make_rsrc(static_cast<const char*>(a.g) + (tok0 + t0) * GS, rows_left * GS);
+    const int col = 2 * lane;
+    uint32_t qv[8], kv[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const uint32_t e = uint32_t((8 * w + r) * DK + col);
+        qv[r] = buf_ld4(rq, e * 2u);
+        kv[r] = buf_ld4(rk, e * 2u);
+    }
+    if (w == 0) {
+        const float gv = uint32_t(lane) < rows_left
+                             ? fmaxf(gate_val<GB>(buf_ld_gate<GB>(rg_, uint32_t(lane))), kGateMin)
+                             : 1.f;   // padding rows: identity steps
+        sm.c[lane] = wave_inclusive_scan(__builtin_amdgcn_logf(gv));
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int rr = 8 * w + r;
+        *reinterpret_cast<uint32_t*>(sm.qo + rr * PQ + col) = qv[r];
+        *reinterpret_cast<uint32_t*>(sm.ko + rr * PQ + col) = kv[r];
+    }
+    lds_barrier();
+    unsigned char* wsc = a.ws + (seq * a.nchunks + ch) * size_t(kWsChunk);
+    const float clast = sm.c[C - 1];
+    if (w == 0) {
+        const float al = __builtin_amdgcn_exp2f(clast);
+        *reinterpret_cast<float2*>(wsc + kWsA + lane * 8) = make_float2(al, al);
+        *reinterpret_cast<float*>(wsc + kWsQ + lane * 4) = __builtin_amdgcn_exp2f(sm.c[lane]);
+    }
+    // k^ transposed: this thread's 8 tokens of key i are one fragment piece
+    {
+        float kh[8][2];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const float f = __builtin_amdgcn_exp2f(clast - sm.c[8 * w + r]);
+            kh[r][0] = __uint_as_float(kv[r] << 16) * f;
+            kh[r][1] = __uint_as_float(kv[r] & 0xffff0000u) * f;
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int i = col + c;
+            float f[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) f[r] = kh[r][c];
+            *reinterpret_cast<uint4*>(wsc + kWsK + (((i >> 4) * 2 + (w >> 2)) * 64 + 16 * (w & 3) + (i & 15)) * 16) =
+                pack8(f);
+        }
+    }
+    // P: the ten lower tiles D'[s][r] = sum_i k_si q_ri over key block sb and row block rb,
+    // scaled by exp(c_r - c_s) and masked, stored straight from the accumulators as half
+    // pieces (the upper halves (0, 1) and (2, 3) the forward reads are zeros)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const int ti = w + 8 * tt;
+        if (ti >= 10) continue;
+        const int rb = ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3;
+        const int sb = ti - (rb * (rb + 1)) / 2;
+        f32x4_t acc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk)
+            acc = mfma16(frag_kc(sm.ko, PQ, 16 * sb, 32 * kk, lane), frag_kc(sm.qo, PQ, 16 * rb, 32 * kk, lane),
+                         acc);
+        const int r = 16 * rb + jl;
+        const float cr = sm.c[r];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int s_ = 16 * sb + 4 * g + j;
+            acc[j] = s_ <= r ? acc[j] * __builtin_amdgcn_exp2f(cr - sm.c[s_]) : 0.f;
+        }
+        unsigned char* piece = wsc + kWsP + ((rb * 2 + (sb >> 1)) * 64 + lane) * 16;
+        *reinterpret_cast<uint2*>(piece + (sb & 1) * 8) =
+            make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+        if (sb == rb && (rb & 1) == 0) *reinterpret_cast<uint2*>(piece + 8) = make_uint2(0, 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // summary (OUT = false) and forward (OUT = true): the chunk walk of one segment
 // ---------------------------------------------------------------------------
 template <int VT>
@@ -304,14 +411,16 @@ struct __align__(16) ChainSmem {
 
 // One chunk's operands in registers: the wave's k^T fragments (state update, key rows
 // 32 w ..), q^ and P fragments (forward), this thread's V pieces and decay piece for the
-// LDS copies.
+// LDS copies, and (SSD) the row factor exp(c_r) of this lane's output row.
 template <int KV>
 struct ChainRegs {
     uint4 kt[4], qf[4], pf[2], vst[KV], ast;
+    uint32_t eq;
 };
 
-// SG only names the instantiation (one decay per token: the SSD workload), so that
-// profiles tell the two workloads apart; the chunk walk itself is the same.
+// SG: one decay per token (SSD). The forward then takes q's fragments from q itself and
+// scales the state part of each output row by the row factor exp(c_r) from the prep;
+// the state update is the same.
 template <bool OUT, int NVT, bool SG>
 __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
     constexpr int VT = 16 * NVT;
@@ -363,6 +472,7 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
     const rsrc_t rw_ = make_rsrc(a.ws + (size_t(seq) * a.nchunks + ch0) * kWsChunk,
                                  uint32_t(nloc) * kWsChunk);
     const rsrc_t rv = make_rsrc(a.v + tok0 * DV, uint32_t(sp.len) * uint32_t(DV) * 2u);
+    const rsrc_t rq = make_rsrc(a.q + tok0 * DK, uint32_t(sp.len) * uint32_t(DK) * 2u);
     const uint32_t obytes = uint32_t(sp.len) * uint32_t(DV) * 2u;
     const rsrc_t ro = make_rsrc(a.o + tok0 * DV, obytes);
     if (!OUT && seg == 0 && a.S0) {
@@ -404,9 +514,18 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
             R.vst[x] = buf_ld16(rv, off);
         }
         if (OUT) {
+            if constexpr (SG) {
+                // q's fragments from q itself: row 16 w + jl, columns 32 kk + 8 g .. + 7
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                R.qf[kk] = buf_ld16(rw_, cb + kWsQ + uint32_t((w * 4 + kk) * 64 + lane) * 16u);
+                for (int kk = 0; kk < 4; ++kk)
+                    R.qf[kk] = buf_ld16(rq, ((t0 + uint32_t(16 * w + jl)) * uint32_t(DK) +
+                                             uint32_t(32 * kk + 8 * g)) * 2u);
+                R.eq = buf_ld4(rw_, cb + kWsQ + uint32_t(16 * w + jl) * 4u);
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    R.qf[kk] = buf_ld16(rw_, cb + kWsQ + uint32_t((w * 4 + kk) * 64 + lane) * 16u);
+            }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
                 R.pf[kk] = buf_ld16(rw_, cb + kWsP + uint32_t((w * 2 + kk) * 64 + lane) * 16u);
@@ -441,6 +560,7 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
                 for (int kk = 0; kk < DK / 32; ++kk)
                     o_ = mfma16(frag_st<NVT>(sm.st[cur], PQ, 0, ct, 32 * kk, lane),
                                 __builtin_bit_cast(bf16x8_t, R.qf[kk]), o_);
+                if constexpr (SG) o_ *= __uint_as_float(R.eq);   // the state part of row rw
                 o_ = mfma16(frag_kr_cols_pk<NVT>(vv, PV, 0, 0, ct, lane),
                             __builtin_bit_cast(bf16x8_t, R.pf[0]), o_);
                 if (nk > 1)
@@ -651,13 +771,18 @@ hipError_t launch_nvt(const Problem& p) {
     a.ntiles = p.dv / VT;
     hipError_t e;
     {
-        const size_t smem = sizeof(PrepSmem);
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_prep_kernel<GB, SG>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
-        if (e != hipSuccess) return e;
         const size_t blocks = size_t(xcd_grid(a.nchunks, (a.nseq + 7) & ~7));
         if (size_t(a.nseq + 7) * size_t(a.nchunks) > 0x7fffffffull) return hipErrorInvalidValue;
-        gla_prep_kernel<GB, SG><<<dim3(unsigned(blocks)), dim3(NTP), smem, p.stream>>>(a);
+        if constexpr (SG) {
+            const size_t smem = sizeof(SsdPrepSmem);
+            ssd_prep_kernel<GB><<<dim3(unsigned(blocks)), dim3(NTP), smem, p.stream>>>(a);
+        } else {
+            const size_t smem = sizeof(PrepSmem);
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_prep_kernel<GB>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+            if (e != hipSuccess) return e;
+            gla_prep_kernel<GB><<<dim3(unsigned(blocks)), dim3(NTP), smem, p.stream>>>(a);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const size_t smem = sizeof(ChainSmem<VT>);
