@@ -363,8 +363,8 @@ def bench_selscan(name, steps, warmup, torch, bd, W, device, stream, graph=True)
 
 
 def bench_backward(name, steps, warmup, torch, bd, W, device, stream):
-    """Backward of the prefill (fp32 VALU kernels): tokens per second of the whole
-    backward (states, reverse chunk walk, partial sums)."""
+    """Backward of the prefill (the default path: matrix cores for SSD, fp32 VALU for GLA):
+    tokens per second of the whole backward (every kernel of la_prefill_backward)."""
     import ctypes
     import numpy as np
     wl = W.WORKLOADS[name]
@@ -375,7 +375,7 @@ def bench_backward(name, steps, warmup, torch, bd, W, device, stream):
     dO = to_dev(W.round_to(rng.standard_normal((wl.B, wl.H, wl.N, wl.dv)), wl.io)[0], torch,
                 device)
     io = bd.LA_BF16 if wl.io == "bf16" else bd.LA_F32
-    desc = bd.make_desc(wl.variant, wl.B, wl.H, wl.N, wl.dk, wl.dv, io, io, wl.eps, "valu")
+    desc = bd.make_desc(wl.variant, wl.B, wl.H, wl.N, wl.dk, wl.dv, io, io, wl.eps, "auto")
     lib = bd.load()
     n = ctypes.c_size_t(0)
     rc = lib.la_prefill_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n))

@@ -252,7 +252,7 @@ def decode_step(q, k, v, S, g=None, beta=None, *, variant: str, z=None, eps: flo
 
 
 def prefill_backward(q, k, v, g, dO, *, variant: str, S0=None, dS_final=None, dq=None, dk=None,
-                     dv=None, dg=None, dS0=None, workspace=None, stream=None):
+                     dv=None, dg=None, dS0=None, path: str = "auto", workspace=None, stream=None):
     """Gradients of ``prefill`` through ``la_prefill_backward`` (GLA and SSD).
 
     q, k, v, g, S0 as given to ``prefill``; dO [B,H,N,dv] (q's dtype); dS_final
@@ -266,7 +266,7 @@ def prefill_backward(q, k, v, g, dO, *, variant: str, S0=None, dS_final=None, dq
                     ("dS_final", dS_final), ("dq", dq), ("dk", dk), ("dv", dv), ("dg", dg),
                     ("dS0", dS0)):
         _require_contig(name, t)
-    desc = make_desc(variant, B, H, N, dk_, dv_, _dtype_code(q), _dtype_code(g), 1e-6, "auto")
+    desc = make_desc(variant, B, H, N, dk_, dv_, _dtype_code(q), _dtype_code(g), 1e-6, path)
     dev = q.device
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk

@@ -356,21 +356,28 @@ int la_decode_step(const la_desc* d, const void* q, const void* k, const void* v
     return err == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
-// Backward: the forward's descriptor (path AUTO or VALU; the backward runs in fp32 on the
-// vector ALUs) and a variant with a backward kernel.
+// Backward: the forward's descriptor and a variant with a backward kernel. Path AUTO takes
+// the matrix-core backward where the shape allows it (SSD, bf16, d_k = 128, d_v = 64),
+// else the fp32 VALU backward.
 static int check_backward_desc(const la_desc* d, la::Problem& p) {
     int rc = check_desc(d, false);
     if (rc != LA_OK) return rc;
     if (!la::backward_supported(d->variant)) return LA_ERR_UNSUPPORTED;
-    if (d->path == LA_PATH_MFMA || (d->chunk != 0 && d->chunk != la::kValuChunk))
-        return LA_ERR_UNSUPPORTED;
     p.B = d->B; p.H = d->H; p.N = d->N; p.dk = d->dk; p.dv = d->dv; p.L = d->N;
     p.variant = d->variant;
     p.io_bf16 = d->io_dtype == LA_BF16;
     p.gate_bf16 = d->gate_dtype == LA_BF16;
-    p.path = LA_PATH_VALU;
-    p.chunk = la::kValuChunk;
+    const bool mfma_ok = la::ssd_backward_mfma_supported(p);
+    if (d->path == LA_PATH_MFMA && !mfma_ok) return LA_ERR_UNSUPPORTED;
+    p.path = (d->path != LA_PATH_VALU && mfma_ok) ? LA_PATH_MFMA : LA_PATH_VALU;
+    p.chunk = p.path == LA_PATH_MFMA ? la::kMfmaChunk : la::kValuChunk;
+    if (d->chunk != 0 && d->chunk != p.chunk) return LA_ERR_UNSUPPORTED;
     return LA_OK;
+}
+
+static size_t backward_workspace(const la::Problem& p) {
+    return p.path == LA_PATH_MFMA ? la::ssd_backward_mfma_workspace_bytes(p)
+                                  : la::backward_workspace_bytes(p);
 }
 
 int la_prefill_backward_workspace_size(const la_desc* d, size_t* bytes) {
@@ -378,7 +385,7 @@ int la_prefill_backward_workspace_size(const la_desc* d, size_t* bytes) {
     la::Problem p;
     const int rc = check_backward_desc(d, p);
     if (rc != LA_OK) return rc;
-    *bytes = la::backward_workspace_bytes(p);
+    *bytes = backward_workspace(p);
     return LA_OK;
 }
 
@@ -413,7 +420,7 @@ int la_prefill_backward(const la_desc* d, const void* q, const void* k, const vo
     for (int a = 0; a < 5; ++a)
         for (const Range& x : all)
             if (&x != &all[7 + a] && overlap(outs[a], x)) return LA_ERR_INVALID;
-    const size_t need = la::backward_workspace_bytes(p);
+    const size_t need = backward_workspace(p);
     if (need > 0) {
         if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return LA_ERR_WORKSPACE;
         const Range rw = range(workspace, need);
@@ -429,7 +436,8 @@ int la_prefill_backward(const la_desc* d, const void* q, const void* k, const vo
     bp.dO = dO; bp.dS_final = dS_final;
     bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dS0 = dS0;
     (void)hipGetLastError();
-    hipError_t err = la::launch_backward(bp);
+    hipError_t err = (p.path == LA_PATH_MFMA && p.N > 0) ? la::launch_backward_ssd_mfma(bp)
+                                                         : la::launch_backward(bp);
     if (err == hipSuccess) err = hipGetLastError();
     return err == hipSuccess ? LA_OK : LA_ERR_HIP;
 }

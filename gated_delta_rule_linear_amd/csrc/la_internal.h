@@ -74,6 +74,10 @@ struct BwdProblem {
 bool backward_supported(int variant);
 size_t backward_workspace_bytes(const Problem& p);
 hipError_t launch_backward(const BwdProblem& p);
+// backward_ssd_mfma.hip (SSD backward on the matrix cores: bf16, d_k = 128, d_v = 64)
+bool ssd_backward_mfma_supported(const Problem& p);
+size_t ssd_backward_mfma_workspace_bytes(const Problem& p);
+hipError_t launch_backward_ssd_mfma(const BwdProblem& p);
 
 // selective_scan.hip (Mamba-1 selective scan), a validated call
 struct ScanProblem {

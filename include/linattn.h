@@ -181,9 +181,12 @@ int la_decode_step(const la_desc* d, const void* q, const void* k, const void* v
  * (the training side of the same prefill; "线性注意力与 SSM" notes that training keeps
  * length-N activations and may recompute states, which this does: the chunk-entering
  * states are recomputed into the workspace). Variants: LA_GLA and LA_SSD (the diagonal
- * transitions); others return LA_ERR_UNSUPPORTED. It runs in fp32 on the vector ALUs
- * (d->path LA_PATH_AUTO or LA_PATH_VALU, chunk 0 or 16) for any supported d_k, d_v and
- * either io dtype.
+ * transitions); others return LA_ERR_UNSUPPORTED. SSD with bf16 io, d_k = 128 and
+ * d_v = 64 runs on the matrix cores (bf16 operands, fp32 accumulation, chunk 64) for
+ * d->path LA_PATH_AUTO or LA_PATH_MFMA; every other case (and LA_PATH_VALU) runs in fp32
+ * on the vector ALUs (chunk 16) for any supported d_k, d_v and either io dtype.
+ * LA_PATH_MFMA for a shape the matrix cores do not take is LA_ERR_UNSUPPORTED; a chunk
+ * other than 0 or the path's is LA_ERR_UNSUPPORTED.
  *   q, k, v, g, S0     the forward's inputs (S0 may be NULL)
  *   dO                 [B, H, N, d_v] io
  *   dq, dk             [B, H, N, d_k] io, written;  dv [B, H, N, d_v] io, written

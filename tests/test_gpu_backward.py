@@ -115,3 +115,19 @@ def test_backward_tiny_gates():
     inp.dev["g"], inp.exact["g"] = W.round_to(g, "f32")
     banner("backward gla tiny gates")
     check(*run_both("gla", inp, dO, dO_x, dSf, dSf_x), TOL["f32"])
+
+
+@pytest.mark.parametrize("N", [64, 200, 257])
+def test_backward_ssd_matrix_cores_vs_valu(N):
+    """The matrix-core SSD backward (bf16, d_k = 128, d_v = 64, chunk 64) against the oracle
+    and against the fp32 VALU backward on the same inputs."""
+    inp, dO, dO_x, dSf, dSf_x = make_case("ssd", 2, 3, N, 128, 64, "bf16", seed=N)
+    banner(f"backward ssd matrix cores N={N}")
+    got, ref = run_both("ssd", inp, dO, dO_x, dSf, dSf_x)
+    check(got, ref, TOL["bf16"])
+    d = {k: dev(v) for k, v in inp.dev.items()}
+    valu = bd.prefill_backward(d["q"], d["k"], d["v"], d["g"], dev(dO), variant="ssd",
+                               S0=d.get("S0"), dS_final=dev(dSf), path="valu")
+    torch.cuda.synchronize()
+    for name, t in zip(("dq", "dk", "dv", "dg", "dS0"), valu):
+        assert relerr(got[name], t.double().cpu().numpy()) <= TOL["bf16"], name
