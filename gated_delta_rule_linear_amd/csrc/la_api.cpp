@@ -459,6 +459,11 @@ int la_selective_scan(const la_scan_desc* d, const void* dt, const float* A, con
     const uint64_t s_h = mul(mul(mul(rows, D), n), 4);
     if (s_tok == UINT64_MAX || s_bc == UINT64_MAX || s_A == UINT64_MAX || s_h == UINT64_MAX)
         return LA_ERR_INVALID;
+    // one batch row of dt / x / y, and of B / C (with a chunk of padding), must stay below
+    // 2 GiB: the kernel addresses a row with 32-bit offsets
+    if (mul(T, mul(D, isz)) >= (uint64_t(1) << 31) - 256 ||
+        mul(T + 32, mul(n, isz)) >= (uint64_t(1) << 31) - 256)
+        return LA_ERR_UNSUPPORTED;
     const bool states = rows * D > 0;
     const bool tokens = states && T > 0;
     if (states && (!A || !h_final)) return LA_ERR_INVALID;

@@ -238,7 +238,8 @@ typedef struct la_scan_desc {
  * and dt_bias 4 bytes. All buffers are device memory owned by the caller; the call only
  * enqueues work on the stream. T = 0 copies h0 (or zeros) to h_final; Bt * D = 0 does
  * nothing. Errors as for la_prefill: LA_ERR_INVALID (null required pointer, bad dtype or
- * flag, negative size, misalignment, overlap), LA_ERR_UNSUPPORTED (n), LA_ERR_HIP. */
+ * flag, negative size, misalignment, overlap), LA_ERR_UNSUPPORTED (n, or one batch row of
+ * dt / x / y or of B / C reaching 2 GiB), LA_ERR_HIP. */
 int la_selective_scan(const la_scan_desc* d, const void* dt, const float* A, const void* Bm,
                       const void* Cm, const void* x, const float* Dskip, const float* dt_bias,
                       const float* h0, void* y, float* h_final, void* stream);

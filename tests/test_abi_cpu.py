@@ -305,6 +305,7 @@ def call_scan(lib, desc, **p):
     ("y_overlaps_x", bd.LA_ERR_INVALID),
     ("h_partial_overlap_h0", bd.LA_ERR_INVALID),
     ("h_overlaps_A", bd.LA_ERR_INVALID),
+    ("row_over_2GiB", bd.LA_ERR_UNSUPPORTED),
 ])
 def test_selective_scan_rejects(lib, case, expect):
     d = bd.ScanDesc(2, 50, 40, 16, bd.LA_BF16, 1)
@@ -339,6 +340,8 @@ def test_selective_scan_rejects(lib, case, expect):
         p["h_final"] = addr(7, 16)
     elif case == "h_overlaps_A":
         p["h_final"] = addr(1, 16)
+    elif case == "row_over_2GiB":
+        d.T, d.D = 1 << 20, 1024   # 2 GiB of bf16 per batch row
     assert call_scan(lib, d, **p) == expect
 
 
