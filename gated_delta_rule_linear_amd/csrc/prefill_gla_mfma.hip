@@ -741,7 +741,11 @@ WsLayout ws_layout(const Problem& p) {
     return L;
 }
 
-int pick_nvt(int dv) { return dv >= 64 ? 4 : dv / 16; }
+// Value columns per workgroup: 64 for d_v = 64 (one tile per sequence), but 32 for
+// d_v = 128: four smaller tiles per sequence put two workgroups on each CU, whose
+// latencies overlap, which measured faster than two 64-column tiles at one per CU even
+// though every tile re-reads the chunk's q^, k^T and P.
+int pick_nvt(int dv) { return dv == 128 ? 2 : dv >= 64 ? 4 : dv / 16; }
 
 template <bool GB, bool SG, int NVT>
 hipError_t launch_nvt(const Problem& p) {
