@@ -7,6 +7,7 @@ missing the first call raises; there is no fallback.
 from __future__ import annotations
 
 import ctypes
+from typing import NamedTuple
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -251,20 +252,30 @@ def decode_step(q, k, v, S, g=None, beta=None, *, variant: str, z=None, eps: flo
     return o
 
 
-def prefill_backward(q, k, v, g, dO, *, variant: str, S0=None, dS_final=None, dq=None, dk=None,
-                     dv=None, dg=None, dS0=None, path: str = "auto", workspace=None, stream=None):
-    """Gradients of ``prefill`` through ``la_prefill_backward`` (GLA and SSD).
+class BackwardGrads(NamedTuple):
+    dq: object
+    dk: object
+    dv: object
+    dg: object
+    dbeta: object   # GDN only, else None
+    dS0: object
 
-    q, k, v, g, S0 as given to ``prefill``; dO [B,H,N,dv] (q's dtype); dS_final
-    [B,H,dk,dv] float32 or None. Returns (dq, dk, dv, dg, dS0).
+
+def prefill_backward(q, k, v, g, dO, *, variant: str, beta=None, S0=None, dS_final=None,
+                     dq=None, dk=None, dv=None, dg=None, dbeta=None, dS0=None,
+                     path: str = "auto", workspace=None, stream=None) -> BackwardGrads:
+    """Gradients of ``prefill`` through ``la_prefill_backward`` (GLA, SSD, GDN).
+
+    q, k, v, g, beta (GDN), S0 as given to ``prefill``; dO [B,H,N,dv] (q's dtype);
+    dS_final [B,H,dk,dv] float32 or None. Returns BackwardGrads(dq, dk, dv, dg, dbeta, dS0).
     """
     import torch
     lib = load()
     B, H, N, dk_ = q.shape
     dv_ = v.shape[-1]
-    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("dO", dO), ("S0", S0),
-                    ("dS_final", dS_final), ("dq", dq), ("dk", dk), ("dv", dv), ("dg", dg),
-                    ("dS0", dS0)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("dO", dO),
+                    ("S0", S0), ("dS_final", dS_final), ("dq", dq), ("dk", dk), ("dv", dv),
+                    ("dg", dg), ("dbeta", dbeta), ("dS0", dS0)):
         _require_contig(name, t)
     desc = make_desc(variant, B, H, N, dk_, dv_, _dtype_code(q), _dtype_code(g), 1e-6, path)
     dev = q.device
@@ -272,6 +283,8 @@ def prefill_backward(q, k, v, g, dO, *, variant: str, S0=None, dS_final=None, dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     dg = torch.empty_like(g) if dg is None else dg
+    if beta is not None and dbeta is None:
+        dbeta = torch.empty_like(beta)
     if dS0 is None:
         dS0 = torch.empty((B, H, dk_, dv_), dtype=torch.float32, device=dev)
     n = ctypes.c_size_t(0)
@@ -281,13 +294,13 @@ def prefill_backward(q, k, v, g, dO, *, variant: str, S0=None, dS_final=None, dq
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = lib.la_prefill_backward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), None,
-                                 _ptr(S0), None, _ptr(dO), _ptr(dS_final), None, _ptr(dq),
-                                 _ptr(dk), _ptr(dv), _ptr(dg), None, _ptr(dS0), None,
-                                 _ptr(workspace if ws_bytes else None), wsz,
+    rc = lib.la_prefill_backward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                 _ptr(beta), _ptr(S0), None, _ptr(dO), _ptr(dS_final), None,
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dS0),
+                                 None, _ptr(workspace if ws_bytes else None), wsz,
                                  _stream_handle(stream, dev))
     _check(rc, "la_prefill_backward")
-    return dq, dk, dv, dg, dS0
+    return BackwardGrads(dq, dk, dv, dg, dbeta, dS0)
 
 
 def selective_scan(dt, A, Bm, Cm, x, Dskip=None, dt_bias=None, *, dt_softplus: bool = True,

@@ -1,0 +1,467 @@
+// Backward of the chunked Gated DeltaNet prefill ("线性注意力与 SSM", section GDN: the
+// gated delta rule S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T, o_t =
+// S_t^T q_t, key-major), in fp32 on the vector ALUs with chunk C = 16.
+//
+// Token form. With u_t = beta_t (v_t - alpha_t p_t), p_t = S_{t-1}^T k_t, and G_t the
+// gradient of the loss with respect to S_t (everything downstream of token t, o_t included):
+//   du_t = G_t^T k_t,  dv_t = beta_t du_t,  dbeta_t = du_t . (v_t - alpha_t p_t),
+//   dq_t = S_t do_t,   dk_t = G_t u_t - alpha_t beta_t S_{t-1} du_t,
+//   dalpha_t = <G_t, S_{t-1}> - beta_t du_t . p_t,
+//   G_{t-1} = alpha_t (G_t - beta_t k_t du_t^T) + q_{t-1} do_{t-1}^T.
+// The gate gradient is taken in this direct form. The log-domain alternative (a reverse
+// cumulative sum of dL/dlog alpha, divided by alpha) cancels down to O(alpha) and loses
+// fp32 accuracy by 1/alpha.
+//
+// Chunk form. Inside a chunk with cumulative log gates c_r (base 2 here), D_rs = 2^(c_r -
+// c_s) for s <= r, L_rs = beta_r D_rs k_r.k_s (s < r), P_rs = D_rs q_r.k_s (s <= r),
+// entering state S0 and leaving-state gradient dS':
+//   U  = (I + L)^-1 X,     X_r = beta_r (v_r - 2^c_r S0^T k_r)          (the forward's U)
+//   dU = (I + L)^-T R,     R_s = 2^(c_last - c_s) dS'^T k_s + sum_{r>=s} P_rs do_r
+// (dU is du of every token: the unrolled G_t, dotted with k_t, is this triangular system),
+//   S_t = 2^c_t S0 + sum_{s<=t} D_ts k_s u_s^T,
+//   G_t = 2^(c_last-c_t) dS' + sum_{r>=t} D_rt q_r do_r^T - sum_{s>t} D_st beta_s k_s du_s^T.
+// Substituting these into the token form turns every gradient into sums, with weights
+// that are products of decays (all <= 1), over the chunk's rows of the value-column dot
+// products A_rs = do_r.u_s, B_rs = du_r.u_s, kappa_s = (dS'^T k_s).u_s, rho_r = (S0^T
+// q_r).do_r, mu_s = (S0^T k_s).du_s, sigma = <dS', S0>, and of d_k-vectors such as S0 do_t.
+//
+// Kernels: one launch runs both chains, each workgroup one (sequence, 16-column value tile)
+// (value columns never mix in either recurrence): the forward chain writes the state
+// entering every chunk, the reverse chain the gradient leaving it (dS_in = 2^c_last dS' +
+// sum_r 2^c_r q_r do_r^T - sum_s beta_s 2^c_s k_s du_s^T), and dS0. Then the grads kernel
+// takes every (sequence, chunk) in parallel, loops over the value tiles accumulating the
+// column sums, and writes final dq, dk, dv, dalpha and dbeta.
+#include "common.hpp"
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+constexpr int C = kValuChunk;  // 16
+constexpr int VT = 16;         // value columns per tile
+constexpr int NT = 256;        // = C * VT = C * C
+static_assert(C * VT == NT && C * C == NT, "thread maps assume 16 x 16");
+
+struct GdnBwdArgs {
+    const void *q, *k, *v, *g, *beta, *dO;
+    const float *S0, *dSf;
+    void *dq, *dk, *dv, *dg, *dbeta;
+    float* dS0;
+    float* Sck;    // [nseq][nchunks][DK][DV] state entering each chunk
+    float* dSck;   // [nseq][nchunks][DK][DV] gradient of the state leaving each chunk
+    int N, nseq, ntiles, nchunks;
+    int io_bf16, gate_bf16;
+};
+
+// The rows of one chunk shared by both kernels: k (and q), the cumulative base-2 log gate,
+// beta and the decay factors. Rows past the end are zero with gate 1 and beta 0, which
+// makes them identity steps.
+template <int DK>
+struct Rows {
+    float q[C][DK + 1], k[C][DK + 1];
+    float c[C], b[C];
+    float eg[C];    // 2^c_r (decay from the chunk start through row r)
+    float el[C];    // 2^(c_last - c_r) (decay after row r to the chunk end)
+};
+
+template <int DK, bool WQ>
+__device__ __forceinline__ void load_rows(Rows<DK>& sm, const GdnBwdArgs& a, size_t tok, int n) {
+    const int tid = threadIdx.x;
+    const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
+    for (int idx = tid; idx < C * DK; idx += NT) {
+        const int r = idx / DK, i = idx % DK;
+        const size_t e = (tok + r) * DK + i;
+        sm.k[r][i] = r < n ? load_elem(a.k, e, iob) : 0.f;
+        if (WQ) sm.q[r][i] = r < n ? load_elem(a.q, e, iob) : 0.f;
+    }
+    if (tid < kWave) {   // one wave: the log gates, their prefix sums, beta
+        const int r = tid;
+        float lg = 0.f, bt = 0.f;
+        if (r < n) {
+            lg = __builtin_amdgcn_logf(load_elem(a.g, tok + r, gb));
+            bt = load_elem(a.beta, tok + r, gb);
+        }
+        const float cs = wave_inclusive_scan(r < C ? lg : 0.f);
+        const float cl = __shfl(cs, C - 1);
+        if (r < C) {
+            sm.c[r] = cs;
+            sm.b[r] = bt;
+            sm.eg[r] = __builtin_amdgcn_exp2f(cs);
+            sm.el[r] = __builtin_amdgcn_exp2f(cl - cs);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------- chains
+template <int DK>
+struct ChainSmem {
+    Rows<DK> rw;
+    float S[DK][VT + 1];    // state (forward) or state gradient (reverse) tile
+    float x[C][VT];         // v (forward) or dO (reverse) tile
+    float L[C][C + 1], P[C][C + 1];
+    float rhs[C][VT], u[C][VT];
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(NT) void gdn_bwd_chains_kernel(GdnBwdArgs a) {
+    __shared__ ChainSmem<DK> sm;
+    const int tid = threadIdx.x;
+    const int nfw = a.nseq * a.ntiles;
+    const bool rev = int(blockIdx.x) >= nfw;
+    const int unit = rev ? int(blockIdx.x) - nfw : int(blockIdx.x);
+    const size_t seq = size_t(unit / a.ntiles);
+    const int c0 = (unit % a.ntiles) * VT;
+    const bool iob = a.io_bf16 != 0;
+    const size_t sbase = seq * DK * DV;
+    const float* init = rev ? a.dSf : a.S0;
+    for (int idx = tid; idx < DK * VT; idx += NT) {
+        const int i = idx / VT, j = idx % VT;
+        sm.S[i][j] = init ? init[sbase + size_t(i) * DV + c0 + j] : 0.f;
+    }
+    float* ck = (rev ? a.dSck : a.Sck) + seq * size_t(a.nchunks) * DK * DV;
+    const int r_me = tid / VT, j_me = tid % VT;
+    for (int it = 0; it < a.nchunks; ++it) {
+        const int ch = rev ? a.nchunks - 1 - it : it;
+        const int t0 = ch * C, n = min(C, a.N - t0);
+        const size_t tok = seq * size_t(a.N) + t0;
+        __syncthreads();   // the previous chunk's update and its readers are done
+        float* ckc = ck + size_t(ch) * DK * DV;
+        for (int idx = tid; idx < DK * VT; idx += NT) {
+            const int i = idx / VT, j = idx % VT;
+            ckc[size_t(i) * DV + c0 + j] = sm.S[i][j];
+        }
+        if (rev) load_rows<DK, true>(sm.rw, a, tok, n);
+        else load_rows<DK, false>(sm.rw, a, tok, n);
+        sm.x[r_me][j_me] = r_me < n ? load_elem(rev ? a.dO : a.v, (tok + r_me) * DV + c0 + j_me, iob)
+                                    : 0.f;
+        __syncthreads();
+        {   // thread (r, s): L and, for the reverse chain, P
+            const int r = tid / C, s = tid % C;
+            float kk = 0.f, qk = 0.f;
+            for (int i = 0; i < DK; ++i) {
+                kk += sm.rw.k[r][i] * sm.rw.k[s][i];
+                if (rev) qk += sm.rw.q[r][i] * sm.rw.k[s][i];
+            }
+            const float d = s <= r ? __builtin_amdgcn_exp2f(sm.rw.c[r] - sm.rw.c[s]) : 0.f;
+            sm.L[r][s] = s < r ? sm.rw.b[r] * d * kk : 0.f;
+            sm.P[r][s] = d * qk;
+        }
+        float ks = 0.f;   // thread (r, j): k_r . S[:, j]
+        for (int i = 0; i < DK; ++i) ks += sm.rw.k[r_me][i] * sm.S[i][j_me];
+        if (!rev) sm.rhs[r_me][j_me] = sm.rw.b[r_me] * (sm.x[r_me][j_me] - sm.rw.eg[r_me] * ks);
+        __syncthreads();
+        if (rev) {
+            float acc = sm.rw.el[r_me] * ks;
+            for (int t = r_me; t < C; ++t) acc += sm.P[t][r_me] * sm.x[t][j_me];
+            sm.rhs[r_me][j_me] = acc;
+            __syncthreads();
+        }
+        if (tid < VT) {   // triangular solve per column
+            const int j = tid;
+            if (!rev) {
+                for (int r = 0; r < C; ++r) {
+                    float u = sm.rhs[r][j];
+                    for (int s = 0; s < r; ++s) u -= sm.L[r][s] * sm.u[s][j];
+                    sm.u[r][j] = u;
+                }
+            } else {
+                for (int s = C - 1; s >= 0; --s) {
+                    float u = sm.rhs[s][j];
+                    for (int r = s + 1; r < C; ++r) u -= sm.L[r][s] * sm.u[r][j];
+                    sm.u[s][j] = u;
+                }
+            }
+        }
+        __syncthreads();
+        const float dl = sm.rw.eg[C - 1];
+        for (int idx = tid; idx < DK * VT; idx += NT) {
+            const int i = idx / VT, j = idx % VT;
+            float acc = 0.f;
+            if (!rev) {
+                for (int s = 0; s < C; ++s) acc += sm.rw.k[s][i] * sm.rw.el[s] * sm.u[s][j];
+            } else {
+                for (int r = 0; r < C; ++r)
+                    acc += sm.rw.eg[r] * (sm.rw.q[r][i] * sm.x[r][j] - sm.rw.b[r] * sm.rw.k[r][i] * sm.u[r][j]);
+            }
+            sm.S[i][j] = dl * sm.S[i][j] + acc;
+        }
+    }
+    if (rev) {
+        __syncthreads();
+        for (int idx = tid; idx < DK * VT; idx += NT) {
+            const int i = idx / VT, j = idx % VT;
+            a.dS0[sbase + size_t(i) * DV + c0 + j] = sm.S[i][j];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------- grads
+template <int DK>
+struct GradSmem {
+    Rows<DK> rw;
+    float gm[C];                 // 2^c_{t-1} (1 for the first row)
+    float D[C][C + 1];           // 2^(c_r - c_s), s <= r; 0 above
+    float Dm[C][C + 1];          // 2^(c_{t-1} - c_s), s < t; 0 elsewhere
+    float KK[C][C + 1], QK[C][C + 1], L[C][C + 1];
+    float S0[DK][VT + 1], dS[DK][VT + 1];
+    float v[C][VT], dO[C][VT];
+    float KS[C][VT], X[C][VT], R[C][VT], U[C][VT], dU[C][VT];
+    float A[C][C + 1], Bm[C][C + 1];
+    float kap[C], rho[C], mu[C], dup[C];
+    float sig[NT / kWave];
+};
+
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<0xB1, 0xf, 0xf>(v);
+    v += dpp_f<0x4E, 0xf, 0xf>(v);
+    v += dpp_f<0x141, 0xf, 0xf>(v);
+    v += dpp_f<0x140, 0xf, 0xf>(v);
+    return v;
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(NT) void gdn_bwd_grads_kernel(GdnBwdArgs a) {
+    constexpr int MQ = C * DK / NT;   // (row, key dim) pairs per thread
+    static_assert(MQ >= 1 && (C * DK) % NT == 0, "d_k >= 16");
+    __shared__ GradSmem<DK> sm;
+    const int tid = threadIdx.x;
+    const int ch = int(blockIdx.x % unsigned(a.nchunks));
+    const size_t seq = blockIdx.x / unsigned(a.nchunks);
+    const int t0 = ch * C, n = min(C, a.N - t0);
+    const size_t tok = seq * size_t(a.N) + t0;
+    const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
+    const int r_me = tid / C, x_me = tid % C;   // (row, column) of the 16 x 16 maps
+    load_rows<DK, true>(sm.rw, a, tok, n);
+    __syncthreads();
+    {
+        const int r = r_me, s = x_me;
+        float kk = 0.f, qk = 0.f;
+        for (int i = 0; i < DK; ++i) {
+            kk += sm.rw.k[r][i] * sm.rw.k[s][i];
+            qk += sm.rw.q[r][i] * sm.rw.k[s][i];
+        }
+        const float d = s <= r ? __builtin_amdgcn_exp2f(sm.rw.c[r] - sm.rw.c[s]) : 0.f;
+        const float cm = r > 0 ? sm.rw.c[r - 1] : 0.f;
+        sm.D[r][s] = d;
+        sm.Dm[r][s] = s < r ? __builtin_amdgcn_exp2f(cm - sm.rw.c[s]) : 0.f;
+        sm.KK[r][s] = kk;
+        sm.QK[r][s] = qk;
+        sm.L[r][s] = s < r ? sm.rw.b[r] * d * kk : 0.f;
+        if (s == 0) sm.gm[r] = r > 0 ? sm.rw.eg[r - 1] : 1.f;
+    }
+    float accq[MQ], acck[MQ];
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) accq[m] = acck[m] = 0.f;
+    float A_acc = 0.f, B_acc = 0.f;                            // (r_me, x_me)
+    float kap = 0.f, rho = 0.f, mu = 0.f, dbt = 0.f, dup = 0.f;  // row r_me (lane x_me == 0)
+    float sig = 0.f;
+    const size_t ckoff = (seq * a.nchunks + ch) * size_t(DK) * DV;
+    for (int tile = 0; tile < a.ntiles; ++tile) {
+        const int c0 = tile * VT;
+        __syncthreads();   // the previous tile's readers are done
+        for (int idx = tid; idx < DK * VT; idx += NT) {
+            const int i = idx / VT, j = idx % VT;
+            const size_t e = ckoff + size_t(i) * DV + c0 + j;
+            const float s0 = a.Sck[e], ds = a.dSck[e];
+            sm.S0[i][j] = s0;
+            sm.dS[i][j] = ds;
+            sig += s0 * ds;
+        }
+        {
+            const int t = r_me, j = x_me;
+            const size_t e = (tok + t) * DV + c0 + j;
+            sm.v[t][j] = t < n ? load_elem(a.v, e, iob) : 0.f;
+            sm.dO[t][j] = t < n ? load_elem(a.dO, e, iob) : 0.f;
+        }
+        __syncthreads();
+        const int t = r_me, j = x_me;
+        float ks = 0.f, kds = 0.f, qs = 0.f;
+        for (int i = 0; i < DK; ++i) {
+            ks += sm.rw.k[t][i] * sm.S0[i][j];
+            kds += sm.rw.k[t][i] * sm.dS[i][j];
+            qs += sm.rw.q[t][i] * sm.S0[i][j];
+        }
+        {
+            float r_ = sm.rw.el[t] * kds;
+            for (int r = t; r < C; ++r) r_ += sm.D[r][t] * sm.QK[r][t] * sm.dO[r][j];
+            sm.KS[t][j] = ks;
+            sm.X[t][j] = sm.rw.b[t] * (sm.v[t][j] - sm.rw.eg[t] * ks);
+            sm.R[t][j] = r_;
+        }
+        __syncthreads();
+        if (tid < VT) {   // U: forward substitution, one column per thread
+            const int jj = tid;
+            for (int r = 0; r < C; ++r) {
+                float u = sm.X[r][jj];
+                for (int s = 0; s < r; ++s) u -= sm.L[r][s] * sm.U[s][jj];
+                sm.U[r][jj] = u;
+            }
+        } else if (tid >= kWave && tid < kWave + VT) {   // dU: back substitution (another wave)
+            const int jj = tid - kWave;
+            for (int s = C - 1; s >= 0; --s) {
+                float u = sm.R[s][jj];
+                for (int r = s + 1; r < C; ++r) u -= sm.L[r][s] * sm.dU[r][jj];
+                sm.dU[s][jj] = u;
+            }
+        }
+        __syncthreads();
+        {
+            const float u = sm.U[t][j], du = sm.dU[t][j];
+            float p = sm.gm[t] * ks, ap = sm.rw.eg[t] * ks;
+            for (int s = 0; s < t; ++s) {
+                const float ku = sm.KK[t][s] * sm.U[s][j];
+                p += sm.Dm[t][s] * ku;
+                ap += sm.D[t][s] * ku;
+            }
+            if (t < n) store_elem(a.dv, (tok + t) * DV + c0 + j, sm.rw.b[t] * du, iob);
+            const float s_kap = row16_sum(kds * u), s_rho = row16_sum(qs * sm.dO[t][j]);
+            const float s_mu = row16_sum(ks * du), s_db = row16_sum(du * (sm.v[t][j] - ap));
+            const float s_dup = row16_sum(du * p);
+            kap += s_kap; rho += s_rho; mu += s_mu; dbt += s_db; dup += s_dup;
+            float av = 0.f, bv = 0.f;   // (r_me, x_me) = (r, s)
+            for (int jj = 0; jj < VT; ++jj) {
+                av += sm.dO[r_me][jj] * sm.U[x_me][jj];
+                bv += sm.dU[r_me][jj] * sm.U[x_me][jj];
+            }
+            A_acc += av;
+            B_acc += bv;
+        }
+#pragma unroll
+        for (int m = 0; m < MQ; ++m) {
+            const int idx = tid + NT * m, tt = idx / DK, i = idx % DK;
+            float so = 0.f, su = 0.f, sdu = 0.f;
+            for (int jj = 0; jj < VT; ++jj) {
+                so += sm.S0[i][jj] * sm.dO[tt][jj];
+                su += sm.dS[i][jj] * sm.U[tt][jj];
+                sdu += sm.S0[i][jj] * sm.dU[tt][jj];
+            }
+            accq[m] += sm.rw.eg[tt] * so;
+            acck[m] += sm.rw.el[tt] * su - sm.rw.b[tt] * sm.rw.eg[tt] * sdu;
+        }
+    }
+    // the column sums over all tiles
+    sm.A[r_me][x_me] = A_acc;
+    sm.Bm[r_me][x_me] = B_acc;
+    if (x_me == 0) {
+        sm.kap[r_me] = kap;
+        sm.rho[r_me] = rho;
+        sm.mu[r_me] = mu;
+        sm.dup[r_me] = dup;
+        if (r_me < n) store_elem(a.dbeta, tok + r_me, dbt, gb);
+    }
+    sig = wave_sum(sig);
+    if ((tid & (kWave - 1)) == 0) sm.sig[tid / kWave] = sig;
+    __syncthreads();
+    {   // dalpha: thread (t, x) takes the terms of row / column x, summed over the 16 lanes
+        const int t = r_me, x = x_me;
+        const float gm = sm.gm[t];
+        float term = 0.f;
+        if (x < t) term += sm.rw.el[t] * sm.Dm[t][x] * sm.kap[x];
+        if (x >= t) {
+            float in = gm * sm.rho[x];
+            for (int s = 0; s < t; ++s) in += sm.Dm[t][s] * sm.QK[x][s] * sm.A[x][s];
+            term += sm.D[x][t] * in;
+        }
+        if (x > t) {
+            float in = gm * sm.mu[x];
+            for (int s = 0; s < t; ++s) in += sm.Dm[t][s] * sm.KK[x][s] * sm.Bm[x][s];
+            term -= sm.D[x][t] * sm.rw.b[x] * in;
+        }
+        term = row16_sum(term);
+        if (x == 0 && t < n) {
+            float sg = 0.f;
+            for (int w = 0; w < NT / kWave; ++w) sg += sm.sig[w];
+            const float da = term + sm.rw.el[t] * gm * sg - sm.rw.b[t] * sm.dup[t];
+            store_elem(a.dg, tok + t, da, gb);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) {
+        const int idx = tid + NT * m, t = idx / DK, i = idx % DK;
+        float dq = accq[m], dk = acck[m];
+        for (int s = 0; s <= t; ++s) dq += sm.D[t][s] * sm.A[t][s] * sm.rw.k[s][i];
+        for (int r = t; r < C; ++r) dk += sm.D[r][t] * sm.A[r][t] * sm.rw.q[r][i];
+        for (int s = t + 1; s < C; ++s) dk -= sm.D[s][t] * sm.Bm[s][t] * sm.rw.b[s] * sm.rw.k[s][i];
+        float bk = 0.f;
+        for (int s = 0; s < t; ++s) bk += sm.D[t][s] * sm.Bm[t][s] * sm.rw.k[s][i];
+        dk -= sm.rw.b[t] * bk;
+        if (t < n) {
+            store_elem(a.dq, (tok + t) * DK + i, dq, iob);
+            store_elem(a.dk, (tok + t) * DK + i, dk, iob);
+        }
+    }
+}
+
+struct GdnLayout {
+    size_t Sck, dSck, total;
+};
+GdnLayout gdn_layout(const Problem& p) {
+    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    const size_t nseq = size_t(p.B) * p.H, nchunks = size_t((p.N + C - 1) / C);
+    GdnLayout L{};
+    L.Sck = 0;
+    L.dSck = al(nseq * nchunks * p.dk * p.dv * 4);
+    L.total = L.dSck + al(nseq * nchunks * p.dk * p.dv * 4);
+    return L;
+}
+
+template <int DK, int DV>
+hipError_t launch_dims(const Problem& p, GdnBwdArgs a) {
+    const unsigned chains = unsigned(2 * a.nseq * a.ntiles);
+    gdn_bwd_chains_kernel<DK, DV><<<dim3(chains), dim3(NT), 0, p.stream>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned units = unsigned(size_t(a.nseq) * a.nchunks);
+    gdn_bwd_grads_kernel<DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int DK>
+hipError_t dispatch_dv(const Problem& p, const GdnBwdArgs& a) {
+    switch (p.dv) {
+        case 16: return launch_dims<DK, 16>(p, a);
+        case 32: return launch_dims<DK, 32>(p, a);
+        case 64: return launch_dims<DK, 64>(p, a);
+        case 128: return launch_dims<DK, 128>(p, a);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t gdn_backward_workspace_bytes(const Problem& p) {
+    if (p.N == 0 || p.B == 0 || p.H == 0) return 0;
+    return gdn_layout(p).total;
+}
+
+hipError_t launch_backward_gdn(const BwdProblem& bp) {
+    const Problem& p = bp.p;
+    const size_t nseq = size_t(p.B) * p.H;
+    const size_t nchunks = size_t((p.N + C - 1) / C);
+    if (2 * nseq * size_t(p.dv / VT) > 0x7fffffffull || nseq * nchunks > 0x7fffffffull)
+        return hipErrorInvalidValue;
+    const GdnLayout L = gdn_layout(p);
+    unsigned char* ws = static_cast<unsigned char*>(p.ws);
+    GdnBwdArgs a{};
+    a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.beta = p.beta; a.dO = bp.dO;
+    a.S0 = p.S0; a.dSf = bp.dS_final;
+    a.dq = bp.dq; a.dk = bp.dk; a.dv = bp.dv; a.dg = bp.dg; a.dbeta = bp.dbeta;
+    a.dS0 = bp.dS0;
+    a.Sck = reinterpret_cast<float*>(ws + L.Sck);
+    a.dSck = reinterpret_cast<float*>(ws + L.dSck);
+    a.N = p.N;
+    a.nseq = int(nseq);
+    a.ntiles = p.dv / VT;
+    a.nchunks = int(nchunks);
+    a.io_bf16 = p.io_bf16;
+    a.gate_bf16 = p.gate_bf16;
+    switch (p.dk) {
+        case 16: return dispatch_dv<16>(p, a);
+        case 32: return dispatch_dv<32>(p, a);
+        case 64: return dispatch_dv<64>(p, a);
+        case 128: return dispatch_dv<128>(p, a);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace la

@@ -428,10 +428,13 @@ __global__ void bwd_copy_kernel(const float* dSf, float* dS0, size_t n) {
 
 }  // namespace
 
-bool backward_supported(int variant) { return variant == LA_GLA || variant == LA_SSD; }
+bool backward_supported(int variant) {
+    return variant == LA_GLA || variant == LA_SSD || variant == LA_GDN;
+}
 
 size_t backward_workspace_bytes(const Problem& p) {
     if (p.N == 0 || p.B == 0 || p.H == 0) return 0;
+    if (p.variant == LA_GDN) return gdn_backward_workspace_bytes(p);
     return bwd_layout(p).total;
 }
 
@@ -444,6 +447,7 @@ hipError_t launch_backward(const BwdProblem& bp) {
         bwd_copy_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, p.stream>>>(bp.dS_final, bp.dS0, n);
         return hipGetLastError();
     }
+    if (p.variant == LA_GDN) return launch_backward_gdn(bp);
     const size_t nseq = size_t(p.B) * p.H;
     const size_t nchunks = size_t((p.N + C - 1) / C);
     if (nseq * nchunks * size_t(p.dv / VT) > 0x7fffffffull ||

@@ -397,15 +397,18 @@ int la_prefill_backward(const la_desc* d, const void* q, const void* k, const vo
     la::Problem p;
     int rc = check_backward_desc(d, p);
     if (rc != LA_OK) return rc;
-    // GLA and SSD take no beta and no normaliser
-    if (beta || z0 || dz_final || dbeta || dz0) return LA_ERR_INVALID;
+    // no variant built here has a normaliser; only GDN (the delta rule) takes beta
+    const bool delta = d->variant == LA_GDN;
+    if (z0 || dz_final || dz0) return LA_ERR_INVALID;
+    if (!delta && (beta || dbeta)) return LA_ERR_INVALID;
     const bool seqs = (uint64_t(d->B) * uint64_t(d->H)) > 0;
     const bool tokens = seqs && d->N > 0;
     if (seqs && !dS0) return LA_ERR_INVALID;
     if (tokens && (!q || !k || !v || !g || !dO || !dq || !dk || !dv || !dg)) return LA_ERR_INVALID;
-    // alignment: dq, dk as q; dv, dO as v; dg as g; the fp32 states 16 bytes
-    if (!check_alignment(*d, q, k, v, g, nullptr, S0, nullptr, dv, dS0, nullptr) ||
-        !check_alignment(*d, dq, dk, dO, dg, nullptr, dS_final, nullptr, nullptr, nullptr, nullptr))
+    if (tokens && delta && (!beta || !dbeta)) return LA_ERR_INVALID;
+    // alignment: dq, dk as q; dv, dO as v; dg as g; dbeta as beta; the fp32 states 16 bytes
+    if (!check_alignment(*d, q, k, v, g, beta, S0, nullptr, dv, dS0, nullptr) ||
+        !check_alignment(*d, dq, dk, dO, dg, dbeta, dS_final, nullptr, nullptr, nullptr, nullptr))
         return LA_ERR_INVALID;
     const Sizes s = sizes_of(*d);
     const uint64_t tk = tokens ? 1 : 0;
@@ -413,13 +416,14 @@ int la_prefill_backward(const la_desc* d, const void* q, const void* k, const vo
                 rg = range(g, s.g * tk), rS0 = range(S0, s.S), rdO = range(dO, s.o * tk),
                 rdSf = range(dS_final, s.S), rdq = range(dq, s.q * tk), rdk = range(dk, s.k * tk),
                 rdv = range(dv, s.v * tk), rdg = range(dg, s.g * tk),
-                rdS0 = range(dS0, s.S);
+                rdS0 = range(dS0, s.S), rb = range(beta, s.beta * tk),
+                rdb = range(dbeta, s.beta * tk);
     // outputs overlap nothing: not the inputs, not each other
-    const Range outs[] = {rdq, rdk, rdv, rdg, rdS0};
-    const Range all[] = {rq, rk, rv, rg, rS0, rdO, rdSf, rdq, rdk, rdv, rdg, rdS0};
-    for (int a = 0; a < 5; ++a)
+    const Range outs[] = {rdq, rdk, rdv, rdg, rdS0, rdb};
+    const Range all[] = {rq, rk, rv, rg, rS0, rdO, rdSf, rb, rdq, rdk, rdv, rdg, rdS0, rdb};
+    for (int a = 0; a < 6; ++a)
         for (const Range& x : all)
-            if (&x != &all[7 + a] && overlap(outs[a], x)) return LA_ERR_INVALID;
+            if (&x != &all[8 + a] && overlap(outs[a], x)) return LA_ERR_INVALID;
     const size_t need = backward_workspace(p);
     if (need > 0) {
         if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return LA_ERR_WORKSPACE;
@@ -428,13 +432,13 @@ int la_prefill_backward(const la_desc* d, const void* q, const void* k, const vo
             if (overlap(rw, x)) return LA_ERR_INVALID;
     }
     if (!seqs) return LA_OK;
-    p.q = q; p.k = k; p.v = v; p.g = g; p.S0 = S0;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.S0 = S0;
     p.ws = workspace; p.ws_bytes = workspace_bytes;
     p.stream = static_cast<hipStream_t>(stream);
     la::BwdProblem bp;
     bp.p = p;
     bp.dO = dO; bp.dS_final = dS_final;
-    bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dS0 = dS0;
+    bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dbeta = dbeta; bp.dS0 = dS0;
     (void)hipGetLastError();
     hipError_t err = (p.path == LA_PATH_MFMA && p.N > 0) ? la::launch_backward_ssd_mfma(bp)
                                                          : la::launch_backward(bp);

@@ -63,17 +63,22 @@ bool gdn_mfma_supported(int dk, int dv, bool io_bf16);
 size_t gdn_mfma_workspace_bytes(const Problem& p);
 hipError_t launch_prefill_gdn_mfma(const Problem& p);
 
-// backward_valu.hip (backward of the prefill, diagonal transitions), a validated call
+// backward_valu.hip (backward of the prefill: GLA, SSD; GDN by backward_gdn_valu.hip), a
+// validated call
 struct BwdProblem {
     Problem p;                       // the forward call (inputs, shapes, workspace, stream)
     const void* dO = nullptr;        // dL/do [B,H,N,dv] io
     const float* dS_final = nullptr; // dL/dS_final [B,H,dk,dv] or null (zero)
     void *dq = nullptr, *dk = nullptr, *dv = nullptr, *dg = nullptr;
+    void* dbeta = nullptr;           // GDN: dL/dbeta [B,H,N] gate dtype
     float* dS0 = nullptr;
 };
 bool backward_supported(int variant);
 size_t backward_workspace_bytes(const Problem& p);
 hipError_t launch_backward(const BwdProblem& p);
+// backward_gdn_valu.hip (GDN backward, fp32 vector ALUs); called through launch_backward
+size_t gdn_backward_workspace_bytes(const Problem& p);
+hipError_t launch_backward_gdn(const BwdProblem& p);
 // backward_ssd_mfma.hip (SSD backward on the matrix cores: bf16, d_k = 128, d_v = 64)
 bool ssd_backward_mfma_supported(const Problem& p);
 size_t ssd_backward_mfma_workspace_bytes(const Problem& p);

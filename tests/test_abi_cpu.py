@@ -375,8 +375,13 @@ def call_bwd(lib, desc, ws=None, ws_bytes=0, **p):
 
 @pytest.mark.parametrize("case,expect", [
     ("null_desc", bd.LA_ERR_INVALID),
-    ("gdn_unsupported", bd.LA_ERR_UNSUPPORTED),
+    ("kda_unsupported", bd.LA_ERR_UNSUPPORTED),
     ("kath_unsupported", bd.LA_ERR_UNSUPPORTED),
+    ("gdn_null_beta", bd.LA_ERR_INVALID),
+    ("gdn_null_dbeta", bd.LA_ERR_INVALID),
+    ("gdn_dbeta_overlaps_beta", bd.LA_ERR_INVALID),
+    ("gdn_dbeta_overlaps_dg", bd.LA_ERR_INVALID),
+    ("gdn_z0_given", bd.LA_ERR_INVALID),
     ("mfma_path", bd.LA_ERR_UNSUPPORTED),
     ("beta_given", bd.LA_ERR_INVALID),
     ("null_dO", bd.LA_ERR_INVALID),
@@ -389,9 +394,13 @@ def call_bwd(lib, desc, ws=None, ws_bytes=0, **p):
     ("no_workspace", bd.LA_ERR_WORKSPACE),
 ])
 def test_backward_rejects(lib, case, expect):
-    variant = {"gdn_unsupported": "gdn", "kath_unsupported": "kath"}.get(case, "gla")
+    variant = {"kda_unsupported": "kda", "kath_unsupported": "kath"}.get(case, "gla")
+    if case.startswith("gdn_"):
+        variant = "gdn"
     d = good(variant)
     p = bwd_args()
+    if variant == "gdn":
+        p["beta"], p["dbeta"] = addr(4), addr(15)
     ws, wsb = addr(20), 1 << 32
     if case == "null_desc":
         d = None
@@ -415,7 +424,26 @@ def test_backward_rejects(lib, case, expect):
         p["dS0"] = addr(5)
     elif case == "no_workspace":
         ws, wsb = None, 0
+    elif case == "gdn_null_beta":
+        p["beta"] = None
+    elif case == "gdn_null_dbeta":
+        p["dbeta"] = None
+    elif case == "gdn_dbeta_overlaps_beta":
+        p["dbeta"] = addr(4, 64)
+    elif case == "gdn_dbeta_overlaps_dg":
+        p["dbeta"] = addr(13, 2)
+    elif case == "gdn_z0_given":
+        p["z0"] = addr(8)
     assert call_bwd(lib, d, ws, wsb, **p) == expect, case
+
+
+def test_backward_gdn_accepts_beta(lib):
+    """The delta rule's backward takes beta and writes dbeta; with no sequences it enqueues
+    nothing, so the call returns LA_OK without a device."""
+    d = good("gdn", B=0)
+    p = bwd_args()
+    p["beta"], p["dbeta"] = addr(4), addr(15)
+    assert call_bwd(lib, d, **p) == bd.LA_OK
 
 
 def test_backward_workspace_query(lib):
@@ -424,6 +452,9 @@ def test_backward_workspace_query(lib):
     assert lib.la_prefill_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == bd.LA_OK
     assert n.value > 0
     d = good("gdn")
+    assert lib.la_prefill_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == bd.LA_OK
+    assert n.value > 0
+    d = good("kda")
     assert lib.la_prefill_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == \
         bd.LA_ERR_UNSUPPORTED
     d = good("gla", B=0)

@@ -1,4 +1,4 @@
-"""Parity of the prefill backward (GLA, SSD) against the fp64 oracle's reverse-mode
+"""Parity of the prefill backward (GLA, SSD, GDN) against the fp64 oracle's reverse-mode
 gradients (GPU)."""
 import numpy as np
 import pytest
@@ -17,6 +17,8 @@ def make_case(variant, B, H, N, dk, dv, io, seed, gate_kind="default", with_stat
     kw = dict(seed=seed, qk_scale=dk ** -0.5, gate_kind=gate_kind)
     if variant == "gla":
         kw["v_scale"] = dk ** -0.5
+    if variant == "gdn":
+        kw["l2norm_qk"] = True
     wl = W.Workload("b", variant, B, H, N, dk, dv, io, io, **kw)
     inp = W.make_inputs(wl, with_state=with_state)
     rng = np.random.default_rng(seed + 77)
@@ -29,17 +31,18 @@ def make_case(variant, B, H, N, dk, dv, io, seed, gate_kind="default", with_stat
 
 def run_both(variant, inp, dO, dO_x, dSf, dSf_x, seqs=None, threads=0):
     d = {k: dev(v) for k, v in inp.dev.items()}
-    dq, dk, dv, dg, dS0 = bd.prefill_backward(d["q"], d["k"], d["v"], d["g"], dev(dO),
-                                              variant=variant, S0=d.get("S0"),
-                                              dS_final=dev(dSf))
+    gr = bd.prefill_backward(d["q"], d["k"], d["v"], d["g"], dev(dO), variant=variant,
+                             beta=d.get("beta"), S0=d.get("S0"), dS_final=dev(dSf))
     torch.cuda.synchronize()
     e = inp.exact
     sel = (lambda a: a) if seqs is None else \
         (lambda a: None if a is None else a.reshape((-1,) + a.shape[2:])[seqs][None])
     ref = oracle.prefill_backward(variant, sel(e["q"]), sel(e["k"]), sel(e["v"]), sel(e["g"]),
-                                  None, sel(e.get("S0")), None, sel(dO_x), sel(dSf_x),
-                                  threads=threads)
-    got = {"dq": dq, "dk": dk, "dv": dv, "dg": dg, "dS0": dS0}
+                                  sel(e.get("beta")), sel(e.get("S0")), None, sel(dO_x),
+                                  sel(dSf_x), threads=threads)
+    got = {"dq": gr.dq, "dk": gr.dk, "dv": gr.dv, "dg": gr.dg, "dS0": gr.dS0}
+    if gr.dbeta is not None:
+        got["dbeta"] = gr.dbeta
     if seqs is not None:
         got = {k: v.reshape((-1,) + tuple(v.shape[2:]))[seqs][None] for k, v in got.items()}
     return got, ref
@@ -52,7 +55,7 @@ def check(got, ref, tol):
     return errs
 
 
-@pytest.mark.parametrize("variant", ["gla", "ssd"])
+@pytest.mark.parametrize("variant", ["gla", "ssd", "gdn"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (128, 128), (128, 64)])
 def test_backward_shapes(variant, io, dk, dv):
@@ -61,7 +64,7 @@ def test_backward_shapes(variant, io, dk, dv):
     check(*run_both(variant, *case), TOL[io])
 
 
-@pytest.mark.parametrize("variant", ["gla", "ssd"])
+@pytest.mark.parametrize("variant", ["gla", "ssd", "gdn"])
 @pytest.mark.parametrize("N", [1, 15, 16, 17, 70])
 def test_backward_lengths(variant, N):
     case = make_case(variant, 1, 3, N, 32, 16, "f32", seed=N, gate_kind="slow")
@@ -70,7 +73,8 @@ def test_backward_lengths(variant, N):
 
 
 @pytest.mark.parametrize("variant,kind", [("gla", "fast"), ("gla", "ones"), ("ssd", "fast"),
-                                          ("ssd", "ones")])
+                                          ("ssd", "ones"), ("gdn", "default"), ("gdn", "ones"),
+                                          ("gdn", "beta0"), ("gdn", "beta1")])
 def test_backward_gate_kinds(variant, kind):
     case = make_case(variant, 1, 2, 50, 64, 32, "f32", seed=9, gate_kind=kind)
     banner(f"backward {variant} gates={kind}")
@@ -83,15 +87,17 @@ def test_backward_without_state_or_final_gradient():
     check(*run_both("gla", *case), TOL["bf16"])
 
 
-def test_backward_empty_sequence():
+@pytest.mark.parametrize("variant", ["ssd", "gdn"])
+def test_backward_empty_sequence(variant):
     """N = 0: the initial state's gradient is the final state's."""
-    inp, dO, dO_x, dSf, dSf_x = make_case("ssd", 2, 3, 0, 32, 16, "f32", seed=3)
-    banner("backward N=0")
-    got, ref = run_both("ssd", inp, dO, dO_x, dSf, dSf_x)
+    inp, dO, dO_x, dSf, dSf_x = make_case(variant, 2, 3, 0, 32, 16, "f32", seed=3)
+    banner(f"backward {variant} N=0")
+    got, ref = run_both(variant, inp, dO, dO_x, dSf, dSf_x)
     assert torch.equal(got["dS0"].cpu(), torch.from_numpy(dSf))
 
 
-@pytest.mark.parametrize("name", ["gla_bf16_b2h8_n2048_d128", "ssd_bf16_b2h32_n4096_dk128_dv64"])
+@pytest.mark.parametrize("name", ["gla_bf16_b2h8_n2048_d128", "ssd_bf16_b2h32_n4096_dk128_dv64",
+                                  "gdn_bf16_b4h16_n8192_d128"])
 def test_backward_full_workload_sampled(name):
     """The full-size workload; the oracle checks sampled sequences one by one."""
     wl = W.WORKLOADS[name]
@@ -106,15 +112,16 @@ def test_backward_full_workload_sampled(name):
         print(name, s, errs, flush=True)
 
 
-def test_backward_tiny_gates():
+@pytest.mark.parametrize("variant", ["gla", "gdn"])
+def test_backward_tiny_gates(variant):
     """Gates down to 1e-7 (5% of them): the gate gradient is taken directly from the states,
     so tiny gates cost no accuracy (fp32 bound)."""
-    inp, dO, dO_x, dSf, dSf_x = make_case("gla", 1, 2, 60, 64, 32, "f32", seed=21)
+    inp, dO, dO_x, dSf, dSf_x = make_case(variant, 1, 2, 60, 64, 32, "f32", seed=21)
     rng = np.random.default_rng(22)
     g = np.where(rng.random(inp.exact["g"].shape) < 0.05, 1e-7, inp.exact["g"])
     inp.dev["g"], inp.exact["g"] = W.round_to(g, "f32")
-    banner("backward gla tiny gates")
-    check(*run_both("gla", inp, dO, dO_x, dSf, dSf_x), TOL["f32"])
+    banner(f"backward {variant} tiny gates")
+    check(*run_both(variant, inp, dO, dO_x, dSf, dSf_x), TOL["f32"])
 
 
 @pytest.mark.parametrize("N", [64, 200, 257])
@@ -129,5 +136,5 @@ def test_backward_ssd_matrix_cores_vs_valu(N):
     valu = bd.prefill_backward(d["q"], d["k"], d["v"], d["g"], dev(dO), variant="ssd",
                                S0=d.get("S0"), dS_final=dev(dSf), path="valu")
     torch.cuda.synchronize()
-    for name, t in zip(("dq", "dk", "dv", "dg", "dS0"), valu):
-        assert relerr(got[name], t.double().cpu().numpy()) <= TOL["bf16"], name
+    for name in ("dq", "dk", "dv", "dg", "dS0"):
+        assert relerr(got[name], getattr(valu, name).double().cpu().numpy()) <= TOL["bf16"], name
