@@ -363,8 +363,8 @@ def bench_selscan(name, steps, warmup, torch, bd, W, device, stream, graph=True)
 
 
 def bench_backward(name, steps, warmup, torch, bd, W, device, stream):
-    """Backward of the prefill (the default path: matrix cores for SSD, fp32 VALU for GLA
-    and GDN):
+    """Backward of the prefill (the default path: matrix cores for SSD, fp32 VALU for KATH,
+    GLA and GDN):
     tokens per second of the whole backward (every kernel of la_prefill_backward)."""
     import ctypes
     import numpy as np
@@ -384,13 +384,15 @@ def bench_backward(name, steps, warmup, torch, bd, W, device, stream):
         raise bd.LinAttnError(rc, "la_prefill_backward_workspace_size")
     ws = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=device)
     outs = [torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"]),
-            torch.empty_like(d["g"]),
+            torch.empty_like(d["g"]) if "g" in d else None,
             torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=device),
-            torch.empty_like(d["beta"]) if "beta" in d else None]
+            torch.empty_like(d["beta"]) if "beta" in d else None,
+            torch.empty((wl.B, wl.H, wl.dk), dtype=torch.float32, device=device)
+            if wl.variant == "kath" else None]
     P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
-    args = (P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d.get("beta")), None, None, P(dO),
-            None, None, P(outs[0]), P(outs[1]), P(outs[2]), P(outs[3]), P(outs[5]), P(outs[4]),
-            None, P(ws), int(n.value), ctypes.c_void_p(stream.cuda_stream))
+    args = (P(d["q"]), P(d["k"]), P(d["v"]), P(d.get("g")), P(d.get("beta")), None, None,
+            P(dO), None, None, P(outs[0]), P(outs[1]), P(outs[2]), P(outs[3]), P(outs[5]),
+            P(outs[4]), P(outs[6]), P(ws), int(n.value), ctypes.c_void_p(stream.cuda_stream))
     pd = ctypes.byref(desc)
 
     def fn(i):
@@ -524,7 +526,7 @@ def main():
             results[name] = bench_decode(name, 1000, 10, torch, bd, W, device, stream)
             torch.cuda.empty_cache()
         for name in ("gla_bf16_b2h8_n2048_d128", "ssd_bf16_b2h32_n4096_dk128_dv64",
-                     "gdn_bf16_b4h16_n8192_d128"):
+                     "gdn_bf16_b4h16_n8192_d128", "kath_bf16_b1h16_n32768_dk128_dv64"):
             results["backward_" + name] = bench_backward(name, max(5, args.steps // 80), 2,
                                                          torch, bd, W, device, stream)
             torch.cuda.empty_cache()

@@ -259,30 +259,39 @@ class BackwardGrads(NamedTuple):
     dg: object
     dbeta: object   # GDN only, else None
     dS0: object
+    dz0: object = None   # KATH only
 
 
-def prefill_backward(q, k, v, g, dO, *, variant: str, beta=None, S0=None, dS_final=None,
-                     dq=None, dk=None, dv=None, dg=None, dbeta=None, dS0=None,
-                     path: str = "auto", workspace=None, stream=None) -> BackwardGrads:
-    """Gradients of ``prefill`` through ``la_prefill_backward`` (GLA, SSD, GDN).
+def prefill_backward(q, k, v, g, dO, *, variant: str, beta=None, S0=None, z0=None,
+                     dS_final=None, dz_final=None, dq=None, dk=None, dv=None, dg=None,
+                     dbeta=None, dS0=None, dz0=None, eps: float = 1e-6, path: str = "auto",
+                     workspace=None, stream=None) -> BackwardGrads:
+    """Gradients of ``prefill`` through ``la_prefill_backward`` (KATH, GLA, SSD, GDN).
 
-    q, k, v, g, beta (GDN), S0 as given to ``prefill``; dO [B,H,N,dv] (q's dtype);
-    dS_final [B,H,dk,dv] float32 or None. Returns BackwardGrads(dq, dk, dv, dg, dbeta, dS0).
+    q, k, v, g (None for KATH), beta (GDN), S0, z0 (KATH) as given to ``prefill``; dO
+    [B,H,N,dv] (q's dtype); dS_final [B,H,dk,dv] and dz_final [B,H,dk] float32 or None.
+    Returns BackwardGrads(dq, dk, dv, dg, dbeta, dS0, dz0).
     """
     import torch
     lib = load()
     B, H, N, dk_ = q.shape
     dv_ = v.shape[-1]
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("dO", dO),
-                    ("S0", S0), ("dS_final", dS_final), ("dq", dq), ("dk", dk), ("dv", dv),
-                    ("dg", dg), ("dbeta", dbeta), ("dS0", dS0)):
+                    ("S0", S0), ("z0", z0), ("dS_final", dS_final), ("dz_final", dz_final),
+                    ("dq", dq), ("dk", dk), ("dv", dv), ("dg", dg), ("dbeta", dbeta),
+                    ("dS0", dS0), ("dz0", dz0)):
         _require_contig(name, t)
-    desc = make_desc(variant, B, H, N, dk_, dv_, _dtype_code(q), _dtype_code(g), 1e-6, path)
+    kath = variant == "kath"
+    desc = make_desc(variant, B, H, N, dk_, dv_, _dtype_code(q),
+                     _dtype_code(q if g is None else g), eps, path)
     dev = q.device
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    dg = torch.empty_like(g) if dg is None else dg
+    if g is not None and dg is None:
+        dg = torch.empty_like(g)
+    if kath and dz0 is None:
+        dz0 = torch.empty((B, H, dk_), dtype=torch.float32, device=dev)
     if beta is not None and dbeta is None:
         dbeta = torch.empty_like(beta)
     if dS0 is None:
@@ -295,12 +304,13 @@ def prefill_backward(q, k, v, g, dO, *, variant: str, beta=None, S0=None, dS_fin
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = lib.la_prefill_backward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                 _ptr(beta), _ptr(S0), None, _ptr(dO), _ptr(dS_final), None,
-                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dS0),
-                                 None, _ptr(workspace if ws_bytes else None), wsz,
+                                 _ptr(beta), _ptr(S0), _ptr(z0), _ptr(dO), _ptr(dS_final),
+                                 _ptr(dz_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                                 _ptr(dbeta), _ptr(dS0), _ptr(dz0),
+                                 _ptr(workspace if ws_bytes else None), wsz,
                                  _stream_handle(stream, dev))
     _check(rc, "la_prefill_backward")
-    return BackwardGrads(dq, dk, dv, dg, dbeta, dS0)
+    return BackwardGrads(dq, dk, dv, dg, dbeta, dS0, dz0)
 
 
 def selective_scan(dt, A, Bm, Cm, x, Dskip=None, dt_bias=None, *, dt_softplus: bool = True,

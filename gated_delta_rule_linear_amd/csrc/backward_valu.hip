@@ -30,6 +30,16 @@
 // (one thread per state element walks the chunks forward for S_in and backward for
 // dS_out, in place), grads (every chunk and value tile in parallel: dV, and partials of
 // dQ, dK and dg over the tile's columns), then the finishing sums of the partials.
+//
+// KATH (normalised ELU+1 attention, "Linear / RNN 路线" section 2.1) is the same machinery
+// with gate 1, phi(q) and phi(k) in place of q and k, and one more value column. With
+// num_t = S_t^T phi(q_t) and den_t = phi(q_t).z_t + eps, o_t = num_t / den_t gives dL/dnum_t
+// = do_t / den_t and dL/dden_t = -(do_t . o_t) / den_t; the normaliser z is a state column
+// whose value is 1 and whose output gradient is dL/dden, so the augmented state [S, z]
+// follows S_t = S_{t-1} + phi(k_t) [v_t, 1]^T and the GLA formulas with dO = [dnum, dden]
+// give dphi(q), dphi(k), dv, dS0 and dz0 at once. The forward is recomputed first (the fp32
+// prefill, which also hands back den_t) to form dnum and dden; the chain rule through phi
+// is phi'(x) = min(phi(x), 1).
 #include "common.hpp"
 #include "la_internal.h"
 
@@ -45,6 +55,9 @@ struct BwdArgs {
     const float *S0, *dSf;
     void *dq, *dk, *dv, *dg;
     float* dS0;
+    const float *dnum, *dden;   // KATH: dL/dnum [tokens][DV] and dL/dden [tokens] (fp32)
+    const float *z0, *dzf;      // KATH: initial normaliser and its final gradient, or null
+    float* dz0;                 // KATH
     float* Sst;      // [nseq][nchunks][DK][DV]: dS_c, then S_in (in place)
     float* dSt;      // [nseq][nchunks][DK][DV]: G_c, then dS_out (in place)
     float* ac;       // [nseq][nchunks][DK] (GLA) or [nseq][nchunks] (SSD): chunk decay
@@ -56,7 +69,13 @@ struct BwdArgs {
 };
 
 template <int VAR>
-constexpr bool scalar_gate() { return VAR == LA_SSD; }
+constexpr bool scalar_gate() { return VAR == LA_SSD || VAR == LA_KATH; }
+
+constexpr bool scalar_gate_rt(int variant) { return variant == LA_SSD || variant == LA_KATH; }
+
+// Columns of the carried state: d_v, plus one tile whose first column is KATH's normaliser.
+template <int VAR, int DV>
+constexpr int state_width() { return DV + (VAR == LA_KATH ? VT : 0); }
 
 // One chunk's operands in LDS: q, k, the gates and their cumulative base-2 logarithms,
 // and the value tile of v and dO. Rows past the end are zero with gate 1.
@@ -75,16 +94,23 @@ struct ChunkSmem {
     float v[C][VT], dO[C][VT];
 };
 
-template <int DK, int DV, bool SG>
+template <int VAR, int DK, int DV, bool SG>
 __device__ __forceinline__ void load_chunk(ChunkSmem<DK, SG>& sm, const BwdArgs& a, size_t tok0,
                                            int t0, int n, int c0) {
+    constexpr bool KA = VAR == LA_KATH;
     const int tid = threadIdx.x;
     const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
     for (int idx = tid; idx < C * DK; idx += NT) {
         const int r = idx / DK, i = idx % DK;
         const size_t e = (tok0 + t0 + r) * DK + i;
-        sm.q[r][i] = r < n ? load_elem(a.q, e, iob) : 0.f;
-        sm.k[r][i] = r < n ? load_elem(a.k, e, iob) : 0.f;
+        float qv = r < n ? load_elem(a.q, e, iob) : 0.f;
+        float kv = r < n ? load_elem(a.k, e, iob) : 0.f;
+        if (KA && r < n) {
+            qv = elu_plus_one(qv);
+            kv = elu_plus_one(kv);
+        }
+        sm.q[r][i] = qv;
+        sm.k[r][i] = kv;
         if (!SG) {
             const float gv = r < n ? load_elem(a.g, e, gb) : 1.f;
             sm.gt[r][i] = gv;
@@ -92,15 +118,28 @@ __device__ __forceinline__ void load_chunk(ChunkSmem<DK, SG>& sm, const BwdArgs&
         }
     }
     if (SG && tid < C) {
-        const float gv = tid < n ? load_elem(a.g, tok0 + t0 + tid, gb) : 1.f;
+        const float gv = (tid < n && !KA) ? load_elem(a.g, tok0 + t0 + tid, gb) : 1.f;
         sm.sgt[tid] = gv;
         sm.sc[tid] = __builtin_amdgcn_logf(gv);
     }
     {
         const int r = tid / VT, c = tid % VT;
-        const size_t e = (tok0 + t0 + r) * DV + c0 + c;
-        sm.v[r][c] = r < n ? load_elem(a.v, e, iob) : 0.f;
-        sm.dO[r][c] = r < n ? load_elem(a.dO, e, iob) : 0.f;
+        const size_t tk = tok0 + t0 + r, e = tk * DV + c0 + c;
+        float vv = 0.f, dd = 0.f;
+        if (r < n) {
+            if (!KA) {
+                vv = load_elem(a.v, e, iob);
+                dd = load_elem(a.dO, e, iob);
+            } else if (c0 < DV) {
+                vv = load_elem(a.v, e, iob);
+                dd = a.dnum[e];
+            } else if (c == 0) {   // the normaliser column
+                vv = 1.f;
+                dd = a.dden[tk];
+            }
+        }
+        sm.v[r][c] = vv;
+        sm.dO[r][c] = dd;
     }
     __syncthreads();
     if (!SG) {
@@ -148,14 +187,15 @@ __device__ __forceinline__ ChunkUnit chunk_unit(const BwdArgs& a) {
 template <int VAR, int DK, int DV>
 __global__ __launch_bounds__(NT) void bwd_sums_kernel(BwdArgs a) {
     constexpr bool SG = scalar_gate<VAR>();
+    constexpr int SW = state_width<VAR, DV>();
     __shared__ ChunkSmem<DK, SG> sm;
     const ChunkUnit u = chunk_unit(a);
     const int c0 = u.tile * VT, t0 = u.ch * C, n = min(C, a.N - t0);
     const size_t tok0 = u.seq * size_t(a.N);
-    load_chunk<DK, DV, SG>(sm, a, tok0, t0, n, c0);
+    load_chunk<VAR, DK, DV, SG>(sm, a, tok0, t0, n, c0);
     auto EQ = [&](int r, int i) { return SG ? sm.seq[r] : sm.eq[r][i]; };
     auto EK = [&](int r, int i) { return SG ? sm.sek[r] : sm.ek[r][i]; };
-    const size_t sbase = (u.seq * a.nchunks + u.ch) * size_t(DK) * DV;
+    const size_t sbase = (u.seq * a.nchunks + u.ch) * size_t(DK) * SW;
     for (int idx = threadIdx.x; idx < DK * VT; idx += NT) {
         const int i = idx / VT, c = idx % VT;
         float ds = 0.f, gq = 0.f;
@@ -163,8 +203,8 @@ __global__ __launch_bounds__(NT) void bwd_sums_kernel(BwdArgs a) {
             ds += EK(s_, i) * sm.k[s_][i] * sm.v[s_][c];
             gq += EQ(s_, i) * sm.q[s_][i] * sm.dO[s_][c];
         }
-        a.Sst[sbase + size_t(i) * DV + c0 + c] = ds;
-        a.dSt[sbase + size_t(i) * DV + c0 + c] = gq;
+        a.Sst[sbase + size_t(i) * SW + c0 + c] = ds;
+        a.dSt[sbase + size_t(i) * SW + c0 + c] = gq;
     }
     if (u.tile == 0) {
         float* ac = a.ac + (u.seq * a.nchunks + u.ch) * (SG ? 1 : DK);
@@ -181,33 +221,44 @@ __global__ __launch_bounds__(NT) void bwd_sums_kernel(BwdArgs a) {
 template <int VAR, int DK, int DV>
 __global__ __launch_bounds__(NT) void bwd_scans_kernel(BwdArgs a) {
     constexpr bool SG = scalar_gate<VAR>();
+    constexpr int SW = state_width<VAR, DV>();
     const size_t e = size_t(blockIdx.x) * NT + threadIdx.x;
-    if (e >= size_t(a.nseq) * DK * DV) return;
-    const size_t seq = e / (size_t(DK) * DV), ij = e % (size_t(DK) * DV);
-    const int i = int(ij / DV);
-    const size_t stride = size_t(DK) * DV;
+    if (e >= size_t(a.nseq) * DK * SW) return;
+    const size_t seq = e / (size_t(DK) * SW), ij = e % (size_t(DK) * SW);
+    const int i = int(ij / SW), col = int(ij % SW);
+    const size_t stride = size_t(DK) * SW;
+    const size_t es = (seq * DK + i) * DV + col;   // the [B,H,dk,dv] element (col < DV)
+    const size_t ez = seq * DK + i;                // the [B,H,dk] element (col == DV)
     float* Ss = a.Sst + seq * a.nchunks * stride + ij;
     float* dSs = a.dSt + seq * a.nchunks * stride + ij;
     const float* ac = a.ac + seq * a.nchunks * (SG ? 1 : DK) + (SG ? 0 : i);
-    float S = a.S0 ? a.S0[e] : 0.f;
+    float S = 0.f, dS = 0.f;
+    if (col < DV) {
+        if (a.S0) S = a.S0[es];
+        if (a.dSf) dS = a.dSf[es];
+    } else if (col == DV) {
+        if (a.z0) S = a.z0[ez];
+        if (a.dzf) dS = a.dzf[ez];
+    }
     for (int ch = 0; ch < a.nchunks; ++ch) {
         const float d = Ss[ch * stride];
         Ss[ch * stride] = S;
         S = ac[ch * (SG ? 1 : DK)] * S + d;
     }
-    float dS = a.dSf ? a.dSf[e] : 0.f;
     for (int ch = a.nchunks - 1; ch >= 0; --ch) {
         const float gq = dSs[ch * stride];
         dSs[ch * stride] = dS;
         dS = ac[ch * (SG ? 1 : DK)] * dS + gq;
     }
-    a.dS0[e] = dS;
+    if (col < DV) a.dS0[es] = dS;
+    else if (col == DV) a.dz0[ez] = dS;
 }
 
 // ---------------------------------------------------------------------------- grads
 template <int VAR, int DK, int DV>
 __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
     constexpr bool SG = scalar_gate<VAR>();
+    constexpr int SW = state_width<VAR, DV>();
     __shared__ ChunkSmem<DK, SG> sm;
     // rows padded to VT + 1 floats: the dQ / dK step reads a column down consecutive rows
     __shared__ float sdS[DK][VT + 1];    // gradient of the state leaving the chunk
@@ -218,13 +269,13 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
     const int c0 = u.tile * VT, t0 = u.ch * C, n = min(C, a.N - t0);
     const bool iob = a.io_bf16 != 0;
     const size_t tok0 = u.seq * size_t(a.N);
-    const size_t sbase = (u.seq * a.nchunks + u.ch) * size_t(DK) * DV;
+    const size_t sbase = (u.seq * a.nchunks + u.ch) * size_t(DK) * SW;
     for (int idx = tid; idx < DK * VT; idx += NT) {
         const int i = idx / VT, c = idx % VT;
-        sSin[i][c] = a.Sst[sbase + size_t(i) * DV + c0 + c];
-        sdS[i][c] = a.dSt[sbase + size_t(i) * DV + c0 + c];
+        sSin[i][c] = a.Sst[sbase + size_t(i) * SW + c0 + c];
+        sdS[i][c] = a.dSt[sbase + size_t(i) * SW + c0 + c];
     }
-    load_chunk<DK, DV, SG>(sm, a, tok0, t0, n, c0);   // ends with a barrier
+    load_chunk<VAR, DK, DV, SG>(sm, a, tok0, t0, n, c0);   // ends with a barrier
     float* dqp = a.dqp + size_t(u.tile) * a.nseq * a.N * DK;
     float* dkp = a.dkp + size_t(u.tile) * a.nseq * a.N * DK;
     float* dgp = a.dgp + size_t(u.tile) * a.nseq * a.N * DK;
@@ -260,7 +311,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
         float acc = 0.f;
         for (int r = s; r < C; ++r) acc += sP[r][s] * sm.dO[r][c];
         for (int i = 0; i < DK; ++i) acc += sm.k[s][i] * EK(s, i) * sdS[i][c];
-        if (s < n) store_elem(a.dv, (tok0 + t0 + s) * DV + c0 + c, acc, iob);
+        if (s < n && c0 < DV) store_elem(a.dv, (tok0 + t0 + s) * DV + c0 + c, acc, iob);
     }
     // partial dQ and dK over this tile's columns
     for (int idx = tid; idx < C * DK; idx += NT) {
@@ -281,7 +332,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
     // partial dg: thread (row group rg, column c) owns elements (rg + 16 m, c); for each
     // it rebuilds S_{s-1} forward and dS_s backward over the chunk, and the products are
     // summed over the 16 column lanes (consecutive lanes) with DPP
-    {
+    if constexpr (VAR != LA_KATH) {
         const int c = tid % VT, rg = tid / VT;
 #pragma unroll 1
         for (int m = 0; m < DK / 16; ++m) {
@@ -328,7 +379,19 @@ __global__ __launch_bounds__(NT) void bwd_sum_kernel(BwdArgs a) {
     const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
     const size_t ntok = size_t(a.nseq) * a.N;
     const size_t stride = ntok * DK;
-    if constexpr (!SG) {
+    if constexpr (VAR == LA_KATH) {   // through phi: phi'(x) = min(phi(x), 1)
+        const size_t e = size_t(blockIdx.x) * NT + threadIdx.x;
+        if (e >= stride) return;
+        float dq = 0.f, dk = 0.f;
+        for (int t = 0; t < a.ntiles; ++t) {
+            dq += a.dqp[t * stride + e];
+            dk += a.dkp[t * stride + e];
+        }
+        dq *= fminf(elu_plus_one(load_elem(a.q, e, iob)), 1.f);
+        dk *= fminf(elu_plus_one(load_elem(a.k, e, iob)), 1.f);
+        store_elem(a.dq, e, dq, iob);
+        store_elem(a.dk, e, dk, iob);
+    } else if constexpr (!SG) {
         const size_t e = size_t(blockIdx.x) * NT + threadIdx.x;
         if (e >= stride) return;
         float dq = 0.f, dk = 0.f, dg = 0.f;
@@ -361,39 +424,89 @@ __global__ __launch_bounds__(NT) void bwd_sum_kernel(BwdArgs a) {
     }
 }
 
+// KATH: dnum = dO / den and dden = -(dO . o) / den per token, one wave per token
+template <int DV>
+__global__ __launch_bounds__(NT) void kath_pre_kernel(BwdArgs a, const void* o, const float* den,
+                                                      float* dnum, float* dden, size_t ntok) {
+    const size_t tok = size_t(blockIdx.x) * (NT / kWave) + threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    if (tok >= ntok) return;   // a whole wave leaves together
+    const bool iob = a.io_bf16 != 0;
+    const float dn = den[tok];
+    float w = 0.f;
+    for (int j = lane; j < DV; j += kWave) {
+        const size_t e = tok * DV + j;
+        const float d = load_elem(a.dO, e, iob);
+        w += d * load_elem(o, e, iob);
+        dnum[e] = d / dn;
+    }
+    w = wave_sum(w);
+    if (lane == 0) dden[tok] = -w / dn;
+}
+
 struct BwdLayout {
-    size_t Sst, dSt, ac, dqp, dkp, dgp, total;
+    size_t Sst, dSt, ac, dqp, dkp, dgp;
+    size_t o, den, Sf, zf, dnum, dden;   // KATH only
+    size_t total;
 };
 BwdLayout bwd_layout(const Problem& p) {
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
-    const size_t nseq = size_t(p.B) * p.H, ntiles = size_t(p.dv / VT);
+    const bool ka = p.variant == LA_KATH;
+    const size_t sw = size_t(p.dv) + (ka ? VT : 0);
+    const size_t nseq = size_t(p.B) * p.H, ntiles = sw / VT;
     const size_t nchunks = size_t((p.N + C - 1) / C), ntok = nseq * size_t(p.N);
     BwdLayout L{};
     size_t off = 0;
-    L.Sst = off; off += al(nseq * nchunks * p.dk * p.dv * 4);
-    L.dSt = off; off += al(nseq * nchunks * p.dk * p.dv * 4);
-    L.ac = off; off += al(nseq * nchunks * (p.variant == LA_SSD ? 1 : p.dk) * 4);
+    L.Sst = off; off += al(nseq * nchunks * p.dk * sw * 4);
+    L.dSt = off; off += al(nseq * nchunks * p.dk * sw * 4);
+    L.ac = off; off += al(nseq * nchunks * (scalar_gate_rt(p.variant) ? 1 : p.dk) * 4);
     L.dqp = off; off += al(ntiles * ntok * p.dk * 4);
     L.dkp = off; off += al(ntiles * ntok * p.dk * 4);
-    L.dgp = off; off += al(ntiles * ntok * p.dk * 4);
+    L.dgp = off; off += ka ? 0 : al(ntiles * ntok * p.dk * 4);
+    if (ka) {
+        L.o = off; off += al(ntok * p.dv * 4);
+        L.den = off; off += al(ntok * 4);
+        L.Sf = off; off += al(nseq * p.dk * p.dv * 4);
+        L.zf = off; off += al(nseq * p.dk * 4);
+        L.dnum = off; off += al(ntok * p.dv * 4);
+        L.dden = off; off += al(ntok * 4);
+    }
     L.total = off;
     return L;
 }
 
 template <int VAR, int DK, int DV>
 hipError_t launch_dims(const Problem& p, BwdArgs a) {
+    constexpr int SW = state_width<VAR, DV>();
+    const size_t ntok = size_t(a.nseq) * a.N;
+    hipError_t e;
+    if constexpr (VAR == LA_KATH) {
+        // recompute the forward for o and the denominators, then dnum and dden
+        const BwdLayout L = bwd_layout(p);
+        unsigned char* ws = static_cast<unsigned char*>(p.ws);
+        Problem f = p;
+        f.o = ws + L.o;
+        f.S = reinterpret_cast<float*>(ws + L.Sf);
+        f.z = reinterpret_cast<float*>(ws + L.zf);
+        f.den = reinterpret_cast<float*>(ws + L.den);
+        f.path = LA_PATH_VALU;
+        if ((e = launch_prefill_valu(f)) != hipSuccess) return e;
+        const size_t blocks = (ntok + NT / kWave - 1) / (NT / kWave);
+        kath_pre_kernel<DV><<<dim3(unsigned(blocks)), dim3(NT), 0, p.stream>>>(
+            a, f.o, f.den, const_cast<float*>(a.dnum), const_cast<float*>(a.dden), ntok);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const unsigned units = unsigned(size_t(a.nseq) * a.nchunks * a.ntiles);
     bwd_sums_kernel<VAR, DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const size_t nel = size_t(a.nseq) * DK * DV;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t nel = size_t(a.nseq) * DK * SW;
     bwd_scans_kernel<VAR, DK, DV><<<dim3(unsigned((nel + NT - 1) / NT)), dim3(NT), 0, p.stream>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     bwd_grads_kernel<VAR, DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const size_t ntok = size_t(a.nseq) * a.N;
-    const size_t sblocks = scalar_gate<VAR>() ? (ntok + NT / kWave - 1) / (NT / kWave)
-                                              : (ntok * DK + NT - 1) / NT;
+    const size_t sblocks = (scalar_gate<VAR>() && VAR != LA_KATH)
+                               ? (ntok + NT / kWave - 1) / (NT / kWave)
+                               : (ntok * DK + NT - 1) / NT;
     bwd_sum_kernel<VAR, DK><<<dim3(unsigned(sblocks)), dim3(NT), 0, p.stream>>>(a);
     return hipGetLastError();
 }
@@ -420,16 +533,18 @@ hipError_t dispatch_dk(const Problem& p, const BwdArgs& a) {
     return hipErrorInvalidValue;
 }
 
-// N = 0: the gradient of the initial state is the final-state gradient itself
-__global__ void bwd_copy_kernel(const float* dSf, float* dS0, size_t n) {
+// N = 0: the gradients of the initial state (and normaliser) are the final ones
+__global__ void bwd_copy_kernel(const float* dSf, float* dS0, size_t n, const float* dzf,
+                                float* dz0, size_t nz) {
     const size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i < n) dS0[i] = dSf ? dSf[i] : 0.f;
+    if (dz0 && i < nz) dz0[i] = dzf ? dzf[i] : 0.f;
 }
 
 }  // namespace
 
 bool backward_supported(int variant) {
-    return variant == LA_GLA || variant == LA_SSD || variant == LA_GDN;
+    return variant == LA_GLA || variant == LA_SSD || variant == LA_GDN || variant == LA_KATH;
 }
 
 size_t backward_workspace_bytes(const Problem& p) {
@@ -442,16 +557,19 @@ hipError_t launch_backward(const BwdProblem& bp) {
     const Problem& p = bp.p;
     if (p.N == 0) {
         const size_t n = size_t(p.B) * p.H * p.dk * p.dv;
+        const size_t nz = p.variant == LA_KATH ? size_t(p.B) * p.H * p.dk : 0;
         const size_t blocks = (n + 255) / 256;
         if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
-        bwd_copy_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, p.stream>>>(bp.dS_final, bp.dS0, n);
+        bwd_copy_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, p.stream>>>(
+            bp.dS_final, bp.dS0, n, bp.dz_final, p.variant == LA_KATH ? bp.dz0 : nullptr, nz);
         return hipGetLastError();
     }
     if (p.variant == LA_GDN) return launch_backward_gdn(bp);
+    const bool ka = p.variant == LA_KATH;
     const size_t nseq = size_t(p.B) * p.H;
     const size_t nchunks = size_t((p.N + C - 1) / C);
-    if (nseq * nchunks * size_t(p.dv / VT) > 0x7fffffffull ||
-        nseq * size_t(p.dk) * p.dv / NT > 0x7fffffffull ||
+    const size_t sw = size_t(p.dv) + (ka ? VT : 0);
+    if (nseq * nchunks * (sw / VT) > 0x7fffffffull || nseq * size_t(p.dk) * sw / NT > 0x7fffffffull ||
         nseq * size_t(p.N) * p.dk / NT > 0x7fffffffull)
         return hipErrorInvalidValue;
     const BwdLayout L = bwd_layout(p);
@@ -465,16 +583,24 @@ hipError_t launch_backward(const BwdProblem& bp) {
     a.ac = reinterpret_cast<float*>(ws + L.ac);
     a.dqp = reinterpret_cast<float*>(ws + L.dqp);
     a.dkp = reinterpret_cast<float*>(ws + L.dkp);
-    a.dgp = reinterpret_cast<float*>(ws + L.dgp);
+    a.dgp = ka ? nullptr : reinterpret_cast<float*>(ws + L.dgp);
+    if (ka) {
+        a.dnum = reinterpret_cast<const float*>(ws + L.dnum);
+        a.dden = reinterpret_cast<const float*>(ws + L.dden);
+        a.z0 = p.z0;
+        a.dzf = bp.dz_final;
+        a.dz0 = bp.dz0;
+    }
     a.N = p.N;
     a.nseq = int(nseq);
-    a.ntiles = p.dv / VT;
+    a.ntiles = int(sw / VT);
     a.nchunks = (p.N + C - 1) / C;
     a.io_bf16 = p.io_bf16;
     a.gate_bf16 = p.gate_bf16;
     switch (p.variant) {
         case LA_GLA: return dispatch_dk<LA_GLA>(p, a);
         case LA_SSD: return dispatch_dk<LA_SSD>(p, a);
+        case LA_KATH: return dispatch_dk<LA_KATH>(p, a);
     }
     return hipErrorInvalidValue;
 }

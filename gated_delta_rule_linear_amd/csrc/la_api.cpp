@@ -367,6 +367,7 @@ static int check_backward_desc(const la_desc* d, la::Problem& p) {
     p.variant = d->variant;
     p.io_bf16 = d->io_dtype == LA_BF16;
     p.gate_bf16 = d->gate_dtype == LA_BF16;
+    p.eps = d->eps;
     const bool mfma_ok = la::ssd_backward_mfma_supported(p);
     if (d->path == LA_PATH_MFMA && !mfma_ok) return LA_ERR_UNSUPPORTED;
     p.path = (d->path != LA_PATH_VALU && mfma_ok) ? LA_PATH_MFMA : LA_PATH_VALU;
@@ -397,18 +398,20 @@ int la_prefill_backward(const la_desc* d, const void* q, const void* k, const vo
     la::Problem p;
     int rc = check_backward_desc(d, p);
     if (rc != LA_OK) return rc;
-    // no variant built here has a normaliser; only GDN (the delta rule) takes beta
-    const bool delta = d->variant == LA_GDN;
-    if (z0 || dz_final || dz0) return LA_ERR_INVALID;
+    // GDN (the delta rule) takes beta; KATH has no gate and carries the normaliser z
+    const bool delta = d->variant == LA_GDN, kath = d->variant == LA_KATH;
+    if (!kath && (z0 || dz_final || dz0)) return LA_ERR_INVALID;
+    if (kath && (g || dg)) return LA_ERR_INVALID;
     if (!delta && (beta || dbeta)) return LA_ERR_INVALID;
     const bool seqs = (uint64_t(d->B) * uint64_t(d->H)) > 0;
     const bool tokens = seqs && d->N > 0;
-    if (seqs && !dS0) return LA_ERR_INVALID;
-    if (tokens && (!q || !k || !v || !g || !dO || !dq || !dk || !dv || !dg)) return LA_ERR_INVALID;
+    if (seqs && (!dS0 || (kath && !dz0))) return LA_ERR_INVALID;
+    if (tokens && (!q || !k || !v || !dO || !dq || !dk || !dv)) return LA_ERR_INVALID;
+    if (tokens && !kath && (!g || !dg)) return LA_ERR_INVALID;
     if (tokens && delta && (!beta || !dbeta)) return LA_ERR_INVALID;
     // alignment: dq, dk as q; dv, dO as v; dg as g; dbeta as beta; the fp32 states 16 bytes
-    if (!check_alignment(*d, q, k, v, g, beta, S0, nullptr, dv, dS0, nullptr) ||
-        !check_alignment(*d, dq, dk, dO, dg, dbeta, dS_final, nullptr, nullptr, nullptr, nullptr))
+    if (!check_alignment(*d, q, k, v, g, beta, S0, z0, dv, dS0, dz0) ||
+        !check_alignment(*d, dq, dk, dO, dg, dbeta, dS_final, dz_final, nullptr, nullptr, nullptr))
         return LA_ERR_INVALID;
     const Sizes s = sizes_of(*d);
     const uint64_t tk = tokens ? 1 : 0;
@@ -417,13 +420,15 @@ int la_prefill_backward(const la_desc* d, const void* q, const void* k, const vo
                 rdSf = range(dS_final, s.S), rdq = range(dq, s.q * tk), rdk = range(dk, s.k * tk),
                 rdv = range(dv, s.v * tk), rdg = range(dg, s.g * tk),
                 rdS0 = range(dS0, s.S), rb = range(beta, s.beta * tk),
-                rdb = range(dbeta, s.beta * tk);
+                rdb = range(dbeta, s.beta * tk), rz0 = range(z0, s.z),
+                rdzf = range(dz_final, s.z), rdz0 = range(dz0, s.z);
     // outputs overlap nothing: not the inputs, not each other
-    const Range outs[] = {rdq, rdk, rdv, rdg, rdS0, rdb};
-    const Range all[] = {rq, rk, rv, rg, rS0, rdO, rdSf, rb, rdq, rdk, rdv, rdg, rdS0, rdb};
-    for (int a = 0; a < 6; ++a)
+    const Range outs[] = {rdq, rdk, rdv, rdg, rdS0, rdb, rdz0};
+    const Range all[] = {rq,  rk,  rv,  rg,  rS0,  rdO, rdSf, rb, rz0,
+                         rdzf, rdq, rdk, rdv, rdg, rdS0, rdb, rdz0};
+    for (int a = 0; a < 7; ++a)
         for (const Range& x : all)
-            if (&x != &all[8 + a] && overlap(outs[a], x)) return LA_ERR_INVALID;
+            if (&x != &all[10 + a] && overlap(outs[a], x)) return LA_ERR_INVALID;
     const size_t need = backward_workspace(p);
     if (need > 0) {
         if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return LA_ERR_WORKSPACE;
@@ -432,13 +437,14 @@ int la_prefill_backward(const la_desc* d, const void* q, const void* k, const vo
             if (overlap(rw, x)) return LA_ERR_INVALID;
     }
     if (!seqs) return LA_OK;
-    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.S0 = S0;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.S0 = S0; p.z0 = z0;
     p.ws = workspace; p.ws_bytes = workspace_bytes;
     p.stream = static_cast<hipStream_t>(stream);
     la::BwdProblem bp;
     bp.p = p;
     bp.dO = dO; bp.dS_final = dS_final;
     bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dbeta = dbeta; bp.dS0 = dS0;
+    bp.dz_final = dz_final; bp.dz0 = dz0;
     (void)hipGetLastError();
     hipError_t err = (p.path == LA_PATH_MFMA && p.N > 0) ? la::launch_backward_ssd_mfma(bp)
                                                          : la::launch_backward(bp);

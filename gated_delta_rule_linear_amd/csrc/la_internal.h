@@ -33,6 +33,7 @@ struct Problem {
     void* ws = nullptr;
     size_t ws_bytes = 0;
     hipStream_t stream = nullptr;
+    float* den = nullptr;     // KATH, fp32 prefill only: per-token denominators, or null
 };
 
 constexpr int kValuChunk = 16;
@@ -72,6 +73,8 @@ struct BwdProblem {
     void *dq = nullptr, *dk = nullptr, *dv = nullptr, *dg = nullptr;
     void* dbeta = nullptr;           // GDN: dL/dbeta [B,H,N] gate dtype
     float* dS0 = nullptr;
+    const float* dz_final = nullptr; // KATH: dL/dz_final [B,H,dk] or null (zero)
+    float* dz0 = nullptr;            // KATH: dL/dz0 [B,H,dk]
 };
 bool backward_supported(int variant);
 size_t backward_workspace_bytes(const Problem& p);

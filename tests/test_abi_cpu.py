@@ -376,7 +376,10 @@ def call_bwd(lib, desc, ws=None, ws_bytes=0, **p):
 @pytest.mark.parametrize("case,expect", [
     ("null_desc", bd.LA_ERR_INVALID),
     ("kda_unsupported", bd.LA_ERR_UNSUPPORTED),
-    ("kath_unsupported", bd.LA_ERR_UNSUPPORTED),
+    ("kath_g_given", bd.LA_ERR_INVALID),
+    ("kath_null_dz0", bd.LA_ERR_INVALID),
+    ("kath_dz0_overlaps_z0", bd.LA_ERR_INVALID),
+    ("gla_z0_given", bd.LA_ERR_INVALID),
     ("gdn_null_beta", bd.LA_ERR_INVALID),
     ("gdn_null_dbeta", bd.LA_ERR_INVALID),
     ("gdn_dbeta_overlaps_beta", bd.LA_ERR_INVALID),
@@ -394,13 +397,18 @@ def call_bwd(lib, desc, ws=None, ws_bytes=0, **p):
     ("no_workspace", bd.LA_ERR_WORKSPACE),
 ])
 def test_backward_rejects(lib, case, expect):
-    variant = {"kda_unsupported": "kda", "kath_unsupported": "kath"}.get(case, "gla")
+    variant = {"kda_unsupported": "kda"}.get(case, "gla")
     if case.startswith("gdn_"):
         variant = "gdn"
+    if case.startswith("kath_"):
+        variant = "kath"
     d = good(variant)
     p = bwd_args()
     if variant == "gdn":
         p["beta"], p["dbeta"] = addr(4), addr(15)
+    if variant == "kath":
+        p["g"], p["dg"] = None, None
+        p["z0"], p["dz0"] = addr(8), addr(16)
     ws, wsb = addr(20), 1 << 32
     if case == "null_desc":
         d = None
@@ -434,6 +442,14 @@ def test_backward_rejects(lib, case, expect):
         p["dbeta"] = addr(13, 2)
     elif case == "gdn_z0_given":
         p["z0"] = addr(8)
+    elif case == "kath_g_given":
+        p["g"] = addr(3)
+    elif case == "kath_null_dz0":
+        p["dz0"] = None
+    elif case == "kath_dz0_overlaps_z0":
+        p["dz0"] = addr(8, 64)
+    elif case == "gla_z0_given":
+        p["z0"] = addr(8)
     assert call_bwd(lib, d, ws, wsb, **p) == expect, case
 
 
@@ -443,6 +459,10 @@ def test_backward_gdn_accepts_beta(lib):
     d = good("gdn", B=0)
     p = bwd_args()
     p["beta"], p["dbeta"] = addr(4), addr(15)
+    assert call_bwd(lib, d, **p) == bd.LA_OK
+    d = good("kath", B=0)
+    p = bwd_args()
+    p["g"], p["dg"], p["dz0"] = None, None, addr(16)
     assert call_bwd(lib, d, **p) == bd.LA_OK
 
 

@@ -1,5 +1,5 @@
-"""Parity of the prefill backward (GLA, SSD, GDN) against the fp64 oracle's reverse-mode
-gradients (GPU)."""
+"""Parity of the prefill backward (KATH, GLA, SSD, GDN) against the fp64 oracle's
+reverse-mode gradients (GPU)."""
 import numpy as np
 import pytest
 import torch
@@ -26,23 +26,34 @@ def make_case(variant, B, H, N, dk, dv, io, seed, gate_kind="default", with_stat
     dSf = dSf_x = None
     if with_dsf:
         dSf, dSf_x = W.round_to(rng.standard_normal((B, H, dk, dv)) * 0.1, "f32")
+        if variant == "kath":   # the normaliser's final gradient rides along with dS_final
+            dzf, dzf_x = W.round_to(rng.standard_normal((B, H, dk)) * 0.01, "f32")
+            dSf, dSf_x = (dSf, dzf), (dSf_x, dzf_x)
     return inp, dO, dO_x, dSf, dSf_x
 
 
-def run_both(variant, inp, dO, dO_x, dSf, dSf_x, seqs=None, threads=0):
+def run_both(variant, inp, dO, dO_x, dSf, dSf_x, seqs=None, threads=0, eps=1e-6):
     d = {k: dev(v) for k, v in inp.dev.items()}
-    gr = bd.prefill_backward(d["q"], d["k"], d["v"], d["g"], dev(dO), variant=variant,
-                             beta=d.get("beta"), S0=d.get("S0"), dS_final=dev(dSf))
+    dSf, dzf = dSf if isinstance(dSf, tuple) else (dSf, None)
+    dSf_x, dzf_x = dSf_x if isinstance(dSf_x, tuple) else (dSf_x, None)
+    gr = bd.prefill_backward(d["q"], d["k"], d["v"], d.get("g"), dev(dO), variant=variant,
+                             beta=d.get("beta"), S0=d.get("S0"), z0=d.get("z0"),
+                             dS_final=dev(dSf), dz_final=dev(dzf), eps=eps)
     torch.cuda.synchronize()
     e = inp.exact
     sel = (lambda a: a) if seqs is None else \
         (lambda a: None if a is None else a.reshape((-1,) + a.shape[2:])[seqs][None])
-    ref = oracle.prefill_backward(variant, sel(e["q"]), sel(e["k"]), sel(e["v"]), sel(e["g"]),
-                                  sel(e.get("beta")), sel(e.get("S0")), None, sel(dO_x),
-                                  sel(dSf_x), threads=threads)
-    got = {"dq": gr.dq, "dk": gr.dk, "dv": gr.dv, "dg": gr.dg, "dS0": gr.dS0}
+    ref = oracle.prefill_backward(variant, sel(e["q"]), sel(e["k"]), sel(e["v"]),
+                                  sel(e.get("g")), sel(e.get("beta")), sel(e.get("S0")),
+                                  sel(e.get("z0")), sel(dO_x), sel(dSf_x), sel(dzf_x), eps=eps,
+                                  threads=threads)
+    got = {"dq": gr.dq, "dk": gr.dk, "dv": gr.dv, "dS0": gr.dS0}
+    if gr.dg is not None:
+        got["dg"] = gr.dg
     if gr.dbeta is not None:
         got["dbeta"] = gr.dbeta
+    if gr.dz0 is not None:
+        got["dz0"] = gr.dz0
     if seqs is not None:
         got = {k: v.reshape((-1,) + tuple(v.shape[2:]))[seqs][None] for k, v in got.items()}
     return got, ref
@@ -55,7 +66,7 @@ def check(got, ref, tol):
     return errs
 
 
-@pytest.mark.parametrize("variant", ["gla", "ssd", "gdn"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "ssd", "gdn"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (128, 128), (128, 64)])
 def test_backward_shapes(variant, io, dk, dv):
@@ -64,7 +75,7 @@ def test_backward_shapes(variant, io, dk, dv):
     check(*run_both(variant, *case), TOL[io])
 
 
-@pytest.mark.parametrize("variant", ["gla", "ssd", "gdn"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "ssd", "gdn"])
 @pytest.mark.parametrize("N", [1, 15, 16, 17, 70])
 def test_backward_lengths(variant, N):
     case = make_case(variant, 1, 3, N, 32, 16, "f32", seed=N, gate_kind="slow")
@@ -87,17 +98,21 @@ def test_backward_without_state_or_final_gradient():
     check(*run_both("gla", *case), TOL["bf16"])
 
 
-@pytest.mark.parametrize("variant", ["ssd", "gdn"])
+@pytest.mark.parametrize("variant", ["ssd", "gdn", "kath"])
 def test_backward_empty_sequence(variant):
     """N = 0: the initial state's gradient is the final state's."""
     inp, dO, dO_x, dSf, dSf_x = make_case(variant, 2, 3, 0, 32, 16, "f32", seed=3)
     banner(f"backward {variant} N=0")
     got, ref = run_both(variant, inp, dO, dO_x, dSf, dSf_x)
+    if variant == "kath":
+        assert torch.equal(got["dz0"].cpu(), torch.from_numpy(dSf[1]))
+        dSf = dSf[0]
     assert torch.equal(got["dS0"].cpu(), torch.from_numpy(dSf))
 
 
 @pytest.mark.parametrize("name", ["gla_bf16_b2h8_n2048_d128", "ssd_bf16_b2h32_n4096_dk128_dv64",
-                                  "gdn_bf16_b4h16_n8192_d128"])
+                                  "gdn_bf16_b4h16_n8192_d128",
+                                  "kath_bf16_b1h16_n32768_dk128_dv64"])
 def test_backward_full_workload_sampled(name):
     """The full-size workload; the oracle checks sampled sequences one by one."""
     wl = W.WORKLOADS[name]
@@ -107,7 +122,8 @@ def test_backward_full_workload_sampled(name):
     banner(f"backward full workload {name}")
     nseq = wl.B * wl.H
     for s in (0, nseq - 1):
-        got, ref = run_both(wl.variant, inp, dO, dO_x, None, None, seqs=[s], threads=1)
+        got, ref = run_both(wl.variant, inp, dO, dO_x, None, None, seqs=[s], threads=1,
+                            eps=wl.eps)
         errs = check(got, ref, TOL["bf16"])
         print(name, s, errs, flush=True)
 
