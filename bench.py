@@ -364,7 +364,7 @@ def bench_selscan(name, steps, warmup, torch, bd, W, device, stream, graph=True)
 
 def bench_backward(name, steps, warmup, torch, bd, W, device, stream):
     """Backward of the prefill (the default path: matrix cores for SSD, fp32 VALU for KATH,
-    GLA and GDN):
+    GLA, GDN and KDA):
     tokens per second of the whole backward (every kernel of la_prefill_backward)."""
     import ctypes
     import numpy as np
@@ -526,7 +526,8 @@ def main():
             results[name] = bench_decode(name, 1000, 10, torch, bd, W, device, stream)
             torch.cuda.empty_cache()
         for name in ("gla_bf16_b2h8_n2048_d128", "ssd_bf16_b2h32_n4096_dk128_dv64",
-                     "gdn_bf16_b4h16_n8192_d128", "kath_bf16_b1h16_n32768_dk128_dv64"):
+                     "gdn_bf16_b4h16_n8192_d128", "kda_bf16_b4h16_n8192_d128",
+                     "kath_bf16_b1h16_n32768_dk128_dv64"):
             results["backward_" + name] = bench_backward(name, max(5, args.steps // 80), 2,
                                                          torch, bd, W, device, stream)
             torch.cuda.empty_cache()

@@ -31,6 +31,16 @@
 // sum_r 2^c_r q_r do_r^T - sum_s beta_s 2^c_s k_s du_s^T), and dS0. Then the grads kernel
 // takes every (sequence, chunk) in parallel, loops over the value tiles accumulating the
 // column sums, and writes final dq, dk, dv, dalpha and dbeta.
+//
+// KDA ("状态空间与线性注意力", section KDA: the decay Diag(alpha_t) applied first, then
+// the delta write, with alpha_t per key dim) takes the same route with per-key-dim
+// cumulative logs b_r[i]: every decay factor 2^(c_x - c_y) becomes the vector 2^(b_x - b_y)
+// inside the key-dim sums (L_rs = beta_r sum_i k_ri k_si 2^(b_ri - b_si), X_r = beta_r (v_r
+// - S0^T (k_r 2^b_r)), the state update Diag(2^b_last) S + sum_s (k_s 2^(b_last - b_s))
+// u_s^T, and so on), p_t = S-bar_t^T k_t with S-bar_t = Diag(alpha_t) S_{t-1}, dk_t = G_t
+// u_t - beta_t S-bar_t du_t, and the gate gradient per key dim, dalpha_t[i] = sum_j
+// G_t[i,j] S_{t-1}[i,j] - beta_t k_t[i] (S_{t-1} du_t)[i], whose chunk form needs the
+// d_k x C matrices S0 dO^T, dS' U^T and S0 dU^T besides A and B.
 #include "common.hpp"
 #include "la_internal.h"
 
@@ -392,6 +402,352 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_kernel(GdnBwdArgs a) {
     }
 }
 
+
+// ---------------------------------------------------------------------------- KDA
+// Rows of one chunk with a gate per key dim: cumulative base-2 logs bq (rows past the end
+// have gate 1, so their logs repeat the last real row's).
+template <int DK>
+struct RowsK {
+    float q[C][DK + 1], k[C][DK + 1], bq[C][DK + 1];
+    float b[C];
+};
+
+template <int DK, bool WQ>
+__device__ __forceinline__ void load_rows_kda(RowsK<DK>& sm, const GdnBwdArgs& a, size_t tok, int n) {
+    const int tid = threadIdx.x;
+    const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
+    for (int idx = tid; idx < C * DK; idx += NT) {
+        const int r = idx / DK, i = idx % DK;
+        const size_t e = (tok + r) * DK + i;
+        const bool in = r < n;
+        sm.k[r][i] = in ? load_elem(a.k, e, iob) : 0.f;
+        if (WQ) sm.q[r][i] = in ? load_elem(a.q, e, iob) : 0.f;
+        sm.bq[r][i] = in ? __builtin_amdgcn_logf(load_elem(a.g, e, gb)) : 0.f;
+    }
+    if (tid < C) sm.b[tid] = tid < n ? load_elem(a.beta, tok + tid, gb) : 0.f;
+    __syncthreads();
+    for (int i = tid; i < DK; i += NT) {
+        float acc = 0.f;
+        for (int r = 0; r < C; ++r) {
+            acc += sm.bq[r][i];
+            sm.bq[r][i] = acc;
+        }
+    }
+}
+
+template <int DK>
+struct ChainSmemK {
+    RowsK<DK> rw;
+    float kd[C][DK + 1];    // k_r 2^b_r
+    float kt[C][DK + 1];    // k_r 2^(b_last - b_r)
+    float qd[C][DK + 1];    // q_r 2^b_r (reverse)
+    float S[DK][VT + 1];
+    float x[C][VT];
+    float L[C][C + 1], P[C][C + 1];
+    float rhs[C][VT], u[C][VT];
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(NT) void kda_bwd_chains_kernel(GdnBwdArgs a) {
+    __shared__ ChainSmemK<DK> sm;
+    const int tid = threadIdx.x;
+    const int nfw = a.nseq * a.ntiles;
+    const bool rev = int(blockIdx.x) >= nfw;
+    const int unit = rev ? int(blockIdx.x) - nfw : int(blockIdx.x);
+    const size_t seq = size_t(unit / a.ntiles);
+    const int c0 = (unit % a.ntiles) * VT;
+    const bool iob = a.io_bf16 != 0;
+    const size_t sbase = seq * DK * DV;
+    const float* init = rev ? a.dSf : a.S0;
+    for (int idx = tid; idx < DK * VT; idx += NT) {
+        const int i = idx / VT, j = idx % VT;
+        sm.S[i][j] = init ? init[sbase + size_t(i) * DV + c0 + j] : 0.f;
+    }
+    float* ck = (rev ? a.dSck : a.Sck) + seq * size_t(a.nchunks) * DK * DV;
+    const int r_me = tid / VT, j_me = tid % VT;
+    for (int it = 0; it < a.nchunks; ++it) {
+        const int ch = rev ? a.nchunks - 1 - it : it;
+        const int t0 = ch * C, n = min(C, a.N - t0);
+        const size_t tok = seq * size_t(a.N) + t0;
+        __syncthreads();
+        float* ckc = ck + size_t(ch) * DK * DV;
+        for (int idx = tid; idx < DK * VT; idx += NT) {
+            const int i = idx / VT, j = idx % VT;
+            ckc[size_t(i) * DV + c0 + j] = sm.S[i][j];
+        }
+        if (rev) load_rows_kda<DK, true>(sm.rw, a, tok, n);
+        else load_rows_kda<DK, false>(sm.rw, a, tok, n);
+        sm.x[r_me][j_me] = r_me < n ? load_elem(rev ? a.dO : a.v, (tok + r_me) * DV + c0 + j_me, iob)
+                                    : 0.f;
+        __syncthreads();
+        for (int idx = tid; idx < C * DK; idx += NT) {
+            const int r = idx / DK, i = idx % DK;
+            const float br = sm.rw.bq[r][i];
+            sm.kd[r][i] = sm.rw.k[r][i] * __builtin_amdgcn_exp2f(br);
+            sm.kt[r][i] = sm.rw.k[r][i] * __builtin_amdgcn_exp2f(sm.rw.bq[C - 1][i] - br);
+            if (rev) sm.qd[r][i] = sm.rw.q[r][i] * __builtin_amdgcn_exp2f(br);
+        }
+        {   // thread (r, s): L and, for the reverse chain, P (decays inside the key-dim sums)
+            const int r = tid / C, s = tid % C;
+            float kk = 0.f, qk = 0.f;
+            if (s <= r) {
+                for (int i = 0; i < DK; ++i) {
+                    const float d = __builtin_amdgcn_exp2f(sm.rw.bq[r][i] - sm.rw.bq[s][i]);
+                    kk += sm.rw.k[r][i] * sm.rw.k[s][i] * d;
+                    if (rev) qk += sm.rw.q[r][i] * sm.rw.k[s][i] * d;
+                }
+            }
+            sm.L[r][s] = s < r ? sm.rw.b[r] * kk : 0.f;
+            sm.P[r][s] = qk;
+        }
+        __syncthreads();
+        float ks = 0.f;   // thread (r, j): (k_r 2^b_r) . S[:, j], or (k_r 2^(b_last - b_r)) . dS[:, j]
+        if (!rev) {
+            for (int i = 0; i < DK; ++i) ks += sm.kd[r_me][i] * sm.S[i][j_me];
+            sm.rhs[r_me][j_me] = sm.rw.b[r_me] * (sm.x[r_me][j_me] - ks);
+        } else {
+            for (int i = 0; i < DK; ++i) ks += sm.kt[r_me][i] * sm.S[i][j_me];
+            for (int t = r_me; t < C; ++t) ks += sm.P[t][r_me] * sm.x[t][j_me];
+            sm.rhs[r_me][j_me] = ks;
+        }
+        __syncthreads();
+        if (tid < VT) {
+            const int j = tid;
+            if (!rev) {
+                for (int r = 0; r < C; ++r) {
+                    float u = sm.rhs[r][j];
+                    for (int s = 0; s < r; ++s) u -= sm.L[r][s] * sm.u[s][j];
+                    sm.u[r][j] = u;
+                }
+            } else {
+                for (int s = C - 1; s >= 0; --s) {
+                    float u = sm.rhs[s][j];
+                    for (int r = s + 1; r < C; ++r) u -= sm.L[r][s] * sm.u[r][j];
+                    sm.u[s][j] = u;
+                }
+            }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < DK * VT; idx += NT) {
+            const int i = idx / VT, j = idx % VT;
+            float acc = 0.f;
+            if (!rev) {
+                for (int s = 0; s < C; ++s) acc += sm.kt[s][i] * sm.u[s][j];
+            } else {
+                for (int r = 0; r < C; ++r)
+                    acc += sm.qd[r][i] * sm.x[r][j] - sm.rw.b[r] * sm.kd[r][i] * sm.u[r][j];
+            }
+            sm.S[i][j] = __builtin_amdgcn_exp2f(sm.rw.bq[C - 1][i]) * sm.S[i][j] + acc;
+        }
+    }
+    if (rev) {
+        __syncthreads();
+        for (int idx = tid; idx < DK * VT; idx += NT) {
+            const int i = idx / VT, j = idx % VT;
+            a.dS0[sbase + size_t(i) * DV + c0 + j] = sm.S[i][j];
+        }
+    }
+}
+
+template <int DK>
+struct GradSmemK {
+    RowsK<DK> rw;
+    float L[C][C + 1], Lt[C][C + 1], P[C][C + 1], A[C][C + 1], Bm[C][C + 1];
+    float v[C][VT], dO[C][VT], KS[C][VT], X[C][VT], R[C][VT], U[C][VT], dU[C][VT];
+    float sig[DK];
+    union {
+        struct {   // the tile loop
+            float S0[DK][VT + 1], dS[DK][VT + 1], kd[C][DK + 1], kt[C][DK + 1];
+        } t;
+        struct {   // after it: (S0 dO^T)^T, (dS' U^T)^T, (S0 dU^T)^T, rows by token
+            float SDO[C][DK + 1], DSU[C][DK + 1], SDU[C][DK + 1];
+        } f;
+    } w;
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(NT) void kda_bwd_grads_kernel(GdnBwdArgs a) {
+    constexpr int MQ = C * DK / NT;
+    constexpr int MS = DK * VT / NT;   // state elements per thread in the tile loads
+    static_assert(MQ >= 1 && (C * DK) % NT == 0 && MS >= 1, "d_k >= 16");
+    __shared__ GradSmemK<DK> sm;
+    const int tid = threadIdx.x;
+    const int ch = int(blockIdx.x % unsigned(a.nchunks));
+    const size_t seq = blockIdx.x / unsigned(a.nchunks);
+    const int t0 = ch * C, n = min(C, a.N - t0);
+    const size_t tok = seq * size_t(a.N) + t0;
+    const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
+    const int r_me = tid / C, x_me = tid % C;
+    load_rows_kda<DK, true>(sm.rw, a, tok, n);
+    __syncthreads();
+    {
+        const int r = r_me, s = x_me;
+        float kk = 0.f, qk = 0.f;
+        if (s <= r) {
+            for (int i = 0; i < DK; ++i) {
+                const float d = __builtin_amdgcn_exp2f(sm.rw.bq[r][i] - sm.rw.bq[s][i]);
+                kk += sm.rw.k[r][i] * sm.rw.k[s][i] * d;
+                qk += sm.rw.q[r][i] * sm.rw.k[s][i] * d;
+            }
+        }
+        sm.Lt[r][s] = s < r ? kk : 0.f;
+        sm.L[r][s] = s < r ? sm.rw.b[r] * kk : 0.f;
+        sm.P[r][s] = qk;
+    }
+    float so[MQ], su[MQ], sdu[MQ], sg[MS];
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) so[m] = su[m] = sdu[m] = 0.f;
+#pragma unroll
+    for (int m = 0; m < MS; ++m) sg[m] = 0.f;
+    float A_acc = 0.f, B_acc = 0.f, dbt = 0.f;
+    const size_t ckoff = (seq * a.nchunks + ch) * size_t(DK) * DV;
+    for (int tile = 0; tile < a.ntiles; ++tile) {
+        const int c0 = tile * VT;
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {   // 16 consecutive lanes share a key dim i
+            const int idx = tid + NT * m, i = idx / VT, j = idx % VT;
+            const size_t e = ckoff + size_t(i) * DV + c0 + j;
+            const float s0 = a.Sck[e], ds = a.dSck[e];
+            sm.w.t.S0[i][j] = s0;
+            sm.w.t.dS[i][j] = ds;
+            sg[m] += row16_sum(s0 * ds);
+        }
+        if (tile == 0) {
+            for (int idx = tid; idx < C * DK; idx += NT) {
+                const int r = idx / DK, i = idx % DK;
+                const float br = sm.rw.bq[r][i];
+                sm.w.t.kd[r][i] = sm.rw.k[r][i] * __builtin_amdgcn_exp2f(br);
+                sm.w.t.kt[r][i] = sm.rw.k[r][i] * __builtin_amdgcn_exp2f(sm.rw.bq[C - 1][i] - br);
+            }
+        }
+        {
+            const int t = r_me, j = x_me;
+            const size_t e = (tok + t) * DV + c0 + j;
+            sm.v[t][j] = t < n ? load_elem(a.v, e, iob) : 0.f;
+            sm.dO[t][j] = t < n ? load_elem(a.dO, e, iob) : 0.f;
+        }
+        __syncthreads();
+        const int t = r_me, j = x_me;
+        {
+            float ks = 0.f, kds = 0.f;
+            for (int i = 0; i < DK; ++i) {
+                ks += sm.w.t.kd[t][i] * sm.w.t.S0[i][j];
+                kds += sm.w.t.kt[t][i] * sm.w.t.dS[i][j];
+            }
+            for (int r = t; r < C; ++r) kds += sm.P[r][t] * sm.dO[r][j];
+            sm.KS[t][j] = ks;
+            sm.X[t][j] = sm.rw.b[t] * (sm.v[t][j] - ks);
+            sm.R[t][j] = kds;
+        }
+        __syncthreads();
+        if (tid < VT) {
+            const int jj = tid;
+            for (int r = 0; r < C; ++r) {
+                float u = sm.X[r][jj];
+                for (int s = 0; s < r; ++s) u -= sm.L[r][s] * sm.U[s][jj];
+                sm.U[r][jj] = u;
+            }
+        } else if (tid >= kWave && tid < kWave + VT) {
+            const int jj = tid - kWave;
+            for (int s = C - 1; s >= 0; --s) {
+                float u = sm.R[s][jj];
+                for (int r = s + 1; r < C; ++r) u -= sm.L[r][s] * sm.dU[r][jj];
+                sm.dU[s][jj] = u;
+            }
+        }
+        __syncthreads();
+        {
+            const float du = sm.dU[t][j];
+            float p = sm.KS[t][j];
+            for (int s = 0; s < t; ++s) p += sm.Lt[t][s] * sm.U[s][j];
+            if (t < n) store_elem(a.dv, (tok + t) * DV + c0 + j, sm.rw.b[t] * du, iob);
+            dbt += row16_sum(du * (sm.v[t][j] - p));
+            float av = 0.f, bv = 0.f;
+            for (int jj = 0; jj < VT; ++jj) {
+                av += sm.dO[r_me][jj] * sm.U[x_me][jj];
+                bv += sm.dU[r_me][jj] * sm.U[x_me][jj];
+            }
+            A_acc += av;
+            B_acc += bv;
+        }
+#pragma unroll
+        for (int m = 0; m < MQ; ++m) {
+            const int idx = tid + NT * m, tt = idx / DK, i = idx % DK;
+            float a0 = 0.f, a1 = 0.f, a2 = 0.f;
+            for (int jj = 0; jj < VT; ++jj) {
+                a0 += sm.w.t.S0[i][jj] * sm.dO[tt][jj];
+                a1 += sm.w.t.dS[i][jj] * sm.U[tt][jj];
+                a2 += sm.w.t.S0[i][jj] * sm.dU[tt][jj];
+            }
+            so[m] += a0;
+            su[m] += a1;
+            sdu[m] += a2;
+        }
+    }
+    __syncthreads();   // the last tile's readers of the tile arrays are done
+    sm.A[r_me][x_me] = A_acc;
+    sm.Bm[r_me][x_me] = B_acc;
+    if (x_me == 0 && r_me < n) store_elem(a.dbeta, tok + r_me, dbt, gb);
+#pragma unroll
+    for (int m = 0; m < MS; ++m)
+        if ((tid % VT) == 0) sm.sig[(tid + NT * m) / VT] = sg[m];
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) {
+        const int idx = tid + NT * m, tt = idx / DK, i = idx % DK;
+        sm.w.f.SDO[tt][i] = so[m];
+        sm.w.f.DSU[tt][i] = su[m];
+        sm.w.f.SDU[tt][i] = sdu[m];
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int m = 0; m < MQ; ++m) {
+        const int idx = tid + NT * m, t = idx / DK, i = idx % DK;
+        const auto& rw = sm.rw;
+        const float bt = rw.bq[t][i], btm = t > 0 ? rw.bq[t - 1][i] : 0.f;
+        const float g1 = __builtin_amdgcn_exp2f(btm);              // 2^b_{t-1}
+        const float gt = __builtin_amdgcn_exp2f(bt);               // 2^b_t
+        const float at = __builtin_amdgcn_exp2f(bt - btm);         // alpha_t[i]
+        const float elt = __builtin_amdgcn_exp2f(rw.bq[C - 1][i] - bt);
+        float e2[C];   // 2^(b_{t-1} - b_s) k_s[i] for s < t
+#pragma unroll
+        for (int s = 0; s < C; ++s)
+            e2[s] = s < t ? __builtin_amdgcn_exp2f(btm - rw.bq[s][i]) * rw.k[s][i] : 0.f;
+        float sA = 0.f, sB = 0.f, sD = 0.f;
+#pragma unroll
+        for (int s = 0; s < C; ++s) {
+            sA += e2[s] * sm.A[t][s];
+            sB += e2[s] * sm.Bm[t][s];
+            sD += e2[s] * sm.w.f.DSU[s][i];
+        }
+        const float dq = gt * sm.w.f.SDO[t][i] + sm.A[t][t] * rw.k[t][i] + at * sA;
+        float dk = elt * sm.w.f.DSU[t][i] - rw.b[t] * (gt * sm.w.f.SDU[t][i] + at * sB);
+        float da = elt * (g1 * sm.sig[i] + sD) - rw.b[t] * rw.k[t][i] * (g1 * sm.w.f.SDU[t][i] + sB);
+        for (int r = t; r < C; ++r) {
+            const float er = __builtin_amdgcn_exp2f(rw.bq[r][i] - bt) * rw.q[r][i];
+            dk += sm.A[r][t] * er;
+            float in = g1 * sm.w.f.SDO[r][i];
+#pragma unroll
+            for (int s = 0; s < C; ++s) in += e2[s] * sm.A[r][s];
+            da += er * in;
+        }
+        for (int s2 = t + 1; s2 < C; ++s2) {
+            const float es = __builtin_amdgcn_exp2f(rw.bq[s2][i] - bt) * rw.b[s2] * rw.k[s2][i];
+            dk -= sm.Bm[s2][t] * es;
+            float in = g1 * sm.w.f.SDU[s2][i];
+#pragma unroll
+            for (int s = 0; s < C; ++s) in += e2[s] * sm.Bm[s2][s];
+            da -= es * in;
+        }
+        if (t < n) {
+            const size_t e = (tok + t) * DK + i;
+            store_elem(a.dq, e, dq, iob);
+            store_elem(a.dk, e, dk, iob);
+            store_elem(a.dg, e, da, gb);
+        }
+    }
+}
+
 struct GdnLayout {
     size_t Sck, dSck, total;
 };
@@ -408,10 +764,17 @@ GdnLayout gdn_layout(const Problem& p) {
 template <int DK, int DV>
 hipError_t launch_dims(const Problem& p, GdnBwdArgs a) {
     const unsigned chains = unsigned(2 * a.nseq * a.ntiles);
+    const unsigned units = unsigned(size_t(a.nseq) * a.nchunks);
+    if (p.variant == LA_KDA) {
+        kda_bwd_chains_kernel<DK, DV><<<dim3(chains), dim3(NT), 0, p.stream>>>(a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        kda_bwd_grads_kernel<DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
+        return hipGetLastError();
+    }
     gdn_bwd_chains_kernel<DK, DV><<<dim3(chains), dim3(NT), 0, p.stream>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned units = unsigned(size_t(a.nseq) * a.nchunks);
     gdn_bwd_grads_kernel<DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
     return hipGetLastError();
 }

@@ -544,12 +544,13 @@ __global__ void bwd_copy_kernel(const float* dSf, float* dS0, size_t n, const fl
 }  // namespace
 
 bool backward_supported(int variant) {
-    return variant == LA_GLA || variant == LA_SSD || variant == LA_GDN || variant == LA_KATH;
+    return variant == LA_GLA || variant == LA_SSD || variant == LA_GDN || variant == LA_KDA ||
+           variant == LA_KATH;
 }
 
 size_t backward_workspace_bytes(const Problem& p) {
     if (p.N == 0 || p.B == 0 || p.H == 0) return 0;
-    if (p.variant == LA_GDN) return gdn_backward_workspace_bytes(p);
+    if (p.variant == LA_GDN || p.variant == LA_KDA) return gdn_backward_workspace_bytes(p);
     return bwd_layout(p).total;
 }
 
@@ -564,7 +565,7 @@ hipError_t launch_backward(const BwdProblem& bp) {
             bp.dS_final, bp.dS0, n, bp.dz_final, p.variant == LA_KATH ? bp.dz0 : nullptr, nz);
         return hipGetLastError();
     }
-    if (p.variant == LA_GDN) return launch_backward_gdn(bp);
+    if (p.variant == LA_GDN || p.variant == LA_KDA) return launch_backward_gdn(bp);
     const bool ka = p.variant == LA_KATH;
     const size_t nseq = size_t(p.B) * p.H;
     const size_t nchunks = size_t((p.N + C - 1) / C);

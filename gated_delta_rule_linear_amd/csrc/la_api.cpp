@@ -398,8 +398,8 @@ int la_prefill_backward(const la_desc* d, const void* q, const void* k, const vo
     la::Problem p;
     int rc = check_backward_desc(d, p);
     if (rc != LA_OK) return rc;
-    // GDN (the delta rule) takes beta; KATH has no gate and carries the normaliser z
-    const bool delta = d->variant == LA_GDN, kath = d->variant == LA_KATH;
+    // GDN and KDA (the delta rule) take beta; KATH has no gate and carries the normaliser z
+    const bool delta = d->variant == LA_GDN || d->variant == LA_KDA, kath = d->variant == LA_KATH;
     if (!kath && (z0 || dz_final || dz0)) return LA_ERR_INVALID;
     if (kath && (g || dg)) return LA_ERR_INVALID;
     if (!delta && (beta || dbeta)) return LA_ERR_INVALID;

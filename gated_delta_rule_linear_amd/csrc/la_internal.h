@@ -79,7 +79,8 @@ struct BwdProblem {
 bool backward_supported(int variant);
 size_t backward_workspace_bytes(const Problem& p);
 hipError_t launch_backward(const BwdProblem& p);
-// backward_gdn_valu.hip (GDN backward, fp32 vector ALUs); called through launch_backward
+// backward_gdn_valu.hip (GDN and KDA backward, fp32 vector ALUs); called through
+// launch_backward
 size_t gdn_backward_workspace_bytes(const Problem& p);
 hipError_t launch_backward_gdn(const BwdProblem& p);
 // backward_ssd_mfma.hip (SSD backward on the matrix cores: bf16, d_k = 128, d_v = 64)

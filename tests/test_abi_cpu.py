@@ -375,7 +375,7 @@ def call_bwd(lib, desc, ws=None, ws_bytes=0, **p):
 
 @pytest.mark.parametrize("case,expect", [
     ("null_desc", bd.LA_ERR_INVALID),
-    ("kda_unsupported", bd.LA_ERR_UNSUPPORTED),
+    ("kda_null_beta", bd.LA_ERR_INVALID),
     ("kath_g_given", bd.LA_ERR_INVALID),
     ("kath_null_dz0", bd.LA_ERR_INVALID),
     ("kath_dz0_overlaps_z0", bd.LA_ERR_INVALID),
@@ -397,14 +397,16 @@ def call_bwd(lib, desc, ws=None, ws_bytes=0, **p):
     ("no_workspace", bd.LA_ERR_WORKSPACE),
 ])
 def test_backward_rejects(lib, case, expect):
-    variant = {"kda_unsupported": "kda"}.get(case, "gla")
+    variant = "gla"
     if case.startswith("gdn_"):
         variant = "gdn"
+    if case.startswith("kda_"):
+        variant = "kda"
     if case.startswith("kath_"):
         variant = "kath"
     d = good(variant)
     p = bwd_args()
-    if variant == "gdn":
+    if variant in ("gdn", "kda"):
         p["beta"], p["dbeta"] = addr(4), addr(15)
     if variant == "kath":
         p["g"], p["dg"] = None, None
@@ -432,7 +434,7 @@ def test_backward_rejects(lib, case, expect):
         p["dS0"] = addr(5)
     elif case == "no_workspace":
         ws, wsb = None, 0
-    elif case == "gdn_null_beta":
+    elif case in ("gdn_null_beta", "kda_null_beta"):
         p["beta"] = None
     elif case == "gdn_null_dbeta":
         p["dbeta"] = None
@@ -475,7 +477,7 @@ def test_backward_workspace_query(lib):
     assert lib.la_prefill_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == bd.LA_OK
     assert n.value > 0
     d = good("kda")
-    assert lib.la_prefill_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == \
-        bd.LA_ERR_UNSUPPORTED
+    assert lib.la_prefill_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == bd.LA_OK
+    assert n.value > 0
     d = good("gla", B=0)
     assert call_bwd(lib, d, **bwd_args()) == bd.LA_OK   # no sequences: nothing to do

@@ -1,4 +1,4 @@
-"""Parity of the prefill backward (KATH, GLA, SSD, GDN) against the fp64 oracle's
+"""Parity of the prefill backward (KATH, GLA, SSD, GDN, KDA) against the fp64 oracle's
 reverse-mode gradients (GPU)."""
 import numpy as np
 import pytest
@@ -17,7 +17,7 @@ def make_case(variant, B, H, N, dk, dv, io, seed, gate_kind="default", with_stat
     kw = dict(seed=seed, qk_scale=dk ** -0.5, gate_kind=gate_kind)
     if variant == "gla":
         kw["v_scale"] = dk ** -0.5
-    if variant == "gdn":
+    if variant in ("gdn", "kda"):
         kw["l2norm_qk"] = True
     wl = W.Workload("b", variant, B, H, N, dk, dv, io, io, **kw)
     inp = W.make_inputs(wl, with_state=with_state)
@@ -66,7 +66,7 @@ def check(got, ref, tol):
     return errs
 
 
-@pytest.mark.parametrize("variant", ["kath", "gla", "ssd", "gdn"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "ssd", "gdn", "kda"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (128, 128), (128, 64)])
 def test_backward_shapes(variant, io, dk, dv):
@@ -75,7 +75,7 @@ def test_backward_shapes(variant, io, dk, dv):
     check(*run_both(variant, *case), TOL[io])
 
 
-@pytest.mark.parametrize("variant", ["kath", "gla", "ssd", "gdn"])
+@pytest.mark.parametrize("variant", ["kath", "gla", "ssd", "gdn", "kda"])
 @pytest.mark.parametrize("N", [1, 15, 16, 17, 70])
 def test_backward_lengths(variant, N):
     case = make_case(variant, 1, 3, N, 32, 16, "f32", seed=N, gate_kind="slow")
@@ -85,7 +85,9 @@ def test_backward_lengths(variant, N):
 
 @pytest.mark.parametrize("variant,kind", [("gla", "fast"), ("gla", "ones"), ("ssd", "fast"),
                                           ("ssd", "ones"), ("gdn", "default"), ("gdn", "ones"),
-                                          ("gdn", "beta0"), ("gdn", "beta1")])
+                                          ("gdn", "beta0"), ("gdn", "beta1"),
+                                          ("kda", "default"), ("kda", "ones"), ("kda", "beta0"),
+                                          ("kda", "beta1")])
 def test_backward_gate_kinds(variant, kind):
     case = make_case(variant, 1, 2, 50, 64, 32, "f32", seed=9, gate_kind=kind)
     banner(f"backward {variant} gates={kind}")
@@ -98,7 +100,7 @@ def test_backward_without_state_or_final_gradient():
     check(*run_both("gla", *case), TOL["bf16"])
 
 
-@pytest.mark.parametrize("variant", ["ssd", "gdn", "kath"])
+@pytest.mark.parametrize("variant", ["ssd", "gdn", "kda", "kath"])
 def test_backward_empty_sequence(variant):
     """N = 0: the initial state's gradient is the final state's."""
     inp, dO, dO_x, dSf, dSf_x = make_case(variant, 2, 3, 0, 32, 16, "f32", seed=3)
@@ -111,7 +113,7 @@ def test_backward_empty_sequence(variant):
 
 
 @pytest.mark.parametrize("name", ["gla_bf16_b2h8_n2048_d128", "ssd_bf16_b2h32_n4096_dk128_dv64",
-                                  "gdn_bf16_b4h16_n8192_d128",
+                                  "gdn_bf16_b4h16_n8192_d128", "kda_bf16_b4h16_n8192_d128",
                                   "kath_bf16_b1h16_n32768_dk128_dv64"])
 def test_backward_full_workload_sampled(name):
     """The full-size workload; the oracle checks sampled sequences one by one."""
@@ -128,7 +130,7 @@ def test_backward_full_workload_sampled(name):
         print(name, s, errs, flush=True)
 
 
-@pytest.mark.parametrize("variant", ["gla", "gdn"])
+@pytest.mark.parametrize("variant", ["gla", "gdn", "kda"])
 def test_backward_tiny_gates(variant):
     """Gates down to 1e-7 (5% of them): the gate gradient is taken directly from the states,
     so tiny gates cost no accuracy (fp32 bound)."""
