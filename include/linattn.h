@@ -176,28 +176,34 @@ int la_decode_step(const la_desc* d, const void* q, const void* k, const void* v
                    const void* g, const void* beta, float* S, float* z, void* o,
                    void* stream);
 
-/* Backward of la_prefill: the gradients of every input for a loss with dL/do = dO and
- * dL/dS_final = dS_final (NULL: zero), by reverse-mode differentiation of the recurrence
- * (the training side of the same prefill; "线性注意力与 SSM" notes that training keeps
- * length-N activations and may recompute states, which this does: the chunk-entering
- * states are recomputed into the workspace). Variants: LA_GLA and LA_SSD (the diagonal
- * transitions); others return LA_ERR_UNSUPPORTED. SSD with bf16 io, d_k = 128 and
- * d_v = 64 runs on the matrix cores (bf16 operands, fp32 accumulation, chunk 64) for
- * d->path LA_PATH_AUTO or LA_PATH_MFMA; every other case (and LA_PATH_VALU) runs in fp32
- * on the vector ALUs (chunk 16) for any supported d_k, d_v and either io dtype.
- * LA_PATH_MFMA for a shape the matrix cores do not take is LA_ERR_UNSUPPORTED; a chunk
- * other than 0 or the path's is LA_ERR_UNSUPPORTED.
- *   q, k, v, g, S0     the forward's inputs (S0 may be NULL)
+/* Backward of la_prefill: the gradients of every input for a loss with dL/do = dO,
+ * dL/dS_final = dS_final and, for KATH, dL/dz_final = dz_final (NULL: zero), by
+ * reverse-mode differentiation of the recurrence (the training side of the same prefill;
+ * "线性注意力与 SSM" notes that training keeps length-N activations and may recompute
+ * states, which this does: the chunk-entering states, and for KATH the forward's
+ * denominators, are recomputed into the workspace). Every variant is taken. SSD with bf16
+ * io, d_k = 128 and d_v = 64 runs on the matrix cores (bf16 operands, fp32 accumulation,
+ * chunk 64) for d->path LA_PATH_AUTO or LA_PATH_MFMA; every other case (and
+ * LA_PATH_VALU) runs in fp32 on the vector ALUs (chunk 16) for any supported d_k, d_v and
+ * either io dtype. LA_PATH_MFMA for a shape the matrix cores do not take is
+ * LA_ERR_UNSUPPORTED; a chunk other than 0 or the path's is LA_ERR_UNSUPPORTED. The gate
+ * gradients (dg, GDN's dalpha, KDA's per-key-dim dalpha) are formed directly from pairs of
+ * token states, not through log-gate sums, so tiny gates keep fp32 accuracy.
+ *   q, k, v, g, beta, S0, z0   the forward's inputs (S0, z0 may be NULL; g is NULL for
+ *                      KATH, beta for every variant but GDN and KDA, z0 for all but KATH)
  *   dO                 [B, H, N, d_v] io
  *   dq, dk             [B, H, N, d_k] io, written;  dv [B, H, N, d_v] io, written
  *   dg                 shaped like g (gate dtype), written: dL/dg for the gate as given
+ *                      (NULL for KATH)
+ *   dbeta              [B, H, N] gate dtype, written (GDN, KDA; NULL otherwise)
  *   dS0                [B, H, d_k, d_v] fp32, written (also when S0 is NULL: the gradient
  *                      with respect to the zero initial state)
- *   beta, z0, dz_final, dbeta, dz0   must be NULL (reserved for the variants with a
- *                      delta rule or a normaliser)
+ *   dz_final, dz0      KATH: [B, H, d_k] fp32 (dz_final may be NULL), dz0 written; NULL
+ *                      for the other variants
  *   workspace          at least la_prefill_backward_workspace_size bytes, 256-byte aligned
  * Outputs overlap nothing (no input, no other output, not the workspace). Alignment as for
- * la_prefill (dq, dk as q; dv and dO as v; dg as g). Errors as for la_prefill. */
+ * la_prefill (dq, dk as q; dv and dO as v; dg as g; dbeta as beta; dz0, dz_final 16
+ * bytes). Errors as for la_prefill. */
 int la_prefill_backward_workspace_size(const la_desc* d, size_t* bytes);
 int la_prefill_backward(const la_desc* d, const void* q, const void* k, const void* v,
                         const void* g, const void* beta, const float* S0, const float* z0,
