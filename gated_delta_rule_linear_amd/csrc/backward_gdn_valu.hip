@@ -25,8 +25,10 @@
 // products A_rs = do_r.u_s, B_rs = du_r.u_s, kappa_s = (dS'^T k_s).u_s, rho_r = (S0^T
 // q_r).do_r, mu_s = (S0^T k_s).du_s, sigma = <dS', S0>, and of d_k-vectors such as S0 do_t.
 //
-// Kernels: one launch runs both chains, each workgroup one (sequence, 16-column value tile)
-// (value columns never mix in either recurrence): the forward chain writes the state
+// Kernels: a prep kernel forms every chunk's T = (I + L)^-1 and P in parallel; then one
+// launch runs both chains, each workgroup one (sequence, 16-column value tile), with U = T X
+// and dU = T^T R as small products (value columns never mix in either recurrence): the
+// forward chain writes the state
 // entering every chunk, the reverse chain the gradient leaving it (dS_in = 2^c_last dS' +
 // sum_r 2^c_r q_r do_r^T - sum_s beta_s 2^c_s k_s du_s^T), and dS0. Then the grads kernel
 // takes every (sequence, chunk) in parallel, loops over the value tiles accumulating the
@@ -59,6 +61,8 @@ struct GdnBwdArgs {
     float* dS0;
     float* Sck;    // [nseq][nchunks][DK][DV] state entering each chunk
     float* dSck;   // [nseq][nchunks][DK][DV] gradient of the state leaving each chunk
+    float* Tck;    // [nseq][nchunks][C][C] T = (I + L)^-1 of each chunk
+    float* Pck;    // [nseq][nchunks][C][C] P of each chunk (lower triangle with diagonal)
     int N, nseq, ntiles, nchunks;
     int io_bf16, gate_bf16;
 };
@@ -102,6 +106,84 @@ __device__ __forceinline__ void load_rows(Rows<DK>& sm, const GdnBwdArgs& a, siz
     }
 }
 
+
+// Triangular solves for one value column, the solved rows kept in registers (an LDS round
+// trip per step would put its latency on every row): forward substitution (I + L) u = x
+// and back substitution (I + L)^T u = x, L strictly lower with row pitch C + 1.
+__device__ __forceinline__ void solve_lower(const float (*L)[C + 1], const float (*x)[VT],
+                                            float (*u)[VT], int j) {
+    float w[C];
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+        float acc = x[r][j];
+#pragma unroll
+        for (int s = 0; s < r; ++s) acc -= L[r][s] * w[s];
+        w[r] = acc;
+        u[r][j] = acc;
+    }
+}
+__device__ __forceinline__ void solve_upper_t(const float (*L)[C + 1], const float (*x)[VT],
+                                              float (*u)[VT], int j) {
+    float w[C];
+#pragma unroll
+    for (int s = C - 1; s >= 0; --s) {
+        float acc = x[s][j];
+#pragma unroll
+        for (int r = s + 1; r < C; ++r) acc -= L[r][s] * w[r];
+        w[s] = acc;
+        u[s][j] = acc;
+    }
+}
+
+
+// ---------------------------------------------------------------------------- prep
+// T = (I + L)^-1 (unit lower triangular) by forward substitution on the unit vectors, one
+// column per thread, and P, for every (sequence, chunk) in parallel.
+__device__ __forceinline__ void store_t_and_p(const float (*L)[C + 1], float p, float* Tg,
+                                              float* Pg) {
+    const int tid = threadIdx.x;
+    Pg[tid] = p;   // thread (r, s) = (tid / C, tid % C)
+    if (tid < C) {
+        const int j = tid;
+        float w[C];
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+            float acc = r == j ? 1.f : 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < r; ++s2) acc -= L[r][s2] * w[s2];
+            w[r] = acc;
+            Tg[r * C + j] = acc;
+        }
+    }
+}
+
+template <int DK>
+struct PrepSmem {
+    Rows<DK> rw;
+    float L[C][C + 1];
+};
+
+template <int DK>
+__global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(GdnBwdArgs a) {
+    __shared__ PrepSmem<DK> sm;
+    const int ch = int(blockIdx.x % unsigned(a.nchunks));
+    const size_t seq = blockIdx.x / unsigned(a.nchunks);
+    const int t0 = ch * C, n = min(C, a.N - t0);
+    load_rows<DK, true>(sm.rw, a, seq * size_t(a.N) + t0, n);
+    __syncthreads();
+    const int r = threadIdx.x / C, s2 = threadIdx.x % C;
+    float kk = 0.f, qk = 0.f;
+    for (int i = 0; i < DK; ++i) {
+        kk += sm.rw.k[r][i] * sm.rw.k[s2][i];
+        qk += sm.rw.q[r][i] * sm.rw.k[s2][i];
+    }
+    const float d = s2 <= r ? __builtin_amdgcn_exp2f(sm.rw.c[r] - sm.rw.c[s2]) : 0.f;
+    sm.L[r][s2] = s2 < r ? sm.rw.b[r] * d * kk : 0.f;
+    __syncthreads();
+    const size_t off = (seq * a.nchunks + ch) * size_t(C * C);
+    store_t_and_p(sm.L, d * qk, a.Tck + off, a.Pck + off);
+}
+
 // ---------------------------------------------------------------------------- chains
 template <int DK>
 struct ChainSmem {
@@ -112,8 +194,9 @@ struct ChainSmem {
     float rhs[C][VT], u[C][VT];
 };
 
+// (at most 128 registers: four waves per SIMD keep every chain of a typical launch resident)
 template <int DK, int DV>
-__global__ __launch_bounds__(NT) void gdn_bwd_chains_kernel(GdnBwdArgs a) {
+__global__ __launch_bounds__(NT, 4) void gdn_bwd_chains_kernel(GdnBwdArgs a) {
     __shared__ ChainSmem<DK> sm;
     const int tid = threadIdx.x;
     const int nfw = a.nseq * a.ntiles;
@@ -144,43 +227,31 @@ __global__ __launch_bounds__(NT) void gdn_bwd_chains_kernel(GdnBwdArgs a) {
         else load_rows<DK, false>(sm.rw, a, tok, n);
         sm.x[r_me][j_me] = r_me < n ? load_elem(rev ? a.dO : a.v, (tok + r_me) * DV + c0 + j_me, iob)
                                     : 0.f;
-        __syncthreads();
-        {   // thread (r, s): L and, for the reverse chain, P
-            const int r = tid / C, s = tid % C;
-            float kk = 0.f, qk = 0.f;
-            for (int i = 0; i < DK; ++i) {
-                kk += sm.rw.k[r][i] * sm.rw.k[s][i];
-                if (rev) qk += sm.rw.q[r][i] * sm.rw.k[s][i];
-            }
-            const float d = s <= r ? __builtin_amdgcn_exp2f(sm.rw.c[r] - sm.rw.c[s]) : 0.f;
-            sm.L[r][s] = s < r ? sm.rw.b[r] * d * kk : 0.f;
-            sm.P[r][s] = d * qk;
+        {
+            const size_t off = (seq * a.nchunks + ch) * size_t(C * C);
+            sm.L[tid / C][tid % C] = a.Tck[off + tid];   // T
+            if (rev) sm.P[tid / C][tid % C] = a.Pck[off + tid];
         }
-        float ks = 0.f;   // thread (r, j): k_r . S[:, j]
-        for (int i = 0; i < DK; ++i) ks += sm.rw.k[r_me][i] * sm.S[i][j_me];
-        if (!rev) sm.rhs[r_me][j_me] = sm.rw.b[r_me] * (sm.x[r_me][j_me] - sm.rw.eg[r_me] * ks);
         __syncthreads();
-        if (rev) {
+        float ks = 0.f;   // thread (r, j): k_r . S[:, j]
+#pragma unroll 8
+        for (int i = 0; i < DK; ++i) ks += sm.rw.k[r_me][i] * sm.S[i][j_me];
+        if (!rev) {
+            sm.rhs[r_me][j_me] = sm.rw.b[r_me] * (sm.x[r_me][j_me] - sm.rw.eg[r_me] * ks);
+        } else {
             float acc = sm.rw.el[r_me] * ks;
             for (int t = r_me; t < C; ++t) acc += sm.P[t][r_me] * sm.x[t][j_me];
             sm.rhs[r_me][j_me] = acc;
-            __syncthreads();
         }
-        if (tid < VT) {   // triangular solve per column
-            const int j = tid;
+        __syncthreads();
+        {   // U = T X (forward) or dU = T^T R (reverse)
+            float acc = 0.f;
             if (!rev) {
-                for (int r = 0; r < C; ++r) {
-                    float u = sm.rhs[r][j];
-                    for (int s = 0; s < r; ++s) u -= sm.L[r][s] * sm.u[s][j];
-                    sm.u[r][j] = u;
-                }
+                for (int s2 = 0; s2 <= r_me; ++s2) acc += sm.L[r_me][s2] * sm.rhs[s2][j_me];
             } else {
-                for (int s = C - 1; s >= 0; --s) {
-                    float u = sm.rhs[s][j];
-                    for (int r = s + 1; r < C; ++r) u -= sm.L[r][s] * sm.u[r][j];
-                    sm.u[s][j] = u;
-                }
+                for (int t = r_me; t < C; ++t) acc += sm.L[t][r_me] * sm.rhs[t][j_me];
             }
+            sm.u[r_me][j_me] = acc;
         }
         __syncthreads();
         const float dl = sm.rw.eg[C - 1];
@@ -299,21 +370,9 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_kernel(GdnBwdArgs a) {
             sm.R[t][j] = r_;
         }
         __syncthreads();
-        if (tid < VT) {   // U: forward substitution, one column per thread
-            const int jj = tid;
-            for (int r = 0; r < C; ++r) {
-                float u = sm.X[r][jj];
-                for (int s = 0; s < r; ++s) u -= sm.L[r][s] * sm.U[s][jj];
-                sm.U[r][jj] = u;
-            }
-        } else if (tid >= kWave && tid < kWave + VT) {   // dU: back substitution (another wave)
-            const int jj = tid - kWave;
-            for (int s = C - 1; s >= 0; --s) {
-                float u = sm.R[s][jj];
-                for (int r = s + 1; r < C; ++r) u -= sm.L[r][s] * sm.dU[r][jj];
-                sm.dU[s][jj] = u;
-            }
-        }
+        if (tid < VT) solve_lower(sm.L, sm.X, sm.U, tid);   // U, one column per thread
+        else if (tid >= kWave && tid < kWave + VT)          // dU, on another wave
+            solve_upper_t(sm.L, sm.R, sm.dU, tid - kWave);
         __syncthreads();
         {
             const float u = sm.U[t][j], du = sm.dU[t][j];
@@ -435,12 +494,40 @@ __device__ __forceinline__ void load_rows_kda(RowsK<DK>& sm, const GdnBwdArgs& a
     }
 }
 
+
+template <int DK>
+struct PrepSmemK {
+    RowsK<DK> rw;
+    float L[C][C + 1];
+};
+
+template <int DK>
+__global__ __launch_bounds__(NT) void kda_bwd_prep_kernel(GdnBwdArgs a) {
+    __shared__ PrepSmemK<DK> sm;
+    const int ch = int(blockIdx.x % unsigned(a.nchunks));
+    const size_t seq = blockIdx.x / unsigned(a.nchunks);
+    const int t0 = ch * C, n = min(C, a.N - t0);
+    load_rows_kda<DK, true>(sm.rw, a, seq * size_t(a.N) + t0, n);
+    __syncthreads();
+    const int r = threadIdx.x / C, s2 = threadIdx.x % C;
+    float kk = 0.f, qk = 0.f;
+    if (s2 <= r) {
+        for (int i = 0; i < DK; ++i) {
+            const float d = __builtin_amdgcn_exp2f(sm.rw.bq[r][i] - sm.rw.bq[s2][i]);
+            kk += sm.rw.k[r][i] * sm.rw.k[s2][i] * d;
+            qk += sm.rw.q[r][i] * sm.rw.k[s2][i] * d;
+        }
+    }
+    sm.L[r][s2] = s2 < r ? sm.rw.b[r] * kk : 0.f;
+    __syncthreads();
+    const size_t off = (seq * a.nchunks + ch) * size_t(C * C);
+    store_t_and_p(sm.L, qk, a.Tck + off, a.Pck + off);
+}
+
 template <int DK>
 struct ChainSmemK {
-    RowsK<DK> rw;
-    float kd[C][DK + 1];    // k_r 2^b_r
+    RowsK<DK> rw;           // k and q are replaced in place by k_r 2^b_r and q_r 2^b_r
     float kt[C][DK + 1];    // k_r 2^(b_last - b_r)
-    float qd[C][DK + 1];    // q_r 2^b_r (reverse)
     float S[DK][VT + 1];
     float x[C][VT];
     float L[C][C + 1], P[C][C + 1];
@@ -480,52 +567,40 @@ __global__ __launch_bounds__(NT) void kda_bwd_chains_kernel(GdnBwdArgs a) {
         sm.x[r_me][j_me] = r_me < n ? load_elem(rev ? a.dO : a.v, (tok + r_me) * DV + c0 + j_me, iob)
                                     : 0.f;
         __syncthreads();
-        for (int idx = tid; idx < C * DK; idx += NT) {
+        for (int idx = tid; idx < C * DK; idx += NT) {   // each element read and written by one thread
             const int r = idx / DK, i = idx % DK;
-            const float br = sm.rw.bq[r][i];
-            sm.kd[r][i] = sm.rw.k[r][i] * __builtin_amdgcn_exp2f(br);
-            sm.kt[r][i] = sm.rw.k[r][i] * __builtin_amdgcn_exp2f(sm.rw.bq[C - 1][i] - br);
-            if (rev) sm.qd[r][i] = sm.rw.q[r][i] * __builtin_amdgcn_exp2f(br);
+            const float br = sm.rw.bq[r][i], eb = __builtin_amdgcn_exp2f(br);
+            const float kv = sm.rw.k[r][i];
+            sm.kt[r][i] = kv * __builtin_amdgcn_exp2f(sm.rw.bq[C - 1][i] - br);
+            sm.rw.k[r][i] = kv * eb;
+            if (rev) sm.rw.q[r][i] *= eb;
         }
-        {   // thread (r, s): L and, for the reverse chain, P (decays inside the key-dim sums)
-            const int r = tid / C, s = tid % C;
-            float kk = 0.f, qk = 0.f;
-            if (s <= r) {
-                for (int i = 0; i < DK; ++i) {
-                    const float d = __builtin_amdgcn_exp2f(sm.rw.bq[r][i] - sm.rw.bq[s][i]);
-                    kk += sm.rw.k[r][i] * sm.rw.k[s][i] * d;
-                    if (rev) qk += sm.rw.q[r][i] * sm.rw.k[s][i] * d;
-                }
-            }
-            sm.L[r][s] = s < r ? sm.rw.b[r] * kk : 0.f;
-            sm.P[r][s] = qk;
+        {
+            const size_t off = (seq * a.nchunks + ch) * size_t(C * C);
+            sm.L[tid / C][tid % C] = a.Tck[off + tid];   // T
+            if (rev) sm.P[tid / C][tid % C] = a.Pck[off + tid];
         }
         __syncthreads();
         float ks = 0.f;   // thread (r, j): (k_r 2^b_r) . S[:, j], or (k_r 2^(b_last - b_r)) . dS[:, j]
         if (!rev) {
-            for (int i = 0; i < DK; ++i) ks += sm.kd[r_me][i] * sm.S[i][j_me];
+#pragma unroll 8
+            for (int i = 0; i < DK; ++i) ks += sm.rw.k[r_me][i] * sm.S[i][j_me];
             sm.rhs[r_me][j_me] = sm.rw.b[r_me] * (sm.x[r_me][j_me] - ks);
         } else {
+#pragma unroll 8
             for (int i = 0; i < DK; ++i) ks += sm.kt[r_me][i] * sm.S[i][j_me];
             for (int t = r_me; t < C; ++t) ks += sm.P[t][r_me] * sm.x[t][j_me];
             sm.rhs[r_me][j_me] = ks;
         }
         __syncthreads();
-        if (tid < VT) {
-            const int j = tid;
+        {   // U = T X (forward) or dU = T^T R (reverse)
+            float acc = 0.f;
             if (!rev) {
-                for (int r = 0; r < C; ++r) {
-                    float u = sm.rhs[r][j];
-                    for (int s = 0; s < r; ++s) u -= sm.L[r][s] * sm.u[s][j];
-                    sm.u[r][j] = u;
-                }
+                for (int s2 = 0; s2 <= r_me; ++s2) acc += sm.L[r_me][s2] * sm.rhs[s2][j_me];
             } else {
-                for (int s = C - 1; s >= 0; --s) {
-                    float u = sm.rhs[s][j];
-                    for (int r = s + 1; r < C; ++r) u -= sm.L[r][s] * sm.u[r][j];
-                    sm.u[s][j] = u;
-                }
+                for (int t = r_me; t < C; ++t) acc += sm.L[t][r_me] * sm.rhs[t][j_me];
             }
+            sm.u[r_me][j_me] = acc;
         }
         __syncthreads();
         for (int idx = tid; idx < DK * VT; idx += NT) {
@@ -535,7 +610,7 @@ __global__ __launch_bounds__(NT) void kda_bwd_chains_kernel(GdnBwdArgs a) {
                 for (int s = 0; s < C; ++s) acc += sm.kt[s][i] * sm.u[s][j];
             } else {
                 for (int r = 0; r < C; ++r)
-                    acc += sm.qd[r][i] * sm.x[r][j] - sm.rw.b[r] * sm.kd[r][i] * sm.u[r][j];
+                    acc += sm.rw.q[r][i] * sm.x[r][j] - sm.rw.b[r] * sm.rw.k[r][i] * sm.u[r][j];
             }
             sm.S[i][j] = __builtin_amdgcn_exp2f(sm.rw.bq[C - 1][i]) * sm.S[i][j] + acc;
         }
@@ -641,21 +716,9 @@ __global__ __launch_bounds__(NT) void kda_bwd_grads_kernel(GdnBwdArgs a) {
             sm.R[t][j] = kds;
         }
         __syncthreads();
-        if (tid < VT) {
-            const int jj = tid;
-            for (int r = 0; r < C; ++r) {
-                float u = sm.X[r][jj];
-                for (int s = 0; s < r; ++s) u -= sm.L[r][s] * sm.U[s][jj];
-                sm.U[r][jj] = u;
-            }
-        } else if (tid >= kWave && tid < kWave + VT) {
-            const int jj = tid - kWave;
-            for (int s = C - 1; s >= 0; --s) {
-                float u = sm.R[s][jj];
-                for (int r = s + 1; r < C; ++r) u -= sm.L[r][s] * sm.dU[r][jj];
-                sm.dU[s][jj] = u;
-            }
-        }
+        if (tid < VT) solve_lower(sm.L, sm.X, sm.U, tid);   // U, one column per thread
+        else if (tid >= kWave && tid < kWave + VT)          // dU, on another wave
+            solve_upper_t(sm.L, sm.R, sm.dU, tid - kWave);
         __syncthreads();
         {
             const float du = sm.dU[t][j];
@@ -749,7 +812,7 @@ __global__ __launch_bounds__(NT) void kda_bwd_grads_kernel(GdnBwdArgs a) {
 }
 
 struct GdnLayout {
-    size_t Sck, dSck, total;
+    size_t Sck, dSck, Tck, Pck, total;
 };
 GdnLayout gdn_layout(const Problem& p) {
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
@@ -757,7 +820,9 @@ GdnLayout gdn_layout(const Problem& p) {
     GdnLayout L{};
     L.Sck = 0;
     L.dSck = al(nseq * nchunks * p.dk * p.dv * 4);
-    L.total = L.dSck + al(nseq * nchunks * p.dk * p.dv * 4);
+    L.Tck = L.dSck + al(nseq * nchunks * p.dk * p.dv * 4);
+    L.Pck = L.Tck + al(nseq * nchunks * C * C * 4);
+    L.total = L.Pck + al(nseq * nchunks * C * C * 4);
     return L;
 }
 
@@ -766,15 +831,19 @@ hipError_t launch_dims(const Problem& p, GdnBwdArgs a) {
     const unsigned chains = unsigned(2 * a.nseq * a.ntiles);
     const unsigned units = unsigned(size_t(a.nseq) * a.nchunks);
     if (p.variant == LA_KDA) {
-        kda_bwd_chains_kernel<DK, DV><<<dim3(chains), dim3(NT), 0, p.stream>>>(a);
+        kda_bwd_prep_kernel<DK><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        kda_bwd_chains_kernel<DK, DV><<<dim3(chains), dim3(NT), 0, p.stream>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
         kda_bwd_grads_kernel<DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
         return hipGetLastError();
     }
-    gdn_bwd_chains_kernel<DK, DV><<<dim3(chains), dim3(NT), 0, p.stream>>>(a);
+    gdn_bwd_prep_kernel<DK><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    gdn_bwd_chains_kernel<DK, DV><<<dim3(chains), dim3(NT), 0, p.stream>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     gdn_bwd_grads_kernel<DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
     return hipGetLastError();
 }
@@ -812,6 +881,8 @@ hipError_t launch_backward_gdn(const BwdProblem& bp) {
     a.dS0 = bp.dS0;
     a.Sck = reinterpret_cast<float*>(ws + L.Sck);
     a.dSck = reinterpret_cast<float*>(ws + L.dSck);
+    a.Tck = reinterpret_cast<float*>(ws + L.Tck);
+    a.Pck = reinterpret_cast<float*>(ws + L.Pck);
     a.N = p.N;
     a.nseq = int(nseq);
     a.ntiles = p.dv / VT;
