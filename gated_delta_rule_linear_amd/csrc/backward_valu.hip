@@ -37,9 +37,11 @@
 // = do_t / den_t and dL/dden_t = -(do_t . o_t) / den_t; the normaliser z is a state column
 // whose value is 1 and whose output gradient is dL/dden, so the augmented state [S, z]
 // follows S_t = S_{t-1} + phi(k_t) [v_t, 1]^T and the GLA formulas with dO = [dnum, dden]
-// give dphi(q), dphi(k), dv, dS0 and dz0 at once. The forward is recomputed first (the fp32
-// prefill, which also hands back den_t) to form dnum and dden; the chain rule through phi
-// is phi'(x) = min(phi(x), 1).
+// give dphi(q), dphi(k), dv, dS0 and dz0 at once. dnum and dden need the forward's num_t
+// and den_t, so the sums and scans run in two halves: the state half first (S_in and z_in of
+// every chunk), then a kernel that forms num_t and den_t of every chunk in parallel from them
+// and writes dnum and dden, then the gradient half. The chain rule through phi is phi'(x) =
+// min(phi(x), 1).
 #include "common.hpp"
 #include "la_internal.h"
 
@@ -58,6 +60,8 @@ struct BwdArgs {
     const float *dnum, *dden;   // KATH: dL/dnum [tokens][DV] and dL/dden [tokens] (fp32)
     const float *z0, *dzf;      // KATH: initial normaliser and its final gradient, or null
     float* dz0;                 // KATH
+    float eps;                  // KATH
+    int mode;                   // sums and scans: bit 0 the state half, bit 1 the gradient half
     float* Sst;      // [nseq][nchunks][DK][DV]: dS_c, then S_in (in place)
     float* dSt;      // [nseq][nchunks][DK][DV]: G_c, then dS_out (in place)
     float* ac;       // [nseq][nchunks][DK] (GLA) or [nseq][nchunks] (SSD): chunk decay
@@ -203,8 +207,8 @@ __global__ __launch_bounds__(NT) void bwd_sums_kernel(BwdArgs a) {
             ds += EK(s_, i) * sm.k[s_][i] * sm.v[s_][c];
             gq += EQ(s_, i) * sm.q[s_][i] * sm.dO[s_][c];
         }
-        a.Sst[sbase + size_t(i) * SW + c0 + c] = ds;
-        a.dSt[sbase + size_t(i) * SW + c0 + c] = gq;
+        if (a.mode & 1) a.Sst[sbase + size_t(i) * SW + c0 + c] = ds;
+        if (a.mode & 2) a.dSt[sbase + size_t(i) * SW + c0 + c] = gq;
     }
     if (u.tile == 0) {
         float* ac = a.ac + (u.seq * a.nchunks + u.ch) * (SG ? 1 : DK);
@@ -240,11 +244,12 @@ __global__ __launch_bounds__(NT) void bwd_scans_kernel(BwdArgs a) {
         if (a.z0) S = a.z0[ez];
         if (a.dzf) dS = a.dzf[ez];
     }
-    for (int ch = 0; ch < a.nchunks; ++ch) {
+    for (int ch = 0; (a.mode & 1) && ch < a.nchunks; ++ch) {
         const float d = Ss[ch * stride];
         Ss[ch * stride] = S;
         S = ac[ch * (SG ? 1 : DK)] * S + d;
     }
+    if (!(a.mode & 2)) return;
     for (int ch = a.nchunks - 1; ch >= 0; --ch) {
         const float gq = dSs[ch * stride];
         dSs[ch * stride] = dS;
@@ -424,29 +429,74 @@ __global__ __launch_bounds__(NT) void bwd_sum_kernel(BwdArgs a) {
     }
 }
 
-// KATH: dnum = dO / den and dden = -(dO . o) / den per token, one wave per token
-template <int DV>
-__global__ __launch_bounds__(NT) void kath_pre_kernel(BwdArgs a, const void* o, const float* den,
-                                                      float* dnum, float* dden, size_t ntok) {
-    const size_t tok = size_t(blockIdx.x) * (NT / kWave) + threadIdx.x / kWave;
-    const int lane = threadIdx.x % kWave;
-    if (tok >= ntok) return;   // a whole wave leaves together
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<0xB1, 0xf, 0xf>(v);
+    v += dpp_f<0x4E, 0xf, 0xf>(v);
+    v += dpp_f<0x141, 0xf, 0xf>(v);
+    v += dpp_f<0x140, 0xf, 0xf>(v);
+    return v;
+}
+
+// KATH: the forward's num_t and den_t of every chunk, from the chunk-entering state and
+// normaliser (the state half of the scans), then dnum = dO / den and dden = -(dO . num) /
+// den^2. One workgroup per (sequence, chunk), looping over the value tiles.
+template <int DK, int DV>
+__global__ __launch_bounds__(NT) void kath_out_kernel(BwdArgs a) {
+    constexpr int SW = DV + VT;
+    __shared__ float sq[C][DK + 1], sk[C][DK + 1];
+    __shared__ float sP[C][C + 1], sS[DK][VT + 1], sz[DK];
+    __shared__ float sv[C][VT], sdO[C][VT], sden[C];
+    const int tid = threadIdx.x;
+    const int ch = int(blockIdx.x % unsigned(a.nchunks));
+    const size_t seq = blockIdx.x / unsigned(a.nchunks);
+    const int t0 = ch * C, n = min(C, a.N - t0);
+    const size_t tok = seq * size_t(a.N) + t0;
     const bool iob = a.io_bf16 != 0;
-    const float dn = den[tok];
-    float w = 0.f;
-    for (int j = lane; j < DV; j += kWave) {
-        const size_t e = tok * DV + j;
-        const float d = load_elem(a.dO, e, iob);
-        w += d * load_elem(o, e, iob);
-        dnum[e] = d / dn;
+    const size_t sbase = (seq * a.nchunks + ch) * size_t(DK) * SW;
+    for (int idx = tid; idx < C * DK; idx += NT) {
+        const int r = idx / DK, i = idx % DK;
+        const size_t e = (tok + r) * DK + i;
+        sq[r][i] = r < n ? elu_plus_one(load_elem(a.q, e, iob)) : 0.f;
+        sk[r][i] = r < n ? elu_plus_one(load_elem(a.k, e, iob)) : 0.f;
     }
-    w = wave_sum(w);
-    if (lane == 0) dden[tok] = -w / dn;
+    for (int i = tid; i < DK; i += NT) sz[i] = a.Sst[sbase + size_t(i) * SW + DV];
+    __syncthreads();
+    const int t = tid / C, x = tid % C;   // (row, column) of the 16 x 16 maps
+    {
+        float p = 0.f, zq = 0.f;
+        if (x <= t)
+            for (int i = 0; i < DK; ++i) p += sq[t][i] * sk[x][i];
+        sP[t][x] = p;
+        for (int i = x; i < DK; i += C) zq += sq[t][i] * sz[i];
+        const float den = row16_sum(zq + p) + a.eps;   // phi(q_t).z_in + sum_s P_ts + eps
+        if (x == 0) sden[t] = den;
+    }
+    float w = 0.f;   // dO_t . num_t (lane x == 0 of row t)
+    for (int c0 = 0; c0 < DV; c0 += VT) {
+        __syncthreads();
+        for (int idx = tid; idx < DK * VT; idx += NT) {
+            const int i = idx / VT, j = idx % VT;
+            sS[i][j] = a.Sst[sbase + size_t(i) * SW + c0 + j];
+        }
+        {
+            const size_t e = (tok + t) * DV + c0 + x;
+            sv[t][x] = t < n ? load_elem(a.v, e, iob) : 0.f;
+            sdO[t][x] = t < n ? load_elem(a.dO, e, iob) : 0.f;
+        }
+        __syncthreads();
+        float num = 0.f;
+        for (int i = 0; i < DK; ++i) num += sq[t][i] * sS[i][x];
+        for (int s2 = 0; s2 <= t; ++s2) num += sP[t][s2] * sv[s2][x];
+        const float d = sdO[t][x];
+        w += row16_sum(d * num);
+        if (t < n) const_cast<float*>(a.dnum)[(tok + t) * DV + c0 + x] = d / sden[t];
+    }
+    if (x == 0 && t < n) const_cast<float*>(a.dden)[tok + t] = -w / (sden[t] * sden[t]);
 }
 
 struct BwdLayout {
     size_t Sst, dSt, ac, dqp, dkp, dgp;
-    size_t o, den, Sf, zf, dnum, dden;   // KATH only
+    size_t dnum, dden;   // KATH only
     size_t total;
 };
 BwdLayout bwd_layout(const Problem& p) {
@@ -464,10 +514,6 @@ BwdLayout bwd_layout(const Problem& p) {
     L.dkp = off; off += al(ntiles * ntok * p.dk * 4);
     L.dgp = off; off += ka ? 0 : al(ntiles * ntok * p.dk * 4);
     if (ka) {
-        L.o = off; off += al(ntok * p.dv * 4);
-        L.den = off; off += al(ntok * 4);
-        L.Sf = off; off += al(nseq * p.dk * p.dv * 4);
-        L.zf = off; off += al(nseq * p.dk * 4);
         L.dnum = off; off += al(ntok * p.dv * 4);
         L.dden = off; off += al(ntok * 4);
     }
@@ -480,27 +526,26 @@ hipError_t launch_dims(const Problem& p, BwdArgs a) {
     constexpr int SW = state_width<VAR, DV>();
     const size_t ntok = size_t(a.nseq) * a.N;
     hipError_t e;
-    if constexpr (VAR == LA_KATH) {
-        // recompute the forward for o and the denominators, then dnum and dden
-        const BwdLayout L = bwd_layout(p);
-        unsigned char* ws = static_cast<unsigned char*>(p.ws);
-        Problem f = p;
-        f.o = ws + L.o;
-        f.S = reinterpret_cast<float*>(ws + L.Sf);
-        f.z = reinterpret_cast<float*>(ws + L.zf);
-        f.den = reinterpret_cast<float*>(ws + L.den);
-        f.path = LA_PATH_VALU;
-        if ((e = launch_prefill_valu(f)) != hipSuccess) return e;
-        const size_t blocks = (ntok + NT / kWave - 1) / (NT / kWave);
-        kath_pre_kernel<DV><<<dim3(unsigned(blocks)), dim3(NT), 0, p.stream>>>(
-            a, f.o, f.den, const_cast<float*>(a.dnum), const_cast<float*>(a.dden), ntok);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
     const unsigned units = unsigned(size_t(a.nseq) * a.nchunks * a.ntiles);
+    const size_t nel = size_t(a.nseq) * DK * SW;
+    const dim3 scan_grid(unsigned((nel + NT - 1) / NT));
+    if constexpr (VAR == LA_KATH) {
+        // the state half, then dnum and dden from the forward's num and den, then the rest
+        a.mode = 1;
+        bwd_sums_kernel<VAR, DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        bwd_scans_kernel<VAR, DK, DV><<<scan_grid, dim3(NT), 0, p.stream>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        kath_out_kernel<DK, DV><<<dim3(unsigned(size_t(a.nseq) * a.nchunks)), dim3(NT), 0,
+                                  p.stream>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        a.mode = 2;
+    } else {
+        a.mode = 3;
+    }
     bwd_sums_kernel<VAR, DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const size_t nel = size_t(a.nseq) * DK * SW;
-    bwd_scans_kernel<VAR, DK, DV><<<dim3(unsigned((nel + NT - 1) / NT)), dim3(NT), 0, p.stream>>>(a);
+    bwd_scans_kernel<VAR, DK, DV><<<scan_grid, dim3(NT), 0, p.stream>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     bwd_grads_kernel<VAR, DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -591,6 +636,7 @@ hipError_t launch_backward(const BwdProblem& bp) {
         a.z0 = p.z0;
         a.dzf = bp.dz_final;
         a.dz0 = bp.dz0;
+        a.eps = p.eps;
     }
     a.N = p.N;
     a.nseq = int(nseq);

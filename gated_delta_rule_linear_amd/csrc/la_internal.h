@@ -33,7 +33,6 @@ struct Problem {
     void* ws = nullptr;
     size_t ws_bytes = 0;
     hipStream_t stream = nullptr;
-    float* den = nullptr;     // KATH, fp32 prefill only: per-token denominators, or null
 };
 
 constexpr int kValuChunk = 16;

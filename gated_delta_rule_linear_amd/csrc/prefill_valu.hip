@@ -54,7 +54,6 @@ struct ValuArgs {
     int io_bf16, gate_bf16;
     const int32_t* cu;   // packed variable-length batch, or null
     int H, L;
-    float* den;          // KATH: per-token denominators (for the backward), or null
 };
 
 template <int VAR, int DK, int DV>
@@ -213,11 +212,7 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
                 psum += p;
             }
             float out = acc + intra;
-            if (VAR == LA_KATH) {
-                const float den = sden[r] + psum + a.eps;
-                out = out / den;
-                if (a.den && tile == 0 && c == 0 && r < n) a.den[tok0 + t0 + r] = den;
-            }
+            if (VAR == LA_KATH) out = out / (sden[r] + psum + a.eps);
             if (r < n) store_elem(a.o, (tok0 + t0 + r) * DV + c0 + c, out, iob);
         }
         __syncthreads();  // all reads of the old state are done
@@ -303,7 +298,7 @@ __global__ void state_init_kernel(const float* S0, const float* z0, float* S, fl
 
 hipError_t launch_prefill_valu(const Problem& p) {
     ValuArgs a{p.q, p.k, p.v, p.g, p.beta, p.S0, p.z0, p.o, p.S, p.z, p.N, 1, p.eps,
-               p.io_bf16, p.gate_bf16, p.cu, p.H, p.L, p.den};
+               p.io_bf16, p.gate_bf16, p.cu, p.H, p.L};
     switch (p.variant) {
         case LA_KATH: return dispatch_dk<LA_KATH>(p, a);
         case LA_GLA: return dispatch_dk<LA_GLA>(p, a);
