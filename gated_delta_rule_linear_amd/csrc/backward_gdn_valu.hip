@@ -185,94 +185,177 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(GdnBwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------- chains
-template <int DK>
+// Both chains of GDN and KDA. Each workgroup walks one (sequence, 16-column value tile) in
+// order, forward for the states entering the chunks or in reverse for the gradients leaving
+// them. The tile stays in registers: thread (g, j) holds rows g*RG .. g*RG+RG-1 of column j.
+// Per chunk: the rows' partial dot products with the chunk's (decayed) keys go through a
+// padded LDS buffer to give k_t . S[:, j]; then the right-hand side, U = T X (or dU = T^T R),
+// and the update of the thread's own rows from the keys (and queries) read as broadcast rows.
+template <int VAR, int DK>
 struct ChainSmem {
-    Rows<DK> rw;
-    float S[DK][VT + 1];    // state (forward) or state gradient (reverse) tile
-    float x[C][VT];         // v (forward) or dO (reverse) tile
-    float L[C][C + 1], P[C][C + 1];
-    float rhs[C][VT], u[C][VT];
+    static constexpr bool PK = VAR == LA_KDA;   // a decay per key dim
+    static constexpr int KP = DK + 4;           // row pitch: 16-byte aligned rows
+    float k[C][KP];   // GDN k; KDA k 2^b (after the table step)
+    float q[C][KP];   // reverse: GDN q; KDA q 2^b
+    float kt[PK ? C : 1][PK ? KP : 1];   // KDA: k 2^(b_last - b)
+    union {
+        float bq[PK ? C : 1][PK ? KP : 1];   // KDA: cumulative base-2 log gates
+        float red[C][16 * VT + 16];          // partials over the 16 row groups (padded rows)
+    } w;
+    float T[C][C + 1], P[C][C + 1];
+    float x[C][VT], rhs[C][VT], u[C][VT];
+    float eg[C], el[C], b[C];   // GDN 2^c_r, 2^(c_last - c_r); beta
+    float dl[PK ? DK : 1];      // KDA 2^b_last per key dim
 };
 
-// (at most 128 registers: four waves per SIMD keep every chain of a typical launch resident)
-template <int DK, int DV>
-__global__ __launch_bounds__(NT, 4) void gdn_bwd_chains_kernel(GdnBwdArgs a) {
-    __shared__ ChainSmem<DK> sm;
+template <int VAR, int DK, int DV>
+__global__ __launch_bounds__(NT, 2) void bwd_chains_kernel(GdnBwdArgs a) {
+    constexpr bool PK = VAR == LA_KDA;
+    constexpr int RG = DK / 16;   // rows per thread
+    static_assert(DK % 16 == 0, "16 row groups");
+    __shared__ ChainSmem<VAR, DK> sm;
     const int tid = threadIdx.x;
     const int nfw = a.nseq * a.ntiles;
     const bool rev = int(blockIdx.x) >= nfw;
     const int unit = rev ? int(blockIdx.x) - nfw : int(blockIdx.x);
     const size_t seq = size_t(unit / a.ntiles);
     const int c0 = (unit % a.ntiles) * VT;
-    const bool iob = a.io_bf16 != 0;
+    const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
+    const int grp = tid / VT, j = tid % VT, i0 = grp * RG;   // this thread's rows and column
+    const int t_me = tid / VT;                                // row of the (t, j) maps
     const size_t sbase = seq * DK * DV;
     const float* init = rev ? a.dSf : a.S0;
-    for (int idx = tid; idx < DK * VT; idx += NT) {
-        const int i = idx / VT, j = idx % VT;
-        sm.S[i][j] = init ? init[sbase + size_t(i) * DV + c0 + j] : 0.f;
-    }
+    float S[RG];
+#pragma unroll
+    for (int m = 0; m < RG; ++m) S[m] = init ? init[sbase + size_t(i0 + m) * DV + c0 + j] : 0.f;
     float* ck = (rev ? a.dSck : a.Sck) + seq * size_t(a.nchunks) * DK * DV;
-    const int r_me = tid / VT, j_me = tid % VT;
     for (int it = 0; it < a.nchunks; ++it) {
         const int ch = rev ? a.nchunks - 1 - it : it;
         const int t0 = ch * C, n = min(C, a.N - t0);
         const size_t tok = seq * size_t(a.N) + t0;
-        __syncthreads();   // the previous chunk's update and its readers are done
+        __syncthreads();   // the previous chunk's readers are done
         float* ckc = ck + size_t(ch) * DK * DV;
-        for (int idx = tid; idx < DK * VT; idx += NT) {
-            const int i = idx / VT, j = idx % VT;
-            ckc[size_t(i) * DV + c0 + j] = sm.S[i][j];
+#pragma unroll
+        for (int m = 0; m < RG; ++m) ckc[size_t(i0 + m) * DV + c0 + j] = S[m];
+        for (int idx = tid; idx < C * DK; idx += NT) {
+            const int r = idx / DK, i = idx % DK;
+            const size_t e = (tok + r) * DK + i;
+            const bool in = r < n;
+            sm.k[r][i] = in ? load_elem(a.k, e, iob) : 0.f;
+            if (rev) sm.q[r][i] = in ? load_elem(a.q, e, iob) : 0.f;
+            if (PK) sm.w.bq[r][i] = in ? __builtin_amdgcn_logf(load_elem(a.g, e, gb)) : 0.f;
         }
-        if (rev) load_rows<DK, true>(sm.rw, a, tok, n);
-        else load_rows<DK, false>(sm.rw, a, tok, n);
-        sm.x[r_me][j_me] = r_me < n ? load_elem(rev ? a.dO : a.v, (tok + r_me) * DV + c0 + j_me, iob)
-                                    : 0.f;
+        if (!PK) {
+            if (tid < kWave) {   // one wave: log gates, their prefix sums, beta
+                const int r = tid;
+                float lg = 0.f, bt = 0.f;
+                if (r < n) {
+                    lg = __builtin_amdgcn_logf(load_elem(a.g, tok + r, gb));
+                    bt = load_elem(a.beta, tok + r, gb);
+                }
+                const float cs = wave_inclusive_scan(r < C ? lg : 0.f);
+                const float cl = __shfl(cs, C - 1);
+                if (r < C) {
+                    sm.b[r] = bt;
+                    sm.eg[r] = __builtin_amdgcn_exp2f(cs);
+                    sm.el[r] = __builtin_amdgcn_exp2f(cl - cs);
+                }
+            }
+        } else if (tid < C) {
+            sm.b[tid] = tid < n ? load_elem(a.beta, tok + tid, gb) : 0.f;
+        }
+        sm.x[t_me][j] = t_me < n ? load_elem(rev ? a.dO : a.v, (tok + t_me) * DV + c0 + j, iob) : 0.f;
         {
             const size_t off = (seq * a.nchunks + ch) * size_t(C * C);
-            sm.L[tid / C][tid % C] = a.Tck[off + tid];   // T
+            sm.T[tid / C][tid % C] = a.Tck[off + tid];
             if (rev) sm.P[tid / C][tid % C] = a.Pck[off + tid];
         }
         __syncthreads();
-        float ks = 0.f;   // thread (r, j): k_r . S[:, j]
-#pragma unroll 8
-        for (int i = 0; i < DK; ++i) ks += sm.rw.k[r_me][i] * sm.S[i][j_me];
-        if (!rev) {
-            sm.rhs[r_me][j_me] = sm.rw.b[r_me] * (sm.x[r_me][j_me] - sm.rw.eg[r_me] * ks);
-        } else {
-            float acc = sm.rw.el[r_me] * ks;
-            for (int t = r_me; t < C; ++t) acc += sm.P[t][r_me] * sm.x[t][j_me];
-            sm.rhs[r_me][j_me] = acc;
+        if (PK) {   // prefix sums per key dim, then the decayed key (and query) rows
+            for (int i = tid; i < DK; i += NT) {
+                float acc = 0.f;
+                for (int r = 0; r < C; ++r) {
+                    acc += sm.w.bq[r][i];
+                    sm.w.bq[r][i] = acc;
+                }
+                sm.dl[i] = __builtin_amdgcn_exp2f(acc);
+            }
+            __syncthreads();
+            for (int idx = tid; idx < C * DK; idx += NT) {   // each element owned by one thread
+                const int r = idx / DK, i = idx % DK;
+                const float br = sm.w.bq[r][i], eb = __builtin_amdgcn_exp2f(br);
+                const float kv = sm.k[r][i];
+                sm.kt[r][i] = kv * __builtin_amdgcn_exp2f(sm.w.bq[C - 1][i] - br);
+                sm.k[r][i] = kv * eb;
+                if (rev) sm.q[r][i] *= eb;
+            }
+            __syncthreads();
+        }
+        {   // partial k_t . S[:, j] over this thread's rows, for every row t of the chunk
+            constexpr int KP = ChainSmem<VAR, DK>::KP;
+            const float* kk = (PK && rev) ? &sm.kt[0][0] : &sm.k[0][0];
+#pragma unroll
+            for (int t = 0; t < C; ++t) {
+                float p = 0.f;
+#pragma unroll
+                for (int m = 0; m < RG; ++m) p += kk[t * KP + i0 + m] * S[m];
+                sm.w.red[t][grp * VT + j] = p;
+            }
+        }
+        __syncthreads();
+        {   // thread (t, j): the right-hand side
+            const int t = t_me;
+            float ks = 0.f;
+#pragma unroll
+            for (int g2 = 0; g2 < 16; ++g2) ks += sm.w.red[t][g2 * VT + j];
+            float rhs;
+            if (!rev) {
+                rhs = sm.b[t] * (sm.x[t][j] - (PK ? ks : sm.eg[t] * ks));
+            } else {
+                rhs = PK ? ks : sm.el[t] * ks;
+                for (int r = t; r < C; ++r) rhs += sm.P[r][t] * sm.x[r][j];
+            }
+            sm.rhs[t][j] = rhs;
         }
         __syncthreads();
         {   // U = T X (forward) or dU = T^T R (reverse)
+            const int t = t_me;
             float acc = 0.f;
             if (!rev) {
-                for (int s2 = 0; s2 <= r_me; ++s2) acc += sm.L[r_me][s2] * sm.rhs[s2][j_me];
+                for (int s2 = 0; s2 <= t; ++s2) acc += sm.T[t][s2] * sm.rhs[s2][j];
             } else {
-                for (int t = r_me; t < C; ++t) acc += sm.L[t][r_me] * sm.rhs[t][j_me];
+                for (int r = t; r < C; ++r) acc += sm.T[r][t] * sm.rhs[r][j];
             }
-            sm.u[r_me][j_me] = acc;
+            sm.u[t][j] = acc;
         }
         __syncthreads();
-        const float dl = sm.rw.eg[C - 1];
-        for (int idx = tid; idx < DK * VT; idx += NT) {
-            const int i = idx / VT, j = idx % VT;
-            float acc = 0.f;
+        {   // the update of this thread's rows
+            float acc[RG];
+#pragma unroll
+            for (int m = 0; m < RG; ++m) acc[m] = 0.f;
             if (!rev) {
-                for (int s = 0; s < C; ++s) acc += sm.rw.k[s][i] * sm.rw.el[s] * sm.u[s][j];
+#pragma unroll 4
+                for (int s2 = 0; s2 < C; ++s2) {
+                    const float us = PK ? sm.u[s2][j] : sm.u[s2][j] * sm.el[s2];
+#pragma unroll
+                    for (int m = 0; m < RG; ++m) acc[m] += (PK ? sm.kt[s2][i0 + m] : sm.k[s2][i0 + m]) * us;
+                }
             } else {
-                for (int r = 0; r < C; ++r)
-                    acc += sm.rw.eg[r] * (sm.rw.q[r][i] * sm.x[r][j] - sm.rw.b[r] * sm.rw.k[r][i] * sm.u[r][j]);
+#pragma unroll 4
+                for (int r = 0; r < C; ++r) {
+                    const float xs = PK ? sm.x[r][j] : sm.x[r][j] * sm.eg[r];
+                    const float us = PK ? sm.b[r] * sm.u[r][j] : sm.b[r] * sm.eg[r] * sm.u[r][j];
+#pragma unroll
+                    for (int m = 0; m < RG; ++m) acc[m] += sm.q[r][i0 + m] * xs - sm.k[r][i0 + m] * us;
+                }
             }
-            sm.S[i][j] = dl * sm.S[i][j] + acc;
+#pragma unroll
+            for (int m = 0; m < RG; ++m) S[m] = (PK ? sm.dl[i0 + m] : sm.eg[C - 1]) * S[m] + acc[m];
         }
     }
     if (rev) {
-        __syncthreads();
-        for (int idx = tid; idx < DK * VT; idx += NT) {
-            const int i = idx / VT, j = idx % VT;
-            a.dS0[sbase + size_t(i) * DV + c0 + j] = sm.S[i][j];
-        }
+#pragma unroll
+        for (int m = 0; m < RG; ++m) a.dS0[sbase + size_t(i0 + m) * DV + c0 + j] = S[m];
     }
 }
 
@@ -525,106 +608,6 @@ __global__ __launch_bounds__(NT) void kda_bwd_prep_kernel(GdnBwdArgs a) {
 }
 
 template <int DK>
-struct ChainSmemK {
-    RowsK<DK> rw;           // k and q are replaced in place by k_r 2^b_r and q_r 2^b_r
-    float kt[C][DK + 1];    // k_r 2^(b_last - b_r)
-    float S[DK][VT + 1];
-    float x[C][VT];
-    float L[C][C + 1], P[C][C + 1];
-    float rhs[C][VT], u[C][VT];
-};
-
-template <int DK, int DV>
-__global__ __launch_bounds__(NT) void kda_bwd_chains_kernel(GdnBwdArgs a) {
-    __shared__ ChainSmemK<DK> sm;
-    const int tid = threadIdx.x;
-    const int nfw = a.nseq * a.ntiles;
-    const bool rev = int(blockIdx.x) >= nfw;
-    const int unit = rev ? int(blockIdx.x) - nfw : int(blockIdx.x);
-    const size_t seq = size_t(unit / a.ntiles);
-    const int c0 = (unit % a.ntiles) * VT;
-    const bool iob = a.io_bf16 != 0;
-    const size_t sbase = seq * DK * DV;
-    const float* init = rev ? a.dSf : a.S0;
-    for (int idx = tid; idx < DK * VT; idx += NT) {
-        const int i = idx / VT, j = idx % VT;
-        sm.S[i][j] = init ? init[sbase + size_t(i) * DV + c0 + j] : 0.f;
-    }
-    float* ck = (rev ? a.dSck : a.Sck) + seq * size_t(a.nchunks) * DK * DV;
-    const int r_me = tid / VT, j_me = tid % VT;
-    for (int it = 0; it < a.nchunks; ++it) {
-        const int ch = rev ? a.nchunks - 1 - it : it;
-        const int t0 = ch * C, n = min(C, a.N - t0);
-        const size_t tok = seq * size_t(a.N) + t0;
-        __syncthreads();
-        float* ckc = ck + size_t(ch) * DK * DV;
-        for (int idx = tid; idx < DK * VT; idx += NT) {
-            const int i = idx / VT, j = idx % VT;
-            ckc[size_t(i) * DV + c0 + j] = sm.S[i][j];
-        }
-        if (rev) load_rows_kda<DK, true>(sm.rw, a, tok, n);
-        else load_rows_kda<DK, false>(sm.rw, a, tok, n);
-        sm.x[r_me][j_me] = r_me < n ? load_elem(rev ? a.dO : a.v, (tok + r_me) * DV + c0 + j_me, iob)
-                                    : 0.f;
-        __syncthreads();
-        for (int idx = tid; idx < C * DK; idx += NT) {   // each element read and written by one thread
-            const int r = idx / DK, i = idx % DK;
-            const float br = sm.rw.bq[r][i], eb = __builtin_amdgcn_exp2f(br);
-            const float kv = sm.rw.k[r][i];
-            sm.kt[r][i] = kv * __builtin_amdgcn_exp2f(sm.rw.bq[C - 1][i] - br);
-            sm.rw.k[r][i] = kv * eb;
-            if (rev) sm.rw.q[r][i] *= eb;
-        }
-        {
-            const size_t off = (seq * a.nchunks + ch) * size_t(C * C);
-            sm.L[tid / C][tid % C] = a.Tck[off + tid];   // T
-            if (rev) sm.P[tid / C][tid % C] = a.Pck[off + tid];
-        }
-        __syncthreads();
-        float ks = 0.f;   // thread (r, j): (k_r 2^b_r) . S[:, j], or (k_r 2^(b_last - b_r)) . dS[:, j]
-        if (!rev) {
-#pragma unroll 8
-            for (int i = 0; i < DK; ++i) ks += sm.rw.k[r_me][i] * sm.S[i][j_me];
-            sm.rhs[r_me][j_me] = sm.rw.b[r_me] * (sm.x[r_me][j_me] - ks);
-        } else {
-#pragma unroll 8
-            for (int i = 0; i < DK; ++i) ks += sm.kt[r_me][i] * sm.S[i][j_me];
-            for (int t = r_me; t < C; ++t) ks += sm.P[t][r_me] * sm.x[t][j_me];
-            sm.rhs[r_me][j_me] = ks;
-        }
-        __syncthreads();
-        {   // U = T X (forward) or dU = T^T R (reverse)
-            float acc = 0.f;
-            if (!rev) {
-                for (int s2 = 0; s2 <= r_me; ++s2) acc += sm.L[r_me][s2] * sm.rhs[s2][j_me];
-            } else {
-                for (int t = r_me; t < C; ++t) acc += sm.L[t][r_me] * sm.rhs[t][j_me];
-            }
-            sm.u[r_me][j_me] = acc;
-        }
-        __syncthreads();
-        for (int idx = tid; idx < DK * VT; idx += NT) {
-            const int i = idx / VT, j = idx % VT;
-            float acc = 0.f;
-            if (!rev) {
-                for (int s = 0; s < C; ++s) acc += sm.kt[s][i] * sm.u[s][j];
-            } else {
-                for (int r = 0; r < C; ++r)
-                    acc += sm.rw.q[r][i] * sm.x[r][j] - sm.rw.b[r] * sm.rw.k[r][i] * sm.u[r][j];
-            }
-            sm.S[i][j] = __builtin_amdgcn_exp2f(sm.rw.bq[C - 1][i]) * sm.S[i][j] + acc;
-        }
-    }
-    if (rev) {
-        __syncthreads();
-        for (int idx = tid; idx < DK * VT; idx += NT) {
-            const int i = idx / VT, j = idx % VT;
-            a.dS0[sbase + size_t(i) * DV + c0 + j] = sm.S[i][j];
-        }
-    }
-}
-
-template <int DK>
 struct GradSmemK {
     RowsK<DK> rw;
     float L[C][C + 1], Lt[C][C + 1], P[C][C + 1], A[C][C + 1], Bm[C][C + 1];
@@ -834,7 +817,7 @@ hipError_t launch_dims(const Problem& p, GdnBwdArgs a) {
         kda_bwd_prep_kernel<DK><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        kda_bwd_chains_kernel<DK, DV><<<dim3(chains), dim3(NT), 0, p.stream>>>(a);
+        bwd_chains_kernel<LA_KDA, DK, DV><<<dim3(chains), dim3(NT), 0, p.stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         kda_bwd_grads_kernel<DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
         return hipGetLastError();
@@ -842,7 +825,7 @@ hipError_t launch_dims(const Problem& p, GdnBwdArgs a) {
     gdn_bwd_prep_kernel<DK><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    gdn_bwd_chains_kernel<DK, DV><<<dim3(chains), dim3(NT), 0, p.stream>>>(a);
+    bwd_chains_kernel<LA_GDN, DK, DV><<<dim3(chains), dim3(NT), 0, p.stream>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     gdn_bwd_grads_kernel<DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
     return hipGetLastError();
