@@ -72,7 +72,8 @@ struct GdnBwdArgs {
 // makes them identity steps.
 template <int DK>
 struct Rows {
-    float q[C][DK + 1], k[C][DK + 1];
+    alignas(16) float q[C][DK + 4];
+    alignas(16) float k[C][DK + 4];
     float c[C], b[C];
     float eg[C];    // 2^c_r (decay from the chunk start through row r)
     float el[C];    // 2^(c_last - c_r) (decay after row r to the chunk end)
@@ -367,13 +368,29 @@ struct GradSmem {
     float D[C][C + 1];           // 2^(c_r - c_s), s <= r; 0 above
     float Dm[C][C + 1];          // 2^(c_{t-1} - c_s), s < t; 0 elsewhere
     float KK[C][C + 1], QK[C][C + 1], L[C][C + 1];
-    float S0[DK][VT + 1], dS[DK][VT + 1];
-    float v[C][VT], dO[C][VT];
-    float KS[C][VT], X[C][VT], R[C][VT], U[C][VT], dU[C][VT];
+    alignas(16) float S0[DK][VT + 4];   // 16-byte aligned rows
+    alignas(16) float dS[DK][VT + 4];
+    alignas(16) float v[C][VT];
+    alignas(16) float dO[C][VT];
+    alignas(16) float U[C][VT];
+    alignas(16) float dU[C][VT];
+    float KS[C][VT], X[C][VT], R[C][VT];
     float A[C][C + 1], Bm[C][C + 1];
     float kap[C], rho[C], mu[C], dup[C];
     float sig[NT / kWave];
 };
+
+// Dot product of two 16-float LDS rows (16-byte aligned) read as float4.
+__device__ __forceinline__ float dot16(const float* x, const float* y) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; c += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(x + c);
+        const float4 b = *reinterpret_cast<const float4*>(y + c);
+        acc += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+    }
+    return acc;
+}
 
 __device__ __forceinline__ float row16_sum(float v) {
     v += dpp_f<0xB1, 0xf, 0xf>(v);
@@ -420,30 +437,48 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_kernel(GdnBwdArgs a) {
     float kap = 0.f, rho = 0.f, mu = 0.f, dbt = 0.f, dup = 0.f;  // row r_me (lane x_me == 0)
     float sig = 0.f;
     const size_t ckoff = (seq * a.nchunks + ch) * size_t(DK) * DV;
+    // the next tile's state tiles, v and dO are loaded into registers while this one works
+    constexpr int MS = DK * VT / NT;
+    float pS0[MS], pdS[MS], pv, pdO;
+    auto fetch = [&](int tile) {
+        const int c0 = tile * VT;
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int idx = tid + NT * m, i = idx / VT, j = idx % VT;
+            const size_t e = ckoff + size_t(i) * DV + c0 + j;
+            pS0[m] = a.Sck[e];
+            pdS[m] = a.dSck[e];
+        }
+        const size_t e = (tok + r_me) * DV + c0 + x_me;
+        pv = r_me < n ? load_elem(a.v, e, iob) : 0.f;
+        pdO = r_me < n ? load_elem(a.dO, e, iob) : 0.f;
+    };
+    fetch(0);
     for (int tile = 0; tile < a.ntiles; ++tile) {
         const int c0 = tile * VT;
-        __syncthreads();   // the previous tile's readers are done
-        for (int idx = tid; idx < DK * VT; idx += NT) {
-            const int i = idx / VT, j = idx % VT;
-            const size_t e = ckoff + size_t(i) * DV + c0 + j;
-            const float s0 = a.Sck[e], ds = a.dSck[e];
-            sm.S0[i][j] = s0;
-            sm.dS[i][j] = ds;
-            sig += s0 * ds;
+        lds_barrier();   // the previous tile's readers are done (loads stay in flight)
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int idx = tid + NT * m, i = idx / VT, j = idx % VT;
+            sm.S0[i][j] = pS0[m];
+            sm.dS[i][j] = pdS[m];
+            sig += pS0[m] * pdS[m];
         }
-        {
-            const int t = r_me, j = x_me;
-            const size_t e = (tok + t) * DV + c0 + j;
-            sm.v[t][j] = t < n ? load_elem(a.v, e, iob) : 0.f;
-            sm.dO[t][j] = t < n ? load_elem(a.dO, e, iob) : 0.f;
-        }
-        __syncthreads();
+        sm.v[r_me][x_me] = pv;
+        sm.dO[r_me][x_me] = pdO;
+        if (tile + 1 < a.ntiles) fetch(tile + 1);
+        lds_barrier();
         const int t = r_me, j = x_me;
         float ks = 0.f, kds = 0.f, qs = 0.f;
-        for (int i = 0; i < DK; ++i) {
-            ks += sm.rw.k[t][i] * sm.S0[i][j];
-            kds += sm.rw.k[t][i] * sm.dS[i][j];
-            qs += sm.rw.q[t][i] * sm.S0[i][j];
+#pragma unroll 4
+        for (int i = 0; i < DK; i += 4) {
+            const float4 kv = *reinterpret_cast<const float4*>(&sm.rw.k[t][i]);
+            const float4 qv = *reinterpret_cast<const float4*>(&sm.rw.q[t][i]);
+            const float s0[4] = {sm.S0[i][j], sm.S0[i + 1][j], sm.S0[i + 2][j], sm.S0[i + 3][j]};
+            const float d0[4] = {sm.dS[i][j], sm.dS[i + 1][j], sm.dS[i + 2][j], sm.dS[i + 3][j]};
+            ks += kv.x * s0[0] + kv.y * s0[1] + kv.z * s0[2] + kv.w * s0[3];
+            kds += kv.x * d0[0] + kv.y * d0[1] + kv.z * d0[2] + kv.w * d0[3];
+            qs += qv.x * s0[0] + qv.y * s0[1] + qv.z * s0[2] + qv.w * s0[3];
         }
         {
             float r_ = sm.rw.el[t] * kds;
@@ -452,11 +487,11 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_kernel(GdnBwdArgs a) {
             sm.X[t][j] = sm.rw.b[t] * (sm.v[t][j] - sm.rw.eg[t] * ks);
             sm.R[t][j] = r_;
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < VT) solve_lower(sm.L, sm.X, sm.U, tid);   // U, one column per thread
         else if (tid >= kWave && tid < kWave + VT)          // dU, on another wave
             solve_upper_t(sm.L, sm.R, sm.dU, tid - kWave);
-        __syncthreads();
+        lds_barrier();
         {
             const float u = sm.U[t][j], du = sm.dU[t][j];
             float p = sm.gm[t] * ks, ap = sm.rw.eg[t] * ks;
@@ -470,25 +505,20 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_kernel(GdnBwdArgs a) {
             const float s_mu = row16_sum(ks * du), s_db = row16_sum(du * (sm.v[t][j] - ap));
             const float s_dup = row16_sum(du * p);
             kap += s_kap; rho += s_rho; mu += s_mu; dbt += s_db; dup += s_dup;
-            float av = 0.f, bv = 0.f;   // (r_me, x_me) = (r, s)
-            for (int jj = 0; jj < VT; ++jj) {
-                av += sm.dO[r_me][jj] * sm.U[x_me][jj];
-                bv += sm.dU[r_me][jj] * sm.U[x_me][jj];
-            }
-            A_acc += av;
-            B_acc += bv;
+            A_acc += dot16(sm.dO[r_me], sm.U[x_me]);   // (r_me, x_me) = (r, s)
+            B_acc += dot16(sm.dU[r_me], sm.U[x_me]);
         }
+        {   // this thread's key dim i is the same for every m: its S0 and dS rows once
+            const int i = tid % DK;
 #pragma unroll
-        for (int m = 0; m < MQ; ++m) {
-            const int idx = tid + NT * m, tt = idx / DK, i = idx % DK;
-            float so = 0.f, su = 0.f, sdu = 0.f;
-            for (int jj = 0; jj < VT; ++jj) {
-                so += sm.S0[i][jj] * sm.dO[tt][jj];
-                su += sm.dS[i][jj] * sm.U[tt][jj];
-                sdu += sm.S0[i][jj] * sm.dU[tt][jj];
+            for (int m = 0; m < MQ; ++m) {
+                const int tt = (tid + NT * m) / DK;
+                const float so = dot16(sm.S0[i], sm.dO[tt]);
+                const float su = dot16(sm.dS[i], sm.U[tt]);
+                const float sdu = dot16(sm.S0[i], sm.dU[tt]);
+                accq[m] += sm.rw.eg[tt] * so;
+                acck[m] += sm.rw.el[tt] * su - sm.rw.b[tt] * sm.rw.eg[tt] * sdu;
             }
-            accq[m] += sm.rw.eg[tt] * so;
-            acck[m] += sm.rw.el[tt] * su - sm.rw.b[tt] * sm.rw.eg[tt] * sdu;
         }
     }
     // the column sums over all tiles
@@ -550,7 +580,9 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_kernel(GdnBwdArgs a) {
 // have gate 1, so their logs repeat the last real row's).
 template <int DK>
 struct RowsK {
-    float q[C][DK + 1], k[C][DK + 1], bq[C][DK + 1];
+    alignas(16) float q[C][DK + 4];
+    alignas(16) float k[C][DK + 4];
+    float bq[C][DK + 1];
     float b[C];
 };
 
@@ -611,11 +643,18 @@ template <int DK>
 struct GradSmemK {
     RowsK<DK> rw;
     float L[C][C + 1], Lt[C][C + 1], P[C][C + 1], A[C][C + 1], Bm[C][C + 1];
-    float v[C][VT], dO[C][VT], KS[C][VT], X[C][VT], R[C][VT], U[C][VT], dU[C][VT];
+    alignas(16) float v[C][VT];
+    alignas(16) float dO[C][VT];
+    alignas(16) float U[C][VT];
+    alignas(16) float dU[C][VT];
+    float KS[C][VT], X[C][VT], R[C][VT];
     float sig[DK];
     union {
-        struct {   // the tile loop
-            float S0[DK][VT + 1], dS[DK][VT + 1], kd[C][DK + 1], kt[C][DK + 1];
+        struct {   // the tile loop (16-byte aligned rows)
+            alignas(16) float S0[DK][VT + 4];
+            alignas(16) float dS[DK][VT + 4];
+            alignas(16) float kd[C][DK + 4];
+            alignas(16) float kt[C][DK + 4];
         } t;
         struct {   // after it: (S0 dO^T)^T, (dS' U^T)^T, (S0 dU^T)^T, rows by token
             float SDO[C][DK + 1], DSU[C][DK + 1], SDU[C][DK + 1];
@@ -659,17 +698,30 @@ __global__ __launch_bounds__(NT) void kda_bwd_grads_kernel(GdnBwdArgs a) {
     for (int m = 0; m < MS; ++m) sg[m] = 0.f;
     float A_acc = 0.f, B_acc = 0.f, dbt = 0.f;
     const size_t ckoff = (seq * a.nchunks + ch) * size_t(DK) * DV;
-    for (int tile = 0; tile < a.ntiles; ++tile) {
+    // the next tile's state tiles, v and dO are loaded into registers while this one works
+    float pS0[MS], pdS[MS], pv, pdO;
+    auto fetch = [&](int tile) {
         const int c0 = tile * VT;
-        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int idx = tid + NT * m, i = idx / VT, j = idx % VT;
+            const size_t e = ckoff + size_t(i) * DV + c0 + j;
+            pS0[m] = a.Sck[e];
+            pdS[m] = a.dSck[e];
+        }
+        const size_t e = (tok + r_me) * DV + c0 + x_me;
+        pv = r_me < n ? load_elem(a.v, e, iob) : 0.f;
+        pdO = r_me < n ? load_elem(a.dO, e, iob) : 0.f;
+    };
+    fetch(0);
+    for (int tile = 0; tile < a.ntiles; ++tile) {
+        lds_barrier();   // the previous tile's readers are done (loads stay in flight)
 #pragma unroll
         for (int m = 0; m < MS; ++m) {   // 16 consecutive lanes share a key dim i
             const int idx = tid + NT * m, i = idx / VT, j = idx % VT;
-            const size_t e = ckoff + size_t(i) * DV + c0 + j;
-            const float s0 = a.Sck[e], ds = a.dSck[e];
-            sm.w.t.S0[i][j] = s0;
-            sm.w.t.dS[i][j] = ds;
-            sg[m] += row16_sum(s0 * ds);
+            sm.w.t.S0[i][j] = pS0[m];
+            sm.w.t.dS[i][j] = pdS[m];
+            sg[m] += row16_sum(pS0[m] * pdS[m]);
         }
         if (tile == 0) {
             for (int idx = tid; idx < C * DK; idx += NT) {
@@ -679,56 +731,51 @@ __global__ __launch_bounds__(NT) void kda_bwd_grads_kernel(GdnBwdArgs a) {
                 sm.w.t.kt[r][i] = sm.rw.k[r][i] * __builtin_amdgcn_exp2f(sm.rw.bq[C - 1][i] - br);
             }
         }
-        {
-            const int t = r_me, j = x_me;
-            const size_t e = (tok + t) * DV + c0 + j;
-            sm.v[t][j] = t < n ? load_elem(a.v, e, iob) : 0.f;
-            sm.dO[t][j] = t < n ? load_elem(a.dO, e, iob) : 0.f;
-        }
-        __syncthreads();
+        sm.v[r_me][x_me] = pv;
+        sm.dO[r_me][x_me] = pdO;
+        if (tile + 1 < a.ntiles) fetch(tile + 1);
+        lds_barrier();
         const int t = r_me, j = x_me;
+        const int c0 = tile * VT;
         {
             float ks = 0.f, kds = 0.f;
-            for (int i = 0; i < DK; ++i) {
-                ks += sm.w.t.kd[t][i] * sm.w.t.S0[i][j];
-                kds += sm.w.t.kt[t][i] * sm.w.t.dS[i][j];
+#pragma unroll 4
+            for (int i = 0; i < DK; i += 4) {
+                const float4 kv = *reinterpret_cast<const float4*>(&sm.w.t.kd[t][i]);
+                const float4 tv = *reinterpret_cast<const float4*>(&sm.w.t.kt[t][i]);
+                ks += kv.x * sm.w.t.S0[i][j] + kv.y * sm.w.t.S0[i + 1][j] +
+                      kv.z * sm.w.t.S0[i + 2][j] + kv.w * sm.w.t.S0[i + 3][j];
+                kds += tv.x * sm.w.t.dS[i][j] + tv.y * sm.w.t.dS[i + 1][j] +
+                       tv.z * sm.w.t.dS[i + 2][j] + tv.w * sm.w.t.dS[i + 3][j];
             }
             for (int r = t; r < C; ++r) kds += sm.P[r][t] * sm.dO[r][j];
             sm.KS[t][j] = ks;
             sm.X[t][j] = sm.rw.b[t] * (sm.v[t][j] - ks);
             sm.R[t][j] = kds;
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < VT) solve_lower(sm.L, sm.X, sm.U, tid);   // U, one column per thread
         else if (tid >= kWave && tid < kWave + VT)          // dU, on another wave
             solve_upper_t(sm.L, sm.R, sm.dU, tid - kWave);
-        __syncthreads();
+        lds_barrier();
         {
             const float du = sm.dU[t][j];
             float p = sm.KS[t][j];
             for (int s = 0; s < t; ++s) p += sm.Lt[t][s] * sm.U[s][j];
             if (t < n) store_elem(a.dv, (tok + t) * DV + c0 + j, sm.rw.b[t] * du, iob);
             dbt += row16_sum(du * (sm.v[t][j] - p));
-            float av = 0.f, bv = 0.f;
-            for (int jj = 0; jj < VT; ++jj) {
-                av += sm.dO[r_me][jj] * sm.U[x_me][jj];
-                bv += sm.dU[r_me][jj] * sm.U[x_me][jj];
-            }
-            A_acc += av;
-            B_acc += bv;
+            A_acc += dot16(sm.dO[r_me], sm.U[x_me]);
+            B_acc += dot16(sm.dU[r_me], sm.U[x_me]);
         }
+        {   // this thread's key dim i is the same for every m
+            const int i = tid % DK;
 #pragma unroll
-        for (int m = 0; m < MQ; ++m) {
-            const int idx = tid + NT * m, tt = idx / DK, i = idx % DK;
-            float a0 = 0.f, a1 = 0.f, a2 = 0.f;
-            for (int jj = 0; jj < VT; ++jj) {
-                a0 += sm.w.t.S0[i][jj] * sm.dO[tt][jj];
-                a1 += sm.w.t.dS[i][jj] * sm.U[tt][jj];
-                a2 += sm.w.t.S0[i][jj] * sm.dU[tt][jj];
+            for (int m = 0; m < MQ; ++m) {
+                const int tt = (tid + NT * m) / DK;
+                so[m] += dot16(sm.w.t.S0[i], sm.dO[tt]);
+                su[m] += dot16(sm.w.t.dS[i], sm.U[tt]);
+                sdu[m] += dot16(sm.w.t.S0[i], sm.dU[tt]);
             }
-            so[m] += a0;
-            su[m] += a1;
-            sdu[m] += a2;
         }
     }
     __syncthreads();   // the last tile's readers of the tile arrays are done
