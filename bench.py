@@ -2,6 +2,7 @@
 """Benchmark of the linear-attention hot path on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--only WORKLOAD] [--no-cpu] [--no-extras]
+(WORKLOAD may be backward_<prefill workload> for the backward of that prefill)
 
 A step is one chunked prefill of the headline workload (GLA, B=2 H=8 N=2048
 d_k=d_v=128, bf16 inputs, fp32 state, chunk 64) over one batch of seeded
@@ -495,7 +496,12 @@ def main():
 
     results = {}
     main_name = args.only or MAIN
-    if main_name.startswith("decode"):
+    bwd = main_name.startswith("backward_")
+    if bwd:
+        rec = bench_backward(main_name[len("backward_"):], args.steps, args.warmup, torch, bd, W,
+                             device, stream)
+        main_case = None
+    elif main_name.startswith("decode"):
         rec = bench_decode(main_name, args.steps, args.warmup, torch, bd, W, device, stream)
         main_case = None
     elif main_name.startswith("selscan"):
@@ -537,9 +543,15 @@ def main():
             torch.cuda.empty_cache()
 
     scan = main_name.startswith("selscan")
-    wl = W.SELSCAN[main_name] if scan else W.WORKLOADS[main_name]
+    wl = W.SELSCAN[main_name] if scan else \
+        W.WORKLOADS[main_name[len("backward_"):] if bwd else main_name]
     m = results[main_name]
-    if scan:
+    if bwd:   # every kernel of la_prefill_backward against the algorithmic bytes
+        value, unit = m["Mtok_per_s"], "Mtok/s"
+        roof = {"bound": "hbm", "achieved": m["GB_per_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": m["hbm_frac"], "traffic": None, "kernel": "la_prefill_backward",
+                "duration_us": m["ms"] * 1e3}
+    elif scan:
         value, unit = m["Mtok_per_s"], "Mtok/s"
         roof = {"bound": "alu", "achieved": m["G_state_updates_per_s"],
                 "peak": PEAK_SCAN_UPDATES / 1e9, "unit": "G state updates/s",
