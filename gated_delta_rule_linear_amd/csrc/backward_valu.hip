@@ -57,7 +57,7 @@ struct BwdArgs {
     const float *S0, *dSf;
     void *dq, *dk, *dv, *dg;
     float* dS0;
-    const float *dnum, *dden;   // KATH: dL/dnum [tokens][DV] and dL/dden [tokens] (fp32)
+    float *dnum, *dden;         // KATH: dL/dnum [tokens][DV] and dL/dden [tokens] (fp32)
     const float *z0, *dzf;      // KATH: initial normaliser and its final gradient, or null
     float* dz0;                 // KATH
     float eps;                  // KATH
@@ -489,9 +489,9 @@ __global__ __launch_bounds__(NT) void kath_out_kernel(BwdArgs a) {
         for (int s2 = 0; s2 <= t; ++s2) num += sP[t][s2] * sv[s2][x];
         const float d = sdO[t][x];
         w += row16_sum(d * num);
-        if (t < n) const_cast<float*>(a.dnum)[(tok + t) * DV + c0 + x] = d / sden[t];
+        if (t < n) a.dnum[(tok + t) * DV + c0 + x] = d / sden[t];
     }
-    if (x == 0 && t < n) const_cast<float*>(a.dden)[tok + t] = -w / (sden[t] * sden[t]);
+    if (x == 0 && t < n) a.dden[tok + t] = -w / (sden[t] * sden[t]);
 }
 
 struct BwdLayout {
@@ -631,8 +631,8 @@ hipError_t launch_backward(const BwdProblem& bp) {
     a.dkp = reinterpret_cast<float*>(ws + L.dkp);
     a.dgp = ka ? nullptr : reinterpret_cast<float*>(ws + L.dgp);
     if (ka) {
-        a.dnum = reinterpret_cast<const float*>(ws + L.dnum);
-        a.dden = reinterpret_cast<const float*>(ws + L.dden);
+        a.dnum = reinterpret_cast<float*>(ws + L.dnum);
+        a.dden = reinterpret_cast<float*>(ws + L.dden);
         a.z0 = p.z0;
         a.dzf = bp.dz_final;
         a.dz0 = bp.dz0;

@@ -63,8 +63,8 @@ bool gdn_mfma_supported(int dk, int dv, bool io_bf16);
 size_t gdn_mfma_workspace_bytes(const Problem& p);
 hipError_t launch_prefill_gdn_mfma(const Problem& p);
 
-// backward_valu.hip (backward of the prefill: GLA, SSD; GDN by backward_gdn_valu.hip), a
-// validated call
+// backward_valu.hip (backward of the prefill: GLA, SSD and KATH here, GDN and KDA through
+// backward_gdn_valu.hip), a validated call
 struct BwdProblem {
     Problem p;                       // the forward call (inputs, shapes, workspace, stream)
     const void* dO = nullptr;        // dL/do [B,H,N,dv] io
