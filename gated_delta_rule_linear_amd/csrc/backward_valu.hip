@@ -203,10 +203,10 @@ __global__ __launch_bounds__(NT) void bwd_sums_kernel(BwdArgs a) {
     for (int idx = threadIdx.x; idx < DK * VT; idx += NT) {
         const int i = idx / VT, c = idx % VT;
         float ds = 0.f, gq = 0.f;
-        for (int s_ = 0; s_ < C; ++s_) {
-            ds += EK(s_, i) * sm.k[s_][i] * sm.v[s_][c];
-            gq += EQ(s_, i) * sm.q[s_][i] * sm.dO[s_][c];
-        }
+        if (a.mode & 1)
+            for (int s_ = 0; s_ < C; ++s_) ds += EK(s_, i) * sm.k[s_][i] * sm.v[s_][c];
+        if (a.mode & 2)
+            for (int s_ = 0; s_ < C; ++s_) gq += EQ(s_, i) * sm.q[s_][i] * sm.dO[s_][c];
         if (a.mode & 1) a.Sst[sbase + size_t(i) * SW + c0 + c] = ds;
         if (a.mode & 2) a.dSt[sbase + size_t(i) * SW + c0 + c] = gq;
     }
