@@ -13,13 +13,13 @@ pytestmark = pytest.mark.gpu
 
 
 def make_case(variant, B, H, N, dk, dv, io, seed, gate_kind="default", with_state=True,
-              with_dsf=True):
+              with_dsf=True, gate_io=None):
     kw = dict(seed=seed, qk_scale=dk ** -0.5, gate_kind=gate_kind)
     if variant == "gla":
         kw["v_scale"] = dk ** -0.5
     if variant in ("gdn", "kda"):
         kw["l2norm_qk"] = True
-    wl = W.Workload("b", variant, B, H, N, dk, dv, io, io, **kw)
+    wl = W.Workload("b", variant, B, H, N, dk, dv, io, gate_io or io, **kw)
     inp = W.make_inputs(wl, with_state=with_state)
     rng = np.random.default_rng(seed + 77)
     dO, dO_x = W.round_to(rng.standard_normal((B, H, N, dv)), io)
@@ -92,6 +92,19 @@ def test_backward_gate_kinds(variant, kind):
     case = make_case(variant, 1, 2, 50, 64, 32, "f32", seed=9, gate_kind=kind)
     banner(f"backward {variant} gates={kind}")
     check(*run_both(variant, *case), TOL["f32"])
+
+
+@pytest.mark.parametrize("variant", ["gla", "ssd", "gdn", "kda"])
+@pytest.mark.parametrize("io,gate_io", [("f32", "bf16"), ("bf16", "f32")])
+def test_backward_mixed_dtypes(variant, io, gate_io):
+    """q, k, v, dO in one dtype and the gates (and beta) in the other; every gradient keeps
+    its input's dtype."""
+    case = make_case(variant, 1, 2, 45, 32, 32, io, seed=31, gate_io=gate_io)
+    banner(f"backward {variant} io={io} gates={gate_io}")
+    got, ref = run_both(variant, *case)
+    assert got["dq"].dtype == (torch.float32 if io == "f32" else torch.bfloat16)
+    assert got["dg"].dtype == (torch.float32 if gate_io == "f32" else torch.bfloat16)
+    check(got, ref, TOL["bf16"] if "bf16" in (io, gate_io) else TOL["f32"])
 
 
 def test_backward_without_state_or_final_gradient():
