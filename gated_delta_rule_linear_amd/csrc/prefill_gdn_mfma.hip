@@ -1,7 +1,7 @@
 // Chunked prefill for the gated delta rule on bf16 MFMA (d_k = 128, chunk C = 64).
 //
 // Method ("线性注意力与 SSM", section GDN, rewritten per chunk; the chunkwise UT/WY
-// transform the survey pages name for delta-rule chunking). For one chunk with
+// transform that "状态空间与线性注意力" names for delta-rule chunking). For one chunk with
 // entering state S (key-major, fp32), local rows r, s = 0..C-1:
 //   c_r = sum_{s<=r} log alpha_s,  gamma_r = exp(c_r)
 //   L_rs = beta_r exp(c_r - c_s) k_r.k_s  (s < r),   T = (I + L)^{-1}
