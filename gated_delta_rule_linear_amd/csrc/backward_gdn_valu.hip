@@ -186,13 +186,14 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(GdnBwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------- chains
-// Both chains of GDN and KDA. Each workgroup walks one (sequence, 16-column value tile) in
-// order, forward for the states entering the chunks or in reverse for the gradients leaving
+// Both chains of GDN and KDA. Each workgroup walks one (sequence, CT-column value tile) in
+// order (CT = 32 where d_v allows: one chunk's keys and queries then serve 32 columns; at
+// most 128 registers, so two such workgroups share a CU and every chain stays resident), forward for the states entering the chunks or in reverse for the gradients leaving
 // them. The tile stays in registers: thread (g, j) holds rows g*RG .. g*RG+RG-1 of column j.
 // Per chunk: the rows' partial dot products with the chunk's (decayed) keys go through a
 // padded LDS buffer to give k_t . S[:, j]; then the right-hand side, U = T X (or dU = T^T R),
 // and the update of the thread's own rows from the keys (and queries) read as broadcast rows.
-template <int VAR, int DK>
+template <int VAR, int DK, int CT>
 struct ChainSmem {
     static constexpr bool PK = VAR == LA_KDA;   // a decay per key dim
     static constexpr int KP = DK + 4;           // row pitch: 16-byte aligned rows
@@ -201,29 +202,31 @@ struct ChainSmem {
     float kt[PK ? C : 1][PK ? KP : 1];   // KDA: k 2^(b_last - b)
     union {
         float bq[PK ? C : 1][PK ? KP : 1];   // KDA: cumulative base-2 log gates
-        float red[C][16 * VT + 16];          // partials over the 16 row groups (padded rows)
+        float red[C][16 * CT + 32];          // partials over the 16 row groups (padded rows)
     } w;
     float T[C][C + 1], P[C][C + 1];
-    float x[C][VT], rhs[C][VT], u[C][VT];
+    float x[C][CT], rhs[C][CT], u[C][CT];
     float eg[C], el[C], b[C];   // GDN 2^c_r, 2^(c_last - c_r); beta
     float dl[PK ? DK : 1];      // KDA 2^b_last per key dim
 };
 
-template <int VAR, int DK, int DV>
-__global__ __launch_bounds__(NT, 2) void bwd_chains_kernel(GdnBwdArgs a) {
+template <int VAR, int DK, int DV, int CT>
+__global__ __launch_bounds__(16 * CT, 4) void bwd_chains_kernel(GdnBwdArgs a) {
     constexpr bool PK = VAR == LA_KDA;
     constexpr int RG = DK / 16;   // rows per thread
-    static_assert(DK % 16 == 0, "16 row groups");
-    __shared__ ChainSmem<VAR, DK> sm;
+    constexpr int NTC = 16 * CT;  // threads: 16 row groups x CT columns
+    static_assert(DK % 16 == 0 && DV % CT == 0 && NTC >= C * C, "16 row groups");
+    __shared__ ChainSmem<VAR, DK, CT> sm;
     const int tid = threadIdx.x;
-    const int nfw = a.nseq * a.ntiles;
+    constexpr int ntiles = DV / CT;
+    const int nfw = a.nseq * ntiles;
     const bool rev = int(blockIdx.x) >= nfw;
     const int unit = rev ? int(blockIdx.x) - nfw : int(blockIdx.x);
-    const size_t seq = size_t(unit / a.ntiles);
-    const int c0 = (unit % a.ntiles) * VT;
+    const size_t seq = size_t(unit / ntiles);
+    const int c0 = (unit % ntiles) * CT;
     const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
-    const int grp = tid / VT, j = tid % VT, i0 = grp * RG;   // this thread's rows and column
-    const int t_me = tid / VT;                                // row of the (t, j) maps
+    const int grp = tid / CT, j = tid % CT, i0 = grp * RG;   // this thread's rows and column
+    const int t_me = tid / CT;                                // row of the (t, j) maps
     const size_t sbase = seq * DK * DV;
     const float* init = rev ? a.dSf : a.S0;
     float S[RG];
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_chains_kernel(GdnBwdArgs a) {
         float* ckc = ck + size_t(ch) * DK * DV;
 #pragma unroll
         for (int m = 0; m < RG; ++m) ckc[size_t(i0 + m) * DV + c0 + j] = S[m];
-        for (int idx = tid; idx < C * DK; idx += NT) {
+        for (int idx = tid; idx < C * DK; idx += NTC) {
             const int r = idx / DK, i = idx % DK;
             const size_t e = (tok + r) * DK + i;
             const bool in = r < n;
@@ -266,14 +269,14 @@ __global__ __launch_bounds__(NT, 2) void bwd_chains_kernel(GdnBwdArgs a) {
             sm.b[tid] = tid < n ? load_elem(a.beta, tok + tid, gb) : 0.f;
         }
         sm.x[t_me][j] = t_me < n ? load_elem(rev ? a.dO : a.v, (tok + t_me) * DV + c0 + j, iob) : 0.f;
-        {
+        if (tid < C * C) {
             const size_t off = (seq * a.nchunks + ch) * size_t(C * C);
             sm.T[tid / C][tid % C] = a.Tck[off + tid];
             if (rev) sm.P[tid / C][tid % C] = a.Pck[off + tid];
         }
         __syncthreads();
         if (PK) {   // prefix sums per key dim, then the decayed key (and query) rows
-            for (int i = tid; i < DK; i += NT) {
+            for (int i = tid; i < DK; i += NTC) {
                 float acc = 0.f;
                 for (int r = 0; r < C; ++r) {
                     acc += sm.w.bq[r][i];
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_chains_kernel(GdnBwdArgs a) {
                 sm.dl[i] = __builtin_amdgcn_exp2f(acc);
             }
             __syncthreads();
-            for (int idx = tid; idx < C * DK; idx += NT) {   // each element owned by one thread
+            for (int idx = tid; idx < C * DK; idx += NTC) {   // each element owned by one thread
                 const int r = idx / DK, i = idx % DK;
                 const float br = sm.w.bq[r][i], eb = __builtin_amdgcn_exp2f(br);
                 const float kv = sm.k[r][i];
@@ -293,14 +296,14 @@ __global__ __launch_bounds__(NT, 2) void bwd_chains_kernel(GdnBwdArgs a) {
             __syncthreads();
         }
         {   // partial k_t . S[:, j] over this thread's rows, for every row t of the chunk
-            constexpr int KP = ChainSmem<VAR, DK>::KP;
+            constexpr int KP = ChainSmem<VAR, DK, CT>::KP;
             const float* kk = (PK && rev) ? &sm.kt[0][0] : &sm.k[0][0];
 #pragma unroll
             for (int t = 0; t < C; ++t) {
                 float p = 0.f;
 #pragma unroll
                 for (int m = 0; m < RG; ++m) p += kk[t * KP + i0 + m] * S[m];
-                sm.w.red[t][grp * VT + j] = p;
+                sm.w.red[t][grp * CT + j] = p;
             }
         }
         __syncthreads();
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_chains_kernel(GdnBwdArgs a) {
             const int t = t_me;
             float ks = 0.f;
 #pragma unroll
-            for (int g2 = 0; g2 < 16; ++g2) ks += sm.w.red[t][g2 * VT + j];
+            for (int g2 = 0; g2 < 16; ++g2) ks += sm.w.red[t][g2 * CT + j];
             float rhs;
             if (!rev) {
                 rhs = sm.b[t] * (sm.x[t][j] - (PK ? ks : sm.eg[t] * ks));
@@ -858,13 +861,14 @@ GdnLayout gdn_layout(const Problem& p) {
 
 template <int DK, int DV>
 hipError_t launch_dims(const Problem& p, GdnBwdArgs a) {
-    const unsigned chains = unsigned(2 * a.nseq * a.ntiles);
+    constexpr int CT = DV % 64 == 0 ? 64 : DV % 32 == 0 ? 32 : 16;   // columns per chain
+    const unsigned chains = unsigned(2 * a.nseq * (DV / CT));
     const unsigned units = unsigned(size_t(a.nseq) * a.nchunks);
     if (p.variant == LA_KDA) {
         kda_bwd_prep_kernel<DK><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        bwd_chains_kernel<LA_KDA, DK, DV><<<dim3(chains), dim3(NT), 0, p.stream>>>(a);
+        bwd_chains_kernel<LA_KDA, DK, DV, CT><<<dim3(chains), dim3(16 * CT), 0, p.stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         kda_bwd_grads_kernel<DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
         return hipGetLastError();
@@ -872,7 +876,7 @@ hipError_t launch_dims(const Problem& p, GdnBwdArgs a) {
     gdn_bwd_prep_kernel<DK><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    bwd_chains_kernel<LA_GDN, DK, DV><<<dim3(chains), dim3(NT), 0, p.stream>>>(a);
+    bwd_chains_kernel<LA_GDN, DK, DV, CT><<<dim3(chains), dim3(16 * CT), 0, p.stream>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     gdn_bwd_grads_kernel<DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
     return hipGetLastError();
