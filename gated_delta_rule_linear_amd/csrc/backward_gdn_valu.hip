@@ -404,7 +404,7 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(NT) void gdn_bwd_grads_kernel(GdnBwdArgs a) {
+__global__ __launch_bounds__(NT, 3) void gdn_bwd_grads_kernel(GdnBwdArgs a) {
     constexpr int MQ = C * DK / NT;   // (row, key dim) pairs per thread
     static_assert(MQ >= 1 && (C * DK) % NT == 0, "d_k >= 16");
     __shared__ GradSmem<DK> sm;
