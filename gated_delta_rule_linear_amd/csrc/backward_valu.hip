@@ -261,7 +261,7 @@ __global__ __launch_bounds__(NT) void bwd_scans_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------- grads
 template <int VAR, int DK, int DV>
-__global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT, 4) void bwd_grads_kernel(BwdArgs a) {
     constexpr bool SG = scalar_gate<VAR>();
     constexpr int SW = state_width<VAR, DV>();
     __shared__ ChunkSmem<DK, SG> sm;
