@@ -26,13 +26,13 @@
 // q_r).do_r, mu_s = (S0^T k_s).du_s, sigma = <dS', S0>, and of d_k-vectors such as S0 do_t.
 //
 // Kernels: a prep kernel forms every chunk's T = (I + L)^-1 and P in parallel; then one
-// launch runs both chains, each workgroup one (sequence, 16-column value tile), with U = T X
-// and dU = T^T R as small products (value columns never mix in either recurrence): the
-// forward chain writes the state
-// entering every chunk, the reverse chain the gradient leaving it (dS_in = 2^c_last dS' +
-// sum_r 2^c_r q_r do_r^T - sum_s beta_s 2^c_s k_s du_s^T), and dS0. Then the grads kernel
-// takes every (sequence, chunk) in parallel, loops over the value tiles accumulating the
-// column sums, and writes final dq, dk, dv, dalpha and dbeta.
+// launch runs both chains, each workgroup one (sequence, value tile of up to 64 columns),
+// with U = T X and dU = T^T R as small products (value columns never mix in either
+// recurrence): the forward chain writes the state entering every chunk, the reverse chain
+// the gradient leaving it (dS_in = 2^c_last dS' + sum_r 2^c_r q_r do_r^T - sum_s beta_s
+// 2^c_s k_s du_s^T), and dS0. Then the grads kernel takes every (sequence, chunk) in
+// parallel, loops over 16-column value tiles accumulating the column sums, and writes
+// final dq, dk, dv, dalpha and dbeta.
 //
 // KDA ("状态空间与线性注意力", section KDA: the decay Diag(alpha_t) applied first, then
 // the delta write, with alpha_t per key dim) takes the same route with per-key-dim
