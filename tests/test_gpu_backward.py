@@ -169,3 +169,31 @@ def test_backward_ssd_matrix_cores_vs_valu(N):
     torch.cuda.synchronize()
     for name in ("dq", "dk", "dv", "dg", "dS0"):
         assert relerr(got[name], getattr(valu, name).double().cpu().numpy()) <= TOL["bf16"], name
+
+
+@pytest.mark.parametrize("variant", ["kath", "gla", "ssd", "gdn", "kda"])
+def test_backward_deterministic_and_batch_invariant(variant):
+    """No atomics anywhere: two calls give the same bits, and a sequence's gradients do
+    not depend on the other sequences of the batch (the same bits when it runs alone)."""
+    inp, dO, dO_x, dSf, dSf_x = make_case(variant, 3, 2, 53, 64, 32, "bf16", seed=41)
+    banner(f"backward {variant} determinism / batch invariance")
+    d = {k: dev(v) for k, v in inp.dev.items()}
+    dSf0, dzf = dSf if isinstance(dSf, tuple) else (dSf, None)
+
+    def call(sl):
+        pick = lambda t: None if t is None else t[sl].contiguous()
+        return bd.prefill_backward(pick(d["q"]), pick(d["k"]), pick(d["v"]), pick(d.get("g")),
+                                   pick(dev(dO)), variant=variant, beta=pick(d.get("beta")),
+                                   S0=pick(d.get("S0")), z0=pick(d.get("z0")),
+                                   dS_final=pick(dev(dSf0)), dz_final=pick(dev(dzf)))
+
+    full = slice(0, 3)
+    a, b = call(full), call(full)
+    alone = call(slice(1, 2))
+    torch.cuda.synchronize()
+    for name in ("dq", "dk", "dv", "dg", "dbeta", "dS0", "dz0"):
+        x, y, z = getattr(a, name), getattr(b, name), getattr(alone, name)
+        if x is None:
+            continue
+        assert torch.equal(x, y), f"{name} differs between two calls"
+        assert torch.equal(x[1:2], z), f"{name} of batch row 1 depends on the other rows"
