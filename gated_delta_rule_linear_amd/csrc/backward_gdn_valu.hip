@@ -211,7 +211,7 @@ struct ChainSmem {
 };
 
 template <int VAR, int DK, int DV, int CT>
-__global__ __launch_bounds__(16 * CT, 4) void bwd_chains_kernel(GdnBwdArgs a) {
+__global__ __launch_bounds__(16 * CT, CT >= 32 ? 4 : 2) void bwd_chains_kernel(GdnBwdArgs a) {
     constexpr bool PK = VAR == LA_KDA;
     constexpr int RG = DK / 16;   // rows per thread
     constexpr int NTC = 16 * CT;  // threads: 16 row groups x CT columns

@@ -260,8 +260,9 @@ __global__ __launch_bounds__(NT) void bwd_scans_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------- grads
+// four waves per SIMD where the LDS allows it (GLA's per-key-dim gate tables allow two)
 template <int VAR, int DK, int DV>
-__global__ __launch_bounds__(NT, 4) void bwd_grads_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT, VAR == LA_GLA ? 2 : 4) void bwd_grads_kernel(BwdArgs a) {
     constexpr bool SG = scalar_gate<VAR>();
     constexpr int SW = state_width<VAR, DV>();
     __shared__ ChunkSmem<DK, SG> sm;
