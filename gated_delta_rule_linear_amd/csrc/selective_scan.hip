@@ -237,34 +237,36 @@ __global__ __launch_bounds__(NT) void selective_scan_kernel(ScanArgs a) {
             }
             return acc0 + acc1;
         };
-        // Tokens go in pairs: the next pair's operands are read while this pair's two
+        // Tokens go in blocks of TB: the next block's operands are read while this block's
         // group sums (independent DPP chains, interleaved) complete.
+        constexpr int TB = NS == 1 ? 16 : NS == 2 ? 8 : 4;   // tokens per block (fewer registers per token at small NS)
+        static_assert(TC % TB == 0 && G % TB == 0, "whole token blocks per group");
         float yk = 0.f;   // lane jj keeps the sum of token G m + jj
-        Ops o0, o1;
-        read_ops(o0, 0);
-        read_ops(o1, 1);
+        Ops o[TB];
+#pragma unroll
+        for (int b = 0; b < TB; ++b) read_ops(o[b], b);
 #pragma unroll 2
-        for (int t = 0; t < TC; t += 2) {
-            const float p0 = step(o0);
-            const float p1 = step(o1);
-            if (t + 2 < TC) {
-                read_ops(o0, t + 2);
-                read_ops(o1, t + 3);
+        for (int t = 0; t < TC; t += TB) {
+            float v[TB];
+#pragma unroll
+            for (int b = 0; b < TB; ++b) v[b] = step(o[b]);
+            if (t + TB < TC) {
+#pragma unroll
+                for (int b = 0; b < TB; ++b) read_ops(o[b], t + TB + b);
             }
-            float v0 = p0, v1 = p1;
-            v0 += dpp_f<0xB1, 0xf, 0xf>(v0);   // quad_perm [1,0,3,2]
-            v1 += dpp_f<0xB1, 0xf, 0xf>(v1);
-            v0 += dpp_f<0x4E, 0xf, 0xf>(v0);   // quad_perm [2,3,0,1]
-            v1 += dpp_f<0x4E, 0xf, 0xf>(v1);
-            v0 += dpp_f<0x141, 0xf, 0xf>(v0);  // row_half_mirror
-            v1 += dpp_f<0x141, 0xf, 0xf>(v1);
+#pragma unroll
+            for (int b = 0; b < TB; ++b) v[b] += dpp_f<0xB1, 0xf, 0xf>(v[b]);   // quad_perm [1,0,3,2]
+#pragma unroll
+            for (int b = 0; b < TB; ++b) v[b] += dpp_f<0x4E, 0xf, 0xf>(v[b]);   // quad_perm [2,3,0,1]
+#pragma unroll
+            for (int b = 0; b < TB; ++b) v[b] += dpp_f<0x141, 0xf, 0xf>(v[b]);  // row_half_mirror
             if constexpr (G == 16) {
-                v0 += dpp_f<0x140, 0xf, 0xf>(v0);   // row_mirror
-                v1 += dpp_f<0x140, 0xf, 0xf>(v1);
+#pragma unroll
+                for (int b = 0; b < TB; ++b) v[b] += dpp_f<0x140, 0xf, 0xf>(v[b]);   // row_mirror
             }
-            yk = (t % G) == jj ? v0 : yk;
-            yk = ((t + 1) % G) == jj ? v1 : yk;
-            if ((t + 1) % G == G - 1) sm.ys[r][(t + 1 - (G - 1) + jj) * CH + cl] = yk;
+#pragma unroll
+            for (int b = 0; b < TB; ++b) yk = ((t + b) % G) == jj ? v[b] : yk;
+            if ((t + TB - 1) % G == G - 1) sm.ys[r][(t + TB - G + jj) * CH + cl] = yk;
         }
         lds_barrier();   // ys complete
         const int t0 = ch * TC;
