@@ -141,16 +141,34 @@ __global__ __launch_bounds__(NT) void ssd_bwd_scans_kernel(SbArgs a) {
     float* dSs = a.dSt + seq * a.nch * SS + ij;
     const float* ac = a.ac + seq * a.nch;
     float S = a.S0 ? a.S0[e] : 0.f;
-    for (int ch = 0; ch < a.nch; ++ch) {
-        const float d = Ss[ch * SS];
-        Ss[ch * SS] = S;
-        S = ac[ch] * S + d;
+    // chunks in batches of SB: a batch's loads are issued before its stores (same array)
+    constexpr int SB = 8;
+    for (int c0 = 0; c0 < a.nch; c0 += SB) {
+        float d[SB], g[SB];
+#pragma unroll
+        for (int b = 0; b < SB; ++b) {
+            d[b] = c0 + b < a.nch ? Ss[(c0 + b) * SS] : 0.f;
+            g[b] = c0 + b < a.nch ? ac[c0 + b] : 1.f;
+        }
+#pragma unroll
+        for (int b = 0; b < SB; ++b) {
+            if (c0 + b < a.nch) Ss[(c0 + b) * SS] = S;
+            S = g[b] * S + d[b];
+        }
     }
     float dS = a.dSf ? a.dSf[e] : 0.f;
-    for (int ch = a.nch - 1; ch >= 0; --ch) {
-        const float gq = dSs[ch * SS];
-        dSs[ch * SS] = dS;
-        dS = ac[ch] * dS + gq;
+    for (int c1 = a.nch - 1; c1 >= 0; c1 -= SB) {
+        float d[SB], g[SB];
+#pragma unroll
+        for (int b = 0; b < SB; ++b) {
+            d[b] = c1 - b >= 0 ? dSs[(c1 - b) * SS] : 0.f;
+            g[b] = c1 - b >= 0 ? ac[c1 - b] : 1.f;
+        }
+#pragma unroll
+        for (int b = 0; b < SB; ++b) {
+            if (c1 - b >= 0) dSs[(c1 - b) * SS] = dS;
+            dS = g[b] * dS + d[b];
+        }
     }
     a.dS0[e] = dS;
 }

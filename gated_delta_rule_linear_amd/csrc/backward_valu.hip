@@ -244,16 +244,41 @@ __global__ __launch_bounds__(NT) void bwd_scans_kernel(BwdArgs a) {
         if (a.z0) S = a.z0[ez];
         if (a.dzf) dS = a.dzf[ez];
     }
-    for (int ch = 0; (a.mode & 1) && ch < a.nchunks; ++ch) {
-        const float d = Ss[ch * stride];
-        Ss[ch * stride] = S;
-        S = ac[ch * (SG ? 1 : DK)] * S + d;
+    // Chunks go in batches of SB: the batch's sums and decays are loaded before any of
+    // its stores, so the loads are in flight together instead of each waiting behind the
+    // previous chunk's store to the same array.
+    constexpr int SB = 8;
+    const int astr = SG ? 1 : DK;
+    for (int c0 = 0; (a.mode & 1) && c0 < a.nchunks; c0 += SB) {
+        float d[SB], g[SB];
+#pragma unroll
+        for (int b = 0; b < SB; ++b) {
+            const int ch = c0 + b;
+            d[b] = ch < a.nchunks ? Ss[ch * stride] : 0.f;
+            g[b] = ch < a.nchunks ? ac[ch * astr] : 1.f;
+        }
+#pragma unroll
+        for (int b = 0; b < SB; ++b) {
+            const int ch = c0 + b;
+            if (ch < a.nchunks) Ss[ch * stride] = S;
+            S = g[b] * S + d[b];
+        }
     }
     if (!(a.mode & 2)) return;
-    for (int ch = a.nchunks - 1; ch >= 0; --ch) {
-        const float gq = dSs[ch * stride];
-        dSs[ch * stride] = dS;
-        dS = ac[ch * (SG ? 1 : DK)] * dS + gq;
+    for (int c1 = a.nchunks - 1; c1 >= 0; c1 -= SB) {
+        float d[SB], g[SB];
+#pragma unroll
+        for (int b = 0; b < SB; ++b) {
+            const int ch = c1 - b;
+            d[b] = ch >= 0 ? dSs[ch * stride] : 0.f;
+            g[b] = ch >= 0 ? ac[ch * astr] : 1.f;
+        }
+#pragma unroll
+        for (int b = 0; b < SB; ++b) {
+            const int ch = c1 - b;
+            if (ch >= 0) dSs[ch * stride] = dS;
+            dS = g[b] * dS + d[b];
+        }
     }
     if (col < DV) a.dS0[es] = dS;
     else if (col == DV) a.dz0[ez] = dS;
