@@ -98,6 +98,35 @@ struct ChunkSmem {
     float v[C][VT], dO[C][VT];
 };
 
+// The value tile (columns c0 .. c0 + VT - 1) of v and dO for one chunk; KATH's extra tile
+// holds the normaliser column (v = 1, output gradient dden).
+template <int VAR, int DK, int DV, bool SG>
+__device__ __forceinline__ void load_tile(ChunkSmem<DK, SG>& sm, const BwdArgs& a, size_t tok0,
+                                          int t0, int n, int c0) {
+    constexpr bool KA = VAR == LA_KATH;
+    const int tid = threadIdx.x;
+    const bool iob = a.io_bf16 != 0;
+    {
+        const int r = tid / VT, c = tid % VT;
+        const size_t tk = tok0 + t0 + r, e = tk * DV + c0 + c;
+        float vv = 0.f, dd = 0.f;
+        if (r < n) {
+            if (!KA) {
+                vv = load_elem(a.v, e, iob);
+                dd = load_elem(a.dO, e, iob);
+            } else if (c0 < DV) {
+                vv = load_elem(a.v, e, iob);
+                dd = a.dnum[e];
+            } else if (c == 0) {   // the normaliser column
+                vv = 1.f;
+                dd = a.dden[tk];
+            }
+        }
+        sm.v[r][c] = vv;
+        sm.dO[r][c] = dd;
+    }
+}
+
 template <int VAR, int DK, int DV, bool SG>
 __device__ __forceinline__ void load_chunk(ChunkSmem<DK, SG>& sm, const BwdArgs& a, size_t tok0,
                                            int t0, int n, int c0) {
@@ -126,25 +155,7 @@ __device__ __forceinline__ void load_chunk(ChunkSmem<DK, SG>& sm, const BwdArgs&
         sm.sgt[tid] = gv;
         sm.sc[tid] = __builtin_amdgcn_logf(gv);
     }
-    {
-        const int r = tid / VT, c = tid % VT;
-        const size_t tk = tok0 + t0 + r, e = tk * DV + c0 + c;
-        float vv = 0.f, dd = 0.f;
-        if (r < n) {
-            if (!KA) {
-                vv = load_elem(a.v, e, iob);
-                dd = load_elem(a.dO, e, iob);
-            } else if (c0 < DV) {
-                vv = load_elem(a.v, e, iob);
-                dd = a.dnum[e];
-            } else if (c == 0) {   // the normaliser column
-                vv = 1.f;
-                dd = a.dden[tk];
-            }
-        }
-        sm.v[r][c] = vv;
-        sm.dO[r][c] = dd;
-    }
+    load_tile<VAR, DK, DV, SG>(sm, a, tok0, t0, n, c0);
     __syncthreads();
     if (!SG) {
         for (int i = tid; i < DK; i += NT) {
@@ -188,29 +199,42 @@ __device__ __forceinline__ ChunkUnit chunk_unit(const BwdArgs& a) {
 }
 
 // ---------------------------------------------------------------------------- sums
+// one workgroup per (sequence, chunk): the chunk's rows and decay tables once, then every
+// value tile in turn
 template <int VAR, int DK, int DV>
 __global__ __launch_bounds__(NT) void bwd_sums_kernel(BwdArgs a) {
     constexpr bool SG = scalar_gate<VAR>();
     constexpr int SW = state_width<VAR, DV>();
     __shared__ ChunkSmem<DK, SG> sm;
-    const ChunkUnit u = chunk_unit(a);
-    const int c0 = u.tile * VT, t0 = u.ch * C, n = min(C, a.N - t0);
+    ChunkUnit u;
+    u.ch = int(blockIdx.x % unsigned(a.nchunks));
+    u.seq = blockIdx.x / unsigned(a.nchunks);
+    u.tile = 0;
+    const int t0 = u.ch * C, n = min(C, a.N - t0);
     const size_t tok0 = u.seq * size_t(a.N);
-    load_chunk<VAR, DK, DV, SG>(sm, a, tok0, t0, n, c0);
+    load_chunk<VAR, DK, DV, SG>(sm, a, tok0, t0, n, 0);   // rows and tile 0
     auto EQ = [&](int r, int i) { return SG ? sm.seq[r] : sm.eq[r][i]; };
     auto EK = [&](int r, int i) { return SG ? sm.sek[r] : sm.ek[r][i]; };
     const size_t sbase = (u.seq * a.nchunks + u.ch) * size_t(DK) * SW;
-    for (int idx = threadIdx.x; idx < DK * VT; idx += NT) {
-        const int i = idx / VT, c = idx % VT;
-        float ds = 0.f, gq = 0.f;
-        if (a.mode & 1)
-            for (int s_ = 0; s_ < C; ++s_) ds += EK(s_, i) * sm.k[s_][i] * sm.v[s_][c];
-        if (a.mode & 2)
-            for (int s_ = 0; s_ < C; ++s_) gq += EQ(s_, i) * sm.q[s_][i] * sm.dO[s_][c];
-        if (a.mode & 1) a.Sst[sbase + size_t(i) * SW + c0 + c] = ds;
-        if (a.mode & 2) a.dSt[sbase + size_t(i) * SW + c0 + c] = gq;
+    for (int tile = 0; tile < a.ntiles; ++tile) {
+        const int c0 = tile * VT;
+        if (tile > 0) {
+            __syncthreads();   // the previous tile's readers are done
+            load_tile<VAR, DK, DV, SG>(sm, a, tok0, t0, n, c0);
+            __syncthreads();
+        }
+        for (int idx = threadIdx.x; idx < DK * VT; idx += NT) {
+            const int i = idx / VT, c = idx % VT;
+            float ds = 0.f, gq = 0.f;
+            if (a.mode & 1)
+                for (int s_ = 0; s_ < C; ++s_) ds += EK(s_, i) * sm.k[s_][i] * sm.v[s_][c];
+            if (a.mode & 2)
+                for (int s_ = 0; s_ < C; ++s_) gq += EQ(s_, i) * sm.q[s_][i] * sm.dO[s_][c];
+            if (a.mode & 1) a.Sst[sbase + size_t(i) * SW + c0 + c] = ds;
+            if (a.mode & 2) a.dSt[sbase + size_t(i) * SW + c0 + c] = gq;
+        }
     }
-    if (u.tile == 0) {
+    {
         float* ac = a.ac + (u.seq * a.nchunks + u.ch) * (SG ? 1 : DK);
         if (SG) {
             if (threadIdx.x == 0) ac[0] = __builtin_amdgcn_exp2f(sm.sc[C - 1]);
@@ -553,12 +577,13 @@ hipError_t launch_dims(const Problem& p, BwdArgs a) {
     const size_t ntok = size_t(a.nseq) * a.N;
     hipError_t e;
     const unsigned units = unsigned(size_t(a.nseq) * a.nchunks * a.ntiles);
+    const unsigned chunks = unsigned(size_t(a.nseq) * a.nchunks);   // sums: one per chunk
     const size_t nel = size_t(a.nseq) * DK * SW;
     const dim3 scan_grid(unsigned((nel + NT - 1) / NT));
     if constexpr (VAR == LA_KATH) {
         // the state half, then dnum and dden from the forward's num and den, then the rest
         a.mode = 1;
-        bwd_sums_kernel<VAR, DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
+        bwd_sums_kernel<VAR, DK, DV><<<dim3(chunks), dim3(NT), 0, p.stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         bwd_scans_kernel<VAR, DK, DV><<<scan_grid, dim3(NT), 0, p.stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -569,7 +594,7 @@ hipError_t launch_dims(const Problem& p, BwdArgs a) {
     } else {
         a.mode = 3;
     }
-    bwd_sums_kernel<VAR, DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
+    bwd_sums_kernel<VAR, DK, DV><<<dim3(chunks), dim3(NT), 0, p.stream>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     bwd_scans_kernel<VAR, DK, DV><<<scan_grid, dim3(NT), 0, p.stream>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
