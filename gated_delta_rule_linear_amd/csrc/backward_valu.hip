@@ -26,10 +26,10 @@
 // gradient contribution G_c = sum_r diag(exp(B_r)) q_r dO_r^T and its decay a_c =
 // exp(B_last),
 //   S_in[c+1] = a_c o S_in[c] + dS_c,    dS_out[c-1] = a_c o dS_out[c] + G_c.
-// So the work runs in four kernels: sums (every chunk in parallel: dS_c, G_c, a_c), scans
+// So the work runs in three kernels: sums (every chunk in parallel: dS_c, G_c, a_c), scans
 // (one thread per state element walks the chunks forward for S_in and backward for
-// dS_out, in place), grads (every chunk and value tile in parallel: dV, and partials of
-// dQ, dK and dg over the tile's columns), then the finishing sums of the partials.
+// dS_out, in place), and grads (every chunk in parallel, looping over the value tiles: dV,
+// and dQ, dK and dg summed over the tiles).
 //
 // KATH (normalised ELU+1 attention, "Linear / RNN 路线" section 2.1) is the same machinery
 // with gate 1, phi(q) and phi(k) in place of q and k, and one more value column. With
@@ -65,9 +65,6 @@ struct BwdArgs {
     float* Sst;      // [nseq][nchunks][DK][DV]: dS_c, then S_in (in place)
     float* dSt;      // [nseq][nchunks][DK][DV]: G_c, then dS_out (in place)
     float* ac;       // [nseq][nchunks][DK] (GLA) or [nseq][nchunks] (SSD): chunk decay
-    float* dqp;      // [ntiles][nseq * N][DK] partial dq
-    float* dkp;      // [ntiles][nseq * N][DK] partial dk
-    float* dgp;      // [ntiles][nseq * N][DK] partial dg (per key dim)
     int N, nseq, ntiles, nchunks;
     int io_bf16, gate_bf16;
 };
@@ -184,19 +181,11 @@ __device__ __forceinline__ void load_chunk(ChunkSmem<DK, SG>& sm, const BwdArgs&
     __syncthreads();
 }
 
-// workgroup -> (sequence, chunk, value tile), the tiles of one chunk adjacent
+// workgroup -> (sequence, chunk)
 struct ChunkUnit {
     size_t seq;
-    int ch, tile;
+    int ch;
 };
-__device__ __forceinline__ ChunkUnit chunk_unit(const BwdArgs& a) {
-    const size_t b = blockIdx.x;
-    ChunkUnit u;
-    u.tile = int(b % a.ntiles);
-    u.ch = int((b / a.ntiles) % a.nchunks);
-    u.seq = b / (size_t(a.ntiles) * a.nchunks);
-    return u;
-}
 
 // ---------------------------------------------------------------------------- sums
 // one workgroup per (sequence, chunk): the chunk's rows and decay tables once, then every
@@ -209,7 +198,6 @@ __global__ __launch_bounds__(NT) void bwd_sums_kernel(BwdArgs a) {
     ChunkUnit u;
     u.ch = int(blockIdx.x % unsigned(a.nchunks));
     u.seq = blockIdx.x / unsigned(a.nchunks);
-    u.tile = 0;
     const int t0 = u.ch * C, n = min(C, a.N - t0);
     const size_t tok0 = u.seq * size_t(a.N);
     load_chunk<VAR, DK, DV, SG>(sm, a, tok0, t0, n, 0);   // rows and tile 0
@@ -308,177 +296,6 @@ __global__ __launch_bounds__(NT) void bwd_scans_kernel(BwdArgs a) {
     else if (col == DV) a.dz0[ez] = dS;
 }
 
-// ---------------------------------------------------------------------------- grads
-// four waves per SIMD where the LDS allows it (GLA's per-key-dim gate tables allow two)
-template <int VAR, int DK, int DV>
-__global__ __launch_bounds__(NT, VAR == LA_GLA ? 2 : 4) void bwd_grads_kernel(BwdArgs a) {
-    constexpr bool SG = scalar_gate<VAR>();
-    constexpr int SW = state_width<VAR, DV>();
-    __shared__ ChunkSmem<DK, SG> sm;
-    // rows padded to VT + 1 floats: the dQ / dK step reads a column down consecutive rows
-    __shared__ float sdS[DK][VT + 1];    // gradient of the state leaving the chunk
-    __shared__ float sSin[DK][VT + 1];   // state entering it
-    __shared__ float sP[C][C + 1], sA[C][C + 1];
-    const int tid = threadIdx.x;
-    const ChunkUnit u = chunk_unit(a);
-    const int c0 = u.tile * VT, t0 = u.ch * C, n = min(C, a.N - t0);
-    const bool iob = a.io_bf16 != 0;
-    const size_t tok0 = u.seq * size_t(a.N);
-    const size_t sbase = (u.seq * a.nchunks + u.ch) * size_t(DK) * SW;
-    for (int idx = tid; idx < DK * VT; idx += NT) {
-        const int i = idx / VT, c = idx % VT;
-        sSin[i][c] = a.Sst[sbase + size_t(i) * SW + c0 + c];
-        sdS[i][c] = a.dSt[sbase + size_t(i) * SW + c0 + c];
-    }
-    load_chunk<VAR, DK, DV, SG>(sm, a, tok0, t0, n, c0);   // ends with a barrier
-    float* dqp = a.dqp + size_t(u.tile) * a.nseq * a.N * DK;
-    float* dkp = a.dkp + size_t(u.tile) * a.nseq * a.N * DK;
-    float* dgp = a.dgp + size_t(u.tile) * a.nseq * a.N * DK;
-    auto EQ = [&](int r, int i) { return SG ? sm.seq[r] : sm.eq[r][i]; };
-    auto EK = [&](int r, int i) { return SG ? sm.sek[r] : sm.ek[r][i]; };
-    // exp(B_r - B_s) for s <= r
-    auto PF = [&](int r, int s, int i) {
-        return SG ? sm.pd[r][s] : __builtin_amdgcn_exp2f(sm.lg[r][i] - sm.lg[s][i]);
-    };
-    auto gate = [&](int r, int i) { return SG ? sm.sgt[r] : sm.gt[r][i]; };
-
-    // P (all key dims) and A (this tile's value columns), lower triangles
-    {
-        const int r = tid / C, s = tid % C;
-        float p = 0.f, av = 0.f;
-        if (s <= r) {
-            if (SG) {
-                for (int i = 0; i < DK; ++i) p += sm.q[r][i] * sm.k[s][i];
-                p *= sm.pd[r][s];
-            } else {
-                for (int i = 0; i < DK; ++i)
-                    p += sm.q[r][i] * sm.k[s][i] * __builtin_amdgcn_exp2f(sm.lg[r][i] - sm.lg[s][i]);
-            }
-            for (int c = 0; c < VT; ++c) av += sm.dO[r][c] * sm.v[s][c];
-        }
-        sP[r][s] = p;
-        sA[r][s] = av;
-    }
-    __syncthreads();
-    // dV (final for this tile's columns)
-    {
-        const int s = tid / VT, c = tid % VT;
-        float acc = 0.f;
-        for (int r = s; r < C; ++r) acc += sP[r][s] * sm.dO[r][c];
-        for (int i = 0; i < DK; ++i) acc += sm.k[s][i] * EK(s, i) * sdS[i][c];
-        if (s < n && c0 < DV) store_elem(a.dv, (tok0 + t0 + s) * DV + c0 + c, acc, iob);
-    }
-    // partial dQ and dK over this tile's columns
-    for (int idx = tid; idx < C * DK; idx += NT) {
-        const int r = idx / DK, i = idx % DK;
-        if (r >= n) continue;
-        float sd = 0.f, kv = 0.f;
-        for (int c = 0; c < VT; ++c) {
-            sd += sm.dO[r][c] * sSin[i][c];
-            kv += sdS[i][c] * sm.v[r][c];
-        }
-        float dq = EQ(r, i) * sd;
-        for (int s = 0; s <= r; ++s) dq += sA[r][s] * sm.k[s][i] * PF(r, s, i);
-        float dk = EK(r, i) * kv;
-        for (int t = r; t < C; ++t) dk += sA[t][r] * sm.q[t][i] * PF(t, r, i);
-        dqp[(tok0 + t0 + r) * DK + i] = dq;
-        dkp[(tok0 + t0 + r) * DK + i] = dk;
-    }
-    // partial dg: thread (row group rg, column c) owns elements (rg + 16 m, c); for each
-    // it rebuilds S_{s-1} forward and dS_s backward over the chunk, and the products are
-    // summed over the 16 column lanes (consecutive lanes) with DPP
-    if constexpr (VAR != LA_KATH) {
-        const int c = tid % VT, rg = tid / VT;
-#pragma unroll 1
-        for (int m = 0; m < DK / 16; ++m) {
-            const int i = rg + 16 * m;
-            float sp[C];   // S_{s-1}[i][c]
-            float st = sSin[i][c];
-#pragma unroll
-            for (int s_ = 0; s_ < C; ++s_) {
-                sp[s_] = st;
-                st = gate(s_, i) * st + sm.k[s_][i] * sm.v[s_][c];
-            }
-            float dsv = sdS[i][c];   // dS_s[i][c], from the chunk's end backward
-            float pr[C];
-#pragma unroll
-            for (int s_ = C - 1; s_ >= 0; --s_) {
-                if (s_ < C - 1) dsv *= gate(s_ + 1, i);
-                dsv += sm.q[s_][i] * sm.dO[s_][c];
-                pr[s_] = dsv * sp[s_];
-            }
-#pragma unroll
-            for (int s_ = 0; s_ < C; ++s_) {
-                float v_ = pr[s_];
-                v_ += dpp_f<0xB1, 0xf, 0xf>(v_);
-                v_ += dpp_f<0x4E, 0xf, 0xf>(v_);
-                v_ += dpp_f<0x141, 0xf, 0xf>(v_);
-                v_ += dpp_f<0x140, 0xf, 0xf>(v_);
-                pr[s_] = v_;
-            }
-            if (c == 0) {
-#pragma unroll
-                for (int s_ = 0; s_ < C; ++s_)
-                    if (s_ < n) dgp[(tok0 + t0 + s_) * DK + i] = pr[s_];
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------- finish
-// dq, dk, dg = sums of the tile partials (dg summed over the key dims too for SSD, one
-// wave per token).
-template <int VAR, int DK>
-__global__ __launch_bounds__(NT) void bwd_sum_kernel(BwdArgs a) {
-    constexpr bool SG = scalar_gate<VAR>();
-    const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
-    const size_t ntok = size_t(a.nseq) * a.N;
-    const size_t stride = ntok * DK;
-    if constexpr (VAR == LA_KATH) {   // through phi: phi'(x) = min(phi(x), 1)
-        const size_t e = size_t(blockIdx.x) * NT + threadIdx.x;
-        if (e >= stride) return;
-        float dq = 0.f, dk = 0.f;
-        for (int t = 0; t < a.ntiles; ++t) {
-            dq += a.dqp[t * stride + e];
-            dk += a.dkp[t * stride + e];
-        }
-        dq *= fminf(elu_plus_one(load_elem(a.q, e, iob)), 1.f);
-        dk *= fminf(elu_plus_one(load_elem(a.k, e, iob)), 1.f);
-        store_elem(a.dq, e, dq, iob);
-        store_elem(a.dk, e, dk, iob);
-    } else if constexpr (!SG) {
-        const size_t e = size_t(blockIdx.x) * NT + threadIdx.x;
-        if (e >= stride) return;
-        float dq = 0.f, dk = 0.f, dg = 0.f;
-        for (int t = 0; t < a.ntiles; ++t) {
-            dq += a.dqp[t * stride + e];
-            dk += a.dkp[t * stride + e];
-            dg += a.dgp[t * stride + e];
-        }
-        store_elem(a.dq, e, dq, iob);
-        store_elem(a.dk, e, dk, iob);
-        store_elem(a.dg, e, dg, gb);
-    } else {
-        const size_t tok = size_t(blockIdx.x) * (NT / kWave) + threadIdx.x / kWave;
-        const int lane = threadIdx.x % kWave;
-        if (tok >= ntok) return;   // a whole wave leaves together
-        float dg = 0.f;
-        for (int i = lane; i < DK; i += kWave) {
-            const size_t e = tok * DK + i;
-            float dq = 0.f, dk = 0.f;
-            for (int t = 0; t < a.ntiles; ++t) {
-                dq += a.dqp[t * stride + e];
-                dk += a.dkp[t * stride + e];
-                dg += a.dgp[t * stride + e];
-            }
-            store_elem(a.dq, e, dq, iob);
-            store_elem(a.dk, e, dk, iob);
-        }
-        dg = wave_sum(dg);
-        if (lane == 0) store_elem(a.dg, tok, dg, gb);
-    }
-}
-
 __device__ __forceinline__ float row16_sum(float v) {
     v += dpp_f<0xB1, 0xf, 0xf>(v);
     v += dpp_f<0x4E, 0xf, 0xf>(v);
@@ -544,8 +361,179 @@ __global__ __launch_bounds__(NT) void kath_out_kernel(BwdArgs a) {
     if (x == 0 && t < n) a.dden[tok + t] = -w / (sden[t] * sden[t]);
 }
 
+// ---------------------------------------------------------------------------- grads
+// One workgroup per (sequence, chunk): P once over all key dims, then every value tile in
+// turn (A = (dO V^T) o M, dV, and the tile's shares of dQ, dK and the gate gradient, summed
+// over the tiles in registers and LDS), then the final dq, dk (through phi' for KATH) and
+// dg. Four waves per SIMD where the LDS allows it (GLA's per-key-dim gate tables allow two).
+template <int VAR, int DK, int DV>
+__global__ __launch_bounds__(NT, VAR == LA_KATH ? 3 : 2) void bwd_grads_kernel(BwdArgs a) {
+    constexpr bool SG = scalar_gate<VAR>();
+    constexpr bool KA = VAR == LA_KATH;
+    constexpr int SW = state_width<VAR, DV>();
+    constexpr int MQ = C * DK / NT;   // (row, key dim) pairs per thread
+    static_assert((C * DK) % NT == 0 && NT % DK == 0, "pairs per thread");
+    __shared__ ChunkSmem<DK, SG> sm;
+    // rows padded to VT + 1 floats: the dQ / dK step reads a column down consecutive rows
+    __shared__ float sdS[DK][VT + 1];    // gradient of the state leaving the chunk
+    __shared__ float sSin[DK][VT + 1];   // state entering it
+    __shared__ float sP[C][C + 1], sA[C][C + 1];
+    __shared__ float sdg[KA ? 1 : C][KA ? 1 : DK];   // gate gradient, summed over the tiles
+    const int tid = threadIdx.x;
+    const int ch = int(blockIdx.x % unsigned(a.nchunks));
+    const size_t seq = blockIdx.x / unsigned(a.nchunks);
+    const int t0 = ch * C, n = min(C, a.N - t0);
+    const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
+    const size_t tok0 = seq * size_t(a.N);
+    const size_t sbase = (seq * a.nchunks + ch) * size_t(DK) * SW;
+    auto load_states = [&](int c0) {
+        for (int idx = tid; idx < DK * VT; idx += NT) {
+            const int i = idx / VT, c = idx % VT;
+            sSin[i][c] = a.Sst[sbase + size_t(i) * SW + c0 + c];
+            sdS[i][c] = a.dSt[sbase + size_t(i) * SW + c0 + c];
+        }
+    };
+    load_states(0);
+    load_chunk<VAR, DK, DV, SG>(sm, a, tok0, t0, n, 0);   // rows and tile 0; ends with a barrier
+    auto EQ = [&](int r, int i) { return SG ? sm.seq[r] : sm.eq[r][i]; };
+    auto EK = [&](int r, int i) { return SG ? sm.sek[r] : sm.ek[r][i]; };
+    // exp(B_r - B_s) for s <= r
+    auto PF = [&](int r, int s, int i) {
+        return SG ? sm.pd[r][s] : __builtin_amdgcn_exp2f(sm.lg[r][i] - sm.lg[s][i]);
+    };
+    auto gate = [&](int r, int i) { return SG ? sm.sgt[r] : sm.gt[r][i]; };
+
+    {   // P over all key dims, lower triangle
+        const int r = tid / C, s = tid % C;
+        float p = 0.f;
+        if (s <= r) {
+            if (SG) {
+                for (int i = 0; i < DK; ++i) p += sm.q[r][i] * sm.k[s][i];
+                p *= sm.pd[r][s];
+            } else {
+                for (int i = 0; i < DK; ++i)
+                    p += sm.q[r][i] * sm.k[s][i] * __builtin_amdgcn_exp2f(sm.lg[r][i] - sm.lg[s][i]);
+            }
+        }
+        sP[r][s] = p;
+    }
+    if constexpr (!KA)
+        for (int idx = tid; idx < C * DK; idx += NT) sdg[idx / DK][idx % DK] = 0.f;
+    float dq[MQ], dk[MQ];
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) dq[m] = dk[m] = 0.f;
+
+    for (int tile = 0; tile < a.ntiles; ++tile) {
+        const int c0 = tile * VT;
+        if (tile > 0) {
+            __syncthreads();   // the previous tile's readers are done
+            load_states(c0);
+            load_tile<VAR, DK, DV, SG>(sm, a, tok0, t0, n, c0);
+        }
+        __syncthreads();
+        {   // A = (dO V^T) o M over this tile's value columns
+            const int r = tid / C, s = tid % C;
+            float av = 0.f;
+            if (s <= r)
+                for (int c = 0; c < VT; ++c) av += sm.dO[r][c] * sm.v[s][c];
+            sA[r][s] = av;
+        }
+        __syncthreads();
+        {   // dV (final for this tile's columns)
+            const int s = tid / VT, c = tid % VT;
+            float acc = 0.f;
+            for (int r = s; r < C; ++r) acc += sP[r][s] * sm.dO[r][c];
+            for (int i = 0; i < DK; ++i) acc += sm.k[s][i] * EK(s, i) * sdS[i][c];
+            if (s < n && c0 < DV) store_elem(a.dv, (tok0 + t0 + s) * DV + c0 + c, acc, iob);
+        }
+        // this tile's share of dQ and dK
+#pragma unroll
+        for (int m = 0; m < MQ; ++m) {
+            const int idx = tid + NT * m, r = idx / DK, i = idx % DK;
+            float sd = 0.f, kv = 0.f;
+            for (int c = 0; c < VT; ++c) {
+                sd += sm.dO[r][c] * sSin[i][c];
+                kv += sdS[i][c] * sm.v[r][c];
+            }
+            float q_ = EQ(r, i) * sd;
+            for (int s2 = 0; s2 <= r; ++s2) q_ += sA[r][s2] * sm.k[s2][i] * PF(r, s2, i);
+            float k_ = EK(r, i) * kv;
+            for (int t = r; t < C; ++t) k_ += sA[t][r] * sm.q[t][i] * PF(t, r, i);
+            dq[m] += q_;
+            dk[m] += k_;
+        }
+        // this tile's share of dg: thread (row group rg, column c) owns elements (rg + 16 m,
+        // c); for each it rebuilds S_{s-1} forward and dS_s backward over the chunk, and the
+        // products are summed over the 16 column lanes (consecutive lanes) with DPP
+        if constexpr (!KA) {
+            const int c = tid % VT, rg = tid / VT;
+#pragma unroll 1
+            for (int m = 0; m < DK / 16; ++m) {
+                const int i = rg + 16 * m;
+                float sp[C];   // S_{s-1}[i][c]
+                float st = sSin[i][c];
+#pragma unroll
+                for (int s_ = 0; s_ < C; ++s_) {
+                    sp[s_] = st;
+                    st = gate(s_, i) * st + sm.k[s_][i] * sm.v[s_][c];
+                }
+                float dsv = sdS[i][c];   // dS_s[i][c], from the chunk's end backward
+                float pr[C];
+#pragma unroll
+                for (int s_ = C - 1; s_ >= 0; --s_) {
+                    if (s_ < C - 1) dsv *= gate(s_ + 1, i);
+                    dsv += sm.q[s_][i] * sm.dO[s_][c];
+                    pr[s_] = dsv * sp[s_];
+                }
+#pragma unroll
+                for (int s_ = 0; s_ < C; ++s_) {
+                    float v_ = pr[s_];
+                    v_ += dpp_f<0xB1, 0xf, 0xf>(v_);
+                    v_ += dpp_f<0x4E, 0xf, 0xf>(v_);
+                    v_ += dpp_f<0x141, 0xf, 0xf>(v_);
+                    v_ += dpp_f<0x140, 0xf, 0xf>(v_);
+                    pr[s_] = v_;
+                }
+                if (c == 0) {   // one thread per (s, i): no other writer
+#pragma unroll
+                    for (int s_ = 0; s_ < C; ++s_) sdg[s_][i] += pr[s_];
+                }
+            }
+        }
+    }
+    // final dq, dk (KATH: through phi'(x) = min(phi(x), 1), phi of the inputs in LDS)
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) {
+        const int idx = tid + NT * m, r = idx / DK, i = idx % DK;
+        if (r >= n) continue;
+        float q_ = dq[m], k_ = dk[m];
+        if (KA) {
+            q_ *= fminf(sm.q[r][i], 1.f);
+            k_ *= fminf(sm.k[r][i], 1.f);
+        }
+        const size_t e = (tok0 + t0 + r) * DK + i;
+        store_elem(a.dq, e, q_, iob);
+        store_elem(a.dk, e, k_, iob);
+    }
+    if constexpr (!KA) {
+        __syncthreads();   // sdg complete
+        if constexpr (!SG) {
+            for (int idx = tid; idx < C * DK; idx += NT) {
+                const int r = idx / DK, i = idx % DK;
+                if (r < n) store_elem(a.dg, (tok0 + t0 + r) * DK + i, sdg[r][i], gb);
+            }
+        } else {   // one decay per token: the sum over the key dims, thread (row, part)
+            const int r = tid / 16, pt = tid % 16;
+            float acc = 0.f;
+            for (int i = pt; i < DK; i += 16) acc += sdg[r][i];
+            acc = row16_sum(acc);
+            if (pt == 0 && r < n) store_elem(a.dg, tok0 + t0 + r, acc, gb);
+        }
+    }
+}
+
 struct BwdLayout {
-    size_t Sst, dSt, ac, dqp, dkp, dgp;
+    size_t Sst, dSt, ac;
     size_t dnum, dden;   // KATH only
     size_t total;
 };
@@ -553,16 +541,13 @@ BwdLayout bwd_layout(const Problem& p) {
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
     const bool ka = p.variant == LA_KATH;
     const size_t sw = size_t(p.dv) + (ka ? VT : 0);
-    const size_t nseq = size_t(p.B) * p.H, ntiles = sw / VT;
+    const size_t nseq = size_t(p.B) * p.H;
     const size_t nchunks = size_t((p.N + C - 1) / C), ntok = nseq * size_t(p.N);
     BwdLayout L{};
     size_t off = 0;
     L.Sst = off; off += al(nseq * nchunks * p.dk * sw * 4);
     L.dSt = off; off += al(nseq * nchunks * p.dk * sw * 4);
     L.ac = off; off += al(nseq * nchunks * (scalar_gate_rt(p.variant) ? 1 : p.dk) * 4);
-    L.dqp = off; off += al(ntiles * ntok * p.dk * 4);
-    L.dkp = off; off += al(ntiles * ntok * p.dk * 4);
-    L.dgp = off; off += ka ? 0 : al(ntiles * ntok * p.dk * 4);
     if (ka) {
         L.dnum = off; off += al(ntok * p.dv * 4);
         L.dden = off; off += al(ntok * 4);
@@ -574,9 +559,7 @@ BwdLayout bwd_layout(const Problem& p) {
 template <int VAR, int DK, int DV>
 hipError_t launch_dims(const Problem& p, BwdArgs a) {
     constexpr int SW = state_width<VAR, DV>();
-    const size_t ntok = size_t(a.nseq) * a.N;
     hipError_t e;
-    const unsigned units = unsigned(size_t(a.nseq) * a.nchunks * a.ntiles);
     const unsigned chunks = unsigned(size_t(a.nseq) * a.nchunks);   // sums: one per chunk
     const size_t nel = size_t(a.nseq) * DK * SW;
     const dim3 scan_grid(unsigned((nel + NT - 1) / NT));
@@ -598,12 +581,7 @@ hipError_t launch_dims(const Problem& p, BwdArgs a) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     bwd_scans_kernel<VAR, DK, DV><<<scan_grid, dim3(NT), 0, p.stream>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    bwd_grads_kernel<VAR, DK, DV><<<dim3(units), dim3(NT), 0, p.stream>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const size_t sblocks = (scalar_gate<VAR>() && VAR != LA_KATH)
-                               ? (ntok + NT / kWave - 1) / (NT / kWave)
-                               : (ntok * DK + NT - 1) / NT;
-    bwd_sum_kernel<VAR, DK><<<dim3(unsigned(sblocks)), dim3(NT), 0, p.stream>>>(a);
+    bwd_grads_kernel<VAR, DK, DV><<<dim3(chunks), dim3(NT), 0, p.stream>>>(a);
     return hipGetLastError();
 }
 
@@ -678,9 +656,6 @@ hipError_t launch_backward(const BwdProblem& bp) {
     a.Sst = reinterpret_cast<float*>(ws + L.Sst);
     a.dSt = reinterpret_cast<float*>(ws + L.dSt);
     a.ac = reinterpret_cast<float*>(ws + L.ac);
-    a.dqp = reinterpret_cast<float*>(ws + L.dqp);
-    a.dkp = reinterpret_cast<float*>(ws + L.dkp);
-    a.dgp = ka ? nullptr : reinterpret_cast<float*>(ws + L.dgp);
     if (ka) {
         a.dnum = reinterpret_cast<float*>(ws + L.dnum);
         a.dden = reinterpret_cast<float*>(ws + L.dden);
