@@ -371,8 +371,11 @@ __global__ __launch_bounds__(NT, VAR == LA_KATH ? 3 : 2) void bwd_grads_kernel(B
     constexpr bool SG = scalar_gate<VAR>();
     constexpr bool KA = VAR == LA_KATH;
     constexpr int SW = state_width<VAR, DV>();
-    constexpr int MQ = C * DK / NT;   // (row, key dim) pairs per thread
-    static_assert((C * DK) % NT == 0 && NT % DK == 0, "pairs per thread");
+    // dQ / dK: work item (row pair rp, key block ib) = rows 2 rp, 2 rp + 1 and key dims
+    // 4 ib .. 4 ib + 3; 8 row pairs x DK / 4 key blocks, at most one item per thread
+    constexpr int NB = DK / 4, NI = (C / 2) * NB;
+    static_assert(NI <= NT && C == 16, "one dQ / dK item per thread");
+    constexpr int MQ = 8;   // outputs per item
     __shared__ ChunkSmem<DK, SG> sm;
     // rows padded to VT + 1 floats: the dQ / dK step reads a column down consecutive rows
     __shared__ float sdS[DK][VT + 1];    // gradient of the state leaving the chunk
@@ -446,21 +449,63 @@ __global__ __launch_bounds__(NT, VAR == LA_KATH ? 3 : 2) void bwd_grads_kernel(B
             for (int i = 0; i < DK; ++i) acc += sm.k[s][i] * EK(s, i) * sdS[i][c];
             if (s < n && c0 < DV) store_elem(a.dv, (tok0 + t0 + s) * DV + c0 + c, acc, iob);
         }
-        // this tile's share of dQ and dK
-#pragma unroll
-        for (int m = 0; m < MQ; ++m) {
-            const int idx = tid + NT * m, r = idx / DK, i = idx % DK;
-            float sd = 0.f, kv = 0.f;
+        // this tile's share of dQ and dK, 2 rows x 4 key dims per thread:
+        //   dq_ri += e^{B_ri} (dO_r . S_in[i, :]) + sum_{s<=r} A_rs e^{B_ri - B_si} k_si
+        //   dk_ri += e^{B_last,i - B_ri} (v_r . dS_out[i, :]) + sum_{t>=r} A_tr e^{B_ti - B_ri} q_ti
+        // (A and the pair factors are zero above the diagonal)
+        if (tid < NI) {
+            const int r0 = 2 * (tid / NB), i0 = 4 * (tid % NB);
+            float sd[2][4] = {}, kv[2][4] = {};
             for (int c = 0; c < VT; ++c) {
-                sd += sm.dO[r][c] * sSin[i][c];
-                kv += sdS[i][c] * sm.v[r][c];
+                const float o0 = sm.dO[r0][c], o1 = sm.dO[r0 + 1][c];
+                const float v0 = sm.v[r0][c], v1 = sm.v[r0 + 1][c];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float si = sSin[i0 + u][c], di = sdS[i0 + u][c];
+                    sd[0][u] += o0 * si;
+                    sd[1][u] += o1 * si;
+                    kv[0][u] += v0 * di;
+                    kv[1][u] += v1 * di;
+                }
             }
-            float q_ = EQ(r, i) * sd;
-            for (int s2 = 0; s2 <= r; ++s2) q_ += sA[r][s2] * sm.k[s2][i] * PF(r, s2, i);
-            float k_ = EK(r, i) * kv;
-            for (int t = r; t < C; ++t) k_ += sA[t][r] * sm.q[t][i] * PF(t, r, i);
-            dq[m] += q_;
-            dk[m] += k_;
+            float qa[2][4], ka[2][4];
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    qa[rr][u] = EQ(r0 + rr, i0 + u) * sd[rr][u];
+                    ka[rr][u] = EK(r0 + rr, i0 + u) * kv[rr][u];
+                }
+#pragma unroll 2
+            for (int s2 = 0; s2 < C; ++s2) {
+                const float a0 = sA[r0][s2], a1 = sA[r0 + 1][s2];      // q side: rows >= s2
+                const float b0 = sA[s2][r0], b1 = sA[s2][r0 + 1];      // k side: rows <= s2
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = i0 + u;
+                    const float kk = sm.k[s2][i], qq = sm.q[s2][i];
+                    if (SG) {
+                        qa[0][u] += a0 * sm.pd[r0][s2] * kk;
+                        qa[1][u] += a1 * sm.pd[r0 + 1][s2] * kk;
+                        ka[0][u] += b0 * sm.pd[s2][r0] * qq;
+                        ka[1][u] += b1 * sm.pd[s2][r0 + 1] * qq;
+                    } else {
+                        const float ls = sm.lg[s2][i];
+                        const float l0 = sm.lg[r0][i], l1 = sm.lg[r0 + 1][i];
+                        if (s2 <= r0) qa[0][u] += a0 * kk * __builtin_amdgcn_exp2f(l0 - ls);
+                        if (s2 <= r0 + 1) qa[1][u] += a1 * kk * __builtin_amdgcn_exp2f(l1 - ls);
+                        if (s2 >= r0) ka[0][u] += b0 * qq * __builtin_amdgcn_exp2f(ls - l0);
+                        if (s2 >= r0 + 1) ka[1][u] += b1 * qq * __builtin_amdgcn_exp2f(ls - l1);
+                    }
+                }
+            }
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    dq[rr * 4 + u] += qa[rr][u];
+                    dk[rr * 4 + u] += ka[rr][u];
+                }
         }
         // this tile's share of dg: thread (row group rg, column c) owns elements (rg + 16 m,
         // c); for each it rebuilds S_{s-1} forward and dS_s backward over the chunk, and the
@@ -504,8 +549,8 @@ __global__ __launch_bounds__(NT, VAR == LA_KATH ? 3 : 2) void bwd_grads_kernel(B
     // final dq, dk (KATH: through phi'(x) = min(phi(x), 1), phi of the inputs in LDS)
 #pragma unroll
     for (int m = 0; m < MQ; ++m) {
-        const int idx = tid + NT * m, r = idx / DK, i = idx % DK;
-        if (r >= n) continue;
+        const int r = 2 * (tid / NB) + m / 4, i = 4 * (tid % NB) + m % 4;
+        if (tid >= NI || r >= n) continue;
         float q_ = dq[m], k_ = dk[m];
         if (KA) {
             q_ *= fminf(sm.q[r][i], 1.f);
