@@ -95,6 +95,17 @@ struct ChunkSmem {
     float v[C][VT], dO[C][VT];
 };
 
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
+template <class T>
+__device__ __forceinline__ float ld(const void* p, size_t i) {
+    return to_f32(static_cast<const T*>(p)[i]);
+}
+
+// The loaders below fix the storage type once per call and read rows past the end of the
+// sequence as its last row (zeroed afterwards), so their loads form one straight run that
+// the compiler can issue together instead of one branch per element.
+
 // The value tile (columns c0 .. c0 + VT - 1) of v and dO for one chunk; KATH's extra tile
 // holds the normaliser column (v = 1, output gradient dden).
 template <int VAR, int DK, int DV, bool SG>
@@ -105,22 +116,25 @@ __device__ __forceinline__ void load_tile(ChunkSmem<DK, SG>& sm, const BwdArgs& 
     const bool iob = a.io_bf16 != 0;
     {
         const int r = tid / VT, c = tid % VT;
-        const size_t tk = tok0 + t0 + r, e = tk * DV + c0 + c;
+        const size_t tk = tok0 + t0 + min(r, n - 1), e = tk * DV + c0 + c;   // n >= 1
         float vv = 0.f, dd = 0.f;
-        if (r < n) {
-            if (!KA) {
-                vv = load_elem(a.v, e, iob);
-                dd = load_elem(a.dO, e, iob);
-            } else if (c0 < DV) {
-                vv = load_elem(a.v, e, iob);
-                dd = a.dnum[e];
-            } else if (c == 0) {   // the normaliser column
-                vv = 1.f;
-                dd = a.dden[tk];
+        if (!KA) {
+            if (iob) {
+                vv = ld<uint16_t>(a.v, e);
+                dd = ld<uint16_t>(a.dO, e);
+            } else {
+                vv = ld<float>(a.v, e);
+                dd = ld<float>(a.dO, e);
             }
+        } else if (c0 < DV) {
+            vv = iob ? ld<uint16_t>(a.v, e) : ld<float>(a.v, e);
+            dd = a.dnum[e];
+        } else if (c == 0) {   // the normaliser column
+            vv = 1.f;
+            dd = a.dden[tk];
         }
-        sm.v[r][c] = vv;
-        sm.dO[r][c] = dd;
+        sm.v[r][c] = r < n ? vv : 0.f;
+        sm.dO[r][c] = r < n ? dd : 0.f;
     }
 }
 
@@ -130,22 +144,50 @@ __device__ __forceinline__ void load_chunk(ChunkSmem<DK, SG>& sm, const BwdArgs&
     constexpr bool KA = VAR == LA_KATH;
     const int tid = threadIdx.x;
     const bool iob = a.io_bf16 != 0, gb = a.gate_bf16 != 0;
-    for (int idx = tid; idx < C * DK; idx += NT) {
-        const int r = idx / DK, i = idx % DK;
-        const size_t e = (tok0 + t0 + r) * DK + i;
-        float qv = r < n ? load_elem(a.q, e, iob) : 0.f;
-        float kv = r < n ? load_elem(a.k, e, iob) : 0.f;
-        if (KA && r < n) {
-            qv = elu_plus_one(qv);
-            kv = elu_plus_one(kv);
+    constexpr int NL = C * DK / NT;   // elements per thread (n >= 1)
+    static_assert(NL * NT == C * DK, "row tiling");
+    auto qk = [&](auto tag) {
+        using T = decltype(tag);
+        float qv[NL], kv[NL];
+#pragma unroll
+        for (int m = 0; m < NL; ++m) {
+            const int idx = tid + NT * m, r = idx / DK, i = idx % DK;
+            const size_t e = (tok0 + t0 + min(r, n - 1)) * DK + i;
+            qv[m] = ld<T>(a.q, e);
+            kv[m] = ld<T>(a.k, e);
         }
-        sm.q[r][i] = qv;
-        sm.k[r][i] = kv;
-        if (!SG) {
-            const float gv = r < n ? load_elem(a.g, e, gb) : 1.f;
-            sm.gt[r][i] = gv;
-            sm.lg[r][i] = __builtin_amdgcn_logf(gv);
+#pragma unroll
+        for (int m = 0; m < NL; ++m) {
+            const int idx = tid + NT * m, r = idx / DK, i = idx % DK;
+            sm.q[r][i] = r < n ? (KA ? elu_plus_one(qv[m]) : qv[m]) : 0.f;
+            sm.k[r][i] = r < n ? (KA ? elu_plus_one(kv[m]) : kv[m]) : 0.f;
         }
+    };
+    auto gates = [&](auto tag) {
+        using T = decltype(tag);
+        float gv[NL];
+#pragma unroll
+        for (int m = 0; m < NL; ++m) {
+            const int idx = tid + NT * m, r = idx / DK, i = idx % DK;
+            gv[m] = ld<T>(a.g, (tok0 + t0 + min(r, n - 1)) * DK + i);
+        }
+#pragma unroll
+        for (int m = 0; m < NL; ++m) {
+            const int idx = tid + NT * m, r = idx / DK, i = idx % DK;
+            const float g_ = r < n ? gv[m] : 1.f;
+            sm.gt[r][i] = g_;
+            sm.lg[r][i] = __builtin_amdgcn_logf(g_);
+        }
+    };
+    if (iob)
+        qk(uint16_t{});
+    else
+        qk(float{});
+    if (!SG) {
+        if (gb)
+            gates(uint16_t{});
+        else
+            gates(float{});
     }
     if (SG && tid < C) {
         const float gv = (tid < n && !KA) ? load_elem(a.g, tok0 + t0 + tid, gb) : 1.f;
@@ -304,61 +346,161 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
-// KATH: the forward's num_t and den_t of every chunk, from the chunk-entering state and
-// normaliser (the state half of the scans), then dnum = dO / den and dden = -(dO . num) /
-// den^2. One workgroup per (sequence, chunk), looping over the value tiles.
+// KATH, one workgroup per (sequence, chunk): the forward's numerator num_t = phi(q_t)^T S_t
+// and denominator den_t (state and normaliser entering the chunk, from the state half of
+// the scans, plus the causal in-chunk part; fp32) give dnum = dO / den and dden = -(dO .
+// num) / den^2, the output gradients of the state and normaliser recurrences. Every global
+// load of the chunk is issued at once and staged in LDS, so a chunk waits on memory about
+// once; DV / 16 wavefronts (at most 4), each over its own slice of
+// the value columns, and each thread owns RPG rows x 4 columns of num.
+constexpr int kath_out_threads(int dv) { return 64 * (dv / 16 < 4 ? dv / 16 : 4); }
 template <int DK, int DV>
-__global__ __launch_bounds__(NT) void kath_out_kernel(BwdArgs a) {
-    constexpr int SW = DV + VT;
-    __shared__ float sq[C][DK + 1], sk[C][DK + 1];
-    __shared__ float sP[C][C + 1], sS[DK][VT + 1], sz[DK];
-    __shared__ float sv[C][VT], sdO[C][VT], sden[C];
-    const int tid = threadIdx.x;
+__global__ __launch_bounds__(kath_out_threads(DV)) void kath_out_kernel(BwdArgs a) {
+    constexpr int SW = DV + VT, L = kath_out_threads(DV), NW = L / 64;
+    constexpr int CG = DV / 4 / NW, RG = 64 / CG, RPG = C / RG;   // per wave: column groups,
+    static_assert(RG * RPG == C && RG * CG == 64, "thread tiling"); // row groups
+    constexpr int EP = 256 / L, LP = C / EP;   // P entries per thread, threads per row of P
+    static_assert(EP * L == C * C, "P tiling");
+    constexpr int TP = C + 4;                  // transposed row pitch, float4 aligned
+    constexpr int NQ = C * DK / L, NS = DK * DV / 4 / L, NV = C * DV / L;   // loads per thread
+    static_assert(NQ * L == C * DK && NS * 4 * L == DK * DV && NV * L == C * DV, "loads");
+    __shared__ __align__(16) float sqT[DK][TP];     // phi(q): [key dim][row]
+    __shared__ __align__(16) float skT[DK][TP];     // phi(k): [key dim][row]
+    __shared__ __align__(16) float sS[DK][DV];      // state entering the chunk
+    __shared__ __align__(16) float sv[C][DV];
+    __shared__ float sP[C][C + 1], sz[DK], sden[C], sw[NW][C];
+    const int lane = threadIdx.x;
     const int ch = int(blockIdx.x % unsigned(a.nchunks));
     const size_t seq = blockIdx.x / unsigned(a.nchunks);
-    const int t0 = ch * C, n = min(C, a.N - t0);
+    const int t0 = ch * C, n = min(C, a.N - t0), nl = n - 1;   // n >= 1
     const size_t tok = seq * size_t(a.N) + t0;
     const bool iob = a.io_bf16 != 0;
     const size_t sbase = (seq * a.nchunks + ch) * size_t(DK) * SW;
-    for (int idx = tid; idx < C * DK; idx += NT) {
-        const int r = idx / DK, i = idx % DK;
-        const size_t e = (tok + r) * DK + i;
-        sq[r][i] = r < n ? elu_plus_one(load_elem(a.q, e, iob)) : 0.f;
-        sk[r][i] = r < n ? elu_plus_one(load_elem(a.k, e, iob)) : 0.f;
+    const int wv = lane / 64, cg = lane % CG, r0 = (lane % 64 / CG) * RPG;
+    const int x0 = 4 * (wv * CG + cg);
+
+    // all loads first (rows past the end clamped to the last row and zeroed below), with
+    // the storage type fixed once so that the loads are not split by per-element branches
+    float qr[NQ], kr[NQ], vr[NV], dr[RPG][4];
+    auto load_all = [&](auto tag) {
+        using T = decltype(tag);
+        const T* q = static_cast<const T*>(a.q);
+        const T* k = static_cast<const T*>(a.k);
+        const T* v = static_cast<const T*>(a.v);
+        const T* dO = static_cast<const T*>(a.dO);
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) {
+            const int idx = lane + L * m, r = idx / DK, i = idx % DK;
+            const size_t e = (tok + min(r, nl)) * DK + i;
+            qr[m] = to_f32(q[e]);
+            kr[m] = to_f32(k[e]);
+        }
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+            const int idx = lane + L * m, r = idx / DV, c = idx % DV;
+            vr[m] = to_f32(v[(tok + min(r, nl)) * DV + c]);
+        }
+#pragma unroll
+        for (int rr = 0; rr < RPG; ++rr)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                dr[rr][u] = to_f32(dO[(tok + min(r0 + rr, nl)) * DV + x0 + u]);
+    };
+    if (iob)
+        load_all(uint16_t{});
+    else
+        load_all(float{});
+#pragma unroll
+    for (int m = 0; m < NS; ++m) {
+        const int idx = lane + L * m, i = idx / (DV / 4), c4 = idx % (DV / 4);
+        *reinterpret_cast<float4*>(&sS[i][4 * c4]) =
+            *reinterpret_cast<const float4*>(a.Sst + sbase + size_t(i) * SW + 4 * c4);
     }
-    for (int i = tid; i < DK; i += NT) sz[i] = a.Sst[sbase + size_t(i) * SW + DV];
+    for (int i = lane; i < DK; i += L) sz[i] = a.Sst[sbase + size_t(i) * SW + DV];
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+        const int idx = lane + L * m, r = idx / DK, i = idx % DK;
+        sqT[i][r] = r < n ? elu_plus_one(qr[m]) : 0.f;
+        skT[i][r] = r < n ? elu_plus_one(kr[m]) : 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+        const int idx = lane + L * m, r = idx / DV, c = idx % DV;
+        sv[r][c] = r < n ? vr[m] : 0.f;
+    }
     __syncthreads();
-    const int t = tid / C, x = tid % C;   // (row, column) of the 16 x 16 maps
     {
-        float p = 0.f, zq = 0.f;
-        if (x <= t)
-            for (int i = 0; i < DK; ++i) p += sq[t][i] * sk[x][i];
-        sP[t][x] = p;
-        for (int i = x; i < DK; i += C) zq += sq[t][i] * sz[i];
-        const float den = row16_sum(zq + p) + a.eps;   // phi(q_t).z_in + sum_s P_ts + eps
-        if (x == 0) sden[t] = den;
-    }
-    float w = 0.f;   // dO_t . num_t (lane x == 0 of row t)
-    for (int c0 = 0; c0 < DV; c0 += VT) {
-        __syncthreads();
-        for (int idx = tid; idx < DK * VT; idx += NT) {
-            const int i = idx / VT, j = idx % VT;
-            sS[i][j] = a.Sst[sbase + size_t(i) * SW + c0 + j];
+        // P_ts = phi(q_t) . phi(k_s) (s <= t), thread -> row t, columns s0 .. s0 + EP - 1;
+        // den_t = phi(q_t) . z_in + sum_s P_ts + eps, the z part split over the LP threads
+        // (consecutive lanes) of row t
+        const int t = lane / LP, s0 = (lane % LP) * EP;
+        float p[EP] = {}, zq = 0.f;
+#pragma unroll 4
+        for (int i = 0; i < DK; ++i) {
+            const float qi = sqT[i][t];
+#pragma unroll
+            for (int u = 0; u < EP; ++u) p[u] += qi * skT[i][s0 + u];
         }
-        {
-            const size_t e = (tok + t) * DV + c0 + x;
-            sv[t][x] = t < n ? load_elem(a.v, e, iob) : 0.f;
-            sdO[t][x] = t < n ? load_elem(a.dO, e, iob) : 0.f;
+        for (int i = lane % LP; i < DK; i += LP) zq += sqT[i][t] * sz[i];
+#pragma unroll
+        for (int u = 0; u < EP; ++u) {
+            const float pu = s0 + u <= t ? p[u] : 0.f;
+            sP[t][s0 + u] = pu;
+            zq += pu;
         }
-        __syncthreads();
-        float num = 0.f;
-        for (int i = 0; i < DK; ++i) num += sq[t][i] * sS[i][x];
-        for (int s2 = 0; s2 <= t; ++s2) num += sP[t][s2] * sv[s2][x];
-        const float d = sdO[t][x];
-        w += row16_sum(d * num);
-        if (t < n) a.dnum[(tok + t) * DV + c0 + x] = d / sden[t];
+#pragma unroll
+        for (int m = 1; m < LP; m <<= 1) zq += __shfl_xor(zq, m);
+        if (lane % LP == 0) sden[t] = zq + a.eps;
     }
-    if (x == 0 && t < n) a.dden[tok + t] = -w / (sden[t] * sden[t]);
+    __syncthreads();
+    float num[RPG][4] = {};
+#pragma unroll 8
+    for (int i = 0; i < DK; ++i) {
+        const float4 s4 = *reinterpret_cast<const float4*>(&sS[i][x0]);
+#pragma unroll
+        for (int rr = 0; rr < RPG; ++rr) {
+            const float qv = sqT[i][r0 + rr];
+            num[rr][0] += qv * s4.x;
+            num[rr][1] += qv * s4.y;
+            num[rr][2] += qv * s4.z;
+            num[rr][3] += qv * s4.w;
+        }
+    }
+#pragma unroll 4
+    for (int s2 = 0; s2 < C; ++s2) {   // sP is zero above the diagonal, sv past the end
+        const float4 v4 = *reinterpret_cast<const float4*>(&sv[s2][x0]);
+#pragma unroll
+        for (int rr = 0; rr < RPG; ++rr) {
+            const float pv = sP[r0 + rr][s2];
+            num[rr][0] += pv * v4.x;
+            num[rr][1] += pv * v4.y;
+            num[rr][2] += pv * v4.z;
+            num[rr][3] += pv * v4.w;
+        }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RPG; ++rr) {
+        const int t = r0 + rr;
+        const float den = sden[t];
+        float w = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w += dr[rr][u] * num[rr][u];
+        if (t < n)
+            *reinterpret_cast<float4*>(a.dnum + (tok + t) * DV + x0) =
+                make_float4(dr[rr][0] / den, dr[rr][1] / den, dr[rr][2] / den, dr[rr][3] / den);
+        // w_t: over the row group's CG consecutive lanes, then over the waves
+#pragma unroll
+        for (int m = 1; m < CG; m <<= 1) w += __shfl_xor(w, m);
+        if (cg == 0) sw[wv][t] = w;
+    }
+    __syncthreads();
+    if (lane < n) {
+        float w = 0.f;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) w += sw[v][lane];
+        const float den = sden[lane];
+        a.dden[tok + lane] = -w / (den * den);
+    }
 }
 
 // ---------------------------------------------------------------------------- grads
@@ -615,7 +757,8 @@ hipError_t launch_dims(const Problem& p, BwdArgs a) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
         bwd_scans_kernel<VAR, DK, DV><<<scan_grid, dim3(NT), 0, p.stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        kath_out_kernel<DK, DV><<<dim3(unsigned(size_t(a.nseq) * a.nchunks)), dim3(NT), 0,
+        kath_out_kernel<DK, DV><<<dim3(unsigned(size_t(a.nseq) * a.nchunks)),
+                                  dim3(kath_out_threads(DV)), 0,
                                   p.stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         a.mode = 2;
