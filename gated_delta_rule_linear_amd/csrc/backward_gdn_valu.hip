@@ -233,29 +233,83 @@ __global__ __launch_bounds__(16 * CT, CT >= 32 ? 4 : 2) void bwd_chains_kernel(G
 #pragma unroll
     for (int m = 0; m < RG; ++m) S[m] = init ? init[sbase + size_t(i0 + m) * DV + c0 + j] : 0.f;
     float* ck = (rev ? a.dSck : a.Sck) + seq * size_t(a.nchunks) * DK * DV;
+    // A chunk's inputs are fetched into registers one chunk ahead (storage types fixed once,
+    // rows past the end read as the last row and zeroed when staged), so the chain waits on
+    // them only while the previous chunk computes.
+    constexpr int NLK = (C * DK + NTC - 1) / NTC;
+    float rk[NLK] = {}, rq[NLK] = {}, rg[NLK] = {};
+    float rlg = 1.f, rbt = 0.f, rx = 0.f, rT = 0.f, rP = 0.f;
+    auto fetch = [&](int ch) {
+        const int nl = min(C, a.N - ch * C) - 1;   // >= 0
+        const size_t tok = seq * size_t(a.N) + size_t(ch) * C;
+        auto io = [&](auto tag, auto rv) {
+            using T = decltype(tag);
+            constexpr bool R = decltype(rv)::value;
+#pragma unroll
+            for (int m = 0; m < NLK; ++m) {
+                const int idx = tid + NTC * m;
+                if (idx < C * DK) {
+                    const size_t e = (tok + min(idx / DK, nl)) * DK + idx % DK;
+                    rk[m] = ld<T>(a.k, e);
+                    if (R) rq[m] = ld<T>(a.q, e);
+                }
+            }
+            rx = ld<T>(R ? a.dO : a.v, (tok + min(t_me, nl)) * DV + c0 + j);
+        };
+        auto gates = [&](auto tag) {
+            using T = decltype(tag);
+            if (PK) {
+#pragma unroll
+                for (int m = 0; m < NLK; ++m) {
+                    const int idx = tid + NTC * m;
+                    if (idx < C * DK) rg[m] = ld<T>(a.g, (tok + min(idx / DK, nl)) * DK + idx % DK);
+                }
+            } else if (tid < C) {
+                rlg = ld<T>(a.g, tok + min(tid, nl));
+            }
+            if (tid < C) rbt = ld<T>(a.beta, tok + min(tid, nl));
+        };
+        if (iob) {
+            if (rev) io(uint16_t{}, std::true_type{});
+            else io(uint16_t{}, std::false_type{});
+        } else {
+            if (rev) io(float{}, std::true_type{});
+            else io(float{}, std::false_type{});
+        }
+        if (gb) gates(uint16_t{});
+        else gates(float{});
+        if (tid < C * C) {
+            const size_t off = (seq * a.nchunks + ch) * size_t(C * C);
+            rT = a.Tck[off + tid];
+            if (rev) rP = a.Pck[off + tid];
+        }
+    };
+    fetch(rev ? a.nchunks - 1 : 0);
     for (int it = 0; it < a.nchunks; ++it) {
         const int ch = rev ? a.nchunks - 1 - it : it;
         const int t0 = ch * C, n = min(C, a.N - t0);
-        const size_t tok = seq * size_t(a.N) + t0;
         __syncthreads();   // the previous chunk's readers are done
         float* ckc = ck + size_t(ch) * DK * DV;
 #pragma unroll
         for (int m = 0; m < RG; ++m) ckc[size_t(i0 + m) * DV + c0 + j] = S[m];
-        for (int idx = tid; idx < C * DK; idx += NTC) {
-            const int r = idx / DK, i = idx % DK;
-            const size_t e = (tok + r) * DK + i;
-            const bool in = r < n;
-            sm.k[r][i] = in ? load_elem(a.k, e, iob) : 0.f;
-            if (rev) sm.q[r][i] = in ? load_elem(a.q, e, iob) : 0.f;
-            if (PK) sm.w.bq[r][i] = in ? __builtin_amdgcn_logf(load_elem(a.g, e, gb)) : 0.f;
+#pragma unroll
+        for (int m = 0; m < NLK; ++m) {
+            const int idx = tid + NTC * m;
+            if (idx < C * DK) {
+                const int r = idx / DK, i = idx % DK;
+                const bool in = r < n;
+                sm.k[r][i] = in ? rk[m] : 0.f;
+                if (rev) sm.q[r][i] = in ? rq[m] : 0.f;
+                if (PK) sm.w.bq[r][i] = in ? __builtin_amdgcn_logf(rg[m]) : 0.f;
+            }
         }
         if (!PK) {
             if (tid < kWave) {   // one wave: log gates, their prefix sums, beta
                 const int r = tid;
                 float lg = 0.f, bt = 0.f;
                 if (r < n) {
-                    lg = __builtin_amdgcn_logf(load_elem(a.g, tok + r, gb));
-                    bt = load_elem(a.beta, tok + r, gb);
+                    lg = __builtin_amdgcn_logf(rlg);
+                    bt = rbt;
                 }
                 const float cs = wave_inclusive_scan(r < C ? lg : 0.f);
                 const float cl = __shfl(cs, C - 1);
@@ -266,14 +320,14 @@ __global__ __launch_bounds__(16 * CT, CT >= 32 ? 4 : 2) void bwd_chains_kernel(G
                 }
             }
         } else if (tid < C) {
-            sm.b[tid] = tid < n ? load_elem(a.beta, tok + tid, gb) : 0.f;
+            sm.b[tid] = tid < n ? rbt : 0.f;
         }
-        sm.x[t_me][j] = t_me < n ? load_elem(rev ? a.dO : a.v, (tok + t_me) * DV + c0 + j, iob) : 0.f;
+        sm.x[t_me][j] = t_me < n ? rx : 0.f;
         if (tid < C * C) {
-            const size_t off = (seq * a.nchunks + ch) * size_t(C * C);
-            sm.T[tid / C][tid % C] = a.Tck[off + tid];
-            if (rev) sm.P[tid / C][tid % C] = a.Pck[off + tid];
+            sm.T[tid / C][tid % C] = rT;
+            if (rev) sm.P[tid / C][tid % C] = rP;
         }
+        if (it + 1 < a.nchunks) fetch(rev ? ch - 1 : ch + 1);
         __syncthreads();
         if (PK) {   // prefix sums per key dim, then the decayed key (and query) rows
             for (int i = tid; i < DK; i += NTC) {

@@ -95,13 +95,6 @@ struct ChunkSmem {
     float v[C][VT], dO[C][VT];
 };
 
-__device__ __forceinline__ float to_f32(float x) { return x; }
-__device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
-template <class T>
-__device__ __forceinline__ float ld(const void* p, size_t i) {
-    return to_f32(static_cast<const T*>(p)[i]);
-}
-
 // The loaders below fix the storage type once per call and read rows past the end of the
 // sequence as its last row (zeroed afterwards), so their loads form one straight run that
 // the compiler can issue together instead of one branch per element.

@@ -60,6 +60,15 @@ __device__ __forceinline__ float load_elem(const void* p, size_t i, bool bf16) {
                 : static_cast<const float*>(p)[i];
 }
 
+// Element i of an array whose storage type is fixed at compile time (float or bf16 bits):
+// loaders that pick the type once per call keep their loads in one straight run.
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
+template <class T>
+__device__ __forceinline__ float ld(const void* p, size_t i) {
+    return to_f32(static_cast<const T*>(p)[i]);
+}
+
 __device__ __forceinline__ void store_elem(void* p, size_t i, float x, bool bf16) {
     if (bf16)
         static_cast<uint16_t*>(p)[i] = f32_to_bf16(x);
