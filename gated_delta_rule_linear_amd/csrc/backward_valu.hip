@@ -99,36 +99,47 @@ struct ChunkSmem {
 // sequence as its last row (zeroed afterwards), so their loads form one straight run that
 // the compiler can issue together instead of one branch per element.
 
-// The value tile (columns c0 .. c0 + VT - 1) of v and dO for one chunk; KATH's extra tile
-// holds the normaliser column (v = 1, output gradient dden).
-template <int VAR, int DK, int DV, bool SG>
-__device__ __forceinline__ void load_tile(ChunkSmem<DK, SG>& sm, const BwdArgs& a, size_t tok0,
-                                          int t0, int n, int c0) {
+// The value tile (columns c0 .. c0 + VT - 1) of v and dO for one chunk, one element of each
+// per thread: fetched into registers (so the next tile can be in flight while this one
+// works), then stashed in LDS. KATH's extra tile holds the normaliser column (v = 1, output
+// gradient dden).
+template <int VAR, int DV>
+__device__ __forceinline__ float2 fetch_tile(const BwdArgs& a, size_t tok0, int t0, int n, int c0) {
     constexpr bool KA = VAR == LA_KATH;
     const int tid = threadIdx.x;
     const bool iob = a.io_bf16 != 0;
-    {
-        const int r = tid / VT, c = tid % VT;
-        const size_t tk = tok0 + t0 + min(r, n - 1), e = tk * DV + c0 + c;   // n >= 1
-        float vv = 0.f, dd = 0.f;
-        if (!KA) {
-            if (iob) {
-                vv = ld<uint16_t>(a.v, e);
-                dd = ld<uint16_t>(a.dO, e);
-            } else {
-                vv = ld<float>(a.v, e);
-                dd = ld<float>(a.dO, e);
-            }
-        } else if (c0 < DV) {
-            vv = iob ? ld<uint16_t>(a.v, e) : ld<float>(a.v, e);
-            dd = a.dnum[e];
-        } else if (c == 0) {   // the normaliser column
-            vv = 1.f;
-            dd = a.dden[tk];
+    const int r = tid / VT, c = tid % VT;
+    const size_t tk = tok0 + t0 + min(r, n - 1), e = tk * DV + c0 + c;   // n >= 1
+    float vv = 0.f, dd = 0.f;
+    if (!KA) {
+        if (iob) {
+            vv = ld<uint16_t>(a.v, e);
+            dd = ld<uint16_t>(a.dO, e);
+        } else {
+            vv = ld<float>(a.v, e);
+            dd = ld<float>(a.dO, e);
         }
-        sm.v[r][c] = r < n ? vv : 0.f;
-        sm.dO[r][c] = r < n ? dd : 0.f;
+    } else if (c0 < DV) {
+        vv = iob ? ld<uint16_t>(a.v, e) : ld<float>(a.v, e);
+        dd = a.dnum[e];
+    } else if (c == 0) {   // the normaliser column
+        vv = 1.f;
+        dd = a.dden[tk];
     }
+    return make_float2(vv, dd);
+}
+
+template <int DK, bool SG>
+__device__ __forceinline__ void stash_tile(ChunkSmem<DK, SG>& sm, float2 x, int n) {
+    const int r = int(threadIdx.x) / VT, c = int(threadIdx.x) % VT;
+    sm.v[r][c] = r < n ? x.x : 0.f;
+    sm.dO[r][c] = r < n ? x.y : 0.f;
+}
+
+template <int VAR, int DK, int DV, bool SG>
+__device__ __forceinline__ void load_tile(ChunkSmem<DK, SG>& sm, const BwdArgs& a, size_t tok0,
+                                          int t0, int n, int c0) {
+    stash_tile(sm, fetch_tile<VAR, DV>(a, tok0, t0, n, c0), n);
 }
 
 template <int VAR, int DK, int DV, bool SG>
@@ -239,22 +250,54 @@ __global__ __launch_bounds__(NT) void bwd_sums_kernel(BwdArgs a) {
     auto EQ = [&](int r, int i) { return SG ? sm.seq[r] : sm.eq[r][i]; };
     auto EK = [&](int r, int i) { return SG ? sm.sek[r] : sm.ek[r][i]; };
     const size_t sbase = (u.seq * a.nchunks + u.ch) * size_t(DK) * SW;
+    // thread -> key dim i and CPT consecutive columns of every tile; its decayed key and
+    // query columns stay in registers across the tiles, so a multiply-add reads LDS once
+    // (a value row element shared by the lanes of one column run)
+    constexpr int CPT = DK * VT / NT;
+    static_assert(CPT >= 1 && CPT * NT == DK * VT, "columns per thread");
+    const int i = int(threadIdx.x) % DK, cb = (int(threadIdx.x) / DK) * CPT;
+    float wk[C], wq[C];
+#pragma unroll
+    for (int s_ = 0; s_ < C; ++s_) {
+        wk[s_] = EK(s_, i) * sm.k[s_][i];
+        wq[s_] = EQ(s_, i) * sm.q[s_][i];
+    }
+    auto put = [&](float* dst, const float (&x)[CPT]) {
+        if constexpr (CPT % 4 == 0) {
+#pragma unroll
+            for (int u2 = 0; u2 < CPT; u2 += 4)
+                *reinterpret_cast<float4*>(dst + u2) = make_float4(x[u2], x[u2 + 1], x[u2 + 2], x[u2 + 3]);
+        } else {
+#pragma unroll
+            for (int u2 = 0; u2 < CPT; ++u2) dst[u2] = x[u2];
+        }
+    };
+    float2 nx = make_float2(0.f, 0.f);   // the next tile's v and dO element
+    if (a.ntiles > 1) nx = fetch_tile<VAR, DV>(a, tok0, t0, n, VT);
     for (int tile = 0; tile < a.ntiles; ++tile) {
         const int c0 = tile * VT;
         if (tile > 0) {
             __syncthreads();   // the previous tile's readers are done
-            load_tile<VAR, DK, DV, SG>(sm, a, tok0, t0, n, c0);
+            stash_tile(sm, nx, n);
+            if (tile + 1 < a.ntiles) nx = fetch_tile<VAR, DV>(a, tok0, t0, n, c0 + VT);
             __syncthreads();
         }
-        for (int idx = threadIdx.x; idx < DK * VT; idx += NT) {
-            const int i = idx / VT, c = idx % VT;
-            float ds = 0.f, gq = 0.f;
-            if (a.mode & 1)
-                for (int s_ = 0; s_ < C; ++s_) ds += EK(s_, i) * sm.k[s_][i] * sm.v[s_][c];
-            if (a.mode & 2)
-                for (int s_ = 0; s_ < C; ++s_) gq += EQ(s_, i) * sm.q[s_][i] * sm.dO[s_][c];
-            if (a.mode & 1) a.Sst[sbase + size_t(i) * SW + c0 + c] = ds;
-            if (a.mode & 2) a.dSt[sbase + size_t(i) * SW + c0 + c] = gq;
+        const size_t o = sbase + size_t(i) * SW + c0 + cb;
+        if (a.mode & 1) {   // dS_c = sum_s diag(e^{B_last - B_s}) k_s v_s^T
+            float ds[CPT] = {};
+#pragma unroll
+            for (int s_ = 0; s_ < C; ++s_)
+#pragma unroll
+                for (int u2 = 0; u2 < CPT; ++u2) ds[u2] += wk[s_] * sm.v[s_][cb + u2];
+            put(a.Sst + o, ds);
+        }
+        if (a.mode & 2) {   // G_c = sum_r diag(e^{B_r}) q_r dO_r^T
+            float gq[CPT] = {};
+#pragma unroll
+            for (int s_ = 0; s_ < C; ++s_)
+#pragma unroll
+                for (int u2 = 0; u2 < CPT; ++u2) gq[u2] += wq[s_] * sm.dO[s_][cb + u2];
+            put(a.dSt + o, gq);
         }
     }
     {
@@ -561,12 +604,33 @@ __global__ __launch_bounds__(NT, VAR == LA_KATH ? 3 : 2) void bwd_grads_kernel(B
 #pragma unroll
     for (int m = 0; m < MQ; ++m) dq[m] = dk[m] = 0.f;
 
+    // the next tile's state columns, v and dO are fetched into registers while this one works
+    constexpr int MSG = DK * VT / NT;
+    static_assert(MSG * NT == DK * VT, "state tile per thread");
+    float ps[MSG], pds[MSG];
+    float2 nx = make_float2(0.f, 0.f);
+    auto fetch_next = [&](int c0) {
+#pragma unroll
+        for (int m = 0; m < MSG; ++m) {
+            const int idx = tid + NT * m, i = idx / VT, c = idx % VT;
+            ps[m] = a.Sst[sbase + size_t(i) * SW + c0 + c];
+            pds[m] = a.dSt[sbase + size_t(i) * SW + c0 + c];
+        }
+        nx = fetch_tile<VAR, DV>(a, tok0, t0, n, c0);
+    };
+    if (a.ntiles > 1) fetch_next(VT);
     for (int tile = 0; tile < a.ntiles; ++tile) {
         const int c0 = tile * VT;
         if (tile > 0) {
             __syncthreads();   // the previous tile's readers are done
-            load_states(c0);
-            load_tile<VAR, DK, DV, SG>(sm, a, tok0, t0, n, c0);
+#pragma unroll
+            for (int m = 0; m < MSG; ++m) {
+                const int idx = tid + NT * m, i = idx / VT, c = idx % VT;
+                sSin[i][c] = ps[m];
+                sdS[i][c] = pds[m];
+            }
+            stash_tile(sm, nx, n);
+            if (tile + 1 < a.ntiles) fetch_next(c0 + VT);
         }
         __syncthreads();
         {   // A = (dO V^T) o M over this tile's value columns
