@@ -237,7 +237,7 @@ struct ChunkUnit {
 // one workgroup per (sequence, chunk): the chunk's rows and decay tables once, then every
 // value tile in turn
 template <int VAR, int DK, int DV>
-__global__ __launch_bounds__(NT) void bwd_sums_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT, VAR == LA_GLA ? 2 : 6) void bwd_sums_kernel(BwdArgs a) {
     constexpr bool SG = scalar_gate<VAR>();
     constexpr int SW = state_width<VAR, DV>();
     __shared__ ChunkSmem<DK, SG> sm;
@@ -336,8 +336,9 @@ __global__ __launch_bounds__(NT) void bwd_scans_kernel(BwdArgs a) {
     }
     // Chunks go in batches of SB: the batch's sums and decays are loaded before any of
     // its stores, so the loads are in flight together instead of each waiting behind the
-    // previous chunk's store to the same array.
-    constexpr int SB = 8;
+    // previous chunk's store to the same array. Wider batches pay off where the per-key-dim
+    // decays add a third load per chunk; the scalar-gate scans run near the HBM rate at 8.
+    constexpr int SB = SG ? 8 : 32;
     const int astr = SG ? 1 : DK;
     for (int c0 = 0; (a.mode & 1) && c0 < a.nchunks; c0 += SB) {
         float d[SB], g[SB];
