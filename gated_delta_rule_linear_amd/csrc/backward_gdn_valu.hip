@@ -45,6 +45,7 @@
 // d_k x C matrices S0 dO^T, dS' U^T and S0 dU^T besides A and B.
 #include "common.hpp"
 #include "la_internal.h"
+#include "mfma.hpp"
 
 namespace la {
 namespace {
@@ -431,7 +432,7 @@ struct GradSmem {
     alignas(16) float dO[C][VT];
     alignas(16) float U[C][VT];
     alignas(16) float dU[C][VT];
-    float KS[C][VT], X[C][VT], R[C][VT];
+    float KS[C][VT], KDS[C][VT], QS[C][VT], X[C][VT], R[C][VT];
     float A[C][C + 1], Bm[C][C + 1];
     float kap[C], rho[C], mu[C], dup[C];
     float sig[NT / kWave];
@@ -525,22 +526,33 @@ __global__ __launch_bounds__(NT, 3) void gdn_bwd_grads_kernel(GdnBwdArgs a) {
         sm.dO[r_me][x_me] = pdO;
         if (tile + 1 < a.ntiles) fetch(tile + 1);
         lds_barrier();
-        const int t = r_me, j = x_me;
-        float ks = 0.f, kds = 0.f, qs = 0.f;
-#pragma unroll 4
-        for (int i = 0; i < DK; i += 4) {
-            const float4 kv = *reinterpret_cast<const float4*>(&sm.rw.k[t][i]);
-            const float4 qv = *reinterpret_cast<const float4*>(&sm.rw.q[t][i]);
-            const float s0[4] = {sm.S0[i][j], sm.S0[i + 1][j], sm.S0[i + 2][j], sm.S0[i + 3][j]};
-            const float d0[4] = {sm.dS[i][j], sm.dS[i + 1][j], sm.dS[i + 2][j], sm.dS[i + 3][j]};
-            ks += kv.x * s0[0] + kv.y * s0[1] + kv.z * s0[2] + kv.w * s0[3];
-            kds += kv.x * d0[0] + kv.y * d0[1] + kv.z * d0[2] + kv.w * d0[3];
-            qs += qv.x * s0[0] + qv.y * s0[1] + qv.z * s0[2] + qv.w * s0[3];
+        {
+            // K S_in, K dS_out and Q S_in (16 x d_k by d_k x 16) on the fp32 matrix cores,
+            // one product per wave, two interleaved accumulators. Lane layout of the
+            // 16x16x4 fp32 MFMA (g = lane / 16, jl = lane % 16): A (16 x 4) row jl, k = g;
+            // B (4 x 16) column jl, k = g; D (16 x 16) column jl, rows 4g .. 4g + 3.
+            const int w = tid / kWave, l = tid % kWave, g = l >> 4, jl = l & 15;
+            if (w < 3) {
+                const float* Ar = w == 2 ? &sm.rw.q[jl][0] : &sm.rw.k[jl][0];
+                const float(*Bt)[VT + 4] = w == 1 ? sm.dS : sm.S0;
+                f32x4_t c0v = {0.f, 0.f, 0.f, 0.f}, c1v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+                for (int kk = 0; kk < DK; kk += 8) {
+                    c0v = __builtin_amdgcn_mfma_f32_16x16x4f32(Ar[kk + g], Bt[kk + g][jl], c0v, 0, 0, 0);
+                    c1v = __builtin_amdgcn_mfma_f32_16x16x4f32(Ar[kk + 4 + g], Bt[kk + 4 + g][jl],
+                                                                c1v, 0, 0, 0);
+                }
+                float(*Out)[VT] = w == 0 ? sm.KS : (w == 1 ? sm.KDS : sm.QS);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Out[4 * g + r][jl] = c0v[r] + c1v[r];
+            }
         }
+        lds_barrier();
+        const int t = r_me, j = x_me;
+        const float ks = sm.KS[t][j], kds = sm.KDS[t][j], qs = sm.QS[t][j];
         {
             float r_ = sm.rw.el[t] * kds;
             for (int r = t; r < C; ++r) r_ += sm.D[r][t] * sm.QK[r][t] * sm.dO[r][j];
-            sm.KS[t][j] = ks;
             sm.X[t][j] = sm.rw.b[t] * (sm.v[t][j] - sm.rw.eg[t] * ks);
             sm.R[t][j] = r_;
         }
