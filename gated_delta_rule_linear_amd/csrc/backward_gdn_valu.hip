@@ -807,18 +807,30 @@ __global__ __launch_bounds__(NT) void kda_bwd_grads_kernel(GdnBwdArgs a) {
         const int t = r_me, j = x_me;
         const int c0 = tile * VT;
         {
-            float ks = 0.f, kds = 0.f;
-#pragma unroll 4
-            for (int i = 0; i < DK; i += 4) {
-                const float4 kv = *reinterpret_cast<const float4*>(&sm.w.t.kd[t][i]);
-                const float4 tv = *reinterpret_cast<const float4*>(&sm.w.t.kt[t][i]);
-                ks += kv.x * sm.w.t.S0[i][j] + kv.y * sm.w.t.S0[i + 1][j] +
-                      kv.z * sm.w.t.S0[i + 2][j] + kv.w * sm.w.t.S0[i + 3][j];
-                kds += tv.x * sm.w.t.dS[i][j] + tv.y * sm.w.t.dS[i + 1][j] +
-                       tv.z * sm.w.t.dS[i + 2][j] + tv.w * sm.w.t.dS[i + 3][j];
+            // (decayed K) S_in into KS and (decayed K) dS_out into R on the fp32 matrix cores
+            // (16x16x4, one product per wave, two interleaved accumulators; A row jl with
+            // k = g, B column jl with k = g, D column jl with rows 4g .. 4g + 3)
+            const int w = tid / kWave, l = tid % kWave, g = l >> 4, jl = l & 15;
+            if (w < 2) {
+                const float* Ar = w == 0 ? &sm.w.t.kd[jl][0] : &sm.w.t.kt[jl][0];
+                const float(*Bt)[VT + 4] = w == 0 ? sm.w.t.S0 : sm.w.t.dS;
+                f32x4_t c0v = {0.f, 0.f, 0.f, 0.f}, c1v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+                for (int kk = 0; kk < DK; kk += 8) {
+                    c0v = __builtin_amdgcn_mfma_f32_16x16x4f32(Ar[kk + g], Bt[kk + g][jl], c0v, 0, 0, 0);
+                    c1v = __builtin_amdgcn_mfma_f32_16x16x4f32(Ar[kk + 4 + g], Bt[kk + 4 + g][jl],
+                                                                c1v, 0, 0, 0);
+                }
+                float(*Out)[VT] = w == 0 ? sm.KS : sm.R;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Out[4 * g + r][jl] = c0v[r] + c1v[r];
             }
+        }
+        lds_barrier();
+        {
+            const float ks = sm.KS[t][j];
+            float kds = sm.R[t][j];
             for (int r = t; r < C; ++r) kds += sm.P[r][t] * sm.dO[r][j];
-            sm.KS[t][j] = ks;
             sm.X[t][j] = sm.rw.b[t] * (sm.v[t][j] - ks);
             sm.R[t][j] = kds;
         }
