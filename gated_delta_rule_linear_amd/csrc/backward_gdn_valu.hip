@@ -432,7 +432,9 @@ struct GradSmem {
     alignas(16) float dO[C][VT];
     alignas(16) float U[C][VT];
     alignas(16) float dU[C][VT];
-    float KS[C][VT], KDS[C][VT], QS[C][VT], X[C][VT], R[C][VT];
+    // K dS_out and Q S_in land in X and R: thread (t, j) reads its own element of each
+    // into a register before it writes X[t][j] and R[t][j], and nothing reads them later
+    float KS[C][VT], X[C][VT], R[C][VT];
     float A[C][C + 1], Bm[C][C + 1];
     float kap[C], rho[C], mu[C], dup[C];
     float sig[NT / kWave];
@@ -542,14 +544,14 @@ __global__ __launch_bounds__(NT, 3) void gdn_bwd_grads_kernel(GdnBwdArgs a) {
                     c1v = __builtin_amdgcn_mfma_f32_16x16x4f32(Ar[kk + 4 + g], Bt[kk + 4 + g][jl],
                                                                 c1v, 0, 0, 0);
                 }
-                float(*Out)[VT] = w == 0 ? sm.KS : (w == 1 ? sm.KDS : sm.QS);
+                float(*Out)[VT] = w == 0 ? sm.KS : (w == 1 ? sm.X : sm.R);   // KS, K dS_out, Q S_in
 #pragma unroll
                 for (int r = 0; r < 4; ++r) Out[4 * g + r][jl] = c0v[r] + c1v[r];
             }
         }
         lds_barrier();
         const int t = r_me, j = x_me;
-        const float ks = sm.KS[t][j], kds = sm.KDS[t][j], qs = sm.QS[t][j];
+        const float ks = sm.KS[t][j], kds = sm.X[t][j], qs = sm.R[t][j];
         {
             float r_ = sm.rw.el[t] * kds;
             for (int r = t; r < C; ++r) r_ += sm.D[r][t] * sm.QK[r][t] * sm.dO[r][j];

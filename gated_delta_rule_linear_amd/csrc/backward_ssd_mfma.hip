@@ -179,7 +179,8 @@ struct __align__(16) GradsSmem {
     __align__(16) uint16_t v[C * PV], dO[C * PV];
     __align__(16) uint16_t sin[DK * PV], dso[DK * PV];   // S_in, dS_out as [key][column]
     __align__(16) uint16_t P[C * PV], A[C * PV], M[C * PV], Y[C * PV];
-    float c[C], alpha[C], beta[C], t2[C];
+    float c[C], alpha[C], beta[C];
+    float t2w[NT / 64][C];   // per-wave partials of term2, summed in wave order
     float red[NT / 64];
 };
 
@@ -193,7 +194,7 @@ __global__ __launch_bounds__(NT) void ssd_bwd_grads_kernel(SbArgs a) {
     const int ch = blockIdx.x % a.nch, t0 = ch * C, n = min(C, a.N - t0);
     const size_t tok0 = seq * size_t(a.N);
     chunk_logs<GB>(sm.c, a, tok0, t0, n);
-    if (tid < C) { sm.alpha[tid] = 0.f; sm.beta[tid] = 0.f; sm.t2[tid] = 0.f; }
+    if (tid < C) { sm.alpha[tid] = 0.f; sm.beta[tid] = 0.f; }
     stage_rows<DK, PQ>(sm.q, a.q, tok0, t0, n, [](int) { return 1.f; });
     stage_rows<DK, PQ>(sm.k, a.k, tok0, t0, n, [](int) { return 1.f; });
     stage_rows<DV, PV>(sm.v, a.v, tok0, t0, n, [](int) { return 1.f; });
@@ -330,7 +331,10 @@ __global__ __launch_bounds__(NT) void ssd_bwd_grads_kernel(SbArgs a) {
                 const int r = r0 + 4 * g + e;
                 if (s <= r) part += __builtin_amdgcn_exp2f(sm.c[r] - sm.c[s]) * z[e];
             }
-            atomicAdd(&sm.t2[s], part);
+            // the four lane groups' rows in a fixed order, then one partial per wave
+            part += __shfl_xor(part, 16, 64);
+            part += __shfl_xor(part, 32, 64);
+            if (g == 0) sm.t2w[w][s] = part;
         }
     }
     __syncthreads();
@@ -340,7 +344,9 @@ __global__ __launch_bounds__(NT) void ssd_bwd_grads_kernel(SbArgs a) {
         float t1 = 0.f, t4 = 0.f;
         for (int r = s; r < C; ++r) t1 += __builtin_amdgcn_exp2f(sm.c[r] - sm.c[s]) * sm.alpha[r];
         for (int u = 0; u < s; ++u) t4 += __builtin_amdgcn_exp2f(cm1(s) - sm.c[u]) * sm.beta[u];
-        const float da = es1 * t1 + sm.t2[s] + fs * es1 * gamma + fs * t4;
+        static_assert(NT == 256, "four waves");
+        const float t2 = ((sm.t2w[0][s] + sm.t2w[1][s]) + sm.t2w[2][s]) + sm.t2w[3][s];
+        const float da = es1 * t1 + t2 + fs * es1 * gamma + fs * t4;
         const size_t e = tok0 + t0 + s;
         if (GB) static_cast<uint16_t*>(a.dg)[e] = f32_to_bf16(da);
         else static_cast<float*>(a.dg)[e] = da;

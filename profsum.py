@@ -11,8 +11,8 @@ Two summaries are produced from rocprofv3's CSV files:
   copy. The result goes to ``traffic.json``, keyed by the hash of the kernel
   sources so that ``bench.py`` ignores it once a kernel changes.
 
-    python -m gated_delta_rule_linear_amd.profsum stats STATS_CSV OUT_TXT --command CMD
-    python -m gated_delta_rule_linear_amd.profsum traffic FETCH_CSV WRITE_CSV OUT_JSON OUT_TXT \
+    python profsum.py stats STATS_CSV OUT_TXT --command CMD
+    python profsum.py traffic FETCH_CSV WRITE_CSV OUT_JSON OUT_TXT \
         --command CMD
 """
 from __future__ import annotations
@@ -25,7 +25,7 @@ import os
 import re
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 
 # kernels that make up one step of each workload (matched on the demangled name)
 STEP_KERNELS = {

@@ -239,18 +239,19 @@ FULL = ["gla_bf16_b2h8_n2048_d128", "kath_bf16_b1h16_n32768_dk128_dv64",
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_workload_sampled(name):
-    """Full-size run in the benchmark's launch configuration; the oracle checks sampled
-    sequences (first, last and one in the middle) element by element."""
+def test_full_workload(name):
+    """Full-size run in the benchmark's launch configuration; the oracle runs every
+    sequence and o, S_final (z_final) are compared element by element on all of them."""
     wl = W.WORKLOADS[name]
     inp = W.make_inputs(wl)
     banner(f"full workload {name}")
     got = run_gpu(inp, path="auto")
+    ref = run_oracle(inp)
+    errs = check(inp, got, ref)
+    # the worst single sequence, against its own max|ref| (stricter than the per-tensor bound)
     nseq = wl.B * wl.H
-    seqs = [0, nseq // 2 + 1, nseq - 1]
-    for s in seqs:
-        ref = run_oracle(inp, seqs=[s])
-        errs = check(inp, got, ref, seqs=[s])
-        print(name, s, errs, flush=True)
-    o = got[0]
-    assert torch.isfinite(o.float()).all()
+    o = f64(got[0]).reshape(nseq, -1)
+    o_ref = ref[0].reshape(nseq, -1)
+    per_seq = np.max(np.abs(o - o_ref), axis=1) / np.max(np.abs(o_ref), axis=1)
+    print(name, errs, "worst sequence o", float(per_seq.max()), int(per_seq.argmax()), flush=True)
+    assert float(per_seq.max()) <= TOL["bf16"]
