@@ -20,7 +20,7 @@ LA_PATH_AUTO, LA_PATH_VALU, LA_PATH_MFMA = 0, 1, 2
 
 VARIANTS = {"kath": LA_KATH, "gla": LA_GLA, "gdn": LA_GDN, "kda": LA_KDA, "ssd": LA_SSD}
 PATHS = {"auto": LA_PATH_AUTO, "valu": LA_PATH_VALU, "mfma": LA_PATH_MFMA}
-EXPORTS = ("la_prefill", "la_prefill_workspace_size", "la_prefill_varlen",
+EXPORTS = ("la_prefill", "la_prefill_workspace_size", "la_prefill_noalloc", "la_prefill_varlen",
            "la_prefill_varlen_workspace_size", "la_decode_step", "la_prefill_backward",
            "la_prefill_backward_workspace_size", "la_selective_scan",
            "la_status_str", "la_abi_version")
@@ -65,6 +65,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     dp = ctypes.POINTER(Desc)
     lib.la_prefill.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.la_prefill.restype = ctypes.c_int
+    lib.la_prefill_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.la_prefill_noalloc.restype = ctypes.c_int
     lib.la_prefill_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
     lib.la_prefill_workspace_size.restype = ctypes.c_int
     i32 = ctypes.c_int32

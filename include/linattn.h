@@ -50,7 +50,8 @@
  * Ownership and threading: the caller allocates every buffer in device memory and
  * passes plain device pointers and a hipStream_t (NULL = the default stream). The
  * library never allocates, frees or synchronizes; calls only enqueue work on the
- * given stream and return. It keeps no mutable global state and is re-entrant.
+ * given stream and return. It keeps no mutable global state and is re-entrant, apart
+ * from the one device array per GPU that la_prefill_noalloc uses as its workspace.
  *
  * Errors: every entry point validates all arguments first. On any error it returns
  * a nonzero status, enqueues nothing and touches no output. No exception crosses
@@ -210,6 +211,25 @@ int la_prefill_backward(const la_desc* d, const void* q, const void* k, const vo
                         const void* dO, const float* dS_final, const float* dz_final, void* dq,
                         void* dk, void* dv, void* dg, void* dbeta, float* dS0, float* dz0,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* la_prefill without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, results and errors as la_prefill, minus the workspace: the workspace
+ * comes from one fixed array of LA_NOALLOC_SCRATCH_BYTES in the library's device code,
+ * one copy per GPU, held until the process ends. The call allocates nothing and calls no
+ * allocating routine.
+ *   A descriptor whose la_prefill_workspace_size exceeds LA_NOALLOC_SCRATCH_BYTES is
+ *   rejected with LA_ERR_WORKSPACE before anything is enqueued.
+ *   The stream must belong to the current device (LA_ERR_INVALID otherwise); NULL is the
+ *   current device's default stream.
+ *   Every call on one GPU uses that GPU's one array: calls whose work overlaps in time on
+ *   one GPU (different streams, or host threads) race on it and must be serialised by the
+ *   caller. Calls in order on one stream are safe; nothing in the array carries over from
+ *   one call to the next. */
+#define LA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int la_prefill_noalloc(const la_desc* d, const void* q, const void* k, const void* v,
+                       const void* g, const void* beta, const float* S0, const float* z0,
+                       void* o, float* S_final, float* z_final, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * Selective scan (Mamba-1 / S6): "Linear / RNN 路线", section 3.5 (the boxed
