@@ -277,8 +277,8 @@ def bench_varlen(name, steps, warmup, torch, bd, W, device, stream):
 
     ms, per = time_calls(fn, steps, warmup, torch, stream)
     tokens = int(cu[-1])
-    per = W.algorithmic_bytes_per_token_head(wl)
-    byts = tokens * wl.H * per + nseq * wl.H * wl.dk * wl.dv * 4
+    per_tok = W.algorithmic_bytes_per_token_head(wl)
+    byts = tokens * wl.H * per_tok + nseq * wl.H * wl.dk * wl.dv * 4
     flops = W.algorithmic_flops(wl)   # the packed layout's token count, B = 1
     s = ms / 1e3
     gbs = byts / s / 1e9

@@ -33,9 +33,15 @@ SOURCES = ["la_api.cpp", "decode.hip", "prefill_valu.hip", "prefill_kath_mfma.hi
            "prefill_gla_mfma.hip", "prefill_gdn_mfma.hip", "noalloc.hip"]
 
 
+# per-file code generation options: matrix-core results kept in ordinary vector registers
+# (no copies out of the accumulation registers) where a kernel's vector-ALU work consumes
+# them every chunk
+EXTRA = {"prefill_gdn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

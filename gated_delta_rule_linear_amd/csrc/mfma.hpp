@@ -220,6 +220,20 @@ __device__ __forceinline__ void buf_st16(rsrc_t r, uint32_t off, uint4 v) {
     typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, 0);
 }
+// The same with a constant byte offset folded into the instruction (0 .. 4095), for
+// loops whose per-lane offset register stays fixed while the resource moves.
+__device__ __forceinline__ uint4 buf_ld16_off(rsrc_t r, uint32_t off, int imm) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + uint32_t(imm), 0, 1));
+}
+__device__ __forceinline__ void buf_st8_off(rsrc_t r, uint32_t off, int imm, uint2 v) {
+    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, off + uint32_t(imm), 0, 0);
+}
+template <bool GB>
+__device__ __forceinline__ uint32_t buf_ld_gate_off(rsrc_t r, uint32_t off) {
+    if constexpr (GB) return buf_ld2(r, off);
+    else return buf_ld4(r, off);
+}
 // One gate element (bf16 or fp32 storage) as raw bits, converted with gate_val.
 template <bool GB>
 __device__ __forceinline__ uint32_t buf_ld_gate(rsrc_t r, uint32_t index) {

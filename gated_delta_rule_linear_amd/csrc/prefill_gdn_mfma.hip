@@ -24,21 +24,19 @@
 //   prep     one workgroup per (sequence, chunk), fully parallel: T = (I + L)^{-1} of
 //            every chunk, written to the workspace in bf16 and in MFMA fragment order
 //            (T depends only on the chunk's k, alpha, beta, never on the state);
-//   forward  one workgroup per (sequence, value tile): walks the chunks in order with
-//            its fp32 state tile in MFMA accumulators. Columns of S never mix, so value
-//            tiles are independent chains; the tiles of one sequence share an XCD so
-//            their q/k/T/P reads hit the same L2.
-// Per chunk the forward kernel has three barriers: (S^T q, S^T k) -> X | U = T X and
-// the causal score tile P_rs = exp(c_r - c_s) q_r.k_s (s <= r) of the wave's rows |
-// O = gamma (S^T q) + P U and S = gamma_last S + K^T U^. Each wave loads the operands
-// that only it uses (rows of q, T, V; its own alpha/beta) straight into registers in
-// fragment layout through per-sequence buffer resources, two chunks ahead; K and the
-// bf16 copy of S^T are shared through LDS. P stays in registers in the order the
-// matrix cores return it. Ragged tails need no branches: buffer loads past the
-// sequence read zeros and stores past it are dropped.
+//   forward  one workgroup per (sequence, value tile of 16 or 32 columns): chain waves
+//            that each carry 16 columns of the fp32 state through the chunks in
+//            registers (columns of S never mix, so a chain needs no other wave's
+//            results), and two output waves one chunk behind that form the causal
+//            score tiles P_rs = exp(c_r - c_s) q_r.k_s (s <= r) and the outputs
+//            O = gamma (S^T q) + P U from the copies of S and U the chains leave in LDS.
+//            One barrier per chunk; the tiles of one sequence share an XCD so their
+//            q / k / T reads hit the same L2.
 //
 // Fragments whose K index runs along tile rows use the LDS transpose read; result
 // tiles are written to LDS with 8-byte stores.
+#include <type_traits>
+
 #include "la_internal.h"
 #include "mfma.hpp"
 
@@ -61,17 +59,6 @@ struct __align__(16) PrepSmem {
     __align__(16) uint16_t yb[32 * PY];    // level-b scratch: Y = L[32:64, 0:32] A^{-1}
     __align__(16) float ld[4][16 * PD];    // diagonal blocks of L, fp32
     float cum[C], beta[C];
-};
-
-template <int VT>
-struct __align__(16) FwdSmem {
-    static constexpr int PV = VT + 8;
-    __align__(16) uint16_t k[2][C * PQ];   // K [s][i] of the current and the next chunk
-    __align__(16) uint16_t st[VT * PQ];    // S^T [c][i], bf16 copy of the state tile
-    __align__(16) uint16_t x[C * PV];      // X [s][c]
-    __align__(16) uint16_t u[C * PV];      // U [s][c]
-    __align__(16) uint16_t uh[C * PV];     // U scaled by exp(c_last - c_s)
-    __align__(16) float cum[8][C];         // each wave's prefix sums of log alpha
 };
 
 struct GdnArgs {
@@ -243,288 +230,501 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
         store_dT(sm.t, PC, 16 * jb, 32 + 16 * rb, -d, lane);
     }
     lds_barrier();
-    // T in fragment order: 16-byte piece (rb, kk, lane = 16 g + j) holds row 16 rb + j,
-    // columns 32 kk + 8 g .. + 7, so that a wave of the forward kernel reads its B
-    // fragment as one contiguous kilobyte
+    // T in fragment order with the column slots of a pair of matrix-core result tiles:
+    // 16-byte piece (rb, kk, lane = 16 g + j) holds row 16 rb + j, columns 32 kk + 4 g ..
+    // + 3 then 32 kk + 16 + 4 g .. + 3, so that a forward wave reads its A fragment as one
+    // contiguous kilobyte and multiplies it with a B fragment packed straight from two of
+    // its own result tiles
     uint16_t* Tg = a.T + (seq * a.nchunks + ch) * size_t(C * C);
 #pragma unroll
     for (int x2 = 0; x2 < 2; ++x2) {
         const int x = tid + NT * x2, rb = x >> 7, kk = (x >> 6) & 1, l = x & 63;
-        const int off = (16 * rb + (l & 15)) * PC + 32 * kk + 8 * (l >> 4);
-        *reinterpret_cast<uint4*>(Tg + 8 * x) = *reinterpret_cast<const uint4*>(sm.t + off);
+        const int off = (16 * rb + (l & 15)) * PC + 32 * kk + 4 * (l >> 4);
+        const uint2 lo = *reinterpret_cast<const uint2*>(sm.t + off);
+        const uint2 hi = *reinterpret_cast<const uint2*>(sm.t + off + 16);
+        *reinterpret_cast<uint4*>(Tg + 8 * x) = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
 }
 
 // ---------------------------------------------------------------------------
 // forward kernel
 // ---------------------------------------------------------------------------
-// Per-chunk operands a wave reads straight from global memory in MFMA fragment layout
-// (lane = 16 g + j): rows 16 rb + j of q and T, K halves 8 g .. 8 g + 7 of each 32-wide
-// slice; V at the X tile's D layout; the chunk's alpha / beta at lane = token; and this
-// thread's share of the chunk's K rows for the LDS copy.
-template <int NVT, int KST>
-struct ChunkRegs {
-    uint4 q[4], t[2], kst[KST];
-    uint2 v[NVT];
-    uint32_t ga, gb;
+// One workgroup per (sequence, VT = 16 NCW value columns): NCW chain waves and two
+// output waves, one workgroup barrier per chunk.
+//
+// A chain wave owns 16 value columns of the state for all 128 key rows, as eight fp32
+// 16 x 16 result tiles in registers (lane 16 g + j: key rows 16 ib + 4 g .. + 3 of
+// column j). Columns of S never mix, so its walk over the chunks needs nothing from
+// another wave but the chunk's staged operands. For chunk c:
+//   S^T (bf16, the state entering the chunk) -> LDS, for the output waves
+//   KS = K S                       (A: rows of K; B: S packed from its own tiles)
+//   X = beta (V - gamma KS)        (V read in the result-tile layout)
+//   U = T X                        (A: T in the order the prep stored it)
+//   U^T (bf16) -> LDS, for the output waves
+//   S <- gamma_last S + K^T (d U),  d_r = exp(c_last - c_r)   (A: K^T by transpose reads)
+// Every B fragment is packed straight from two result tiles, so its K slots come in the
+// order the matrix cores return them (rows 4 g .. + 3 of the lower tile, then of the
+// upper one), and each matching A fragment is read in that slot order.
+//
+// The two output waves run one chunk behind: wave p takes the row blocks {0, 3} (p = 0)
+// or {1, 2} (p = 1), five causal score tiles each. In the iteration of chunk c they form
+// the score tiles P^T_{c-1} = (K Q^T) o D of their rows (D_sr = exp(c_r - c_s), s <= r)
+// and write O_{c-1}^T = gamma (S^T Q^T) + U^T P^T from the copies the chain waves left in
+// LDS.
+//
+// The chunk operands that several waves share (K, T) go from global memory straight into
+// LDS (buffer loads with an LDS destination, 16 bytes per lane), two chunks ahead, into a
+// ring of four slots, every wave copying its share; each wave waits for its own copies of
+// the next chunk before the barrier that ends the current one. A chain wave loads its
+// value columns straight into registers in the result-tile layout, also two chunks ahead. Every slot is an LDS object of its
+// own and the chunk loop is unrolled by four, so the compiler sees which slot each access
+// touches and never waits on a copy in flight to another slot. Per-sequence buffer
+// resources make every load past the end of the sequence read zero and drop every store
+// past it, so ragged tails need no branches.
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+// 16 bytes per lane from a buffer straight into LDS at lds + 16 lane (lds wave-uniform).
+__device__ __forceinline__ void dma16(rsrc_t r, const uint16_t* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds), 16, voff, 0, 0, 0);
+}
+// A fragment of the transpose of a row-major [K rows][columns] bf16 tile: M = columns
+// n0 .. n0 + 15, K = rows 32 kk .. + 31 in the pair-of-tiles slot order (LDS transpose
+// reads: lane L of a 16-lane group addresses row L / 4 of a 4-row block).
+__device__ __forceinline__ bf16x8_t frag_tr_pk(const uint16_t* t, int pitch, int kk, int n0,
+                                               int lane) {
+    const int g = lane >> 4, L = lane & 15;
+    const uint16_t* p = t + (32 * kk + 4 * g + (L >> 2)) * pitch + n0 + 4 * (L & 3);
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 16 * pitch));
+    const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+// A fragment over K = 32 kk .. + 31 of row `row` of a padded row-major bf16 tile, pair-of-
+// tiles slot order.
+__device__ __forceinline__ bf16x8_t frag_row_pk(const uint16_t* t, int pitch, int row, int kk,
+                                                int lane) {
+    const uint16_t* p = t + row * pitch + 32 * kk + 4 * (lane >> 4);
+    const uint2 lo = *reinterpret_cast<const uint2*>(p);
+    const uint2 hi = *reinterpret_cast<const uint2*>(p + 16);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+__device__ __forceinline__ uint2 pack4(f32x4_t d) {
+    return make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+}
+// s_waitcnt vmcnt(N) (other counters left alone), through the builtin so that the
+// compiler's own wait placement knows of it
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int NCW>
+struct FwdShape {
+    static constexpr int VT = 16 * NCW;
+    static constexpr int NW = NCW + 2;                 // waves per workgroup
+    // the padded K tile is 64 rows of 17 16-byte pieces (16 of data, one of padding):
+    // 17 blocks of 1 KiB; each wave issues KDMA of them (some twice, so that every wave
+    // issues the same number)
+    static constexpr int KBLK = C * (PQ / 8) / 64;
+    static constexpr int KDMA = (KBLK + NW - 1) / NW;
+    // T of a chunk is 8 blocks of 1 KiB, split over all waves the same way
+    static constexpr int TDMA = (8 + NW - 1) / NW;
+    static constexpr int VLD = 16;                     // 2-byte value loads per lane
+    // vector-memory operations a wave issues per iteration before the barrier's wait
+    // (loads only; the output waves' stores are not counted, so the wait is at least as
+    // strict as needed)
+    static constexpr int VM_CHAIN = KDMA + TDMA + VLD + 2;
+    static constexpr int VM_OUT = KDMA + TDMA + 8 + 1;
+    // two iterations of copies in flight stay within the 6-bit vector-memory counter
+    static_assert(2 * VM_CHAIN <= 63 && 2 * VM_OUT <= 63, "vmcnt range");
+};
+static_assert(PQ % 8 == 0 && C * (PQ / 8) % 64 == 0, "padded K rows in whole 1 KiB blocks");
+
+template <int J>
+using Ic = std::integral_constant<int, J>;
+
+// One chunk's operands that several waves read: K [s][i] (padded rows) and T in fragment
+// order, copied straight from global memory.
+struct __align__(16) ChunkSmem {
+    __align__(16) uint16_t k[C * PQ];
+    __align__(16) uint16_t t[C * C];
 };
 
-// Forward kernel. A workgroup owns VT = 16 NVT CG value columns of one sequence and
-// runs 4 CG waves: wave w works on row block rb = w % 4 of every chunk (rows of q, T, P,
-// key rows 32 rb .. of S) for column group cg = w / 4 (16 NVT columns). The CG column
-// groups share the LDS copy of K and load the same q / T lines, so a wider group cuts
-// the vector-memory traffic per column.
-template <int NVT, int CG, bool GB>
-__global__ __launch_bounds__(NT * CG) void gdn_fwd_kernel(GdnArgs a) {
-    constexpr int VT = 16 * NVT * CG;
-    constexpr int NTW = NT * CG;          // threads per workgroup
-    constexpr int KST = (C * DK / 8) / NTW;   // 16-byte K pieces per thread
-    constexpr int PV = FwdSmem<VT>::PV;
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    FwdSmem<VT>& sm = *reinterpret_cast<FwdSmem<VT>*>(smem_raw);
+template <int NCW, bool GB>
+__global__ __launch_bounds__(64 * (NCW + 2)) void gdn_fwd_kernel(GdnArgs a) {
+    using Sh = FwdShape<NCW>;
+    constexpr int VT = Sh::VT, NW = Sh::NW;
+    // a ring of four chunks (slot = chunk mod 4), each slot one LDS object holding the
+    // chunk's K and T
+    __shared__ ChunkSmem sl0, sl1, sl2, sl3;
+    __shared__ __align__(16) uint16_t st0[VT * PQ], st1[VT * PQ];   // S^T [col][i]
+    __shared__ __align__(16) uint16_t ut0[VT * PC], ut1[VT * PC];   // U^T [col][s]
+    __shared__ __align__(16) float gs[NCW + 2][3][C];               // per-wave gate factors
+    auto slot_ = [&](auto I) -> ChunkSmem& {
+        constexpr int s = decltype(I)::value & 3;
+        if constexpr (s == 0) return sl0; else if constexpr (s == 1) return sl1;
+        else if constexpr (s == 2) return sl2; else return sl3;
+    };
+    auto ks_ = [&](auto I) -> uint16_t* { return slot_(I).k; };
+    auto ts_ = [&](auto I) -> uint16_t* { return slot_(I).t; };
+    auto sts_ = [&](auto I) -> uint16_t* {
+        if constexpr ((decltype(I)::value & 1) == 0) return st0; else return st1;
+    };
+    auto uts_ = [&](auto I) -> uint16_t* {
+        if constexpr ((decltype(I)::value & 1) == 0) return ut0; else return ut1;
+    };
 
     const XcdMap mp = xcd_map(blockIdx.x, a.ntiles, a.nseq);
     if (!mp.valid) return;
-    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
-    const int rb = w & 3, cg = w >> 2;
+    const int lane = threadIdx.x & 63, w = wave_id();
     const int g = lane >> 4, jl = lane & 15;
     const int DV = a.ntiles * VT;
-    const int cw = 16 * NVT * cg;      // first column of this wave, within the tile
-    const int c0 = mp.tile * VT + cw;  // ... and within the row
+    const int c0 = mp.tile * VT;                 // first column of the tile
     const size_t seq = size_t(mp.seq);
     const SeqSpan sp = seq_span(int(seq), a.H, a.N, a.L, a.cu);
     const size_t tok0 = sp.base;
-    const int nchunks = (sp.len + C - 1) / C;   // this sequence's chunks
-    const int rw = 16 * rb + jl;       // this lane's row of the wave's 16-row block
-    const int nk = rb < 2 ? 1 : 2;     // T and P vanish for s >= 16 (rb + 1)
+    const int nchunks = (sp.len + C - 1) / C;
+    // one iteration per chunk plus one for the output waves, in whole groups of four; a
+    // chunk past the end reads zeros and leaves the state unchanged
+    const int niter = ((nchunks + 1 + 3) / 4) * 4;
 
-    // state tiles held by this wave: key blocks 2 rb + ib, column tiles ct (D layout)
-    f32x4_t S[2][NVT];
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-        for (int ct = 0; ct < NVT; ++ct)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int i = 16 * (2 * rb + ib) + 4 * g + j, c = colmap<NVT>(ct, jl);
-                S[ib][ct][j] = a.S0 ? a.S0[seq * DK * DV + size_t(i) * DV + c0 + c] : 0.f;
-            }
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-        for (int ct = 0; ct < NVT; ++ct)
-            store_st<NVT>(sm.st, PQ, 16 * (2 * rb + ib), cw, ct, S[ib][ct], lane);
-
-    // Per-sequence buffer resources: rows past the end of the sequence read as zero
-    // (the ragged last chunk's padding) and o rows past it are dropped on store.
-    const rsrc_t rq = make_rsrc(a.q + tok0 * DK, uint32_t(sp.len) * DK * 2u);
-    const rsrc_t rk = make_rsrc(a.k + tok0 * DK, uint32_t(sp.len) * DK * 2u);
-    const rsrc_t rv = make_rsrc(a.v + tok0 * DV, uint32_t(sp.len) * uint32_t(DV) * 2u);
-    const rsrc_t ro = make_rsrc(a.o + tok0 * DV, uint32_t(sp.len) * uint32_t(DV) * 2u);
-    const rsrc_t rt = make_rsrc(a.T + seq * size_t(a.nchunks) * size_t(C * C),
-                                uint32_t(nchunks) * (C * C * 2u));
     constexpr uint32_t GS = GB ? 2u : 4u;
-    const rsrc_t ra = make_rsrc(static_cast<const char*>(a.alpha) + tok0 * GS, uint32_t(sp.len) * GS);
-    const rsrc_t rb_ = make_rsrc(static_cast<const char*>(a.beta) + tok0 * GS, uint32_t(sp.len) * GS);
 
-    // loads of one chunk, all unconditional (a chunk index past the end reads zeros);
-    // K first, since its LDS copy is written before the other operands are needed
-    // A chunk's loads go out in three parts spread over the processing of the chunk two
-    // before it (gates and K, then q, then T and V), so that the memory unit's queue is
-    // not handed all of them at once. Each part stays together and in program order:
-    // the memory-counter waits before a chunk is used count the loads issued after it.
-    auto load_part = [&](ChunkRegs<NVT, KST>& R, int ch, int part) {
-        const uint32_t t0 = uint32_t(ch) * C;
-        if (part == 0) {
-            R.ga = buf_ld_gate<GB>(ra, t0 + lane);
-            R.gb = buf_ld_gate<GB>(rb_, t0 + lane);
+    // this wave's 1 KiB blocks of the padded K tile: piece p = 64 b + lane is row p / 17,
+    // 16-byte chunk p % 17 (chunk 16 is padding, filled with chunk 0); a wave may repeat a
+    // block of another so that every wave issues the same number. The global offsets
+    // within a chunk are fixed per lane.
+    // Each copy's per-lane offset is fixed for the whole walk (registers never rewritten
+    // while a copy that names them may still be in flight); the chunk is selected by the
+    // buffer resource, built per chunk from scalars with the bytes left in the sequence
+    // (none past its end, so those copies fill zeros).
+    uint32_t koff[Sh::KDMA];
 #pragma unroll
-            for (int x4 = 0; x4 < KST; ++x4) {
-                const int x = tid + NTW * x4, r = x >> 4, col = (x & 15) * 8;
-                R.kst[x4] = buf_ld16(rk, ((t0 + r) * DK + col) * 2u);
-            }
-        } else if (part == 1) {
-            const uint32_t oq = ((t0 + rw) * DK + 8 * g) * 2u;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) R.q[kk] = buf_ld16(rq, oq + 64u * kk);
-        } else {
-            const uint32_t ot = (uint32_t(ch) * (C * C) + (2 * rb * 64 + lane) * 8) * 2u;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) R.t[kk] = buf_ld16(rt, ot + 1024u * kk);
-            const uint32_t ov = ((t0 + rw) * uint32_t(DV) + c0 + colmap<NVT>(0, 4 * g)) * 2u;
-            if constexpr (NVT == 2) {
-                const uint4 v4 = buf_ld16(rv, ov);
-                R.v[0] = make_uint2(v4.x, v4.y);
-                R.v[1] = make_uint2(v4.z, v4.w);
-            } else {
-                R.v[0] = buf_ld8(rv, ov);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    auto load_chunk = [&](ChunkRegs<NVT, KST>& R, int ch) {
-        load_part(R, ch, 0);
-        load_part(R, ch, 1);
-        load_part(R, ch, 2);
-    };
-    auto stage_k = [&](const ChunkRegs<NVT, KST>& R, uint16_t* kb) {
-#pragma unroll
-        for (int x4 = 0; x4 < KST; ++x4) {
-            const int x = tid + NTW * x4, r = x >> 4, col = (x & 15) * 8;
-            *reinterpret_cast<uint4*>(kb + r * PQ + col) = R.kst[x4];
-        }
-    };
-
-    auto process = [&](const ChunkRegs<NVT, KST>& R, const ChunkRegs<NVT, KST>& Rn,
-                       ChunkRegs<NVT, KST>& Rl, int ch, int cur) {
-        load_part(Rl, ch + 2, 0);
-        const int t0 = ch * C, n = min(C, sp.len - t0);
-        const uint16_t* kc = sm.k[cur];
-        // gates: every wave scans log alpha itself (lane = token); lane (g, j) then
-        // takes the values of token 16 rb + j
-        const float lg = fast_log(gate_val<GB>(R.ga));
-        const float cum = wave_inclusive_scan(lane < n ? lg : 0.f);
-        const float clast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), 63));
-        const float braw = gate_val<GB>(R.gb);
-        const float cr = __shfl(cum, rw, 64);
-        const float br = rw < n ? __shfl(braw, rw, 64) : 0.f;
-        const float gr = fast_exp(cr);
-        const float dr = fast_exp(clast - cr);
-        const float glast = fast_exp(clast);
-        sm.cum[w][lane] = cum;   // read back by this wave only (for the P tiles)
-
-        // ---- (S^T Q^T) and (S^T K^T) for rows 16 rb .. : D[c][r]; the S^T fragment
-        // is shared by both products
-        f32x4_t oq[NVT], ks[NVT];
-#pragma unroll
-        for (int ct = 0; ct < NVT; ++ct) { oq[ct] = zero4(); ks[ct] = zero4(); }
-#pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) {
-            const bf16x8_t kf = frag_kc(kc, PQ, 16 * rb, 32 * kk, lane);
-            const bf16x8_t qf = __builtin_bit_cast(bf16x8_t, R.q[kk]);   // rows >= n unused
-#pragma unroll
-            for (int ct = 0; ct < NVT; ++ct) {
-                const bf16x8_t sf = frag_st<NVT>(sm.st, PQ, cw, ct, 32 * kk, lane);
-                oq[ct] = mfma16(sf, qf, oq[ct]);
-                ks[ct] = mfma16(sf, kf, ks[ct]);
-            }
-        }
-        // ---- X[s][c] = beta_s (v_s,c - gamma_s (S^T k_s)_c), s = 16 rb + j
-#pragma unroll
-        for (int ct = 0; ct < NVT; ++ct) {
-            const uint2 vv = R.v[ct];
-            const float vf[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
-                                 __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
-            f32x4_t x_;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) x_[j] = br * (vf[j] - gr * ks[ct][j]);
-            store_rows<NVT>(sm.x, PV, cw, ct, 16 * rb, x_, lane);   // X[s][c]
-        }
-        lds_barrier();
-        load_part(Rl, ch + 2, 1);
-
-        // ---- U^T = X^T T^T for rows 16 rb .. : D[c][r] -> U[r][c], U^[r][c]
-#pragma unroll
-        for (int ct = 0; ct < NVT; ++ct) {
-            f32x4_t u_ = mfma16(frag_kr_cols<NVT>(sm.x, PV, 0, cw, ct, lane),
-                                __builtin_bit_cast(bf16x8_t, R.t[0]), zero4());
-            if (nk > 1)
-                u_ = mfma16(frag_kr_cols<NVT>(sm.x, PV, 32, cw, ct, lane),
-                            __builtin_bit_cast(bf16x8_t, R.t[1]), u_);
-            store_rows<NVT>(sm.u, PV, cw, ct, 16 * rb, u_, lane);
-            store_rows<NVT>(sm.uh, PV, cw, ct, 16 * rb, u_ * dr, lane);
-        }
-        // ---- P^T tiles of rows 16 rb ..: D[s][r] = exp(c_r - c_s) k_s . q_r (s <= r),
-        // kept as B fragments in the order the matrix cores return them
-        f32x4_t pt[4];
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            pt[sb] = zero4();
-            if (sb <= rb) {
-#pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk)
-                    pt[sb] = mfma16(frag_kc(kc, PQ, 16 * sb, 32 * kk, lane),
-                                    __builtin_bit_cast(bf16x8_t, R.q[kk]), pt[sb]);
-                const float4 cs = *reinterpret_cast<const float4*>(sm.cum[w] + 16 * sb + 4 * g);
-                const float csv[4] = {cs.x, cs.y, cs.z, cs.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int s = 16 * sb + 4 * g + j;
-                    const float e = fast_exp(cr - csv[j]) * pt[sb][j];
-                    pt[sb][j] = s <= rw ? e : 0.f;
-                }
-            }
-        }
-        const bf16x8_t pf0 = pack_pk(pt[0], pt[1]), pf1 = pack_pk(pt[2], pt[3]);
-        lds_barrier();
-        load_part(Rl, ch + 2, 2);
-
-        // ---- O^T = gamma_r (S^T Q^T) + U^T P^T -> o rows 16 rb ..
-        uint2 ow[NVT];
-#pragma unroll
-        for (int ct = 0; ct < NVT; ++ct) {
-            f32x4_t o_ = mfma16(frag_kr_cols_pk<NVT>(sm.u, PV, 0, cw, ct, lane), pf0, oq[ct] * gr);
-            if (nk > 1) o_ = mfma16(frag_kr_cols_pk<NVT>(sm.u, PV, 1, cw, ct, lane), pf1, o_);
-            ow[ct].x = pack_bf16x2(o_[0], o_[1]);
-            ow[ct].y = pack_bf16x2(o_[2], o_[3]);
-        }
-        {
-            const uint32_t oo = ((uint32_t(t0) + rw) * uint32_t(DV) + c0 + colmap<NVT>(0, 4 * g)) * 2u;
-            if constexpr (NVT == 2) buf_st16(ro, oo, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
-            else buf_st8(ro, oo, ow[0]);
-        }
-        // ---- S = gamma_last S + K^T U^ (key rows 32 rb ..), bf16 copy to st
-        bf16x8_t uf[2][NVT];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int ct = 0; ct < NVT; ++ct)
-                uf[kk][ct] = frag_kr_cols<NVT>(sm.uh, PV, 32 * kk, cw, ct, lane);
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-            const int i0 = 16 * (2 * rb + ib);
-            const bf16x8_t kt0 = frag_kr(kc, PQ, 0, i0, lane);
-            const bf16x8_t kt1 = frag_kr(kc, PQ, 32, i0, lane);
-#pragma unroll
-            for (int ct = 0; ct < NVT; ++ct) {
-                f32x4_t s_ = S[ib][ct] * glast;
-                s_ = mfma16(kt0, uf[0][ct], s_);
-                s_ = mfma16(kt1, uf[1][ct], s_);
-                S[ib][ct] = s_;
-                store_st<NVT>(sm.st, PQ, i0, cw, ct, s_, lane);
-            }
-        }
-        // next chunk's K into the other buffer (its readers finished before the
-        // previous barrier)
-        stage_k(Rn, sm.k[cur ^ 1]);
-        lds_barrier();
-    };
-
-    // three register sets rotate so that each chunk's loads are issued two chunks
-    // before it is processed (one chunk of compute is shorter than the memory latency)
-    ChunkRegs<NVT, KST> RA, RB, RC;
-    load_chunk(RA, 0);
-    load_chunk(RB, 1);
-    stage_k(RA, sm.k[0]);
-    lds_barrier();
-    // whole triples only: a chunk past the end reads zeros (alpha = beta = 0 masked to
-    // the identity step, T = 0), leaves the state unchanged and stores nothing, so no
-    // exit sits between the triple's memory operations
-    for (int ch = 0; ch < nchunks; ch += 3) {
-        process(RA, RB, RC, ch, ch & 1);
-        process(RB, RC, RA, ch + 1, (ch + 1) & 1);
-        process(RC, RA, RB, ch + 2, ch & 1);
+    for (int x = 0; x < Sh::KDMA; ++x) {
+        const int b = (w + NW * x) % Sh::KBLK, pz = 64 * b + lane;
+        const int row = pz / (PQ / 8), ck = pz % (PQ / 8);
+        koff[x] = uint32_t(row * DK + (ck < DK / 8 ? ck : 0) * 8) * 2u;
     }
+    auto rows_left = [&](int ch) { return uint32_t(max(0, sp.len - ch * C)); };
+    // resources over one chunk (and what follows it in the sequence) of a token-major array
+    auto gate_rsrc = [&](const void* base, int ch) {
+        return make_rsrc(static_cast<const char*>(base) + (tok0 + size_t(ch) * C) * GS, rows_left(ch) * GS);
+    };
+    const uint32_t goff = uint32_t(lane) * GS;   // lane = token
+    // copies of K of chunk ch into kb
+    auto dma_k = [&](uint16_t* kb, int ch) {
+        const rsrc_t r = make_rsrc(a.k + (tok0 + size_t(ch) * C) * DK, rows_left(ch) * DK * 2u);
+#pragma unroll
+        for (int x = 0; x < Sh::KDMA; ++x) {
+            const int b = (w + NW * x) % Sh::KBLK;
+            dma16(r, kb + b * 512, koff[x]);
+        }
+    };
+    // this wave's 1 KiB blocks of T of a chunk (stored in fragment order by the prep)
+    uint32_t toff[Sh::TDMA];
+#pragma unroll
+    for (int x = 0; x < Sh::TDMA; ++x) toff[x] = uint32_t((w + NW * x) % 8) * 1024u + lane * 16u;
+    auto dma_t = [&](uint16_t* tb_, int ch) {
+        const rsrc_t r1 = make_rsrc(a.T + (seq * size_t(a.nchunks) + size_t(ch)) * (C * C),
+                                    ch < nchunks ? C * C * 2u : 0u);
+#pragma unroll
+        for (int x = 0; x < Sh::TDMA; ++x) dma16(r1, tb_ + ((w + NW * x) % 8) * 512, toff[x]);
+    };
+    float (*gw)[C] = gs[w];
 
+    if (w < NCW) {
+        // =========================== chain wave ===========================
+        const int cb = 16 * w;   // first column of this wave within the tile
+        f32x4_t S[8];
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
+        for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
-        for (int ct = 0; ct < NVT; ++ct)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int i = 16 * (2 * rb + ib) + 4 * g + j, c = colmap<NVT>(ct, jl);
-                a.S[seq * DK * DV + size_t(i) * DV + c0 + c] = S[ib][ct][j];
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * ib + 4 * g + e;
+                S[ib][e] = a.S0 ? a.S0[seq * DK * DV + size_t(i) * DV + c0 + cb + jl] : 0.f;
             }
+        // this lane's value column cb + j of token rows 4 g + e (+ 16 tb), the result-tile
+        // layout of KS, straight from global memory
+        const uint32_t voff = ((4 * g) * uint32_t(DV) + c0 + cb + jl) * 2u;
+        struct VSet { uint32_t v[4][4]; };
+        auto load_v = [&](VSet& V, int ch) {
+            const rsrc_t r2 = make_rsrc(a.v + (tok0 + size_t(ch) * C) * DV,
+                                        rows_left(ch) * uint32_t(DV) * 2u);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    V.v[tb][e] = __builtin_amdgcn_raw_buffer_load_b16(
+                        r2, voff + uint32_t((16 * tb + e) * DV * 2), 0, 0);
+        };
+        VSet VS[4];
+        struct Gate { uint32_t ga, gb; };
+        auto load_g = [&](Gate& G, int ch) {
+            G.ga = buf_ld_gate_off<GB>(gate_rsrc(a.alpha, ch), goff);
+            G.gb = buf_ld_gate_off<GB>(gate_rsrc(a.beta, ch), goff);
+        };
+        Gate G[4];
+
+        auto step = [&](auto J, int ch) {
+            constexpr int j = decltype(J)::value;
+            dma_k(ks_(Ic<j + 2>{}), ch + 2);
+            dma_t(ts_(Ic<j + 2>{}), ch + 2);
+            load_v(VS[(j + 2) & 3], ch + 2);
+            load_g(G[(j + 2) & 3], ch + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            const Gate& Gc = G[j];
+            const int n = min(C, sp.len - ch * C);
+            const uint16_t* kc = ks_(J);
+            const uint16_t* tc = ts_(J);
+            // per-token gate factors (lane = token; padding rows are identity steps)
+            const float lg = lane < n ? fast_log(gate_val<GB>(Gc.ga)) : 0.f;
+            const float cum = wave_inclusive_scan(lg);
+            const float clast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), 63));
+            gw[0][lane] = fast_exp(cum);            // gamma_r
+            gw[1][lane] = fast_exp(clast - cum);    // d_r
+            gw[2][lane] = lane < n ? gate_val<GB>(Gc.gb) : 0.f;
+            // S as B fragments (keys in pair-of-tiles slot order), and S^T entering the chunk
+            // for the output waves from the same packed words
+            bf16x8_t Sb[4];
+            uint16_t* stc = sts_(J);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                Sb[kk] = pack_pk(S[2 * kk], S[2 * kk + 1]);
+                const uint4 wd = __builtin_bit_cast(uint4, Sb[kk]);
+                *reinterpret_cast<uint2*>(stc + (cb + jl) * PQ + 32 * kk + 4 * g) = make_uint2(wd.x, wd.y);
+                *reinterpret_cast<uint2*>(stc + (cb + jl) * PQ + 32 * kk + 16 + 4 * g) = make_uint2(wd.z, wd.w);
+            }
+            // KS = K S, rows 16 tb + 4 g + e; the next row block's A fragments are read
+            // while the current one's products issue
+            f32x4_t ks[4];
+            bf16x8_t ka[2][4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) ka[0][kk] = frag_row_pk(kc, PQ, jl, kk, lane);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                if (tb < 3) {
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        ka[(tb + 1) & 1][kk] = frag_row_pk(kc, PQ, 16 * (tb + 1) + jl, kk, lane);
+                }
+                ks[tb] = zero4();
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) ks[tb] = mfma16(ka[tb & 1][kk], Sb[kk], ks[tb]);
+            }
+            // T fragments and the value tile (independent of the state)
+            bf16x8_t tf[6];
+            const int pc[6] = {0, 2, 4, 5, 6, 7};   // piece 2 tb + kk of T
+#pragma unroll
+            for (int x = 0; x < 6; ++x)
+                tf[x] = *reinterpret_cast<const bf16x8_t*>(tc + (pc[x] * 64 + lane) * 8);
+            float vv[4][4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vv[tb][e] = __uint_as_float(VS[j].v[tb][e] << 16);
+            wave_lds_sync();   // this wave's gate factors are in LDS
+            // X = beta (V - gamma KS)
+            f32x4_t X[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const float4 g4 = *reinterpret_cast<const float4*>(&gw[0][16 * tb + 4 * g]);
+                const float4 b4 = *reinterpret_cast<const float4*>(&gw[2][16 * tb + 4 * g]);
+                X[tb][0] = b4.x * (vv[tb][0] - g4.x * ks[tb][0]);
+                X[tb][1] = b4.y * (vv[tb][1] - g4.y * ks[tb][1]);
+                X[tb][2] = b4.z * (vv[tb][2] - g4.z * ks[tb][2]);
+                X[tb][3] = b4.w * (vv[tb][3] - g4.w * ks[tb][3]);
+            }
+            const bf16x8_t Xb0 = pack_pk(X[0], X[1]), Xb1 = pack_pk(X[2], X[3]);
+            // U = T X (T lower triangular: row blocks 0, 1 need tokens 0..31 only)
+            f32x4_t u[4];
+            u[0] = mfma16(tf[0], Xb0, zero4());
+            u[1] = mfma16(tf[1], Xb0, zero4());
+            u[2] = mfma16(tf[2], Xb0, zero4());
+            u[2] = mfma16(tf[3], Xb1, u[2]);
+            u[3] = mfma16(tf[4], Xb0, zero4());
+            u[3] = mfma16(tf[5], Xb1, u[3]);
+            // U^T for the output waves
+            uint16_t* utc = uts_(J);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                *reinterpret_cast<uint2*>(utc + (cb + jl) * PC + 16 * tb + 4 * g) = pack4(u[tb]);
+            // S <- gamma_last S + K^T (d U)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const float4 d4 = *reinterpret_cast<const float4*>(&gw[1][16 * tb + 4 * g]);
+                u[tb][0] *= d4.x; u[tb][1] *= d4.y; u[tb][2] *= d4.z; u[tb][3] *= d4.w;
+            }
+            const bf16x8_t Ub0 = pack_pk(u[0], u[1]), Ub1 = pack_pk(u[2], u[3]);
+            const float glast = fast_exp(clast);
+            bf16x8_t kt[2][2];
+            kt[0][0] = frag_tr_pk(kc, PQ, 0, 0, lane);
+            kt[0][1] = frag_tr_pk(kc, PQ, 1, 0, lane);
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib) {
+                if (ib < 7) {
+                    kt[(ib + 1) & 1][0] = frag_tr_pk(kc, PQ, 0, 16 * (ib + 1), lane);
+                    kt[(ib + 1) & 1][1] = frag_tr_pk(kc, PQ, 1, 16 * (ib + 1), lane);
+                }
+                f32x4_t s_ = S[ib] * glast;
+                s_ = mfma16(kt[ib & 1][0], Ub0, s_);
+                s_ = mfma16(kt[ib & 1][1], Ub1, s_);
+                S[ib] = s_;
+            }
+            // the next chunk's K and T (copies issued an iteration ago) have landed
+            wait_vmcnt<Sh::VM_CHAIN>();
+            lds_barrier();
+        };
+
+        dma_k(sl0.k, 0);
+        dma_t(sl0.t, 0);
+        dma_k(sl1.k, 1);
+        dma_t(sl1.t, 1);
+        load_v(VS[0], 0);
+        load_v(VS[1], 1);
+        load_g(G[0], 0);
+        load_g(G[1], 1);
+        wait_vmcnt<0>();
+        lds_barrier();
+        for (int ch = 0; ch < niter; ch += 4) {
+            step(Ic<0>{}, ch);
+            step(Ic<1>{}, ch + 1);
+            step(Ic<2>{}, ch + 2);
+            step(Ic<3>{}, ch + 3);
+        }
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * ib + 4 * g + e;
+                a.S[seq * DK * DV + size_t(i) * DV + c0 + cb + jl] = S[ib][e];
+            }
+    } else {
+        // =========================== output wave ===========================
+        struct QSet {
+            uint4 q[2][4];    // rows 16 rb + j of q (the wave's two row blocks), keys 32 kk + 8 g ..
+            uint32_t ga;
+        };
+        auto run = [&](auto pc) {
+            constexpr int P = decltype(pc)::value;
+            constexpr int RB[2] = {P == 0 ? 0 : 1, P == 0 ? 3 : 2};
+            // per-lane offsets of the wave's q rows within a chunk and of its output rows
+            uint32_t qoff[2], ooff[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                qoff[h] = ((16 * RB[h] + jl) * DK + 8 * g) * 2u;
+                ooff[h] = ((16 * RB[h] + jl) * uint32_t(DV) + c0 + 4 * g) * 2u;
+            }
+            auto load_q = [&](QSet& Q, int ch) {
+                Q.ga = buf_ld_gate_off<GB>(gate_rsrc(a.alpha, ch), goff);
+                const rsrc_t r = make_rsrc(a.q + (tok0 + size_t(ch) * C) * DK, rows_left(ch) * DK * 2u);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) Q.q[h][kk] = buf_ld16_off(r, qoff[h], 64 * kk);
+            };
+            // rows of row block RB[h] of chunk cp: scores, then outputs
+            auto rows = [&](const QSet& Qp, auto hc, const rsrc_t& orc, const uint16_t* kc,
+                            const uint16_t* stc, const uint16_t* utc) {
+                constexpr int h = decltype(hc)::value;
+                constexpr int rb = RB[h];
+                const int r = 16 * rb + jl;
+                const float crr = gw[0][r];
+                f32x4_t pt[4] = {zero4(), zero4(), zero4(), zero4()};
+                bf16x8_t kf[2][4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) kf[0][kk] = frag_kc(kc, PQ, 0, 32 * kk, lane);
+#pragma unroll
+                for (int sb = 0; sb <= rb; ++sb) {
+                    if (sb < rb) {
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk)
+                            kf[(sb + 1) & 1][kk] = frag_kc(kc, PQ, 16 * (sb + 1), 32 * kk, lane);
+                    }
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        pt[sb] = mfma16(kf[sb & 1][kk], __builtin_bit_cast(bf16x8_t, Qp.q[h][kk]), pt[sb]);
+                }
+                bf16x8_t sf[NCW][4];
+#pragma unroll
+                for (int ct = 0; ct < NCW; ++ct)
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) sf[ct][kk] = frag_kc(stc, PQ, 16 * ct, 32 * kk, lane);
+                bf16x8_t uf[NCW][2];
+#pragma unroll
+                for (int ct = 0; ct < NCW; ++ct)
+#pragma unroll
+                    for (int kk = 0; kk < (rb >= 2 ? 2 : 1); ++kk)
+                        uf[ct][kk] = frag_row_pk(utc, PC, 16 * ct + jl, kk, lane);
+#pragma unroll
+                for (int sb = 0; sb <= rb; ++sb) {
+                    const float4 cs = *reinterpret_cast<const float4*>(&gw[0][16 * sb + 4 * g]);
+                    const float csv[4] = {cs.x, cs.y, cs.z, cs.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s = 16 * sb + 4 * g + e;
+                        const float x = fast_exp(crr - csv[e]) * pt[sb][e];
+                        pt[sb][e] = (sb < rb || s <= r) ? x : 0.f;
+                    }
+                }
+                const bf16x8_t pf0 = pack_pk(pt[0], pt[1]), pf1 = pack_pk(pt[2], pt[3]);
+                const float gr = fast_exp(crr);
+                // O^T = gamma (S^T Q^T) + U^T P^T: columns 16 ct + 4 g .. of token r
+#pragma unroll
+                for (int ct = 0; ct < NCW; ++ct) {
+                    f32x4_t oq = zero4();
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        oq = mfma16(sf[ct][kk], __builtin_bit_cast(bf16x8_t, Qp.q[h][kk]), oq);
+                    f32x4_t o_ = oq * gr;
+                    o_ = mfma16(uf[ct][0], pf0, o_);
+                    if constexpr (rb >= 2) o_ = mfma16(uf[ct][1], pf1, o_);
+                    buf_st8_off(orc, ooff[h], 32 * ct, pack4(o_));
+                }
+            };
+            QSet Q[4];   // chunk x's q in set x mod 4, loaded two iterations ahead
+            auto step = [&](auto J, int ch) {
+                constexpr int j = decltype(J)::value;
+                dma_k(ks_(Ic<j + 2>{}), ch + 2);
+                dma_t(ts_(Ic<j + 2>{}), ch + 2);
+                load_q(Q[(j + 2) & 3], ch + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                const int cp = ch - 1;
+                if (cp >= 0) {
+                    const QSet& Qp = Q[(j + 3) & 3];
+                    const int n = min(C, sp.len - cp * C);
+                    const float lg = lane < n ? fast_log(gate_val<GB>(Qp.ga)) : 0.f;
+                    gw[0][lane] = wave_inclusive_scan(lg);
+                    wave_lds_sync();
+                    const uint16_t* kc = ks_(Ic<j + 3>{});
+                    const uint16_t* stc = sts_(Ic<j + 1>{});
+                    const uint16_t* utc = uts_(Ic<j + 1>{});
+                    const rsrc_t orc = make_rsrc(a.o + (tok0 + size_t(cp) * C) * DV,
+                                                 rows_left(cp) * uint32_t(DV) * 2u);
+                    rows(Qp, Ic<0>{}, orc, kc, stc, utc);
+                    rows(Qp, Ic<1>{}, orc, kc, stc, utc);
+                }
+                wait_vmcnt<Sh::VM_OUT>();
+                lds_barrier();
+            };
+            dma_k(sl0.k, 0);
+            dma_t(sl0.t, 0);
+            dma_k(sl1.k, 1);
+            dma_t(sl1.t, 1);
+            load_q(Q[0], 0);
+            load_q(Q[1], 1);
+            wait_vmcnt<0>();
+            lds_barrier();
+            for (int ch = 0; ch < niter; ch += 4) {
+                step(Ic<0>{}, ch);
+                step(Ic<1>{}, ch + 1);
+                step(Ic<2>{}, ch + 2);
+                step(Ic<3>{}, ch + 3);
+            }
+        };
+        if (w == NCW) run(Ic<0>{});
+        else run(Ic<1>{});
+    }
 }
 
 GdnArgs make_args(const Problem& p) {
@@ -548,9 +748,9 @@ GdnArgs make_args(const Problem& p) {
     return a;
 }
 
-template <int NVT, int CG, bool GB>
+template <int NCW, bool GB>
 hipError_t launch_cfg(const Problem& p) {
-    constexpr int VT = 16 * NVT * CG;
+    constexpr int VT = 16 * NCW;
     GdnArgs a = make_args(p);
     a.ntiles = p.dv / VT;
     hipError_t e;
@@ -564,18 +764,14 @@ hipError_t launch_cfg(const Problem& p) {
         gdn_prep_kernel<GB><<<dim3(unsigned(blocks)), dim3(NT), smem, p.stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const size_t smem = sizeof(FwdSmem<VT>);
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gdn_fwd_kernel<NVT, CG, GB>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
-    if (e != hipSuccess) return e;
-    gdn_fwd_kernel<NVT, CG, GB>
-        <<<dim3(xcd_grid(a.ntiles, a.nseq)), dim3(NT * CG), smem, p.stream>>>(a);
+    gdn_fwd_kernel<NCW, GB>
+        <<<dim3(xcd_grid(a.ntiles, a.nseq)), dim3(64 * (NCW + 2)), 0, p.stream>>>(a);
     return hipGetLastError();
 }
 
 template <bool GB>
-hipError_t launch_gb(const Problem& p, bool wide) {
-    return wide ? launch_cfg<2, 1, GB>(p) : launch_cfg<1, 1, GB>(p);
+hipError_t launch_gb(const Problem& p) {
+    return p.dv >= 32 ? launch_cfg<2, GB>(p) : launch_cfg<1, GB>(p);
 }
 
 }  // namespace
@@ -594,15 +790,8 @@ hipError_t launch_prefill_gdn_mfma(const Problem& p) {
     if (nseq > (1u << 26) || !p.ws) return hipErrorInvalidValue;
     // buffer offsets are 32-bit: one sequence's rows and its chunk transforms
     if (size_t(p.L) * DK * 4 >= (size_t(1) << 31)) return hipErrorInvalidValue;
-    // Forward shape: each value tile is an independent chain of chunks, so the tile
-    // count sets the parallelism, while every tile re-reads the chunk's q, K, T and P
-    // through the vector memory path, whose request rate bounds the loop. 32-column
-    // tiles on 4 waves (one workgroup per CU at 64 sequences x 128 columns) halve that
-    // traffic per column and measure faster than 16-column tiles at two per CU, or
-    // 32-column tiles on 8 waves.
-    const bool wide = p.dv >= 32;
-    if (p.gate_bf16) return launch_gb<true>(p, wide);
-    return launch_gb<false>(p, wide);
+    if (p.gate_bf16) return launch_gb<true>(p);
+    return launch_gb<false>(p);
 }
 
 }  // namespace la

@@ -4,6 +4,8 @@ Two summaries are produced from rocprofv3's CSV files:
 
 * ``stats``: per-kernel call counts and durations from a ``--kernel-trace --stats``
   run (``*_kernel_stats.csv``), written as a text table.
+* ``pmc``: per-dispatch means of any counters of ``--pmc`` runs for the kernels that
+  match a pattern, with MFMA-busy, wait and LDS-conflict ratios.
 * ``traffic``: HBM bytes per benchmark step from two ``--pmc`` runs, one with
   ``FETCH_SIZE`` and one with ``WRITE_SIZE`` (KiB per dispatch). Both runs include
   ``bench.py --copy-calib``, whose plain 512 MiB device copies calibrate the
@@ -14,6 +16,7 @@ Two summaries are produced from rocprofv3's CSV files:
     python profsum.py stats STATS_CSV OUT_TXT --command CMD
     python profsum.py traffic FETCH_CSV WRITE_CSV OUT_JSON OUT_TXT \
         --command CMD
+    python profsum.py pmc KERNEL_REGEX OUT_TXT COUNTER_CSV [COUNTER_CSV ...] --command CMD
 """
 from __future__ import annotations
 
@@ -128,6 +131,39 @@ def traffic(fetch_csv: str, write_csv: str, out_json: str, out_txt: str, command
         fh.write("\n".join(lines) + "\n")
 
 
+def pmc(csv_paths, kernel_pat: str, out_txt: str, command: str) -> None:
+    """Per-dispatch averages of every counter in the given counter_collection CSVs, for the
+    kernels whose demangled name matches kernel_pat, with a few ratios derived from them."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in csv_paths:
+        acc = collections.defaultdict(float)
+        names = {}
+        for r in csv.DictReader(open(path)):
+            if not re.search(kernel_pat, short(r["Kernel_Name"])):
+                continue
+            key = (r["Dispatch_Id"], r["Counter_Name"])
+            acc[key] += float(r["Counter_Value"])
+            names[key] = short(r["Kernel_Name"])
+        for (disp, cname), v in acc.items():
+            vals[names[(disp, cname)]][cname].append(v)
+    lines = ["# rocprofv3 counters, mean per dispatch", f"# command: {command}", "#"]
+    for kern, cs in vals.items():
+        lines.append(f"  {kern}")
+        m = {c: sum(v) / len(v) for c, v in cs.items()}
+        for c in sorted(m):
+            lines.append(f"    {c:<32} {m[c]:>18.1f}   ({len(cs[c])} dispatches)")
+        def ratio(label, a, b):
+            if a in m and b in m and m[b] > 0:
+                lines.append(f"    {label:<32} {m[a] / m[b]:>18.4f}")
+        ratio("MFMA busy / busy cycles", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES")
+        ratio("LDS wait / wave cycles", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES")
+        ratio("any wait / wave cycles", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES")
+        ratio("LDS bank conflict / LDS active", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS")
+        ratio("VMEM active / wave cycles", "SQ_ACTIVE_INST_VMEM", "SQ_WAVE_CYCLES")
+    with open(out_txt, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -141,9 +177,16 @@ def main() -> None:
     t.add_argument("out_json")
     t.add_argument("out_txt")
     t.add_argument("--command", required=True)
+    c = sub.add_parser("pmc")
+    c.add_argument("kernel", help="regular expression on the demangled kernel name")
+    c.add_argument("out")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--command", required=True)
     a = ap.parse_args()
     if a.what == "stats":
         stats(a.csv, a.out, a.command)
+    elif a.what == "pmc":
+        pmc(a.csv, a.kernel, a.out, a.command)
     else:
         traffic(a.fetch_csv, a.write_csv, a.out_json, a.out_txt, a.command)
 
