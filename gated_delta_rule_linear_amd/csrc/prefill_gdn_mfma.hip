@@ -46,7 +46,8 @@ namespace {
 constexpr int DK = 128;
 constexpr int C = kMfmaChunk;  // 64
 constexpr int NT = 256;
-constexpr int PQ = DK + 8;     // pitch (elements) of [*][128] bf16 tiles
+constexpr int PQ = DK + 16;    // pitch (elements) of [*][128] bf16 tiles (72 dwords: 16-byte
+                               // reads of 16 rows at one column are free of bank conflicts)
 constexpr int PC = C + 8;      // pitch of [*][64] bf16 tiles
 constexpr int PD = 16 + 4;     // pitch of the fp32 16 x 16 diagonal L blocks
 constexpr int PY = 32 + 8;     // pitch of the bf16 32-row scratch tiles
@@ -249,64 +250,63 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
 // ---------------------------------------------------------------------------
 // forward kernel
 // ---------------------------------------------------------------------------
-// One workgroup per (sequence, VT = 16 NCW value columns): NCW chain waves and two
-// output waves, one workgroup barrier per chunk.
+// One workgroup per (sequence, VT = 16 NCB value columns, NCB = 1 or 2): NCB chain waves
+// and three output waves, one workgroup barrier per chunk. The chain waves are waves 0
+// and 4, which share one SIMD: a wave does not issue vector ALU work while its own
+// matrix-core product runs, but another wave on the same SIMD does, so each chain wave's
+// packing and scaling fill the other's matrix-core time.
 //
-// A chain wave owns 16 value columns of the state for all 128 key rows, as eight fp32
-// 16 x 16 result tiles in registers (lane 16 g + j: key rows 16 ib + 4 g .. + 3 of
-// column j). Columns of S never mix, so its walk over the chunks needs nothing from
-// another wave but the chunk's staged operands. For chunk c:
+// Chain wave c owns 16 value columns (16 c .. + 15 of the tile) of the state for all 128
+// key rows, as eight fp32 16 x 16 result tiles in registers. Its walk over the chunks
+// needs nothing from the other waves but the chunk's staged operands. For chunk c:
 //   S^T (bf16, the state entering the chunk) -> LDS, for the output waves
-//   KS = K S                       (A: rows of K; B: S packed from its own tiles)
+//   KS = K S                       (A: rows of K)
 //   X = beta (V - gamma KS)        (V read in the result-tile layout)
 //   U = T X                        (A: T in the order the prep stored it)
 //   U^T (bf16) -> LDS, for the output waves
 //   S <- gamma_last S + K^T (d U),  d_r = exp(c_last - c_r)   (A: K^T by transpose reads)
-// Every B fragment is packed straight from two result tiles, so its K slots come in the
-// order the matrix cores return them (rows 4 g .. + 3 of the lower tile, then of the
-// upper one), and each matching A fragment is read in that slot order.
+// The state's key rows are kept in a permuted order: row 4 g + e of tiles 2 kk and 2 kk + 1
+// (lane 16 g + j) hold keys 32 kk + 8 g + e and 32 kk + 8 g + 4 + e. A sum over keys does
+// not depend on their order, and with this one the B fragment packed from two result tiles
+// carries keys 32 kk + 8 g .. + 7 in natural order, so K's rows are read 16 bytes at a time
+// and S^T is written 16 bytes at a time. The token slots of the products over the chunk
+// come in the order the matrix cores return them (rows 4 g .. + 3 of the lower tile, then
+// of the upper one), and each matching A fragment is read in that order. S^T and U^T go
+// to LDS in the order the chain wave holds them, 16 contiguous bytes per lane (strided
+// LDS writes cost several times more than contiguous ones).
 //
-// The two output waves run one chunk behind: wave p takes the row blocks {0, 3} (p = 0)
-// or {1, 2} (p = 1), five causal score tiles each. In the iteration of chunk c they form
-// the score tiles P^T_{c-1} = (K Q^T) o D of their rows (D_sr = exp(c_r - c_s), s <= r)
-// and write O_{c-1}^T = gamma (S^T Q^T) + U^T P^T from the copies the chain waves left in
-// LDS.
+// The three output waves run one chunk behind: wave p takes the row blocks {3}, {2} and
+// {0, 1} (p = 0, 1, 2: 28, 24 and 32 products). In the iteration of chunk c they form the
+// score tiles P^T_{c-1} = (K Q^T) o D of their rows (D_sr = exp(c_r - c_s), s <= r),
+// reading each K block and the S^T and U^T fragments once for all their row blocks, and
+// write O_{c-1}^T = gamma (S^T Q^T) + U^T P^T from the copies the chain waves left in LDS.
 //
-// The chunk operands that several waves share (K, T) go from global memory straight into
-// LDS (buffer loads with an LDS destination, 16 bytes per lane), two chunks ahead, into a
-// ring of four slots, every wave copying its share; each wave waits for its own copies of
-// the next chunk before the barrier that ends the current one. A chain wave loads its
-// value columns straight into registers in the result-tile layout, also two chunks ahead. Every slot is an LDS object of its
-// own and the chunk loop is unrolled by four, so the compiler sees which slot each access
-// touches and never waits on a copy in flight to another slot. Per-sequence buffer
-// resources make every load past the end of the sequence read zero and drop every store
-// past it, so ragged tails need no branches.
+// The chunk operands (K, T, the value tile) go from global memory straight into LDS
+// (buffer loads with an LDS destination, 16 bytes per lane), two chunks ahead, into a ring
+// of four slots; the output waves issue all of these copies, every third 1 KiB block each,
+// and wait for their own copies of the next chunk before the barrier that ends the current
+// one. Output wave 0 also lays out each chunk's gate factors one chunk ahead. Every slot is
+// an LDS object of its own and the chunk loop is unrolled by four, so the compiler sees
+// which slot each access touches and never waits on a copy in flight to another slot.
+// Per-sequence buffer resources make every load past the end of the sequence read zero and
+// drop every store past it, so ragged tails need no branches.
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 // 16 bytes per lane from a buffer straight into LDS at lds + 16 lane (lds wave-uniform).
 __device__ __forceinline__ void dma16(rsrc_t r, const uint16_t* lds, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds), 16, voff, 0, 0, 0);
 }
-// A fragment of the transpose of a row-major [K rows][columns] bf16 tile: M = columns
-// n0 .. n0 + 15, K = rows 32 kk .. + 31 in the pair-of-tiles slot order (LDS transpose
-// reads: lane L of a 16-lane group addresses row L / 4 of a 4-row block).
-__device__ __forceinline__ bf16x8_t frag_tr_pk(const uint16_t* t, int pitch, int kk, int n0,
-                                               int lane) {
+// A fragment of K^T for the state update: M = the 16 state rows of tile 2 kk + h in the
+// permuted key order (keys 32 kk + 4 h + 8 q + e, q, e < 4), K = tokens 32 tkk .. + 31 in
+// the pair-of-tiles slot order. LDS transpose reads: lane L of a 16-lane group addresses
+// token row L / 4 of a 4-row block and four keys that land in lanes 4 (L & 3) .. + 3.
+__device__ __forceinline__ bf16x8_t frag_kt(const uint16_t* t, int tkk, int kk, int h, int lane) {
     const int g = lane >> 4, L = lane & 15;
-    const uint16_t* p = t + (32 * kk + 4 * g + (L >> 2)) * pitch + n0 + 4 * (L & 3);
+    const uint16_t* p = t + (32 * tkk + 4 * g + (L >> 2)) * PQ + 32 * kk + 4 * h + 8 * (L & 3);
     const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
-    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 16 * pitch));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 16 * PQ));
     const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8_t, v);
-}
-// A fragment over K = 32 kk .. + 31 of row `row` of a padded row-major bf16 tile, pair-of-
-// tiles slot order.
-__device__ __forceinline__ bf16x8_t frag_row_pk(const uint16_t* t, int pitch, int row, int kk,
-                                                int lane) {
-    const uint16_t* p = t + row * pitch + 32 * kk + 4 * (lane >> 4);
-    const uint2 lo = *reinterpret_cast<const uint2*>(p);
-    const uint2 hi = *reinterpret_cast<const uint2*>(p + 16);
-    return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 __device__ __forceinline__ uint2 pack4(f32x4_t d) {
     return make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
@@ -319,55 +319,60 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int NCW>
+template <int NCB>
 struct FwdShape {
-    static constexpr int VT = 16 * NCW;
-    static constexpr int NW = NCW + 2;                 // waves per workgroup
-    // the padded K tile is 64 rows of 17 16-byte pieces (16 of data, one of padding):
-    // 17 blocks of 1 KiB; each wave issues KDMA of them (some twice, so that every wave
-    // issues the same number)
+    static constexpr int VT = 16 * NCB;
+    static constexpr int NW = NCB == 2 ? 5 : 4;        // waves per workgroup
+    // Copies into LDS are issued by the three output waves, output wave p taking the 1 KiB
+    // blocks p, p + 3, ...: the padded K tile (64 rows of PQ / 8 16-byte pieces), T (8
+    // blocks) and the value tile (64 rows of VT / 8 pieces).
     static constexpr int KBLK = C * (PQ / 8) / 64;
-    static constexpr int KDMA = (KBLK + NW - 1) / NW;
-    // T of a chunk is 8 blocks of 1 KiB, split over all waves the same way
-    static constexpr int TDMA = (8 + NW - 1) / NW;
-    static constexpr int VLD = 16;                     // 2-byte value loads per lane
-    // vector-memory operations a wave issues per iteration before the barrier's wait
-    // (loads only; the output waves' stores are not counted, so the wait is at least as
-    // strict as needed)
-    static constexpr int VM_CHAIN = KDMA + TDMA + VLD + 2;
-    static constexpr int VM_OUT = KDMA + TDMA + 8 + 1;
-    // two iterations of copies in flight stay within the 6-bit vector-memory counter
-    static_assert(2 * VM_CHAIN <= 63 && 2 * VM_OUT <= 63, "vmcnt range");
+    static constexpr int TBLK = 8;
+    static constexpr int VBLK = C * (VT / 8) / 64;
+    static constexpr int share(int nb, int p) { return (nb - p + 2) / 3; }
+    // row blocks of output wave p: {3}, {2}, {0, 1}
+    static constexpr int nrb(int p) { return p == 2 ? 2 : 1; }
+    // vector-memory loads output wave p issues per iteration: copies, q rows, and the
+    // gates for wave 0 (its stores come after them, so waiting for all but this many is
+    // at least as strict as needed)
+    static constexpr int vm_out(int p) {
+        return share(KBLK, p) + share(TBLK, p) + share(VBLK, p) + 4 * nrb(p) + (p == 0 ? 2 : 0);
+    }
+    // two iterations of loads in flight stay within the 6-bit vector-memory counter
+    static_assert(2 * vm_out(0) <= 63 && 2 * vm_out(1) <= 63 && 2 * vm_out(2) <= 63, "vmcnt range");
 };
 static_assert(PQ % 8 == 0 && C * (PQ / 8) % 64 == 0, "padded K rows in whole 1 KiB blocks");
 
 template <int J>
 using Ic = std::integral_constant<int, J>;
 
-// One chunk's operands that several waves read: K [s][i] (padded rows) and T in fragment
-// order, copied straight from global memory.
+// One chunk's operands as the waves read them, copied straight from global memory: K
+// [s][i] (padded rows), T in fragment order, the value tile [s][col].
+template <int VT>
 struct __align__(16) ChunkSmem {
     __align__(16) uint16_t k[C * PQ];
     __align__(16) uint16_t t[C * C];
+    __align__(16) uint16_t v[C * VT];
 };
 
-template <int NCW, bool GB>
-__global__ __launch_bounds__(64 * (NCW + 2)) void gdn_fwd_kernel(GdnArgs a) {
-    using Sh = FwdShape<NCW>;
-    constexpr int VT = Sh::VT, NW = Sh::NW;
-    // a ring of four chunks (slot = chunk mod 4), each slot one LDS object holding the
-    // chunk's K and T
-    __shared__ ChunkSmem sl0, sl1, sl2, sl3;
-    __shared__ __align__(16) uint16_t st0[VT * PQ], st1[VT * PQ];   // S^T [col][i]
-    __shared__ __align__(16) uint16_t ut0[VT * PC], ut1[VT * PC];   // U^T [col][s]
-    __shared__ __align__(16) float gs[NCW + 2][3][C];               // per-wave gate factors
-    auto slot_ = [&](auto I) -> ChunkSmem& {
+template <int NCB, bool GB>
+__global__ __launch_bounds__(320) void gdn_fwd_kernel(GdnArgs a) {
+    using Sh = FwdShape<NCB>;
+    constexpr int VT = Sh::VT;
+    // a ring of four chunks (slot = chunk mod 4), each slot one LDS object
+    __shared__ ChunkSmem<VT> sl0, sl1, sl2, sl3;
+    // S^T and U^T as the output waves' A fragments, in the order the chain wave holds them
+    // (fragment-major, 16 bytes per lane: every write and read covers 1 KiB contiguously)
+    __shared__ __align__(16) uint16_t st0[NCB * 4 * 512], st1[NCB * 4 * 512];
+    __shared__ __align__(16) uint16_t ut0[NCB * 2 * 512], ut1[NCB * 2 * 512];
+    // per-chunk gate factors (slot = chunk mod 4): cumulative log gate c_r, gamma_r =
+    // exp(c_r), d_r = exp(c_last - c_r), beta_r (zero on padding rows)
+    __shared__ __align__(16) float gsl[4][4][C];
+    auto slot_ = [&](auto I) -> ChunkSmem<VT>& {
         constexpr int s = decltype(I)::value & 3;
         if constexpr (s == 0) return sl0; else if constexpr (s == 1) return sl1;
         else if constexpr (s == 2) return sl2; else return sl3;
     };
-    auto ks_ = [&](auto I) -> uint16_t* { return slot_(I).k; };
-    auto ts_ = [&](auto I) -> uint16_t* { return slot_(I).t; };
     auto sts_ = [&](auto I) -> uint16_t* {
         if constexpr ((decltype(I)::value & 1) == 0) return st0; else return st1;
     };
@@ -389,331 +394,321 @@ __global__ __launch_bounds__(64 * (NCW + 2)) void gdn_fwd_kernel(GdnArgs a) {
     // chunk past the end reads zeros and leaves the state unchanged
     const int niter = ((nchunks + 1 + 3) / 4) * 4;
 
-    constexpr uint32_t GS = GB ? 2u : 4u;
-
-    // this wave's 1 KiB blocks of the padded K tile: piece p = 64 b + lane is row p / 17,
-    // 16-byte chunk p % 17 (chunk 16 is padding, filled with chunk 0); a wave may repeat a
-    // block of another so that every wave issues the same number. The global offsets
-    // within a chunk are fixed per lane.
-    // Each copy's per-lane offset is fixed for the whole walk (registers never rewritten
-    // while a copy that names them may still be in flight); the chunk is selected by the
-    // buffer resource, built per chunk from scalars with the bytes left in the sequence
-    // (none past its end, so those copies fill zeros).
-    uint32_t koff[Sh::KDMA];
-#pragma unroll
-    for (int x = 0; x < Sh::KDMA; ++x) {
-        const int b = (w + NW * x) % Sh::KBLK, pz = 64 * b + lane;
-        const int row = pz / (PQ / 8), ck = pz % (PQ / 8);
-        koff[x] = uint32_t(row * DK + (ck < DK / 8 ? ck : 0) * 8) * 2u;
-    }
-    auto rows_left = [&](int ch) { return uint32_t(max(0, sp.len - ch * C)); };
-    // resources over one chunk (and what follows it in the sequence) of a token-major array
-    auto gate_rsrc = [&](const void* base, int ch) {
-        return make_rsrc(static_cast<const char*>(base) + (tok0 + size_t(ch) * C) * GS, rows_left(ch) * GS);
-    };
-    const uint32_t goff = uint32_t(lane) * GS;   // lane = token
-    // copies of K of chunk ch into kb
-    auto dma_k = [&](uint16_t* kb, int ch) {
-        const rsrc_t r = make_rsrc(a.k + (tok0 + size_t(ch) * C) * DK, rows_left(ch) * DK * 2u);
-#pragma unroll
-        for (int x = 0; x < Sh::KDMA; ++x) {
-            const int b = (w + NW * x) % Sh::KBLK;
-            dma16(r, kb + b * 512, koff[x]);
-        }
-    };
-    // this wave's 1 KiB blocks of T of a chunk (stored in fragment order by the prep)
-    uint32_t toff[Sh::TDMA];
-#pragma unroll
-    for (int x = 0; x < Sh::TDMA; ++x) toff[x] = uint32_t((w + NW * x) % 8) * 1024u + lane * 16u;
-    auto dma_t = [&](uint16_t* tb_, int ch) {
-        const rsrc_t r1 = make_rsrc(a.T + (seq * size_t(a.nchunks) + size_t(ch)) * (C * C),
-                                    ch < nchunks ? C * C * 2u : 0u);
-#pragma unroll
-        for (int x = 0; x < Sh::TDMA; ++x) dma16(r1, tb_ + ((w + NW * x) % 8) * 512, toff[x]);
-    };
-    float (*gw)[C] = gs[w];
-
-    if (w < NCW) {
+    if (w == 0 || w == 4) {
         // =========================== chain wave ===========================
-        const int cb = 16 * w;   // first column of this wave within the tile
+        // Reads only LDS: the chunk's K, T and value tile and its gate factors are in
+        // place when the iteration starts. S[2 kk + h][e] is key 32 kk + 8 g + 4 h + e of
+        // column c0 + 16 cb + j.
+        const int cb = w == 0 ? 0 : 1;
         f32x4_t S[8];
+        auto key = [&](int ib, int e) { return 32 * (ib >> 1) + 8 * g + 4 * (ib & 1) + e; };
 #pragma unroll
         for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * ib + 4 * g + e;
-                S[ib][e] = a.S0 ? a.S0[seq * DK * DV + size_t(i) * DV + c0 + cb + jl] : 0.f;
-            }
-        // this lane's value column cb + j of token rows 4 g + e (+ 16 tb), the result-tile
-        // layout of KS, straight from global memory
-        const uint32_t voff = ((4 * g) * uint32_t(DV) + c0 + cb + jl) * 2u;
-        struct VSet { uint32_t v[4][4]; };
-        auto load_v = [&](VSet& V, int ch) {
-            const rsrc_t r2 = make_rsrc(a.v + (tok0 + size_t(ch) * C) * DV,
-                                        rows_left(ch) * uint32_t(DV) * 2u);
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    V.v[tb][e] = __builtin_amdgcn_raw_buffer_load_b16(
-                        r2, voff + uint32_t((16 * tb + e) * DV * 2), 0, 0);
-        };
-        VSet VS[4];
-        struct Gate { uint32_t ga, gb; };
-        auto load_g = [&](Gate& G, int ch) {
-            G.ga = buf_ld_gate_off<GB>(gate_rsrc(a.alpha, ch), goff);
-            G.gb = buf_ld_gate_off<GB>(gate_rsrc(a.beta, ch), goff);
-        };
-        Gate G[4];
+            for (int e = 0; e < 4; ++e)
+                S[ib][e] = a.S0 ? a.S0[seq * DK * DV + size_t(key(ib, e)) * DV + c0 + 16 * cb + jl] : 0.f;
 
-        auto step = [&](auto J, int ch) {
+        auto step = [&](auto J) {
             constexpr int j = decltype(J)::value;
-            dma_k(ks_(Ic<j + 2>{}), ch + 2);
-            dma_t(ts_(Ic<j + 2>{}), ch + 2);
-            load_v(VS[(j + 2) & 3], ch + 2);
-            load_g(G[(j + 2) & 3], ch + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            const Gate& Gc = G[j];
-            const int n = min(C, sp.len - ch * C);
-            const uint16_t* kc = ks_(J);
-            const uint16_t* tc = ts_(J);
-            // per-token gate factors (lane = token; padding rows are identity steps)
-            const float lg = lane < n ? fast_log(gate_val<GB>(Gc.ga)) : 0.f;
-            const float cum = wave_inclusive_scan(lg);
-            const float clast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), 63));
-            gw[0][lane] = fast_exp(cum);            // gamma_r
-            gw[1][lane] = fast_exp(clast - cum);    // d_r
-            gw[2][lane] = lane < n ? gate_val<GB>(Gc.gb) : 0.f;
-            // S as B fragments (keys in pair-of-tiles slot order), and S^T entering the chunk
-            // for the output waves from the same packed words
+            const uint16_t* kc = slot_(J).k;
+            const uint16_t* tc = slot_(J).t;
+            const uint16_t* vc = slot_(J).v;
+            const float (*gc)[C] = gsl[j & 3];
+            // S as B fragments (keys 32 kk + 8 g .. + 7), and S^T entering the chunk for
+            // the output waves from the same words (row 16 cb + j, keys 32 kk + 8 g ..: the
+            // output waves' A fragment (cb, kk) of lane 16 g + j)
             bf16x8_t Sb[4];
             uint16_t* stc = sts_(J);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 Sb[kk] = pack_pk(S[2 * kk], S[2 * kk + 1]);
-                const uint4 wd = __builtin_bit_cast(uint4, Sb[kk]);
-                *reinterpret_cast<uint2*>(stc + (cb + jl) * PQ + 32 * kk + 4 * g) = make_uint2(wd.x, wd.y);
-                *reinterpret_cast<uint2*>(stc + (cb + jl) * PQ + 32 * kk + 16 + 4 * g) = make_uint2(wd.z, wd.w);
+                *reinterpret_cast<bf16x8_t*>(stc + ((4 * cb + kk) * 64 + lane) * 8) = Sb[kk];
             }
             // KS = K S, rows 16 tb + 4 g + e; the next row block's A fragments are read
             // while the current one's products issue
             f32x4_t ks[4];
             bf16x8_t ka[2][4];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) ka[0][kk] = frag_row_pk(kc, PQ, jl, kk, lane);
+            for (int kk = 0; kk < 4; ++kk) ka[0][kk] = frag_kc(kc, PQ, 0, 32 * kk, lane);
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
                 if (tb < 3) {
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk)
-                        ka[(tb + 1) & 1][kk] = frag_row_pk(kc, PQ, 16 * (tb + 1) + jl, kk, lane);
+                        ka[(tb + 1) & 1][kk] = frag_kc(kc, PQ, 16 * (tb + 1), 32 * kk, lane);
                 }
                 ks[tb] = zero4();
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) ks[tb] = mfma16(ka[tb & 1][kk], Sb[kk], ks[tb]);
             }
-            // T fragments and the value tile (independent of the state)
+            // T fragments and the value tile in the result-tile layout (transpose reads:
+            // lane j receives column 16 cb + j of rows 16 tb + 4 g .. + 3)
             bf16x8_t tf[6];
             const int pc[6] = {0, 2, 4, 5, 6, 7};   // piece 2 tb + kk of T
 #pragma unroll
             for (int x = 0; x < 6; ++x)
                 tf[x] = *reinterpret_cast<const bf16x8_t*>(tc + (pc[x] * 64 + lane) * 8);
-            float vv[4][4];
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) vv[tb][e] = __uint_as_float(VS[j].v[tb][e] << 16);
-            wave_lds_sync();   // this wave's gate factors are in LDS
             // X = beta (V - gamma KS)
             f32x4_t X[4];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                const float4 g4 = *reinterpret_cast<const float4*>(&gw[0][16 * tb + 4 * g]);
-                const float4 b4 = *reinterpret_cast<const float4*>(&gw[2][16 * tb + 4 * g]);
-                X[tb][0] = b4.x * (vv[tb][0] - g4.x * ks[tb][0]);
-                X[tb][1] = b4.y * (vv[tb][1] - g4.y * ks[tb][1]);
-                X[tb][2] = b4.z * (vv[tb][2] - g4.z * ks[tb][2]);
-                X[tb][3] = b4.w * (vv[tb][3] - g4.w * ks[tb][3]);
+                const uint16_t* p = vc + (16 * tb + 4 * g + (jl >> 2)) * VT + 16 * cb + 4 * (jl & 3);
+                const i16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+                const float4 g4 = *reinterpret_cast<const float4*>(&gc[1][16 * tb + 4 * g]);
+                const float4 b4 = *reinterpret_cast<const float4*>(&gc[3][16 * tb + 4 * g]);
+                const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = __uint_as_float(uint32_t(uint16_t(x[e])) << 16);
+                    X[tb][e] = bv[e] * (v - gv[e] * ks[tb][e]);
+                }
             }
             const bf16x8_t Xb0 = pack_pk(X[0], X[1]), Xb1 = pack_pk(X[2], X[3]);
-            // U = T X (T lower triangular: row blocks 0, 1 need tokens 0..31 only)
+            // U = T X (T lower triangular: row blocks 0, 1 need tokens 0..31 only); U^T for
+            // the output waves (row 16 cb + j, tokens of tiles 2 kk and 2 kk + 1 in the pair-
+            // of-tiles slot order: their A fragment (cb, kk)); then d U as B fragments
             f32x4_t u[4];
             u[0] = mfma16(tf[0], Xb0, zero4());
             u[1] = mfma16(tf[1], Xb0, zero4());
             u[2] = mfma16(tf[2], Xb0, zero4());
-            u[2] = mfma16(tf[3], Xb1, u[2]);
             u[3] = mfma16(tf[4], Xb0, zero4());
+            u[2] = mfma16(tf[3], Xb1, u[2]);
             u[3] = mfma16(tf[5], Xb1, u[3]);
-            // U^T for the output waves
             uint16_t* utc = uts_(J);
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-                *reinterpret_cast<uint2*>(utc + (cb + jl) * PC + 16 * tb + 4 * g) = pack4(u[tb]);
-            // S <- gamma_last S + K^T (d U)
+            for (int kk = 0; kk < 2; ++kk)
+                *reinterpret_cast<bf16x8_t*>(utc + ((2 * cb + kk) * 64 + lane) * 8) =
+                    pack_pk(u[2 * kk], u[2 * kk + 1]);
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                const float4 d4 = *reinterpret_cast<const float4*>(&gw[1][16 * tb + 4 * g]);
+                const float4 d4 = *reinterpret_cast<const float4*>(&gc[2][16 * tb + 4 * g]);
                 u[tb][0] *= d4.x; u[tb][1] *= d4.y; u[tb][2] *= d4.z; u[tb][3] *= d4.w;
             }
             const bf16x8_t Ub0 = pack_pk(u[0], u[1]), Ub1 = pack_pk(u[2], u[3]);
-            const float glast = fast_exp(clast);
+            // S <- gamma_last S + K^T (d U)
+            const float glast = gc[1][C - 1];
             bf16x8_t kt[2][2];
-            kt[0][0] = frag_tr_pk(kc, PQ, 0, 0, lane);
-            kt[0][1] = frag_tr_pk(kc, PQ, 1, 0, lane);
+            kt[0][0] = frag_kt(kc, 0, 0, 0, lane);
+            kt[0][1] = frag_kt(kc, 1, 0, 0, lane);
 #pragma unroll
             for (int ib = 0; ib < 8; ++ib) {
                 if (ib < 7) {
-                    kt[(ib + 1) & 1][0] = frag_tr_pk(kc, PQ, 0, 16 * (ib + 1), lane);
-                    kt[(ib + 1) & 1][1] = frag_tr_pk(kc, PQ, 1, 16 * (ib + 1), lane);
+                    kt[(ib + 1) & 1][0] = frag_kt(kc, 0, (ib + 1) >> 1, (ib + 1) & 1, lane);
+                    kt[(ib + 1) & 1][1] = frag_kt(kc, 1, (ib + 1) >> 1, (ib + 1) & 1, lane);
                 }
                 f32x4_t s_ = S[ib] * glast;
                 s_ = mfma16(kt[ib & 1][0], Ub0, s_);
                 s_ = mfma16(kt[ib & 1][1], Ub1, s_);
                 S[ib] = s_;
             }
-            // the next chunk's K and T (copies issued an iteration ago) have landed
-            wait_vmcnt<Sh::VM_CHAIN>();
             lds_barrier();
         };
 
-        dma_k(sl0.k, 0);
-        dma_t(sl0.t, 0);
-        dma_k(sl1.k, 1);
-        dma_t(sl1.t, 1);
-        load_v(VS[0], 0);
-        load_v(VS[1], 1);
-        load_g(G[0], 0);
-        load_g(G[1], 1);
-        wait_vmcnt<0>();
         lds_barrier();
         for (int ch = 0; ch < niter; ch += 4) {
-            step(Ic<0>{}, ch);
-            step(Ic<1>{}, ch + 1);
-            step(Ic<2>{}, ch + 2);
-            step(Ic<3>{}, ch + 3);
+            step(Ic<0>{});
+            step(Ic<1>{});
+            step(Ic<2>{});
+            step(Ic<3>{});
         }
 #pragma unroll
         for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * ib + 4 * g + e;
-                a.S[seq * DK * DV + size_t(i) * DV + c0 + cb + jl] = S[ib][e];
-            }
+            for (int e = 0; e < 4; ++e)
+                a.S[seq * DK * DV + size_t(key(ib, e)) * DV + c0 + 16 * cb + jl] = S[ib][e];
     } else {
         // =========================== output wave ===========================
-        struct QSet {
-            uint4 q[2][4];    // rows 16 rb + j of q (the wave's two row blocks), keys 32 kk + 8 g ..
-            uint32_t ga;
+        // Output wave p (0, 1, 2: waves 1, 2, 3) copies every third 1 KiB block of the chunk
+        // operands two chunks ahead, wave 0 also loads the gates three chunks ahead and lays
+        // out the next chunk's gate factors; each then writes the outputs of its row blocks
+        // of the chunk before the chain's.
+        constexpr uint32_t GS = GB ? 2u : 4u;
+        auto rows_left = [&](int ch) { return uint32_t(max(0, sp.len - ch * C)); };
+        auto gate_rsrc = [&](const void* base, int ch) {
+            return make_rsrc(static_cast<const char*>(base) + (tok0 + size_t(ch) * C) * GS,
+                             rows_left(ch) * GS);
         };
+        const uint32_t goff = uint32_t(lane) * GS;   // lane = token
+        struct Gate { uint32_t ga, gb; };
         auto run = [&](auto pc) {
             constexpr int P = decltype(pc)::value;
-            constexpr int RB[2] = {P == 0 ? 0 : 1, P == 0 ? 3 : 2};
-            // per-lane offsets of the wave's q rows within a chunk and of its output rows
-            uint32_t qoff[2], ooff[2];
+            constexpr int NRB = Sh::nrb(P);
+            // the wave's row blocks: {3}, {2}, {0, 1}; RL is the last (largest)
+            constexpr int RL = P == 0 ? 3 : (P == 1 ? 2 : 1);
+            constexpr int RF = P == 2 ? 0 : RL;
+            constexpr int NK = Sh::share(Sh::KBLK, P), NT_ = Sh::share(Sh::TBLK, P),
+                          NV = Sh::share(Sh::VBLK, P);
+            // Each copy's per-lane offset is fixed for the whole walk (registers never
+            // rewritten while a copy that names them may still be in flight); the chunk is
+            // selected by the buffer resource, built per chunk from scalars with the bytes
+            // left in the sequence (none past its end, so those copies fill zeros).
+            // K: piece 64 b + lane of the padded tile is row / column piece (pieces past the
+            // 16 of a row are padding, filled with piece 0)
+            uint32_t koff[NK], toff[NT_], voff[NV > 0 ? NV : 1];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                qoff[h] = ((16 * RB[h] + jl) * DK + 8 * g) * 2u;
-                ooff[h] = ((16 * RB[h] + jl) * uint32_t(DV) + c0 + 4 * g) * 2u;
+            for (int x = 0; x < NK; ++x) {
+                const int pz = 64 * (3 * x + P) + lane;
+                const int row = pz / (PQ / 8), ck = pz % (PQ / 8);
+                koff[x] = uint32_t(row * DK + (ck < DK / 8 ? ck : 0) * 8) * 2u;
             }
+#pragma unroll
+            for (int x = 0; x < NT_; ++x) toff[x] = uint32_t(3 * x + P) * 1024u + lane * 16u;
+#pragma unroll
+            for (int x = 0; x < NV; ++x) {
+                const int pz = 64 * (3 * x + P) + lane;
+                const int row = pz / (VT / 8), ck = pz % (VT / 8);
+                voff[x] = uint32_t(row * DV + c0 + 8 * ck) * 2u;
+            }
+            auto copies = [&](ChunkSmem<VT>& dst, int ch) {
+                const rsrc_t rk = make_rsrc(a.k + (tok0 + size_t(ch) * C) * DK, rows_left(ch) * DK * 2u);
+#pragma unroll
+                for (int x = 0; x < NK; ++x) dma16(rk, dst.k + (3 * x + P) * 512, koff[x]);
+                const rsrc_t rt = make_rsrc(a.T + (seq * size_t(a.nchunks) + size_t(ch)) * (C * C),
+                                            ch < nchunks ? C * C * 2u : 0u);
+#pragma unroll
+                for (int x = 0; x < NT_; ++x) dma16(rt, dst.t + (3 * x + P) * 512, toff[x]);
+                const rsrc_t rv = make_rsrc(a.v + (tok0 + size_t(ch) * C) * DV,
+                                            rows_left(ch) * uint32_t(DV) * 2u);
+#pragma unroll
+                for (int x = 0; x < NV; ++x) dma16(rv, dst.v + (3 * x + P) * 512, voff[x]);
+            };
+            // per-lane offsets of the wave's q rows within a chunk and of its output rows
+            uint32_t qoff[NRB], ooff[NRB];
+#pragma unroll
+            for (int h = 0; h < NRB; ++h) {
+                const int rb = h == NRB - 1 ? RL : RF;
+                qoff[h] = ((16 * rb + jl) * DK + 8 * g) * 2u;
+                ooff[h] = ((16 * rb + jl) * uint32_t(DV) + c0 + 4 * g) * 2u;
+            }
+            struct QSet {
+                uint4 q[NRB][4];   // rows 16 rb + j of q (the wave's row blocks), keys 32 kk + 8 g ..
+            };
             auto load_q = [&](QSet& Q, int ch) {
-                Q.ga = buf_ld_gate_off<GB>(gate_rsrc(a.alpha, ch), goff);
                 const rsrc_t r = make_rsrc(a.q + (tok0 + size_t(ch) * C) * DK, rows_left(ch) * DK * 2u);
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                for (int h = 0; h < NRB; ++h)
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) Q.q[h][kk] = buf_ld16_off(r, qoff[h], 64 * kk);
             };
-            // rows of row block RB[h] of chunk cp: scores, then outputs
-            auto rows = [&](const QSet& Qp, auto hc, const rsrc_t& orc, const uint16_t* kc,
-                            const uint16_t* stc, const uint16_t* utc) {
-                constexpr int h = decltype(hc)::value;
-                constexpr int rb = RB[h];
-                const int r = 16 * rb + jl;
-                const float crr = gw[0][r];
-                f32x4_t pt[4] = {zero4(), zero4(), zero4(), zero4()};
+            auto load_g = [&](Gate& G, int ch) {
+                G.ga = buf_ld_gate_off<GB>(gate_rsrc(a.alpha, ch), goff);
+                G.gb = buf_ld_gate_off<GB>(gate_rsrc(a.beta, ch), goff);
+            };
+            // gate factors of chunk ch (lane = token; padding rows are identity steps)
+            auto gates = [&](const Gate& G, int ch, float (*dst)[C]) {
+                const int n = min(C, sp.len - ch * C);
+                const float lg = lane < n ? fast_log(gate_val<GB>(G.ga)) : 0.f;
+                const float cum = wave_inclusive_scan(lg);
+                const float clast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), 63));
+                dst[0][lane] = cum;
+                dst[1][lane] = fast_exp(cum);
+                dst[2][lane] = fast_exp(clast - cum);
+                dst[3][lane] = lane < n ? gate_val<GB>(G.gb) : 0.f;
+            };
+            // the wave's row blocks of chunk cp: scores, then outputs
+            auto rows = [&](const QSet& Qp, const rsrc_t& orc, const uint16_t* kc,
+                            const uint16_t* stc, const uint16_t* utc, const float* cum) {
+                // score tiles P^T[s][r] of the row blocks (h = NRB - 1: RL, h = 0: RF), each K
+                // block read once
+                f32x4_t pt[NRB][4];
+#pragma unroll
+                for (int h = 0; h < NRB; ++h)
+#pragma unroll
+                    for (int sb = 0; sb < 4; ++sb) pt[h][sb] = zero4();
                 bf16x8_t kf[2][4];
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) kf[0][kk] = frag_kc(kc, PQ, 0, 32 * kk, lane);
 #pragma unroll
-                for (int sb = 0; sb <= rb; ++sb) {
-                    if (sb < rb) {
+                for (int sb = 0; sb <= RL; ++sb) {
+                    if (sb < RL) {
 #pragma unroll
                         for (int kk = 0; kk < 4; ++kk)
                             kf[(sb + 1) & 1][kk] = frag_kc(kc, PQ, 16 * (sb + 1), 32 * kk, lane);
                     }
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk)
-                        pt[sb] = mfma16(kf[sb & 1][kk], __builtin_bit_cast(bf16x8_t, Qp.q[h][kk]), pt[sb]);
-                }
-                bf16x8_t sf[NCW][4];
-#pragma unroll
-                for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) sf[ct][kk] = frag_kc(stc, PQ, 16 * ct, 32 * kk, lane);
-                bf16x8_t uf[NCW][2];
-#pragma unroll
-                for (int ct = 0; ct < NCW; ++ct)
-#pragma unroll
-                    for (int kk = 0; kk < (rb >= 2 ? 2 : 1); ++kk)
-                        uf[ct][kk] = frag_row_pk(utc, PC, 16 * ct + jl, kk, lane);
-#pragma unroll
-                for (int sb = 0; sb <= rb; ++sb) {
-                    const float4 cs = *reinterpret_cast<const float4*>(&gw[0][16 * sb + 4 * g]);
-                    const float csv[4] = {cs.x, cs.y, cs.z, cs.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int s = 16 * sb + 4 * g + e;
-                        const float x = fast_exp(crr - csv[e]) * pt[sb][e];
-                        pt[sb][e] = (sb < rb || s <= r) ? x : 0.f;
+                    for (int kk = 0; kk < 4; ++kk) {
+                        pt[NRB - 1][sb] = mfma16(kf[sb & 1][kk], __builtin_bit_cast(bf16x8_t, Qp.q[NRB - 1][kk]),
+                                                 pt[NRB - 1][sb]);
+                        if (NRB == 2 && sb <= RF)
+                            pt[0][sb] = mfma16(kf[sb & 1][kk], __builtin_bit_cast(bf16x8_t, Qp.q[0][kk]), pt[0][sb]);
                     }
                 }
-                const bf16x8_t pf0 = pack_pk(pt[0], pt[1]), pf1 = pack_pk(pt[2], pt[3]);
-                const float gr = fast_exp(crr);
-                // O^T = gamma (S^T Q^T) + U^T P^T: columns 16 ct + 4 g .. of token r
+                // S^T and U^T fragments, read once for all the row blocks
+                bf16x8_t sf[NCB][4];
 #pragma unroll
-                for (int ct = 0; ct < NCW; ++ct) {
-                    f32x4_t oq = zero4();
+                for (int ct = 0; ct < NCB; ++ct)
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk)
-                        oq = mfma16(sf[ct][kk], __builtin_bit_cast(bf16x8_t, Qp.q[h][kk]), oq);
-                    f32x4_t o_ = oq * gr;
-                    o_ = mfma16(uf[ct][0], pf0, o_);
-                    if constexpr (rb >= 2) o_ = mfma16(uf[ct][1], pf1, o_);
-                    buf_st8_off(orc, ooff[h], 32 * ct, pack4(o_));
+                        sf[ct][kk] = *reinterpret_cast<const bf16x8_t*>(stc + ((4 * ct + kk) * 64 + lane) * 8);
+                bf16x8_t uf[NCB][2];
+#pragma unroll
+                for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+                    for (int kk = 0; kk < (RL >= 2 ? 2 : 1); ++kk)
+                        uf[ct][kk] = *reinterpret_cast<const bf16x8_t*>(utc + ((2 * ct + kk) * 64 + lane) * 8);
+#pragma unroll
+                for (int h = 0; h < NRB; ++h) {
+                    const int rb = h == NRB - 1 ? RL : RF;
+                    const int r = 16 * rb + jl;
+                    const float crr = cum[r];
+#pragma unroll
+                    for (int sb = 0; sb < 4; ++sb) {
+                        if (sb > rb) continue;
+                        const float4 cs = *reinterpret_cast<const float4*>(&cum[16 * sb + 4 * g]);
+                        const float csv[4] = {cs.x, cs.y, cs.z, cs.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int s = 16 * sb + 4 * g + e;
+                            const float x = fast_exp(crr - csv[e]) * pt[h][sb][e];
+                            pt[h][sb][e] = (sb < rb || s <= r) ? x : 0.f;
+                        }
+                    }
+                    const bf16x8_t pf0 = pack_pk(pt[h][0], pt[h][1]), pf1 = pack_pk(pt[h][2], pt[h][3]);
+                    const float gr = fast_exp(crr);
+                    // O^T = gamma (S^T Q^T) + U^T P^T: columns 16 ct + 4 g .. of token r
+#pragma unroll
+                    for (int ct = 0; ct < NCB; ++ct) {
+                        f32x4_t oq = zero4();
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk)
+                            oq = mfma16(sf[ct][kk], __builtin_bit_cast(bf16x8_t, Qp.q[h][kk]), oq);
+                        f32x4_t o_ = oq * gr;
+                        o_ = mfma16(uf[ct][0], pf0, o_);
+                        if (rb >= 2) o_ = mfma16(uf[ct][1], pf1, o_);
+                        buf_st8_off(orc, ooff[h], 32 * ct, pack4(o_));
+                    }
                 }
             };
             QSet Q[4];   // chunk x's q in set x mod 4, loaded two iterations ahead
+            Gate G[4];   // chunk x's gates in set x mod 4, loaded three iterations ahead
             auto step = [&](auto J, int ch) {
                 constexpr int j = decltype(J)::value;
-                dma_k(ks_(Ic<j + 2>{}), ch + 2);
-                dma_t(ts_(Ic<j + 2>{}), ch + 2);
+                copies(slot_(Ic<j + 2>{}), ch + 2);
                 load_q(Q[(j + 2) & 3], ch + 2);
+                if constexpr (P == 0) load_g(G[(j + 3) & 3], ch + 3);
                 __builtin_amdgcn_sched_barrier(0);
+                if constexpr (P == 0) gates(G[(j + 1) & 3], ch + 1, gsl[(j + 1) & 3]);
                 const int cp = ch - 1;
                 if (cp >= 0) {
-                    const QSet& Qp = Q[(j + 3) & 3];
-                    const int n = min(C, sp.len - cp * C);
-                    const float lg = lane < n ? fast_log(gate_val<GB>(Qp.ga)) : 0.f;
-                    gw[0][lane] = wave_inclusive_scan(lg);
-                    wave_lds_sync();
-                    const uint16_t* kc = ks_(Ic<j + 3>{});
-                    const uint16_t* stc = sts_(Ic<j + 1>{});
-                    const uint16_t* utc = uts_(Ic<j + 1>{});
                     const rsrc_t orc = make_rsrc(a.o + (tok0 + size_t(cp) * C) * DV,
                                                  rows_left(cp) * uint32_t(DV) * 2u);
-                    rows(Qp, Ic<0>{}, orc, kc, stc, utc);
-                    rows(Qp, Ic<1>{}, orc, kc, stc, utc);
+                    rows(Q[(j + 3) & 3], orc, slot_(Ic<j + 3>{}).k, sts_(Ic<j + 1>{}),
+                         uts_(Ic<j + 1>{}), gsl[(j + 3) & 3][0]);
                 }
-                wait_vmcnt<Sh::VM_OUT>();
+                wait_vmcnt<Sh::vm_out(P)>();
                 lds_barrier();
             };
-            dma_k(sl0.k, 0);
-            dma_t(sl0.t, 0);
-            dma_k(sl1.k, 1);
-            dma_t(sl1.t, 1);
+            copies(sl0, 0);
+            copies(sl1, 1);
             load_q(Q[0], 0);
             load_q(Q[1], 1);
+            if constexpr (P == 0) {
+                load_g(G[0], 0);
+                load_g(G[1], 1);
+                load_g(G[2], 2);
+            }
             wait_vmcnt<0>();
+            if constexpr (P == 0) gates(G[0], 0, gsl[0]);
             lds_barrier();
             for (int ch = 0; ch < niter; ch += 4) {
                 step(Ic<0>{}, ch);
@@ -722,8 +717,9 @@ __global__ __launch_bounds__(64 * (NCW + 2)) void gdn_fwd_kernel(GdnArgs a) {
                 step(Ic<3>{}, ch + 3);
             }
         };
-        if (w == NCW) run(Ic<0>{});
-        else run(Ic<1>{});
+        if (w == 1) run(Ic<0>{});
+        else if (w == 2) run(Ic<1>{});
+        else run(Ic<2>{});
     }
 }
 
@@ -748,9 +744,9 @@ GdnArgs make_args(const Problem& p) {
     return a;
 }
 
-template <int NCW, bool GB>
+template <int NCB, bool GB>
 hipError_t launch_cfg(const Problem& p) {
-    constexpr int VT = 16 * NCW;
+    constexpr int VT = 16 * NCB;
     GdnArgs a = make_args(p);
     a.ntiles = p.dv / VT;
     hipError_t e;
@@ -764,8 +760,8 @@ hipError_t launch_cfg(const Problem& p) {
         gdn_prep_kernel<GB><<<dim3(unsigned(blocks)), dim3(NT), smem, p.stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    gdn_fwd_kernel<NCW, GB>
-        <<<dim3(xcd_grid(a.ntiles, a.nseq)), dim3(64 * (NCW + 2)), 0, p.stream>>>(a);
+    gdn_fwd_kernel<NCB, GB>
+        <<<dim3(xcd_grid(a.ntiles, a.nseq)), dim3(64 * FwdShape<NCB>::NW), 0, p.stream>>>(a);
     return hipGetLastError();
 }
 
