@@ -251,10 +251,10 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
 // forward kernel
 // ---------------------------------------------------------------------------
 // One workgroup per (sequence, VT = 16 NCB value columns, NCB = 1 or 2): NCB chain waves
-// and three output waves, one workgroup barrier per chunk. The chain waves are waves 0
-// and 4, which share one SIMD: a wave does not issue vector ALU work while its own
-// matrix-core product runs, but another wave on the same SIMD does, so each chain wave's
-// packing and scaling fill the other's matrix-core time.
+// (waves 0 and 1) and four output waves (waves 2 .. 5), one workgroup barrier per chunk.
+// Waves w and w + 4 share a SIMD. A wave does not issue vector ALU work while its own
+// matrix-core product runs, but another wave on the same SIMD does, so each chain wave is
+// paired with one of the two lightest output waves, whose work fills the chain's stalls.
 //
 // Chain wave c owns 16 value columns (16 c .. + 15 of the tile) of the state for all 128
 // key rows, as eight fp32 16 x 16 result tiles in registers. Its walk over the chunks
@@ -275,15 +275,14 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
 // to LDS in the order the chain wave holds them, 16 contiguous bytes per lane (strided
 // LDS writes cost several times more than contiguous ones).
 //
-// The three output waves run one chunk behind: wave p takes the row blocks {3}, {2} and
-// {0, 1} (p = 0, 1, 2: 28, 24 and 32 products). In the iteration of chunk c they form the
-// score tiles P^T_{c-1} = (K Q^T) o D of their rows (D_sr = exp(c_r - c_s), s <= r),
-// reading each K block and the S^T and U^T fragments once for all their row blocks, and
-// write O_{c-1}^T = gamma (S^T Q^T) + U^T P^T from the copies the chain waves left in LDS.
+// The four output waves run one chunk behind: output wave p (wave 2 + p) takes row block
+// 3 - p (28, 24, 18 and 14 products). In the iteration of chunk c it forms the score tiles
+// P^T_{c-1} = (K Q^T) o D of its rows (D_sr = exp(c_r - c_s), s <= r) and writes
+// O_{c-1}^T = gamma (S^T Q^T) + U^T P^T from the copies the chain waves left in LDS.
 //
 // The chunk operands (K, T, the value tile) go from global memory straight into LDS
 // (buffer loads with an LDS destination, 16 bytes per lane), two chunks ahead, into a ring
-// of four slots; the output waves issue all of these copies, every third 1 KiB block each,
+// of four slots; the output waves issue all of these copies, every fourth 1 KiB block each,
 // and wait for their own copies of the next chunk before the barrier that ends the current
 // one. Output wave 0 also lays out each chunk's gate factors one chunk ahead. Every slot is
 // an LDS object of its own and the chunk loop is unrolled by four, so the compiler sees
@@ -322,24 +321,23 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int NCB>
 struct FwdShape {
     static constexpr int VT = 16 * NCB;
-    static constexpr int NW = NCB == 2 ? 5 : 4;        // waves per workgroup
-    // Copies into LDS are issued by the three output waves, output wave p taking the 1 KiB
-    // blocks p, p + 3, ...: the padded K tile (64 rows of PQ / 8 16-byte pieces), T (8
+    static constexpr int NW = 6;                       // waves per workgroup
+    static constexpr int NO = 4;                       // output waves
+    // Copies into LDS are issued by the output waves, output wave p taking the 1 KiB
+    // blocks p, p + 4, ...: the padded K tile (64 rows of PQ / 8 16-byte pieces), T (8
     // blocks) and the value tile (64 rows of VT / 8 pieces).
     static constexpr int KBLK = C * (PQ / 8) / 64;
     static constexpr int TBLK = 8;
     static constexpr int VBLK = C * (VT / 8) / 64;
-    static constexpr int share(int nb, int p) { return (nb - p + 2) / 3; }
-    // row blocks of output wave p: {3}, {2}, {0, 1}
-    static constexpr int nrb(int p) { return p == 2 ? 2 : 1; }
+    static constexpr int share(int nb, int p) { return (nb - p + NO - 1) / NO; }
     // vector-memory loads output wave p issues per iteration: copies, q rows, and the
     // gates for wave 0 (its stores come after them, so waiting for all but this many is
     // at least as strict as needed)
     static constexpr int vm_out(int p) {
-        return share(KBLK, p) + share(TBLK, p) + share(VBLK, p) + 4 * nrb(p) + (p == 0 ? 2 : 0);
+        return share(KBLK, p) + share(TBLK, p) + share(VBLK, p) + 4 + (p == 0 ? 2 : 0);
     }
     // two iterations of loads in flight stay within the 6-bit vector-memory counter
-    static_assert(2 * vm_out(0) <= 63 && 2 * vm_out(1) <= 63 && 2 * vm_out(2) <= 63, "vmcnt range");
+    static_assert(2 * vm_out(0) <= 63, "vmcnt range");
 };
 static_assert(PQ % 8 == 0 && C * (PQ / 8) % 64 == 0, "padded K rows in whole 1 KiB blocks");
 
@@ -356,7 +354,7 @@ struct __align__(16) ChunkSmem {
 };
 
 template <int NCB, bool GB>
-__global__ __launch_bounds__(320) void gdn_fwd_kernel(GdnArgs a) {
+__global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
     using Sh = FwdShape<NCB>;
     constexpr int VT = Sh::VT;
     // a ring of four chunks (slot = chunk mod 4), each slot one LDS object
@@ -394,22 +392,27 @@ __global__ __launch_bounds__(320) void gdn_fwd_kernel(GdnArgs a) {
     // chunk past the end reads zeros and leaves the state unchanged
     const int niter = ((nchunks + 1 + 3) / 4) * 4;
 
-    if (w == 0 || w == 4) {
+    if (w < 2) {
         // =========================== chain wave ===========================
         // Reads only LDS: the chunk's K, T and value tile and its gate factors are in
         // place when the iteration starts. S[2 kk + h][e] is key 32 kk + 8 g + 4 h + e of
         // column c0 + 16 cb + j.
-        const int cb = w == 0 ? 0 : 1;
+        const int cb = w;
         f32x4_t S[8];
         auto key = [&](int ib, int e) { return 32 * (ib >> 1) + 8 * g + 4 * (ib & 1) + e; };
 #pragma unroll
         for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                S[ib][e] = a.S0 ? a.S0[seq * DK * DV + size_t(key(ib, e)) * DV + c0 + 16 * cb + jl] : 0.f;
+                S[ib][e] = (a.S0 && cb < NCB) ? a.S0[seq * DK * DV + size_t(key(ib, e)) * DV + c0 + 16 * cb + jl]
+                                              : 0.f;
 
         auto step = [&](auto J) {
             constexpr int j = decltype(J)::value;
+            if (cb >= NCB) {   // no columns for this wave: keep the barriers only
+                lds_barrier();
+                return;
+            }
             const uint16_t* kc = slot_(J).k;
             const uint16_t* tc = slot_(J).t;
             const uint16_t* vc = slot_(J).v;
@@ -511,17 +514,19 @@ __global__ __launch_bounds__(320) void gdn_fwd_kernel(GdnArgs a) {
             step(Ic<2>{});
             step(Ic<3>{});
         }
+        if (cb < NCB) {
 #pragma unroll
-        for (int ib = 0; ib < 8; ++ib)
+            for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                a.S[seq * DK * DV + size_t(key(ib, e)) * DV + c0 + 16 * cb + jl] = S[ib][e];
+                for (int e = 0; e < 4; ++e)
+                    a.S[seq * DK * DV + size_t(key(ib, e)) * DV + c0 + 16 * cb + jl] = S[ib][e];
+        }
     } else {
         // =========================== output wave ===========================
-        // Output wave p (0, 1, 2: waves 1, 2, 3) copies every third 1 KiB block of the chunk
-        // operands two chunks ahead, wave 0 also loads the gates three chunks ahead and lays
-        // out the next chunk's gate factors; each then writes the outputs of its row blocks
-        // of the chunk before the chain's.
+        // Output wave p (waves 2 .. 5) copies every fourth 1 KiB block of the chunk operands
+        // two chunks ahead, output wave 0 also loads the gates three chunks ahead and lays
+        // out the next chunk's gate factors; each then writes the outputs of its row block of
+        // the chunk before the chain's.
         constexpr uint32_t GS = GB ? 2u : 4u;
         auto rows_left = [&](int ch) { return uint32_t(max(0, sp.len - ch * C)); };
         auto gate_rsrc = [&](const void* base, int ch) {
@@ -532,10 +537,8 @@ __global__ __launch_bounds__(320) void gdn_fwd_kernel(GdnArgs a) {
         struct Gate { uint32_t ga, gb; };
         auto run = [&](auto pc) {
             constexpr int P = decltype(pc)::value;
-            constexpr int NRB = Sh::nrb(P);
-            // the wave's row blocks: {3}, {2}, {0, 1}; RL is the last (largest)
-            constexpr int RL = P == 0 ? 3 : (P == 1 ? 2 : 1);
-            constexpr int RF = P == 2 ? 0 : RL;
+            constexpr int NRB = 1;
+            constexpr int RL = 3 - P, RF = RL;   // the wave's row block
             constexpr int NK = Sh::share(Sh::KBLK, P), NT_ = Sh::share(Sh::TBLK, P),
                           NV = Sh::share(Sh::VBLK, P);
             // Each copy's per-lane offset is fixed for the whole walk (registers never
@@ -547,30 +550,30 @@ __global__ __launch_bounds__(320) void gdn_fwd_kernel(GdnArgs a) {
             uint32_t koff[NK], toff[NT_], voff[NV > 0 ? NV : 1];
 #pragma unroll
             for (int x = 0; x < NK; ++x) {
-                const int pz = 64 * (3 * x + P) + lane;
+                const int pz = 64 * (Sh::NO * x + P) + lane;
                 const int row = pz / (PQ / 8), ck = pz % (PQ / 8);
                 koff[x] = uint32_t(row * DK + (ck < DK / 8 ? ck : 0) * 8) * 2u;
             }
 #pragma unroll
-            for (int x = 0; x < NT_; ++x) toff[x] = uint32_t(3 * x + P) * 1024u + lane * 16u;
+            for (int x = 0; x < NT_; ++x) toff[x] = uint32_t(Sh::NO * x + P) * 1024u + lane * 16u;
 #pragma unroll
             for (int x = 0; x < NV; ++x) {
-                const int pz = 64 * (3 * x + P) + lane;
+                const int pz = 64 * (Sh::NO * x + P) + lane;
                 const int row = pz / (VT / 8), ck = pz % (VT / 8);
                 voff[x] = uint32_t(row * DV + c0 + 8 * ck) * 2u;
             }
             auto copies = [&](ChunkSmem<VT>& dst, int ch) {
                 const rsrc_t rk = make_rsrc(a.k + (tok0 + size_t(ch) * C) * DK, rows_left(ch) * DK * 2u);
 #pragma unroll
-                for (int x = 0; x < NK; ++x) dma16(rk, dst.k + (3 * x + P) * 512, koff[x]);
+                for (int x = 0; x < NK; ++x) dma16(rk, dst.k + (Sh::NO * x + P) * 512, koff[x]);
                 const rsrc_t rt = make_rsrc(a.T + (seq * size_t(a.nchunks) + size_t(ch)) * (C * C),
                                             ch < nchunks ? C * C * 2u : 0u);
 #pragma unroll
-                for (int x = 0; x < NT_; ++x) dma16(rt, dst.t + (3 * x + P) * 512, toff[x]);
+                for (int x = 0; x < NT_; ++x) dma16(rt, dst.t + (Sh::NO * x + P) * 512, toff[x]);
                 const rsrc_t rv = make_rsrc(a.v + (tok0 + size_t(ch) * C) * DV,
                                             rows_left(ch) * uint32_t(DV) * 2u);
 #pragma unroll
-                for (int x = 0; x < NV; ++x) dma16(rv, dst.v + (3 * x + P) * 512, voff[x]);
+                for (int x = 0; x < NV; ++x) dma16(rv, dst.v + (Sh::NO * x + P) * 512, voff[x]);
             };
             // per-lane offsets of the wave's q rows within a chunk and of its output rows
             uint32_t qoff[NRB], ooff[NRB];
@@ -717,9 +720,10 @@ __global__ __launch_bounds__(320) void gdn_fwd_kernel(GdnArgs a) {
                 step(Ic<3>{}, ch + 3);
             }
         };
-        if (w == 1) run(Ic<0>{});
-        else if (w == 2) run(Ic<1>{});
-        else run(Ic<2>{});
+        if (w == 2) run(Ic<0>{});
+        else if (w == 3) run(Ic<1>{});
+        else if (w == 4) run(Ic<2>{});
+        else run(Ic<3>{});
     }
 }
 
