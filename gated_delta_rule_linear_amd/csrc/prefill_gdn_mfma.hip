@@ -22,19 +22,18 @@
 //
 // Two kernels:
 //   prep     one workgroup per (sequence, chunk), fully parallel: T = (I + L)^{-1} of
-//            every chunk, written to the workspace in bf16 and in MFMA fragment order
-//            (T depends only on the chunk's k, alpha, beta, never on the state);
+//            every chunk, written to the workspace as T diag(beta) in bf16 and in MFMA
+//            fragment order (T depends only on the chunk's k, alpha, beta, never on the
+//            state; with beta folded in, U = (T diag(beta)) (V - gamma K S));
 //   forward  one workgroup per (sequence, value tile of 16 or 32 columns): chain waves
 //            that each carry 16 columns of the fp32 state through the chunks in
 //            registers (columns of S never mix, so a chain needs no other wave's
-//            results), and two output waves one chunk behind that form the causal
-//            score tiles P_rs = exp(c_r - c_s) q_r.k_s (s <= r) and the outputs
+//            results), and output waves one chunk behind that form the causal score
+//            tiles P_rs = exp(c_r - c_s) q_r.k_s (s <= r) and the outputs
 //            O = gamma (S^T q) + P U from the copies of S and U the chains leave in LDS.
 //            One barrier per chunk; the tiles of one sequence share an XCD so their
 //            q / k / T reads hit the same L2.
 //
-// Fragments whose K index runs along tile rows use the LDS transpose read; result
-// tiles are written to LDS with 8-byte stores.
 #include <type_traits>
 
 #include "la_internal.h"
@@ -231,19 +230,29 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
         store_dT(sm.t, PC, 16 * jb, 32 + 16 * rb, -d, lane);
     }
     lds_barrier();
-    // T in fragment order with the column slots of a pair of matrix-core result tiles:
-    // 16-byte piece (rb, kk, lane = 16 g + j) holds row 16 rb + j, columns 32 kk + 4 g ..
-    // + 3 then 32 kk + 16 + 4 g .. + 3, so that a forward wave reads its A fragment as one
-    // contiguous kilobyte and multiplies it with a B fragment packed straight from two of
-    // its own result tiles
+    // T diag(beta) (so that the forward forms U = (T diag(beta)) (V - gamma K S) without
+    // scaling by beta itself), in fragment order with the column slots of a pair of
+    // matrix-core result tiles: 16-byte piece (rb, kk, lane = 16 g + j) holds row 16 rb + j,
+    // columns 32 kk + 4 g .. + 3 then 32 kk + 16 + 4 g .. + 3, so that a forward wave reads
+    // its A fragment as one contiguous kilobyte and multiplies it with a B fragment packed
+    // straight from two of its own result tiles
     uint16_t* Tg = a.T + (seq * a.nchunks + ch) * size_t(C * C);
 #pragma unroll
     for (int x2 = 0; x2 < 2; ++x2) {
         const int x = tid + NT * x2, rb = x >> 7, kk = (x >> 6) & 1, l = x & 63;
-        const int off = (16 * rb + (l & 15)) * PC + 32 * kk + 4 * (l >> 4);
-        const uint2 lo = *reinterpret_cast<const uint2*>(sm.t + off);
-        const uint2 hi = *reinterpret_cast<const uint2*>(sm.t + off + 16);
-        *reinterpret_cast<uint4*>(Tg + 8 * x) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        const int c = 32 * kk + 4 * (l >> 4);
+        const int off = (16 * rb + (l & 15)) * PC + c;
+        uint32_t wv[4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const uint2 t2 = *reinterpret_cast<const uint2*>(sm.t + off + 16 * hh);
+            const float4 b4 = *reinterpret_cast<const float4*>(sm.beta + c + 16 * hh);
+            wv[2 * hh] = pack_bf16x2(__uint_as_float(t2.x << 16) * b4.x,
+                                     __uint_as_float(t2.x & 0xffff0000u) * b4.y);
+            wv[2 * hh + 1] = pack_bf16x2(__uint_as_float(t2.y << 16) * b4.z,
+                                         __uint_as_float(t2.y & 0xffff0000u) * b4.w);
+        }
+        *reinterpret_cast<uint4*>(Tg + 8 * x) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     }
 }
 
@@ -261,8 +270,8 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
 // needs nothing from the other waves but the chunk's staged operands. For chunk c:
 //   S^T (bf16, the state entering the chunk) -> LDS, for the output waves
 //   KS = K S                       (A: rows of K)
-//   X = beta (V - gamma KS)        (V read in the result-tile layout)
-//   U = T X                        (A: T in the order the prep stored it)
+//   X = V - gamma KS               (V read in the result-tile layout)
+//   U = T diag(beta) X             (A: T diag(beta) as the prep stored it)
 //   U^T (bf16) -> LDS, for the output waves
 //   S <- gamma_last S + K^T (d U),  d_r = exp(c_last - c_r)   (A: K^T by transpose reads)
 // The state's key rows are kept in a permuted order: row 4 g + e of tiles 2 kk and 2 kk + 1
@@ -334,7 +343,7 @@ struct FwdShape {
     // gates for wave 0 (its stores come after them, so waiting for all but this many is
     // at least as strict as needed)
     static constexpr int vm_out(int p) {
-        return share(KBLK, p) + share(TBLK, p) + share(VBLK, p) + 4 + (p == 0 ? 2 : 0);
+        return share(KBLK, p) + share(TBLK, p) + share(VBLK, p) + 4 + (p == 0 ? 1 : 0);
     }
     // two iterations of loads in flight stay within the 6-bit vector-memory counter
     static_assert(2 * vm_out(0) <= 63, "vmcnt range");
@@ -364,8 +373,8 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
     __shared__ __align__(16) uint16_t st0[NCB * 4 * 512], st1[NCB * 4 * 512];
     __shared__ __align__(16) uint16_t ut0[NCB * 2 * 512], ut1[NCB * 2 * 512];
     // per-chunk gate factors (slot = chunk mod 4): cumulative log gate c_r, gamma_r =
-    // exp(c_r), d_r = exp(c_last - c_r), beta_r (zero on padding rows)
-    __shared__ __align__(16) float gsl[4][4][C];
+    // exp(c_r), d_r = exp(c_last - c_r)
+    __shared__ __align__(16) float gsl[4][3][C];
     auto slot_ = [&](auto I) -> ChunkSmem<VT>& {
         constexpr int s = decltype(I)::value & 3;
         if constexpr (s == 0) return sl0; else if constexpr (s == 1) return sl1;
@@ -451,19 +460,18 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
 #pragma unroll
             for (int x = 0; x < 6; ++x)
                 tf[x] = *reinterpret_cast<const bf16x8_t*>(tc + (pc[x] * 64 + lane) * 8);
-            // X = beta (V - gamma KS)
+            // X = V - gamma KS (beta is folded into T)
             f32x4_t X[4];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
                 const uint16_t* p = vc + (16 * tb + 4 * g + (jl >> 2)) * VT + 16 * cb + 4 * (jl & 3);
                 const i16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
                 const float4 g4 = *reinterpret_cast<const float4*>(&gc[1][16 * tb + 4 * g]);
-                const float4 b4 = *reinterpret_cast<const float4*>(&gc[3][16 * tb + 4 * g]);
-                const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
+                const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float v = __uint_as_float(uint32_t(uint16_t(x[e])) << 16);
-                    X[tb][e] = bv[e] * (v - gv[e] * ks[tb][e]);
+                    X[tb][e] = v - gv[e] * ks[tb][e];
                 }
             }
             const bf16x8_t Xb0 = pack_pk(X[0], X[1]), Xb1 = pack_pk(X[2], X[3]);
@@ -534,7 +542,7 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
                              rows_left(ch) * GS);
         };
         const uint32_t goff = uint32_t(lane) * GS;   // lane = token
-        struct Gate { uint32_t ga, gb; };
+        struct Gate { uint32_t ga; };
         auto run = [&](auto pc) {
             constexpr int P = decltype(pc)::value;
             constexpr int NRB = 1;
@@ -593,10 +601,7 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) Q.q[h][kk] = buf_ld16_off(r, qoff[h], 64 * kk);
             };
-            auto load_g = [&](Gate& G, int ch) {
-                G.ga = buf_ld_gate_off<GB>(gate_rsrc(a.alpha, ch), goff);
-                G.gb = buf_ld_gate_off<GB>(gate_rsrc(a.beta, ch), goff);
-            };
+            auto load_g = [&](Gate& G, int ch) { G.ga = buf_ld_gate_off<GB>(gate_rsrc(a.alpha, ch), goff); };
             // gate factors of chunk ch (lane = token; padding rows are identity steps)
             auto gates = [&](const Gate& G, int ch, float (*dst)[C]) {
                 const int n = min(C, sp.len - ch * C);
@@ -606,7 +611,6 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
                 dst[0][lane] = cum;
                 dst[1][lane] = fast_exp(cum);
                 dst[2][lane] = fast_exp(clast - cum);
-                dst[3][lane] = lane < n ? gate_val<GB>(G.gb) : 0.f;
             };
             // the wave's row blocks of chunk cp: scores, then outputs
             auto rows = [&](const QSet& Qp, const rsrc_t& orc, const uint16_t* kc,
