@@ -328,6 +328,19 @@ def bench_decode(name, steps, warmup, torch, bd, W, device, stream, check_heads=
            "algorithmic_bytes": byts, "timed_calls": steps,
            "finite": bool(torch.isfinite(S).all().item())}
     rec.update(summarize(per))
+    # the ceiling beside it: the plain in-place pass over the same state bytes
+    # (la_stream_rmw, x <- 1 x), timed the same way
+    sbytes = S.numel() * S.element_size()
+
+    def rmw(i):
+        rc = lib.la_stream_rmw(ctypes.c_void_p(S.data_ptr()), S.numel(), ctypes.c_float(1.0), sh)
+        if rc != 0:
+            raise bd.LinAttnError(rc, "la_stream_rmw")
+
+    ms_c, per_c = time_calls(rmw, steps, warmup, torch, stream)
+    rec["ceiling"] = {"kernel": "la_stream_rmw", "bytes": 2 * sbytes, "us_per_step": ms_c * 1e3,
+                      "GB_per_s": 2 * sbytes / (ms_c / 1e3) / 1e9,
+                      "step_over_ceiling": ms / ms_c, "us_median": summarize(per_c)["ms_median"] * 1e3}
     # the check step: token set j from the current states of the first check_heads heads
     nh = wl.B * wl.H
     hc = min(check_heads, nh)

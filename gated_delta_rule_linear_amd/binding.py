@@ -22,7 +22,7 @@ VARIANTS = {"kath": LA_KATH, "gla": LA_GLA, "gdn": LA_GDN, "kda": LA_KDA, "ssd":
 PATHS = {"auto": LA_PATH_AUTO, "valu": LA_PATH_VALU, "mfma": LA_PATH_MFMA}
 EXPORTS = ("la_prefill", "la_prefill_workspace_size", "la_prefill_noalloc", "la_prefill_varlen",
            "la_prefill_varlen_workspace_size", "la_decode_step", "la_prefill_backward",
-           "la_prefill_backward_workspace_size", "la_selective_scan",
+           "la_prefill_backward_workspace_size", "la_selective_scan", "la_stream_rmw",
            "la_status_str", "la_abi_version")
 
 
@@ -84,6 +84,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.la_selective_scan.argtypes = [ctypes.POINTER(ScanDesc), vp, vp, vp, vp, vp, vp, vp, vp,
                                       vp, vp, vp]
     lib.la_selective_scan.restype = ctypes.c_int
+    lib.la_stream_rmw.argtypes = [vp, ctypes.c_uint64, ctypes.c_float, vp]
+    lib.la_stream_rmw.restype = ctypes.c_int
     lib.la_status_str.argtypes = [ctypes.c_int]
     lib.la_status_str.restype = ctypes.c_char_p
     lib.la_abi_version.argtypes = []

@@ -19,6 +19,9 @@
 //   SSD  r = S^T q;  S <- a S + k v^T;  o = a r + (q . k) v
 // ("Linear / RNN 路线", sections 2.1, 2.2, 3.6 and 4.1; "线性注意力与 SSM", section GDN;
 // "状态空间与线性注意力", section KDA.)
+#include <algorithm>
+#include <atomic>
+
 #include "common.hpp"
 #include "la_internal.h"
 
@@ -202,11 +205,210 @@ __global__ __launch_bounds__(decode_threads(DK, DV, decode_nthreads<VAR, DV>()))
     if (rg == 0) store4(a.o, seq * DV + size_t(cg) * 4, o4, iob);
 }
 
+// Persistent form: a grid of a few workgroups per compute unit walks the states
+// (blockIdx.x, + gridDim.x, ...). Each iteration first issues the loads of the next state
+// it will take (into a second register set) and of that state's q, k, v and gates, then
+// reduces, updates and stores the current one, so the HBM reads of one state overlap the
+// reductions, barriers and writes of the previous. LDS is double-buffered by iteration
+// parity; the two barriers of an iteration separate every write of a buffer from the
+// reads of the iteration that last used it.
+template <int VAR, int DK, int DV, int NTH, bool IOB, bool GB, int MAXIT>
+__global__ __launch_bounds__(decode_threads(DK, DV, NTH)) void decode_persist_kernel(DecodeArgs a, int nseq) {
+    using Sh = DecodeShape<DK, DV, NTH>;
+    constexpr int NCG = Sh::NCG, RG = Sh::RG, RPT = Sh::RPT, NT = Sh::NT;
+    static_assert(DK <= NT && DV <= NT, "one small element per thread");
+    const int tid = threadIdx.x;
+    const int cg = tid % NCG, rg = tid / NCG;
+    // storage types are template arguments: a run-time choice would put branches between
+    // the loads, and the waits after them could no longer count the loads in flight
+    constexpr bool iob = IOB, gb = GB;
+
+    __shared__ float sq[2][DK], sk[2][DK], sw[2][DK];   // sw: the gate per key dim (GLA, KDA)
+    __shared__ float sv[2][DV];
+    __shared__ float4 red[2][2][RG][NCG];
+    __shared__ float scal[2][4];
+
+    // The small per-token inputs are loaded as raw bits and converted only where they are
+    // used, so that no wait for them (and hence for the state loads issued before them)
+    // lands in the middle of the iteration.
+    struct Small { uint32_t q, k, w, v, ga, be; };
+    auto raw = [](const void* p, size_t i, bool bf16) -> uint32_t {
+        if (bf16) return uint32_t(static_cast<const uint16_t*>(p)[i]);
+        return static_cast<const uint32_t*>(p)[i];
+    };
+    auto val = [](uint32_t r, bool bf16) { return __uint_as_float(bf16 ? r << 16 : r); };
+    // every thread issues the same loads (indices wrapped), so the number of loads in
+    // flight is the same on every path and the waits stay exact
+    auto load_small = [&](size_t seq, Small& m) {
+        m.q = raw(a.q, seq * DK + tid % DK, iob);
+        m.k = raw(a.k, seq * DK + tid % DK, iob);
+        if (has_channel_gate<VAR>()) m.w = raw(a.g, seq * DK + tid % DK, gb);
+        m.v = raw(a.v, seq * DV + tid % DV, iob);
+        if (VAR == LA_GDN || VAR == LA_SSD) m.ga = raw(a.g, seq, gb);
+        if (has_delta<VAR>()) m.be = raw(a.beta, seq, gb);
+    };
+    auto load_state = [&](size_t seq, float4 (&s)[RPT]) {
+        const float* S = a.S + seq * (size_t(DK) * DV);
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) s[r] = load_nt4(S + size_t(rg + RG * r) * DV + cg * 4);
+    };
+
+    // One state: t, with its state in cur and inputs in mc; the next state's loads go to
+    // nxt and mn. Returns false after the last state of this workgroup.
+    auto step = [&](int& t, float4 (&cur)[RPT], float4 (&nxt)[RPT], const Small& mc, Small& mn,
+                    int par) -> bool {
+        const size_t seq = size_t(t);
+        const int tn = t + int(gridDim.x);
+        if (tn < nseq) {
+            load_state(size_t(tn), nxt);
+            load_small(size_t(tn), mn);
+        }
+        // stage this state's vectors
+        if (tid < DK) {
+            float qi = val(mc.q, iob), ki = val(mc.k, iob);
+            if (VAR == LA_KATH) {
+                qi = elu_plus_one(qi);
+                ki = elu_plus_one(ki);
+            }
+            sq[par][tid] = qi;
+            sk[par][tid] = ki;
+            if (has_channel_gate<VAR>()) sw[par][tid] = val(mc.w, gb);
+        }
+        if (tid < DV) sv[par][tid] = val(mc.v, iob);
+        __syncthreads();
+        // wave 0: the scalar dot products
+        if (tid < kWave) {
+            float qk = 0.f, qz = 0.f;
+            for (int i = tid; i < DK; i += kWave) {
+                qk += sq[par][i] * sk[par][i];
+                if (VAR == LA_KATH) qz += sq[par][i] * (a.z[seq * DK + i] + sk[par][i]);
+            }
+            qk = wave_sum(qk);
+            if (VAR == LA_KATH) qz = wave_sum(qz);
+            if (tid == 0) {
+                scal[par][0] = qk;
+                scal[par][1] = qz + a.eps;
+                if (VAR == LA_GDN || VAR == LA_SSD) scal[par][2] = val(mc.ga, gb);
+                if (has_delta<VAR>()) scal[par][3] = val(mc.be, gb);
+            }
+        }
+        // partial reductions of the old state over this thread's rows
+        float4 pr = make_float4(0.f, 0.f, 0.f, 0.f), rr = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int i = rg + RG * r;
+            float wq = sq[par][i];
+            if (has_channel_gate<VAR>()) wq *= sw[par][i];
+            rr.x += cur[r].x * wq; rr.y += cur[r].y * wq; rr.z += cur[r].z * wq; rr.w += cur[r].w * wq;
+            if (has_delta<VAR>()) {
+                const float ki = VAR == LA_KDA ? sk[par][i] * sw[par][i] : sk[par][i];
+                pr.x += cur[r].x * ki; pr.y += cur[r].y * ki; pr.z += cur[r].z * ki; pr.w += cur[r].w * ki;
+            }
+        }
+        red[par][0][rg][cg] = rr;
+        if (has_delta<VAR>()) red[par][1][rg][cg] = pr;
+        __syncthreads();
+        float4 R = make_float4(0.f, 0.f, 0.f, 0.f), P = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+        for (int x = 0; x < RG; ++x) {
+            const float4 t1 = red[par][0][x][cg];
+            R.x += t1.x; R.y += t1.y; R.z += t1.z; R.w += t1.w;
+            if (has_delta<VAR>()) {
+                const float4 t2 = red[par][1][x][cg];
+                P.x += t2.x; P.y += t2.y; P.z += t2.z; P.w += t2.w;
+            }
+        }
+        float* S = a.S + seq * (size_t(DK) * DV);
+        const float qk = scal[par][0];
+        const float4 v4 = make_float4(sv[par][cg * 4], sv[par][cg * 4 + 1], sv[par][cg * 4 + 2], sv[par][cg * 4 + 3]);
+        float4 o4;
+        if (has_delta<VAR>()) {
+            // GDN: u = beta (v - alpha p), S <- alpha S + k u^T, o = alpha r + (k.q) u;
+            // KDA: u = beta (v - p), S <- Diag(a) S + k u^T, o = r + (k.q) u
+            const float al = VAR == LA_GDN ? scal[par][2] : 1.f, be = scal[par][3];
+            float4 u;
+            u.x = be * (v4.x - al * P.x); u.y = be * (v4.y - al * P.y);
+            u.z = be * (v4.z - al * P.z); u.w = be * (v4.w - al * P.w);
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                const int i = rg + RG * r;
+                const float ki = sk[par][i], ai = VAR == LA_KDA ? sw[par][i] : al;
+                float4 n;
+                n.x = ai * cur[r].x + ki * u.x; n.y = ai * cur[r].y + ki * u.y;
+                n.z = ai * cur[r].z + ki * u.z; n.w = ai * cur[r].w + ki * u.w;
+                store_nt4(S + size_t(i) * DV + cg * 4, n);
+            }
+            o4.x = al * R.x + qk * u.x; o4.y = al * R.y + qk * u.y;
+            o4.z = al * R.z + qk * u.z; o4.w = al * R.w + qk * u.w;
+        } else {
+            const float as = VAR == LA_SSD ? scal[par][2] : 1.f;   // SSD: the token's decay
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                const int i = rg + RG * r;
+                const float ki = sk[par][i];
+                const float gi = VAR == LA_GLA ? sw[par][i] : as;
+                float4 n;
+                n.x = gi * cur[r].x + ki * v4.x; n.y = gi * cur[r].y + ki * v4.y;
+                n.z = gi * cur[r].z + ki * v4.z; n.w = gi * cur[r].w + ki * v4.w;
+                store_nt4(S + size_t(i) * DV + cg * 4, n);
+            }
+            o4.x = as * R.x + qk * v4.x; o4.y = as * R.y + qk * v4.y;
+            o4.z = as * R.z + qk * v4.z; o4.w = as * R.w + qk * v4.w;
+            if (VAR == LA_KATH) {
+                const float inv = 1.f / scal[par][1];
+                o4.x *= inv; o4.y *= inv; o4.z *= inv; o4.w *= inv;
+            }
+        }
+        if (VAR == LA_KATH) {
+            // z is read by wave 0 above; every thread is past the reduction barrier,
+            // so the old values have been consumed before any write below.
+            if (tid < DK) a.z[seq * DK + tid] += sk[par][tid];
+        }
+        if (rg == 0) store4(a.o, seq * DV + size_t(cg) * 4, o4, iob);
+        t = tn;
+        return tn < nseq;
+    };
+
+    int t = blockIdx.x;
+    if (t >= nseq) return;
+    float4 sa[RPT], sb[RPT];
+    Small ma{}, mb{};
+    load_state(size_t(t), sa);
+    load_small(size_t(t), ma);
+    // at most MAXIT states per workgroup, fully unrolled: two register sets swapped by
+    // unrolling rather than copied (a copy would wait for the loads in flight), and
+    // straight-line code, in which the waits count exactly which loads are in flight
+#pragma unroll
+    for (int it = 0; it < MAXIT; it += 2) {
+        if (!step(t, sa, sb, ma, mb, 0)) break;
+        if (it + 1 >= MAXIT || !step(t, sb, sa, mb, ma, 1)) break;
+    }
+}
+
+// The persistent form for bf16 token inputs and gates with d_k = 128 (the large states):
+// threads per workgroup and states per workgroup as measured best for an in-place step of
+// 8,192 states on MI355X (GLA and SSD at d_v = 128: 1024 threads, up to 16 states; the
+// others: 512 threads, up to 8), at least two workgroups per compute unit.
+template <int VAR, int DV>
+constexpr int persist_threads() { return (VAR == LA_GLA || VAR == LA_SSD) && DV >= 128 ? 1024 : 512; }
+template <int VAR, int DV>
+constexpr int persist_states() { return persist_threads<VAR, DV>() == 1024 ? 16 : 8; }
+
 template <int VAR, int DK, int DV>
 hipError_t launch_one(const Problem& p, const DecodeArgs& a) {
-    const unsigned nseq = unsigned(size_t(p.B) * size_t(p.H));
+    const size_t nseq = size_t(p.B) * size_t(p.H);
+    if constexpr (DK == 128 && DV >= 64) {
+        if (p.io_bf16 && p.gate_bf16) {
+            constexpr int NTH = persist_threads<VAR, DV>(), MAXIT = persist_states<VAR, DV>();
+            const size_t need = (nseq + MAXIT - 1) / MAXIT;
+            const size_t grid = std::min(nseq, std::max(size_t(device_cus()) * 2, need));
+            decode_persist_kernel<VAR, DK, DV, NTH, true, true, MAXIT>
+                <<<dim3(unsigned(grid)), dim3(DecodeShape<DK, DV, NTH>::NT), 0, p.stream>>>(a, int(nseq));
+            return hipGetLastError();
+        }
+    }
     decode_kernel<VAR, DK, DV>
-        <<<dim3(nseq), dim3(DecodeShape<DK, DV, decode_nthreads<VAR, DV>()>::NT), 0, p.stream>>>(a);
+        <<<dim3(unsigned(nseq)), dim3(DecodeShape<DK, DV, decode_nthreads<VAR, DV>()>::NT), 0, p.stream>>>(a);
     return hipGetLastError();
 }
 
@@ -234,8 +436,27 @@ hipError_t dispatch_dk(const Problem& p, const DecodeArgs& a) {
 
 }  // namespace
 
+// compute units of the current device (queried once per device; 256 if the query fails)
+int device_cus() {
+    static std::atomic<int> cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 hipError_t launch_decode(const Problem& p) {
-    if (size_t(p.B) * size_t(p.H) > 0x7fffffffull) return hipErrorInvalidValue;
+    if (size_t(p.B) * size_t(p.H) > 0x7fffffffull) return hipErrorInvalidValue;   // fits int
     DecodeArgs a{p.q, p.k, p.v, p.g, p.beta, p.S, p.z, p.o, p.eps, p.io_bf16, p.gate_bf16};
     switch (p.variant) {
         case LA_KATH: return dispatch_dk<LA_KATH>(p, a);

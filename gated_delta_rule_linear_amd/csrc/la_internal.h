@@ -40,6 +40,8 @@ constexpr int kMfmaChunk = 64;
 
 // decode.hip
 hipError_t launch_decode(const Problem& p);
+// compute units of the current device (queried once per device)
+int device_cus();
 // prefill_valu.hip
 hipError_t launch_prefill_valu(const Problem& p);
 // state_init.hip: S_final <- S0 (or 0), z_final <- z0 (or 0), for N = 0

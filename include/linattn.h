@@ -270,6 +270,17 @@ int la_selective_scan(const la_scan_desc* d, const void* dt, const float* A, con
                       const void* Cm, const void* x, const float* Dskip, const float* dt_bias,
                       const float* h0, void* y, float* h_final, void* stream);
 
+/* The in-place streaming ceiling of a decode step. Decode is a read-modify-write of the
+ * carried state and nothing else of size ("线性注意力与 SSM", sections 01 and 02: its cost
+ * follows the state's size), so the fastest plain in-place pass over the same bytes bounds
+ * it. This call makes that pass: x[i] <- a * x[i] for i < n, fp32, in place, every element
+ * read once and written once with 16-byte accesses (a grid of two workgroups per compute
+ * unit walks 16 KiB tiles, loading the next tile before storing the current one).
+ *   x   n floats of device memory owned by the caller, 16-byte aligned; n a multiple of 4.
+ * Only enqueues work on the stream. Errors: LA_ERR_INVALID (x NULL with n > 0, n not a
+ * multiple of 4, x misaligned), LA_ERR_HIP. n = 0 does nothing. */
+int la_stream_rmw(float* x, uint64_t n, float a, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* la_status_str(int status);
 

@@ -481,3 +481,15 @@ def test_backward_workspace_query(lib):
     assert n.value > 0
     d = good("gla", B=0)
     assert call_bwd(lib, d, **bwd_args()) == bd.LA_OK   # no sequences: nothing to do
+
+
+def test_stream_rmw_rejects(lib):
+    """la_stream_rmw validates before any HIP call: n = 0 is a no-op even with NULL; a NULL
+    buffer, n not a multiple of 4, or a misaligned buffer is LA_ERR_INVALID."""
+    buf = (ctypes.c_float * 16)()
+    base = ctypes.addressof(buf)
+    assert lib.la_stream_rmw(None, 0, ctypes.c_float(2.0), None) == bd.LA_OK
+    assert lib.la_stream_rmw(None, 4, ctypes.c_float(2.0), None) == bd.LA_ERR_INVALID
+    aligned = base + (-base) % 16
+    assert lib.la_stream_rmw(ctypes.c_void_p(aligned), 6, ctypes.c_float(2.0), None) == bd.LA_ERR_INVALID
+    assert lib.la_stream_rmw(ctypes.c_void_p(aligned + 4), 4, ctypes.c_float(2.0), None) == bd.LA_ERR_INVALID
