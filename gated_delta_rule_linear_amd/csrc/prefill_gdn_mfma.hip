@@ -90,28 +90,43 @@ __device__ __forceinline__ float scan64(float x, int) { return wave_inclusive_sc
 // ---------------------------------------------------------------------------
 // prep kernel: T = (I + L)^{-1} per chunk
 // ---------------------------------------------------------------------------
+// Persistent: a grid of a few workgroups per compute unit walks the (sequence, chunk)
+// units; each iteration issues the next unit's loads (K rows and the gates, through
+// per-chunk buffer resources that read zeros past the sequence's end) before it works on
+// the current one, so the load latency is hidden behind the previous chunk's work.
 template <bool GB>
-__global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
+__global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a, int nunits) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int g = lane >> 4, jl = lane & 15;
-    const size_t seq = blockIdx.x / a.nchunks;
-    const int ch = blockIdx.x % a.nchunks;
+    constexpr uint32_t GS = GB ? 2u : 4u;
+    struct In { uint4 kv[4]; uint32_t graw; };
+    // waves 0 and 1 load the gates alpha and beta, the others alpha again (unused), so
+    // that every thread issues the same loads
+    auto load = [&](int u, In& in) {
+        const int seq = u / a.nchunks, ch = u % a.nchunks;
+        const SeqSpan sp = seq_span(seq, a.H, a.N, a.L, a.cu);
+        const int t0 = ch * C;
+        const uint32_t rows_left = uint32_t(max(0, sp.len - t0));
+        const rsrc_t rk = make_rsrc(a.k + (sp.base + t0) * DK, rows_left * DK * 2u);
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4) {
+            const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
+            in.kv[x4] = buf_ld16_off(rk, uint32_t(r * DK + col) * 2u, 0);
+        }
+        const void* gp = w == 1 ? a.beta : a.alpha;
+        const rsrc_t rg = make_rsrc(static_cast<const char*>(gp) + (sp.base + t0) * GS, rows_left * GS);
+        in.graw = buf_ld_gate_off<GB>(rg, uint32_t(lane) * GS);
+    };
+    auto chunk = [&](int u, const In& in) {
+    const size_t seq = size_t(u / a.nchunks);
+    const int ch = u % a.nchunks;
     const SeqSpan sp = seq_span(int(seq), a.H, a.N, a.L, a.cu);
     const int t0 = ch * C, n = min(C, sp.len - t0);
-    const size_t tok0 = sp.base;
     if (n <= 0) return;   // past this sequence's end: the forward reads zeros instead
-
-    // loads from clamped rows (always valid), padding applied when staging
-    uint4 kv[4];
-#pragma unroll
-    for (int x4 = 0; x4 < 4; ++x4) {
-        const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
-        kv[x4] = ld_g16(a.k + (tok0 + t0 + min(r, n - 1)) * DK + col);
-    }
-    uint32_t graw = 0;
-    if (w < 2) graw = ld_gate_raw<GB>(w == 0 ? a.alpha : a.beta, tok0 + t0 + min(lane, n - 1));
+    const uint4* kv = in.kv;
+    const uint32_t graw = in.graw;
 #pragma unroll
     for (int x4 = 0; x4 < 4; ++x4) {
         const int x = tid + NT * x4, r = x >> 4, col = (x & 15) * 8;
@@ -253,6 +268,23 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a) {
                                          __uint_as_float(t2.y & 0xffff0000u) * b4.w);
         }
         *reinterpret_cast<uint4*>(Tg + 8 * x) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+    };
+
+    int u = blockIdx.x;
+    if (u >= nunits) return;
+    In cur, nxt;
+    load(u, cur);
+    for (;;) {
+        const int un = u + int(gridDim.x);
+        // the next unit's loads stay in flight through this unit's work; the copy below
+        // waits for them
+        if (un < nunits) load(un, nxt);
+        chunk(u, cur);
+        lds_barrier();   // every wave is done with this unit's LDS before the next writes it
+        if (un >= nunits) break;
+        cur = nxt;
+        u = un;
     }
 }
 
@@ -763,9 +795,11 @@ hipError_t launch_cfg(const Problem& p) {
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gdn_prep_kernel<GB>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
         if (e != hipSuccess) return e;
-        const size_t blocks = size_t(a.nseq) * size_t(a.nchunks);
-        if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
-        gdn_prep_kernel<GB><<<dim3(unsigned(blocks)), dim3(NT), smem, p.stream>>>(a);
+        const size_t units = size_t(a.nseq) * size_t(a.nchunks);
+        if (units > 0x7fffffffull) return hipErrorInvalidValue;
+        // three workgroups fit a compute unit's LDS
+        const size_t grid = std::min(units, size_t(device_cus()) * 3);
+        gdn_prep_kernel<GB><<<dim3(unsigned(grid)), dim3(NT), smem, p.stream>>>(a, int(units));
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     gdn_fwd_kernel<NCB, GB>
