@@ -101,12 +101,17 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a, int nunits) {
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int g = lane >> 4, jl = lane & 15;
     constexpr uint32_t GS = GB ? 2u : 4u;
-    struct In { uint4 kv[4]; uint32_t graw; };
+    // a unit's loads, and its sequence span (found once, when its loads are issued: with a
+    // packed batch that reads the sequence bounds, and a wait for them must not fall
+    // after the next unit's loads)
+    struct In { uint4 kv[4]; uint32_t graw; size_t base; int len; };
     // waves 0 and 1 load the gates alpha and beta, the others alpha again (unused), so
     // that every thread issues the same loads
     auto load = [&](int u, In& in) {
         const int seq = u / a.nchunks, ch = u % a.nchunks;
         const SeqSpan sp = seq_span(seq, a.H, a.N, a.L, a.cu);
+        in.base = sp.base;
+        in.len = sp.len;
         const int t0 = ch * C;
         const uint32_t rows_left = uint32_t(max(0, sp.len - t0));
         const rsrc_t rk = make_rsrc(a.k + (sp.base + t0) * DK, rows_left * DK * 2u);
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a, int nunits) {
     auto chunk = [&](int u, const In& in) {
     const size_t seq = size_t(u / a.nchunks);
     const int ch = u % a.nchunks;
-    const SeqSpan sp = seq_span(int(seq), a.H, a.N, a.L, a.cu);
+    const SeqSpan sp{in.base, in.len};
     const int t0 = ch * C, n = min(C, sp.len - t0);
     if (n <= 0) return;   // past this sequence's end: the forward reads zeros instead
     const uint4* kv = in.kv;
@@ -271,20 +276,22 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a, int nunits) {
     }
     };
 
-    int u = blockIdx.x;
-    if (u >= nunits) return;
-    In cur, nxt;
-    load(u, cur);
-    for (;;) {
+    // two input sets, swapped by unrolling rather than copied (a copy would wait for the
+    // loads in flight): each step issues the next unit's loads into the other set, then
+    // works on its own
+    auto step = [&](int& u, const In& cur, In& nxt) -> bool {
         const int un = u + int(gridDim.x);
-        // the next unit's loads stay in flight through this unit's work; the copy below
-        // waits for them
         if (un < nunits) load(un, nxt);
         chunk(u, cur);
         lds_barrier();   // every wave is done with this unit's LDS before the next writes it
-        if (un >= nunits) break;
-        cur = nxt;
         u = un;
+        return un < nunits;
+    };
+    int u = blockIdx.x;
+    if (u >= nunits) return;
+    In ia, ib;
+    load(u, ia);
+    while (step(u, ia, ib) && step(u, ib, ia)) {
     }
 }
 
