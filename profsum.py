@@ -40,10 +40,10 @@ STEP_KERNELS = {
     "kath_f32_n256_d16": [r"prefill_valu_kernel<0,"],
     "selscan_bf16_b2_t4096_d2048_n128": [r"selective_scan_kernel<128,"],
     "selscan_bf16_b2_t4096_d2048_n16": [r"selective_scan_kernel<16,"],
-    "decode_gdn_256x32_d128": [r"decode_kernel<2,"],
-    "decode_gla_256x32_d128": [r"decode_kernel<1,"],
-    "decode_kda_256x32_d128": [r"decode_kernel<3,"],
-    "decode_ssd_256x64_dk128_dv64": [r"decode_kernel<4,"],
+    "decode_gdn_256x32_d128": [r"decode_(persist_)?kernel<2,"],
+    "decode_gla_256x32_d128": [r"decode_(persist_)?kernel<1,"],
+    "decode_kda_256x32_d128": [r"decode_(persist_)?kernel<3,"],
+    "decode_ssd_256x64_dk128_dv64": [r"decode_(persist_)?kernel<4,"],
 }
 COPY_BYTES = 512 << 20
 
