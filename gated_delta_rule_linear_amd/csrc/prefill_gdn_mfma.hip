@@ -50,6 +50,12 @@ constexpr int PQ = DK + 16;    // pitch (elements) of [*][128] bf16 tiles (72 dw
 constexpr int PC = C + 8;      // pitch of [*][64] bf16 tiles
 constexpr int PD = 16 + 4;     // pitch of the fp32 16 x 16 diagonal L blocks
 constexpr int PY = 32 + 8;     // pitch of the bf16 32-row scratch tiles
+// T in fragment order is eight 1 KiB pieces 2 rb + kk; pieces 1 and 3 (row blocks 0 and 1,
+// tokens 32..63) are zero since T is lower triangular, so the workspace holds the other
+// six: stored piece i is fragment piece t_piece(i).
+constexpr int TPC = 6;
+constexpr int TCH = TPC * 512;  // bf16 elements of T per chunk in the workspace
+__host__ __device__ constexpr int t_piece(int i) { return i < 2 ? 2 * i : i + 2; }
 
 struct __align__(16) PrepSmem {
     __align__(16) uint16_t k[C * PQ];
@@ -67,7 +73,7 @@ struct GdnArgs {
     const float* S0;
     uint16_t* o;
     float* S;
-    uint16_t* T;   // workspace: [nseq][nchunks][64][64] bf16, T per chunk
+    uint16_t* T;   // workspace: [nseq][nchunks][TCH] bf16, T diag(beta) per chunk (six pieces)
     int N, nseq, ntiles, nchunks, gate_bf16;
     const int32_t* cu;   // packed variable-length batch, or null
     int H, L;            // heads; longest sequence (chunk counts are sized for it)
@@ -251,15 +257,17 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a, int nunits) {
     }
     lds_barrier();
     // T diag(beta) (so that the forward forms U = (T diag(beta)) (V - gamma K S) without
-    // scaling by beta itself), in fragment order with the column slots of a pair of
+    // scaling by beta itself), its six nonzero pieces in fragment order with the column slots of a pair of
     // matrix-core result tiles: 16-byte piece (rb, kk, lane = 16 g + j) holds row 16 rb + j,
     // columns 32 kk + 4 g .. + 3 then 32 kk + 16 + 4 g .. + 3, so that a forward wave reads
     // its A fragment as one contiguous kilobyte and multiplies it with a B fragment packed
     // straight from two of its own result tiles
-    uint16_t* Tg = a.T + (seq * a.nchunks + ch) * size_t(C * C);
+    uint16_t* Tg = a.T + (seq * a.nchunks + ch) * size_t(TCH);
 #pragma unroll
     for (int x2 = 0; x2 < 2; ++x2) {
-        const int x = tid + NT * x2, rb = x >> 7, kk = (x >> 6) & 1, l = x & 63;
+        const int x = tid + NT * x2;
+        if (x >= TPC * 64) break;
+        const int pi = t_piece(x >> 6), rb = pi >> 1, kk = pi & 1, l = x & 63;
         const int c = 32 * kk + 4 * (l >> 4);
         const int off = (16 * rb + (l & 15)) * PC + c;
         uint32_t wv[4];
@@ -375,7 +383,7 @@ struct FwdShape {
     // blocks p, p + 4, ...: the padded K tile (64 rows of PQ / 8 16-byte pieces), T (8
     // blocks) and the value tile (64 rows of VT / 8 pieces).
     static constexpr int KBLK = C * (PQ / 8) / 64;
-    static constexpr int TBLK = 8;
+    static constexpr int TBLK = TPC;   // the stored pieces of T
     static constexpr int VBLK = C * (VT / 8) / 64;
     static constexpr int share(int nb, int p) { return (nb - p + NO - 1) / NO; }
     // vector-memory loads output wave p issues per iteration: copies, q rows, and the
@@ -602,7 +610,7 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
                 koff[x] = uint32_t(row * DK + (ck < DK / 8 ? ck : 0) * 8) * 2u;
             }
 #pragma unroll
-            for (int x = 0; x < NT_; ++x) toff[x] = uint32_t(Sh::NO * x + P) * 1024u + lane * 16u;
+            for (int x = 0; x < NT_; ++x) toff[x] = uint32_t(Sh::NO * x + P) * 1024u + lane * 16u;   // stored piece
 #pragma unroll
             for (int x = 0; x < NV; ++x) {
                 const int pz = 64 * (Sh::NO * x + P) + lane;
@@ -613,10 +621,10 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
                 const rsrc_t rk = make_rsrc(a.k + (tok0 + size_t(ch) * C) * DK, rows_left(ch) * DK * 2u);
 #pragma unroll
                 for (int x = 0; x < NK; ++x) dma16(rk, dst.k + (Sh::NO * x + P) * 512, koff[x]);
-                const rsrc_t rt = make_rsrc(a.T + (seq * size_t(a.nchunks) + size_t(ch)) * (C * C),
-                                            ch < nchunks ? C * C * 2u : 0u);
+                const rsrc_t rt = make_rsrc(a.T + (seq * size_t(a.nchunks) + size_t(ch)) * TCH,
+                                            ch < nchunks ? TCH * 2u : 0u);
 #pragma unroll
-                for (int x = 0; x < NT_; ++x) dma16(rt, dst.t + (Sh::NO * x + P) * 512, toff[x]);
+                for (int x = 0; x < NT_; ++x) dma16(rt, dst.t + t_piece(Sh::NO * x + P) * 512, toff[x]);
                 const rsrc_t rv = make_rsrc(a.v + (tok0 + size_t(ch) * C) * DV,
                                             rows_left(ch) * uint32_t(DV) * 2u);
 #pragma unroll
@@ -827,7 +835,7 @@ bool gdn_mfma_supported(int dk, int dv, bool io_bf16) {
 
 size_t gdn_mfma_workspace_bytes(const Problem& p) {
     const size_t nchunks = size_t((p.L + C - 1) / C);
-    return size_t(p.B) * size_t(p.H) * nchunks * C * C * sizeof(uint16_t);
+    return size_t(p.B) * size_t(p.H) * nchunks * TCH * sizeof(uint16_t);
 }
 
 hipError_t launch_prefill_gdn_mfma(const Problem& p) {
