@@ -55,7 +55,7 @@ STEP_KERNELS = {
     "kath": "kath_chain_kernel (summary) + kath_scan_kernel + kath_chain_kernel",
     "gdn": "gdn_prep_kernel + gdn_fwd_kernel",
     "kda": "kda_prep_kernel + kda_fwd_kernel",
-    "ssd": "ssd_prep_kernel + gla_chain_kernel (summary, forward; q read as given)",
+    "ssd": "ssd_chain_kernel (summary) + ssd_chain_kernel (forward; one pass over q, k, v, decays)",
 }
 
 

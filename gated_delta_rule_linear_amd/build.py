@@ -30,7 +30,8 @@ COMMON = [
 
 SOURCES = ["la_api.cpp", "decode.hip", "prefill_valu.hip", "prefill_kath_mfma.hip", "prefill_kda_mfma.hip",
            "selective_scan.hip", "backward_valu.hip", "backward_gdn_valu.hip", "backward_ssd_mfma.hip",
-           "prefill_gla_mfma.hip", "prefill_gdn_mfma.hip", "noalloc.hip", "stream_rmw.hip"]
+           "prefill_gla_mfma.hip", "prefill_gdn_mfma.hip", "noalloc.hip", "stream_rmw.hip",
+           "prefill_ssd_mfma.hip"]
 
 
 # per-file code generation options: matrix-core results kept in ordinary vector registers

@@ -141,7 +141,8 @@ size_t workspace_for(const Problem& p) {
     if (p.path == LA_PATH_MFMA)
         return p.variant == LA_GDN   ? la::gdn_mfma_workspace_bytes(p)
                : p.variant == LA_KDA ? la::kda_mfma_workspace_bytes(p)
-               : (p.variant == LA_GLA || p.variant == LA_SSD) ? la::gla_mfma_workspace_bytes(p)
+               : p.variant == LA_GLA ? la::gla_mfma_workspace_bytes(p)
+               : p.variant == LA_SSD ? la::ssd_mfma_workspace_bytes(p)
                                      : la::kath_mfma_workspace_bytes(p);
     return 0;
 }
@@ -273,7 +274,8 @@ int prefill_impl(const la_desc* d, int nseq, const int32_t* cu, int max_len, con
     else if (p.path == LA_PATH_MFMA)
         err = gdn                     ? la::launch_prefill_gdn_mfma(p)
               : kda                   ? la::launch_prefill_kda_mfma(p)
-              : (gla || ssd)          ? la::launch_prefill_gla_mfma(p)
+              : gla                   ? la::launch_prefill_gla_mfma(p)
+              : ssd                   ? la::launch_prefill_ssd_mfma(p)
                                     : la::launch_prefill_kath_mfma(p);
     else
         err = la::launch_prefill_valu(p);

@@ -60,6 +60,9 @@ bool gla_mfma_supported(int dk, int dv, bool io_bf16);
 size_t gla_mfma_workspace_bytes(const Problem& p);
 int gla_mfma_auto_segments(const Problem& p);
 hipError_t launch_prefill_gla_mfma(const Problem& p);
+// prefill_ssd_mfma.hip (SSD in one pass: d_k = 128, bf16 io; segments as for GLA)
+size_t ssd_mfma_workspace_bytes(const Problem& p);
+hipError_t launch_prefill_ssd_mfma(const Problem& p);
 // prefill_gdn_mfma.hip (GDN)
 bool gdn_mfma_supported(int dk, int dv, bool io_bf16);
 size_t gdn_mfma_workspace_bytes(const Problem& p);

@@ -32,8 +32,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 # kernels that make up one step of each workload (matched on the demangled name)
 STEP_KERNELS = {
-    "gla_bf16_b2h8_n2048_d128": [r"gla_prep_kernel<", r"gla_chain_kernel<(true|false), \d, false>"],
-    "ssd_bf16_b2h32_n4096_dk128_dv64": [r"ssd_prep_kernel<", r"gla_chain_kernel<(true|false), \d, true>"],
+    "gla_bf16_b2h8_n2048_d128": [r"gla_prep_kernel<", r"gla_chain_kernel<(true|false), \d>"],
+    "ssd_bf16_b2h32_n4096_dk128_dv64": [r"ssd_chain_kernel<"],
     "kath_bf16_b1h16_n32768_dk128_dv64": [r"kath_chain_kernel<", r"kath_scan_kernel"],
     "gdn_bf16_b4h16_n8192_d128": [r"gdn_prep_kernel<", r"gdn_fwd_kernel<"],
     "kda_bf16_b4h16_n8192_d128": [r"kda_prep_kernel<", r"kda_fwd_kernel<"],
