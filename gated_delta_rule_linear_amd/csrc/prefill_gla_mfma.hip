@@ -47,7 +47,9 @@ constexpr int PQ = DK + 8;     // pitch of [*][128] bf16 tiles
 
 // Workspace of one chunk, written by prep (bytes), each matrix in MFMA fragment order
 // so that a wave reads its fragment as one contiguous kilobyte: q^ (piece (rb, kk, lane =
-// 16 g + j) = row 16 rb + j, columns 32 kk + 8 g .. + 7), k^ transposed (piece (ib, kk,
+// 16 g + j) = row 16 rb + j, key columns 32 kk + 4 g .. + 3 then 32 kk + 16 + 4 g .. + 3:
+// the key order of the S^T fragments the forward packs straight from its state
+// registers), k^ transposed (piece (ib, kk,
 // lane) = key dim 16 ib + j, tokens 32 kk + 8 g .. + 7), P (piece (rb, kk, lane) = row
 // 16 rb + j, tokens 32 kk + 4 g .. + 3 then 32 kk + 16 + 4 g .. + 3: the order in which
 // the matrix cores return the tile, matched by the forward kernel's V fragment), then
@@ -232,10 +234,12 @@ __global__ __launch_bounds__(NTP) void gla_prep_kernel(GlaArgs a) {
                 *reinterpret_cast<uint32_t*>(sm.pc[pair_index(o, b)] + pr * PQ + col) =
                     pack_bf16x2(qt0 * fq[o][0], qt1 * fq[o][1]);
         }
-        // q^ in fragment order: row rr, columns col, col + 1 are a quarter piece
-        const int kk = col >> 5, gg = (col & 31) >> 3;
+        // q^ in fragment order: row rr, columns col, col + 1 are one slot pair of the
+        // piece of lane group gg (key kc = 4 gg + e or 16 + 4 gg + e goes to slot e or 4 + e)
+        const int kk = col >> 5, kc = col & 31, gg = (kc & 15) >> 2;
+        const int slot = (kc & 3) + (kc >= 16 ? 4 : 0);
         *reinterpret_cast<uint32_t*>(wsc + kWsQ + (((rr >> 4) * 4 + kk) * 64 + 16 * gg + pr) * 16 +
-                                     (col & 7) * 2) =
+                                     slot * 2) =
             pack_bf16x2(q0 * (pre[0] * pp[r][0]), q1 * (pre[1] * pp[r][1]));
         kh[r][0] = k0 * (ss[r][0] * suf[0]);
         kh[r][1] = k1 * (ss[r][1] * suf[1]);
@@ -288,12 +292,16 @@ __global__ __launch_bounds__(NTP) void gla_prep_kernel(GlaArgs a) {
 // ---------------------------------------------------------------------------
 // summary (OUT = false) and forward (OUT = true): the chunk walk of one segment
 // ---------------------------------------------------------------------------
+// S^T is kept in fragment order: piece (kk, ct, lane = 16 g + L) holds column
+// colmap(ct, L) of the tile and key rows 32 kk + 4 g .. + 3, 32 kk + 16 + 4 g .. + 3, which
+// is what lane (g, L) of wave kk holds in its two state tiles, so each lane writes one
+// contiguous 16-byte piece and each reader loads one.
 template <int VT>
 struct __align__(16) ChainSmem {
     static constexpr int PV = VT + 8;
-    __align__(16) uint16_t v[2][C * PV];    // V [s][c]
-    __align__(16) uint16_t st[2][VT * PQ];  // S^T [c][i], bf16 (forward only)
-    __align__(16) float a[2][DK];           // chunk decay exp(B_last)
+    __align__(16) uint16_t v[2][C * PV];          // V [s][c]
+    __align__(16) uint4 st[2][4 * (VT / 16) * 64];  // S^T fragments, bf16 (forward only)
+    __align__(16) float a[2][DK];                 // chunk decay exp(B_last)
 };
 
 // One chunk's operands in registers: the wave's k^T fragments (state update, key rows
@@ -368,7 +376,7 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
     }
 
     // A chunk's loads (lc: chunk index within the segment) go out in two parts, at the
-    // start and in the middle of the processing of the chunk two before it, so that the
+    // start and in the middle of the processing of the chunk three before it, so that the
     // memory unit's queue is not handed all of them at once; each part stays in program
     // order (the memory-counter waits before a chunk is used count the loads after it).
     auto load_part = [&](ChainRegs<KV>& R, int lc, int part) {
@@ -421,8 +429,48 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
 
     auto process = [&](const ChainRegs<KV>& R, const ChainRegs<KV>& Rn, ChainRegs<KV>& Rl, int lc,
                        int cur) {
-        load_part(Rl, lc + 2, 0);
+        load_part(Rl, lc + 3, 0);
         const uint16_t* vv = sm.v[cur];
+        // Every LDS operand of the chunk is read first, so that the reads overlap one
+        // another instead of each waiting in front of its own product.
+        constexpr int NS = OUT ? 4 : 1;
+        bf16x8_t sfr[NS][NVT], vpk[NS / 2 + 1][NVT], vf[2][NVT];
+        f32x4_t av[2];
+        if (OUT) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int ct = 0; ct < NVT; ++ct)
+                    sfr[kk][ct] = __builtin_bit_cast(bf16x8_t, sm.st[cur][(kk * NVT + ct) * 64 + lane]);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int ct = 0; ct < NVT; ++ct) vpk[kk][ct] = frag_kr_cols_pk<NVT>(vv, PV, kk, 0, ct, lane);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct) vf[kk][ct] = frag_kr_cols<NVT>(vv, PV, 32 * kk, 0, ct, lane);
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+            const float4 a4 = *reinterpret_cast<const float4*>(sm.a[cur] + 16 * (2 * w + ib) + 4 * g);
+            av[ib] = f32x4_t{a4.x, a4.y, a4.z, a4.w};
+        }
+        // S = diag(a) S + K^^T V (key rows 32 w ..)
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+            if (!OUT) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) aprod[ib][j] *= av[ib][j];
+            }
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct) {
+                f32x4_t s_ = S[ib][ct] * av[ib];
+                s_ = mfma16(__builtin_bit_cast(bf16x8_t, R.kt[2 * ib]), vf[0][ct], s_);
+                s_ = mfma16(__builtin_bit_cast(bf16x8_t, R.kt[2 * ib + 1]), vf[1][ct], s_);
+                S[ib][ct] = s_;
+            }
+        }
         if (OUT) {
             // O^T = S^T q^^T + V^T P^T for rows 16 w ..; 4 NVT contiguous columns per lane
             uint2 ow[NVT];
@@ -431,16 +479,16 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
                 f32x4_t o_ = zero4();
 #pragma unroll
                 for (int kk = 0; kk < DK / 32; ++kk)
-                    o_ = mfma16(frag_st<NVT>(sm.st[cur], PQ, 0, ct, 32 * kk, lane),
-                                __builtin_bit_cast(bf16x8_t, R.qf[kk]), o_);
-                o_ = mfma16(frag_kr_cols_pk<NVT>(vv, PV, 0, 0, ct, lane),
-                            __builtin_bit_cast(bf16x8_t, R.pf[0]), o_);
-                if (nk > 1)
-                    o_ = mfma16(frag_kr_cols_pk<NVT>(vv, PV, 1, 0, ct, lane),
-                                __builtin_bit_cast(bf16x8_t, R.pf[1]), o_);
+                    o_ = mfma16(sfr[kk][ct], __builtin_bit_cast(bf16x8_t, R.qf[kk]), o_);
+                o_ = mfma16(vpk[0][ct], __builtin_bit_cast(bf16x8_t, R.pf[0]), o_);
+                if (nk > 1) o_ = mfma16(vpk[1][ct], __builtin_bit_cast(bf16x8_t, R.pf[1]), o_);
                 ow[ct].x = pack_bf16x2(o_[0], o_[1]);
                 ow[ct].y = pack_bf16x2(o_[2], o_[3]);
             }
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct)
+                sm.st[cur ^ 1][(w * NVT + ct) * 64 + lane] =
+                    __builtin_bit_cast(uint4, pack_pk(S[0][ct], S[1][ct]));
             const uint32_t orow = ((uint32_t(ch0 + lc) * C + rw) * uint32_t(DV) + c0 + 4 * NVT * g) * 2u;
             if constexpr (NVT == 4) {
                 buf_st16(ro, orow, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
@@ -451,40 +499,17 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
                 buf_st8(ro, orow, ow[0]);
             }
         }
-        load_part(Rl, lc + 2, 1);
-        // S = diag(a) S + K^^T V (key rows 32 w ..)
-        bf16x8_t vf[2][NVT];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int ct = 0; ct < NVT; ++ct) vf[kk][ct] = frag_kr_cols<NVT>(vv, PV, 32 * kk, 0, ct, lane);
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-            const int i0 = 16 * (2 * w + ib);
-            const float4 a4 = *reinterpret_cast<const float4*>(sm.a[cur] + i0 + 4 * g);
-            const f32x4_t av = {a4.x, a4.y, a4.z, a4.w};
-            if (!OUT) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) aprod[ib][j] *= av[j];
-            }
-#pragma unroll
-            for (int ct = 0; ct < NVT; ++ct) {
-                f32x4_t s_ = S[ib][ct] * av;
-                s_ = mfma16(__builtin_bit_cast(bf16x8_t, R.kt[2 * ib]), vf[0][ct], s_);
-                s_ = mfma16(__builtin_bit_cast(bf16x8_t, R.kt[2 * ib + 1]), vf[1][ct], s_);
-                S[ib][ct] = s_;
-                if (OUT) store_st<NVT>(sm.st[cur ^ 1], PQ, i0, 0, ct, s_, lane);
-            }
-        }
+        load_part(Rl, lc + 3, 1);
         stage(Rn, cur ^ 1);
         lds_barrier();
     };
 
-    // three register sets rotate: each chunk's loads go out two chunks before it is
+    // four register sets rotate: each chunk's loads go out three chunks before it is
     // processed (a prefetch past the segment reads zeros and is never processed)
-    ChainRegs<KV> RA, RB, RC;
+    ChainRegs<KV> RA, RB, RC, RD;
     load_chunk(RA, 0);
     load_chunk(RB, 1);
+    load_chunk(RC, 2);
     if (OUT) {
         if (a.nseg == 1) {
             if (a.S0) {
@@ -549,19 +574,19 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
             }
         }
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-            for (int ct = 0; ct < NVT; ++ct)
-                store_st<NVT>(sm.st[0], PQ, 16 * (2 * w + ib), 0, ct, S[ib][ct], lane);
+        for (int ct = 0; ct < NVT; ++ct)
+            sm.st[0][(w * NVT + ct) * 64 + lane] = __builtin_bit_cast(uint4, pack_pk(S[0][ct], S[1][ct]));
     }
     stage(RA, 0);
     lds_barrier();
-    for (int lc = 0; lc < nloc; lc += 3) {
-        process(RA, RB, RC, lc, lc & 1);
+    for (int lc = 0; lc < nloc; lc += 4) {
+        process(RA, RB, RD, lc, 0);
         if (lc + 1 >= nloc) break;
-        process(RB, RC, RA, lc + 1, (lc + 1) & 1);
+        process(RB, RC, RA, lc + 1, 1);
         if (lc + 2 >= nloc) break;
-        process(RC, RA, RB, lc + 2, lc & 1);
+        process(RC, RD, RB, lc + 2, 0);
+        if (lc + 3 >= nloc) break;
+        process(RD, RA, RC, lc + 3, 1);
     }
 
     if (OUT) {

@@ -255,3 +255,13 @@ def test_full_workload(name):
     per_seq = np.max(np.abs(o - o_ref), axis=1) / np.max(np.abs(o_ref), axis=1)
     print(name, errs, "worst sequence o", float(per_seq.max()), int(per_seq.argmax()), flush=True)
     assert float(per_seq.max()) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("N,dv,segments", [(64 * 20 + 3, 128, 2), (64 * 70 + 7, 16, 71),
+                                           (64 * 8 + 1, 64, 3)])
+def test_gla_segment_counts(N, dv, segments):
+    """GLA with long segments (eleven chunks), with many short ones (71 segments, so the
+    look-back of the last one reads 70 summaries), and with 64-column tiles."""
+    inp = W.make_inputs(wl_for("gla", 1, 2, N, dv, seed=N % 97), with_state=True)
+    banner(f"mfma gla N={N} dv={dv} segments={segments}")
+    check(inp, run_gpu(inp, segments=segments), run_oracle(inp))
