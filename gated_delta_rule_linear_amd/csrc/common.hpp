@@ -132,10 +132,10 @@ __device__ __forceinline__ float fast_log(float x) { return __builtin_amdgcn_log
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504f); }
 
 // ELU(x) + 1 with the hardware exponential (a few ulp; used where operands are rounded
-// to bf16), branch-free.
+// to bf16), branch-free: max(x, 0) + exp(min(x, 0)), which is x + 1 for x > 0 (the
+// exponential of 0 is exactly 1) and exp(x) otherwise.
 __device__ __forceinline__ float elu_plus_one_fast(float x) {
-    const float e = fast_exp(fminf(x, 0.f));
-    return x > 0.f ? x + 1.f : e;
+    return fmaxf(x, 0.f) + fast_exp(fminf(x, 0.f));
 }
 
 // DPP lane permutation of a float: lanes outside the enabled rows/banks (or with no

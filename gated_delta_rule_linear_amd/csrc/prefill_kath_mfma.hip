@@ -30,8 +30,8 @@ namespace {
 constexpr int DK = 128;
 constexpr int C = kMfmaChunk;  // 64
 constexpr int NT = 256;
-constexpr int PQ = DK + 8;     // pitch of [*][128] bf16 tiles
-constexpr int PC = C + 8;      // pitch of [*][64] bf16 tiles
+constexpr int PQ = DK + 16;    // pitch of [*][128] bf16 tiles (72 dwords: 16-byte reads of 16 rows
+                               // at one column are free of bank conflicts)
 
 struct KathArgs {
     const uint16_t *q, *k, *v;
@@ -47,19 +47,21 @@ struct KathArgs {
 };
 
 // The summary kernel uses only the fields up to `qt`, and is launched with that much
-// LDS. NW = waves per workgroup.
+// LDS. NW = waves per workgroup. S^T is kept in fragment order per column group: piece
+// (cg, kk, ct, lane = 16 g + L) holds column colmap(ct, L) of the group and key rows
+// 32 kk + 4 g .. + 3, 32 kk + 16 + 4 g .. + 3, which is what lane (g, L) of the group's
+// wave with row block kk holds in its two state tiles; so each lane writes one
+// contiguous 16-byte piece and each reader loads one (the matching phi(q) fragments are
+// read as two 8-byte halves).
 template <int VT, int NW>
 struct __align__(16) ChainSmem {
     static constexpr int PV = VT + 8;
-    __align__(16) uint16_t kt[2][C * PQ];   // phi(k) [s][i]
-    __align__(16) uint16_t v[2][C * PV];    // V [s][c]
-    __align__(16) float zp[2][NW][DK];      // per-wave column sums of phi(k)
-    __align__(16) float z[DK];              // z entering the chunk
-    __align__(16) uint16_t qt[2][C * PQ];   // phi(q) [r][i] (forward)
-    __align__(16) uint16_t st[2][VT * PQ];  // S^T [c][i], bf16 (forward)
-    __align__(16) uint16_t p[C * PC];       // P [r][s] (forward)
-    float psum[10][16];                     // row sums of the P tiles
-    float qz[C];                            // phi(q_r) . z
+    __align__(16) uint16_t kt[2][C * PQ];          // phi(k) [s][i]
+    __align__(16) uint16_t v[2][C * PV];           // V [s][c]
+    __align__(16) float zp[2][NW][DK];             // per-wave column sums of phi(k)
+    __align__(16) float z[2][DK];                  // z entering the chunk
+    __align__(16) uint16_t qt[2][C * PQ];          // phi(q) [r][i] (forward)
+    __align__(16) uint4 st[2][VT / 16 * 4 * 64];   // S^T fragments, bf16 (forward)
 };
 
 template <int KST, int KV>
@@ -70,7 +72,10 @@ struct ChainRegs {
 // A workgroup owns VT = 16 NVT CG value columns of one (sequence, segment) and runs
 // 4 CG waves: wave w takes row block rb = w % 4 (output rows 16 rb .., state key rows
 // 32 rb ..) of column group cg = w / 4 (16 NVT columns). The column groups share the
-// staged phi(q), phi(k), V and P.
+// staged phi(q), phi(k) and V; each wave forms the score tiles of its own row block in
+// registers (the two waves of a row block both do), with their row sums, and phi(q) . z
+// for its rows, so that nothing but the staged chunk and S^T passes through LDS and one
+// barrier per chunk suffices.
 template <bool OUT, int NVT, int CG>
 __global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
     constexpr int VT = 16 * NVT * CG;
@@ -122,19 +127,12 @@ __global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
                 const int i = 16 * (2 * rb + ib) + 4 * g + j, c = c0 + cw + colmap<NVT>(ct, jl);
                 S[ib][ct][j] = Sinit ? Sinit[size_t(i) * DV + c] : 0.f;
             }
-    if (tid < DK) sm.z[tid] = zinit ? zinit[tid] : 0.f;
+    if (tid < DK) sm.z[0][tid] = zinit ? zinit[tid] : 0.f;
     if (OUT) {
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-            for (int ct = 0; ct < NVT; ++ct)
-                store_st<NVT>(sm.st[0], PQ, 16 * (2 * rb + ib), cw, ct, S[ib][ct], lane);
-        // the P blocks above the diagonal that the row-block products read stay zero
-        if (w < 2) {
-            const int zb = w == 0 ? 0 : 2, sb = zb + 1;
-            const int r = 16 * zb + (lane >> 2), s = 16 * sb + (lane & 3) * 4;
-            *reinterpret_cast<uint2*>(sm.p + r * PC + s) = make_uint2(0, 0);
-        }
+        for (int ct = 0; ct < NVT; ++ct)
+            sm.st[0][((cg * 4 + rb) * NVT + ct) * 64 + lane] =
+                __builtin_bit_cast(uint4, pack_pk(S[0][ct], S[1][ct]));
     }
 
     // Per-sequence resources: rows past the end of the sequence read as zero and
@@ -187,19 +185,26 @@ __global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
 #pragma unroll
         for (int x4 = 0; x4 < KST; ++x4) {
             const int x = tid + NTW * x4, r = x >> 4, col = (x & 15) * 8;
+            // rows past the sequence's end read as zeros, whose phi is 1: zero them
             float f[8];
             unpack8(R.kst[x4], f);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) { const float e = elu_plus_one_fast(f[q]); f[q] = r < n ? e : 0.f; }
-            const uint4 pk = pack8(f);
-            *reinterpret_cast<uint4*>(sm.kt[buf] + r * PQ + col) = pk;
-            unpack8(pk, f);   // z sums the bf16 features the matrix cores see
+            for (int q = 0; q < 8; ++q) f[q] = elu_plus_one_fast(f[q]);
+            if (r >= n) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) f[q] = 0.f;
+            }
+            *reinterpret_cast<uint4*>(sm.kt[buf] + r * PQ + col) = pack8(f);
 #pragma unroll
             for (int q = 0; q < 8; ++q) zpart[q] += f[q];
             if (OUT) {
                 unpack8(R.qst[x4], f);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) { const float e = elu_plus_one_fast(f[q]); f[q] = r < n ? e : 0.f; }
+                for (int q = 0; q < 8; ++q) f[q] = elu_plus_one_fast(f[q]);
+                if (r >= n) {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) f[q] = 0.f;
+                }
                 *reinterpret_cast<uint4*>(sm.qt[buf] + r * PQ + col) = pack8(f);
             }
         }
@@ -221,72 +226,88 @@ __global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
         }
     };
 
+    // The two waves that share a SIMD (same row block, column groups 0 and 1) stage the
+    // next chunk at opposite ends of the chunk, so that one's vector work overlaps the
+    // other's products.
+    const bool early = OUT && (cg & 1) != 0;
     auto process = [&](const ChainRegs<KST, KV>& Rn, ChainRegs<KST, KV>& Rl, int lc, int cur) {
         load_part(Rl, lc + 2, 0);
+        if (early) stage(Rn, cur ^ 1, lc + 1);
         const uint16_t* kt = sm.kt[cur];
         const uint16_t* vv = sm.v[cur];
+        // z entering the next chunk
+        if (tid < DK) {
+            float zs = sm.z[cur][tid];
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) zs += sm.zp[cur][ww][tid];
+            sm.z[cur ^ 1][tid] = zs;
+        }
         if (OUT) {
             const uint16_t* qt = sm.qt[cur];
-            // ---- P (10 lower tiles, row sums) and phi(q_r) . z
-            for (int ti = w; ti < 10; ti += NW) {
-                const int pr = ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3;
-                const int sb = ti - (pr * (pr + 1)) / 2;
+            // every LDS operand first: phi(q) of rows 16 rb .. (keys in natural order for
+            // the scores, in the S^T fragments' order for the state part), S^T, V for P V,
+            // and this lane's 32 keys of phi(q) with z
+            bf16x8_t qf[4], qs[4], sf[4][NVT], vpk[2][NVT];
+            const uint16_t* qrow = qt + (16 * rb + jl) * PQ;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                qf[kk] = frag_kc(qt, PQ, 16 * rb, 32 * kk, lane);
+                const uint2 lo = *reinterpret_cast<const uint2*>(qrow + 32 * kk + 4 * g);
+                const uint2 hi = *reinterpret_cast<const uint2*>(qrow + 32 * kk + 16 + 4 * g);
+                qs[kk] = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+                for (int ct = 0; ct < NVT; ++ct)
+                    sf[kk][ct] = __builtin_bit_cast(bf16x8_t, sm.st[cur][((cg * 4 + kk) * NVT + ct) * 64 + lane]);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int ct = 0; ct < NVT; ++ct) vpk[kk][ct] = frag_kr_cols_pk<NVT>(vv, PV, kk, cw, ct, lane);
+            float qz = 0.f;
+#pragma unroll
+            for (int q8 = 0; q8 < 4; ++q8) {
+                float f[8];
+                unpack8(*reinterpret_cast<const uint4*>(qrow + 32 * g + 8 * q8), f);
+                const float4 z0 = *reinterpret_cast<const float4*>(sm.z[cur] + 32 * g + 8 * q8);
+                const float4 z1 = *reinterpret_cast<const float4*>(sm.z[cur] + 32 * g + 8 * q8 + 4);
+                qz += f[0] * z0.x + f[1] * z0.y + f[2] * z0.z + f[3] * z0.w;
+                qz += f[4] * z1.x + f[5] * z1.y + f[6] * z1.z + f[7] * z1.w;
+            }
+            // P^T tiles D[s][r] = phi(k_s) . phi(q_r) of this row block, s <= r (the tiles
+            // past the diagonal vanish under the mask), and their row sums
+            f32x4_t pt[4];
+            float rs = 0.f;
+            const int r = 16 * rb + jl;
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
                 f32x4_t acc = zero4();
 #pragma unroll
                 for (int kk = 0; kk < DK / 32; ++kk)
-                    acc = mfma16(frag_kc(kt, PQ, 16 * sb, 32 * kk, lane),
-                                 frag_kc(qt, PQ, 16 * pr, 32 * kk, lane), acc);   // D[s][r]
-                const int r = 16 * pr + jl;
-                float rs = 0.f;
+                    acc = mfma16(frag_kc(kt, PQ, 16 * sb, 32 * kk, lane), qf[kk], acc);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int s = 16 * sb + 4 * g + j;
-                    acc[j] = s <= r ? acc[j] : 0.f;
+                    acc[j] = 16 * sb + 4 * g + j <= r ? acc[j] : 0.f;
                     rs += acc[j];
                 }
-                store_dT(sm.p, PC, 16 * sb, 16 * pr, acc, lane);
-                rs += __shfl_xor(rs, 16, 64);
-                rs += __shfl_xor(rs, 32, 64);
-                if (g == 0) sm.psum[ti][jl] = rs;
+                pt[sb] = acc;
             }
-            {
-                // NTW / 64 threads per row, with the bf16 features
-                constexpr int TPR = NTW / C, CPT = DK / TPR;
-                const int r = tid / TPR, part = tid % TPR;
-                float acc = 0.f;
-#pragma unroll
-                for (int q8 = 0; q8 < CPT / 8; ++q8) {
-                    const int col = part * CPT + q8 * 8;
-                    float f[8];
-                    unpack8(*reinterpret_cast<const uint4*>(qt + r * PQ + col), f);
-                    const float4 z0 = *reinterpret_cast<const float4*>(sm.z + col);
-                    const float4 z1 = *reinterpret_cast<const float4*>(sm.z + col + 4);
-                    acc += f[0] * z0.x + f[1] * z0.y + f[2] * z0.z + f[3] * z0.w;
-                    acc += f[4] * z1.x + f[5] * z1.y + f[6] * z1.z + f[7] * z1.w;
-                }
-#pragma unroll
-                for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-                if (part == 0) sm.qz[r] = acc;
-            }
-            lds_barrier();
+            rs += __shfl_xor(rs, 16, 64);
+            rs += __shfl_xor(rs, 32, 64);
+            qz += __shfl_xor(qz, 16, 64);
+            qz += __shfl_xor(qz, 32, 64);
+            const float inv = 1.f / (qz + rs + a.eps);
+            const bf16x8_t pb0 = pack_pk(pt[0], pt[1]), pb1 = pack_pk(pt[2], pt[3]);
             load_part(Rl, lc + 2, 1);
-            // ---- O^T = S^T phi(Q)^T + V^T P^T, divided by the row's denominator
-            float den = sm.qz[rw] + a.eps;
-            const int tb = (rb * (rb + 1)) / 2;
-            for (int sb = 0; sb <= rb; ++sb) den += sm.psum[tb + sb][jl];
-            const float inv = 1.f / den;
+            // O^T = S^T phi(Q)^T + V^T P^T, divided by the row's denominator
             const int nk = rb < 2 ? 1 : 2;
             uint2 ow[NVT];
 #pragma unroll
             for (int ct = 0; ct < NVT; ++ct) {
                 f32x4_t o_ = zero4();
 #pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk)
-                    o_ = mfma16(frag_st<NVT>(sm.st[cur], PQ, cw, ct, 32 * kk, lane),
-                                frag_kc(qt, PQ, 16 * rb, 32 * kk, lane), o_);
-                for (int kk = 0; kk < nk; ++kk)
-                    o_ = mfma16(frag_kr_cols<NVT>(vv, PV, 32 * kk, cw, ct, lane),
-                                frag_kc(sm.p, PC, 16 * rb, 32 * kk, lane), o_);
+                for (int kk = 0; kk < DK / 32; ++kk) o_ = mfma16(sf[kk][ct], qs[kk], o_);
+                o_ = mfma16(vpk[0][ct], pb0, o_);
+                if (nk > 1) o_ = mfma16(vpk[1][ct], pb1, o_);
                 o_ = o_ * inv;
                 ow[ct].x = pack_bf16x2(o_[0], o_[1]);
                 ow[ct].y = pack_bf16x2(o_[2], o_[3]);
@@ -302,32 +323,31 @@ __global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
                 buf_st8(ro, orow, ow[0]);
             }
         }
-        // ---- S += phi(K)^T V (key rows 32 rb ..); z += column sums of phi(k)
-        bf16x8_t vf[2][NVT];
+        // ---- S += phi(K)^T V (key rows 32 rb ..)
+        bf16x8_t vf[2][NVT], kf[2][2];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
             for (int ct = 0; ct < NVT; ++ct) vf[kk][ct] = frag_kr_cols<NVT>(vv, PV, 32 * kk, cw, ct, lane);
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-            const int i0 = 16 * (2 * rb + ib);
-            const bf16x8_t k0f = frag_kr(kt, PQ, 0, i0, lane);
-            const bf16x8_t k1f = frag_kr(kt, PQ, 32, i0, lane);
+            for (int ib = 0; ib < 2; ++ib) kf[ib][kk] = frag_kr(kt, PQ, 32 * kk, 16 * (2 * rb + ib), lane);
+        }
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
             for (int ct = 0; ct < NVT; ++ct) {
-                f32x4_t s_ = mfma16(k0f, vf[0][ct], S[ib][ct]);
-                s_ = mfma16(k1f, vf[1][ct], s_);
-                S[ib][ct] = s_;
-                if (OUT) store_st<NVT>(sm.st[cur ^ 1], PQ, i0, cw, ct, s_, lane);
+                f32x4_t s_ = mfma16(kf[ib][0], vf[0][ct], S[ib][ct]);
+                S[ib][ct] = mfma16(kf[ib][1], vf[1][ct], s_);
             }
-        }
-        if (tid < DK) {
-            float zs = sm.z[tid];
+        if (OUT) {
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) zs += sm.zp[cur][ww][tid];
-            sm.z[tid] = zs;
+            for (int ct = 0; ct < NVT; ++ct)
+                sm.st[cur ^ 1][((cg * 4 + rb) * NVT + ct) * 64 + lane] =
+                    __builtin_bit_cast(uint4, pack_pk(S[0][ct], S[1][ct]));
+        } else {
+            load_part(Rl, lc + 2, 1);
         }
-        stage(Rn, cur ^ 1, lc + 1);
+        if (!early) stage(Rn, cur ^ 1, lc + 1);
         lds_barrier();
     };
 
@@ -356,7 +376,7 @@ __global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
                         const int c = c0 + cw + colmap<NVT>(ct, jl);
                         a.S[size_t(seq) * DK * DV + size_t(i) * DV + c] = S[ib][ct][j];
                     }
-            if (tile == 0 && tid < DK) a.z[size_t(seq) * DK + tid] = sm.z[tid];
+            if (tile == 0 && tid < DK) a.z[size_t(seq) * DK + tid] = sm.z[nloc & 1][tid];
         }
     } else {
         float* dS = a.dS + (size_t(seq) * a.nseg + seg + 1) * DK * DV;
@@ -370,7 +390,7 @@ __global__ __launch_bounds__(NT * CG) void kath_chain_kernel(KathArgs a) {
                     const int c = c0 + cw + colmap<NVT>(ct, jl);
                     dS[size_t(i) * DV + c] = S[ib][ct][j];
                 }
-        if (tile == 0 && tid < DK) a.dz[(size_t(seq) * a.nseg + seg + 1) * DK + tid] = sm.z[tid];
+        if (tile == 0 && tid < DK) a.dz[(size_t(seq) * a.nseg + seg + 1) * DK + tid] = sm.z[nloc & 1][tid];
     }
 }
 
