@@ -38,7 +38,8 @@ SOURCES = ["la_api.cpp", "decode.hip", "prefill_valu.hip", "prefill_kath_mfma.hi
 # (no copies out of the accumulation registers) where a kernel's vector-ALU work consumes
 # them every chunk
 EXTRA = {"prefill_gdn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "prefill_gla_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "prefill_gla_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "prefill_kda_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -46,7 +46,9 @@ constexpr float kGateMin = 4.539993e-05f;   // exp(-10)
 
 // Workspace of one chunk (bytes), each matrix in MFMA fragment order (a 16-byte piece
 // per lane, a wave's fragment one contiguous kilobyte):
-//   Q~, K~: piece (rb, kk, lane = 16 g + j) = row 16 rb + j, keys 32 kk + 8 g .. + 7;
+//   Q~, K~: piece (rb, kk, lane = 16 g + j) = row 16 rb + j, keys 32 kk + 4 g .. + 3 then
+//           32 kk + 16 + 4 g .. + 3 (the key order of the S^T fragments the forward
+//           packs straight from its state registers);
 //   K^^T:   piece (ib, kk, lane) = key 16 ib + j, tokens 32 kk + 8 g .. + 7;
 //   P:      piece (rb, kk, lane) = row 16 rb + j, tokens 32 kk + 4 g .. + 3, then
 //           32 kk + 16 + 4 g .. + 3 (the order the matrix cores return the tile);
@@ -253,9 +255,11 @@ __global__ __launch_bounds__(NTP) void kda_prep_kernel(KdaArgs a) {
         *reinterpret_cast<uint32_t*>(sm.u.qo + rr * PQ + col) = pack_bf16x2(q0 * e0, q1 * e1);
         *reinterpret_cast<uint32_t*>(sm.kr + rr * PQ + col) = pack_bf16x2(k0 * e0, k1 * e1);
         *reinterpret_cast<uint32_t*>(sm.ko + rr * PQ + col) = pack_bf16x2(kt0, kt1);
-        // Q~ and K~ in fragment order: row rr, columns col, col + 1 are a quarter piece
-        const int kk = col >> 5, gg = (col & 31) >> 3;
-        const uint32_t piece = (((rr >> 4) * 4 + kk) * 64 + 16 * gg + pr) * 16 + (col & 7) * 2;
+        // Q~ and K~ in fragment order: row rr, columns col, col + 1 are one slot pair of the
+        // piece of lane group gg (key kc = 4 gg + e or 16 + 4 gg + e goes to slot e or 4 + e)
+        const int kk = col >> 5, kc = col & 31, gg = (kc & 15) >> 2;
+        const int slot = (kc & 3) + (kc >= 16 ? 4 : 0);
+        const uint32_t piece = (((rr >> 4) * 4 + kk) * 64 + 16 * gg + pr) * 16 + slot * 2;
         const float G0 = pre[0] * pp[r][0], G1 = pre[1] * pp[r][1];
         *reinterpret_cast<uint32_t*>(wsc + kWsQ + piece) = pack_bf16x2(q0 * G0, q1 * G1);
         *reinterpret_cast<uint32_t*>(wsc + kWsK + piece) = pack_bf16x2(k0 * G0, k1 * G1);
@@ -403,12 +407,16 @@ __global__ __launch_bounds__(NTP) void kda_prep_kernel(KdaArgs a) {
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
+// The bf16 copy of the state is kept as S^T fragments: piece (kk, ct, lane = 16 g + L)
+// holds column colmap(ct, L) and key rows 32 kk + 4 g .. + 3, 32 kk + 16 + 4 g .. + 3, which
+// is what lane (g, L) of wave kk holds in its two state tiles, so each lane writes one
+// contiguous 16-byte piece and each reader loads one.
 template <int VT>
 struct __align__(16) FwdSmem {
     static constexpr int PV = VT + 8;
-    __align__(16) uint16_t st[VT * PQ];    // S^T [c][i], bf16 copy of the state tile
-    __align__(16) uint16_t x[C * PV];      // X [s][c]
-    __align__(16) uint16_t u[C * PV];      // U [s][c]
+    __align__(16) uint4 st[4 * (VT / 16) * 64];   // S^T fragments, bf16
+    __align__(16) uint16_t x[C * PV];            // X [s][c]
+    __align__(16) uint16_t u[C * PV];            // U [s][c]
 };
 
 // Per-chunk operands of one wave (row block rb = w): rows 16 rb + j of Q~, K~, T and P,
@@ -454,9 +462,8 @@ __global__ __launch_bounds__(NTF) void kda_fwd_kernel(KdaArgs a) {
                 S[ib][ct][j] = a.S0 ? a.S0[seq * DK * DV + size_t(i) * DV + c0 + c] : 0.f;
             }
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-        for (int ct = 0; ct < NVT; ++ct) store_st<NVT>(sm.st, PQ, 16 * (2 * rb + ib), 0, ct, S[ib][ct], lane);
+    for (int ct = 0; ct < NVT; ++ct)
+        sm.st[(rb * NVT + ct) * 64 + lane] = __builtin_bit_cast(uint4, pack_pk(S[0][ct], S[1][ct]));
 
     const rsrc_t rw_ = make_rsrc(a.ws + seq * size_t(a.nchunks) * kWsChunk, uint32_t(nchunks) * kWsChunk);
     const uint32_t vbytes = uint32_t(sp.len) * uint32_t(DV) * 2u;
@@ -513,15 +520,20 @@ __global__ __launch_bounds__(NTF) void kda_fwd_kernel(KdaArgs a) {
         const float br = gate_val<GB>(R.b);   // 0 past the end
         // ---- (S^T Q~^T) and (S^T K~^T) for rows 16 rb ..: D[c][r]
         f32x4_t oq[NVT], ks[NVT];
+        bf16x8_t sf[DK / 32][NVT];   // every S^T fragment first, so that the reads overlap
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk)
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct)
+                sf[kk][ct] = __builtin_bit_cast(bf16x8_t, sm.st[(kk * NVT + ct) * 64 + lane]);
 #pragma unroll
         for (int ct = 0; ct < NVT; ++ct) { oq[ct] = zero4(); ks[ct] = zero4(); }
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk) {
 #pragma unroll
             for (int ct = 0; ct < NVT; ++ct) {
-                const bf16x8_t sf = frag_st<NVT>(sm.st, PQ, 0, ct, 32 * kk, lane);
-                oq[ct] = mfma16(sf, __builtin_bit_cast(bf16x8_t, R.q[kk]), oq[ct]);
-                ks[ct] = mfma16(sf, __builtin_bit_cast(bf16x8_t, R.k[kk]), ks[ct]);
+                oq[ct] = mfma16(sf[kk][ct], __builtin_bit_cast(bf16x8_t, R.q[kk]), oq[ct]);
+                ks[ct] = mfma16(sf[kk][ct], __builtin_bit_cast(bf16x8_t, R.k[kk]), ks[ct]);
             }
         }
         // ---- X[s][c] = beta_s (v_s,c - (S^T k~_s)_c), s = 16 rb + j
@@ -574,7 +586,6 @@ __global__ __launch_bounds__(NTF) void kda_fwd_kernel(KdaArgs a) {
             for (int ct = 0; ct < NVT; ++ct) uf[kk][ct] = frag_kr_cols<NVT>(sm.u, PV, 32 * kk, 0, ct, lane);
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
-            const int i0 = 16 * (2 * rb + ib);
             const f32x4_t av = {R.a[ib].x, R.a[ib].y, R.a[ib].z, R.a[ib].w};
 #pragma unroll
             for (int ct = 0; ct < NVT; ++ct) {
@@ -582,9 +593,11 @@ __global__ __launch_bounds__(NTF) void kda_fwd_kernel(KdaArgs a) {
                 s_ = mfma16(__builtin_bit_cast(bf16x8_t, R.kh[2 * ib]), uf[0][ct], s_);
                 s_ = mfma16(__builtin_bit_cast(bf16x8_t, R.kh[2 * ib + 1]), uf[1][ct], s_);
                 S[ib][ct] = s_;
-                store_st<NVT>(sm.st, PQ, i0, 0, ct, s_, lane);
             }
         }
+#pragma unroll
+        for (int ct = 0; ct < NVT; ++ct)
+            sm.st[(rb * NVT + ct) * 64 + lane] = __builtin_bit_cast(uint4, pack_pk(S[0][ct], S[1][ct]));
         lds_barrier();
     };
 
