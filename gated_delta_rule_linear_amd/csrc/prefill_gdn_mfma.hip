@@ -57,15 +57,23 @@ constexpr int TPC = 6;
 constexpr int TCH = TPC * 512;  // bf16 elements of T per chunk in the workspace
 __host__ __device__ constexpr int t_piece(int i) { return i < 2 ? 2 * i : i + 2; }
 
+// 40 KiB, so that four workgroups share a compute unit: the level scratch tiles reuse
+// the K tile, which no wave reads after the L products.
 struct __align__(16) PrepSmem {
-    __align__(16) uint16_t k[C * PQ];
-    __align__(16) uint16_t t[C * PC];      // T [r][s]
-    __align__(16) uint16_t lo[C * PC];     // off-diagonal blocks of L [r][s]
-    __align__(16) uint16_t ya[2][32 * PY];  // level-a scratch: Y = L_ij T_jj (16 rows used)
-    __align__(16) uint16_t yb[32 * PY];    // level-b scratch: Y = L[32:64, 0:32] A^{-1}
-    __align__(16) float ld[4][16 * PD];    // diagonal blocks of L, fp32
+    union {
+        __align__(16) uint16_t k[C * PQ];
+        struct {
+            __align__(16) uint16_t ya[2][32 * PY];  // level-a scratch: Y = L_ij T_jj (rows 0..15
+                                                    // written; the products mask the rest)
+            __align__(16) uint16_t yb[32 * PY];     // level-b scratch: Y = L[32:64, 0:32] A^{-1}
+        };
+    };
+    __align__(16) uint16_t t[C * PC];             // T [r][s]
+    __align__(16) uint16_t lo[(C - 16) * PC];     // off-diagonal blocks of L, rows 16..63 [r - 16][s]
+    __align__(16) float ld[4][16 * PD];           // diagonal blocks of L, fp32
     float cum[C], beta[C];
 };
+static_assert(sizeof(PrepSmem) <= 40960, "four prep workgroups per compute unit");
 
 struct GdnArgs {
     const uint16_t *q, *k, *v;
@@ -150,14 +158,12 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a, int nunits) {
     } else if (w == 1) {
         sm.beta[lane] = lane < n ? gate_val<GB>(graw) : 0.f;
     } else {
-        // zero the six upper blocks of T and the unused rows of the level-a scratch
+        // zero the six upper blocks of T
         const int r = lane >> 2, cc = (lane & 3) * 4;
         const int ub[6][2] = {{0, 1}, {0, 2}, {0, 3}, {1, 2}, {1, 3}, {2, 3}};
         for (int x = w - 2; x < 6; x += 2)
             *reinterpret_cast<uint2*>(sm.t + (16 * ub[x][0] + r) * PC + 16 * ub[x][1] + cc) =
                 make_uint2(0, 0);
-        uint16_t* y = sm.ya[w - 2];
-        for (int x = lane; x < 32 * PY / 4; x += 64) *reinterpret_cast<uint2*>(y + 4 * x) = make_uint2(0, 0);
     }
     lds_barrier();
 
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a, int nunits) {
             const float csv[4] = {cs.x, cs.y, cs.z, cs.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) d[j] *= br * fast_exp(cr - csv[j]);
-            store_dT(sm.lo, PC, 16 * sb, 16 * rb, d, lane);
+            store_dT(sm.lo, PC, 16 * sb, 16 * (rb - 1), d, lane);
         }
     }
     lds_barrier();
@@ -231,7 +237,7 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a, int nunits) {
         uint16_t* y = sm.ya[w - 1];
         // Y^T = T_jj^T L_ij^T -> y[r][jj] (rows 0..15)
         f32x4_t d = mfma16(k16(frag_kr(sm.t, PC, 16 * j, 16 * j, lane), lane),
-                           k16(frag_kc(sm.lo, PC, 16 * i, 16 * j, lane), lane), zero4());
+                           k16(frag_kc(sm.lo, PC, 16 * (i - 1), 16 * j, lane), lane), zero4());
         store_dT(y, PY, 0, 0, d, lane);
         wave_lds_sync();
         // T_ij^T = -(Y^T T_ii^T) -> t[16 i + r][16 j + jj]
@@ -244,7 +250,7 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnArgs a, int nunits) {
     {
         const int jb = w & 1, rb = w >> 1;
         const f32x4_t d = mfma16(frag_kr(sm.t, PC, 0, 16 * jb, lane),
-                                 frag_kc(sm.lo, PC, 32 + 16 * rb, 0, lane), zero4());
+                                 frag_kc(sm.lo, PC, 16 + 16 * rb, 0, lane), zero4());
         store_dT(sm.yb, PY, 16 * jb, 16 * rb, d, lane);   // Y[r][j]
     }
     lds_barrier();
@@ -812,8 +818,8 @@ hipError_t launch_cfg(const Problem& p) {
         if (e != hipSuccess) return e;
         const size_t units = size_t(a.nseq) * size_t(a.nchunks);
         if (units > 0x7fffffffull) return hipErrorInvalidValue;
-        // three workgroups fit a compute unit's LDS
-        const size_t grid = std::min(units, size_t(device_cus()) * 3);
+        // four workgroups fit a compute unit's LDS
+        const size_t grid = std::min(units, size_t(device_cus()) * 4);
         gdn_prep_kernel<GB><<<dim3(unsigned(grid)), dim3(NT), smem, p.stream>>>(a, int(units));
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
