@@ -59,23 +59,41 @@ __device__ __forceinline__ void chunk_logs(float* c, const SbArgs& a, size_t tok
     }
 }
 
-// rows t0 .. t0 + 63 of a [N][W] bf16 matrix into an LDS tile of pitch P, scaled per row
-// by f(row) (padding rows zero); 16-byte pieces
+// A thread's 16-byte pieces of rows t0 .. t0 + 63 of a [N][W] bf16 matrix (rows past the
+// sequence's end read as zero): fetched first and stored to LDS later, so that the loads
+// of all of a chunk's matrices are in flight together instead of one round trip each.
+template <int W>
+struct RowPieces {
+    static constexpr int PPR = W / 8, NP = C * PPR / NT;   // pieces per row, per thread
+    static_assert(C * PPR % NT == 0, "whole pieces per thread");
+    uint4 w[NP];
+};
+template <int W>
+__device__ __forceinline__ void fetch_rows(RowPieces<W>& R, const uint16_t* src, size_t tok0, int t0,
+                                           int n) {
+    constexpr int PPR = RowPieces<W>::PPR;
+    const rsrc_t rs = make_rsrc(src + (tok0 + t0) * W, uint32_t(max(n, 0)) * uint32_t(W) * 2u);
+#pragma unroll
+    for (int x = 0; x < RowPieces<W>::NP; ++x) {
+        const int p = int(threadIdx.x) + NT * x, r = p / PPR, cpos = (p % PPR) * 8;
+        R.w[x] = buf_ld16(rs, uint32_t(r * W + cpos) * 2u);
+    }
+}
+// ... into an LDS tile of pitch P, scaled per row by f(row)
 template <int W, int P, typename F>
-__device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* src, size_t tok0, int t0,
-                                           int n, F scale) {
-    constexpr int PPR = W / 8;   // pieces per row
-    for (int p = threadIdx.x; p < C * PPR; p += NT) {
-        const int r = p / PPR, cpos = (p % PPR) * 8;
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (r < n) w = *reinterpret_cast<const uint4*>(src + (tok0 + t0 + r) * W + cpos);
+__device__ __forceinline__ void stage_rows(uint16_t* dst, const RowPieces<W>& R, F scale) {
+    constexpr int PPR = RowPieces<W>::PPR;
+#pragma unroll
+    for (int x = 0; x < RowPieces<W>::NP; ++x) {
+        const int p = int(threadIdx.x) + NT * x, r = p / PPR, cpos = (p % PPR) * 8;
+        uint4 w = R.w[x];
         const float f = scale(r);
         if (f != 1.f) {
-            float x[8];
-            unpack8(w, x);
+            float y[8];
+            unpack8(w, y);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] *= f;
-            w = pack8(x);
+            for (int e = 0; e < 8; ++e) y[e] *= f;
+            w = pack8(y);
         }
         *reinterpret_cast<uint4*>(dst + r * P + cpos) = w;
     }
@@ -99,13 +117,19 @@ __global__ __launch_bounds__(NT) void ssd_bwd_sums_kernel(SbArgs a) {
     const size_t seq = blockIdx.x / a.nch;
     const int ch = blockIdx.x % a.nch, t0 = ch * C, n = min(C, a.N - t0);
     const size_t tok0 = seq * size_t(a.N);
+    RowPieces<DK> kr, qr;
+    RowPieces<DV> vr, dr;
+    fetch_rows(kr, a.k, tok0, t0, n);
+    fetch_rows(qr, a.q, tok0, t0, n);
+    fetch_rows(vr, a.v, tok0, t0, n);
+    fetch_rows(dr, a.dO, tok0, t0, n);
     chunk_logs<GB>(sm.c, a, tok0, t0, n);
     __syncthreads();
     const float cl = sm.c[C - 1];
-    stage_rows<DK, PQ>(sm.kh, a.k, tok0, t0, n, [&](int r) { return __builtin_amdgcn_exp2f(cl - sm.c[r]); });
-    stage_rows<DK, PQ>(sm.qh, a.q, tok0, t0, n, [&](int r) { return __builtin_amdgcn_exp2f(sm.c[r]); });
-    stage_rows<DV, PV>(sm.v, a.v, tok0, t0, n, [](int) { return 1.f; });
-    stage_rows<DV, PV>(sm.dO, a.dO, tok0, t0, n, [](int) { return 1.f; });
+    stage_rows<DK, PQ>(sm.kh, kr, [&](int r) { return __builtin_amdgcn_exp2f(cl - sm.c[r]); });
+    stage_rows<DK, PQ>(sm.qh, qr, [&](int r) { return __builtin_amdgcn_exp2f(sm.c[r]); });
+    stage_rows<DV, PV>(sm.v, vr, [](int) { return 1.f; });
+    stage_rows<DV, PV>(sm.dO, dr, [](int) { return 1.f; });
     __syncthreads();
     const size_t base = (seq * a.nch + ch) * size_t(DK) * DV;
     // wave w: key rows 32 w .. 32 w + 31 of dS = Kh^T V and G = Qh^T dO
@@ -193,20 +217,36 @@ __global__ __launch_bounds__(NT) void ssd_bwd_grads_kernel(SbArgs a) {
     const size_t seq = blockIdx.x / a.nch;
     const int ch = blockIdx.x % a.nch, t0 = ch * C, n = min(C, a.N - t0);
     const size_t tok0 = seq * size_t(a.N);
+    // every load of the chunk first (q, k, v, dO, S_in, dS_out), then the LDS copies
+    RowPieces<DK> qr, kr;
+    RowPieces<DV> vr, dr;
+    fetch_rows(qr, a.q, tok0, t0, n);
+    fetch_rows(kr, a.k, tok0, t0, n);
+    fetch_rows(vr, a.v, tok0, t0, n);
+    fetch_rows(dr, a.dO, tok0, t0, n);
+    constexpr int NS = DK * DV / 4 / NT;   // float4 pieces of S_in (and of dS_out) per thread
+    float4 s4v[NS], d4v[NS];
+    const size_t base = (seq * a.nch + ch) * size_t(DK) * DV;
+#pragma unroll
+    for (int x = 0; x < NS; ++x) {
+        const size_t p = size_t(tid + NT * x);
+        s4v[x] = *reinterpret_cast<const float4*>(a.Sst + base + 4 * p);
+        d4v[x] = *reinterpret_cast<const float4*>(a.dSt + base + 4 * p);
+    }
     chunk_logs<GB>(sm.c, a, tok0, t0, n);
     if (tid < C) { sm.alpha[tid] = 0.f; sm.beta[tid] = 0.f; }
-    stage_rows<DK, PQ>(sm.q, a.q, tok0, t0, n, [](int) { return 1.f; });
-    stage_rows<DK, PQ>(sm.k, a.k, tok0, t0, n, [](int) { return 1.f; });
-    stage_rows<DV, PV>(sm.v, a.v, tok0, t0, n, [](int) { return 1.f; });
-    stage_rows<DV, PV>(sm.dO, a.dO, tok0, t0, n, [](int) { return 1.f; });
+    stage_rows<DK, PQ>(sm.q, qr, [](int) { return 1.f; });
+    stage_rows<DK, PQ>(sm.k, kr, [](int) { return 1.f; });
+    stage_rows<DV, PV>(sm.v, vr, [](int) { return 1.f; });
+    stage_rows<DV, PV>(sm.dO, dr, [](int) { return 1.f; });
     // S_in and dS_out (fp32 in the workspace) as bf16 tiles, and gamma = <dS_out, S_in>
     {
-        const size_t base = (seq * a.nch + ch) * size_t(DK) * DV;
         float gam = 0.f;
-        for (int p = tid; p < DK * DV / 4; p += NT) {
+#pragma unroll
+        for (int x = 0; x < NS; ++x) {
+            const int p = tid + NT * x;
             const int i = (4 * p) / DV, j = (4 * p) % DV;
-            const float4 s4 = *reinterpret_cast<const float4*>(a.Sst + base + 4 * size_t(p));
-            const float4 d4 = *reinterpret_cast<const float4*>(a.dSt + base + 4 * size_t(p));
+            const float4 s4 = s4v[x], d4 = d4v[x];
             gam += s4.x * d4.x + s4.y * d4.y + s4.z * d4.z + s4.w * d4.w;
             *reinterpret_cast<uint2*>(sm.sin + i * PV + j) =
                 make_uint2(pack_bf16x2(s4.x, s4.y), pack_bf16x2(s4.z, s4.w));
