@@ -36,6 +36,7 @@
 // identity steps: zero key and value, gate 1, beta 0.
 #include "common.hpp"
 #include "la_internal.h"
+#include "mfma.hpp"
 
 namespace la {
 namespace {
@@ -90,36 +91,94 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
 
     const int r_me = tid / VT, c_me = tid % VT;  // (row, column) of this thread's output
     const int nchunks = (len + C - 1) / C;
-    for (int ch = 0; ch < nchunks; ++ch) {
+
+    // A chunk's inputs are fetched as raw words one chunk ahead, while the chunk before it
+    // is processed, so that their latency is not paid once per chunk. The loads are
+    // unconditional (per-chunk buffer resources read zeros past the sequence's end) and
+    // of the storage width, chosen once for all of them.
+    constexpr int NQ = C * DK / NT;   // q / k elements per thread per chunk
+    static_assert(C * DK % NT == 0, "whole elements per thread");
+    struct Raw {
+        uint32_t q[NQ], k[NQ], g[CHG ? NQ : 1], v, gs, bs;
+    };
+    const uint32_t es = iob ? 2u : 4u, gsz = gb ? 2u : 4u;
+    auto fetch = [&](Raw& R, int ch) {
+        const int t0 = ch * C;
+        const uint32_t rows = uint32_t(max(0, min(C, len - t0)));
+        const size_t tk = tok0 + size_t(t0);
+        const rsrc_t rq = make_rsrc(static_cast<const char*>(a.q) + tk * DK * es, rows * DK * es);
+        const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + tk * DK * es, rows * DK * es);
+        const rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) + tk * DV * es, rows * DV * es);
+        const rsrc_t rg = make_rsrc(a.g ? static_cast<const char*>(a.g) + tk * (CHG ? DK : 1) * gsz : nullptr,
+                                    a.g ? rows * (CHG ? DK : 1) * gsz : 0u);
+        const rsrc_t rb = make_rsrc(a.beta ? static_cast<const char*>(a.beta) + tk * gsz : nullptr,
+                                    a.beta ? rows * gsz : 0u);
+        const uint32_t ov = uint32_t(r_me * DV + c0 + c_me);
+        const uint32_t ot = uint32_t(tid < C ? tid : 0);
+        if (iob) {
+#pragma unroll
+            for (int x = 0; x < NQ; ++x) {
+                const uint32_t idx = uint32_t(tid + NT * x);
+                R.q[x] = buf_ld2(rq, idx * 2u);
+                R.k[x] = buf_ld2(rk, idx * 2u);
+            }
+            R.v = buf_ld2(rv, ov * 2u);
+        } else {
+#pragma unroll
+            for (int x = 0; x < NQ; ++x) {
+                const uint32_t idx = uint32_t(tid + NT * x);
+                R.q[x] = buf_ld4(rq, idx * 4u);
+                R.k[x] = buf_ld4(rk, idx * 4u);
+            }
+            R.v = buf_ld4(rv, ov * 4u);
+        }
+        if (gb) {
+            if (CHG) {
+#pragma unroll
+                for (int x = 0; x < NQ; ++x) R.g[x] = buf_ld2(rg, uint32_t(tid + NT * x) * 2u);
+            }
+            if (SCL) R.gs = buf_ld2(rg, ot * 2u);
+            if (DLT) R.bs = buf_ld2(rb, ot * 2u);
+        } else {
+            if (CHG) {
+#pragma unroll
+                for (int x = 0; x < NQ; ++x) R.g[x] = buf_ld4(rg, uint32_t(tid + NT * x) * 4u);
+            }
+            if (SCL) R.gs = buf_ld4(rg, ot * 4u);
+            if (DLT) R.bs = buf_ld4(rb, ot * 4u);
+        }
+    };
+    auto word = [](uint32_t w, bool bf) { return bf ? __uint_as_float(w << 16) : __uint_as_float(w); };
+
+    auto body = [&](const Raw& R, Raw& Rn, int ch) {
         const int t0 = ch * C;
         const int n = min(C, len - t0);
         __syncthreads();  // previous chunk's readers of sQ/sK/sV/sS are done
-        for (int idx = tid; idx < C * DK; idx += NT) {
+#pragma unroll
+        for (int x = 0; x < NQ; ++x) {
+            const int idx = tid + NT * x;
             const int r = idx / DK, i = idx % DK;
             float qv = 0.f, kv = 0.f, lg = 0.f;
             if (r < n) {
-                const size_t e = (tok0 + t0 + r) * DK + i;
-                qv = load_elem(a.q, e, iob);
-                kv = load_elem(a.k, e, iob);
+                qv = word(R.q[x], iob);
+                kv = word(R.k[x], iob);
                 if (VAR == LA_KATH) {
                     qv = elu_plus_one(qv);
                     kv = elu_plus_one(kv);
                 }
-                if (CHG) lg = logf(load_elem(a.g, e, gb));
+                if (CHG) lg = logf(word(R.g[x], gb));
             }
             sQ[r][i] = qv;
             sK[r][i] = kv;
             if (CHG) sLg[r][i] = lg;
         }
-        {
-            const int r = r_me, c = c_me;
-            sV[r][c] = r < n ? load_elem(a.v, (tok0 + t0 + r) * DV + c0 + c, iob) : 0.f;
-        }
+        sV[r_me][c_me] = r_me < n ? word(R.v, iob) : 0.f;
         if ((DLT || SCL) && tid < C) {
             const int r = tid;
-            if (SCL) sc[r] = r < n ? logf(load_elem(a.g, tok0 + t0 + r, gb)) : 0.f;
-            if (DLT) sbeta[r] = r < n ? load_elem(a.beta, tok0 + t0 + r, gb) : 0.f;
+            if (SCL) sc[r] = r < n ? logf(word(R.gs, gb)) : 0.f;
+            if (DLT) sbeta[r] = r < n ? word(R.bs, gb) : 0.f;
         }
+        if (ch + 1 < nchunks) fetch(Rn, ch + 1);
         __syncthreads();
         // in-chunk cumulative log gates
         if (CHG) {
@@ -245,6 +304,14 @@ __global__ __launch_bounds__(NT) void prefill_valu_kernel(ValuArgs a) {
                 sz[i] += acc;
             }
         }
+    };
+    // two sets of raw words, swapped by unrolling
+    Raw RA, RB;
+    if (nchunks > 0) fetch(RA, 0);
+    for (int ch = 0; ch < nchunks; ch += 2) {
+        body(RA, RB, ch);
+        if (ch + 1 >= nchunks) break;
+        body(RB, RA, ch + 1);
     }
     __syncthreads();
     for (int idx = tid; idx < DK * VT; idx += NT) {
