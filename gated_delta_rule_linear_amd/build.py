@@ -30,6 +30,7 @@ COMMON = [
 
 SOURCES = ["la_api.cpp", "decode.hip", "prefill_valu.hip", "prefill_kath_mfma.hip", "prefill_kda_mfma.hip",
            "selective_scan.hip", "backward_valu.hip", "backward_gdn_valu.hip", "backward_ssd_mfma.hip",
+           "backward_gdn_mfma.hip",
            "prefill_gla_mfma.hip", "prefill_gdn_mfma.hip", "noalloc.hip", "stream_rmw.hip",
            "prefill_ssd_mfma.hip"]
 

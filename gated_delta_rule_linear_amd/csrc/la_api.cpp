@@ -359,8 +359,8 @@ int la_decode_step(const la_desc* d, const void* q, const void* k, const void* v
 }
 
 // Backward: the forward's descriptor and a variant with a backward kernel. Path AUTO takes
-// the matrix-core backward where the shape allows it (SSD, bf16, d_k = 128, d_v = 64),
-// else the fp32 VALU backward.
+// the matrix-core backward where the shape allows it (bf16 q, k, v; SSD with d_k = 128,
+// d_v = 64; GDN with d_k = 128, d_v = 64 or 128), else the fp32 VALU backward.
 static int check_backward_desc(const la_desc* d, la::Problem& p) {
     int rc = check_desc(d, false);
     if (rc != LA_OK) return rc;
@@ -370,7 +370,7 @@ static int check_backward_desc(const la_desc* d, la::Problem& p) {
     p.io_bf16 = d->io_dtype == LA_BF16;
     p.gate_bf16 = d->gate_dtype == LA_BF16;
     p.eps = d->eps;
-    const bool mfma_ok = la::ssd_backward_mfma_supported(p);
+    const bool mfma_ok = la::ssd_backward_mfma_supported(p) || la::gdn_backward_mfma_supported(p);
     if (d->path == LA_PATH_MFMA && !mfma_ok) return LA_ERR_UNSUPPORTED;
     p.path = (d->path != LA_PATH_VALU && mfma_ok) ? LA_PATH_MFMA : LA_PATH_VALU;
     p.chunk = p.path == LA_PATH_MFMA ? la::kMfmaChunk : la::kValuChunk;
@@ -379,8 +379,9 @@ static int check_backward_desc(const la_desc* d, la::Problem& p) {
 }
 
 static size_t backward_workspace(const la::Problem& p) {
-    return p.path == LA_PATH_MFMA ? la::ssd_backward_mfma_workspace_bytes(p)
-                                  : la::backward_workspace_bytes(p);
+    if (p.path != LA_PATH_MFMA) return la::backward_workspace_bytes(p);
+    return p.variant == LA_GDN ? la::gdn_backward_mfma_workspace_bytes(p)
+                               : la::ssd_backward_mfma_workspace_bytes(p);
 }
 
 int la_prefill_backward_workspace_size(const la_desc* d, size_t* bytes) {
@@ -448,8 +449,11 @@ int la_prefill_backward(const la_desc* d, const void* q, const void* k, const vo
     bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dbeta = dbeta; bp.dS0 = dS0;
     bp.dz_final = dz_final; bp.dz0 = dz0;
     (void)hipGetLastError();
-    hipError_t err = (p.path == LA_PATH_MFMA && p.N > 0) ? la::launch_backward_ssd_mfma(bp)
-                                                         : la::launch_backward(bp);
+    hipError_t err = hipSuccess;
+    if (p.path == LA_PATH_MFMA && p.N > 0)
+        err = p.variant == LA_GDN ? la::launch_backward_gdn_mfma(bp) : la::launch_backward_ssd_mfma(bp);
+    else
+        err = la::launch_backward(bp);
     if (err == hipSuccess) err = hipGetLastError();
     return err == hipSuccess ? LA_OK : LA_ERR_HIP;
 }

@@ -91,6 +91,10 @@ hipError_t launch_backward_gdn(const BwdProblem& p);
 bool ssd_backward_mfma_supported(const Problem& p);
 size_t ssd_backward_mfma_workspace_bytes(const Problem& p);
 hipError_t launch_backward_ssd_mfma(const BwdProblem& p);
+// backward_gdn_mfma.hip (GDN backward on the matrix cores: bf16, d_k = 128, d_v = 64 or 128)
+bool gdn_backward_mfma_supported(const Problem& p);
+size_t gdn_backward_mfma_workspace_bytes(const Problem& p);
+hipError_t launch_backward_gdn_mfma(const BwdProblem& p);
 
 // selective_scan.hip (Mamba-1 selective scan), a validated call
 struct ScanProblem {

@@ -171,11 +171,30 @@ def test_backward_ssd_matrix_cores_vs_valu(N):
         assert relerr(got[name], getattr(valu, name).double().cpu().numpy()) <= TOL["bf16"], name
 
 
+@pytest.mark.parametrize("dv,N,with_state", [(128, 64, True), (128, 200, True), (128, 257, False),
+                                            (64, 130, True), (64, 1, True)])
+def test_backward_gdn_matrix_cores_vs_valu(dv, N, with_state):
+    """The matrix-core GDN backward (bf16, d_k = 128, chunk 64) against the oracle and
+    against the fp32 VALU backward on the same inputs: several chunks, ragged tails, one
+    token, with and without an initial state."""
+    inp, dO, dO_x, dSf, dSf_x = make_case("gdn", 2, 3, N, 128, dv, "bf16", seed=N + dv,
+                                          with_state=with_state)
+    banner(f"backward gdn matrix cores dv={dv} N={N} S0={with_state}")
+    got, ref = run_both("gdn", inp, dO, dO_x, dSf, dSf_x)
+    check(got, ref, TOL["bf16"])
+    d = {k: dev(v) for k, v in inp.dev.items()}
+    valu = bd.prefill_backward(d["q"], d["k"], d["v"], d["g"], dev(dO), variant="gdn",
+                               beta=d["beta"], S0=d.get("S0"), dS_final=dev(dSf), path="valu")
+    torch.cuda.synchronize()
+    for name in ("dq", "dk", "dv", "dg", "dbeta", "dS0"):
+        assert relerr(got[name], getattr(valu, name).double().cpu().numpy()) <= TOL["bf16"], name
+
+
 @pytest.mark.parametrize("variant,dk,dv,N,path", [
     ("kath", 64, 32, 53, "auto"), ("gla", 64, 32, 53, "auto"), ("ssd", 64, 32, 53, "auto"),
     ("gdn", 64, 32, 53, "auto"), ("kda", 64, 32, 53, "auto"),
-    # the matrix-core SSD backward (bf16, d_k = 128, d_v = 64): several chunks and a tail
-    ("ssd", 128, 64, 200, "mfma")])
+    # the matrix-core backwards (bf16, d_k = 128): several chunks and a tail
+    ("ssd", 128, 64, 200, "mfma"), ("gdn", 128, 128, 200, "mfma")])
 def test_backward_deterministic_and_batch_invariant(variant, dk, dv, N, path):
     """No atomics anywhere: two calls give the same bits, and a sequence's gradients do
     not depend on the other sequences of the batch (the same bits when it runs alone)."""
