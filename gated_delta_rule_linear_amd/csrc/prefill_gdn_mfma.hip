@@ -479,6 +479,21 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
             const uint16_t* tc = slot_(J).t;
             const uint16_t* vc = slot_(J).v;
             const float (*gc)[C] = gsl[j & 3];
+            // The chunk's value tile (transpose reads: lane j receives column 16 cb + j of
+            // rows 16 tb + 4 g .. + 3, the result-tile layout) and its gate factors, read
+            // before any LDS write of this step: the compiler keeps LDS reads behind earlier
+            // LDS writes it cannot tell apart, so read later each would be a round trip of
+            // its own on the chain's dependent path.
+            i16x4_t vx[4];
+            float4 g4[4], d4[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const uint16_t* p = vc + (16 * tb + 4 * g + (jl >> 2)) * VT + 16 * cb + 4 * (jl & 3);
+                vx[tb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+                g4[tb] = *reinterpret_cast<const float4*>(&gc[1][16 * tb + 4 * g]);
+                d4[tb] = *reinterpret_cast<const float4*>(&gc[2][16 * tb + 4 * g]);
+            }
+            const float glast = gc[1][C - 1];
             // S as B fragments (keys 32 kk + 8 g .. + 7), and S^T entering the chunk for
             // the output waves from the same words (row 16 cb + j, keys 32 kk + 8 g ..: the
             // output waves' A fragment (cb, kk) of lane 16 g + j)
@@ -506,8 +521,7 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) ks[tb] = mfma16(ka[tb & 1][kk], Sb[kk], ks[tb]);
             }
-            // T fragments and the value tile in the result-tile layout (transpose reads:
-            // lane j receives column 16 cb + j of rows 16 tb + 4 g .. + 3)
+            // T fragments
             bf16x8_t tf[6];
             const int pc[6] = {0, 2, 4, 5, 6, 7};   // piece 2 tb + kk of T
 #pragma unroll
@@ -517,13 +531,10 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
             f32x4_t X[4];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                const uint16_t* p = vc + (16 * tb + 4 * g + (jl >> 2)) * VT + 16 * cb + 4 * (jl & 3);
-                const i16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
-                const float4 g4 = *reinterpret_cast<const float4*>(&gc[1][16 * tb + 4 * g]);
-                const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
+                const float gv[4] = {g4[tb].x, g4[tb].y, g4[tb].z, g4[tb].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float v = __uint_as_float(uint32_t(uint16_t(x[e])) << 16);
+                    const float v = __uint_as_float(uint32_t(uint16_t(vx[tb][e])) << 16);
                     X[tb][e] = v - gv[e] * ks[tb][e];
                 }
             }
@@ -545,12 +556,10 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
                     pack_pk(u[2 * kk], u[2 * kk + 1]);
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                const float4 d4 = *reinterpret_cast<const float4*>(&gc[2][16 * tb + 4 * g]);
-                u[tb][0] *= d4.x; u[tb][1] *= d4.y; u[tb][2] *= d4.z; u[tb][3] *= d4.w;
+                u[tb][0] *= d4[tb].x; u[tb][1] *= d4[tb].y; u[tb][2] *= d4[tb].z; u[tb][3] *= d4[tb].w;
             }
             const bf16x8_t Ub0 = pack_pk(u[0], u[1]), Ub1 = pack_pk(u[2], u[3]);
             // S <- gamma_last S + K^T (d U)
-            const float glast = gc[1][C - 1];
             bf16x8_t kt[2][2];
             kt[0][0] = frag_kt(kc, 0, 0, 0, lane);
             kt[0][1] = frag_kt(kc, 1, 0, 0, lane);

@@ -549,27 +549,40 @@ __global__ __launch_bounds__(NTF) void kda_fwd_kernel(KdaArgs a) {
         }
         lds_barrier();
         load_part(Rl, ch + 2, 1);
-        // ---- U^T = X^T T^T for rows 16 rb ..
+        // ---- U^T = X^T T^T for rows 16 rb .. (every X fragment read before the first U
+        // row is written: the compiler keeps LDS reads behind LDS writes it cannot tell
+        // apart, which would make each column tile's reads a round trip of its own)
+        bf16x8_t xf[2][NVT];
 #pragma unroll
         for (int ct = 0; ct < NVT; ++ct) {
-            f32x4_t u_ = mfma16(frag_kr_cols<NVT>(sm.x, PV, 0, 0, ct, lane),
-                                __builtin_bit_cast(bf16x8_t, R.t[0]), zero4());
-            if (nk > 1)
-                u_ = mfma16(frag_kr_cols<NVT>(sm.x, PV, 32, 0, ct, lane),
-                            __builtin_bit_cast(bf16x8_t, R.t[1]), u_);
+            xf[0][ct] = frag_kr_cols<NVT>(sm.x, PV, 0, 0, ct, lane);
+            if (nk > 1) xf[1][ct] = frag_kr_cols<NVT>(sm.x, PV, 32, 0, ct, lane);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NVT; ++ct) {
+            f32x4_t u_ = mfma16(xf[0][ct], __builtin_bit_cast(bf16x8_t, R.t[0]), zero4());
+            if (nk > 1) u_ = mfma16(xf[1][ct], __builtin_bit_cast(bf16x8_t, R.t[1]), u_);
             store_rows<NVT>(sm.u, PV, 0, ct, 16 * rb, u_, lane);
         }
         lds_barrier();
         load_part(Rl, ch + 2, 2);
-        // ---- O^T = (S^T Q~^T) + U^T P^T -> o rows 16 rb ..
+        // ---- O^T = (S^T Q~^T) + U^T P^T -> o rows 16 rb .. (every U fragment of this
+        // and of the state update read first)
+        bf16x8_t pu[2][NVT], uf[2][NVT];
+#pragma unroll
+        for (int ct = 0; ct < NVT; ++ct) {
+            pu[0][ct] = frag_kr_cols_pk<NVT>(sm.u, PV, 0, 0, ct, lane);
+            if (nk > 1) pu[1][ct] = frag_kr_cols_pk<NVT>(sm.u, PV, 1, 0, ct, lane);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct) uf[kk][ct] = frag_kr_cols<NVT>(sm.u, PV, 32 * kk, 0, ct, lane);
         uint2 ow[NVT];
 #pragma unroll
         for (int ct = 0; ct < NVT; ++ct) {
-            f32x4_t o_ = mfma16(frag_kr_cols_pk<NVT>(sm.u, PV, 0, 0, ct, lane),
-                                __builtin_bit_cast(bf16x8_t, R.p[0]), oq[ct]);
-            if (nk > 1)
-                o_ = mfma16(frag_kr_cols_pk<NVT>(sm.u, PV, 1, 0, ct, lane),
-                            __builtin_bit_cast(bf16x8_t, R.p[1]), o_);
+            f32x4_t o_ = mfma16(pu[0][ct], __builtin_bit_cast(bf16x8_t, R.p[0]), oq[ct]);
+            if (nk > 1) o_ = mfma16(pu[1][ct], __builtin_bit_cast(bf16x8_t, R.p[1]), o_);
             ow[ct].x = pack_bf16x2(o_[0], o_[1]);
             ow[ct].y = pack_bf16x2(o_[2], o_[3]);
         }
@@ -579,11 +592,6 @@ __global__ __launch_bounds__(NTF) void kda_fwd_kernel(KdaArgs a) {
             else buf_st8(ro, oo, ow[0]);
         }
         // ---- S = Diag(G_last) S + K^^T U (key rows 32 rb ..), bf16 copy to st
-        bf16x8_t uf[2][NVT];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int ct = 0; ct < NVT; ++ct) uf[kk][ct] = frag_kr_cols<NVT>(sm.u, PV, 32 * kk, 0, ct, lane);
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
             const f32x4_t av = {R.a[ib].x, R.a[ib].y, R.a[ib].z, R.a[ib].w};

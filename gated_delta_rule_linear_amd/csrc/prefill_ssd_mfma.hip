@@ -187,24 +187,42 @@ __global__ __launch_bounds__(NT) void ssd_chain_kernel(SsdArgs a) {
         load(Rl, lc + 2);
         const uint16_t* kc = sm.k[cur];
         const float* cc = sm.c[cur];
+        // the chunk's decay sums and the state update's operands, read before any LDS write
+        // of this chunk: the compiler keeps LDS reads behind LDS writes it cannot tell
+        // apart, so read later each would wait a round trip of its own
+        float4 c4[4];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) c4[sb] = *reinterpret_cast<const float4*>(cc + 16 * sb + 4 * g);
+        const float cr = cc[rw], clast = cc[C - 1];
+        bf16x8_t vf[2][NVT], ktf[2][2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct) vf[kk][ct] = frag_kr_cols<NVT>(sm.vh[cur], PV, 32 * kk, 0, ct, lane);
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+            const int i0 = 16 * (2 * w + ib);
+            ktf[ib][0] = frag_kr(kc, PQ, 0, i0, lane);
+            ktf[ib][1] = frag_kr(kc, PQ, 32, i0, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep these reads issued here
         if (OUT) {
             // score tiles P^T[s][r] for this wave's rows r = 16 w + j (s <= r): A = K rows
-            // s, B = q's fragments, then the decay 2^{c_r - c_s} and the causal mask
+            // s, B = q's fragments, then the decay 2^{c_r - c_s} and the causal mask. Every
+            // wave forms all four tiles (the masked ones come out zero): the wave with the
+            // most rows sets the chunk's length either way, and without a branch on the wave
+            // index the compiler schedules the whole chunk as one block.
             f32x4_t pt[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
-                if (sb > w) break;
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
                     pt[sb] = mfma16(frag_kc(kc, PQ, 16 * sb, 32 * kk, lane),
                                     __builtin_bit_cast(bf16x8_t, R.qf[kk]), pt[sb]);
             }
-            const float cr = cc[rw];
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
-                if (sb > w) break;
-                const float4 c4 = *reinterpret_cast<const float4*>(cc + 16 * sb + 4 * g);
-                const float csv[4] = {c4.x, c4.y, c4.z, c4.w};
+                const float csv[4] = {c4[sb].x, c4[sb].y, c4[sb].z, c4[sb].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int s = 16 * sb + 4 * g + e;
@@ -216,17 +234,24 @@ __global__ __launch_bounds__(NT) void ssd_chain_kernel(SsdArgs a) {
             const uint16_t* vv = sm.v[cur];
             // O^T = 2^{c_r} S^T q^T + V^T P^T for rows 16 w ..; 4 NVT contiguous columns
             // per lane
+            bf16x8_t sfr[NVT][DK / 32], pv[2][NVT];
+#pragma unroll
+            for (int ct = 0; ct < NVT; ++ct) {
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) sfr[ct][kk] = frag_st<NVT>(sm.st[cur], PQ, 0, ct, 32 * kk, lane);
+                pv[0][ct] = frag_kr_cols_pk<NVT>(vv, PV, 0, 0, ct, lane);
+                pv[1][ct] = frag_kr_cols_pk<NVT>(vv, PV, 1, 0, ct, lane);
+            }
             uint2 ow[NVT];
 #pragma unroll
             for (int ct = 0; ct < NVT; ++ct) {
                 f32x4_t o_ = zero4();
 #pragma unroll
                 for (int kk = 0; kk < DK / 32; ++kk)
-                    o_ = mfma16(frag_st<NVT>(sm.st[cur], PQ, 0, ct, 32 * kk, lane),
-                                __builtin_bit_cast(bf16x8_t, R.qf[kk]), o_);
+                    o_ = mfma16(sfr[ct][kk], __builtin_bit_cast(bf16x8_t, R.qf[kk]), o_);
                 o_ *= er;
-                o_ = mfma16(frag_kr_cols_pk<NVT>(vv, PV, 0, 0, ct, lane), pf0, o_);
-                if (w >= 2) o_ = mfma16(frag_kr_cols_pk<NVT>(vv, PV, 1, 0, ct, lane), pf1, o_);
+                o_ = mfma16(pv[0][ct], pf0, o_);
+                o_ = mfma16(pv[1][ct], pf1, o_);   // pf1 is zero for w < 2
                 ow[ct].x = pack_bf16x2(o_[0], o_[1]);
                 ow[ct].y = pack_bf16x2(o_[2], o_[3]);
             }
@@ -241,22 +266,16 @@ __global__ __launch_bounds__(NT) void ssd_chain_kernel(SsdArgs a) {
             }
         }
         // S = 2^{c_last} S + K^T V^ (key rows 32 w ..)
-        const float al = __builtin_amdgcn_exp2f(cc[C - 1]);
+        const float al = __builtin_amdgcn_exp2f(clast);
         if (!OUT) aprod *= al;
-        bf16x8_t vf[2][NVT];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int ct = 0; ct < NVT; ++ct) vf[kk][ct] = frag_kr_cols<NVT>(sm.vh[cur], PV, 32 * kk, 0, ct, lane);
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
             const int i0 = 16 * (2 * w + ib);
-            const bf16x8_t kt0 = frag_kr(kc, PQ, 0, i0, lane), kt1 = frag_kr(kc, PQ, 32, i0, lane);
 #pragma unroll
             for (int ct = 0; ct < NVT; ++ct) {
                 f32x4_t s_ = S[ib][ct] * al;
-                s_ = mfma16(kt0, vf[0][ct], s_);
-                s_ = mfma16(kt1, vf[1][ct], s_);
+                s_ = mfma16(ktf[ib][0], vf[0][ct], s_);
+                s_ = mfma16(ktf[ib][1], vf[1][ct], s_);
                 S[ib][ct] = s_;
                 if (OUT) store_st<NVT>(sm.st[cur ^ 1], PQ, i0, 0, ct, s_, lane);
             }
