@@ -418,6 +418,7 @@ struct __align__(16) GradSmem {
             __align__(16) uint16_t v[C * PC], dO[C * PC];      // [token][column]
             __align__(16) uint16_t s0[HV * PQ], ds[HV * PQ];   // S_in^T, dS_out^T [column][key]
             __align__(16) uint16_t xu[HV * PC], rd[HV * PC];   // X^T then U^T, R^T then dU^T
+            __align__(16) uint16_t us[HV * PC], dus[HV * PC];  // (diag(el) U)^T, (-diag(beta eg) dU)^T
         } h;
         struct {   // after both halves
             __align__(16) uint16_t adT[C * PC];   // (D o A)^T [s][t]
@@ -475,37 +476,51 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_mfma(GbArgs a) {
     blk_stage<C, DK, PQ>(sm.k, kb);
     blk_stage<C, C, PC>(sm.t, tb);
     __syncthreads();
-    // Q K^T and K K^T, rows 16 w ..; P^T to LDS
-    f32x4_t qk[4], kk[4];
+    // Q K^T, rows 16 w ..; P^T to LDS
+    f32x4_t qk[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) qk[nt] = kk[nt] = zero4();
+    for (int nt = 0; nt < 4; ++nt) qk[nt] = zero4();
 #pragma unroll
     for (int kc = 0; kc < DK / 32; ++kc) {
-        const bf16x8_t ak = frag_kc(sm.k, PQ, 16 * w, 32 * kc, lane);
         const bf16x8_t aq = frag_kc(sm.q, PQ, 16 * w, 32 * kc, lane);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            const bf16x8_t bk = frag_kc(sm.k, PQ, 16 * nt, 32 * kc, lane);
-            kk[nt] = mfma16(ak, bk, kk[nt]);
-            qk[nt] = mfma16(aq, bk, qk[nt]);
-        }
+        for (int nt = 0; nt < 4; ++nt)
+            qk[nt] = mfma16(aq, frag_kc(sm.k, PQ, 16 * nt, 32 * kc, lane), qk[nt]);
     }
     const float* cc = sm.c;
     const float* bb = sm.b;
+    // The lane's gate factors, read once before any LDS write: LDS reads issued after an LDS
+    // write the compiler cannot tell apart wait for it, one round trip each. Rows r = 16 w +
+    // 4 g + e (the result-tile rows), columns s = 16 nt + j.
     const float cl = cc[C - 1];
+    float cr[4], br[4], cmr[4], egr[4], elr[4], cs4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int r = 16 * w + 4 * g + e;
+        cr[e] = cc[r];
+        br[e] = bb[r];
+        cmr[e] = r > 0 ? cc[r - 1] : 0.f;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) cs4[nt] = cc[16 * nt + jl];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        egr[e] = __builtin_amdgcn_exp2f(cr[e]);
+        elr[e] = __builtin_amdgcn_exp2f(cl - cr[e]);
+    }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
         f32x4_t pv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * w + 4 * g + e, s = 16 * nt + jl;
-            pv[e] = s <= r ? __builtin_amdgcn_exp2f(cc[r] - cc[s]) * qk[nt][e] : 0.f;
+            pv[e] = s <= r ? __builtin_amdgcn_exp2f(cr[e] - cs4[nt]) * qk[nt][e] : 0.f;
         }
         store_dT(sm.pt, PC, 16 * w, 16 * nt, pv, lane);
     }
-    f32x4_t dq[8], dk1[8], dk2[8], A[4], Bm[4];
+    f32x4_t dq[8], dk1[8], A[4], Bm[4];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) dq[nt] = dk1[nt] = dk2[nt] = zero4();
+    for (int nt = 0; nt < 8; ++nt) dq[nt] = dk1[nt] = zero4();
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) A[nt] = Bm[nt] = zero4();
     float kap[4] = {}, rho[4] = {}, mu[4] = {}, vdu[4] = {};
@@ -551,17 +566,23 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_mfma(GbArgs a) {
                 for (int ct = 0; ct < 4; ++ct)
                     pd[ct] = mfma16(ap, frag_kr(sm.h.dO, PC, 32 * kc, 16 * ct, lane), pd[ct]);
             }
+            float vv[4][4], dd[4][4];   // v and dO of the lane's tile entries, read first
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * w + 4 * g + e, j = 16 * ct + jl;
+                    vv[ct][e] = bf16_to_f32(sm.h.v[r * PC + j]);
+                    dd[ct][e] = bf16_to_f32(sm.h.dO[r * PC + j]);
+                }
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
                 f32x4_t xv, rv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * w + 4 * g + e, j = 16 * ct + jl;
-                    const float vv = bf16_to_f32(sm.h.v[r * PC + j]);
-                    const float dd = bf16_to_f32(sm.h.dO[r * PC + j]);
-                    rho[e] += qs[ct][e] * dd;
-                    xv[e] = bb[r] * (vv - __builtin_amdgcn_exp2f(cc[r]) * ks[ct][e]);
-                    rv[e] = __builtin_amdgcn_exp2f(cl - cc[r]) * kd[ct][e] + pd[ct][e];
+                    rho[e] += qs[ct][e] * dd[ct][e];
+                    xv[e] = br[e] * (vv[ct][e] - egr[e] * ks[ct][e]);
+                    rv[e] = elr[e] * kd[ct][e] + pd[ct][e];
                 }
                 store_dT(sm.h.xu, PC, 16 * w, 16 * ct, xv, lane);
                 store_dT(sm.h.rd, PC, 16 * w, 16 * ct, rv, lane);
@@ -581,6 +602,8 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_mfma(GbArgs a) {
                     du[ct] = mfma16(att, frag_kc(sm.h.rd, PC, 16 * ct, 32 * kc, lane), du[ct]);
                 }
             }
+            // dv rows past the sequence's end fall outside the resource and are dropped
+            const rsrc_t rdv = make_rsrc(a.dv + tok * DV + h * HV, uint32_t((n - 1) * DV + HV) * 2u);
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
@@ -588,8 +611,8 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_mfma(GbArgs a) {
                     const int r = 16 * w + 4 * g + e, j = 16 * ct + jl;
                     kap[e] += kd[ct][e] * u[ct][e];
                     mu[e] += ks[ct][e] * du[ct][e];
-                    vdu[e] += bf16_to_f32(sm.h.v[r * PC + j]) * du[ct][e];
-                    if (r < n) a.dv[(tok + r) * DV + h * HV + j] = f32_to_bf16(bb[r] * du[ct][e]);
+                    vdu[e] += vv[ct][e] * du[ct][e];
+                    buf_st2(rdv, uint32_t(r * DV + j) * 2u, f32_to_bf16(br[e] * du[ct][e]));
                 }
             }
             lds_barrier();   // X^T and R^T are read; U^T and dU^T take their place
@@ -597,6 +620,14 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_mfma(GbArgs a) {
             for (int ct = 0; ct < 4; ++ct) {
                 store_dT(sm.h.xu, PC, 16 * w, 16 * ct, u[ct], lane);
                 store_dT(sm.h.rd, PC, 16 * w, 16 * ct, du[ct], lane);
+                f32x4_t us_, dus_;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    us_[e] = elr[e] * u[ct][e];
+                    dus_[e] = -br[e] * egr[e] * du[ct][e];
+                }
+                store_dT(sm.h.us, PC, 16 * w, 16 * ct, us_, lane);
+                store_dT(sm.h.dus, PC, 16 * w, 16 * ct, dus_, lane);
             }
         }
         lds_barrier();
@@ -604,8 +635,9 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_mfma(GbArgs a) {
 #pragma unroll
         for (int kc = 0; kc < HV / 32; ++kc) {
             const bf16x8_t ado = frag_kc(sm.h.dO, PC, 16 * w, 32 * kc, lane);
-            const bf16x8_t au = frag_kr(sm.h.xu, PC, 32 * kc, 16 * w, lane);
             const bf16x8_t adu = frag_kr(sm.h.rd, PC, 32 * kc, 16 * w, lane);
+            const bf16x8_t aus = frag_kr(sm.h.us, PC, 32 * kc, 16 * w, lane);
+            const bf16x8_t adus = frag_kr(sm.h.dus, PC, 32 * kc, 16 * w, lane);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 const bf16x8_t bu = frag_kr(sm.h.xu, PC, 32 * kc, 16 * nt, lane);
@@ -617,8 +649,8 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_mfma(GbArgs a) {
                 const bf16x8_t bs = frag_kr(sm.h.s0, PQ, 32 * kc, 16 * nt, lane);
                 const bf16x8_t bd = frag_kr(sm.h.ds, PQ, 32 * kc, 16 * nt, lane);
                 dq[nt] = mfma16(ado, bs, dq[nt]);
-                dk1[nt] = mfma16(au, bd, dk1[nt]);
-                dk2[nt] = mfma16(adu, bs, dk2[nt]);
+                dk1[nt] = mfma16(aus, bd, dk1[nt]);
+                dk1[nt] = mfma16(adus, bs, dk1[nt]);
             }
         }
         lds_barrier();   // the half's tiles are read
@@ -638,6 +670,22 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_mfma(GbArgs a) {
     sig = wave_sum(sig);
     if (lane == 0) sm.sig[w] = sig;
     {
+        // Q K^T and K K^T of the wave's rows again (q and k are still in LDS): formed anew
+        // here rather than held in registers through the halves
+        f32x4_t qk[4], kk[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) qk[nt] = kk[nt] = zero4();
+#pragma unroll
+        for (int kc = 0; kc < DK / 32; ++kc) {
+            const bf16x8_t ak = frag_kc(sm.k, PQ, 16 * w, 32 * kc, lane);
+            const bf16x8_t aq = frag_kc(sm.q, PQ, 16 * w, 32 * kc, lane);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const bf16x8_t bk = frag_kc(sm.k, PQ, 16 * nt, 32 * kc, lane);
+                kk[nt] = mfma16(ak, bk, kk[nt]);
+                qk[nt] = mfma16(aq, bk, qk[nt]);
+            }
+        }
         float dbp[4] = {}, dupp[4] = {};
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
@@ -645,12 +693,11 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_mfma(GbArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * w + 4 * g + e, s = 16 * nt + jl;
-                const float d = s <= t ? __builtin_amdgcn_exp2f(cc[t] - cc[s]) : 0.f;
-                const float cm = t > 0 ? cc[t - 1] : 0.f;
-                const float dmv = s < t ? __builtin_amdgcn_exp2f(cm - cc[s]) : 0.f;
+                const float d = s <= t ? __builtin_amdgcn_exp2f(cr[e] - cs4[nt]) : 0.f;
+                const float dmv = s < t ? __builtin_amdgcn_exp2f(cmr[e] - cs4[nt]) : 0.f;
                 const float kb2 = kk[nt][e] * Bm[nt][e];
                 ad[e] = d * A[nt][e];
-                mb[e] = s < t ? -bb[t] * d * Bm[nt][e] : 0.f;
+                mb[e] = s < t ? -br[e] * d * Bm[nt][e] : 0.f;
                 if (s < t) dbp[e] += d * kb2;
                 dupp[e] += dmv * kb2;
                 h1[e] = qk[nt][e] * A[nt][e];
@@ -669,25 +716,31 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_mfma(GbArgs a) {
                 sm.dup[16 * w + 4 * g + e] = y;
             }
         }
-        for (int idx = tid; idx < C * C; idx += NT) {
-            const int t = idx / C, s = idx % C;
-            const float cm = t > 0 ? cc[t - 1] : 0.f;
-            sm.f.dm[t * PC + s] = f32_to_bf16(s < t ? __builtin_amdgcn_exp2f(cm - cc[s]) : 0.f);
+        {   // Dm: thread tid fills column s = tid mod C of rows tid / C + 4 i (every read first)
+            static_assert(NT % C == 0, "whole rows per pass");
+            constexpr int NI = C * C / NT;
+            const int s = tid % C, t0r = tid / C;
+            const float csv = cc[s];
+            float cmv[NI];
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int t = t0r + (NT / C) * i;
+                cmv[i] = t > 0 ? cc[t - 1] : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int t = t0r + (NT / C) * i;
+                sm.f.dm[t * PC + s] = f32_to_bf16(s < t ? __builtin_amdgcn_exp2f(cmv[i] - csv) : 0.f);
+            }
         }
     }
     lds_barrier();
     // dq = diag(eg) (dO S_in^T) + (D o A) K; dk = diag(el) (U dS_out^T) - diag(beta eg)
     // (dU S_in^T) + (D o A)^T Q - Mb K - Mb^T K (rows 16 w ..)
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
+    for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * w + 4 * g + e;
-            const float eg = __builtin_amdgcn_exp2f(cc[r]);
-            dq[nt][e] *= eg;
-            dk1[nt][e] = __builtin_amdgcn_exp2f(cl - cc[r]) * dk1[nt][e] - bb[r] * eg * dk2[nt][e];
-        }
-    }
+        for (int e = 0; e < 4; ++e) dq[nt][e] *= egr[e];   // dk1 took its row factors on the way in
 #pragma unroll
     for (int kc = 0; kc < C / 32; ++kc) {
         const bf16x8_t aad = frag_kr(sm.f.adT, PC, 32 * kc, 16 * w, lane);
@@ -704,15 +757,16 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_mfma(GbArgs a) {
             dk1[nt] = mfma16(ambt, bk, dk1[nt]);
         }
     }
+    {   // rows past the sequence's end fall outside the resources and are dropped
+        const rsrc_t rdq = make_rsrc(a.dq + tok * DK, uint32_t(n) * DK * 2u);
+        const rsrc_t rdk = make_rsrc(a.dk + tok * DK, uint32_t(n) * DK * 2u);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
+        for (int nt = 0; nt < 8; ++nt) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * w + 4 * g + e;
-            if (r < n) {
-                const size_t o = (tok + r) * DK + 16 * nt + jl;
-                a.dq[o] = f32_to_bf16(dq[nt][e]);
-                a.dk[o] = f32_to_bf16(dk1[nt][e]);
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t o = uint32_t((16 * w + 4 * g + e) * DK + 16 * nt + jl) * 2u;
+                buf_st2(rdq, o, f32_to_bf16(dq[nt][e]));
+                buf_st2(rdk, o, f32_to_bf16(dk1[nt][e]));
             }
         }
     }
@@ -739,9 +793,9 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_mfma(GbArgs a) {
             for (int e = 0; e < 4; ++e) {
                 const int x = 16 * w + 4 * g + e;
                 if (x >= t) {
-                    const float d = __builtin_amdgcn_exp2f(cc[x] - cc[t]);
+                    const float d = __builtin_amdgcn_exp2f(cr[e] - cs4[nt]);
                     part += d * z1[nt][e];
-                    if (x > t) part -= d * bb[x] * z2[nt][e];
+                    if (x > t) part -= d * br[e] * z2[nt][e];
                 }
             }
             part += __shfl_xor(part, 16, 64);
@@ -754,11 +808,27 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grads_mfma(GbArgs a) {
         const int t = tid;
         const float ct = cc[t], cm = t > 0 ? cc[t - 1] : 0.f;
         const float gm = __builtin_amdgcn_exp2f(cm), el = __builtin_amdgcn_exp2f(cl - ct);
+        // s1 = sum_{x<t} 2^(c_{t-1} - c_x) kap_x and s2 = sum_{x>=t} 2^(c_x - c_t) (rho_x -
+        // [x > t] beta_x mu_x), in increasing x, as one unrolled pass of 16-byte broadcast
+        // reads (a loop with a data-dependent trip count waits on every read)
         float s1 = 0.f, s2 = 0.f;
-        for (int x = 0; x < t; ++x) s1 += __builtin_amdgcn_exp2f(cm - cc[x]) * sm.kap[x];
-        for (int x = t; x < C; ++x) {
-            const float d = __builtin_amdgcn_exp2f(cc[x] - ct);
-            s2 += d * (sm.rho[x] - (x > t ? bb[x] * sm.mu[x] : 0.f));
+#pragma unroll
+        for (int x4 = 0; x4 < C; x4 += 4) {
+            const float4 c4 = *reinterpret_cast<const float4*>(cc + x4);
+            const float4 k4 = *reinterpret_cast<const float4*>(sm.kap + x4);
+            const float4 r4 = *reinterpret_cast<const float4*>(sm.rho + x4);
+            const float4 m4 = *reinterpret_cast<const float4*>(sm.mu + x4);
+            const float4 b4 = *reinterpret_cast<const float4*>(bb + x4);
+            const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, kv[4] = {k4.x, k4.y, k4.z, k4.w},
+                        rv[4] = {r4.x, r4.y, r4.z, r4.w}, mv[4] = {m4.x, m4.y, m4.z, m4.w},
+                        bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int x = x4 + i;
+                const float d = __builtin_amdgcn_exp2f(x < t ? cm - cv[i] : cv[i] - ct);
+                if (x < t) s1 += d * kv[i];
+                else s2 += d * (rv[i] - (x > t ? bv[i] * mv[i] : 0.f));
+            }
         }
         static_assert(NT == 256, "four waves");
         const float zt = ((sm.zw[0][t] + sm.zw[1][t]) + sm.zw[2][t]) + sm.zw[3][t];

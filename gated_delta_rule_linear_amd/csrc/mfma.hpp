@@ -212,6 +212,9 @@ __device__ __forceinline__ uint32_t buf_ld4(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint32_t buf_ld2(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
+__device__ __forceinline__ void buf_st2(rsrc_t r, uint32_t off, uint16_t v) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+}
 __device__ __forceinline__ void buf_st8(rsrc_t r, uint32_t off, uint2 v) {
     typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, off, 0, 0);
