@@ -259,14 +259,32 @@ __global__ __launch_bounds__(NT) void ssd_bwd_grads_kernel(SbArgs a) {
     __syncthreads();
     const float cl = sm.c[C - 1];
     const float gamma = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
-    auto cm1 = [&](int s) { return s > 0 ? sm.c[s - 1] : 0.f; };
-    // Y (elementwise)
-    for (int idx = tid; idx < C * C; idx += NT) {
-        const int s = idx / C, u = idx % C;
-        sm.Y[s * PV + u] = f32_to_bf16(u < s ? __builtin_amdgcn_exp2f(cm1(s) - sm.c[u]) : 0.f);
-    }
-    // P, A, M: wave w owns rows 16 w .. 16 w + 15
+    // P, A, M: wave w owns rows 16 w .. 16 w + 15. The lane's decay sums (rows r = r0 + 4 g
+    // + e, columns s = 16 nt + j) are read once before any LDS write: LDS reads issued after
+    // an LDS write the compiler cannot tell apart wait for it, one round trip each.
     const int r0 = 16 * w;
+    float cr[4], cs4[C / 16];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cr[e] = sm.c[r0 + 4 * g + e];
+#pragma unroll
+    for (int nt = 0; nt < C / 16; ++nt) cs4[nt] = sm.c[16 * nt + jl];
+    {   // Y (elementwise): thread tid fills column u = tid mod C of rows tid / C + 4 i
+        static_assert(NT % C == 0, "whole rows per pass");
+        constexpr int NI = C * C / NT;
+        const int u = tid % C, s0 = tid / C;
+        const float cu = sm.c[u];
+        float cmv[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int s = s0 + (NT / C) * i;
+            cmv[i] = s > 0 ? sm.c[s - 1] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int s = s0 + (NT / C) * i;
+            sm.Y[s * PV + u] = f32_to_bf16(u < s ? __builtin_amdgcn_exp2f(cmv[i] - cu) : 0.f);
+        }
+    }
 #pragma unroll
     for (int nt = 0; nt < C / 16; ++nt) {
         f32x4_t qk = zero4(), ov = zero4();
@@ -280,16 +298,28 @@ __global__ __launch_bounds__(NT) void ssd_bwd_grads_kernel(SbArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = r0 + 4 * g + e;
-            const float d = s <= r ? __builtin_amdgcn_exp2f(sm.c[r] - sm.c[s]) : 0.f;
+            const float d = s <= r ? __builtin_amdgcn_exp2f(cr[e] - cs4[nt]) : 0.f;
             sm.P[r * PV + s] = f32_to_bf16(qk[e] * d);
             sm.A[r * PV + s] = f32_to_bf16(ov[e] * d);
             sm.M[r * PV + s] = f32_to_bf16(qk[e] * ov[e]);
         }
     }
     __syncthreads();
-    auto store_bf = [&](uint16_t* dst, int W, int r, int col, float x) {
-        if (r < n) dst[(tok0 + t0 + r) * size_t(W) + col] = f32_to_bf16(x);
+    // gradient rows past the sequence's end fall outside these resources and are dropped
+    // (branch-free stores)
+    auto rows_rsrc = [&](uint16_t* dst, int W) {
+        return make_rsrc(dst + (tok0 + t0) * size_t(W), uint32_t(n) * uint32_t(W) * 2u);
     };
+    const rsrc_t rdv = rows_rsrc(a.dv, DV), rdq = rows_rsrc(a.dq, DK), rdk = rows_rsrc(a.dk, DK);
+    auto store_bf = [&](const rsrc_t& rs, int W, int r, int col, float x) {
+        buf_st2(rs, uint32_t(r * W + col) * 2u, f32_to_bf16(x));
+    };
+    float er[4], fr[4];   // 2^{c_r} and 2^{c_last - c_r} of the lane's rows
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        er[e] = __builtin_amdgcn_exp2f(cr[e]);
+        fr[e] = __builtin_amdgcn_exp2f(cl - cr[e]);
+    }
     // dV = P^T dO + diag(F) K dS_out (rows s = 16 w ..)
 #pragma unroll
     for (int nt = 0; nt < DV / 16; ++nt) {
@@ -303,7 +333,7 @@ __global__ __launch_bounds__(NT) void ssd_bwd_grads_kernel(SbArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int s = r0 + 4 * g + e;
-            store_bf(a.dv, DV, s, 16 * nt + jl, x[e] + __builtin_amdgcn_exp2f(cl - sm.c[s]) * y[e]);
+            store_bf(rdv, DV, s, 16 * nt + jl, x[e] + fr[e] * y[e]);
         }
     }
     // dQ = diag(E) dO S_in^T + A K, dK = A^T Q + diag(F) V dS_out^T (rows 16 w ..)
@@ -323,8 +353,8 @@ __global__ __launch_bounds__(NT) void ssd_bwd_grads_kernel(SbArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = r0 + 4 * g + e;
-            store_bf(a.dq, DK, r, 16 * nt + jl, __builtin_amdgcn_exp2f(sm.c[r]) * x[e] + y[e]);
-            store_bf(a.dk, DK, r, 16 * nt + jl, u[e] + __builtin_amdgcn_exp2f(cl - sm.c[r]) * z[e]);
+            store_bf(rdq, DK, r, 16 * nt + jl, er[e] * x[e] + y[e]);
+            store_bf(rdk, DK, r, 16 * nt + jl, u[e] + fr[e] * z[e]);
         }
     }
     // alpha_r = sum_j (Q S_in)_rj dO_rj, beta_u = sum_j (K dS_out)_uj v_uj, and term2
@@ -369,7 +399,7 @@ __global__ __launch_bounds__(NT) void ssd_bwd_grads_kernel(SbArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = r0 + 4 * g + e;
-                if (s <= r) part += __builtin_amdgcn_exp2f(sm.c[r] - sm.c[s]) * z[e];
+                if (s <= r) part += __builtin_amdgcn_exp2f(cr[e] - cs4[nt]) * z[e];
             }
             // the four lane groups' rows in a fixed order, then one partial per wave
             part += __shfl_xor(part, 16, 64);
@@ -380,10 +410,27 @@ __global__ __launch_bounds__(NT) void ssd_bwd_grads_kernel(SbArgs a) {
     __syncthreads();
     if (tid < n) {
         const int s = tid;
-        const float es1 = __builtin_amdgcn_exp2f(cm1(s)), fs = __builtin_amdgcn_exp2f(cl - sm.c[s]);
+        const float cs = sm.c[s], cm = s > 0 ? sm.c[s - 1] : 0.f;
+        const float es1 = __builtin_amdgcn_exp2f(cm), fs = __builtin_amdgcn_exp2f(cl - cs);
+        // t1 = sum_{r>=s} 2^(c_r - c_s) alpha_r and t4 = sum_{u<s} 2^(c_{s-1} - c_u) beta_u, in
+        // increasing index, as one unrolled pass of 16-byte broadcast reads (a loop with a
+        // data-dependent trip count waits on every read)
         float t1 = 0.f, t4 = 0.f;
-        for (int r = s; r < C; ++r) t1 += __builtin_amdgcn_exp2f(sm.c[r] - sm.c[s]) * sm.alpha[r];
-        for (int u = 0; u < s; ++u) t4 += __builtin_amdgcn_exp2f(cm1(s) - sm.c[u]) * sm.beta[u];
+#pragma unroll
+        for (int x4 = 0; x4 < C; x4 += 4) {
+            const float4 c4 = *reinterpret_cast<const float4*>(sm.c + x4);
+            const float4 a4 = *reinterpret_cast<const float4*>(sm.alpha + x4);
+            const float4 b4 = *reinterpret_cast<const float4*>(sm.beta + x4);
+            const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, av[4] = {a4.x, a4.y, a4.z, a4.w},
+                        bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int x = x4 + i;
+                const float d = __builtin_amdgcn_exp2f(x >= s ? cv[i] - cs : cm - cv[i]);
+                if (x >= s) t1 += d * av[i];
+                else t4 += d * bv[i];
+            }
+        }
         static_assert(NT == 256, "four waves");
         const float t2 = ((sm.t2w[0][s] + sm.t2w[1][s]) + sm.t2w[2][s]) + sm.t2w[3][s];
         const float da = es1 * t1 + t2 + fs * es1 * gamma + fs * t4;
