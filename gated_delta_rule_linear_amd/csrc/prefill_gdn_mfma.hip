@@ -406,6 +406,16 @@ static_assert(PQ % 8 == 0 && C * (PQ / 8) % 64 == 0, "padded K rows in whole 1 K
 template <int J>
 using Ic = std::integral_constant<int, J>;
 
+// Value column of state column j (0..15) of chain wave cb within the tile. With two chain
+// waves the columns interleave in fours (wave cb holds 8 q + 4 cb + r, j = 4 q + r), so
+// the output rows the result tiles of both waves give one lane are eight contiguous
+// columns: one 16-byte store per lane and row block. Sums over value columns do not exist
+// in this kernel, so the order is free.
+template <int NCB>
+__device__ __forceinline__ int tile_col(int cb, int j) {
+    return NCB == 2 ? 8 * (j >> 2) + 4 * cb + (j & 3) : 16 * cb + j;
+}
+
 // One chunk's operands as the waves read them, copied straight from global memory: K
 // [s][i] (padded rows), T in fragment order, the value tile [s][col].
 template <int VT>
@@ -458,7 +468,7 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
         // =========================== chain wave ===========================
         // Reads only LDS: the chunk's K, T and value tile and its gate factors are in
         // place when the iteration starts. S[2 kk + h][e] is key 32 kk + 8 g + 4 h + e of
-        // column c0 + 16 cb + j.
+        // column c0 + tile_col(cb, j).
         const int cb = w;
         f32x4_t S[8];
         auto key = [&](int ib, int e) { return 32 * (ib >> 1) + 8 * g + 4 * (ib & 1) + e; };
@@ -466,7 +476,7 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
         for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                S[ib][e] = (a.S0 && cb < NCB) ? a.S0[seq * DK * DV + size_t(key(ib, e)) * DV + c0 + 16 * cb + jl]
+                S[ib][e] = (a.S0 && cb < NCB) ? a.S0[seq * DK * DV + size_t(key(ib, e)) * DV + c0 + tile_col<NCB>(cb, jl)]
                                               : 0.f;
 
         auto step = [&](auto J) {
@@ -479,8 +489,8 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
             const uint16_t* tc = slot_(J).t;
             const uint16_t* vc = slot_(J).v;
             const float (*gc)[C] = gsl[j & 3];
-            // The chunk's value tile (transpose reads: lane j receives column 16 cb + j of
-            // rows 16 tb + 4 g .. + 3, the result-tile layout) and its gate factors, read
+            // The chunk's value tile (transpose reads: lane j receives column tile_col(cb, j)
+            // of rows 16 tb + 4 g .. + 3, the result-tile layout) and its gate factors, read
             // before any LDS write of this step: the compiler keeps LDS reads behind earlier
             // LDS writes it cannot tell apart, so read later each would be a round trip of
             // its own on the chain's dependent path.
@@ -488,7 +498,7 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
             float4 g4[4], d4[4];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                const uint16_t* p = vc + (16 * tb + 4 * g + (jl >> 2)) * VT + 16 * cb + 4 * (jl & 3);
+                const uint16_t* p = vc + (16 * tb + 4 * g + (jl >> 2)) * VT + tile_col<NCB>(cb, 4 * (jl & 3));
                 vx[tb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
                 g4[tb] = *reinterpret_cast<const float4*>(&gc[1][16 * tb + 4 * g]);
                 d4[tb] = *reinterpret_cast<const float4*>(&gc[2][16 * tb + 4 * g]);
@@ -589,7 +599,7 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
             for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    a.S[seq * DK * DV + size_t(key(ib, e)) * DV + c0 + 16 * cb + jl] = S[ib][e];
+                    a.S[seq * DK * DV + size_t(key(ib, e)) * DV + c0 + tile_col<NCB>(cb, jl)] = S[ib][e];
         }
     } else {
         // =========================== output wave ===========================
@@ -651,7 +661,7 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
             for (int h = 0; h < NRB; ++h) {
                 const int rb = h == NRB - 1 ? RL : RF;
                 qoff[h] = ((16 * rb + jl) * DK + 8 * g) * 2u;
-                ooff[h] = ((16 * rb + jl) * uint32_t(DV) + c0 + 4 * g) * 2u;
+                ooff[h] = ((16 * rb + jl) * uint32_t(DV) + c0 + (NCB == 2 ? 8 : 4) * g) * 2u;
             }
             struct QSet {
                 uint4 q[NRB][4];   // rows 16 rb + j of q (the wave's row blocks), keys 32 kk + 8 g ..
@@ -734,7 +744,9 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
                     }
                     const bf16x8_t pf0 = pack_pk(pt[h][0], pt[h][1]), pf1 = pack_pk(pt[h][2], pt[h][3]);
                     const float gr = fast_exp(crr);
-                    // O^T = gamma (S^T Q^T) + U^T P^T: columns 16 ct + 4 g .. of token r
+                    // O^T = gamma (S^T Q^T) + U^T P^T: value columns tile_col(ct, 4 g ..) of
+                    // token r, both chain waves' four columns stored together
+                    uint2 ow[NCB];
 #pragma unroll
                     for (int ct = 0; ct < NCB; ++ct) {
                         f32x4_t oq = zero4();
@@ -744,8 +756,10 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
                         f32x4_t o_ = oq * gr;
                         o_ = mfma16(uf[ct][0], pf0, o_);
                         if (rb >= 2) o_ = mfma16(uf[ct][1], pf1, o_);
-                        buf_st8_off(orc, ooff[h], 32 * ct, pack4(o_));
+                        ow[ct] = pack4(o_);
                     }
+                    if constexpr (NCB == 2) buf_st16(orc, ooff[h], make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
+                    else buf_st8_off(orc, ooff[h], 0, ow[0]);
                 }
             };
             QSet Q[4];   // chunk x's q in set x mod 4, loaded two iterations ahead
