@@ -101,7 +101,12 @@ struct __align__(16) PrepSmem {
     __align__(16) uint16_t ko[C * PQ];      // k~, own row block's reference
     __align__(16) uint16_t pc[6][16 * PQ];  // rescaled copy for each off-diagonal pair
     __align__(16) float T[8][DK];           // gate product of each 8-row group
+    // q^ in the workspace's fragment order: every lane forms 4-byte pieces scattered over
+    // the chunk's q^ block, so they are gathered here and written out in whole 16-byte
+    // pieces (scattered 4-byte stores to memory cost far more than the same bytes whole)
+    __align__(16) uint16_t qh[C * DK];
 };
+static_assert(2 * sizeof(PrepSmem) <= 163840, "two prep workgroups per compute unit");
 
 template <bool GB>
 __global__ __launch_bounds__(NTP) void gla_prep_kernel(GlaArgs a) {
@@ -238,8 +243,8 @@ __global__ __launch_bounds__(NTP) void gla_prep_kernel(GlaArgs a) {
         // piece of lane group gg (key kc = 4 gg + e or 16 + 4 gg + e goes to slot e or 4 + e)
         const int kk = col >> 5, kc = col & 31, gg = (kc & 15) >> 2;
         const int slot = (kc & 3) + (kc >= 16 ? 4 : 0);
-        *reinterpret_cast<uint32_t*>(wsc + kWsQ + (((rr >> 4) * 4 + kk) * 64 + 16 * gg + pr) * 16 +
-                                     slot * 2) =
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<unsigned char*>(sm.qh) +
+                                     (((rr >> 4) * 4 + kk) * 64 + 16 * gg + pr) * 16 + slot * 2) =
             pack_bf16x2(q0 * (pre[0] * pp[r][0]), q1 * (pre[1] * pp[r][1]));
         kh[r][0] = k0 * (ss[r][0] * suf[0]);
         kh[r][1] = k1 * (ss[r][1] * suf[1]);
@@ -255,6 +260,13 @@ __global__ __launch_bounds__(NTP) void gla_prep_kernel(GlaArgs a) {
             pack8(f);
     }
     lds_barrier();
+    // q^ to the workspace in whole 16-byte pieces, coalesced
+#pragma unroll
+    for (int x = 0; x < C * DK * 2 / 16 / NTP; ++x) {
+        const int pz = tid + NTP * x;
+        *reinterpret_cast<uint4*>(wsc + kWsQ + pz * 16) =
+            *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(sm.qh) + pz * 16);
+    }
     // P: ten lower tiles, D'[s][r] = sum_i K~_si Q~_ri over key block sb and row block rb,
     // stored straight from the accumulators as half pieces; the two upper half pieces
     // the forward kernel reads, (0, 1) and (2, 3), are written as zeros. Waves 0 and 1
