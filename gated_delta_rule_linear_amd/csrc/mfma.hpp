@@ -223,6 +223,12 @@ __device__ __forceinline__ void buf_st16(rsrc_t r, uint32_t off, uint4 v) {
     typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, 0);
 }
+// Output stores (written once, never read back by the kernel): non-temporal, so the
+// lines stream out instead of displacing the inputs the walk still reads from L2.
+__device__ __forceinline__ void buf_st16_out(rsrc_t r, uint32_t off, uint4 v) {
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, 2);
+}
 // The same with a constant byte offset folded into the instruction (0 .. 4095), for
 // loops whose per-lane offset register stays fixed while the resource moves.
 __device__ __forceinline__ uint4 buf_ld16_off(rsrc_t r, uint32_t off, int imm) {

@@ -758,7 +758,7 @@ __global__ __launch_bounds__(384) void gdn_fwd_kernel(GdnArgs a) {
                         if (rb >= 2) o_ = mfma16(uf[ct][1], pf1, o_);
                         ow[ct] = pack4(o_);
                     }
-                    if constexpr (NCB == 2) buf_st16(orc, ooff[h], make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
+                    if constexpr (NCB == 2) buf_st16_out(orc, ooff[h], make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
                     else buf_st8_off(orc, ooff[h], 0, ow[0]);
                 }
             };

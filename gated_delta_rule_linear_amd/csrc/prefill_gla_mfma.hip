@@ -503,10 +503,10 @@ __global__ __launch_bounds__(NT) void gla_chain_kernel(GlaArgs a) {
                     __builtin_bit_cast(uint4, pack_pk(S[0][ct], S[1][ct]));
             const uint32_t orow = ((uint32_t(ch0 + lc) * C + rw) * uint32_t(DV) + c0 + 4 * NVT * g) * 2u;
             if constexpr (NVT == 4) {
-                buf_st16(ro, orow, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
-                buf_st16(ro, orow + 16u, make_uint4(ow[2].x, ow[2].y, ow[3].x, ow[3].y));
+                buf_st16_out(ro, orow, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
+                buf_st16_out(ro, orow + 16u, make_uint4(ow[2].x, ow[2].y, ow[3].x, ow[3].y));
             } else if constexpr (NVT == 2) {
-                buf_st16(ro, orow, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
+                buf_st16_out(ro, orow, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
             } else {
                 buf_st8(ro, orow, ow[0]);
             }

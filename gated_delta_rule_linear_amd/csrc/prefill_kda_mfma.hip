@@ -588,7 +588,7 @@ __global__ __launch_bounds__(NTF) void kda_fwd_kernel(KdaArgs a) {
         }
         {
             const uint32_t oo = ((t0 + rw) * uint32_t(DV) + c0 + colmap<NVT>(0, 4 * g)) * 2u;
-            if constexpr (NVT == 2) buf_st16(ro, oo, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
+            if constexpr (NVT == 2) buf_st16_out(ro, oo, make_uint4(ow[0].x, ow[0].y, ow[1].x, ow[1].y));
             else buf_st8(ro, oo, ow[0]);
         }
         // ---- S = Diag(G_last) S + K^^T U (key rows 32 rb ..), bf16 copy to st
