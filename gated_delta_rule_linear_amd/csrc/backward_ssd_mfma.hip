@@ -39,7 +39,8 @@ struct SbArgs {
     uint16_t *dq, *dk, *dv;
     void* dg;
     float* dS0;
-    float *Sst, *dSt, *ac;   // [nseq][nch][DK][DV] x 2, [nseq][nch]
+    float *Sst, *dSt, *ac;   // [nseq][nch][DK][DV] x 2 (chunk sums dS, G), [nseq][nch]
+    uint16_t *Sb, *dSb;      // [nseq][nch][DK][DV] x 2: S_in, dS_out of every chunk, bf16
     int N, nseq, nch;
 };
 
@@ -157,44 +158,68 @@ __global__ __launch_bounds__(NT) void ssd_bwd_sums_kernel(SbArgs a) {
 
 // ---------------------------------------------------------------------------- scans
 __global__ __launch_bounds__(NT) void ssd_bwd_scans_kernel(SbArgs a) {
-    const size_t e = size_t(blockIdx.x) * NT + threadIdx.x;
+    // four consecutive state elements per thread: 16-byte reads of the fp32 chunk sums,
+    // 8-byte writes of the bf16 chunk states (the state itself is carried in fp32)
+    const size_t e4 = size_t(blockIdx.x) * NT + threadIdx.x;
     constexpr size_t SS = size_t(DK) * DV;
-    if (e >= size_t(a.nseq) * SS) return;
-    const size_t seq = e / SS, ij = e % SS;
-    float* Ss = a.Sst + seq * a.nch * SS + ij;
-    float* dSs = a.dSt + seq * a.nch * SS + ij;
+    if (e4 >= size_t(a.nseq) * SS / 4) return;
+    const size_t e = 4 * e4, seq = e / SS, ij = e % SS;
+    const float* Ss = a.Sst + seq * a.nch * SS + ij;
+    const float* dSs = a.dSt + seq * a.nch * SS + ij;
+    uint16_t* Sbs = a.Sb + seq * a.nch * SS + ij;
+    uint16_t* dSbs = a.dSb + seq * a.nch * SS + ij;
     const float* ac = a.ac + seq * a.nch;
-    float S = a.S0 ? a.S0[e] : 0.f;
-    // chunks in batches of SB: a batch's loads are issued before its stores (same array)
+    auto ld4 = [](const float* p) { return *reinterpret_cast<const float4*>(p); };
+    auto st4 = [](uint16_t* p, const float (&x)[4]) {
+        *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+    };
+    float S[4] = {0.f, 0.f, 0.f, 0.f};
+    if (a.S0) {
+        const float4 s0 = ld4(a.S0 + e);
+        S[0] = s0.x; S[1] = s0.y; S[2] = s0.z; S[3] = s0.w;
+    }
+    // chunks in batches of SB, every load of a batch issued before its stores
     constexpr int SB = 8;
     for (int c0 = 0; c0 < a.nch; c0 += SB) {
-        float d[SB], g[SB];
+        float4 d[SB];
+        float g[SB];
 #pragma unroll
         for (int b = 0; b < SB; ++b) {
-            d[b] = c0 + b < a.nch ? Ss[(c0 + b) * SS] : 0.f;
+            d[b] = c0 + b < a.nch ? ld4(Ss + (c0 + b) * SS) : make_float4(0.f, 0.f, 0.f, 0.f);
             g[b] = c0 + b < a.nch ? ac[c0 + b] : 1.f;
         }
 #pragma unroll
         for (int b = 0; b < SB; ++b) {
-            if (c0 + b < a.nch) Ss[(c0 + b) * SS] = S;
-            S = g[b] * S + d[b];
+            if (c0 + b < a.nch) st4(Sbs + (c0 + b) * SS, S);
+            S[0] = g[b] * S[0] + d[b].x;
+            S[1] = g[b] * S[1] + d[b].y;
+            S[2] = g[b] * S[2] + d[b].z;
+            S[3] = g[b] * S[3] + d[b].w;
         }
     }
-    float dS = a.dSf ? a.dSf[e] : 0.f;
+    float dS[4] = {0.f, 0.f, 0.f, 0.f};
+    if (a.dSf) {
+        const float4 f = ld4(a.dSf + e);
+        dS[0] = f.x; dS[1] = f.y; dS[2] = f.z; dS[3] = f.w;
+    }
     for (int c1 = a.nch - 1; c1 >= 0; c1 -= SB) {
-        float d[SB], g[SB];
+        float4 d[SB];
+        float g[SB];
 #pragma unroll
         for (int b = 0; b < SB; ++b) {
-            d[b] = c1 - b >= 0 ? dSs[(c1 - b) * SS] : 0.f;
+            d[b] = c1 - b >= 0 ? ld4(dSs + (c1 - b) * SS) : make_float4(0.f, 0.f, 0.f, 0.f);
             g[b] = c1 - b >= 0 ? ac[c1 - b] : 1.f;
         }
 #pragma unroll
         for (int b = 0; b < SB; ++b) {
-            if (c1 - b >= 0) dSs[(c1 - b) * SS] = dS;
-            dS = g[b] * dS + d[b];
+            if (c1 - b >= 0) st4(dSbs + (c1 - b) * SS, dS);
+            dS[0] = g[b] * dS[0] + d[b].x;
+            dS[1] = g[b] * dS[1] + d[b].y;
+            dS[2] = g[b] * dS[2] + d[b].z;
+            dS[3] = g[b] * dS[3] + d[b].w;
         }
     }
-    a.dS0[e] = dS;
+    *reinterpret_cast<float4*>(a.dS0 + e) = make_float4(dS[0], dS[1], dS[2], dS[3]);
 }
 
 // ---------------------------------------------------------------------------- grads
@@ -224,14 +249,14 @@ __global__ __launch_bounds__(NT) void ssd_bwd_grads_kernel(SbArgs a) {
     fetch_rows(kr, a.k, tok0, t0, n);
     fetch_rows(vr, a.v, tok0, t0, n);
     fetch_rows(dr, a.dO, tok0, t0, n);
-    constexpr int NS = DK * DV / 4 / NT;   // float4 pieces of S_in (and of dS_out) per thread
-    float4 s4v[NS], d4v[NS];
+    constexpr int NS = DK * DV / 4 / NT;   // 4-element pieces of S_in (and of dS_out) per thread
+    uint2 s4v[NS], d4v[NS];
     const size_t base = (seq * a.nch + ch) * size_t(DK) * DV;
 #pragma unroll
     for (int x = 0; x < NS; ++x) {
         const size_t p = size_t(tid + NT * x);
-        s4v[x] = *reinterpret_cast<const float4*>(a.Sst + base + 4 * p);
-        d4v[x] = *reinterpret_cast<const float4*>(a.dSt + base + 4 * p);
+        s4v[x] = *reinterpret_cast<const uint2*>(a.Sb + base + 4 * p);
+        d4v[x] = *reinterpret_cast<const uint2*>(a.dSb + base + 4 * p);
     }
     chunk_logs<GB>(sm.c, a, tok0, t0, n);
     if (tid < C) { sm.alpha[tid] = 0.f; sm.beta[tid] = 0.f; }
@@ -239,19 +264,20 @@ __global__ __launch_bounds__(NT) void ssd_bwd_grads_kernel(SbArgs a) {
     stage_rows<DK, PQ>(sm.k, kr, [](int) { return 1.f; });
     stage_rows<DV, PV>(sm.v, vr, [](int) { return 1.f; });
     stage_rows<DV, PV>(sm.dO, dr, [](int) { return 1.f; });
-    // S_in and dS_out (fp32 in the workspace) as bf16 tiles, and gamma = <dS_out, S_in>
+    // S_in and dS_out (bf16 in the workspace) to their LDS tiles, and gamma = <dS_out, S_in>
     {
         float gam = 0.f;
 #pragma unroll
         for (int x = 0; x < NS; ++x) {
             const int p = tid + NT * x;
             const int i = (4 * p) / DV, j = (4 * p) % DV;
-            const float4 s4 = s4v[x], d4 = d4v[x];
-            gam += s4.x * d4.x + s4.y * d4.y + s4.z * d4.z + s4.w * d4.w;
-            *reinterpret_cast<uint2*>(sm.sin + i * PV + j) =
-                make_uint2(pack_bf16x2(s4.x, s4.y), pack_bf16x2(s4.z, s4.w));
-            *reinterpret_cast<uint2*>(sm.dso + i * PV + j) =
-                make_uint2(pack_bf16x2(d4.x, d4.y), pack_bf16x2(d4.z, d4.w));
+            const uint2 s4 = s4v[x], d4 = d4v[x];
+            gam += __uint_as_float(s4.x << 16) * __uint_as_float(d4.x << 16) +
+                   __uint_as_float(s4.x & 0xffff0000u) * __uint_as_float(d4.x & 0xffff0000u) +
+                   __uint_as_float(s4.y << 16) * __uint_as_float(d4.y << 16) +
+                   __uint_as_float(s4.y & 0xffff0000u) * __uint_as_float(d4.y & 0xffff0000u);
+            *reinterpret_cast<uint2*>(sm.sin + i * PV + j) = s4;
+            *reinterpret_cast<uint2*>(sm.dso + i * PV + j) = d4;
         }
         gam = wave_sum(gam);
         if (lane == 0) sm.red[w] = gam;
@@ -441,7 +467,7 @@ __global__ __launch_bounds__(NT) void ssd_bwd_grads_kernel(SbArgs a) {
 }
 
 struct SbLayout {
-    size_t Sst, dSt, ac, total;
+    size_t Sst, dSt, Sb, dSb, ac, total;
 };
 SbLayout sb_layout(const Problem& p) {
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
@@ -450,6 +476,8 @@ SbLayout sb_layout(const Problem& p) {
     size_t off = 0;
     L.Sst = off; off += al(nseq * nch * DK * DV * 4);
     L.dSt = off; off += al(nseq * nch * DK * DV * 4);
+    L.Sb = off; off += al(nseq * nch * DK * DV * 2);
+    L.dSb = off; off += al(nseq * nch * DK * DV * 2);
     L.ac = off; off += al(nseq * nch * 4);
     L.total = off;
     return L;
@@ -464,8 +492,8 @@ hipError_t launch_gb(const BwdProblem& bp, SbArgs a) {
     if (e != hipSuccess) return e;
     ssd_bwd_sums_kernel<GB><<<dim3(units), dim3(NT), sizeof(SumsSmem), p.stream>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const size_t nel = size_t(a.nseq) * DK * DV;
-    ssd_bwd_scans_kernel<<<dim3(unsigned((nel + NT - 1) / NT)), dim3(NT), 0, p.stream>>>(a);
+    const size_t nel4 = size_t(a.nseq) * DK * DV / 4;
+    ssd_bwd_scans_kernel<<<dim3(unsigned((nel4 + NT - 1) / NT)), dim3(NT), 0, p.stream>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ssd_bwd_grads_kernel<GB>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(GradsSmem)));
@@ -506,6 +534,8 @@ hipError_t launch_backward_ssd_mfma(const BwdProblem& bp) {
     a.dS0 = bp.dS0;
     a.Sst = reinterpret_cast<float*>(ws + L.Sst);
     a.dSt = reinterpret_cast<float*>(ws + L.dSt);
+    a.Sb = reinterpret_cast<uint16_t*>(ws + L.Sb);
+    a.dSb = reinterpret_cast<uint16_t*>(ws + L.dSb);
     a.ac = reinterpret_cast<float*>(ws + L.ac);
     a.N = p.N;
     a.nseq = int(nseq);
